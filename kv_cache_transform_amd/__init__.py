@@ -1,0 +1,129 @@
+"""MI355X-native TurboQuant-family KV-cache codec (Python binding of libtq.so).
+
+Every step of the path runs in the HIP kernels behind the C ABI (include/tq.h); this module only
+marshals torch tensors (device memory) and the current HIP stream.  Sources: "Ablation, Statistical
+Inference, and Validation for KV-Cache Compression" (arXiv 2607.09683), §2 TurboQuant.
+"""
+from __future__ import annotations
+
+import ctypes
+from dataclasses import dataclass
+
+import torch
+
+from . import _lib
+from ._lib import TQError, TQ_BF16, TQ_F32
+
+__all__ = ["Codec", "TQError", "get_layout", "encode", "decode", "qk_scores", "decode_attention",
+           "attention_workspace_bytes", "host_tables", "clear_cache"]
+
+_DT = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}
+
+
+@dataclass(frozen=True)
+class Codec:
+    """d: head_dim (64/128/256); b: codebook bits; m: QJL sketch rows (0 = none);
+    n_heads: heads with distinct random state (stream st uses head st % n_heads); seed."""
+    d: int
+    b: int
+    m: int = 0
+    n_heads: int = 1
+    seed: int = 0
+
+    def params(self) -> _lib.Params:
+        return _lib.Params(self.d, self.b, self.m, self.n_heads, self.seed & ((1 << 64) - 1))
+
+
+def _stream(device=None) -> ctypes.c_void_p:
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t: torch.Tensor) -> ctypes.c_void_p:
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def get_layout(codec: Codec, n_streams: int, n_tokens: int) -> dict:
+    lay = _lib.Layout()
+    _lib.check(_lib.lib().tq_get_layout(ctypes.byref(codec.params()), n_streams, n_tokens, ctypes.byref(lay)),
+               "tq_get_layout")
+    return {f: getattr(lay, f) for f, _ in _lib.Layout._fields_}
+
+
+def encode(codec: Codec, x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """x: [n_streams, n_tokens, d] float32 or bfloat16 on the GPU -> packed uint8 buffer."""
+    if x.dim() != 3 or x.shape[-1] != codec.d or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [n_streams, n_tokens, d] tensor")
+    S, N, _ = x.shape
+    lay = get_layout(codec, S, N)
+    if out is None:
+        out = torch.empty(lay["total_bytes"], dtype=torch.uint8, device=x.device)
+    elif out.numel() < lay["total_bytes"] or out.dtype != torch.uint8:
+        raise ValueError("packed buffer too small")
+    _lib.check(_lib.lib().tq_encode(ctypes.byref(codec.params()), _ptr(x), _DT[x.dtype], S, N, _ptr(out),
+                                    _stream(x.device)), "tq_encode")
+    return out
+
+
+def decode(codec: Codec, packed: torch.Tensor, n_streams: int, n_tokens: int,
+           dtype: torch.dtype = torch.float32, out: torch.Tensor | None = None) -> torch.Tensor:
+    if out is None:
+        out = torch.empty(n_streams, n_tokens, codec.d, dtype=dtype, device=packed.device)
+    _lib.check(_lib.lib().tq_decode(ctypes.byref(codec.params()), _ptr(packed), n_streams, n_tokens, _ptr(out),
+                                    _DT[out.dtype], _stream(packed.device)), "tq_decode")
+    return out
+
+
+def qk_scores(codec: Codec, q: torch.Tensor, packed_k: torch.Tensor, n_tokens: int,
+              out: torch.Tensor | None = None, workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """q: [n_streams, n_q, d] -> unscaled score estimates [n_streams, n_q, n_tokens] (float32)."""
+    S, nq, _ = q.shape
+    ws_bytes = _lib.lib().tq_scores_workspace_bytes(ctypes.byref(codec.params()), S, nq)
+    if workspace is None:
+        workspace = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty(S, nq, n_tokens, dtype=torch.float32, device=q.device)
+    _lib.check(_lib.lib().tq_qk_scores(ctypes.byref(codec.params()), _ptr(q), _DT[q.dtype], nq, _ptr(packed_k), S,
+                                       n_tokens, _ptr(out), _ptr(workspace), workspace.numel(),
+                                       _stream(q.device)), "tq_qk_scores")
+    return out
+
+
+def attention_workspace_bytes(ck: Codec, batch: int, n_q_heads: int, n_kv_heads: int, n_tokens: int) -> int:
+    return int(_lib.lib().tq_attention_workspace_bytes(ctypes.byref(ck.params()), batch, n_q_heads, n_kv_heads,
+                                                       n_tokens))
+
+
+def decode_attention(ck: Codec, cv: Codec, q: torch.Tensor, packed_k: torch.Tensor, packed_v: torch.Tensor,
+                     n_kv_heads: int, n_tokens: int, softmax_scale: float = 0.0,
+                     out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+                     workspace: torch.Tensor | None = None) -> torch.Tensor:
+    """q: [batch, n_q_heads, d] -> attention output [batch, n_q_heads, d] over the packed cache."""
+    B, Hq, d = q.shape
+    if workspace is None:
+        workspace = torch.empty(max(attention_workspace_bytes(ck, B, Hq, n_kv_heads, n_tokens), 16),
+                                dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty(B, Hq, d, dtype=out_dtype, device=q.device)
+    _lib.check(_lib.lib().tq_decode_attention(
+        ctypes.byref(ck.params()), ctypes.byref(cv.params()), _ptr(q), _DT[q.dtype], B, Hq, n_kv_heads,
+        _ptr(packed_k), _ptr(packed_v), n_tokens, ctypes.c_float(softmax_scale), _ptr(out), _DT[out.dtype],
+        _ptr(workspace), workspace.numel(), _stream(q.device)), "tq_decode_attention")
+    return out
+
+
+def host_tables(codec: Codec, head: int = 0) -> dict:
+    """Host copies of the library's tables (thresholds, centroids in fp64; signs; S as float)."""
+    import numpy as np
+    L = 1 << codec.b
+    thr = np.zeros(L - 1, dtype=np.float64)
+    cen = np.zeros(L, dtype=np.float64)
+    sg = np.zeros(codec.d, dtype=np.float32)
+    S = np.zeros(max(codec.m, 1) * codec.d, dtype=np.float32)
+    _lib.check(_lib.lib().tq_host_tables(ctypes.byref(codec.params()), head, thr.ctypes.data, cen.ctypes.data,
+                                         sg.ctypes.data, S.ctypes.data), "tq_host_tables")
+    return {"thresholds": thr, "centroids": cen, "signs": sg,
+            "S": S[: codec.m * codec.d].reshape(codec.m, codec.d) if codec.m else None}
+
+
+def clear_cache() -> None:
+    _lib.lib().tq_clear_cache()

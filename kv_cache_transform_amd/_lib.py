@@ -1,0 +1,77 @@
+"""ctypes loader for libtq.so (the C ABI declared in include/tq.h).
+
+The library is required: there is no fallback implementation.  If libtq.so has not been built
+(``python -m kv_cache_transform_amd.build``) every call raises."""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libtq.so")
+
+TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EALIGN, TQ_EWORKSPACE, TQ_EHIP = 0, -1, -2, -3, -4, -5
+TQ_F32, TQ_BF16, TQ_F16 = 0, 1, 2
+
+# every symbol include/tq.h declares
+EXPORTS = ("tq_get_layout", "tq_encode", "tq_decode", "tq_scores_workspace_bytes", "tq_qk_scores",
+           "tq_attention_workspace_bytes", "tq_decode_attention", "tq_host_tables", "tq_status_string",
+           "tq_clear_cache")
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int32), ("b", ctypes.c_int32), ("m", ctypes.c_int32),
+                ("n_heads", ctypes.c_int32), ("seed", ctypes.c_uint64)]
+
+
+class Layout(ctypes.Structure):
+    _fields_ = [("idx_bytes_per_vec", ctypes.c_int64), ("sketch_bytes_per_vec", ctypes.c_int64),
+                ("off_idx", ctypes.c_int64), ("off_sketch", ctypes.c_int64), ("off_norm", ctypes.c_int64),
+                ("off_rnorm", ctypes.c_int64), ("total_bytes", ctypes.c_int64)]
+
+
+class TQError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        super().__init__(f"{what}: {status_string(status)} ({status})")
+        self.status = status
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m kv_cache_transform_amd.build`")
+    L = ctypes.CDLL(LIB_PATH)
+    P, I64, VP, I32, SZ = ctypes.POINTER(Params), ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    sig = {
+        "tq_get_layout": (ctypes.c_int, [P, I64, I64, ctypes.POINTER(Layout)]),
+        "tq_encode": (ctypes.c_int, [P, VP, ctypes.c_int, I64, I64, VP, VP]),
+        "tq_decode": (ctypes.c_int, [P, VP, I64, I64, VP, ctypes.c_int, VP]),
+        "tq_scores_workspace_bytes": (SZ, [P, I64, I64]),
+        "tq_qk_scores": (ctypes.c_int, [P, VP, ctypes.c_int, I64, VP, I64, I64, VP, VP, SZ, VP]),
+        "tq_attention_workspace_bytes": (SZ, [P, I32, I32, I32, I64]),
+        "tq_decode_attention": (ctypes.c_int, [P, P, VP, ctypes.c_int, I32, I32, I32, VP, VP, I64,
+                                               ctypes.c_float, VP, ctypes.c_int, VP, SZ, VP]),
+        "tq_host_tables": (ctypes.c_int, [P, I32, VP, VP, VP, VP]),
+        "tq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+        "tq_clear_cache": (None, []),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(L, name)
+        f.restype = res
+        f.argtypes = args
+    _lib = L
+    return L
+
+
+def status_string(status: int) -> str:
+    return lib().tq_status_string(status).decode()
+
+
+def check(status: int, what: str) -> None:
+    if status != TQ_OK:
+        raise TQError(status, what)

@@ -1,0 +1,93 @@
+// Kernel argument blocks and launcher declarations (host <-> .hip translation units).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tq {
+
+// Device-resident read-only tables for one (d, b, m, n_heads, seed); built on the host.
+struct DevTables {
+    int d = 0, b = 0, m = 0, n_heads = 0;
+    uint64_t seed = 0;
+    int G = 0;                         // search grid cells
+    const uint32_t* grid = nullptr;    // (G+2) x {thr fp32 bits, base}
+    const float* cent = nullptr;       // 2^b centroids (fp32)
+    const float* cent_x1024 = nullptr; // 2^b centroids x 1024 (fp32, exact scaling)
+    const float* lut_f32 = nullptr;    // dequant LUT: 2^(P b) entries of P fp32 (P = lut_group(b))
+    const _Float16* lut_f16 = nullptr; // same in fp16
+    const float* signs_slot = nullptr; // [head][4][d/4] ±1 of coordinate in_coord(d, s, g)
+    const float* signs = nullptr;      // [head][d] ±1
+    const _Float16* S = nullptr;       // [head][m][d] fp16 Gaussian
+    void* blob = nullptr;              // single allocation owning all of the above
+};
+
+struct EncodeArgs {
+    const void* x;           // [n_streams][n_tokens][d]
+    uint8_t* packed;
+    int64_t n_streams, n_tokens;
+    int64_t off_idx, off_sketch, off_norm, off_rnorm;
+    int64_t tiles_per_stream;  // ceil(n_tokens / 16)
+    int64_t n_tiles;           // n_streams * tiles_per_stream
+    int64_t tiles_per_wave;
+    DevTables t;
+};
+
+struct DecodeArgs {
+    const uint8_t* packed;
+    void* out;
+    int64_t n_streams, n_tokens;
+    int64_t off_idx, off_norm;
+    int64_t tiles_per_stream, n_tiles, tiles_per_wave;
+    DevTables t;
+};
+
+struct QPrepArgs {
+    const void* q;          // [n_rows][d], row r belongs to stream r / n_q_per_stream
+    int q_bf16;
+    int64_t n_rows;
+    int n_q_per_stream;     // rows per stream (RNG head = stream % n_heads)
+    _Float16* q_rot;        // [n_rows][d]
+    _Float16* p;            // [n_rows][m] (m > 0)
+    DevTables t;
+};
+
+struct ScoresArgs {
+    const uint8_t* packed;
+    const _Float16* q_rot;  // [n_streams][n_q][d]
+    const _Float16* p;      // [n_streams][n_q][m]
+    float* scores;          // [n_streams][n_q][n_tokens]
+    int64_t n_streams, n_tokens;
+    int n_q;
+    int64_t off_idx, off_sketch, off_norm, off_rnorm;
+    int64_t tiles_per_stream, n_tiles, tiles_per_wave;
+    DevTables t;
+};
+
+struct AttnArgs {
+    const uint8_t* pk;       // packed K
+    const uint8_t* pv;       // packed V
+    const _Float16* q_rot;   // [batch*n_q_heads][d]  (rotated with the K signs of its kv head)
+    const _Float16* p;       // [batch*n_q_heads][m]
+    float* part;             // [batch*n_kv][n_split][16 queries][d] rotated-domain partial sums
+    float* part_ml;          // [batch*n_kv][n_split][16][2] running max (log2 units) and sum
+    void* out;               // [batch][n_q_heads][d]
+    int out_bf16;
+    int64_t n_tokens;
+    int batch, n_q_heads, n_kv_heads, group;  // group = n_q_heads / n_kv_heads
+    int n_split;
+    int64_t tokens_per_split;
+    float scale_log2;        // softmax scale * log2(e)
+    int64_t k_off_idx, k_off_sketch, k_off_norm, k_off_rnorm;
+    int64_t v_off_idx, v_off_norm;
+    DevTables tk, tv;
+};
+
+// launchers: return hipSuccess or the launch error
+hipError_t launch_encode(const EncodeArgs& a, bool x_bf16, int num_cus, hipStream_t s);
+hipError_t launch_decode(const DecodeArgs& a, bool out_bf16, int num_cus, hipStream_t s);
+hipError_t launch_qprep(const QPrepArgs& a, hipStream_t s);
+hipError_t launch_scores(const ScoresArgs& a, int num_cus, hipStream_t s);
+bool attention_supported(int d, int bk, int bv);
+hipError_t launch_attention(const AttnArgs& a, int num_cus, hipStream_t s, bool* supported);
+
+}  // namespace tq

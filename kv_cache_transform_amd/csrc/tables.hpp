@@ -1,0 +1,39 @@
+// Host-side tables of the codec: random signs and Gaussian S (SplitMix64 + Box-Muller), the
+// Lloyd-Max codebook of the rotated-coordinate density, and the derived lookup tables the gfx950
+// kernels read (search grid, dequantisation LUTs, per-lane sign tables).
+#pragma once
+#include <cstdint>
+#include <vector>
+
+namespace tq {
+
+// ---- random state: SplitMix64 (Steele, Lea, Flood 2014), counter form ------------------------
+uint64_t mix64(uint64_t z);
+uint64_t stream_key(uint64_t seed, uint32_t tag, uint32_t head);
+// s_j = -1 iff bit 63 of word j (tag 1)
+void head_signs(uint64_t seed, uint32_t head, int d, std::vector<float>& out);
+// S[row][col] = fp16_rne(sqrt(-2 ln u1) cos(2 pi u2)) from words (2e, 2e+1), e = row*d + col (tag 2)
+void gaussian_matrix_f16(uint64_t seed, uint32_t head, int m, int d, std::vector<uint16_t>& out);
+
+// ---- Lloyd-Max codebook for f(x) ∝ (1-x^2)^((d-3)/2) on [-1,1] ---------------------------------
+// thresholds[L-1], centroids[L] ascending, L = 2^b.  Returns 0 on success.
+int lloyd_max(int d, int b, std::vector<double>& thresholds, std::vector<double>& centroids);
+
+// ---- kernel-side derived tables ---------------------------------------------------------------
+// Search grid over y in [-1,1]: cell c = (uint)(y*G/2 + G/2); entry c = {fp32 bits of the one
+// threshold that can fall in the cell (or +inf), count of thresholds below the cell}; for every fp32
+// y that maps to cell c, #{k : thr_f32[k] <= y} == base + (y >= thr).  G+2 entries.
+struct Grid {
+    int G = 0;
+    std::vector<uint32_t> entries;  // 2 words per cell
+};
+bool build_grid(const std::vector<float>& thr_f32, Grid& out);
+
+// coordinates per dequantisation lookup for b bits
+inline int lut_group(int b) { return (b == 1 || b == 2 || b == 4) ? 8 / b : ((b == 3 || b == 5 || b == 6) ? 2 : 1); }
+
+uint16_t f32_to_f16_bits(float f);     // round to nearest even
+uint16_t f64_to_f16_bits(double f);    // round to nearest even, one rounding
+float f16_bits_to_f32(uint16_t h);
+
+}  // namespace tq

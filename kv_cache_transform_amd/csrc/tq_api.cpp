@@ -1,0 +1,450 @@
+// C ABI of libtq (declared in include/tq.h): argument validation, packed layout, the device table
+// cache and kernel dispatch.  Every entry point validates all arguments before any HIP call.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <memory>
+#include <mutex>
+#include <tuple>
+#include <vector>
+
+#include "../../include/tq.h"
+#include "kernels.hpp"
+#include "tables.hpp"
+
+namespace tq {
+namespace {
+
+constexpr int64_t kAlign = 256;
+int64_t align_up(int64_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int check_params(const tq_params* p) {
+    if (!p) return TQ_EINVAL;
+    if (p->d != 64 && p->d != 128 && p->d != 256) return TQ_EINVAL;
+    if (p->b < 1 || p->b > 8) return TQ_EINVAL;
+    if (p->m < 0 || p->m % 32 != 0 || p->m > p->d) return TQ_EINVAL;
+    if (p->n_heads < 1) return TQ_EINVAL;
+    return TQ_OK;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+void layout_of(const tq_params* p, int64_t n_streams, int64_t n_tokens, tq_layout* o) {
+    const int64_t nv = n_streams * n_tokens;
+    o->idx_bytes_per_vec = (int64_t)p->d * p->b / 8;
+    o->sketch_bytes_per_vec = p->m / 8;
+    o->off_idx = 0;
+    o->off_sketch = align_up(o->off_idx + nv * o->idx_bytes_per_vec);
+    o->off_norm = align_up(o->off_sketch + nv * o->sketch_bytes_per_vec);
+    o->off_rnorm = align_up(o->off_norm + nv * 2);
+    o->total_bytes = align_up(o->off_rnorm + (p->m > 0 ? nv * 2 : 0));
+}
+
+// ---- host codebook cache (per d, b) -----------------------------------------------------------
+struct Codebook {
+    std::vector<double> thr, cent;
+};
+std::mutex g_mu;
+std::map<std::pair<int, int>, Codebook> g_codebooks;
+
+const Codebook& codebook(int d, int b) {  // caller holds g_mu
+    auto key = std::make_pair(d, b);
+    auto it = g_codebooks.find(key);
+    if (it != g_codebooks.end()) return it->second;
+    Codebook cb;
+    lloyd_max(d, b, cb.thr, cb.cent);
+    return g_codebooks.emplace(key, std::move(cb)).first->second;
+}
+
+// ---- device table cache ----------------------------------------------------------------------
+using TableKey = std::tuple<int, int, int, int, int, uint64_t>;  // device, d, b, m, n_heads, seed
+std::map<TableKey, DevTables> g_tables;
+std::map<int, int> g_num_cus;
+
+struct Blob {
+    std::vector<uint8_t> host;
+    int64_t add(const void* src, int64_t bytes) {
+        const int64_t off = align_up((int64_t)host.size());
+        host.resize(off + align_up(bytes));
+        std::memcpy(host.data() + off, src, bytes);
+        return off;
+    }
+};
+
+int build_tables(const tq_params* p, int device, DevTables* out) {  // caller holds g_mu
+    const int d = p->d, b = p->b, m = p->m, H = p->n_heads, L = 1 << b, C = d / 4;
+    const Codebook& cb = codebook(d, b);
+    std::vector<float> thr_f(L - 1), cent_f(L), cent_k(L);
+    for (int i = 0; i < L - 1; ++i) thr_f[i] = (float)cb.thr[i];
+    for (int i = 0; i < L; ++i) {
+        cent_f[i] = (float)cb.cent[i];
+        cent_k[i] = cent_f[i] * 1024.0f;
+    }
+    Grid grid;
+    if (!build_grid(thr_f, grid) || grid.G > 4096) return TQ_EUNSUPPORTED;
+    std::vector<uint32_t> gw(2 * (grid.G + 3));
+    const float inf = INFINITY;
+    std::memcpy(&gw[0], &inf, 4);  // guard cell 0 (NaN inputs land here): idx 0
+    gw[1] = 0;
+    std::memcpy(&gw[2], grid.entries.data(), grid.entries.size() * 4);
+
+    const int P = lut_group(b), NE = 1 << (P * b);
+    std::vector<float> lut32((size_t)NE * P);
+    std::vector<uint16_t> lut16((size_t)NE * P);
+    for (int f = 0; f < NE; ++f)
+        for (int k = 0; k < P; ++k) {
+            const int idx = (f >> (k * b)) & (L - 1);
+            lut32[(size_t)f * P + k] = cent_f[idx];
+            lut16[(size_t)f * P + k] = f32_to_f16_bits(cent_f[idx]);
+        }
+
+    std::vector<float> signs((size_t)H * d), signs_slot((size_t)H * d), sh;
+    std::vector<uint16_t> S((size_t)H * m * d), Sh;
+    for (int h = 0; h < H; ++h) {
+        head_signs(p->seed, h, d, sh);
+        std::memcpy(&signs[(size_t)h * d], sh.data(), d * 4);
+        for (int g = 0; g < 4; ++g)
+            for (int s = 0; s < C; ++s) {
+                const int i = (s % (d / 16)) + g * (d / 16) + (s / (d / 16)) * (d / 4);
+                signs_slot[((size_t)h * 4 + g) * C + s] = sh[i];
+            }
+        if (m > 0) {
+            gaussian_matrix_f16(p->seed, h, m, d, Sh);
+            std::memcpy(&S[(size_t)h * m * d], Sh.data(), (size_t)m * d * 2);
+        }
+    }
+
+    Blob blob;
+    const int64_t o_grid = blob.add(gw.data(), gw.size() * 4);
+    const int64_t o_cent = blob.add(cent_f.data(), L * 4);
+    const int64_t o_centk = blob.add(cent_k.data(), L * 4);
+    const int64_t o_l32 = blob.add(lut32.data(), lut32.size() * 4);
+    const int64_t o_l16 = blob.add(lut16.data(), lut16.size() * 2);
+    const int64_t o_ss = blob.add(signs_slot.data(), signs_slot.size() * 4);
+    const int64_t o_sg = blob.add(signs.data(), signs.size() * 4);
+    const int64_t o_S = m > 0 ? blob.add(S.data(), S.size() * 2) : 0;
+
+    void* dev = nullptr;
+    if (hipMalloc(&dev, blob.host.size()) != hipSuccess) return TQ_EHIP;
+    if (hipMemcpy(dev, blob.host.data(), blob.host.size(), hipMemcpyHostToDevice) != hipSuccess) {
+        (void)hipFree(dev);
+        return TQ_EHIP;
+    }
+    uint8_t* base = static_cast<uint8_t*>(dev);
+    DevTables t;
+    t.d = d; t.b = b; t.m = m; t.n_heads = H; t.seed = p->seed;
+    t.G = grid.G;
+    t.grid = reinterpret_cast<const uint32_t*>(base + o_grid);
+    t.cent = reinterpret_cast<const float*>(base + o_cent);
+    t.cent_x1024 = reinterpret_cast<const float*>(base + o_centk);
+    t.lut_f32 = reinterpret_cast<const float*>(base + o_l32);
+    t.lut_f16 = reinterpret_cast<const _Float16*>(base + o_l16);
+    t.signs_slot = reinterpret_cast<const float*>(base + o_ss);
+    t.signs = reinterpret_cast<const float*>(base + o_sg);
+    t.S = m > 0 ? reinterpret_cast<const _Float16*>(base + o_S) : nullptr;
+    t.blob = dev;
+    (void)device;
+    *out = t;
+    return TQ_OK;
+}
+
+int get_tables(const tq_params* p, DevTables* out, int* num_cus) {
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) return TQ_EHIP;
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto nc = g_num_cus.find(device);
+    if (nc == g_num_cus.end()) {
+        int cus = 0;
+        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) return TQ_EHIP;
+        nc = g_num_cus.emplace(device, cus).first;
+    }
+    *num_cus = nc->second;
+    const TableKey key{device, p->d, p->b, p->m, p->n_heads, p->seed};
+    auto it = g_tables.find(key);
+    if (it != g_tables.end()) {
+        *out = it->second;
+        return TQ_OK;
+    }
+    DevTables t;
+    const int rc = build_tables(p, device, &t);
+    if (rc != TQ_OK) return rc;
+    g_tables.emplace(key, t);
+    *out = t;
+    return TQ_OK;
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_EHIP; }
+
+// attention split geometry (shared by the workspace query and the launch)
+int64_t attn_tokens_per_split(int64_t n_tokens) {
+    int64_t tps = 1024;
+    while ((n_tokens + tps - 1) / tps > 128) tps *= 2;
+    return tps;
+}
+
+struct AttnWs {
+    int64_t o_qrot, o_p, o_part, o_ml, total, n_split;
+};
+
+AttnWs attn_ws(const tq_params* pk, int32_t batch, int32_t hq, int32_t hkv, int64_t n_tokens) {
+    AttnWs w{};
+    const int64_t rows = (int64_t)batch * hq + 16;
+    w.n_split = (n_tokens + attn_tokens_per_split(n_tokens) - 1) / attn_tokens_per_split(n_tokens);
+    if (w.n_split < 1) w.n_split = 1;
+    const int64_t streams = (int64_t)batch * hkv;
+    w.o_qrot = 0;
+    w.o_p = align_up(rows * pk->d * 2);
+    w.o_part = w.o_p + align_up(rows * (pk->m > 0 ? pk->m : 1) * 2);
+    w.o_ml = w.o_part + align_up(streams * w.n_split * 16 * pk->d * 4);
+    w.total = w.o_ml + align_up(streams * w.n_split * 16 * 2 * 4);
+    return w;
+}
+
+}  // namespace
+}  // namespace tq
+
+using namespace tq;
+
+extern "C" {
+
+const char* tq_status_string(int status) {
+    switch (status) {
+        case TQ_OK: return "ok";
+        case TQ_EINVAL: return "invalid argument";
+        case TQ_EUNSUPPORTED: return "unsupported configuration";
+        case TQ_EALIGN: return "device pointer not 16-byte aligned";
+        case TQ_EWORKSPACE: return "workspace too small";
+        case TQ_EHIP: return "HIP runtime error";
+    }
+    return "unknown status";
+}
+
+int tq_get_layout(const tq_params* p, int64_t n_streams, int64_t n_tokens, tq_layout* out) {
+    const int rc = check_params(p);
+    if (rc != TQ_OK) return rc;
+    if (!out || n_streams < 0 || n_tokens < 0) return TQ_EINVAL;
+    layout_of(p, n_streams, n_tokens, out);
+    return TQ_OK;
+}
+
+int tq_host_tables(const tq_params* p, int32_t head, double* thresholds, double* centroids, float* signs,
+                   float* S) {
+    const int rc = check_params(p);
+    if (rc != TQ_OK) return rc;
+    if (head < 0 || head >= p->n_heads) return TQ_EINVAL;
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        const Codebook& cb = codebook(p->d, p->b);
+        if (thresholds) std::memcpy(thresholds, cb.thr.data(), cb.thr.size() * 8);
+        if (centroids) std::memcpy(centroids, cb.cent.data(), cb.cent.size() * 8);
+    }
+    if (signs) {
+        std::vector<float> s;
+        head_signs(p->seed, head, p->d, s);
+        std::memcpy(signs, s.data(), p->d * 4);
+    }
+    if (S && p->m > 0) {
+        std::vector<uint16_t> h;
+        gaussian_matrix_f16(p->seed, head, p->m, p->d, h);
+        for (size_t i = 0; i < h.size(); ++i) S[i] = f16_bits_to_f32(h[i]);
+    }
+    return TQ_OK;
+}
+
+int tq_encode(const tq_params* p, const void* x, tq_dtype x_dtype, int64_t n_streams, int64_t n_tokens,
+              void* packed, void* stream) {
+    int rc = check_params(p);
+    if (rc != TQ_OK) return rc;
+    if (n_streams < 0 || n_tokens < 0) return TQ_EINVAL;
+    if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return TQ_EINVAL;
+    if (n_streams == 0 || n_tokens == 0) return TQ_OK;
+    if (!x || !packed) return TQ_EINVAL;
+    if (!aligned16(x) || !aligned16(packed)) return TQ_EALIGN;
+    DevTables t;
+    int cus = 0;
+    if ((rc = get_tables(p, &t, &cus)) != TQ_OK) return rc;
+    tq_layout lay;
+    layout_of(p, n_streams, n_tokens, &lay);
+    EncodeArgs a{};
+    a.x = x;
+    a.packed = static_cast<uint8_t*>(packed);
+    a.n_streams = n_streams;
+    a.n_tokens = n_tokens;
+    a.off_idx = lay.off_idx;
+    a.off_sketch = lay.off_sketch;
+    a.off_norm = lay.off_norm;
+    a.off_rnorm = lay.off_rnorm;
+    a.tiles_per_stream = (n_tokens + 15) / 16;
+    a.n_tiles = n_streams * a.tiles_per_stream;
+    a.t = t;
+    return hip_status(launch_encode(a, x_dtype == TQ_BF16, cus, static_cast<hipStream_t>(stream)));
+}
+
+int tq_decode(const tq_params* p, const void* packed, int64_t n_streams, int64_t n_tokens, void* x_hat,
+              tq_dtype out_dtype, void* stream) {
+    int rc = check_params(p);
+    if (rc != TQ_OK) return rc;
+    if (n_streams < 0 || n_tokens < 0) return TQ_EINVAL;
+    if (out_dtype != TQ_F32 && out_dtype != TQ_BF16) return TQ_EINVAL;
+    if (n_streams == 0 || n_tokens == 0) return TQ_OK;
+    if (!x_hat || !packed) return TQ_EINVAL;
+    if (!aligned16(x_hat) || !aligned16(packed)) return TQ_EALIGN;
+    DevTables t;
+    int cus = 0;
+    if ((rc = get_tables(p, &t, &cus)) != TQ_OK) return rc;
+    tq_layout lay;
+    layout_of(p, n_streams, n_tokens, &lay);
+    DecodeArgs a{};
+    a.packed = static_cast<const uint8_t*>(packed);
+    a.out = x_hat;
+    a.n_streams = n_streams;
+    a.n_tokens = n_tokens;
+    a.off_idx = lay.off_idx;
+    a.off_norm = lay.off_norm;
+    a.tiles_per_stream = (n_tokens + 15) / 16;
+    a.n_tiles = n_streams * a.tiles_per_stream;
+    a.t = t;
+    return hip_status(launch_decode(a, out_dtype == TQ_BF16, cus, static_cast<hipStream_t>(stream)));
+}
+
+size_t tq_scores_workspace_bytes(const tq_params* pk, int64_t n_streams, int64_t n_q) {
+    if (check_params(pk) != TQ_OK || n_streams < 0 || n_q < 0) return 0;
+    const int64_t rows = n_streams * n_q + 16;
+    return (size_t)(align_up(rows * pk->d * 2) + align_up(rows * (pk->m > 0 ? pk->m : 1) * 2));
+}
+
+int tq_qk_scores(const tq_params* pk, const void* q, tq_dtype q_dtype, int64_t n_q, const void* packed_k,
+                 int64_t n_streams, int64_t n_tokens, float* scores, void* workspace, size_t workspace_bytes,
+                 void* stream) {
+    int rc = check_params(pk);
+    if (rc != TQ_OK) return rc;
+    if (n_streams < 0 || n_tokens < 0 || n_q < 0 || n_q > 256) return TQ_EINVAL;
+    if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_EINVAL;
+    if (n_streams == 0 || n_tokens == 0 || n_q == 0) return TQ_OK;
+    if (!q || !packed_k || !scores || !workspace) return TQ_EINVAL;
+    if (!aligned16(q) || !aligned16(packed_k) || !aligned16(scores) || !aligned16(workspace)) return TQ_EALIGN;
+    if (workspace_bytes < tq_scores_workspace_bytes(pk, n_streams, n_q)) return TQ_EWORKSPACE;
+    DevTables t;
+    int cus = 0;
+    if ((rc = get_tables(pk, &t, &cus)) != TQ_OK) return rc;
+    tq_layout lay;
+    layout_of(pk, n_streams, n_tokens, &lay);
+    const int64_t rows = n_streams * n_q + 16;
+    _Float16* qrot = static_cast<_Float16*>(workspace);
+    _Float16* pp = reinterpret_cast<_Float16*>(static_cast<uint8_t*>(workspace) + align_up(rows * pk->d * 2));
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    QPrepArgs qa{};
+    qa.q = q;
+    qa.q_bf16 = q_dtype == TQ_BF16;
+    qa.n_rows = n_streams * n_q;
+    qa.n_q_per_stream = (int)n_q;
+    qa.q_rot = qrot;
+    qa.p = pp;
+    qa.t = t;
+    if ((rc = hip_status(launch_qprep(qa, s))) != TQ_OK) return rc;
+    ScoresArgs a{};
+    a.packed = static_cast<const uint8_t*>(packed_k);
+    a.q_rot = qrot;
+    a.p = pp;
+    a.scores = scores;
+    a.n_streams = n_streams;
+    a.n_tokens = n_tokens;
+    a.n_q = (int)n_q;
+    a.off_idx = lay.off_idx;
+    a.off_sketch = lay.off_sketch;
+    a.off_norm = lay.off_norm;
+    a.off_rnorm = lay.off_rnorm;
+    a.tiles_per_stream = (n_tokens + 15) / 16;
+    a.n_tiles = n_streams * a.tiles_per_stream;
+    a.t = t;
+    return hip_status(launch_scores(a, cus, s));
+}
+
+size_t tq_attention_workspace_bytes(const tq_params* pk, int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
+                                    int64_t n_tokens) {
+    if (check_params(pk) != TQ_OK || batch < 0 || n_q_heads < 0 || n_kv_heads < 1 || n_tokens < 0) return 0;
+    return (size_t)attn_ws(pk, batch, n_q_heads, n_kv_heads, n_tokens).total;
+}
+
+int tq_decode_attention(const tq_params* pk, const tq_params* pv, const void* q, tq_dtype q_dtype, int32_t batch,
+                        int32_t n_q_heads, int32_t n_kv_heads, const void* packed_k, const void* packed_v,
+                        int64_t n_tokens, float softmax_scale, void* out, tq_dtype out_dtype, void* workspace,
+                        size_t workspace_bytes, void* stream) {
+    int rc = check_params(pk);
+    if (rc != TQ_OK) return rc;
+    if ((rc = check_params(pv)) != TQ_OK) return rc;
+    if (pv->m != 0 || pk->d != pv->d) return TQ_EINVAL;
+    if (batch < 0 || n_q_heads < 1 || n_kv_heads < 1 || n_tokens < 0) return TQ_EINVAL;
+    if (n_q_heads % n_kv_heads != 0 || n_q_heads / n_kv_heads > 16) return TQ_EINVAL;
+    if (pk->n_heads != n_kv_heads || pv->n_heads != n_kv_heads) return TQ_EINVAL;
+    if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return TQ_EINVAL;
+    if (out_dtype != TQ_F32 && out_dtype != TQ_BF16) return TQ_EINVAL;
+    if (!(softmax_scale >= 0.0f) || std::isinf(softmax_scale)) return TQ_EINVAL;
+    if (batch == 0) return TQ_OK;
+    if (n_tokens == 0) return TQ_EINVAL;  // softmax over an empty cache is undefined
+    if (!q || !packed_k || !packed_v || !out || !workspace) return TQ_EINVAL;
+    if (!aligned16(q) || !aligned16(packed_k) || !aligned16(packed_v) || !aligned16(out) || !aligned16(workspace))
+        return TQ_EALIGN;
+    const AttnWs w = attn_ws(pk, batch, n_q_heads, n_kv_heads, n_tokens);
+    if (workspace_bytes < (size_t)w.total) return TQ_EWORKSPACE;
+    if (!attention_supported(pk->d, pk->b, pv->b)) return TQ_EUNSUPPORTED;
+    DevTables tk, tv;
+    int cus = 0;
+    if ((rc = get_tables(pk, &tk, &cus)) != TQ_OK) return rc;
+    if ((rc = get_tables(pv, &tv, &cus)) != TQ_OK) return rc;
+    const int64_t streams = (int64_t)batch * n_kv_heads;
+    tq_layout lk, lv;
+    layout_of(pk, streams, n_tokens, &lk);
+    layout_of(pv, streams, n_tokens, &lv);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    QPrepArgs qa{};
+    qa.q = q;
+    qa.q_bf16 = q_dtype == TQ_BF16;
+    qa.n_rows = (int64_t)batch * n_q_heads;
+    qa.n_q_per_stream = n_q_heads / n_kv_heads;
+    qa.q_rot = reinterpret_cast<_Float16*>(ws + w.o_qrot);
+    qa.p = reinterpret_cast<_Float16*>(ws + w.o_p);
+    qa.t = tk;
+    if ((rc = hip_status(launch_qprep(qa, s))) != TQ_OK) return rc;
+    AttnArgs a{};
+    a.pk = static_cast<const uint8_t*>(packed_k);
+    a.pv = static_cast<const uint8_t*>(packed_v);
+    a.q_rot = qa.q_rot;
+    a.p = qa.p;
+    a.part = reinterpret_cast<float*>(ws + w.o_part);
+    a.part_ml = reinterpret_cast<float*>(ws + w.o_ml);
+    a.out = out;
+    a.out_bf16 = out_dtype == TQ_BF16;
+    a.n_tokens = n_tokens;
+    a.batch = batch;
+    a.n_q_heads = n_q_heads;
+    a.n_kv_heads = n_kv_heads;
+    a.group = n_q_heads / n_kv_heads;
+    a.n_split = (int)w.n_split;
+    a.tokens_per_split = attn_tokens_per_split(n_tokens);
+    const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)pk->d);
+    a.scale_log2 = scale * 1.4426950408889634f;
+    a.k_off_idx = lk.off_idx;
+    a.k_off_sketch = lk.off_sketch;
+    a.k_off_norm = lk.off_norm;
+    a.k_off_rnorm = lk.off_rnorm;
+    a.v_off_idx = lv.off_idx;
+    a.v_off_norm = lv.off_norm;
+    a.tk = tk;
+    a.tv = tv;
+    bool supported = true;
+    const hipError_t e = launch_attention(a, cus, s, &supported);
+    if (!supported) return TQ_EUNSUPPORTED;
+    return hip_status(e);
+}
+
+void tq_clear_cache(void) {
+    std::lock_guard<std::mutex> lk(g_mu);
+    for (auto& kv : g_tables) (void)hipFree(kv.second.blob);
+    g_tables.clear();
+}
+
+}  // extern "C"

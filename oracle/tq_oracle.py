@@ -83,9 +83,10 @@ def head_signs(seed: int, head: int, d: int) -> np.ndarray:
 
 
 def gaussian_matrix(seed: int, head: int, m: int, d: int) -> np.ndarray:
-    """QJL projection S (m x d), i.i.d. N(0,1) rounded to fp32, row-major element e uses words
-    2e and 2e+1: u1 = (w>>11 + 1)·2^-53 in (0,1], u2 = (w>>11)·2^-53 in [0,1),
-    g = sqrt(-2 ln u1)·cos(2·pi·u2) in fp64 via libm (Python math) [BM], then fp32 round-to-nearest."""
+    """QJL projection S (m x d), i.i.d. N(0,1) rounded to fp16 (round-to-nearest-even; |g| < 8.6
+    always fits), row-major element e uses words 2e and 2e+1: u1 = (w>>11 + 1)·2^-53 in (0,1],
+    u2 = (w>>11)·2^-53 in [0,1), g = sqrt(-2 ln u1)·cos(2·pi·u2) in fp64 via libm (Python math) [BM].
+    The pages fix only "Gaussian"; fp16 entries make S exactly representable in half precision."""
     n = m * d
     w = words(stream_key(seed, TAG_GAUSS, head), 2 * n)
     a = (w[0::2] >> np.uint64(11)).tolist()
@@ -97,7 +98,7 @@ def gaussian_matrix(seed: int, head: int, m: int, d: int) -> np.ndarray:
         u1 = (a[k] + 1) * sc
         u2 = c[k] * sc
         out[k] = math.sqrt(-2.0 * math.log(u1)) * math.cos(two_pi * u2)
-    return out.astype(np.float32).reshape(m, d)
+    return out.astype(np.float16).reshape(m, d)
 
 
 # ----------------------------------------------------------------------------------------------
@@ -147,7 +148,7 @@ def lloyd_max(d: int, b: int, tol: float = 1e-16, max_iter: int = 2_000_000):
 
     Iteration (Lloyd): thresholds at midpoints of neighbouring centroids, centroids at the
     conditional mean of their cell, started from the quantiles F^-1((i+1/2)/L), until the largest
-    centroid change is <= tol (or stops decreasing).  The density is log-concave, so the fixed
+    centroid change is <= tol (or has stopped reaching new lows at rounding level).  The density is log-concave, so the fixed
     point is unique."""
     if d < 2:
         raise ValueError("d must be >= 2")
@@ -159,15 +160,21 @@ def lloyd_max(d: int, b: int, tol: float = 1e-16, max_iter: int = 2_000_000):
     # quantile start, positive half: F(x) = (K + k + 1/2)/L  <=>  sf(x) = (K - k - 1/2)/L
     p_up = (K - np.arange(K) - 0.5) / L
     c = 1.0 - 2.0 * special.betaincinv(a, a, p_up)
-    prev = np.inf
+    best, since_best = np.inf, 0
     for _ in range(max_iter):
         t = np.concatenate(([0.0], 0.5 * (c[:-1] + c[1:]), [1.0]))
         c_new = first_moment(t[:-1], t[1:], d) / upper_mass(t[:-1], t[1:], d)
         delta = float(np.max(np.abs(c_new - c)))
         c = c_new
-        if delta <= tol or (delta >= prev and delta < 1e-13):
+        if delta <= tol:
             break
-        prev = delta
+        # Lloyd contracts slowly for many levels: keep going while the step still reaches new lows
+        if delta < best:
+            best, since_best = delta, 0
+        else:
+            since_best += 1
+            if since_best > 2000 and delta < 1e-12:
+                break
     t_inner = 0.5 * (c[:-1] + c[1:])
     thresholds = np.concatenate((-t_inner[::-1], [0.0], t_inner))
     centroids = np.concatenate((-c[::-1], c))

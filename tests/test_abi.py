@@ -1,0 +1,123 @@
+"""C-ABI checks that need no GPU: the library loads, exports every symbol include/tq.h declares,
+computes the packed layout and host tables exactly like the oracle, and rejects bad arguments
+before touching the device."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import tq_oracle as O
+from tests.conftest import ROOT
+
+T = pytest.importorskip("kv_cache_transform_amd")
+from kv_cache_transform_amd import _lib  # noqa: E402
+
+
+def _lib_or_skip():
+    if not os.path.exists(_lib.LIB_PATH):
+        pytest.fail("libtq.so is not built (run python -m kv_cache_transform_amd.build)")
+    return _lib.lib()
+
+
+def test_exports_every_declared_symbol():
+    L = _lib_or_skip()
+    header = open(os.path.join(ROOT, "include", "tq.h")).read()
+    declared = set(re.findall(r"\b(tq_[a-z_]+)\s*\(", header))
+    assert declared == set(_lib.EXPORTS)
+    for name in declared:
+        assert hasattr(L, name), name
+
+
+@pytest.mark.parametrize("d,b,m", [(64, 4, 0), (128, 3, 128), (128, 4, 32), (256, 6, 256), (256, 1, 64)])
+def test_layout_matches_oracle(d, b, m):
+    _lib_or_skip()
+    for S, N in ((1, 1), (3, 1000), (32, 32768), (0, 5)):
+        got = T.get_layout(T.Codec(d, b, m, 1, 0), S, N)
+        assert got == O.layout(d, b, m, S, N)
+
+
+@pytest.mark.parametrize("d", [64, 128, 256])
+@pytest.mark.parametrize("b", [1, 2, 3, 4, 5, 6])
+def test_host_codebook_matches_oracle(d, b):
+    _lib_or_skip()
+    h = T.host_tables(T.Codec(d, b, 0, 1, 7))
+    t, c = O.lloyd_max(d, b)
+    assert np.max(np.abs(h["centroids"] - c) / np.abs(c)) < 1e-11
+    assert np.max(np.abs(h["thresholds"] - t)) < 1e-12
+    # fp32 device thresholds: at most a handful may round differently (values within 1e-11 of an
+    # fp32 midpoint); count them
+    diff = np.sum(h["thresholds"].astype(np.float32) != t.astype(np.float32))
+    assert diff <= 1
+
+
+@pytest.mark.parametrize("seed,head,d,m", [(4001, 0, 128, 128), (4001, 7, 128, 128), (5001, 3, 256, 256),
+                                         (2**63 + 11, 2, 64, 32)])
+def test_host_signs_and_S_match_oracle_exactly(seed, head, d, m):
+    _lib_or_skip()
+    h = T.host_tables(T.Codec(d, 2, m, head + 1, seed), head)
+    assert np.array_equal(h["signs"], O.head_signs(seed, head, d).astype(np.float32))
+    assert np.array_equal(h["S"], O.gaussian_matrix(seed, head, m, d).astype(np.float32))
+
+
+def test_status_strings():
+    _lib_or_skip()
+    for s in (0, -1, -2, -3, -4, -5):
+        assert _lib.status_string(s)
+    assert _lib.status_string(-99) == "unknown status"
+
+
+def _p(d=128, b=4, m=0, H=1, seed=0):
+    return ctypes.byref(_lib.Params(d, b, m, H, seed))
+
+
+def test_argument_validation_before_any_gpu_call():
+    L = _lib_or_skip()
+    lay = _lib.Layout()
+    bad = [(_p(d=96), "d"), (_p(d=32), "d"), (_p(b=0), "b"), (_p(b=9), "b"), (_p(m=48), "m%32"),
+           (_p(m=256, d=128), "m>d"), (_p(H=0), "n_heads")]
+    for p, why in bad:
+        assert L.tq_get_layout(p, 1, 1, ctypes.byref(lay)) == _lib.TQ_EINVAL, why
+        assert L.tq_encode(p, ctypes.c_void_p(16), 1, 1, 1, ctypes.c_void_p(16), None) == _lib.TQ_EINVAL, why
+    p = _p()
+    assert L.tq_get_layout(None, 1, 1, ctypes.byref(lay)) == _lib.TQ_EINVAL
+    assert L.tq_get_layout(p, -1, 1, ctypes.byref(lay)) == _lib.TQ_EINVAL
+    # null pointers, bad dtype, misaligned pointers: rejected on the host
+    assert L.tq_encode(p, None, 1, 2, 2, ctypes.c_void_p(16), None) == _lib.TQ_EINVAL
+    assert L.tq_encode(p, ctypes.c_void_p(16), 7, 2, 2, ctypes.c_void_p(16), None) == _lib.TQ_EINVAL
+    assert L.tq_encode(p, ctypes.c_void_p(18), 1, 2, 2, ctypes.c_void_p(16), None) == _lib.TQ_EALIGN
+    assert L.tq_decode(p, ctypes.c_void_p(16), 2, 2, ctypes.c_void_p(20), 0, None) == _lib.TQ_EALIGN
+    # empty inputs are a valid no-op
+    assert L.tq_encode(p, None, 1, 0, 5, None, None) == _lib.TQ_OK
+    assert L.tq_decode(p, None, 3, 0, None, 0, None) == _lib.TQ_OK
+    # scores: workspace too small, too many queries
+    pk = _p(m=128)
+    ws = L.tq_scores_workspace_bytes(pk, 2, 32)
+    assert ws > 0
+    v = ctypes.c_void_p(256)
+    assert L.tq_qk_scores(pk, v, 1, 32, v, 2, 10, v, v, ws - 1, None) == _lib.TQ_EWORKSPACE
+    assert L.tq_qk_scores(pk, v, 1, 257, v, 2, 10, v, v, ws, None) == _lib.TQ_EINVAL
+    # attention cross-argument rules
+    pv = _p(m=0, H=8)
+    pk8 = _p(m=128, H=8)
+    wsa = L.tq_attention_workspace_bytes(pk8, 2, 32, 8, 1000)
+    call = lambda pk_, pv_, hq, hkv, n, scale=0.0, wsb=wsa: L.tq_decode_attention(
+        pk_, pv_, v, 1, 2, hq, hkv, v, v, n, ctypes.c_float(scale), v, 1, v, wsb, None)
+    assert call(pk8, _p(m=128, H=8), 32, 8, 1000) == _lib.TQ_EINVAL   # QJL on V
+    assert call(pk8, _p(d=64, H=8), 32, 8, 1000) == _lib.TQ_EINVAL    # d mismatch
+    assert call(pk8, pv, 30, 8, 1000) == _lib.TQ_EINVAL               # heads not divisible
+    assert call(pk8, pv, 32 * 17, 32, 1000) == _lib.TQ_EINVAL         # group > 16 (and n_heads)
+    assert call(pk8, _p(H=4), 32, 8, 1000) == _lib.TQ_EINVAL          # n_heads != n_kv_heads
+    assert call(pk8, pv, 32, 8, 0) == _lib.TQ_EINVAL                  # empty cache
+    assert call(pk8, pv, 32, 8, 1000, scale=-1.0) == _lib.TQ_EINVAL
+    assert call(pk8, pv, 32, 8, 1000, wsb=wsa - 1) == _lib.TQ_EWORKSPACE
+
+
+def test_product_package_does_not_import_the_oracle():
+    pkg = os.path.join(ROOT, "kv_cache_transform_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for f in files:
+            if f.endswith((".py", ".cpp", ".hip", ".hpp", ".h")):
+                txt = open(os.path.join(dirpath, f)).read()
+                assert "oracle" not in txt.replace("no oracle", ""), f

@@ -1,0 +1,208 @@
+"""GPU parity of the HIP path (through the C ABI) against the oracle, on seeded synthetic inputs
+shaped like the five workloads, at sizes the oracle finishes in seconds (several tiles plus a ragged
+tail), and edge cases.  Full-size runs live in test_gpu_fullsize.py."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_transform_amd as T
+from oracle import tq_oracle as O
+from synth import inputs as I
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    T._lib.lib()            # fail loudly if libtq.so is missing
+    yield
+
+
+def _enc(codec, x):
+    buf = T.encode(codec, x)
+    torch.cuda.synchronize()
+    return buf.cpu().numpy()
+
+
+def _x64(x):
+    if x.dtype == torch.bfloat16:
+        return O.bf16_bits_to_f64(I.bf16_bits(x))
+    return x.detach().cpu().numpy().astype(np.float64)
+
+
+# ---------------------------------------------------------------------------------------------
+# encode / decode over the parameter space
+MATRIX = ([(d, b, 0, torch.bfloat16) for d in (64, 128, 256) for b in range(1, 7)]
+          + [(128, b, 0, torch.bfloat16) for b in (7, 8)]
+          + [(d, b, m, torch.bfloat16) for d in (64, 128, 256) for b in (2, 3, 4) for m in (32, d)]
+          + [(d, 4, 0, torch.float32) for d in (64, 128, 256)] + [(64, 3, 64, torch.float32)])
+
+
+@pytest.mark.parametrize("d,b,m,dt", MATRIX)
+def test_encode_decode_parity(d, b, m, dt):
+    S, N, H, seed = 3, 37, 2, 900 + d + b + m
+    codec = T.Codec(d, b, m, H, seed)
+    x = I.gaussian((S, N, d), seed, device=DEV, dtype=dt)
+    buf = _enc(codec, x)
+    tb = P.Tables(d, b, m, H, seed)
+    st = P.check_encode(tb, _x64(x), buf)
+    recs = st["recs"]
+    xh = T.decode(codec, torch.as_tensor(buf, device=DEV), S, N, torch.float32).cpu().numpy()
+    P.check_decode_f32(tb, recs, list(range(S)), xh)
+    xb = T.decode(codec, torch.as_tensor(buf, device=DEV), S, N, torch.bfloat16)
+    P.check_decode_bf16(tb, recs, list(range(S)), O.bf16_bits_to_f64(I.bf16_bits(xb)))
+
+
+def test_cfg1_full_round_trip_and_determinism():
+    """Single head, d=64, 4096 fp32 keys with per-channel std U[0.5,2]; b=4, no QJL."""
+    w = I.CONFIGS["cfg1"]
+    codec = T.Codec(w.d, w.b, 0, 1, w.seed_k)
+    xh = I.per_channel_gaussian(4096, 64, 1)[None]
+    x = torch.as_tensor(xh, device=DEV)
+    buf = _enc(codec, x)
+    assert np.array_equal(buf, _enc(codec, x)), "encode is not deterministic"
+    tb = P.Tables(w.d, w.b, 0, 1, w.seed_k)
+    st = P.check_encode(tb, xh.astype(np.float64), buf)
+    print(f"cfg1: flagged={st['flagged']} idx_mismatch={st['idx_mismatch']} n16_1ulp={st['n16_1ulp']}")
+    out = T.decode(codec, torch.as_tensor(buf, device=DEV), 1, 4096, torch.float32).cpu().numpy()
+    err = P.check_decode_f32(tb, st["recs"], [0], out)
+    print(f"cfg1: decode rel L2 vs oracle {err:.2e}")
+
+
+def test_cfg2_reduced_outliers():
+    w = I.CONFIGS["cfg2"]
+    S, N = 4, 1000
+    for seed in (w.seed_k, w.seed_v):
+        codec = T.Codec(128, 4, 0, S, seed)
+        x = I.outlier_gaussian(S, N, 128, 4, 10.0, seed, device=DEV)
+        buf = _enc(codec, x)
+        tb = P.Tables(128, 4, 0, S, seed)
+        st = P.check_encode(tb, _x64(x), buf)
+        out = T.decode(codec, torch.as_tensor(buf, device=DEV), S, N, torch.float32).cpu().numpy()
+        P.check_decode_f32(tb, st["recs"], list(range(S)), out)
+
+
+@pytest.mark.parametrize("b,m,nq", [(3, 128, 32), (4, 0, 20), (2, 64, 7)])
+def test_cfg3_reduced_scores(b, m, nq):
+    S, N, seed = 2, 3000, 3001
+    codec = T.Codec(128, b, m, S, seed)
+    k = I.gaussian((S, N, 128), seed, device=DEV)
+    q = I.gaussian((S, nq, 128), seed + 17, device=DEV)
+    buf = _enc(codec, k)
+    tb = P.Tables(128, b, m, S, seed)
+    st = P.check_encode(tb, _x64(k), buf)
+    sc = T.qk_scores(codec, q, torch.as_tensor(buf, device=DEV), N).cpu().numpy()
+    worst = P.check_scores(tb, st["recs"], list(range(S)), _x64(q), sc)
+    print(f"scores b={b} m={m}: worst row rel L2 {worst:.2e}")
+
+
+def _attention_case(batch, hq, hkv, N, d, b, m, out_dtype, seed=4001, scale=0.0):
+    ck, cv = T.Codec(d, b, m, hkv, seed), T.Codec(d, b, 0, hkv, seed + 1)
+    K = I.rope_gaussian(batch * hkv, N, d, seed, device=DEV)
+    V = I.rope_gaussian(batch * hkv, N, d, seed + 1, device=DEV)
+    q = I.cfg4_queries(batch, hq, d, N, seed + 2, device=DEV)
+    pk, pv = T.encode(ck, K), T.encode(cv, V)
+    out = T.decode_attention(ck, cv, q, pk, pv, hkv, N, scale, out_dtype=out_dtype)
+    torch.cuda.synchronize()
+    tk, tv = P.Tables(d, b, m, hkv, seed), P.Tables(d, b, 0, hkv, seed + 1)
+    rk = O.unpack_tensor(pk.cpu().numpy(), d, b, m, batch * hkv, N)
+    rv = O.unpack_tensor(pv.cpu().numpy(), d, b, 0, batch * hkv, N)
+    q64 = _x64(q)
+    sc = scale if scale > 0 else 1.0 / math.sqrt(d)
+    g = hq // hkv
+    ref = np.zeros((batch, hq, d))
+    for bi in range(batch):
+        for h in range(hq):
+            st = bi * hkv + h // g
+            ref[bi, h] = P.oracle_attention_row(tk, tv, rk[st], rv[st], st, q64[bi, h], sc)
+    got = out.float().cpu().numpy().astype(np.float64)
+    return P.rel_l2(got, ref), max(P.rel_l2(got[bi, h], ref[bi, h]) for bi in range(batch) for h in range(hq))
+
+
+@pytest.mark.parametrize("batch,hq,hkv,N,d,b,m", [
+    (2, 8, 2, 5000, 128, 4, 128),      # cfg4 shape, reduced; several splits + ragged tail
+    (1, 4, 4, 777, 128, 4, 0),         # MHA, no QJL
+    (2, 16, 1, 2100, 64, 4, 64),       # d=64, 16 queries per kv head
+    (1, 6, 2, 1500, 256, 3, 256),      # d=256, b=3
+    (1, 2, 1, 33, 128, 2, 32),         # tiny cache
+])
+def test_decode_attention_reduced(batch, hq, hkv, N, d, b, m):
+    e32, row32 = _attention_case(batch, hq, hkv, N, d, b, m, torch.float32)
+    eb, rowb = _attention_case(batch, hq, hkv, N, d, b, m, torch.bfloat16)
+    print(f"attention {batch}x{hq}/{hkv} N={N} d={d} b={b} m={m}: rel L2 f32 {e32:.2e} (row max {row32:.2e}),"
+          f" bf16 {eb:.2e} (row max {rowb:.2e})")
+    assert e32 <= 2e-3 and eb <= 2e-3
+
+
+def test_decode_attention_explicit_scale():
+    e, _ = _attention_case(1, 4, 2, 900, 128, 4, 128, torch.float32, scale=0.05)
+    assert e <= 2e-3
+
+
+@pytest.mark.parametrize("b", [2, 3, 5, 6])
+@pytest.mark.parametrize("m", [0, 256])
+def test_cfg5_reduced_heavy_tail(b, m):
+    S, N, nq, seed = 2, 1200, 8, 5001
+    codec = T.Codec(256, b, m, S, seed + b)
+    k = I.student_t(S, N, 256, 3, seed, device=DEV)
+    q = I.gaussian((S, nq, 256), seed + 99, device=DEV)
+    buf = _enc(codec, k)
+    tb = P.Tables(256, b, m, S, seed + b)
+    st = P.check_encode(tb, _x64(k), buf)
+    out = T.decode(codec, torch.as_tensor(buf, device=DEV), S, N, torch.float32).cpu().numpy()
+    P.check_decode_f32(tb, st["recs"], list(range(S)), out)
+    sc = T.qk_scores(codec, q, torch.as_tensor(buf, device=DEV), N).cpu().numpy()
+    P.check_scores(tb, st["recs"], list(range(S)), _x64(q), sc)
+
+
+# ---------------------------------------------------------------------------------------------
+# edge cases
+def test_zero_vectors_and_single_token():
+    d, b = 128, 4
+    codec = T.Codec(d, b, 128, 1, 3)
+    x = torch.zeros(1, 1, d, dtype=torch.bfloat16, device=DEV)
+    buf = _enc(codec, x)
+    r = O.unpack_tensor(buf, d, b, 128, 1, 1)[0]
+    assert np.all(r["idx"] == 8) and r["n16"][0] == 0 and r["r16"][0] >= 0
+    out = T.decode(codec, torch.as_tensor(buf, device=DEV), 1, 1).cpu().numpy()
+    assert np.all(out == 0)
+
+
+def test_norm_above_fp16_range_is_inf():
+    d = 64
+    codec = T.Codec(d, 3, 0, 1, 5)
+    x = torch.full((1, 2, d), 1.0e4, dtype=torch.float32, device=DEV)   # norm 8e4 > 65504
+    buf = _enc(codec, x)
+    r = O.unpack_tensor(buf, d, 3, 0, 1, 2)[0]
+    assert np.all(np.isinf(r["n16"]))
+
+
+def test_empty_inputs_are_noops():
+    codec = T.Codec(128, 4, 0, 1, 0)
+    x = torch.zeros(0, 5, 128, dtype=torch.bfloat16, device=DEV)
+    T.encode(codec, x)
+    torch.cuda.synchronize()
+
+
+def test_misaligned_pointer_rejected():
+    codec = T.Codec(64, 4, 0, 1, 0)
+    x = torch.zeros(2 * 64 * 2 + 8, dtype=torch.bfloat16, device=DEV)
+    xm = x[1:1 + 2 * 64].view(1, 2, 64)        # 2-byte offset
+    with pytest.raises(T.TQError) as ei:
+        T.encode(codec, xm)
+    assert ei.value.status == T._lib.TQ_EALIGN
+
+
+def test_unsupported_attention_combination():
+    ck, cv = T.Codec(128, 4, 128, 2, 1), T.Codec(128, 2, 0, 2, 2)
+    q = torch.zeros(1, 4, 128, dtype=torch.bfloat16, device=DEV)
+    pk = torch.zeros(T.get_layout(ck, 2, 64)["total_bytes"], dtype=torch.uint8, device=DEV)
+    pv = torch.zeros(T.get_layout(cv, 2, 64)["total_bytes"], dtype=torch.uint8, device=DEV)
+    with pytest.raises(T.TQError) as ei:
+        T.decode_attention(ck, cv, q, pk, pv, 2, 64)
+    assert ei.value.status == T._lib.TQ_EUNSUPPORTED

@@ -54,9 +54,9 @@ def test_gaussian_moments_and_ks():
     assert g.dtype == np.float64
 
 
-def test_gaussian_is_fp32_and_prefix_stable():
+def test_gaussian_is_fp16_and_prefix_stable():
     a = O.gaussian_matrix(5, 2, 32, 64)
-    assert a.dtype == np.float32
+    assert a.dtype == np.float16
     b = O.gaussian_matrix(5, 2, 64, 64)
     # row-major counter: the first 32 rows of an m=64 table equal the m=32 table
     assert np.array_equal(a, b[:32])
@@ -67,5 +67,5 @@ def test_box_muller_first_element_by_hand():
     w0, w1 = O.words(key, 2).tolist()
     u1 = ((w0 >> 11) + 1) * 2.0 ** -53
     u2 = (w1 >> 11) * 2.0 ** -53
-    g = np.float32(math.sqrt(-2 * math.log(u1)) * math.cos(2 * math.pi * u2))
+    g = np.float16(math.sqrt(-2 * math.log(u1)) * math.cos(2 * math.pi * u2))
     assert O.gaussian_matrix(77, 0, 1, 1)[0, 0] == g
