@@ -27,15 +27,96 @@ __device__ __forceinline__ float max4(float t) {
     return fmaxf(a, b);
 }
 
+// Everything one 32-token chunk needs, loaded with wide per-lane loads.  Lane (l16, g):
+//   kw[T]  packed K chunk g of token 16T + l16 (score A operand rows)
+//   ks[T]  its sketch bytes [g·m/32, (g+1)·m/32)
+//   kn/kr/vn[T]  the 4 fp16 norms of tokens 16T + 4g + {0..3} (the rows its score outputs hold)
+//   vw[r]  packed V bytes of coordinates [NT·l16, NT·l16 + NT) of token τ(g, r), where
+//          τ(g, r) = 4g + r for r < 4 and 16 + 4g + (r - 4) otherwise
+template <int NWK, int NWV>
+struct AttnChunk {
+    uint32_t kw[2][NWK];
+    uint32_t ks[2][2];
+    u32x2 kn[2], kr[2], vn[2];
+    uint32_t vw[8][NWV];
+};
+
+__device__ __forceinline__ int64_t tau_tok(int g, int r) { return r < 4 ? 4 * g + r : 16 + 4 * g + (r - 4); }
+
+template <int D, int BK, int BV, bool QJL, int NWK, int NWV>
+__device__ __forceinline__ void attn_load(AttnChunk<NWK, NWV>& c, int64_t t0, int64_t t_end, int l16, int g, int m,
+                                          const uint8_t* kidx, const uint8_t* ksk, const _Float16* kn,
+                                          const _Float16* kr, const uint8_t* vidx, const _Float16* vn) {
+    constexpr int C = D / 4;
+    constexpr int CBK = C * BK / 8, CAK = cmin(pow2_align(CBK), 16);
+    constexpr int NT = D / 16, VB = NT * BV / 8, VA = cmin(pow2_align(VB), 16);
+    const bool full = t0 + 32 <= t_end;
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+        const int64_t tk = t0 + 16 * T + l16;
+        if (full || tk < t_end) {
+            load_bytes<CBK, CAK>(kidx + tk * (D * BK / 8) + g * CBK, c.kw[T]);
+            if constexpr (QJL) {
+                const uint8_t* sp = ksk + tk * (m / 8) + g * (m / 32);
+                if ((m & 127) == 0) {
+                    c.ks[T][0] = *reinterpret_cast<const uint32_t*>(sp);
+                    c.ks[T][1] = m == 256 ? *reinterpret_cast<const uint32_t*>(sp + 4) : 0u;
+                } else {
+                    uint32_t w0 = 0, w1 = 0;
+                    for (int q = 0; q < (m >> 5); ++q) {
+                        if (q < 4) w0 |= uint32_t(sp[q]) << (8 * q);
+                        else w1 |= uint32_t(sp[q]) << (8 * (q - 4));
+                    }
+                    c.ks[T][0] = w0;
+                    c.ks[T][1] = w1;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int k = 0; k < NWK; ++k) c.kw[T][k] = 0u;
+            c.ks[T][0] = c.ks[T][1] = 0u;
+        }
+        const int64_t tn = t0 + 16 * T + 4 * g;   // 4 consecutive tokens, 8-byte aligned
+        if (full || tn + 4 <= t_end) {
+            c.kn[T] = *reinterpret_cast<const u32x2*>(kn + tn);
+            if constexpr (QJL) c.kr[T] = *reinterpret_cast<const u32x2*>(kr + tn);
+            c.vn[T] = *reinterpret_cast<const u32x2*>(vn + tn);
+        } else {
+            uint32_t a[4] = {0, 0, 0, 0}, b[4] = {0, 0, 0, 0}, e[4] = {0, 0, 0, 0};
+            for (int i = 0; i < 4; ++i)
+                if (tn + i < t_end) {
+                    a[i] = *reinterpret_cast<const uint16_t*>(kn + tn + i);
+                    if constexpr (QJL) b[i] = *reinterpret_cast<const uint16_t*>(kr + tn + i);
+                    e[i] = *reinterpret_cast<const uint16_t*>(vn + tn + i);
+                }
+            c.kn[T] = u32x2{a[0] | (a[1] << 16), a[2] | (a[3] << 16)};
+            c.kr[T] = u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
+            c.vn[T] = u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const int64_t tt = t0 + tau_tok(g, r);
+        if (full || tt < t_end) load_bytes<VB, VA>(vidx + tt * (D * BV / 8) + l16 * VB, c.vw[r]);
+        else {
+#pragma unroll
+            for (int k = 0; k < NWV; ++k) c.vw[r][k] = 0u;
+        }
+    }
+}
+
+__device__ __forceinline__ float half_of(const u32x2& v, int i) {
+    const uint32_t w = v[i >> 1];
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)((i & 1) ? (w >> 16) : (w & 0xffffu)));
+}
+
 template <int D, int BK, int BV, bool QJL>
 __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     constexpr int C = D / 4;
     constexpr int KS = C / 8;                       // k-steps over d
     constexpr int PK = lut_group_c(BK), NEK = 1 << (PK * BK);
-    constexpr int NWK = (C * BK + 31) / 32, CBK = C * BK / 8, CAK = cmin(pow2_align(CBK), 16);
+    constexpr int NWK = (C * BK + 31) / 32;
     constexpr int NT = D / 16;                      // value tiles (16 coordinates each)
-    constexpr int VB = NT * BV / 8;                 // packed value bytes per lane and token
-    constexpr int VA = cmin(pow2_align(VB), 16);
     constexpr int NWV = (NT * BV + 31) / 32;
     constexpr int LV = 1 << BV;
 
@@ -91,30 +172,28 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
     const uint8_t* vidx = a.pv + a.v_off_idx + st * a.n_tokens * (int64_t)(D * BV / 8);
     const _Float16* vn = reinterpret_cast<const _Float16*>(a.pv + a.v_off_norm) + st * a.n_tokens;
 
+    AttnChunk<NWK, NWV> nxt;
+    attn_load<D, BK, BV, QJL>(nxt, t_begin, t_end, l16, g, m, kidx, ksk, kn, kr, vidx, vn);
+#pragma unroll 1
     for (int64_t t0 = t_begin; t0 < t_end; t0 += 32) {
+        const AttnChunk<NWK, NWV> cur = nxt;
+        if (t0 + 32 < t_end)   // issue the next chunk's loads before computing this one
+            attn_load<D, BK, BV, QJL>(nxt, t0 + 32, t_end, l16, g, m, kidx, ksk, kn, kr, vidx, vn);
+        const bool full = t0 + 32 <= t_end;
         // ---- scores for the two 16-token tiles ----------------------------------------------
         float lg[8];
 #pragma unroll
         for (int T = 0; T < 2; ++T) {
-            const int64_t tk = t0 + 16 * T + l16;             // A-operand row token of this lane
-            const bool kval = tk < t_end;
-            uint32_t w[NWK];
-            if (kval) load_bytes<CBK, CAK>(kidx + tk * (D * BK / 8) + g * CBK, w);
-            else {
-#pragma unroll
-                for (int k = 0; k < NWK; ++k) w[k] = 0u;
-            }
             half8 ka[KS];
-            // dequantise (same grouping as the score kernel)
 #pragma unroll
             for (int k = 0; k < KS; ++k) {
                 if constexpr (PK == 8) {
-                    const uint32_t f = get_bits<8 * BK>(w, (8 * k) * BK);
+                    const uint32_t f = get_bits<8 * BK>(cur.kw[T], (8 * k) * BK);
                     ka[k] = *reinterpret_cast<const half8*>(klut + f * 8);
                 } else if constexpr (PK == 4) {
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
-                        const uint32_t f = get_bits<4 * BK>(w, (8 * k + 4 * h) * BK);
+                        const uint32_t f = get_bits<4 * BK>(cur.kw[T], (8 * k + 4 * h) * BK);
                         const half4 e = *reinterpret_cast<const half4*>(klut + f * 4);
                         ka[k][4 * h + 0] = e[0]; ka[k][4 * h + 1] = e[1];
                         ka[k][4 * h + 2] = e[2]; ka[k][4 * h + 3] = e[3];
@@ -122,14 +201,14 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
                 } else if constexpr (PK == 2) {
 #pragma unroll
                     for (int h = 0; h < 4; ++h) {
-                        const uint32_t f = get_bits<2 * BK>(w, (8 * k + 2 * h) * BK);
+                        const uint32_t f = get_bits<2 * BK>(cur.kw[T], (8 * k + 2 * h) * BK);
                         const half2v e = *reinterpret_cast<const half2v*>(klut + f * 2);
                         ka[k][2 * h] = e[0];
                         ka[k][2 * h + 1] = e[1];
                     }
                 } else {
 #pragma unroll
-                    for (int h = 0; h < 8; ++h) ka[k][h] = klut[get_bits<BK>(w, (8 * k + h) * BK)];
+                    for (int h = 0; h < 8; ++h) ka[k][h] = klut[get_bits<BK>(cur.kw[T], (8 * k + h) * BK)];
                 }
             }
             floatx4 s1 = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -137,11 +216,10 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
             for (int k = 0; k < KS; ++k) s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[k], qb[k], s1, 0, 0, 0);
             floatx4 s2 = {0.0f, 0.0f, 0.0f, 0.0f};
             if constexpr (QJL) {
-                const uint8_t* sp = ksk + tk * (m / 8) + g * (m / 32);
 #pragma unroll
                 for (int k = 0; k < KS; ++k) {
                     if (k < mks) {
-                        const uint32_t byte = kval ? sp[k] : 0u;
+                        const uint32_t byte = (cur.ks[T][k >> 2] >> (8 * (k & 3))) & 0xffu;
                         const half8 sa = *reinterpret_cast<const half8*>(sgn + byte * 8);
                         s2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(sa, pb[k], s2, 0, 0, 0);
                     }
@@ -150,14 +228,10 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
             // output lane (q = l16, g) holds tokens t0 + 16T + 4g + i
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int64_t tt = t0 + 16 * T + 4 * g + i;
-                float v = -INFINITY;
-                if (tt < t_end) {
-                    const float n16 = (float)kn[tt];
-                    float sc = s1[i];
-                    if constexpr (QJL) sc = fmaf(lam * (float)kr[tt], s2[i], sc);
-                    v = n16 * sc * a.scale_log2;
-                }
+                float sc = s1[i];
+                if constexpr (QJL) sc = fmaf(lam * half_of(cur.kr[T], i), s2[i], sc);
+                float v = half_of(cur.kn[T], i) * sc * a.scale_log2;
+                if (!full && t0 + 16 * T + 4 * g + i >= t_end) v = -INFINITY;
                 lg[4 * T + i] = v;
             }
         }
@@ -173,32 +247,20 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         half8 wb;
 #pragma unroll
         for (int r = 0; r < 8; ++r) {
-            const int64_t tt = t0 + (r < 4 ? 4 * g + r : 16 + 4 * g + (r - 4));
             const float w = exp2f(lg[r] - m_new);
             const _Float16 wh = (_Float16)w;
             wsum += (float)wh;
-            const float nv = tt < t_end ? (float)vn[tt] : 0.0f;
-            wb[r] = (_Float16)((float)wh * nv);
+            wb[r] = (_Float16)((float)wh * half_of(cur.vn[r >> 2], r & 3));
         }
         l_run = l_run * alpha + wsum;
 #pragma unroll
         for (int n = 0; n < NT; ++n) oacc[n] *= alpha;
         // ---- values: A = V̂^T tile n (row = coordinate NT*l16 + n), 8 tokens of k-block g ---------
-        uint32_t vw[8][NWV];
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int64_t tt = t0 + (r < 4 ? 4 * g + r : 16 + 4 * g + (r - 4));
-            if (tt < t_end) load_bytes<VB, VA>(vidx + tt * (D * BV / 8) + l16 * VB, vw[r]);
-            else {
-#pragma unroll
-                for (int k = 0; k < NWV; ++k) vw[r][k] = 0u;
-            }
-        }
 #pragma unroll
         for (int n = 0; n < NT; ++n) {
             half8 va;
 #pragma unroll
-            for (int r = 0; r < 8; ++r) va[r] = vlut[get_bits<BV>(vw[r], n * BV)];
+            for (int r = 0; r < 8; ++r) va[r] = vlut[get_bits<BV>(cur.vw[r], n * BV)];
             oacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, wb, oacc[n], 0, 0, 0);
         }
     }
