@@ -29,6 +29,8 @@ struct EncodeArgs {
     int64_t tiles_per_stream;  // ceil(n_tokens / 16)
     int64_t n_tiles;           // n_streams * tiles_per_stream
     int64_t tiles_per_wave;
+    int64_t blocks_per_stream; // grid = n_streams * blocks_per_stream
+    int64_t tiles_per_block;
     DevTables t;
 };
 
