@@ -33,34 +33,56 @@ __device__ __forceinline__ float max4(float t) {
 //   kn/kr/vn[T]  the 4 fp16 norms of tokens 16T + 4g + {0..3} (the rows its score outputs hold)
 //   vw[r]  packed V bytes of coordinates [NT·l16, NT·l16 + NT) of token τ(g, r), where
 //          τ(g, r) = 4g + r for r < 4 and 16 + 4g + (r - 4) otherwise
-template <int NWK, int NWV>
+template <int NWK, int NWV, int NKS>
 struct AttnChunk {
     uint32_t kw[2][NWK];
-    uint32_t ks[2][2];
+    uint32_t ks[2][NKS];
     u32x2 kn[2], kr[2], vn[2];
     uint32_t vw[8][NWV];
 };
 
-__device__ __forceinline__ int64_t tau_tok(int g, int r) { return r < 4 ? 4 * g + r : 16 + 4 * g + (r - 4); }
+template <int D, int BK, int BV>
+struct AttnGeom {
+    static constexpr int C = D / 4, KS = C / 8;
+    static constexpr int PK = lut_group_c(BK), NEK = 1 << (PK * BK);
+    static constexpr int NWK = (C * BK + 31) / 32, CBK = C * BK / 8, CAK = cmin(pow2_align(CBK), 16);
+    static constexpr int NT = D / 16, VB = NT * BV / 8, VA = cmin(pow2_align(VB), 16);
+    static constexpr int NWV = (NT * BV + 31) / 32;
+    static constexpr int KROW = D * BK / 8, VROW = D * BV / 8;
+    static constexpr bool VPAIR = BV == 4;           // two-token pair LUT for 4-bit values
+    static constexpr int NKS = D >= 256 ? 2 : 1;     // sketch words per lane (m <= d)
+};
 
-template <int D, int BK, int BV, bool QJL, int NWK, int NWV>
-__device__ __forceinline__ void attn_load(AttnChunk<NWK, NWV>& c, int64_t t0, int64_t t_end, int l16, int g, int m,
-                                          const uint8_t* kidx, const uint8_t* ksk, const _Float16* kn,
-                                          const _Float16* kr, const uint8_t* vidx, const _Float16* vn) {
-    constexpr int C = D / 4;
-    constexpr int CBK = C * BK / 8, CAK = cmin(pow2_align(CBK), 16);
-    constexpr int NT = D / 16, VB = NT * BV / 8, VA = cmin(pow2_align(VB), 16);
-    const bool full = t0 + 32 <= t_end;
+// Per-wave base pointers of one stream (chunk offsets are added as wave-uniform values).
+struct AttnPtrs {
+    const uint8_t* kidx;
+    const uint8_t* ksk;
+    const uint8_t* kn;
+    const uint8_t* kr;
+    const uint8_t* vidx;
+    const uint8_t* vn;
+};
+
+template <int D, int BK, int BV, bool QJL, bool FULL>
+__device__ __forceinline__ void attn_load(AttnChunk<AttnGeom<D, BK, BV>::NWK, AttnGeom<D, BK, BV>::NWV, AttnGeom<D, BK, BV>::NKS>& c,
+                                          const AttnPtrs& P, int64_t t0, int64_t t_end, int l16, int g, int m) {
+    using Gm = AttnGeom<D, BK, BV>;
+    // wave-uniform chunk bases, 32-bit lane offsets
+    const uint8_t* kb = P.kidx + t0 * Gm::KROW;
+    const uint8_t* vb = P.vidx + t0 * Gm::VROW;
+    const uint32_t koff = l16 * Gm::KROW + g * Gm::CBK;
+    const uint32_t voff = (4 * g) * Gm::VROW + l16 * Gm::VB;
+    const uint32_t noff = 8 * g;                       // 4 fp16 norms of tokens 4g..4g+3
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
-        const int64_t tk = t0 + 16 * T + l16;
-        if (full || tk < t_end) {
-            load_bytes<CBK, CAK>(kidx + tk * (D * BK / 8) + g * CBK, c.kw[T]);
+        const int rem = (int)(t_end - t0);             // tokens left (FULL: >= 32)
+        if (FULL || 16 * T + l16 < rem) {
+            load_bytes<Gm::CBK, Gm::CAK>(kb + koff + T * 16 * Gm::KROW, c.kw[T]);
             if constexpr (QJL) {
-                const uint8_t* sp = ksk + tk * (m / 8) + g * (m / 32);
+                const uint8_t* sp = P.ksk + (t0 + 16 * T + l16) * (m / 8) + g * (m / 32);
                 if ((m & 127) == 0) {
                     c.ks[T][0] = *reinterpret_cast<const uint32_t*>(sp);
-                    c.ks[T][1] = m == 256 ? *reinterpret_cast<const uint32_t*>(sp + 4) : 0u;
+                    if constexpr (Gm::NKS > 1) c.ks[T][1] = m == 256 ? *reinterpret_cast<const uint32_t*>(sp + 4) : 0u;
                 } else {
                     uint32_t w0 = 0, w1 = 0;
                     for (int q = 0; q < (m >> 5); ++q) {
@@ -68,39 +90,40 @@ __device__ __forceinline__ void attn_load(AttnChunk<NWK, NWV>& c, int64_t t0, in
                         else w1 |= uint32_t(sp[q]) << (8 * (q - 4));
                     }
                     c.ks[T][0] = w0;
-                    c.ks[T][1] = w1;
+                    if constexpr (Gm::NKS > 1) c.ks[T][1] = w1;
                 }
             }
         } else {
 #pragma unroll
-            for (int k = 0; k < NWK; ++k) c.kw[T][k] = 0u;
-            c.ks[T][0] = c.ks[T][1] = 0u;
+            for (int k = 0; k < Gm::NWK; ++k) c.kw[T][k] = 0u;
+#pragma unroll
+            for (int k = 0; k < Gm::NKS; ++k) c.ks[T][k] = 0u;
         }
-        const int64_t tn = t0 + 16 * T + 4 * g;   // 4 consecutive tokens, 8-byte aligned
-        if (full || tn + 4 <= t_end) {
-            c.kn[T] = *reinterpret_cast<const u32x2*>(kn + tn);
-            if constexpr (QJL) c.kr[T] = *reinterpret_cast<const u32x2*>(kr + tn);
-            c.vn[T] = *reinterpret_cast<const u32x2*>(vn + tn);
+        if (FULL || 16 * T + 4 * g + 4 <= rem) {
+            c.kn[T] = *reinterpret_cast<const u32x2*>(P.kn + t0 * 2 + noff + 32 * T);
+            if constexpr (QJL) c.kr[T] = *reinterpret_cast<const u32x2*>(P.kr + t0 * 2 + noff + 32 * T);
+            c.vn[T] = *reinterpret_cast<const u32x2*>(P.vn + t0 * 2 + noff + 32 * T);
         } else {
-            uint32_t a[4] = {0, 0, 0, 0}, b[4] = {0, 0, 0, 0}, e[4] = {0, 0, 0, 0};
+            uint32_t e0[4] = {0, 0, 0, 0}, e1[4] = {0, 0, 0, 0}, e2[4] = {0, 0, 0, 0};
             for (int i = 0; i < 4; ++i)
-                if (tn + i < t_end) {
-                    a[i] = *reinterpret_cast<const uint16_t*>(kn + tn + i);
-                    if constexpr (QJL) b[i] = *reinterpret_cast<const uint16_t*>(kr + tn + i);
-                    e[i] = *reinterpret_cast<const uint16_t*>(vn + tn + i);
+                if (16 * T + 4 * g + i < rem) {
+                    const int64_t o = t0 * 2 + noff + 32 * T + 2 * i;
+                    e0[i] = *reinterpret_cast<const uint16_t*>(P.kn + o);
+                    if constexpr (QJL) e1[i] = *reinterpret_cast<const uint16_t*>(P.kr + o);
+                    e2[i] = *reinterpret_cast<const uint16_t*>(P.vn + o);
                 }
-            c.kn[T] = u32x2{a[0] | (a[1] << 16), a[2] | (a[3] << 16)};
-            c.kr[T] = u32x2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
-            c.vn[T] = u32x2{e[0] | (e[1] << 16), e[2] | (e[3] << 16)};
+            c.kn[T] = u32x2{e0[0] | (e0[1] << 16), e0[2] | (e0[3] << 16)};
+            c.kr[T] = u32x2{e1[0] | (e1[1] << 16), e1[2] | (e1[3] << 16)};
+            c.vn[T] = u32x2{e2[0] | (e2[1] << 16), e2[2] | (e2[3] << 16)};
         }
     }
 #pragma unroll
     for (int r = 0; r < 8; ++r) {
-        const int64_t tt = t0 + tau_tok(g, r);
-        if (full || tt < t_end) load_bytes<VB, VA>(vidx + tt * (D * BV / 8) + l16 * VB, c.vw[r]);
+        const int tr = r < 4 ? r : 16 + (r - 4);          // τ(g, r) - 4g
+        if (FULL || 4 * g + tr < (int)(t_end - t0)) load_bytes<Gm::VB, Gm::VA>(vb + voff + tr * Gm::VROW, c.vw[r]);
         else {
 #pragma unroll
-            for (int k = 0; k < NWV; ++k) c.vw[r][k] = 0u;
+            for (int k = 0; k < Gm::NWV; ++k) c.vw[r][k] = 0u;
         }
     }
 }
@@ -110,21 +133,154 @@ __device__ __forceinline__ float half_of(const u32x2& v, int i) {
     return (float)__builtin_bit_cast(_Float16, (uint16_t)((i & 1) ? (w >> 16) : (w & 0xffffu)));
 }
 
+// running state of the online softmax for the wave's 16 query columns
+template <int NT>
+struct AttnState {
+    floatx4 oacc[NT];
+    float m_run, l_run;
+};
+
+template <int D, int BK, int BV, bool QJL, bool FULL>
+__device__ __forceinline__ void attn_chunk(const AttnChunk<AttnGeom<D, BK, BV>::NWK, AttnGeom<D, BK, BV>::NWV, AttnGeom<D, BK, BV>::NKS>& cur,
+                                           AttnState<AttnGeom<D, BK, BV>::NT>& S, int64_t t0, int64_t t_end,
+                                           int g, int mks, float lam, float scale_log2,
+                                           const half8 (&qb)[AttnGeom<D, BK, BV>::KS], const half8* pb,
+                                           const _Float16* klut, const _Float16* vlut, const uint32_t* vlut2,
+                                           const _Float16* sgn) {
+    using Gm = AttnGeom<D, BK, BV>;
+    constexpr int KS = Gm::KS, PK = Gm::PK, NT = Gm::NT;
+    // ---- scores for the two 16-token tiles ----------------------------------------------------
+    float lg[8];
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+        half8 ka[KS];
+#pragma unroll
+        for (int k = 0; k < KS; ++k) {
+            if constexpr (PK == 8) {
+                const uint32_t f = get_bits<8 * BK>(cur.kw[T], (8 * k) * BK);
+                ka[k] = *reinterpret_cast<const half8*>(klut + f * 8);
+            } else if constexpr (PK == 4) {
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t f = get_bits<4 * BK>(cur.kw[T], (8 * k + 4 * h) * BK);
+                    const half4 e = *reinterpret_cast<const half4*>(klut + f * 4);
+                    ka[k][4 * h + 0] = e[0]; ka[k][4 * h + 1] = e[1];
+                    ka[k][4 * h + 2] = e[2]; ka[k][4 * h + 3] = e[3];
+                }
+            } else if constexpr (PK == 2) {
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    const uint32_t f = get_bits<2 * BK>(cur.kw[T], (8 * k + 2 * h) * BK);
+                    const half2v e = *reinterpret_cast<const half2v*>(klut + f * 2);
+                    ka[k][2 * h] = e[0];
+                    ka[k][2 * h + 1] = e[1];
+                }
+            } else {
+#pragma unroll
+                for (int h = 0; h < 8; ++h) ka[k][h] = klut[get_bits<BK>(cur.kw[T], (8 * k + h) * BK)];
+            }
+        }
+        floatx4 s1 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int k = 0; k < KS; ++k) s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[k], qb[k], s1, 0, 0, 0);
+        floatx4 s2 = {0.0f, 0.0f, 0.0f, 0.0f};
+        if constexpr (QJL) {
+#pragma unroll
+            for (int k = 0; k < KS; ++k) {
+                if (k < mks) {
+                    const uint32_t byte = (cur.ks[T][k >> 2] >> (8 * (k & 3))) & 0xffu;
+                    const half8 sa = *reinterpret_cast<const half8*>(sgn + byte * 8);
+                    s2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(sa, pb[k], s2, 0, 0, 0);
+                }
+            }
+        }
+        // output lane (q = l16, g) holds tokens t0 + 16T + 4g + i
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            float sc = s1[i];
+            if constexpr (QJL) sc = fmaf(lam * half_of(cur.kr[T], i), s2[i], sc);
+            float v = half_of(cur.kn[T], i) * scale_log2 * sc;
+            if (!FULL && t0 + 16 * T + 4 * g + i >= t_end) v = -INFINITY;
+            lg[4 * T + i] = v;
+        }
+    }
+    // ---- online softmax (base 2) per query column; rescale only when a running max moved ---------
+    float cmax = lg[0];
+#pragma unroll
+    for (int r = 1; r < 8; ++r) cmax = fmaxf(cmax, lg[r]);
+    cmax = max4(cmax);
+    const float m_new = fmaxf(S.m_run, cmax);
+    if (__builtin_amdgcn_read_exec() & __ballot(m_new != S.m_run)) {
+        const float alpha = __builtin_amdgcn_exp2f(S.m_run - m_new);
+        S.l_run *= alpha;
+#pragma unroll
+        for (int n = 0; n < NT; ++n) S.oacc[n] *= alpha;
+        S.m_run = m_new;
+    }
+    float wsum = 0.0f;
+    half8 wb;
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const _Float16 wh = (_Float16)__builtin_amdgcn_exp2f(lg[r] - m_new);
+        wsum += (float)wh;
+        wb[r] = wh * (_Float16)half_of(cur.vn[r >> 2], r & 3);
+    }
+    S.l_run += wsum;
+    // ---- values: A = V̂^T tile n (row = coordinate NT*l16 + n), 8 tokens of k-block g -------------
+    if constexpr (Gm::VPAIR) {
+        // tokens (2p, 2p+1) share one lookup: byte k of z[p][0] / z[p][1] = the two 4-bit indices of
+        // tile 2k / 2k+1 of word j (tiles 8j..8j+7)
+#pragma unroll
+        for (int j = 0; j < Gm::NWV; ++j) {
+            uint32_t ze[4], zo[4];
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+                const uint32_t w0 = cur.vw[2 * p][j], w1 = cur.vw[2 * p + 1][j];
+                ze[p] = (w0 & 0x0f0f0f0fu) | ((w1 << 4) & 0xf0f0f0f0u);
+                zo[p] = ((w0 >> 4) & 0x0f0f0f0fu) | (w1 & 0xf0f0f0f0u);
+            }
+#pragma unroll
+            for (int q = 0; q < 8 && 8 * j + q < NT; ++q) {
+                half8 va;
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    const uint32_t z = (q & 1) ? zo[p] : ze[p];
+                    const uint32_t e = vlut2[(z >> (8 * (q >> 1))) & 0xffu];
+                    const half2v hv = __builtin_bit_cast(half2v, e);
+                    va[2 * p] = hv[0];
+                    va[2 * p + 1] = hv[1];
+                }
+                S.oacc[8 * j + q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, wb, S.oacc[8 * j + q], 0, 0, 0);
+            }
+        }
+    } else {
+#pragma unroll
+        for (int n = 0; n < NT; ++n) {
+            half8 va;
+#pragma unroll
+            for (int r = 0; r < 8; ++r) va[r] = vlut[get_bits<BV>(cur.vw[r], n * BV)];
+            S.oacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, wb, S.oacc[n], 0, 0, 0);
+        }
+    }
+}
+
 template <int D, int BK, int BV, bool QJL>
-__global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
-    constexpr int C = D / 4;
-    constexpr int KS = C / 8;                       // k-steps over d
-    constexpr int PK = lut_group_c(BK), NEK = 1 << (PK * BK);
-    constexpr int NWK = (C * BK + 31) / 32;
-    constexpr int NT = D / 16;                      // value tiles (16 coordinates each)
-    constexpr int NWV = (NT * BV + 31) / 32;
+__global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attn_kernel(AttnArgs a) {
+    using Gm = AttnGeom<D, BK, BV>;
+    constexpr int C = Gm::C, KS = Gm::KS, PK = Gm::PK, NEK = Gm::NEK, NT = Gm::NT;
     constexpr int LV = 1 << BV;
 
     __shared__ _Float16 klut[NEK * PK];
     __shared__ _Float16 vlut[LV];
+    __shared__ uint32_t vlut2[Gm::VPAIR ? 256 : 1];
     __shared__ _Float16 sgn[QJL ? 256 * 8 : 8];
     for (int i = threadIdx.x; i < NEK * PK; i += blockDim.x) klut[i] = a.tk.lut_f16[i];
     for (int i = threadIdx.x; i < LV; i += blockDim.x) vlut[i] = (_Float16)a.tv.cent[i];
+    if constexpr (Gm::VPAIR)
+        for (int i = threadIdx.x; i < 256; i += blockDim.x) {
+            const half2v hv = {(_Float16)a.tv.cent[i & 15], (_Float16)a.tv.cent[i >> 4]};
+            vlut2[i] = __builtin_bit_cast(uint32_t, hv);
+        }
     if constexpr (QJL)
         for (int i = threadIdx.x; i < 256; i += blockDim.x)
 #pragma unroll
@@ -160,122 +316,57 @@ __global__ __launch_bounds__(256) void attn_kernel(AttnArgs a) {
         }
     }
 
-    floatx4 oacc[NT];
+    AttnState<NT> S;
 #pragma unroll
-    for (int n = 0; n < NT; ++n) oacc[n] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-    float m_run = -INFINITY, l_run = 0.0f;
+    for (int n = 0; n < NT; ++n) S.oacc[n] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    S.m_run = -INFINITY;
+    S.l_run = 0.0f;
 
-    const uint8_t* kidx = a.pk + a.k_off_idx + st * a.n_tokens * (int64_t)(D * BK / 8);
-    const uint8_t* ksk = a.pk + a.k_off_sketch + st * a.n_tokens * (int64_t)(m / 8);
-    const _Float16* kn = reinterpret_cast<const _Float16*>(a.pk + a.k_off_norm) + st * a.n_tokens;
-    const _Float16* kr = reinterpret_cast<const _Float16*>(a.pk + a.k_off_rnorm) + st * a.n_tokens;
-    const uint8_t* vidx = a.pv + a.v_off_idx + st * a.n_tokens * (int64_t)(D * BV / 8);
-    const _Float16* vn = reinterpret_cast<const _Float16*>(a.pv + a.v_off_norm) + st * a.n_tokens;
+    AttnPtrs P;
+    P.kidx = a.pk + a.k_off_idx + st * a.n_tokens * (int64_t)Gm::KROW;
+    P.ksk = a.pk + a.k_off_sketch + st * a.n_tokens * (int64_t)(m / 8);
+    P.kn = a.pk + a.k_off_norm + st * a.n_tokens * 2;
+    P.kr = a.pk + a.k_off_rnorm + st * a.n_tokens * 2;
+    P.vidx = a.pv + a.v_off_idx + st * a.n_tokens * (int64_t)Gm::VROW;
+    P.vn = a.pv + a.v_off_norm + st * a.n_tokens * 2;
 
-    AttnChunk<NWK, NWV> nxt;
-    attn_load<D, BK, BV, QJL>(nxt, t_begin, t_end, l16, g, m, kidx, ksk, kn, kr, vidx, vn);
+    // full 32-token chunks through two ping-pong buffers (next chunk's loads overlap this one's
+    // math), then at most one guarded partial chunk
+    AttnChunk<Gm::NWK, Gm::NWV, Gm::NKS> A, B;
+    const int64_t n_full = (t_end - t_begin) >> 5;
+    int64_t c = 0;
+    if (n_full > 0) attn_load<D, BK, BV, QJL, true>(A, P, t_begin, t_end, l16, g, m);
 #pragma unroll 1
-    for (int64_t t0 = t_begin; t0 < t_end; t0 += 32) {
-        const AttnChunk<NWK, NWV> cur = nxt;
-        if (t0 + 32 < t_end)   // issue the next chunk's loads before computing this one
-            attn_load<D, BK, BV, QJL>(nxt, t0 + 32, t_end, l16, g, m, kidx, ksk, kn, kr, vidx, vn);
-        const bool full = t0 + 32 <= t_end;
-        // ---- scores for the two 16-token tiles ----------------------------------------------
-        float lg[8];
-#pragma unroll
-        for (int T = 0; T < 2; ++T) {
-            half8 ka[KS];
-#pragma unroll
-            for (int k = 0; k < KS; ++k) {
-                if constexpr (PK == 8) {
-                    const uint32_t f = get_bits<8 * BK>(cur.kw[T], (8 * k) * BK);
-                    ka[k] = *reinterpret_cast<const half8*>(klut + f * 8);
-                } else if constexpr (PK == 4) {
-#pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const uint32_t f = get_bits<4 * BK>(cur.kw[T], (8 * k + 4 * h) * BK);
-                        const half4 e = *reinterpret_cast<const half4*>(klut + f * 4);
-                        ka[k][4 * h + 0] = e[0]; ka[k][4 * h + 1] = e[1];
-                        ka[k][4 * h + 2] = e[2]; ka[k][4 * h + 3] = e[3];
-                    }
-                } else if constexpr (PK == 2) {
-#pragma unroll
-                    for (int h = 0; h < 4; ++h) {
-                        const uint32_t f = get_bits<2 * BK>(cur.kw[T], (8 * k + 2 * h) * BK);
-                        const half2v e = *reinterpret_cast<const half2v*>(klut + f * 2);
-                        ka[k][2 * h] = e[0];
-                        ka[k][2 * h + 1] = e[1];
-                    }
-                } else {
-#pragma unroll
-                    for (int h = 0; h < 8; ++h) ka[k][h] = klut[get_bits<BK>(cur.kw[T], (8 * k + h) * BK)];
-                }
-            }
-            floatx4 s1 = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int k = 0; k < KS; ++k) s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[k], qb[k], s1, 0, 0, 0);
-            floatx4 s2 = {0.0f, 0.0f, 0.0f, 0.0f};
-            if constexpr (QJL) {
-#pragma unroll
-                for (int k = 0; k < KS; ++k) {
-                    if (k < mks) {
-                        const uint32_t byte = (cur.ks[T][k >> 2] >> (8 * (k & 3))) & 0xffu;
-                        const half8 sa = *reinterpret_cast<const half8*>(sgn + byte * 8);
-                        s2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(sa, pb[k], s2, 0, 0, 0);
-                    }
-                }
-            }
-            // output lane (q = l16, g) holds tokens t0 + 16T + 4g + i
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                float sc = s1[i];
-                if constexpr (QJL) sc = fmaf(lam * half_of(cur.kr[T], i), s2[i], sc);
-                float v = half_of(cur.kn[T], i) * sc * a.scale_log2;
-                if (!full && t0 + 16 * T + 4 * g + i >= t_end) v = -INFINITY;
-                lg[4 * T + i] = v;
-            }
-        }
-        // ---- online softmax (base 2) per query column -----------------------------------------
-        float cmax = lg[0];
-#pragma unroll
-        for (int r = 1; r < 8; ++r) cmax = fmaxf(cmax, lg[r]);
-        cmax = max4(cmax);
-        const float m_new = fmaxf(m_run, cmax);
-        const float alpha = exp2f(m_run - m_new);
-        m_run = m_new;
-        float wsum = 0.0f;
-        half8 wb;
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const float w = exp2f(lg[r] - m_new);
-            const _Float16 wh = (_Float16)w;
-            wsum += (float)wh;
-            wb[r] = (_Float16)((float)wh * half_of(cur.vn[r >> 2], r & 3));
-        }
-        l_run = l_run * alpha + wsum;
-#pragma unroll
-        for (int n = 0; n < NT; ++n) oacc[n] *= alpha;
-        // ---- values: A = V̂^T tile n (row = coordinate NT*l16 + n), 8 tokens of k-block g ---------
-#pragma unroll
-        for (int n = 0; n < NT; ++n) {
-            half8 va;
-#pragma unroll
-            for (int r = 0; r < 8; ++r) va[r] = vlut[get_bits<BV>(cur.vw[r], n * BV)];
-            oacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(va, wb, oacc[n], 0, 0, 0);
-        }
+    for (; c + 2 <= n_full; c += 2) {
+        attn_load<D, BK, BV, QJL, true>(B, P, t_begin + (c + 1) * 32, t_end, l16, g, m);
+        attn_chunk<D, BK, BV, QJL, true>(A, S, t_begin + c * 32, t_end, g, mks, lam, a.scale_log2, qb, pb, klut,
+                                         vlut, vlut2, sgn);
+        if (c + 2 < n_full) attn_load<D, BK, BV, QJL, true>(A, P, t_begin + (c + 2) * 32, t_end, l16, g, m);
+        attn_chunk<D, BK, BV, QJL, true>(B, S, t_begin + (c + 1) * 32, t_end, g, mks, lam, a.scale_log2, qb, pb,
+                                         klut, vlut, vlut2, sgn);
+    }
+    if (c < n_full) {
+        attn_chunk<D, BK, BV, QJL, true>(A, S, t_begin + c * 32, t_end, g, mks, lam, a.scale_log2, qb, pb, klut,
+                                         vlut, vlut2, sgn);
+        ++c;
+    }
+    if (t_begin + c * 32 < t_end) {
+        attn_load<D, BK, BV, QJL, false>(A, P, t_begin + c * 32, t_end, l16, g, m);
+        attn_chunk<D, BK, BV, QJL, false>(A, S, t_begin + c * 32, t_end, g, mks, lam, a.scale_log2, qb, pb, klut,
+                                          vlut, vlut2, sgn);
     }
     // ---- partial results: lane (q = l16, g) holds O[coord NT*(4g+i) + n][q] --------------------
-    l_run = sum4(l_run);
+    const float l_tot = sum4(S.l_run);
     if (qvalid) {
         float* dst = a.part + ((st * a.n_split + split) * 16 + l16) * (int64_t)D;
 #pragma unroll
         for (int n = 0; n < NT; ++n)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) dst[NT * (4 * g + i) + n] = oacc[n][i];
+            for (int i = 0; i < 4; ++i) dst[NT * (4 * g + i) + n] = S.oacc[n][i];
         if (g == 0) {
             float* ml = a.part_ml + ((st * a.n_split + split) * 16 + l16) * 2;
-            ml[0] = m_run;
-            ml[1] = l_run;
+            ml[0] = S.m_run;
+            ml[1] = l_tot;
         }
     }
 }
@@ -286,29 +377,41 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     const int bidx = (int)(row / a.n_q_heads), h = (int)(row - (int64_t)bidx * a.n_q_heads);
     const int kvh = h / a.group, r = h - kvh * a.group;
     const int64_t st = (int64_t)bidx * a.n_kv_heads + kvh;
-    const int d = a.tv.d;
+    const int d = a.tv.d, ns = a.n_split;
     __shared__ float buf[256];
-    __shared__ float red[2];
-    if (threadIdx.x == 0) {
-        float M = -INFINITY;
-        for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, a.part_ml[((st * a.n_split + s) * 16 + r) * 2]);
-        float Lsum = 0.0f;
-        for (int s = 0; s < a.n_split; ++s) {
-            const float* ml = a.part_ml + ((st * a.n_split + s) * 16 + r) * 2;
-            Lsum += ml[1] * exp2f(ml[0] - M);
-        }
-        red[0] = M;
-        red[1] = Lsum;
-    }
+    __shared__ float wsp[1024];                          // per-split weights (n_split <= 1024)
+    __shared__ float red[8];
+    const float* ml = a.part_ml + (st * ns * 16 + r) * 2;   // split s at ml[s * 32]
+    // max over splits
+    float mx = -INFINITY;
+    for (int s = threadIdx.x; s < ns; s += blockDim.x) mx = fmaxf(mx, ml[s * 32]);
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
     __syncthreads();
-    const float M = red[0], Linv = 1.0f / red[1];
+    const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    float ls = 0.0f;
+    for (int s = threadIdx.x; s < ns; s += blockDim.x) {
+        const float w = exp2f(ml[s * 32] - M);
+        wsp[s] = w;
+        ls += w * ml[s * 32 + 1];
+    }
+    for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o);
+    __syncthreads();
+    if ((threadIdx.x & 63) == 0) red[4 + (threadIdx.x >> 6)] = ls;
+    __syncthreads();
+    const float Linv = 1.0f / (red[4] + red[5] + red[6] + red[7]);
+    const float* part = a.part + (st * ns * 16 + r) * (int64_t)d;  // split s at part[s * 16 d]
     for (int j = threadIdx.x; j < d; j += blockDim.x) {
-        float acc = 0.0f;
-        for (int s = 0; s < a.n_split; ++s) {
-            const float wgt = exp2f(a.part_ml[((st * a.n_split + s) * 16 + r) * 2] - M);
-            acc = fmaf(wgt, a.part[((st * a.n_split + s) * 16 + r) * (int64_t)d + j], acc);
+        float acc0 = 0.0f, acc1 = 0.0f, acc2 = 0.0f, acc3 = 0.0f;
+        int s = 0;
+        for (; s + 4 <= ns; s += 4) {
+            acc0 = fmaf(wsp[s], part[(int64_t)s * 16 * d + j], acc0);
+            acc1 = fmaf(wsp[s + 1], part[(int64_t)(s + 1) * 16 * d + j], acc1);
+            acc2 = fmaf(wsp[s + 2], part[(int64_t)(s + 2) * 16 * d + j], acc2);
+            acc3 = fmaf(wsp[s + 3], part[(int64_t)(s + 3) * 16 * d + j], acc3);
         }
-        buf[j] = acc * Linv;
+        for (; s < ns; ++s) acc0 = fmaf(wsp[s], part[(int64_t)s * 16 * d + j], acc0);
+        buf[j] = ((acc0 + acc1) + (acc2 + acc3)) * Linv;
     }
     __syncthreads();
     for (int hh = 1; hh < d; hh <<= 1) {

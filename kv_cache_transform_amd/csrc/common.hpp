@@ -31,6 +31,20 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
 __device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
 
+// bf16 pair dot products with an inline zero accumulator (three-operand VOP3P form):
+//   dot2_bf16(a, b)        = a.lo*b.lo + a.hi*b.hi
+//   dot2_bf16_nhi(a, b)    = a.lo*b.lo - a.hi*b.hi   (neg_hi on the second operand)
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b) {
+    float r;
+    asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+__device__ __forceinline__ float dot2_bf16_nhi(uint32_t a, uint32_t b) {
+    float r;
+    asm("v_dot2_f32_bf16 %0, %1, %2, 0 neg_hi:[0,1,0]" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 // swap rows 1,3 of a with rows 0,2 of b (rows = 16-lane groups)
 __device__ __forceinline__ void xswap16(float& a, float& b) {
     auto r = __builtin_amdgcn_permlane16_swap(f2u(a), f2u(b), false, false);

@@ -28,33 +28,45 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
     const int lane = threadIdx.x & 63;
     const int v = lane & 15, g = lane >> 4;
-    const int64_t wave_id = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    int64_t tile = wave_id * a.tiles_per_wave;
-    const int64_t tile_end = tile + a.tiles_per_wave < a.n_tiles ? tile + a.tiles_per_wave : a.n_tiles;
-
-    int cur_head = -1;
+    const int wave = threadIdx.x >> 6;
+    // block = one stream's tile range; waves take every 4th tile
+    const int64_t st = blockIdx.x / a.blocks_per_stream;
+    const int64_t sub = blockIdx.x - st * a.blocks_per_stream;
+    const int64_t tb0 = sub * a.tiles_per_block;
+    const int64_t tb1 = tb0 + a.tiles_per_block < a.tiles_per_stream ? tb0 + a.tiles_per_block : a.tiles_per_stream;
+    const int head = (int)(st % a.t.n_heads);
     uint32_t smask[C];
-    for (; tile < tile_end; ++tile) {
-        const int64_t st = tile / a.tiles_per_stream;
-        const int64_t tok = (tile - st * a.tiles_per_stream) * 16 + v;
-        const bool valid = tok < a.n_tokens;
-        const int head = (int)(st % a.t.n_heads);
-        if (head != cur_head) {
-            cur_head = head;
-            const float* ss = a.t.signs_slot + ((int64_t)head * 4 + g) * C;
+    {
+        const float* ss = a.t.signs_slot + ((int64_t)head * 4 + g) * C;
 #pragma unroll
-            for (int s = 0; s < C; ++s) smask[s] = f2u(ss[s]) & 0x80000000u;
-        }
-        const int64_t vec = st * a.n_tokens + (valid ? tok : 0);
-        uint32_t w[NW];
-        float nrm = 0.0f;
-        if (valid) {
-            load_bytes<CB, CA>(a.packed + a.off_idx + vec * (int64_t)(D * B / 8) + g * CB, w);
-            nrm = (float)*reinterpret_cast<const _Float16*>(a.packed + a.off_norm + vec * 2);
+        for (int s = 0; s < C; ++s) smask[s] = f2u(ss[s]) & 0x80000000u;
+    }
+    const uint8_t* pidx = a.packed + a.off_idx + st * a.n_tokens * (int64_t)(D * B / 8) + g * CB;
+    const uint16_t* pnrm = reinterpret_cast<const uint16_t*>(a.packed + a.off_norm) + st * a.n_tokens;
+    // packed words and norm of one tile for this lane (zeros past the end)
+    auto load_tile = [&](uint32_t (&w)[NW], uint32_t& nb, int64_t tl) {
+        const int64_t tok = tl * 16 + v;
+        if (tl < tb1 && tok < a.n_tokens) {
+            load_bytes<CB, CA>(pidx + tok * (D * B / 8), w);
+            nb = pnrm[tok];
         } else {
 #pragma unroll
             for (int k = 0; k < NW; ++k) w[k] = 0u;
+            nb = 0u;
         }
+    };
+    uint32_t wn[NW], nbn;
+    load_tile(wn, nbn, tb0 + wave);
+#pragma unroll 1
+    for (int64_t tile = tb0 + wave; tile < tb1; tile += 4) {
+        const int64_t tok = tile * 16 + v;
+        const bool valid = tok < a.n_tokens;
+        const int64_t vec = st * a.n_tokens + (valid ? tok : 0);
+        uint32_t w[NW];
+#pragma unroll
+        for (int k = 0; k < NW; ++k) w[k] = wn[k];
+        const float nrm = (float)__builtin_bit_cast(_Float16, (uint16_t)nbn);
+        load_tile(wn, nbn, tile + 4);       // next tile's loads overlap this tile's math
         float x[C];
 #pragma unroll
         for (int q = 0; q < C / P; ++q) {
@@ -98,12 +110,14 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeArgs a) {
 
 template <int D, int B, bool BF>
 static hipError_t launch_one(const DecodeArgs& a, int num_cus, hipStream_t s) {
-    const int64_t max_waves = (int64_t)num_cus * 16;
-    const int64_t waves = a.n_tiles < max_waves ? a.n_tiles : max_waves;
-    const int64_t blocks = (waves + 3) / 4;
     DecodeArgs b = a;
-    b.tiles_per_wave = (a.n_tiles + blocks * 4 - 1) / (blocks * 4);
-    hipLaunchKernelGGL((decode_kernel<D, B, BF>), dim3((unsigned)blocks), dim3(256), 0, s, b);
+    const int64_t target = (int64_t)num_cus * 4;
+    int64_t bps = (target + a.n_streams - 1) / a.n_streams;
+    if (bps > a.tiles_per_stream) bps = a.tiles_per_stream;
+    if (bps < 1) bps = 1;
+    b.blocks_per_stream = bps;
+    b.tiles_per_block = (a.tiles_per_stream + bps - 1) / bps;
+    hipLaunchKernelGGL((decode_kernel<D, B, BF>), dim3((unsigned)(a.n_streams * bps)), dim3(256), 0, s, b);
     return hipGetLastError();
 }
 

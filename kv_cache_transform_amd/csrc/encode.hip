@@ -57,16 +57,13 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
     const float gA = 0.5f * (float)G;
     const float gB = 0.5f * (float)G + 1.0f;       // entry 0 is a guard cell
 
-    uint32_t Ps[BF16 ? C / 2 : 1], Ms[BF16 ? C / 2 : 1];
+    uint32_t Ps[BF16 ? C / 2 : 1];
     float sg[BF16 ? 1 : C];
     {
         const float* ss = a.t.signs_slot + ((int64_t)head * 4 + g) * C;
         if constexpr (BF16) {
 #pragma unroll
-            for (int k = 0; k < C / 2; ++k) {
-                Ps[k] = (f2u(ss[2 * k]) >> 16) | (f2u(ss[2 * k + 1]) & 0xffff0000u);
-                Ms[k] = Ps[k] ^ 0x80000000u;
-            }
+            for (int k = 0; k < C / 2; ++k) Ps[k] = (f2u(ss[2 * k]) >> 16) | (f2u(ss[2 * k + 1]) & 0xffff0000u);
         } else {
 #pragma unroll
             for (int s = 0; s < C; ++s) sg[s] = ss[s];
@@ -77,8 +74,40 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
     const int rho = lane & 15;
     const int row_base = (rho >> 2) * (m >> 2) + (rho & 3);
 
+    // raw input words of one 16-vector group (runs of R coordinates, see common.hpp)
+    constexpr int NIW = BF16 ? C / 2 : C;
+    auto load_group = [&](uint32_t (&w)[NIW], int64_t tile) {
+        const int64_t tok = tile * 16 + v;
+        const bool valid = tile < tb1 && tok < a.n_tokens;
+        const int64_t vec = st * a.n_tokens + (valid ? tok : 0);
+        constexpr int ES = BF16 ? 2 : 4;              // element size
+        constexpr int RB = ES * R;                    // bytes per run
+        constexpr int RA = cmin(pow2_align(RB), 16);
+        const uint8_t* base = reinterpret_cast<const uint8_t*>(a.x) + vec * (int64_t)(ES * D) + ES * g * R;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if (valid) load_bytes<RB, RA>(base + r * (ES * D / 4), &w[r * (NIW / 4)]);
+            else {
+#pragma unroll
+                for (int k = 0; k < NIW / 4; ++k) w[r * (NIW / 4) + k] = 0u;
+            }
+        }
+    };
+    uint32_t nxt[NG][NIW];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) load_group(nxt[gi], tb0 + wave * NG + gi);
+
 #pragma unroll 1
     for (int64_t t = tb0 + wave * NG; t < tb1; t += 4 * NG) {
+        uint32_t cur[NG][NIW];
+#pragma unroll
+        for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+            for (int k = 0; k < NIW; ++k) cur[gi][k] = nxt[gi][k];
+        if (t + 4 * NG < tb1) {            // issue the next pass's loads before this pass's math
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) load_group(nxt[gi], t + 4 * NG + gi);
+        }
         half8 bh[NG][QJL ? C / 8 : 1], bl[NG][QJL ? C / 8 : 1];
         float e2v[NG];
         bool validv[NG];
@@ -91,43 +120,20 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
             validv[gi] = valid;
             vecv[gi] = vec;
 
-            // ---- load, sign, first butterfly stage, norm ------------------------------------
+            // ---- sign, first butterfly stage, norm ----------------------------------------------
             float x[C];
             float n2 = 0.0f;
+            const uint32_t (&w)[NIW] = cur[gi];
             if constexpr (BF16) {
-                uint32_t w[C / 2];
-                constexpr int RB = 2 * R;              // bytes per run
-                constexpr int RA = cmin(pow2_align(RB), 16);
-                const uint8_t* base = reinterpret_cast<const uint8_t*>(a.x) + vec * (int64_t)(2 * D) + 2 * g * R;
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    if (valid) load_bytes<RB, RA>(base + r * (D / 2), &w[r * (R / 2)]);
-                    else {
-#pragma unroll
-                        for (int k = 0; k < R / 2; ++k) w[r * (R / 2) + k] = 0u;
-                    }
-                }
 #pragma unroll
                 for (int k = 0; k < C / 2; ++k) {
                     const bf16x2 wv = __builtin_bit_cast(bf16x2, w[k]);
-                    x[2 * k] = __builtin_amdgcn_fdot2_f32_bf16(wv, __builtin_bit_cast(bf16x2, Ps[k]), 0.0f, false);
-                    x[2 * k + 1] = __builtin_amdgcn_fdot2_f32_bf16(wv, __builtin_bit_cast(bf16x2, Ms[k]), 0.0f, false);
+                    x[2 * k] = dot2_bf16(w[k], Ps[k]);          // s_i x_i + s_{i+1} x_{i+1}
+                    x[2 * k + 1] = dot2_bf16_nhi(w[k], Ps[k]);  // s_i x_i - s_{i+1} x_{i+1}
                     n2 = __builtin_amdgcn_fdot2_f32_bf16(wv, wv, n2, false);
                 }
                 fwht_slots<C, 2>(x);
             } else {
-                constexpr int RB = 4 * R;
-                constexpr int RA = cmin(pow2_align(RB), 16);
-                const uint8_t* base = reinterpret_cast<const uint8_t*>(a.x) + vec * (int64_t)(4 * D) + 4 * g * R;
-                uint32_t w[C];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    if (valid) load_bytes<RB, RA>(base + r * D, &w[r * R]);
-                    else {
-#pragma unroll
-                        for (int k = 0; k < R; ++k) w[r * R + k] = 0u;
-                    }
-                }
 #pragma unroll
                 for (int s = 0; s < C; ++s) {
                     const float xv = u2f(w[s]);
@@ -140,18 +146,26 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
             n2 = sum4(n2);
             const float n = sqrtf(n2);
             const float sc = n > 0.0f ? kInvSqrtD / n : 0.0f;
+            const float sA = sc * gA;
 
             // ---- scalar quantiser + pack (and the scaled residual for QJL) ----------------------
+            // The grid lives in the affine domain u = y G/2 + G/2 + 1; thresholds are stored there.
             uint32_t pk[NW];
 #pragma unroll
             for (int k = 0; k < NW; ++k) pk[k] = 0u;
             float e2 = 0.0f;
 #pragma unroll
             for (int s = 0; s < C; ++s) {
-                const float y = x[s] * sc;
-                const uint32_t cell = (uint32_t)fmaf(y, gA, gB);
+                float y, u;
+                if constexpr (QJL) {
+                    y = x[s] * sc;
+                    u = fmaf(y, gA, gB);
+                } else {
+                    u = fmaf(x[s], sA, gB);
+                }
+                const uint32_t cell = (uint32_t)u;
                 const uint32_t thr = lds[2 * cell], base = lds[2 * cell + 1];
-                const uint32_t idx = base + (y >= u2f(thr) ? 1u : 0u);
+                const uint32_t idx = base + (u >= u2f(thr) ? 1u : 0u);
                 put_bits<B>(pk, s * B, idx);
                 if constexpr (QJL) {
                     const float e = fmaf(y, 1024.0f, -lds_c[idx]);   // 2^10 (y - c[idx])

@@ -40,6 +40,7 @@ struct DecodeArgs {
     int64_t n_streams, n_tokens;
     int64_t off_idx, off_norm;
     int64_t tiles_per_stream, n_tiles, tiles_per_wave;
+    int64_t blocks_per_stream, tiles_per_block;
     DevTables t;
 };
 
@@ -62,6 +63,7 @@ struct ScoresArgs {
     int n_q;
     int64_t off_idx, off_sketch, off_norm, off_rnorm;
     int64_t tiles_per_stream, n_tiles, tiles_per_wave;
+    int64_t blocks_per_stream, tiles_per_block;
     DevTables t;
 };
 

@@ -124,17 +124,19 @@ __global__ __launch_bounds__(256) void scores_kernel(ScoresArgs a) {
 
     const int lane = threadIdx.x & 63;
     const int t16 = lane & 15, g = lane >> 4;
-    const int64_t wave_id = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
-    int64_t tile = wave_id * a.tiles_per_wave;
-    const int64_t tile_end = tile + a.tiles_per_wave < a.n_tiles ? tile + a.tiles_per_wave : a.n_tiles;
+    const int wave = threadIdx.x >> 6;
+    const int64_t st = blockIdx.x / a.blocks_per_stream;
+    const int64_t sub = blockIdx.x - st * a.blocks_per_stream;
+    const int64_t tb0 = sub * a.tiles_per_block;
+    const int64_t tb1 = tb0 + a.tiles_per_block < a.tiles_per_stream ? tb0 + a.tiles_per_block : a.tiles_per_stream;
     const int m = a.t.m;
     const int mks = m >> 5;                     // sketch k-steps (m/4 bits per lane, 8 per step)
     const float lam = QJL ? 1.2533141373155003f / (float)m : 0.0f;   // sqrt(pi/2)/m
     const int nqt = (a.n_q + 15) >> 4;
 
-    for (; tile < tile_end; ++tile) {
-        const int64_t st = tile / a.tiles_per_stream;
-        const int64_t tok = (tile - st * a.tiles_per_stream) * 16 + t16;
+#pragma unroll 1
+    for (int64_t tile = tb0 + wave; tile < tb1; tile += 4) {
+        const int64_t tok = tile * 16 + t16;
         const bool valid = tok < a.n_tokens;
         const int64_t vec = st * a.n_tokens + (valid ? tok : 0);
         uint32_t w[NW];
@@ -195,12 +197,14 @@ __global__ __launch_bounds__(256) void scores_kernel(ScoresArgs a) {
 
 template <int D, int B, bool QJL>
 static hipError_t launch_one(const ScoresArgs& a, int num_cus, hipStream_t s) {
-    const int64_t max_waves = (int64_t)num_cus * 16;
-    const int64_t waves = a.n_tiles < max_waves ? a.n_tiles : max_waves;
-    const int64_t blocks = (waves + 3) / 4;
     ScoresArgs b = a;
-    b.tiles_per_wave = (a.n_tiles + blocks * 4 - 1) / (blocks * 4);
-    hipLaunchKernelGGL((scores_kernel<D, B, QJL>), dim3((unsigned)blocks), dim3(256), 0, s, b);
+    const int64_t target = (int64_t)num_cus * 4;
+    int64_t bps = (target + a.n_streams - 1) / a.n_streams;
+    if (bps > a.tiles_per_stream) bps = a.tiles_per_stream;
+    if (bps < 1) bps = 1;
+    b.blocks_per_stream = bps;
+    b.tiles_per_block = (a.tiles_per_stream + bps - 1) / bps;
+    hipLaunchKernelGGL((scores_kernel<D, B, QJL>), dim3((unsigned)(a.n_streams * bps)), dim3(256), 0, s, b);
     return hipGetLastError();
 }
 

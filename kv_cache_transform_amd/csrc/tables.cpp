@@ -196,28 +196,32 @@ int lloyd_max(int d, int b, std::vector<double>& thresholds, std::vector<double>
 }
 
 // ---------------------------------------------------------------------------------------------
-bool build_grid(const std::vector<float>& thr, Grid& out) {
-    const double eps = std::ldexp(1.0, -20);  // covers the fp32 rounding of y*G/2 + G/2
-    for (int G = 64; G <= 8192; G *= 2) {
-        std::vector<uint32_t> e(2 * (G + 2));
+bool build_grid(const std::vector<double>& thr_y, Grid& out) {
+    const double eps = 1.0 / 256.0;  // in u units; the fp32 rounding of u is below 2^-11
+    for (int G = 64; G <= 4096; G *= 2) {
+        const double gA = 0.5 * G, gB = 0.5 * G + 1.0;
+        std::vector<float> tu(thr_y.size());
+        for (size_t k = 0; k < thr_y.size(); ++k) tu[k] = (float)(thr_y[k] * gA + gB);
+        std::vector<uint32_t> e(2 * (G + 3));
         bool ok = true;
-        for (int cidx = 0; cidx < G + 2 && ok; ++cidx) {
-            const double lo = cidx * 2.0 / G - 1.0 - eps;
-            const double hi = (cidx + 1) * 2.0 / G - 1.0 + eps;
+        for (int c = 0; c < G + 3 && ok; ++c) {
+            const double lo = c - eps, hi = c + 1 + eps;
             int base = 0, inside = 0;
             float cand = std::numeric_limits<float>::infinity();
-            for (float tf : thr) {
+            for (float tf : tu) {
                 if ((double)tf < lo) ++base;
                 else if ((double)tf <= hi) { ++inside; cand = tf; }
             }
             if (inside > 1) ok = false;
+            if (c == 0) { base = 0; cand = std::numeric_limits<float>::infinity(); }
             uint32_t bits;
             std::memcpy(&bits, &cand, 4);
-            e[2 * cidx] = bits;
-            e[2 * cidx + 1] = (uint32_t)base;
+            e[2 * c] = bits;
+            e[2 * c + 1] = (uint32_t)base;
         }
         if (ok) {
             out.G = G;
+            out.thr_u.swap(tu);
             out.entries.swap(e);
             return true;
         }

@@ -20,14 +20,17 @@ void gaussian_matrix_f16(uint64_t seed, uint32_t head, int m, int d, std::vector
 int lloyd_max(int d, int b, std::vector<double>& thresholds, std::vector<double>& centroids);
 
 // ---- kernel-side derived tables ---------------------------------------------------------------
-// Search grid over y in [-1,1]: cell c = (uint)(y*G/2 + G/2); entry c = {fp32 bits of the one
-// threshold that can fall in the cell (or +inf), count of thresholds below the cell}; for every fp32
-// y that maps to cell c, #{k : thr_f32[k] <= y} == base + (y >= thr).  G+2 entries.
+// Search grid in the affine domain u = y·G/2 + G/2 + 1 (y in [-1,1] -> u in [1, G+1]): the fp32
+// thresholds thr_u = fp32(t·G/2 + G/2 + 1) are compared with the kernel's fp32 u.  Entry c (c = 0..G+2)
+// covers u in [c, c+1) and holds {fp32 bits of the one threshold that can fall in the cell widened
+// by a rounding margin (or +inf), count of thresholds below it}; for every u that lands in cell c,
+// #{k : thr_u[k] <= u} == base + (u >= thr).  Cell 0 (NaN and rounding below -1) yields index 0.
 struct Grid {
     int G = 0;
-    std::vector<uint32_t> entries;  // 2 words per cell
+    std::vector<float> thr_u;
+    std::vector<uint32_t> entries;  // 2 words per cell, G+3 cells
 };
-bool build_grid(const std::vector<float>& thr_f32, Grid& out);
+bool build_grid(const std::vector<double>& thr_y, Grid& out);
 
 // coordinates per dequantisation lookup for b bits
 inline int lut_group(int b) { return (b == 1 || b == 2 || b == 4) ? 8 / b : ((b == 3 || b == 5 || b == 6) ? 2 : 1); }

@@ -76,19 +76,14 @@ struct Blob {
 int build_tables(const tq_params* p, int device, DevTables* out) {  // caller holds g_mu
     const int d = p->d, b = p->b, m = p->m, H = p->n_heads, L = 1 << b, C = d / 4;
     const Codebook& cb = codebook(d, b);
-    std::vector<float> thr_f(L - 1), cent_f(L), cent_k(L);
-    for (int i = 0; i < L - 1; ++i) thr_f[i] = (float)cb.thr[i];
+    std::vector<float> cent_f(L), cent_k(L);
     for (int i = 0; i < L; ++i) {
         cent_f[i] = (float)cb.cent[i];
         cent_k[i] = cent_f[i] * 1024.0f;
     }
     Grid grid;
-    if (!build_grid(thr_f, grid) || grid.G > 4096) return TQ_EUNSUPPORTED;
-    std::vector<uint32_t> gw(2 * (grid.G + 3));
-    const float inf = INFINITY;
-    std::memcpy(&gw[0], &inf, 4);  // guard cell 0 (NaN inputs land here): idx 0
-    gw[1] = 0;
-    std::memcpy(&gw[2], grid.entries.data(), grid.entries.size() * 4);
+    if (!build_grid(cb.thr, grid)) return TQ_EUNSUPPORTED;
+    const std::vector<uint32_t>& gw = grid.entries;
 
     const int P = lut_group(b), NE = 1 << (P * b);
     std::vector<float> lut32((size_t)NE * P);
@@ -177,11 +172,17 @@ int get_tables(const tq_params* p, DevTables* out, int* num_cus) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_EHIP; }
 
-// attention split geometry (shared by the workspace query and the launch)
-int64_t attn_tokens_per_split(int64_t n_tokens) {
-    int64_t tps = 1024;
-    while ((n_tokens + tps - 1) / tps > 128) tps *= 2;
-    return tps;
+// attention split geometry (shared by the workspace query and the launch): about 4096 waves in
+// total, at least 256 tokens per split, token ranges a multiple of 32, at most 1024 splits
+int64_t attn_tokens_per_split(int64_t n_streams, int64_t n_tokens) {
+    int64_t ns = (4096 + n_streams - 1) / (n_streams > 0 ? n_streams : 1);
+    const int64_t max_ns = (n_tokens + 255) / 256;
+    if (ns > max_ns) ns = max_ns;
+    if (ns > 1024) ns = 1024;
+    if (ns < 1) ns = 1;
+    int64_t tps = (n_tokens + ns - 1) / ns;
+    tps = (tps + 31) / 32 * 32;
+    return tps < 32 ? 32 : tps;
 }
 
 struct AttnWs {
@@ -191,7 +192,8 @@ struct AttnWs {
 AttnWs attn_ws(const tq_params* pk, int32_t batch, int32_t hq, int32_t hkv, int64_t n_tokens) {
     AttnWs w{};
     const int64_t rows = (int64_t)batch * hq + 16;
-    w.n_split = (n_tokens + attn_tokens_per_split(n_tokens) - 1) / attn_tokens_per_split(n_tokens);
+    const int64_t tps = attn_tokens_per_split((int64_t)batch * hkv, n_tokens);
+    w.n_split = (n_tokens + tps - 1) / tps;
     if (w.n_split < 1) w.n_split = 1;
     const int64_t streams = (int64_t)batch * hkv;
     w.o_qrot = 0;
@@ -424,7 +426,7 @@ int tq_decode_attention(const tq_params* pk, const tq_params* pv, const void* q,
     a.n_kv_heads = n_kv_heads;
     a.group = n_q_heads / n_kv_heads;
     a.n_split = (int)w.n_split;
-    a.tokens_per_split = attn_tokens_per_split(n_tokens);
+    a.tokens_per_split = attn_tokens_per_split(streams, n_tokens);
     const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)pk->d);
     a.scale_log2 = scale * 1.4426950408889634f;
     a.k_off_idx = lk.off_idx;
