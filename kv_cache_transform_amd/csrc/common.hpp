@@ -45,6 +45,15 @@ __device__ __forceinline__ float dot2_bf16_nhi(uint32_t a, uint32_t b) {
     return r;
 }
 
+// (e0 - h.lo, e1 - h.hi) rounded to fp16 and packed, for a packed fp16 pair h and fp32 e0, e1
+// (v_fma_mix{lo,hi}_f16: fp32 fma with an fp16 operand, fp16 result into one half)
+__device__ __forceinline__ uint32_t sub_f16pair_from_f32(uint32_t h, float e0, float e1) {
+    uint32_t r = 0u;
+    asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "+v"(r) : "v"(h), "v"(e0));
+    asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(r) : "v"(h), "v"(e1));
+    return r;
+}
+
 // swap rows 1,3 of a with rows 0,2 of b (rows = 16-lane groups)
 __device__ __forceinline__ void xswap16(float& a, float& b) {
     auto r = __builtin_amdgcn_permlane16_swap(f2u(a), f2u(b), false, false);

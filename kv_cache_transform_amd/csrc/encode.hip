@@ -7,8 +7,8 @@
 // Search: a uniform grid over y in [-1,1] held in LDS maps y to the one threshold that can lie in
 // its cell plus the count of thresholds below; one compare finishes the search for any b.
 // S·e: v_mfma_f32_16x16x32_f16 with the lane's own residual as the B operand (lane l = vector
-// l%16, k-block l/16 matches the MFMA operand layout), e split exactly into fp16 hi + lo parts
-// (prescaled by 2^10), S stored as fp16 values; accumulation in fp32.
+// l%16, k-block l/16 matches the MFMA operand layout), e split into fp16 hi + lo parts (prescaled
+// by 2^14, |e| 2^14 < 2^15 always), S stored as fp16 values; accumulation in fp32.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -168,7 +168,7 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
                 const uint32_t idx = base + (u >= u2f(thr) ? 1u : 0u);
                 put_bits<B>(pk, s * B, idx);
                 if constexpr (QJL) {
-                    const float e = fmaf(y, 1024.0f, -lds_c[idx]);   // 2^10 (y - c[idx])
+                    const float e = fmaf(y, 16384.0f, -lds_c[idx]);  // 2^14 (y - c[idx])
                     x[s] = e;
                     e2 = fmaf(e, e, e2);
                 }
@@ -182,16 +182,16 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
                 // B operands: lane's residual slots [8k, 8k+8) for k-step k, exact hi + lo split
 #pragma unroll
                 for (int k = 0; k < C / 8; ++k) {
+                    u32x4 hv, lv;
 #pragma unroll
                     for (int u = 0; u < 4; ++u) {
                         const float e0 = x[8 * k + 2 * u], e1 = x[8 * k + 2 * u + 1];
-                        const half2v h = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(e0, e1));
-                        const half2v l = __builtin_bit_cast(half2v, __builtin_amdgcn_cvt_pkrtz(e0 - (float)h[0], e1 - (float)h[1]));
-                        bh[gi][k][2 * u] = h[0];
-                        bh[gi][k][2 * u + 1] = h[1];
-                        bl[gi][k][2 * u] = l[0];
-                        bl[gi][k][2 * u + 1] = l[1];
+                        const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(e0, e1));
+                        hv[u] = h;
+                        lv[u] = sub_f16pair_from_f32(h, e0, e1);
                     }
+                    bh[gi][k] = __builtin_bit_cast(half8, hv);
+                    bl[gi][k] = __builtin_bit_cast(half8, lv);
                 }
             }
         }
@@ -199,45 +199,48 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
         if constexpr (QJL) {
             const _Float16* Sg = S_LDS ? (lds_S + g * C) : (a.t.S + (int64_t)head * m * D + g * C);
             const int rs = S_LDS ? SP : D;
-            uint32_t bits[NG];
+            // sketch bits of lane part g: rows [g m/4, (g+1) m/4), 32 per word; within a word the
+            // 8 tiles are visited in descending order and each z shifts its sign bit in at bit 0
+            // (alignbit), so bit p ends up holding row p; the word is inverted at the end (z >= 0).
+            const int nbits = m >> 2;
+            for (int wb = 0; wb < nbits; wb += 32) {
+                const int nt = (nbits - wb) >= 32 ? 8 : ((nbits - wb) >> 2);
+                uint32_t bits[NG];
 #pragma unroll
-            for (int gi = 0; gi < NG; ++gi) bits[gi] = 0u;
-            const int ntile = m >> 4;
-            for (int tau = 0; tau < ntile; ++tau) {
-                floatx4 acc[NG];
+                for (int gi = 0; gi < NG; ++gi) bits[gi] = 0u;
 #pragma unroll
-                for (int gi = 0; gi < NG; ++gi) acc[gi] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-                const _Float16* Srow = Sg + (row_base + 4 * tau) * rs;
+                for (int tt = 7; tt >= 0; --tt) {
+                    if (tt < nt) {
+                        const int tau = (wb >> 2) + tt;
+                        floatx4 acc[NG];
 #pragma unroll
-                for (int k = 0; k < C / 8; ++k) {
-                    const half8 A = *reinterpret_cast<const half8*>(Srow + 8 * k);
+                        for (int gi = 0; gi < NG; ++gi) acc[gi] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+                        const _Float16* Srow = Sg + (row_base + 4 * tau) * rs;
 #pragma unroll
-                    for (int gi = 0; gi < NG; ++gi) {
-                        acc[gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bh[gi][k], acc[gi], 0, 0, 0);
-                        acc[gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bl[gi][k], acc[gi], 0, 0, 0);
+                        for (int k = 0; k < C / 8; ++k) {
+                            const half8 A = *reinterpret_cast<const half8*>(Srow + 8 * k);
+#pragma unroll
+                            for (int gi = 0; gi < NG; ++gi) {
+                                acc[gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bh[gi][k], acc[gi], 0, 0, 0);
+                                acc[gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bl[gi][k], acc[gi], 0, 0, 0);
+                            }
+                        }
+#pragma unroll
+                        for (int gi = 0; gi < NG; ++gi)
+#pragma unroll
+                            for (int i = 3; i >= 0; --i) bits[gi] = __builtin_amdgcn_alignbit(bits[gi], f2u(acc[gi][i]), 31);
                     }
                 }
-                const int pos = (4 * tau) & 31;
-                const bool word_done = (pos == 28) || (tau == ntile - 1);
+                const int nb = nt >> 1;                       // bytes in this word
 #pragma unroll
                 for (int gi = 0; gi < NG; ++gi) {
-                    uint32_t bw = bits[gi];
-                    bw |= (acc[gi][0] >= 0.0f ? 1u : 0u) << pos;
-                    bw |= (acc[gi][1] >= 0.0f ? 1u : 0u) << (pos + 1);
-                    bw |= (acc[gi][2] >= 0.0f ? 1u : 0u) << (pos + 2);
-                    bw |= (acc[gi][3] >= 0.0f ? 1u : 0u) << (pos + 3);
-                    if (word_done) {
-                        if (validv[gi]) {
-                            uint8_t* dst = a.packed + a.off_sketch + vecv[gi] * (int64_t)(m / 8) + g * (m / 32) +
-                                           ((4 * tau) >> 5) * 4;
-                            const int nb = (4 * (tau + 1) - ((4 * tau) & ~31)) / 8;   // bytes filled
-                            if (nb == 4 && (m & 127) == 0) *reinterpret_cast<uint32_t*>(dst) = bw;
-                            else if (nb == 2 && (m & 63) == 0) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)bw;
-                            else for (int q = 0; q < nb; ++q) dst[q] = (uint8_t)(bw >> (8 * q));
-                        }
-                        bw = 0u;
+                    if (validv[gi]) {
+                        const uint32_t bw = ~bits[gi];
+                        uint8_t* dst = a.packed + a.off_sketch + vecv[gi] * (int64_t)(m / 8) + g * (m / 32) + (wb >> 3);
+                        if (nb == 4 && (m & 127) == 0) *reinterpret_cast<uint32_t*>(dst) = bw;
+                        else if (nb == 2 && (m & 63) == 0) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)bw;
+                        else for (int q = 0; q < nb; ++q) dst[q] = (uint8_t)(bw >> (8 * q));
                     }
-                    bits[gi] = bw;
                 }
             }
 #pragma unroll
@@ -245,7 +248,7 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
                 const float e2 = sum4(e2v[gi]);
                 if (validv[gi] && g == 0)
                     *reinterpret_cast<_Float16*>(a.packed + a.off_rnorm + vecv[gi] * 2) =
-                        (_Float16)(sqrtf(e2) * (1.0f / 1024.0f));
+                        (_Float16)(sqrtf(e2) * (1.0f / 16384.0f));
             }
         }
     }

@@ -12,7 +12,7 @@ struct DevTables {
     int G = 0;                         // search grid cells
     const uint32_t* grid = nullptr;    // (G+2) x {thr fp32 bits, base}
     const float* cent = nullptr;       // 2^b centroids (fp32)
-    const float* cent_x1024 = nullptr; // 2^b centroids x 1024 (fp32, exact scaling)
+    const float* cent_x1024 = nullptr; // 2^b centroids x 2^14 (fp32, exact scaling)
     const float* lut_f32 = nullptr;    // dequant LUT: 2^(P b) entries of P fp32 (P = lut_group(b))
     const _Float16* lut_f16 = nullptr; // same in fp16
     const float* signs_slot = nullptr; // [head][4][d/4] ±1 of coordinate in_coord(d, s, g)

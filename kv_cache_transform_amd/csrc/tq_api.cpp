@@ -79,7 +79,7 @@ int build_tables(const tq_params* p, int device, DevTables* out) {  // caller ho
     std::vector<float> cent_f(L), cent_k(L);
     for (int i = 0; i < L; ++i) {
         cent_f[i] = (float)cb.cent[i];
-        cent_k[i] = cent_f[i] * 1024.0f;
+        cent_k[i] = cent_f[i] * 16384.0f;
     }
     Grid grid;
     if (!build_grid(cb.thr, grid)) return TQ_EUNSUPPORTED;

@@ -231,6 +231,18 @@ def quantise(y: np.ndarray, thresholds: np.ndarray) -> np.ndarray:
     return np.searchsorted(thresholds, y, side="right").astype(np.int64)
 
 
+def boundary_distance(y: np.ndarray, thresholds: np.ndarray, idx: np.ndarray | None = None) -> np.ndarray:
+    """min_i |y - t_i| over the sorted thresholds: attained at a neighbour of the insertion point
+    idx = #{t_i <= y}, i.e. at t[idx-1] or t[idx]."""
+    if idx is None:
+        idx = quantise(y, thresholds)
+    tp = np.concatenate((thresholds, [np.inf]))
+    lo = np.abs(y - tp[np.maximum(idx - 1, 0)])
+    lo = np.where(idx > 0, lo, np.inf)
+    hi = np.abs(tp[idx] - y)
+    return np.minimum(lo, hi)
+
+
 def encode(x: np.ndarray, s: np.ndarray, thresholds: np.ndarray, centroids: np.ndarray,
            S: np.ndarray | None = None) -> dict:
     """Encode rows of x (N, d) that share one RNG head.
@@ -243,8 +255,8 @@ def encode(x: np.ndarray, s: np.ndarray, thresholds: np.ndarray, centroids: np.n
     u = np.where(n[:, None] > 0, x / safe[:, None], 0.0)
     y = rotate(u, s)
     idx = quantise(y, thresholds)
-    dist = np.min(np.abs(y[..., None] - thresholds[None, None, :]), axis=-1)
-    out = {"idx": idx, "n16": fp16_rne(n), "flag": dist < FLAG_TOL, "y": y, "norm": n}
+    out = {"idx": idx, "n16": fp16_rne(n), "flag": boundary_distance(y, thresholds, idx) < FLAG_TOL,
+           "y": y, "norm": n}
     if S is not None:
         e = y - centroids[idx]
         z = e @ np.asarray(S, dtype=np.float64).T

@@ -85,6 +85,14 @@ def test_brute_force_scalar_argmin_d8(b):
     assert np.array_equal(am, r["idx"])
 
 
+@pytest.mark.parametrize("b", [1, 3, 6])
+def test_boundary_distance_equals_brute_force_minimum(b):
+    t, _ = O.lloyd_max(64, b)
+    y = np.concatenate([np.random.default_rng(b).uniform(-1, 1, 5000), t, t + 1e-9, t - 1e-9, [-1.0, 1.0, 0.0]])
+    brute = np.min(np.abs(y[:, None] - t[None, :]), axis=1)
+    assert np.array_equal(O.boundary_distance(y, t), brute)
+
+
 def test_flags_mark_exactly_the_near_boundary_coordinates():
     d, b = 64, 3
     t, c = O.lloyd_max(d, b)
