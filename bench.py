@@ -137,6 +137,8 @@ def main():
                              "hbm_frac": round(dec_alg / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     del xh
 
+    copy = copy_ceiling(torch, dev, stream)
+
     dom = max(names, key=lambda n: kms[n])
     roof = {"bound": "hbm", "kernel": dom, "achieved": kern[dom]["achieved_GBs"], "peak": HBM_PEAK_GBS,
             "unit": "GB/s", "frac": kern[dom]["hbm_frac"], "traffic": None,
@@ -159,8 +161,30 @@ def main():
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kern,
+        "copy_ceiling": copy,
     }
     print(json.dumps(line))
+
+
+def copy_ceiling(torch, dev, stream, n_bytes: int = 1 << 30, reps: int = 5):
+    """Practical HBM ceiling: torch's device copy of an n_bytes buffer (read n_bytes + write n_bytes),
+    timed with HIP events over `reps` launches.  Its hardware byte counters also calibrate the
+    FETCH_SIZE / WRITE_SIZE figures of the codec kernels."""
+    src = torch.empty(n_bytes // 2, dtype=torch.bfloat16, device=dev).fill_(1.0)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del src, dst
+    return {"kernel": "torch copy_ of a 1 GiB bf16 buffer", "bytes_per_launch": 2 * n_bytes,
+            "ms": round(ms, 4), "GBs": round(2 * n_bytes / (ms * 1e-3) / 1e9, 1),
+            "frac_of_peak": round(2 * n_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
 def cpu_baseline(K, V, q, pk, pv, ck, cv, B, Hq, Hkv, N, d, budget_s):

@@ -9,20 +9,25 @@
 // S·e: v_mfma_f32_16x16x32_f16 with the lane's own residual as the B operand (lane l = vector
 // l%16, k-block l/16 matches the MFMA operand layout), e split into fp16 hi + lo parts (prescaled
 // by 2^14, |e| 2^14 < 2^15 always), S stored as fp16 values; accumulation in fp32.
+#include <map>
+#include <mutex>
+#include <type_traits>
+#include <utility>
+
 #include "common.hpp"
 #include "kernels.hpp"
 
 namespace tq {
 
 template <int D, int B, bool QJL, bool BF16, bool S_LDS>
-__global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
+__global__ __launch_bounds__(256, ((D > 128 && (QJL || !BF16)) || (QJL && !BF16) ? 1 : 3)) void encode_kernel(EncodeArgs a) {
     constexpr int C = D / 4, R = D / 16, L = 1 << B;
     constexpr int NW = (C * B + 31) / 32;          // packed words per lane
     constexpr int CB = C * B / 8;                   // packed bytes per lane
     constexpr int CA = cmin(pow2_align(CB), 16);
     constexpr float kInvSqrtD = D == 64 ? 0.125f : (D == 128 ? 0.08838834764831845f : 0.0625f);
-    constexpr int NG = (QJL && D <= 128) ? 2 : 1;   // 16-vector groups per pass (S-tile reuse)
-    constexpr int SP = D + 8;                       // padded LDS row of S (halves)
+    constexpr int NG = (QJL && D <= 128 && !BF16) ? 2 : 1;   // 16-vector groups per pass (S-tile reuse)
+    constexpr int KS = D / 32;                      // k-steps of 32 coordinates
 
     // ---- block = one stream's tile range; the RNG head is block-uniform -----------------------
     const int64_t st = blockIdx.x / a.blocks_per_stream;
@@ -34,19 +39,69 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
 
     extern __shared__ uint32_t lds[];
     const int G = a.t.G;
-    const int ngw = 2 * (G + 3);
-    for (int i = threadIdx.x; i < ngw; i += blockDim.x) lds[i] = a.t.grid[i];
+    // search grid, replicated 2^rl times with the copies interleaved per cell, so lanes that use
+    // different copies read different banks: cell c of copy r = words 2 (c 2^rl + r) + {0, 1}
+    const int rl = a.grid_rep_log2;
+    const int ngw = (2 * (G + 3)) << rl;
+    for (int i = threadIdx.x; i < ((G + 3) << rl); i += blockDim.x) {
+        const int c = i >> rl;
+        lds[2 * i] = a.t.grid[2 * c];
+        lds[2 * i + 1] = a.t.grid[2 * c + 1];
+    }
     float* lds_c = reinterpret_cast<float*>(lds + ngw);
-    _Float16* lds_S = reinterpret_cast<_Float16*>(lds + ngw + L + ((ngw + L) & 3 ? 4 - ((ngw + L) & 3) : 0));
+    constexpr int NKB = D / 32;                     // K blocks of the 32-point transform
+    constexpr int NAW = BF16 ? 2 * NKB * 64 * 4 : 0; // LDS words of the signed A tiles
+    const int a_off = (ngw + L + 3) & ~3;
+    u32x4* lds_A = reinterpret_cast<u32x4*>(lds + a_off);
+    _Float16* lds_S = reinterpret_cast<_Float16*>(lds + a_off + NAW);
     if constexpr (QJL) {
         for (int i = threadIdx.x; i < L; i += blockDim.x) lds_c[i] = a.t.cent_x1024[i];
         if constexpr (S_LDS) {
+            // S in the order the MFMA A operand reads it (see the sketch loop): the 16-byte piece
+            // of lane l for row tile tau and k-step k sits at piece index (tau KS + k) 64 + l, so
+            // every A read is one contiguous 1 KiB wave access.  Lane l = rho + 16 gp reads row
+            // (rho/4)(m/4) + 4 tau + rho%4, columns gp C + 8k .. +8.
             const u32x4* src = reinterpret_cast<const u32x4*>(a.t.S + (int64_t)head * m * D);
+            u32x4* dst = reinterpret_cast<u32x4*>(lds_S);
             const int n16 = m * D / 8;             // 16-byte pieces
+            const int mq = m >> 2;
             for (int i = threadIdx.x; i < n16; i += blockDim.x) {
                 const int row = i / (D / 8), col = i - row * (D / 8);
-                *reinterpret_cast<u32x4*>(lds_S + row * SP + col * 8) = src[i];
+                const int q = row / mq, rem = row - q * mq;
+                const int tau = rem >> 2, rh = 4 * q + (rem & 3);
+                const int gp = col / KS, k = col - gp * KS;
+                dst[(tau * KS + k) * 64 + rh + 16 * gp] = src[i];
             }
+        }
+    }
+    // bf16 input: the Hadamard transform over the 5 index bits {0,1,2, n-2, n-1} (n = log2 d) is a
+    // dense 32-point block, run as v_mfma_f32_16x16x32_bf16 with the ±1 matrix as the A operand
+    // (exact: ±1 and the bf16 inputs are exact, accumulation in fp32); the remaining middle bits
+    // are radix-2 butterflies in registers.  Lane part g holds coordinates [g C, g C + C) both on
+    // input (K block kb = 8 coordinates g C + 8 kb + jj) and on output (slot s = coordinate g C + s).
+    // A tile (h, kb) of lane l holds row 4 mg + mi = l % 16, columns 8 (l/16) + jj:
+    //   H[output (mg, h, mi)][input (l/16, jj)] * sign of input coordinate (l/16) C + 8 kb + jj,
+    // with output coordinate bits {n-2,n-1} = mg, bit 2 = h, bits {0,1} = mi.  The random signs of
+    // the head are folded in, so the tiles are built per block in LDS (one 16-byte entry per lane).
+    if constexpr (BF16) {
+        for (int e = threadIdx.x; e < 2 * NKB * 64; e += blockDim.x) {
+            const int l = e & 63, tile = e >> 6, h = tile / NKB, kb = tile - h * NKB;
+            const int lg = l >> 4, mi = l & 3, mg = (l >> 2) & 3;
+            const float* sh = a.t.signs + (int64_t)head * D + lg * C + 8 * kb;
+            u32x4 wv;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                uint32_t w2 = 0u;
+#pragma unroll
+                for (int q = 0; q < 2; ++q) {
+                    const int jj = 2 * t + q;
+                    const uint32_t par = (uint32_t)((__builtin_popcount(mi & jj & 3) + h * (jj >> 2) +
+                                                     __builtin_popcount(mg & lg)) & 1) ^ (f2u(sh[jj]) >> 31);
+                    w2 |= (0x3f80u | (par << 15)) << (16 * q);
+                }
+                wv[t] = w2;
+            }
+            lds_A[e] = wv;
         }
     }
     __syncthreads();
@@ -57,39 +112,41 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
     const float gA = 0.5f * (float)G;
     const float gB = 0.5f * (float)G + 1.0f;       // entry 0 is a guard cell
 
-    uint32_t Ps[BF16 ? C / 2 : 1];
     float sg[BF16 ? 1 : C];
-    {
+    if constexpr (!BF16) {
         const float* ss = a.t.signs_slot + ((int64_t)head * 4 + g) * C;
-        if constexpr (BF16) {
 #pragma unroll
-            for (int k = 0; k < C / 2; ++k) Ps[k] = (f2u(ss[2 * k]) >> 16) | (f2u(ss[2 * k + 1]) & 0xffff0000u);
-        } else {
-#pragma unroll
-            for (int s = 0; s < C; ++s) sg[s] = ss[s];
-        }
+        for (int s = 0; s < C; ++s) sg[s] = ss[s];
     }
     // QJL A-operand rows: MFMA row slot rho of tile tau is sketch row (rho/4)*(m/4) + 4 tau + rho%4,
     // so lane part g collects rows [g m/4, (g+1) m/4), a contiguous bit chunk of the sketch.
     const int rho = lane & 15;
     const int row_base = (rho >> 2) * (m >> 2) + (rho & 3);
+    const uint32_t goff = (uint32_t)(lane & ((1 << rl) - 1)) << 3;   // byte offset of the lane's grid copy
 
-    // raw input words of one 16-vector group (runs of R coordinates, see common.hpp)
+    // raw input words of one 16-vector group: bf16 = the lane's C contiguous coordinates; fp32 =
+    // runs of R coordinates in the i(s, g) order of the butterfly network (see common.hpp)
     constexpr int NIW = BF16 ? C / 2 : C;
     auto load_group = [&](uint32_t (&w)[NIW], int64_t tile) {
         const int64_t tok = tile * 16 + v;
         const bool valid = tile < tb1 && tok < a.n_tokens;
         const int64_t vec = st * a.n_tokens + (valid ? tok : 0);
-        constexpr int ES = BF16 ? 2 : 4;              // element size
-        constexpr int RB = ES * R;                    // bytes per run
-        constexpr int RA = cmin(pow2_align(RB), 16);
-        const uint8_t* base = reinterpret_cast<const uint8_t*>(a.x) + vec * (int64_t)(ES * D) + ES * g * R;
+        if constexpr (BF16) {
+            // a vector past the end reads token 0 of the stream (in bounds); nothing of it is stored,
+            // and every MFMA column / 4-lane reduction stays within one vector
+            const uint8_t* base = reinterpret_cast<const uint8_t*>(a.x) + vec * (int64_t)(2 * D) + 2 * g * C;
+            load_bytes<2 * C, 16>(base, w);
+        } else {
+            constexpr int RB = 4 * R;                     // bytes per run
+            constexpr int RA = cmin(pow2_align(RB), 16);
+            const uint8_t* base = reinterpret_cast<const uint8_t*>(a.x) + vec * (int64_t)(4 * D) + 4 * g * R;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            if (valid) load_bytes<RB, RA>(base + r * (ES * D / 4), &w[r * (NIW / 4)]);
-            else {
+            for (int r = 0; r < 4; ++r) {
+                if (valid) load_bytes<RB, RA>(base + r * D, &w[r * (NIW / 4)]);
+                else {
 #pragma unroll
-                for (int k = 0; k < NIW / 4; ++k) w[r * (NIW / 4) + k] = 0u;
+                    for (int k = 0; k < NIW / 4; ++k) w[r * (NIW / 4) + k] = 0u;
+                }
             }
         }
     };
@@ -99,15 +156,8 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
 
 #pragma unroll 1
     for (int64_t t = tb0 + wave * NG; t < tb1; t += 4 * NG) {
-        uint32_t cur[NG][NIW];
-#pragma unroll
-        for (int gi = 0; gi < NG; ++gi)
-#pragma unroll
-            for (int k = 0; k < NIW; ++k) cur[gi][k] = nxt[gi][k];
-        if (t + 4 * NG < tb1) {            // issue the next pass's loads before this pass's math
-#pragma unroll
-            for (int gi = 0; gi < NG; ++gi) load_group(nxt[gi], t + 4 * NG + gi);
-        }
+        // keep the LDS operand tables in LDS (re-read per pass) instead of pinned in registers
+        asm volatile("" ::: "memory");
         half8 bh[NG][QJL ? C / 8 : 1], bl[NG][QJL ? C / 8 : 1];
         float e2v[NG];
         bool validv[NG];
@@ -123,16 +173,31 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
             // ---- sign, first butterfly stage, norm ----------------------------------------------
             float x[C];
             float n2 = 0.0f;
-            const uint32_t (&w)[NIW] = cur[gi];
+            uint32_t (&w)[NIW] = nxt[gi];
             if constexpr (BF16) {
 #pragma unroll
                 for (int k = 0; k < C / 2; ++k) {
                     const bf16x2 wv = __builtin_bit_cast(bf16x2, w[k]);
-                    x[2 * k] = dot2_bf16(w[k], Ps[k]);          // s_i x_i + s_{i+1} x_{i+1}
-                    x[2 * k + 1] = dot2_bf16_nhi(w[k], Ps[k]);  // s_i x_i - s_{i+1} x_{i+1}
                     n2 = __builtin_amdgcn_fdot2_f32_bf16(wv, wv, n2, false);
                 }
-                fwht_slots<C, 2>(x);
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb) {
+                    const bf16x8 Bv = __builtin_bit_cast(bf16x8, u32x4{w[4 * kb], w[4 * kb + 1], w[4 * kb + 2], w[4 * kb + 3]});
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const floatx4 r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                            __builtin_bit_cast(bf16x8, lds_A[(h * NKB + kb) * 64 + lane]), Bv,
+                            floatx4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) x[8 * kb + 4 * h + i] = r[i];
+                    }
+                }
+                // last reads of the raw words: the next pass's loads may reuse their registers
+#pragma unroll
+                for (int k = 0; k < NIW; ++k) asm volatile("" ::"v"(w[k]) : "memory");
+                asm volatile("" ::"v"(n2) : "memory");
+                if (t + 4 * NG < tb1) load_group(nxt[gi], t + 4 * NG + gi);
+                fwht_slots<C, 8>(x);
             } else {
 #pragma unroll
                 for (int s = 0; s < C; ++s) {
@@ -140,13 +205,15 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
                     n2 = fmaf(xv, xv, n2);
                     x[s] = xv * sg[s];
                 }
+                if (t + 4 * NG < tb1) load_group(nxt[gi], t + 4 * NG + gi);
                 fwht_slots<C, 1>(x);
+                fwht_cross<C>(x);
             }
-            fwht_cross<C>(x);
             n2 = sum4(n2);
             const float n = sqrtf(n2);
             const float sc = n > 0.0f ? kInvSqrtD / n : 0.0f;
             const float sA = sc * gA;
+            const float sE = sc * 16384.0f;
 
             // ---- scalar quantiser + pack (and the scaled residual for QJL) ----------------------
             // The grid lives in the affine domain u = y G/2 + G/2 + 1; thresholds are stored there.
@@ -156,19 +223,14 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
             float e2 = 0.0f;
 #pragma unroll
             for (int s = 0; s < C; ++s) {
-                float y, u;
-                if constexpr (QJL) {
-                    y = x[s] * sc;
-                    u = fmaf(y, gA, gB);
-                } else {
-                    u = fmaf(x[s], sA, gB);
-                }
+                const float u = fmaf(x[s], sA, gB);
                 const uint32_t cell = (uint32_t)u;
-                const uint32_t thr = lds[2 * cell], base = lds[2 * cell + 1];
+                const u32x2 ent = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(lds) + ((cell << (3 + rl)) + goff));
+                const uint32_t thr = ent[0], base = ent[1];
                 const uint32_t idx = base + (u >= u2f(thr) ? 1u : 0u);
                 put_bits<B>(pk, s * B, idx);
                 if constexpr (QJL) {
-                    const float e = fmaf(y, 16384.0f, -lds_c[idx]);  // 2^14 (y - c[idx])
+                    const float e = fmaf(x[s], sE, -lds_c[idx]);  // 2^14 (y - c[idx])
                     x[s] = e;
                     e2 = fmaf(e, e, e2);
                 }
@@ -197,28 +259,28 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
         }
 
         if constexpr (QJL) {
-            const _Float16* Sg = S_LDS ? (lds_S + g * C) : (a.t.S + (int64_t)head * m * D + g * C);
-            const int rs = S_LDS ? SP : D;
+            const _Float16* Sg = S_LDS ? (lds_S + 8 * lane) : (a.t.S + ((int64_t)head * m + row_base) * D + g * C);
             // sketch bits of lane part g: rows [g m/4, (g+1) m/4), 32 per word; within a word the
             // 8 tiles are visited in descending order and each z shifts its sign bit in at bit 0
             // (alignbit), so bit p ends up holding row p; the word is inverted at the end (z >= 0).
-            const int nbits = m >> 2;
-            for (int wb = 0; wb < nbits; wb += 32) {
-                const int nt = (nbits - wb) >= 32 ? 8 : ((nbits - wb) >> 2);
+            // Full words run branch-free; a trailing partial word (m/4 not a multiple of 32) has
+            // nt < 8 tiles.
+            auto sketch_word = [&](int wb, int nt, auto full) {
+                constexpr bool FULL = decltype(full)::value;
                 uint32_t bits[NG];
 #pragma unroll
                 for (int gi = 0; gi < NG; ++gi) bits[gi] = 0u;
 #pragma unroll
                 for (int tt = 7; tt >= 0; --tt) {
-                    if (tt < nt) {
+                    if (FULL || tt < nt) {
                         const int tau = (wb >> 2) + tt;
                         floatx4 acc[NG];
 #pragma unroll
                         for (int gi = 0; gi < NG; ++gi) acc[gi] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-                        const _Float16* Srow = Sg + (row_base + 4 * tau) * rs;
 #pragma unroll
-                        for (int k = 0; k < C / 8; ++k) {
-                            const half8 A = *reinterpret_cast<const half8*>(Srow + 8 * k);
+                        for (int k = 0; k < KS; ++k) {
+                            const half8 A = *reinterpret_cast<const half8*>(
+                                S_LDS ? Sg + (tau * KS + k) * 512 : Sg + 4 * tau * D + 8 * k);
 #pragma unroll
                             for (int gi = 0; gi < NG; ++gi) {
                                 acc[gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bh[gi][k], acc[gi], 0, 0, 0);
@@ -231,18 +293,21 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
                             for (int i = 3; i >= 0; --i) bits[gi] = __builtin_amdgcn_alignbit(bits[gi], f2u(acc[gi][i]), 31);
                     }
                 }
-                const int nb = nt >> 1;                       // bytes in this word
+                const int nb = FULL ? 4 : (nt >> 1);          // bytes in this word
 #pragma unroll
                 for (int gi = 0; gi < NG; ++gi) {
                     if (validv[gi]) {
                         const uint32_t bw = ~bits[gi];
                         uint8_t* dst = a.packed + a.off_sketch + vecv[gi] * (int64_t)(m / 8) + g * (m / 32) + (wb >> 3);
-                        if (nb == 4 && (m & 127) == 0) *reinterpret_cast<uint32_t*>(dst) = bw;
+                        if (FULL && (m & 127) == 0) *reinterpret_cast<uint32_t*>(dst) = bw;
                         else if (nb == 2 && (m & 63) == 0) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)bw;
                         else for (int q = 0; q < nb; ++q) dst[q] = (uint8_t)(bw >> (8 * q));
                     }
                 }
-            }
+            };
+            const int nbits = m >> 2;
+            for (int wb = 0; wb + 32 <= nbits; wb += 32) sketch_word(wb, 8, std::true_type{});
+            if (nbits & 31) sketch_word(nbits & ~31, (nbits & 31) >> 2, std::false_type{});
 #pragma unroll
             for (int gi = 0; gi < NG; ++gi) {
                 const float e2 = sum4(e2v[gi]);
@@ -254,23 +319,48 @@ __global__ __launch_bounds__(256) void encode_kernel(EncodeArgs a) {
     }
 }
 
+// resident blocks per CU of kernel k at `lds` bytes of dynamic LDS (cached per kernel and size)
+static int blocks_per_cu(const void* k, size_t lds) {
+    static std::mutex mu;
+    static std::map<std::pair<const void*, size_t>, int> cache;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = cache.find({k, lds});
+    if (it != cache.end()) return it->second;
+    int n = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, 256, lds) != hipSuccess || n < 1) n = 1;
+    cache[{k, lds}] = n;
+    return n;
+}
+
 template <int D, int B, bool QJL, bool BF16>
 static hipError_t launch_one(const EncodeArgs& a, int num_cus, hipStream_t s) {
     EncodeArgs b = a;
-    const int64_t target = (int64_t)num_cus * 4;
+    const int L = 1 << B;
+    // grid copies: up to 16 (8 with the sketch, whose S tile also lives in LDS) within 16 KiB / 8 KiB
+    const size_t grid_bytes = (size_t)(a.t.G + 3) * 8;
+    int rl = QJL ? 3 : 4;
+    while (rl > 0 && (grid_bytes << rl) > (QJL ? 8192u : 16384u)) --rl;
+    b.grid_rep_log2 = rl;
+    const size_t head_bytes = (grid_bytes << rl) + (size_t)(L + 4) * 4 + (BF16 ? (size_t)2 * (D / 32) * 64 * 16 : 0);
+    const size_t s_bytes = (size_t)a.t.m * D * 2;
+    const bool s_lds = QJL && (D <= 128 || s_bytes <= 65536);   // m <= d: always for d <= 128
+    const size_t lds = head_bytes + (s_lds ? s_bytes : 0);
+    const void* kern = s_lds ? reinterpret_cast<const void*>(&encode_kernel<D, B, QJL, BF16, true>)
+                             : reinterpret_cast<const void*>(&encode_kernel<D, B, QJL, BF16, (D <= 128)>);
+    // one wave of blocks: as many 256-thread blocks as fit on every CU at once
+    const int64_t target = (int64_t)num_cus * blocks_per_cu(kern, lds);
     int64_t bps = (target + a.n_streams - 1) / a.n_streams;
     if (bps > a.tiles_per_stream) bps = a.tiles_per_stream;
     if (bps < 1) bps = 1;
     b.blocks_per_stream = bps;
     b.tiles_per_block = (a.tiles_per_stream + bps - 1) / bps;
-    const int L = 1 << B;
-    const size_t head_bytes = (size_t)(2 * (a.t.G + 3) + L + 4) * 4;
-    const size_t s_bytes = (size_t)a.t.m * (D + 8) * 2;
-    const bool s_lds = QJL && s_bytes <= 65536;
-    const size_t lds = head_bytes + (s_lds ? s_bytes : 0);
     const dim3 grid((unsigned)(a.n_streams * bps));
-    if (s_lds) hipLaunchKernelGGL((encode_kernel<D, B, QJL, BF16, true>), grid, dim3(256), lds, s, b);
-    else hipLaunchKernelGGL((encode_kernel<D, B, QJL, BF16, false>), grid, dim3(256), lds, s, b);
+    if constexpr (D <= 128) {
+        hipLaunchKernelGGL((encode_kernel<D, B, QJL, BF16, true>), grid, dim3(256), lds, s, b);
+    } else {
+        if (s_lds) hipLaunchKernelGGL((encode_kernel<D, B, QJL, BF16, true>), grid, dim3(256), lds, s, b);
+        else hipLaunchKernelGGL((encode_kernel<D, B, QJL, BF16, false>), grid, dim3(256), lds, s, b);
+    }
     return hipGetLastError();
 }
 

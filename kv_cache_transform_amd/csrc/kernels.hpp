@@ -31,6 +31,7 @@ struct EncodeArgs {
     int64_t tiles_per_wave;
     int64_t blocks_per_stream; // grid = n_streams * blocks_per_stream
     int64_t tiles_per_block;
+    int grid_rep_log2;         // the search grid is held in LDS 2^grid_rep_log2 times (bank spread)
     DevTables t;
 };
 
