@@ -328,21 +328,24 @@ def pack_tensor(d: int, b: int, m: int, n_streams: int, n_tokens: int, enc: list
 
 
 def unpack_tensor(buf: np.ndarray, d: int, b: int, m: int, n_streams: int, n_tokens: int,
-                  streams=None) -> list[dict]:
-    """Read planes back (for the listed streams): idx, n16, and with m>0 sigma, r16."""
+                  streams=None, token_range=None) -> list[dict]:
+    """Read planes back (for the listed streams, optionally only tokens [t0, t1) of each):
+    idx, n16, and with m>0 sigma, r16."""
     lay = layout(d, b, m, n_streams, n_tokens)
     buf = np.asarray(buf, dtype=np.uint8)
     ib, sb = lay["idx_bytes_per_vec"], lay["sketch_bytes_per_vec"]
+    t0, t1 = (0, n_tokens) if token_range is None else token_range
+    n = t1 - t0
     out = []
     for st in (range(n_streams) if streams is None else streams):
-        v0 = st * n_tokens
-        r = {"idx": unpack_bits(buf[lay["off_idx"] + v0 * ib: lay["off_idx"] + (v0 + n_tokens) * ib]
-                                .reshape(n_tokens, ib), b, d),
-             "n16": buf[lay["off_norm"] + 2 * v0: lay["off_norm"] + 2 * (v0 + n_tokens)].view(np.float16)}
+        v0 = st * n_tokens + t0
+        r = {"idx": unpack_bits(buf[lay["off_idx"] + v0 * ib: lay["off_idx"] + (v0 + n) * ib]
+                                .reshape(n, ib), b, d),
+             "n16": buf[lay["off_norm"] + 2 * v0: lay["off_norm"] + 2 * (v0 + n)].view(np.float16)}
         if m > 0:
-            r["sigma"] = unpack_bits(buf[lay["off_sketch"] + v0 * sb: lay["off_sketch"] + (v0 + n_tokens) * sb]
-                                     .reshape(n_tokens, sb), 1, m).astype(bool)
-            r["r16"] = buf[lay["off_rnorm"] + 2 * v0: lay["off_rnorm"] + 2 * (v0 + n_tokens)].view(np.float16)
+            r["sigma"] = unpack_bits(buf[lay["off_sketch"] + v0 * sb: lay["off_sketch"] + (v0 + n) * sb]
+                                     .reshape(n, sb), 1, m).astype(bool)
+            r["r16"] = buf[lay["off_rnorm"] + 2 * v0: lay["off_rnorm"] + 2 * (v0 + n)].view(np.float16)
         out.append(r)
     return out
 

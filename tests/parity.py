@@ -49,12 +49,14 @@ def fp16_ulp_diff(a, b):
     return np.abs(a16 - b16)
 
 
-def check_encode(tb: Tables, x64: np.ndarray, buf: np.ndarray, streams=None, n_streams=None) -> dict:
-    """x64: [S_sel, N, d] fp64 inputs of the selected streams; buf: the GPU's packed bytes."""
-    N = x64.shape[1]
+def check_encode(tb: Tables, x64: np.ndarray, buf: np.ndarray, streams=None, n_streams=None,
+                 n_tokens=None, token_range=None) -> dict:
+    """x64: [S_sel, n, d] fp64 inputs of the selected streams (tokens token_range = [t0, t1) of
+    n_tokens, default all); buf: the GPU's packed bytes of the whole tensor."""
+    N = n_tokens if n_tokens is not None else x64.shape[1]
     S_all = n_streams if n_streams is not None else x64.shape[0]
     streams = list(range(S_all)) if streams is None else list(streams)
-    recs = O.unpack_tensor(buf, tb.d, tb.b, tb.m, S_all, N, streams)
+    recs = O.unpack_tensor(buf, tb.d, tb.b, tb.m, S_all, N, streams, token_range)
     st_flag = st_mis = st_n16 = st_sflag = st_smis = st_r16 = 0
     for k, st in enumerate(streams):
         h = tb.head(st)

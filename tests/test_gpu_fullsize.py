@@ -1,0 +1,235 @@
+"""GPU parity at the workloads' full sizes, in the launch configuration the benchmark uses.
+
+The HIP path runs over the whole tensors; the oracle checks contiguous token ranges (start, middle,
+ragged end) of a few streams, which it computes one vector at a time, and properties that hold at
+any size are checked over everything.  Quality figures (score error with and without the QJL
+sketch, softmax KL on the heavy-tailed regime) are printed for the record.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_transform_amd as T
+from oracle import tq_oracle as O
+from synth import inputs as I
+from tests import parity as P
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    T._lib.lib()
+    yield
+    torch.cuda.empty_cache()
+
+
+def _x64(x):
+    return O.bf16_bits_to_f64(I.bf16_bits(x))
+
+
+def _ranges(n, w):
+    """three token ranges of width <= w: the start, the middle and the end of a stream"""
+    w = min(w, n)
+    mid = max(0, n // 2 - w // 2)
+    return [(0, w), (mid, mid + w), (n - w, n)]
+
+
+def _check_ranges(tb, x, buf, streams, ranges, n_streams, n_tokens, decode_f32=None, decode_bf16=None):
+    """encode parity (and fp32 / bf16 decode parity) of tokens [t0, t1) of the given streams"""
+    flagged = mism = 0
+    for st in streams:
+        for t0, t1 in ranges:
+            r = P.check_encode(tb, _x64(x[st:st + 1, t0:t1]), buf, [st], n_streams, n_tokens, (t0, t1))
+            flagged += r["flagged"]
+            mism += r["idx_mismatch"]
+            if decode_f32 is not None:
+                P.check_decode_f32(tb, r["recs"], [st], decode_f32[st:st + 1, t0:t1].cpu().numpy())
+            if decode_bf16 is not None:
+                P.check_decode_bf16(tb, r["recs"], [st], _x64(decode_bf16[st:st + 1, t0:t1]))
+    return flagged, mism
+
+
+def _bf16_rounds(lo: torch.Tensor, hi: torch.Tensor) -> bool:
+    """every bf16 value `lo` is within one bf16 rounding of the fp32 value `hi`"""
+    a, b = lo.float(), hi.float()
+    return bool(((a - b).abs() <= b.abs() * 2.0 ** -8 + 1e-30).all())
+
+
+@pytest.mark.timeout(900)
+def test_cfg2_full_encode_decode():
+    """K, V [32, 32768, 128] bf16, N(0,1) with 4 outlier channels x10 per head; b = 4 on both."""
+    H, N, d, b = 32, 32768, 128, 4
+    for seed in (2001, 2002):
+        x = I.outlier_gaussian(H, N, d, 4, 10.0, seed, device=DEV)
+        codec = T.Codec(d, b, 0, H, seed)
+        buf = T.encode(codec, x)
+        xf = T.decode(codec, buf, H, N, torch.float32)
+        xb = T.decode(codec, buf, H, N, torch.bfloat16)
+        torch.cuda.synchronize()
+        hbuf = buf.cpu().numpy()
+        tb = P.Tables(d, b, 0, H, seed)
+        fl, mi = _check_ranges(tb, x, hbuf, [0, 17, 31], _ranges(N, 2048), H, N, decode_f32=xf, decode_bf16=xb)
+        # any size: each bf16 output is the fp32 result rounded to bf16
+        assert _bf16_rounds(xb, xf)
+        # any size: relative reconstruction error of every stream near the codebook's distortion
+        t, c = P.codebook(d, b)
+        dist = d * O.codebook_mse(d, t, c)
+        xx = x.float()
+        rel = ((xf - xx).pow(2).sum(dim=(1, 2)) / xx.pow(2).sum(dim=(1, 2))).cpu().numpy()
+        assert np.all(rel > 0.3 * dist) and np.all(rel < 3.0 * dist), (rel.min(), rel.max(), dist)
+        print(f"\ncfg2 seed {seed}: flagged {fl}, index mismatches {mi} (all flagged); "
+              f"rel. reconstruction error {rel.mean():.5f} (codebook distortion {dist:.5f})")
+        del x, buf, xf, xb, xx
+        torch.cuda.empty_cache()
+
+
+@pytest.mark.timeout(900)
+def test_cfg3_full_encode_and_scores():
+    """K [8, 65536, 128] N(0,1) bf16, b = 3 + QJL m = 128; 32 queries per head; estimated q.k."""
+    H, N, d, b, m, nq, seed = 8, 65536, 128, 3, 128, 32, 3001
+    k = I.gaussian((H, N, d), seed, device=DEV)
+    q = I.gaussian((H, nq, d), seed + 7, device=DEV)
+    codec = T.Codec(d, b, m, H, seed)
+    buf = T.encode(codec, k)
+    sc = T.qk_scores(codec, q, buf, N)
+    torch.cuda.synchronize()
+    hbuf = buf.cpu().numpy()
+    tb = P.Tables(d, b, m, H, seed)
+    q64 = _x64(q)
+    worst = 0.0
+    for st in (0, 5):
+        for t0, t1 in _ranges(N, 4096):
+            r = P.check_encode(tb, _x64(k[st:st + 1, t0:t1]), hbuf, [st], H, N, (t0, t1))
+            worst = max(worst, P.check_scores(tb, r["recs"], [st], q64[st:st + 1],
+                                              sc[st:st + 1, :, t0:t1].cpu().numpy()))
+    # quality (any size): error of the estimate against the exact q.k, with and without the sketch
+    exact = torch.matmul(q.double(), k.double().transpose(1, 2))
+    xh = T.decode(codec, buf, H, N, torch.float32).double()
+    mse_only = torch.matmul(q.double(), xh.transpose(1, 2))
+    e_qjl = (sc.double() - exact).pow(2).mean().sqrt().item()
+    e_mse = (mse_only - exact).pow(2).mean().sqrt().item()
+    bias_qjl = (sc.double() - exact).mean().item()
+    scale = exact.pow(2).mean().sqrt().item()
+    print(f"\ncfg3: worst sampled score rel L2 {worst:.2e}; RMS error vs exact q.k: with QJL {e_qjl / scale:.4f}, "
+          f"codebook only {e_mse / scale:.4f} (relative to RMS q.k); mean error with QJL {bias_qjl / scale:+.2e}")
+    assert abs(bias_qjl) < 0.01 * scale
+
+
+def _attention_rows(batch, hq, hkv, N, d, q, pk, pv, ck, cv, outs, picks):
+    """relative L2 over the picked rows, and the worst row, of each output in `outs`"""
+    tk, tv = P.Tables(d, ck.b, ck.m, hkv, ck.seed), P.Tables(d, cv.b, 0, hkv, cv.seed)
+    hk, hv = pk.cpu().numpy(), pv.cpu().numpy()
+    q64 = _x64(q)
+    grp = hq // hkv
+    ref, got = [], [[] for _ in outs]
+    for bi, h in picks:
+        st = bi * hkv + h
+        rk = O.unpack_tensor(hk, d, ck.b, ck.m, batch * hkv, N, [st])[0]
+        rv = O.unpack_tensor(hv, d, cv.b, 0, batch * hkv, N, [st])[0]
+        for j in range(grp):
+            ref.append(P.oracle_attention_row(tk, tv, rk, rv, st, q64[bi, h * grp + j], 1.0 / math.sqrt(d)))
+            for o, out in enumerate(outs):
+                got[o].append(out[bi, h * grp + j].float().cpu().numpy())
+    ref = np.array(ref)
+    res = []
+    for g in got:
+        g = np.array(g)
+        res.append((P.rel_l2(g, ref), max(P.rel_l2(a, r) for a, r in zip(g, ref))))
+    return res
+
+
+@pytest.mark.timeout(900)
+def test_cfg4_full_decode_attention():
+    """batch 16, 32 q / 8 kv heads, context 131072, d = 128; K b = 4 + QJL m = 128, V b = 4."""
+    batch, hq, hkv, N, d = 16, 32, 8, 131072, 128
+    ck, cv = T.Codec(d, 4, 128, hkv, 4001), T.Codec(d, 4, 0, hkv, 4002)
+    K = I.rope_gaussian(batch * hkv, N, d, 4001, device=DEV)
+    V = I.rope_gaussian(batch * hkv, N, d, 4002, device=DEV)
+    q = I.cfg4_queries(batch, hq, d, N, 4003, device=DEV)
+    pk, pv = T.encode(ck, K), T.encode(cv, V)
+    out = T.decode_attention(ck, cv, q, pk, pv, hkv, N)
+    out32 = T.decode_attention(ck, cv, q, pk, pv, hkv, N, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    picks = [(0, 0), (7, 3), (15, 7)]
+    # encode parity on token ranges of the picked streams
+    hk, hv = pk.cpu().numpy(), pv.cpu().numpy()
+    tk, tv = P.Tables(d, 4, 128, hkv, 4001), P.Tables(d, 4, 0, hkv, 4002)
+    sts = [bi * hkv + h for bi, h in picks]
+    _check_ranges(tk, K, hk, sts, _ranges(N, 2048), batch * hkv, N)
+    _check_ranges(tv, V, hv, sts, _ranges(N, 2048), batch * hkv, N)
+    del hk, hv
+    (e_all, e_row), (e32, e32_row) = _attention_rows(batch, hq, hkv, N, d, q, pk, pv, ck, cv, [out, out32], picks)
+    print(f"\ncfg4: attention rel L2 over the checked rows: bf16 out {e_all:.2e} (worst row {e_row:.2e}), "
+          f"fp32 out {e32:.2e} (worst row {e32_row:.2e})")
+    assert e_all <= 2e-3 and e32 <= 2e-3
+    # every output row: the bf16 output is the fp32 output rounded
+    assert _bf16_rounds(out, out32)
+
+
+@pytest.fixture(scope="module")
+def cfg5_data():
+    H, N, d = 16, 262144, 256
+    k = I.student_t(H, N, d, 3, 5001, device=DEV)
+    v = I.student_t(H, N, d, 3, 5002, device=DEV)
+    q = I.gaussian((H, 64, d), 5003, device=DEV)
+    yield k, v, q
+    del k, v, q
+    torch.cuda.empty_cache()
+
+
+def _kl_softmax(q, k, sc, d, chunk=2):
+    """mean KL( softmax(q.k/sqrt d) || softmax(est/sqrt d) ) over heads and queries, fp64"""
+    tot, n = 0.0, 0
+    for h0 in range(0, q.shape[0], chunk):
+        ex = torch.matmul(q[h0:h0 + chunk].double(), k[h0:h0 + chunk].double().transpose(1, 2)) / math.sqrt(d)
+        es = sc[h0:h0 + chunk].double() / math.sqrt(d)
+        lp = torch.log_softmax(ex, dim=-1)
+        lq = torch.log_softmax(es, dim=-1)
+        tot += (lp.exp() * (lp - lq)).sum(dim=-1).sum().item()
+        n += ex.shape[0] * ex.shape[1]
+        del ex, es, lp, lq
+    return tot / n
+
+
+@pytest.mark.timeout(900)
+def test_cfg5_full_sweep_and_kl(cfg5_data):
+    """Student-t nu = 3, d = 256, 16 heads x 262144 tokens; b in {2,3,5,6} x {m = 0, m = 256 on K}."""
+    k, v, q = cfg5_data
+    H, N, d = k.shape
+    kl = {}
+    for b in (2, 3, 5, 6):
+        for m in (0, 256):
+            ck = T.Codec(d, b, m, H, 5001 + b)
+            pk = T.encode(ck, k)
+            kf = T.decode(ck, pk, H, N, torch.float32)
+            sc = T.qk_scores(ck, q, pk, N)
+            torch.cuda.synchronize()
+            hk = pk.cpu().numpy()
+            tb = P.Tables(d, b, m, H, 5001 + b)
+            for st in (3, 15):
+                for t0, t1 in _ranges(N, 1024):
+                    r = P.check_encode(tb, _x64(k[st:st + 1, t0:t1]), hk, [st], H, N, (t0, t1))
+                    P.check_decode_f32(tb, r["recs"], [st], kf[st:st + 1, t0:t1].cpu().numpy())
+                    P.check_scores(tb, r["recs"], [st], _x64(q[st:st + 1]), sc[st:st + 1, :, t0:t1].cpu().numpy())
+            kl[(b, m)] = _kl_softmax(q, k, sc, d)
+            del pk, kf, sc, hk
+            torch.cuda.empty_cache()
+        cv = T.Codec(d, b, 0, H, 5101 + b)
+        pv = T.encode(cv, v)
+        vf = T.decode(cv, pv, H, N, torch.float32)
+        torch.cuda.synchronize()
+        hv = pv.cpu().numpy()
+        tv = P.Tables(d, b, 0, H, 5101 + b)
+        _check_ranges(tv, v, hv, [0, 9], _ranges(N, 1024), H, N, decode_f32=vf)
+        del pv, vf, hv
+        torch.cuda.empty_cache()
+    print("\ncfg5 mean softmax KL over 16 heads x 64 queries: " +
+          ", ".join(f"b={b} m={m}: {kl[(b, m)]:.3e}" for (b, m) in sorted(kl)))
+    for m in (0, 256):
+        ks = [kl[(b, m)] for b in (2, 3, 5, 6)]
+        assert all(np.isfinite(ks)) and all(ks[i] > ks[i + 1] for i in range(3)), ks
