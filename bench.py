@@ -26,6 +26,43 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published (the sketch projection's operand type)
+
+# HBM bytes per launch from two rocprofv3 counter runs of this benchmark (FETCH_SIZE, WRITE_SIZE,
+# per dispatch), scaled by what the same counters read for the 1 GiB copy that copy_ceiling()
+# times: 1 FETCH_SIZE unit = 2048 B, 1 WRITE_SIZE unit = 1024 B.  A figure is reported only while
+# the kernel's sources are the ones it was measured on (sha256 of the .hip file + shared headers).
+FETCH_UNIT_B, WRITE_UNIT_B = 2048, 1024
+TRAFFIC = {
+    "encode_k": {"fetch": 2098027.125, "write": 1390973.90625, "src": "encode.hip",
+                 "sha": "28642df3117ae8d8603b339b5d3893f75fc9088930f7d207c1dc69212aa631b5"},
+    "encode_v": {"fetch": 2097226.1875, "write": 1092480.34375, "src": "encode.hip",
+                 "sha": "28642df3117ae8d8603b339b5d3893f75fc9088930f7d207c1dc69212aa631b5"},
+    "decode_attention": {"fetch": 1230639.4375, "write": 8320.0, "src": "attention.hip",     # split-K kernel
+                         "sha": "d6d9fe87fdf22523ebc2d32f1f654e6d20c4212285b45c5e7426e6829f2d7689"},
+    "decode_v_bf16": {"fetch": 553413.4375, "write": 4235279.3125, "src": "decode.hip",
+                      "sha": "9a2ad666db3693ec7c2275b537ca6064e4fb2abca123ed9db201e01c5c0771cd"},
+}
+TRAFFIC_HEADERS_SHA = ("01ae2d556f9fd52ae7d358b78db3db73ba040c21c4b22c480403fb0ae957946c"   # common.hpp
+                       "975bef9109dcb956abdef4d6ffd92c4b63ddfbb2d89263b94ff3ae72c906a3c1")  # kernels.hpp
+
+
+def _sha(path: str) -> str:
+    import hashlib
+    with open(path, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()
+
+
+def traffic_bytes(kernel: str):
+    """calibrated HBM bytes per launch of `kernel`, or None if its sources changed since measured"""
+    t = TRAFFIC.get(kernel)
+    csrc = os.path.join(ROOT, "kv_cache_transform_amd", "csrc")
+    if t is None or _sha(os.path.join(csrc, t["src"])) != t["sha"]:
+        return None
+    hdr = _sha(os.path.join(csrc, "common.hpp")) + _sha(os.path.join(csrc, "kernels.hpp"))
+    if TRAFFIC_HEADERS_SHA is not None and hdr != TRAFFIC_HEADERS_SHA:
+        return None
+    return int(round(t["fetch"] * FETCH_UNIT_B + t["write"] * WRITE_UNIT_B))
 
 
 def parse():
@@ -139,10 +176,23 @@ def main():
 
     copy = copy_ceiling(torch, dev, stream)
 
+    for n in kern:
+        kern[n]["traffic_bytes"] = traffic_bytes(n)
+
+    # roofline of the dominant kernel: the sketch encode is a dense m x d contraction (MFMA bound,
+    # 2 m d flop per key), every other kernel streams HBM
     dom = max(names, key=lambda n: kms[n])
-    roof = {"bound": "hbm", "kernel": dom, "achieved": kern[dom]["achieved_GBs"], "peak": HBM_PEAK_GBS,
-            "unit": "GB/s", "frac": kern[dom]["hbm_frac"], "traffic": None,
-            "alg_bytes_per_launch": alg[dom], "avg_launch_ms": kern[dom]["ms"]}
+    if dom == "encode_k" and ck.m > 0:
+        flops = nvec * 2 * ck.m * d
+        ach = flops / (kms[dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": dom, "achieved": round(ach, 1), "peak": MFMA_F16_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(ach / MFMA_F16_PEAK_TFLOPS, 4), "traffic": traffic_bytes(dom),
+                "alg_flops_per_launch": flops, "alg_bytes_per_launch": alg[dom], "avg_launch_ms": kern[dom]["ms"],
+                "hbm_achieved_GBs": kern[dom]["achieved_GBs"], "hbm_frac": kern[dom]["hbm_frac"]}
+    else:
+        roof = {"bound": "hbm", "kernel": dom, "achieved": kern[dom]["achieved_GBs"], "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": kern[dom]["hbm_frac"], "traffic": traffic_bytes(dom),
+                "alg_bytes_per_launch": alg[dom], "avg_launch_ms": kern[dom]["ms"]}
 
     cpu = None
     if not args.no_cpu_baseline:
