@@ -60,7 +60,7 @@ typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
 typedef struct {
     int32_t d;        /* head_dim: 64, 128 or 256 */
     int32_t b;        /* codebook bits per coordinate, 1..8 */
-    int32_t m;        /* QJL sketch rows; 0 = no sketch; a multiple of 32, at most 4·d */
+    int32_t m;        /* QJL sketch rows; 0 = no sketch; a multiple of 32, at most d */
     int32_t n_heads;  /* heads with distinct random state; stream st uses head st % n_heads */
     uint64_t seed;    /* keys the random signs and S */
 } tq_params;
