@@ -51,7 +51,23 @@ struct AttnGeom {
     static constexpr int KROW = D * BK / 8, VROW = D * BV / 8;
     static constexpr bool VPAIR = BV == 4;           // two-token pair LUT for 4-bit values
     static constexpr int NKS = D >= 256 ? 2 : 1;     // sketch words per lane (m <= d)
+    // The K dequantisation LUT and the value pair LUT are read at random entries.  LDS has 32
+    // banks of 4 bytes and serves 128 bytes per cycle, i.e. 128/E lanes of an E-byte read at once;
+    // holding 128/E copies with entry e of copy c at (e·copies + c)·E gives every lane of such a
+    // phase its own banks (lane l reads copy l % copies).  Done when the copies fit in 32 KiB.
+    static constexpr int KE = 2 * PK;                // bytes per K LUT entry
+    static constexpr int KR = (NEK * KE * (128 / KE) <= 32768) ? 128 / KE : 1;
+    static constexpr int VR = VPAIR ? 32 : 1;        // copies of the 1 KiB value pair LUT
+    // 4-bit keys and values: both LUTs have 256 entries of 4 bytes, so one table of 256-byte rows
+    // holds entry e of both (32 K copies, then 32 V copies), and a lane's address is the byte
+    // index shifted by 8 or-ed with its copy offset: one v_perm_b32 per lookup.
+    static constexpr bool KV256 = VPAIR && PK == 2 && NEK == 256;
 };
+
+// byte offset (idx << 8) | off, idx = byte `which` of w, off < 256: D = {0, 0, w.byte[which], off.byte0}
+__device__ __forceinline__ uint32_t row256(uint32_t w, uint32_t off, int which) {
+    return __builtin_amdgcn_perm(w, off, 0x0c0c0000u | ((uint32_t)(4 + which) << 8));
+}
 
 // Per-wave base pointers of one stream (chunk offsets are added as wave-uniform values).
 struct AttnPtrs {
@@ -143,10 +159,10 @@ struct AttnState {
 template <int D, int BK, int BV, bool QJL, bool FULL>
 __device__ __forceinline__ void attn_chunk(const AttnChunk<AttnGeom<D, BK, BV>::NWK, AttnGeom<D, BK, BV>::NWV, AttnGeom<D, BK, BV>::NKS>& cur,
                                            AttnState<AttnGeom<D, BK, BV>::NT>& S, int64_t t0, int64_t t_end,
-                                           int g, int mks, float lam, float scale_log2,
+                                           int g, int mks,
                                            const half8 (&qb)[AttnGeom<D, BK, BV>::KS], const half8* pb,
-                                           const _Float16* klut, const _Float16* vlut, const uint32_t* vlut2,
-                                           const _Float16* sgn) {
+                                           const uint8_t* kl, const _Float16* vlut, const uint8_t* vl2,
+                                           const u32x2* sgn4, const uint8_t* kvl, uint32_t koff, uint32_t voff) {
     using Gm = AttnGeom<D, BK, BV>;
     constexpr int KS = Gm::KS, PK = Gm::PK, NT = Gm::NT;
     // ---- scores for the two 16-token tiles ----------------------------------------------------
@@ -156,28 +172,38 @@ __device__ __forceinline__ void attn_chunk(const AttnChunk<AttnGeom<D, BK, BV>::
         half8 ka[KS];
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
+            constexpr int KST = Gm::KR * Gm::KE;      // bytes between entries of one copy
             if constexpr (PK == 8) {
                 const uint32_t f = get_bits<8 * BK>(cur.kw[T], (8 * k) * BK);
-                ka[k] = *reinterpret_cast<const half8*>(klut + f * 8);
+                ka[k] = *reinterpret_cast<const half8*>(kl + f * KST);
             } else if constexpr (PK == 4) {
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const uint32_t f = get_bits<4 * BK>(cur.kw[T], (8 * k + 4 * h) * BK);
-                    const half4 e = *reinterpret_cast<const half4*>(klut + f * 4);
+                    const half4 e = *reinterpret_cast<const half4*>(kl + f * KST);
                     ka[k][4 * h + 0] = e[0]; ka[k][4 * h + 1] = e[1];
                     ka[k][4 * h + 2] = e[2]; ka[k][4 * h + 3] = e[3];
+                }
+            } else if constexpr (Gm::KV256) {
+                // coordinates (8k + 2h, +1) are byte h of packed word k
+#pragma unroll
+                for (int h = 0; h < 4; ++h) {
+                    const half2v e = *reinterpret_cast<const half2v*>(kvl + row256(cur.kw[T][k], koff, h));
+                    ka[k][2 * h] = e[0];
+                    ka[k][2 * h + 1] = e[1];
                 }
             } else if constexpr (PK == 2) {
 #pragma unroll
                 for (int h = 0; h < 4; ++h) {
                     const uint32_t f = get_bits<2 * BK>(cur.kw[T], (8 * k + 2 * h) * BK);
-                    const half2v e = *reinterpret_cast<const half2v*>(klut + f * 2);
+                    const half2v e = *reinterpret_cast<const half2v*>(kl + f * KST);
                     ka[k][2 * h] = e[0];
                     ka[k][2 * h + 1] = e[1];
                 }
             } else {
 #pragma unroll
-                for (int h = 0; h < 8; ++h) ka[k][h] = klut[get_bits<BK>(cur.kw[T], (8 * k + h) * BK)];
+                for (int h = 0; h < 8; ++h)
+                    ka[k][h] = *reinterpret_cast<const _Float16*>(kl + get_bits<BK>(cur.kw[T], (8 * k + h) * BK) * KST);
             }
         }
         floatx4 s1 = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -188,18 +214,22 @@ __device__ __forceinline__ void attn_chunk(const AttnChunk<AttnGeom<D, BK, BV>::
 #pragma unroll
             for (int k = 0; k < KS; ++k) {
                 if (k < mks) {
-                    const uint32_t byte = (cur.ks[T][k >> 2] >> (8 * (k & 3))) & 0xffu;
-                    const half8 sa = *reinterpret_cast<const half8*>(sgn + byte * 8);
+                    const uint32_t wsk = cur.ks[T][k >> 2];
+                    const u32x2 lo = sgn4[(wsk >> (8 * (k & 3))) & 0xfu];
+                    const u32x2 hi = sgn4[(wsk >> (8 * (k & 3) + 4)) & 0xfu];
+                    const half8 sa = __builtin_bit_cast(half8, u32x4{lo[0], lo[1], hi[0], hi[1]});
                     s2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(sa, pb[k], s2, 0, 0, 0);
                 }
             }
         }
-        // output lane (q = l16, g) holds tokens t0 + 16T + 4g + i
+        // output lane (q = l16, g) holds tokens t0 + 16T + 4g + i; the queries (and their sketch
+        // projections) already carry the softmax scale in log2 units (and sqrt(pi/2)/m), so the
+        // base-2 logit is n16 (s1 + r16 s2)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float sc = s1[i];
-            if constexpr (QJL) sc = fmaf(lam * half_of(cur.kr[T], i), s2[i], sc);
-            float v = half_of(cur.kn[T], i) * scale_log2 * sc;
+            if constexpr (QJL) sc = fmaf(half_of(cur.kr[T], i), s2[i], sc);
+            float v = half_of(cur.kn[T], i) * sc;
             if (!FULL && t0 + 16 * T + 4 * g + i >= t_end) v = -INFINITY;
             lg[4 * T + i] = v;
         }
@@ -245,7 +275,9 @@ __device__ __forceinline__ void attn_chunk(const AttnChunk<AttnGeom<D, BK, BV>::
 #pragma unroll
                 for (int p = 0; p < 4; ++p) {
                     const uint32_t z = (q & 1) ? zo[p] : ze[p];
-                    const uint32_t e = vlut2[(z >> (8 * (q >> 1))) & 0xffu];
+                    uint32_t e;
+                    if constexpr (Gm::KV256) e = *reinterpret_cast<const uint32_t*>(kvl + row256(z, voff, q >> 1));
+                    else e = *reinterpret_cast<const uint32_t*>(vl2 + ((z >> (8 * (q >> 1))) & 0xffu) * (4 * Gm::VR));
                     const half2v hv = __builtin_bit_cast(half2v, e);
                     va[2 * p] = hv[0];
                     va[2 * p + 1] = hv[1];
@@ -270,25 +302,56 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attn_kernel(AttnArgs 
     constexpr int C = Gm::C, KS = Gm::KS, PK = Gm::PK, NEK = Gm::NEK, NT = Gm::NT;
     constexpr int LV = 1 << BV;
 
-    __shared__ _Float16 klut[NEK * PK];
+    constexpr int KR = Gm::KR, KE = Gm::KE, VR = Gm::VR;
+    constexpr bool KV = Gm::KV256;
+    __shared__ uint32_t klut[KV ? 1 : NEK * KE / 4 * KR];          // copy c of entry e at (e KR + c) KE bytes
     __shared__ _Float16 vlut[LV];
-    __shared__ uint32_t vlut2[Gm::VPAIR ? 256 : 1];
-    __shared__ _Float16 sgn[QJL ? 256 * 8 : 8];
-    for (int i = threadIdx.x; i < NEK * PK; i += blockDim.x) klut[i] = a.tk.lut_f16[i];
+    __shared__ uint32_t vlut2[Gm::VPAIR && !KV ? 256 * VR : 1];  // copy c of entry e at word e VR + c
+    __shared__ uint32_t kvlut[KV ? 256 * 64 : 1];                 // row e: 32 K copies, 32 V copies
+    __shared__ u32x2 sgn4[16];                                     // ±1 halves of the 4 bits of a nibble
+    if constexpr (KV) {
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(a.tk.lut_f16);
+        for (int i = threadIdx.x; i < 256 * 64; i += blockDim.x) {
+            const int e = i >> 6, c = i & 63;
+            if (c < 32) {
+                kvlut[i] = src[e];
+            } else {
+                const half2v hv = {(_Float16)a.tv.cent[e & 15], (_Float16)a.tv.cent[e >> 4]};
+                kvlut[i] = __builtin_bit_cast(uint32_t, hv);
+            }
+        }
+    } else {
+        const uint16_t* src = reinterpret_cast<const uint16_t*>(a.tk.lut_f16);
+        uint16_t* dst = reinterpret_cast<uint16_t*>(klut);
+        for (int i = threadIdx.x; i < NEK * KR; i += blockDim.x) {
+            const int e = i / KR, c = i - e * KR;
+#pragma unroll
+            for (int h = 0; h < PK; ++h) dst[(e * KR + c) * PK + h] = src[e * PK + h];
+        }
+    }
     for (int i = threadIdx.x; i < LV; i += blockDim.x) vlut[i] = (_Float16)a.tv.cent[i];
-    if constexpr (Gm::VPAIR)
-        for (int i = threadIdx.x; i < 256; i += blockDim.x) {
-            const half2v hv = {(_Float16)a.tv.cent[i & 15], (_Float16)a.tv.cent[i >> 4]};
+    if constexpr (Gm::VPAIR && !KV)
+        for (int i = threadIdx.x; i < 256 * VR; i += blockDim.x) {
+            const int e = i / VR;
+            const half2v hv = {(_Float16)a.tv.cent[e & 15], (_Float16)a.tv.cent[e >> 4]};
             vlut2[i] = __builtin_bit_cast(uint32_t, hv);
         }
-    if constexpr (QJL)
-        for (int i = threadIdx.x; i < 256; i += blockDim.x)
+    if (threadIdx.x < 16) {
+        uint32_t w[2];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) sgn[i * 8 + k] = ((i >> k) & 1) ? (_Float16)1.0f : (_Float16)-1.0f;
+        for (int j = 0; j < 2; ++j)
+            w[j] = (((threadIdx.x >> (2 * j)) & 1) ? 0x3c00u : 0xbc00u) |
+                   ((((threadIdx.x >> (2 * j + 1)) & 1) ? 0x3c00u : 0xbc00u) << 16);
+        sgn4[threadIdx.x] = u32x2{w[0], w[1]};
+    }
     __syncthreads();
 
     const int lane = threadIdx.x & 63;
     const int l16 = lane & 15, g = lane >> 4;
+    const uint8_t* kl = reinterpret_cast<const uint8_t*>(klut) + (lane % KR) * KE;      // the lane's copies
+    const uint8_t* vl2 = reinterpret_cast<const uint8_t*>(vlut2) + (lane % VR) * 4;
+    const uint8_t* kvl = reinterpret_cast<const uint8_t*>(kvlut);
+    const uint32_t koff = (uint32_t)(lane & 31) * 4u, voff = 128u + (uint32_t)(lane & 31) * 4u;
     const int64_t item = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     const int64_t n_streams = (int64_t)a.batch * a.n_kv_heads;
     if (item >= n_streams * a.n_split) return;
@@ -298,7 +361,6 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attn_kernel(AttnArgs 
     const int64_t t_end = t_begin + a.tokens_per_split < a.n_tokens ? t_begin + a.tokens_per_split : a.n_tokens;
     const int m = a.tk.m;
     const int mks = m >> 5;
-    const float lam = QJL ? 1.2533141373155003f / (float)m : 0.0f;
 
     // query operands (B of the score products): lane column q = l16, k-block g
     const int bidx = (int)(st / a.n_kv_heads), kvh = (int)(st - (int64_t)bidx * a.n_kv_heads);
@@ -339,21 +401,21 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attn_kernel(AttnArgs 
 #pragma unroll 1
     for (; c + 2 <= n_full; c += 2) {
         attn_load<D, BK, BV, QJL, true>(B, P, t_begin + (c + 1) * 32, t_end, l16, g, m);
-        attn_chunk<D, BK, BV, QJL, true>(A, S, t_begin + c * 32, t_end, g, mks, lam, a.scale_log2, qb, pb, klut,
-                                         vlut, vlut2, sgn);
+        attn_chunk<D, BK, BV, QJL, true>(A, S, t_begin + c * 32, t_end, g, mks, qb, pb, kl,
+                                         vlut, vl2, sgn4, kvl, koff, voff);
         if (c + 2 < n_full) attn_load<D, BK, BV, QJL, true>(A, P, t_begin + (c + 2) * 32, t_end, l16, g, m);
-        attn_chunk<D, BK, BV, QJL, true>(B, S, t_begin + (c + 1) * 32, t_end, g, mks, lam, a.scale_log2, qb, pb,
-                                         klut, vlut, vlut2, sgn);
+        attn_chunk<D, BK, BV, QJL, true>(B, S, t_begin + (c + 1) * 32, t_end, g, mks, qb, pb,
+                                         kl, vlut, vl2, sgn4, kvl, koff, voff);
     }
     if (c < n_full) {
-        attn_chunk<D, BK, BV, QJL, true>(A, S, t_begin + c * 32, t_end, g, mks, lam, a.scale_log2, qb, pb, klut,
-                                         vlut, vlut2, sgn);
+        attn_chunk<D, BK, BV, QJL, true>(A, S, t_begin + c * 32, t_end, g, mks, qb, pb, kl,
+                                         vlut, vl2, sgn4, kvl, koff, voff);
         ++c;
     }
     if (t_begin + c * 32 < t_end) {
         attn_load<D, BK, BV, QJL, false>(A, P, t_begin + c * 32, t_end, l16, g, m);
-        attn_chunk<D, BK, BV, QJL, false>(A, S, t_begin + c * 32, t_end, g, mks, lam, a.scale_log2, qb, pb, klut,
-                                          vlut, vlut2, sgn);
+        attn_chunk<D, BK, BV, QJL, false>(A, S, t_begin + c * 32, t_end, g, mks, qb, pb, kl,
+                                          vlut, vl2, sgn4, kvl, koff, voff);
     }
     // ---- partial results: lane (q = l16, g) holds O[coord NT*(4g+i) + n][q] --------------------
     const float l_tot = sum4(S.l_run);

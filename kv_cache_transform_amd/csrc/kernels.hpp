@@ -50,8 +50,9 @@ struct QPrepArgs {
     int q_bf16;
     int64_t n_rows;
     int n_q_per_stream;     // rows per stream (RNG head = stream % n_heads)
-    _Float16* q_rot;        // [n_rows][d]
-    _Float16* p;            // [n_rows][m] (m > 0)
+    _Float16* q_rot;        // [n_rows][d], times q_scale
+    _Float16* p;            // [n_rows][m] (m > 0), times p_scale
+    float q_scale, p_scale; // 1 for scores; attention folds its softmax scale (and the QJL factor) in
     DevTables t;
 };
 
@@ -71,8 +72,8 @@ struct ScoresArgs {
 struct AttnArgs {
     const uint8_t* pk;       // packed K
     const uint8_t* pv;       // packed V
-    const _Float16* q_rot;   // [batch*n_q_heads][d]  (rotated with the K signs of its kv head)
-    const _Float16* p;       // [batch*n_q_heads][m]
+    const _Float16* q_rot;   // [batch*n_q_heads][d]  rotated with the K signs of its kv head, times scale_log2
+    const _Float16* p;       // [batch*n_q_heads][m]  S q_rot, times scale_log2 sqrt(pi/2)/m
     float* part;             // [batch*n_kv][n_split][16 queries][d] rotated-domain partial sums
     float* part_ml;          // [batch*n_kv][n_split][16][2] running max (log2 units) and sum
     void* out;               // [batch][n_q_heads][d]

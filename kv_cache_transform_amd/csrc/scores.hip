@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void qprep_kernel(QPrepArgs a) {
     for (int j = threadIdx.x; j < d; j += blockDim.x) {
         const float r = buf[j] * inv;
         buf[j] = r;
-        a.q_rot[row * d + j] = (_Float16)r;
+        a.q_rot[row * d + j] = (_Float16)(r * a.q_scale);
     }
     __syncthreads();
     if (m > 0) {
@@ -52,7 +52,7 @@ __global__ __launch_bounds__(256) void qprep_kernel(QPrepArgs a) {
         for (int i = threadIdx.x; i < m; i += blockDim.x) {
             float acc = 0.0f;
             for (int j = 0; j < d; ++j) acc = fmaf((float)S[(int64_t)i * d + j], buf[j], acc);
-            a.p[row * m + i] = (_Float16)acc;
+            a.p[row * m + i] = (_Float16)(acc * a.p_scale);
         }
     }
 }

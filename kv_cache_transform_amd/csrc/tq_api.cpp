@@ -342,6 +342,8 @@ int tq_qk_scores(const tq_params* pk, const void* q, tq_dtype q_dtype, int64_t n
     qa.q_bf16 = q_dtype == TQ_BF16;
     qa.n_rows = n_streams * n_q;
     qa.n_q_per_stream = (int)n_q;
+    qa.q_scale = 1.0f;
+    qa.p_scale = 1.0f;
     qa.q_rot = qrot;
     qa.p = pp;
     qa.t = t;
@@ -410,6 +412,12 @@ int tq_decode_attention(const tq_params* pk, const tq_params* pv, const void* q,
     qa.q_rot = reinterpret_cast<_Float16*>(ws + w.o_qrot);
     qa.p = reinterpret_cast<_Float16*>(ws + w.o_p);
     qa.t = tk;
+    // the attention kernel works with base-2 logits: fold scale·log2(e) into the rotated queries
+    // and scale·log2(e)·sqrt(pi/2)/m into their sketch projections
+    const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)pk->d);
+    const float scale_log2 = scale * 1.4426950408889634f;
+    qa.q_scale = scale_log2;
+    qa.p_scale = pk->m > 0 ? scale_log2 * (float)(std::sqrt(M_PI / 2.0) / pk->m) : 0.0f;
     if ((rc = hip_status(launch_qprep(qa, s))) != TQ_OK) return rc;
     AttnArgs a{};
     a.pk = static_cast<const uint8_t*>(packed_k);
@@ -427,8 +435,7 @@ int tq_decode_attention(const tq_params* pk, const tq_params* pv, const void* q,
     a.group = n_q_heads / n_kv_heads;
     a.n_split = (int)w.n_split;
     a.tokens_per_split = attn_tokens_per_split(streams, n_tokens);
-    const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)pk->d);
-    a.scale_log2 = scale * 1.4426950408889634f;
+    a.scale_log2 = scale_log2;
     a.k_off_idx = lk.off_idx;
     a.k_off_sketch = lk.off_sketch;
     a.k_off_norm = lk.off_norm;
