@@ -36,7 +36,7 @@ __device__ __forceinline__ float max4(float t) {
 template <int NWK, int NWV, int NKS>
 struct AttnChunk {
     uint32_t kw[2][NWK];
-    uint32_t ks[2][NKS];
+    uint32_t ks[2][NKS + 1];     // covering aligned dwords; the lane's bytes start at byte (g m/32) % 4
     u32x2 kn[2], kr[2], vn[2];
     uint32_t vw[8][NWV];
 };
@@ -95,25 +95,20 @@ __device__ __forceinline__ void attn_load(AttnChunk<AttnGeom<D, BK, BV>::NWK, At
         if (FULL || 16 * T + l16 < rem) {
             load_bytes<Gm::CBK, Gm::CAK>(kb + koff + T * 16 * Gm::KROW, c.kw[T]);
             if constexpr (QJL) {
-                const uint8_t* sp = P.ksk + (t0 + 16 * T + l16) * (m / 8) + g * (m / 32);
-                if ((m & 127) == 0) {
-                    c.ks[T][0] = *reinterpret_cast<const uint32_t*>(sp);
-                    if constexpr (Gm::NKS > 1) c.ks[T][1] = m == 256 ? *reinterpret_cast<const uint32_t*>(sp + 4) : 0u;
-                } else {
-                    uint32_t w0 = 0, w1 = 0;
-                    for (int q = 0; q < (m >> 5); ++q) {
-                        if (q < 4) w0 |= uint32_t(sp[q]) << (8 * q);
-                        else w1 |= uint32_t(sp[q]) << (8 * (q - 4));
-                    }
-                    c.ks[T][0] = w0;
-                    if constexpr (Gm::NKS > 1) c.ks[T][1] = w1;
-                }
+                // the lane's m/32 sketch bytes start at any byte offset: read the covering aligned
+                // dwords and funnel-shift (branch-free, so the load counters stay static).  Bytes past
+                // m/32 are never used; the over-read stays inside the packed buffer, whose norm
+                // planes follow the sketch plane.
+                // (the byte offset within the dword is (g m/32) % 4: rows are multiples of 4 bytes)
+                const uint8_t* sp = P.ksk + (t0 + 16 * T + l16) * (m / 8) + ((g * (m / 32)) & ~3);
+#pragma unroll
+                for (int k = 0; k <= Gm::NKS; ++k) c.ks[T][k] = reinterpret_cast<const uint32_t*>(sp)[k];
             }
         } else {
 #pragma unroll
             for (int k = 0; k < Gm::NWK; ++k) c.kw[T][k] = 0u;
 #pragma unroll
-            for (int k = 0; k < Gm::NKS; ++k) c.ks[T][k] = 0u;
+            for (int k = 0; k <= Gm::NKS; ++k) c.ks[T][k] = 0u;
         }
         if (FULL || 16 * T + 4 * g + 4 <= rem) {
             c.kn[T] = *reinterpret_cast<const u32x2*>(P.kn + t0 * 2 + noff + 32 * T);
@@ -162,7 +157,8 @@ __device__ __forceinline__ void attn_chunk(const AttnChunk<AttnGeom<D, BK, BV>::
                                            int g, int mks,
                                            const half8 (&qb)[AttnGeom<D, BK, BV>::KS], const half8* pb,
                                            const uint8_t* kl, const _Float16* vlut, const uint8_t* vl2,
-                                           const u32x2* sgn4, const uint8_t* kvl, uint32_t koff, uint32_t voff) {
+                                           const u32x2* sgn4, const uint8_t* kvl, uint32_t koff, uint32_t voff,
+                                           uint32_t ksh) {
     using Gm = AttnGeom<D, BK, BV>;
     constexpr int KS = Gm::KS, PK = Gm::PK, NT = Gm::NT;
     // ---- scores for the two 16-token tiles ----------------------------------------------------
@@ -214,7 +210,7 @@ __device__ __forceinline__ void attn_chunk(const AttnChunk<AttnGeom<D, BK, BV>::
 #pragma unroll
             for (int k = 0; k < KS; ++k) {
                 if (k < mks) {
-                    const uint32_t wsk = cur.ks[T][k >> 2];
+                    const uint32_t wsk = __builtin_amdgcn_alignbit(cur.ks[T][(k >> 2) + 1], cur.ks[T][k >> 2], ksh);
                     const u32x2 lo = sgn4[(wsk >> (8 * (k & 3))) & 0xfu];
                     const u32x2 hi = sgn4[(wsk >> (8 * (k & 3) + 4)) & 0xfu];
                     const half8 sa = __builtin_bit_cast(half8, u32x4{lo[0], lo[1], hi[0], hi[1]});
@@ -352,6 +348,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attn_kernel(AttnArgs 
     const uint8_t* vl2 = reinterpret_cast<const uint8_t*>(vlut2) + (lane % VR) * 4;
     const uint8_t* kvl = reinterpret_cast<const uint8_t*>(kvlut);
     const uint32_t koff = (uint32_t)(lane & 31) * 4u, voff = 128u + (uint32_t)(lane & 31) * 4u;
+    const uint32_t ksh = (uint32_t)((g * (a.tk.m >> 5)) & 3) * 8u;   // bit offset of the lane's sketch bytes
     const int64_t item = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     const int64_t n_streams = (int64_t)a.batch * a.n_kv_heads;
     if (item >= n_streams * a.n_split) return;
@@ -393,29 +390,40 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attn_kernel(AttnArgs 
     P.vn = a.pv + a.v_off_norm + st * a.n_tokens * 2;
 
     // full 32-token chunks through two ping-pong buffers (next chunk's loads overlap this one's
-    // math), then at most one guarded partial chunk
+    // math), then at most one guarded partial chunk.  Every load in the loop is unconditional (the
+    // last refill re-reads the final chunk) so the load counters stay static and a wait covers only
+    // the buffer about to be used.
     AttnChunk<Gm::NWK, Gm::NWV, Gm::NKS> A, B;
     const int64_t n_full = (t_end - t_begin) >> 5;
     int64_t c = 0;
-    if (n_full > 0) attn_load<D, BK, BV, QJL, true>(A, P, t_begin, t_end, l16, g, m);
+    if (n_full > 0) {
+        attn_load<D, BK, BV, QJL, true>(A, P, t_begin, t_end, l16, g, m);
 #pragma unroll 1
-    for (; c + 2 <= n_full; c += 2) {
-        attn_load<D, BK, BV, QJL, true>(B, P, t_begin + (c + 1) * 32, t_end, l16, g, m);
-        attn_chunk<D, BK, BV, QJL, true>(A, S, t_begin + c * 32, t_end, g, mks, qb, pb, kl,
-                                         vlut, vl2, sgn4, kvl, koff, voff);
-        if (c + 2 < n_full) attn_load<D, BK, BV, QJL, true>(A, P, t_begin + (c + 2) * 32, t_end, l16, g, m);
-        attn_chunk<D, BK, BV, QJL, true>(B, S, t_begin + (c + 1) * 32, t_end, g, mks, qb, pb,
-                                         kl, vlut, vl2, sgn4, kvl, koff, voff);
-    }
-    if (c < n_full) {
-        attn_chunk<D, BK, BV, QJL, true>(A, S, t_begin + c * 32, t_end, g, mks, qb, pb, kl,
-                                         vlut, vl2, sgn4, kvl, koff, voff);
-        ++c;
+        for (; c + 2 <= n_full; c += 2) {
+            // (scheduling barriers keep each buffer's loads together, ahead of the other buffer's
+            // math, so the wait before a chunk leaves the other buffer's loads in flight)
+            attn_load<D, BK, BV, QJL, true>(B, P, t_begin + (c + 1) * 32, t_end, l16, g, m);
+            __builtin_amdgcn_sched_barrier(0);
+            attn_chunk<D, BK, BV, QJL, true>(A, S, t_begin + c * 32, t_end, g, mks, qb, pb, kl,
+                                             vlut, vl2, sgn4, kvl, koff, voff, ksh);
+            __builtin_amdgcn_sched_barrier(0);
+            const int64_t cn = c + 2 < n_full ? c + 2 : n_full - 1;
+            attn_load<D, BK, BV, QJL, true>(A, P, t_begin + cn * 32, t_end, l16, g, m);
+            __builtin_amdgcn_sched_barrier(0);
+            attn_chunk<D, BK, BV, QJL, true>(B, S, t_begin + (c + 1) * 32, t_end, g, mks, qb, pb, kl,
+                                             vlut, vl2, sgn4, kvl, koff, voff, ksh);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        if (c < n_full) {          // odd count: A holds chunk c
+            attn_chunk<D, BK, BV, QJL, true>(A, S, t_begin + c * 32, t_end, g, mks, qb, pb, kl,
+                                             vlut, vl2, sgn4, kvl, koff, voff, ksh);
+            ++c;
+        }
     }
     if (t_begin + c * 32 < t_end) {
         attn_load<D, BK, BV, QJL, false>(A, P, t_begin + c * 32, t_end, l16, g, m);
         attn_chunk<D, BK, BV, QJL, false>(A, S, t_begin + c * 32, t_end, g, mks, qb, pb, kl,
-                                          vlut, vl2, sgn4, kvl, koff, voff);
+                                          vlut, vl2, sgn4, kvl, koff, voff, ksh);
     }
     // ---- partial results: lane (q = l16, g) holds O[coord NT*(4g+i) + n][q] --------------------
     const float l_tot = sum4(S.l_run);
