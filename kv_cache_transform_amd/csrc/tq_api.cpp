@@ -145,17 +145,26 @@ int build_tables(const tq_params* p, int device, DevTables* out) {  // caller ho
     return TQ_OK;
 }
 
-int get_tables(const tq_params* p, DevTables* out, int* num_cus) {
+// CU count of the current device (cached)
+int device_cus(int* cus) {
     int device = 0;
     if (hipGetDevice(&device) != hipSuccess) return TQ_EHIP;
     std::lock_guard<std::mutex> lk(g_mu);
     auto nc = g_num_cus.find(device);
     if (nc == g_num_cus.end()) {
-        int cus = 0;
-        if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) return TQ_EHIP;
-        nc = g_num_cus.emplace(device, cus).first;
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) return TQ_EHIP;
+        nc = g_num_cus.emplace(device, n).first;
     }
-    *num_cus = nc->second;
+    *cus = nc->second;
+    return TQ_OK;
+}
+
+int get_tables(const tq_params* p, DevTables* out, int* num_cus) {
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) return TQ_EHIP;
+    if (device_cus(num_cus) != TQ_OK) return TQ_EHIP;
+    std::lock_guard<std::mutex> lk(g_mu);
     const TableKey key{device, p->d, p->b, p->m, p->n_heads, p->seed};
     auto it = g_tables.find(key);
     if (it != g_tables.end()) {
@@ -172,10 +181,15 @@ int get_tables(const tq_params* p, DevTables* out, int* num_cus) {
 
 int hip_status(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_EHIP; }
 
-// attention split geometry (shared by the workspace query and the launch): about 4096 waves in
-// total, at least 256 tokens per split, token ranges a multiple of 32, at most 1024 splits
-int64_t attn_tokens_per_split(int64_t n_streams, int64_t n_tokens) {
-    int64_t ns = (4096 + n_streams - 1) / (n_streams > 0 ? n_streams : 1);
+// attention split geometry (shared by the workspace query and the launch, and a function of the
+// arguments only so the workspace size needs no device): one wave per (stream, split), as many
+// waves as a 256-CU MI355X holds at once (two 4-wave blocks per CU for d <= 128, one for d = 256),
+// so every wave streams one long token range; at least 256 tokens per split, token ranges a
+// multiple of 32, at most 1024 splits
+constexpr int kAttnCUs = 256;
+int64_t attn_tokens_per_split(int d, int64_t n_streams, int64_t n_tokens) {
+    const int64_t target = (int64_t)kAttnCUs * (d <= 128 ? 8 : 4);
+    int64_t ns = (target + n_streams - 1) / (n_streams > 0 ? n_streams : 1);
     const int64_t max_ns = (n_tokens + 255) / 256;
     if (ns > max_ns) ns = max_ns;
     if (ns > 1024) ns = 1024;
@@ -192,7 +206,7 @@ struct AttnWs {
 AttnWs attn_ws(const tq_params* pk, int32_t batch, int32_t hq, int32_t hkv, int64_t n_tokens) {
     AttnWs w{};
     const int64_t rows = (int64_t)batch * hq + 16;
-    const int64_t tps = attn_tokens_per_split((int64_t)batch * hkv, n_tokens);
+    const int64_t tps = attn_tokens_per_split(pk->d, (int64_t)batch * hkv, n_tokens);
     w.n_split = (n_tokens + tps - 1) / tps;
     if (w.n_split < 1) w.n_split = 1;
     const int64_t streams = (int64_t)batch * hkv;
@@ -434,7 +448,7 @@ int tq_decode_attention(const tq_params* pk, const tq_params* pv, const void* q,
     a.n_kv_heads = n_kv_heads;
     a.group = n_q_heads / n_kv_heads;
     a.n_split = (int)w.n_split;
-    a.tokens_per_split = attn_tokens_per_split(streams, n_tokens);
+    a.tokens_per_split = attn_tokens_per_split(pk->d, streams, n_tokens);
     a.scale_log2 = scale_log2;
     a.k_off_idx = lk.off_idx;
     a.k_off_sketch = lk.off_sketch;
