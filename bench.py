@@ -73,6 +73,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--context", type=int, default=131072)
+    ap.add_argument("--no-extra", action="store_true", help="skip the per-kernel lines of the other workloads")
     return ap.parse_args()
 
 
@@ -175,6 +176,9 @@ def main():
     del xh
 
     copy = copy_ceiling(torch, dev, stream)
+    del K, V
+    torch.cuda.empty_cache()
+    extra = None if args.no_extra else other_workloads(torch, T, I, dev, stream)
 
     for n in kern:
         kern[n]["traffic_bytes"] = traffic_bytes(n)
@@ -212,8 +216,81 @@ def main():
         "cpu_baseline": cpu,
         "kernels": kern,
         "copy_ceiling": copy,
+        "other_workloads": extra,
     }
     print(json.dumps(line))
+
+
+def _time(torch, stream, fn, reps: int = 5) -> float:
+    """average ms of fn() over reps launches on `stream` (after one untimed call)"""
+    fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def _line(ms: float, alg_bytes: int) -> dict:
+    gbs = alg_bytes / (ms * 1e-3) / 1e9
+    return {"ms": round(ms, 4), "alg_bytes": alg_bytes, "achieved_GBs": round(gbs, 1),
+            "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def other_workloads(torch, T, I, dev, stream) -> dict:
+    """Per-kernel lines (not part of `value`) for the other workload shapes: encode / decode of
+    outlier-channel K,V (32 heads x 32768 x 128, b = 4), encode with a QJL sketch and q.k scores
+    (8 heads x 65536 x 128, b = 3, m = 128, 32 queries per head), and heavy-tailed d = 256 vectors
+    (16 heads x 262144, Student-t nu = 3, b = 3, with and without a sketch of m = 256)."""
+    out = {}
+    H, N, d = 32, 32768, 128
+    x = I.outlier_gaussian(H, N, d, 4, 10.0, 2001, device=dev)
+    c = T.Codec(d, 4, 0, H, 2001)
+    pk = T.encode(c, x)
+    xh = torch.empty(H, N, d, dtype=torch.bfloat16, device=dev)
+    nv = H * N
+    out["outlier K 32x32768x128 b4: encode"] = _line(_time(torch, stream, lambda: T.encode(c, x, pk)), nv * (256 + 66))
+    out["outlier K 32x32768x128 b4: decode to bf16"] = _line(
+        _time(torch, stream, lambda: T.decode(c, pk, H, N, torch.bfloat16, out=xh)), nv * (66 + 256))
+    del x, pk, xh
+
+    H, N, d, nq = 8, 65536, 128, 32
+    x = I.gaussian((H, N, d), 3001, device=dev)
+    q = I.gaussian((H, nq, d), 3008, device=dev)
+    c = T.Codec(d, 3, 128, H, 3001)
+    pk = T.encode(c, x)
+    sc = torch.empty(H, nq, N, dtype=torch.float32, device=dev)
+    import ctypes
+    ws = torch.empty(max(int(T._lib.lib().tq_scores_workspace_bytes(ctypes.byref(c.params()), H, nq)), 16),
+                     dtype=torch.uint8, device=dev)
+    nv = H * N
+    out["gaussian K 8x65536x128 b3 m128: encode"] = _line(_time(torch, stream, lambda: T.encode(c, x, pk)),
+                                                         nv * (256 + 48 + 16 + 4))
+    out["gaussian K 8x65536x128 b3 m128: scores, 32 queries"] = _line(
+        _time(torch, stream, lambda: T.qk_scores(c, q, pk, N, out=sc, workspace=ws)), nv * (48 + 16 + 4 + 4 * nq))
+    del x, q, pk, sc, ws
+
+    H, N, d = 16, 262144, 256
+    x = I.student_t(H, N, d, 3, 5001, device=dev)
+    nv = H * N
+    for m in (0, 256):
+        c = T.Codec(d, 3, m, H, 5004)
+        pk = T.encode(c, x)
+        rec = 96 + m // 8 + 2 + (2 if m else 0)
+        out[f"student-t K 16x262144x256 b3 m{m}: encode"] = _line(_time(torch, stream, lambda: T.encode(c, x, pk)),
+                                                                 nv * (512 + rec))
+        if m == 0:
+            xh = torch.empty(H, N, d, dtype=torch.bfloat16, device=dev)
+            out["student-t K 16x262144x256 b3: decode to bf16"] = _line(
+                _time(torch, stream, lambda: T.decode(c, pk, H, N, torch.bfloat16, out=xh)), nv * (rec + 512))
+            del xh
+        del pk
+    del x
+    torch.cuda.empty_cache()
+    return out
 
 
 def copy_ceiling(torch, dev, stream, n_bytes: int = 1 << 30, reps: int = 5):

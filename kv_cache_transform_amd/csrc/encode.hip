@@ -20,7 +20,7 @@
 namespace tq {
 
 template <int D, int B, bool QJL, bool BF16, bool S_LDS>
-__global__ __launch_bounds__(256, ((D > 128 && (QJL || !BF16)) || (QJL && !BF16) ? 1 : 3)) void encode_kernel(EncodeArgs a) {
+__global__ __launch_bounds__(256, ((D > 128 && (QJL || !BF16)) || (QJL && !BF16) ? 1 : (D > 128 ? 2 : 3))) void encode_kernel(EncodeArgs a) {
     constexpr int C = D / 4, R = D / 16, L = 1 << B;
     constexpr int NW = (C * B + 31) / 32;          // packed words per lane
     constexpr int CB = C * B / 8;                   // packed bytes per lane

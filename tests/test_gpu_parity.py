@@ -40,6 +40,7 @@ def _x64(x):
 MATRIX = ([(d, b, 0, torch.bfloat16) for d in (64, 128, 256) for b in range(1, 7)]
           + [(128, b, 0, torch.bfloat16) for b in (7, 8)]
           + [(d, b, m, torch.bfloat16) for d in (64, 128, 256) for b in (2, 3, 4) for m in (32, d)]
+          + [(256, b, 128, torch.bfloat16) for b in (3, 4)]
           + [(d, 4, 0, torch.float32) for d in (64, 128, 256)] + [(64, 3, 64, torch.float32)])
 
 
