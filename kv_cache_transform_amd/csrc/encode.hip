@@ -336,17 +336,33 @@ template <int D, int B, bool QJL, bool BF16>
 static hipError_t launch_one(const EncodeArgs& a, int num_cus, hipStream_t s) {
     EncodeArgs b = a;
     const int L = 1 << B;
-    // grid copies: up to 16 (8 with the sketch, whose S tile also lives in LDS) within 16 KiB / 8 KiB
+    // S lives in LDS whenever it fits beside the rest (160 KiB per CU; for d = 256 and m = 256 the
+    // 128 KiB of S leave room for one block per CU); the grid is held in up to 16 copies (8 with the
+    // sketch) within 16 KiB / 8 KiB, fewer if S needs the room
+    constexpr size_t kLdsMax = 163840;
     const size_t grid_bytes = (size_t)(a.t.G + 3) * 8;
-    int rl = QJL ? 3 : 4;
-    while (rl > 0 && (grid_bytes << rl) > (QJL ? 8192u : 16384u)) --rl;
-    b.grid_rep_log2 = rl;
-    const size_t head_bytes = (grid_bytes << rl) + (size_t)(L + 4) * 4 + (BF16 ? (size_t)2 * (D / 32) * 64 * 16 : 0);
+    const size_t fixed = (size_t)(L + 4) * 4 + (BF16 ? (size_t)2 * (D / 32) * 64 * 16 : 0);
     const size_t s_bytes = (size_t)a.t.m * D * 2;
-    const bool s_lds = QJL && (D <= 128 || s_bytes <= 65536);   // m <= d: always for d <= 128
+    const bool s_lds = QJL && (D <= 128 || fixed + grid_bytes + s_bytes <= kLdsMax);   // always for d <= 128
+    int rl = QJL ? 3 : 4;
+    while (rl > 0 && ((grid_bytes << rl) > (QJL ? 8192u : 16384u) ||
+                      (s_lds && fixed + (grid_bytes << rl) + s_bytes > kLdsMax)))
+        --rl;
+    b.grid_rep_log2 = rl;
+    const size_t head_bytes = (grid_bytes << rl) + fixed;
     const size_t lds = head_bytes + (s_lds ? s_bytes : 0);
     const void* kern = s_lds ? reinterpret_cast<const void*>(&encode_kernel<D, B, QJL, BF16, true>)
                              : reinterpret_cast<const void*>(&encode_kernel<D, B, QJL, BF16, (D <= 128)>);
+    if (lds > 65536) {           // above the default dynamic LDS limit: raise it once per kernel
+        static std::mutex mu;
+        static bool raised = false;
+        std::lock_guard<std::mutex> lock(mu);
+        if (!raised) {
+            const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax);
+            if (e != hipSuccess) return e;
+            raised = true;
+        }
+    }
     // one wave of blocks: as many 256-thread blocks as fit on every CU at once
     const int64_t target = (int64_t)num_cus * blocks_per_cu(kern, lds);
     int64_t bps = (target + a.n_streams - 1) / a.n_streams;
