@@ -85,6 +85,18 @@ __device__ __forceinline__ void fwht_slots(float (&x)[C]) {
     }
 }
 
+// the same swaps on raw 32-bit words
+__device__ __forceinline__ void xswap16u(uint32_t& a, uint32_t& b) {
+    auto r = __builtin_amdgcn_permlane16_swap(a, b, false, false);
+    a = r[0];
+    b = r[1];
+}
+__device__ __forceinline__ void xswap32u(uint32_t& a, uint32_t& b) {
+    auto r = __builtin_amdgcn_permlane32_swap(a, b, false, false);
+    a = r[0];
+    b = r[1];
+}
+
 // the two cross-lane stages (see the header comment)
 template <int C>
 __device__ __forceinline__ void fwht_cross(float (&x)[C]) {

@@ -15,6 +15,7 @@ struct DevTables {
     const float* cent_x1024 = nullptr; // 2^b centroids x 2^14 (fp32, exact scaling)
     const float* lut_f32 = nullptr;    // dequant LUT: 2^(P b) entries of P fp32 (P = lut_group(b))
     const _Float16* lut_f16 = nullptr; // same in fp16
+    const _Float16* lut_hl = nullptr;  // per entry: P fp16 hi parts, then P fp16 lo parts of 2^12 x centroid
     const float* signs_slot = nullptr; // [head][4][d/4] ±1 of coordinate in_coord(d, s, g)
     const float* signs = nullptr;      // [head][d] ±1
     const _Float16* S = nullptr;       // [head][m][d] fp16 Gaussian

@@ -87,12 +87,18 @@ int build_tables(const tq_params* p, int device, DevTables* out) {  // caller ho
 
     const int P = lut_group(b), NE = 1 << (P * b);
     std::vector<float> lut32((size_t)NE * P);
-    std::vector<uint16_t> lut16((size_t)NE * P);
+    std::vector<uint16_t> lut16((size_t)NE * P), luthl((size_t)NE * P * 2);
     for (int f = 0; f < NE; ++f)
         for (int k = 0; k < P; ++k) {
             const int idx = (f >> (k * b)) & (L - 1);
             lut32[(size_t)f * P + k] = cent_f[idx];
             lut16[(size_t)f * P + k] = f32_to_f16_bits(cent_f[idx]);
+            // fp16 hi + lo of 2^12 c, = 2^12 times the fp32 centroid to 2^-22 relative (the difference
+            // is exact; the 2^12 keeps lo out of the fp16 subnormal range)
+            const float cs = cent_f[idx] * 4096.0f;
+            const uint16_t hi = f32_to_f16_bits(cs);
+            luthl[(size_t)f * 2 * P + k] = hi;
+            luthl[(size_t)f * 2 * P + P + k] = f32_to_f16_bits(cs - f16_bits_to_f32(hi));
         }
 
     std::vector<float> signs((size_t)H * d), signs_slot((size_t)H * d), sh;
@@ -117,6 +123,7 @@ int build_tables(const tq_params* p, int device, DevTables* out) {  // caller ho
     const int64_t o_centk = blob.add(cent_k.data(), L * 4);
     const int64_t o_l32 = blob.add(lut32.data(), lut32.size() * 4);
     const int64_t o_l16 = blob.add(lut16.data(), lut16.size() * 2);
+    const int64_t o_lhl = blob.add(luthl.data(), luthl.size() * 2);
     const int64_t o_ss = blob.add(signs_slot.data(), signs_slot.size() * 4);
     const int64_t o_sg = blob.add(signs.data(), signs.size() * 4);
     const int64_t o_S = m > 0 ? blob.add(S.data(), S.size() * 2) : 0;
@@ -136,6 +143,7 @@ int build_tables(const tq_params* p, int device, DevTables* out) {  // caller ho
     t.cent_x1024 = reinterpret_cast<const float*>(base + o_centk);
     t.lut_f32 = reinterpret_cast<const float*>(base + o_l32);
     t.lut_f16 = reinterpret_cast<const _Float16*>(base + o_l16);
+    t.lut_hl = reinterpret_cast<const _Float16*>(base + o_lhl);
     t.signs_slot = reinterpret_cast<const float*>(base + o_ss);
     t.signs = reinterpret_cast<const float*>(base + o_sg);
     t.S = m > 0 ? reinterpret_cast<const _Float16*>(base + o_S) : nullptr;
