@@ -34,17 +34,17 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published (the sketch p
 # the kernel's sources are the ones it was measured on (sha256 of the .hip file + shared headers).
 FETCH_UNIT_B, WRITE_UNIT_B = 2048, 1024
 TRAFFIC = {
-    "encode_k": {"fetch": 2098027.125, "write": 1390973.90625, "src": "encode.hip",
-                 "sha": "28642df3117ae8d8603b339b5d3893f75fc9088930f7d207c1dc69212aa631b5"},
-    "encode_v": {"fetch": 2097226.1875, "write": 1092480.34375, "src": "encode.hip",
-                 "sha": "28642df3117ae8d8603b339b5d3893f75fc9088930f7d207c1dc69212aa631b5"},
-    "decode_attention": {"fetch": 1230639.4375, "write": 8320.0, "src": "attention.hip",     # split-K kernel
-                         "sha": "d6d9fe87fdf22523ebc2d32f1f654e6d20c4212285b45c5e7426e6829f2d7689"},
-    "decode_v_bf16": {"fetch": 553413.4375, "write": 4235279.3125, "src": "decode.hip",
-                      "sha": "9a2ad666db3693ec7c2275b537ca6064e4fb2abca123ed9db201e01c5c0771cd"},
+    "encode_k": {"fetch": 2098025.375, "write": 1391707.84375, "src": "encode.hip",
+        "sha": "96bbda8c00975444861aa8b7e569fce557d7b872f6c2719db99a63d417063e34"},
+    "encode_v": {"fetch": 2097223.25, "write": 1092332.84375, "src": "encode.hip",
+        "sha": "96bbda8c00975444861aa8b7e569fce557d7b872f6c2719db99a63d417063e34"},
+    "decode_attention": {"fetch": 1229638.5625, "write": 4160.0, "src": "attention.hip",
+        "sha": "928a924af0421b170117dd4d03b4a24eb397a6d49842374465a8112789982bec"},
+    "decode_v_bf16": {"fetch": 551138.8125, "write": 4194304.0, "src": "decode.hip",
+        "sha": "5a3129d3790b8270d5ecf5a4d85b72e2f8f55ccf96c6adabbec4f1d0b6e5fda1"},
 }
-TRAFFIC_HEADERS_SHA = ("01ae2d556f9fd52ae7d358b78db3db73ba040c21c4b22c480403fb0ae957946c"   # common.hpp
-                       "975bef9109dcb956abdef4d6ffd92c4b63ddfbb2d89263b94ff3ae72c906a3c1")  # kernels.hpp
+TRAFFIC_HEADERS_SHA = ("9241f7e7fc6398e3b61bd782d033f3beac2c8fe34392745cceb9f2f364e6409c"   # common.hpp
+                       "377a1b066127f7208daee3eefdc2a15cc9ce6d34cd3fada46c623eb8e04674af")  # kernels.hpp
 
 
 def _sha(path: str) -> str:
