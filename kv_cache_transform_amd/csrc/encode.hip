@@ -260,44 +260,70 @@ __global__ __launch_bounds__(256, ((D > 128 && (QJL || !BF16)) || (QJL && !BF16)
 
         if constexpr (QJL) {
             const _Float16* Sg = S_LDS ? (lds_S + 8 * lane) : (a.t.S + ((int64_t)head * m + row_base) * D + g * C);
-            // sketch bits of lane part g: rows [g m/4, (g+1) m/4), 32 per word; within a word the
-            // 8 tiles are visited in descending order and each z shifts its sign bit in at bit 0
-            // (alignbit), so bit p ends up holding row p; the word is inverted at the end (z >= 0).
+            // sketch bits of lane part g: rows [g m/4, (g+1) m/4), 32 per word; tile tt of a word
+            // holds rows 4 tt + i (bit 4 tt + i).  The products run k-step outer, tile inner, so
+            // the 8 tiles' accumulations are independent MFMA chains and the S reads of later steps
+            // can be in flight meanwhile.  Bits are gathered as one byte per tile pair (alignbit
+            // shifts each sign in at bit 0), the bytes joined, and the word inverted (z >= 0).
             // Full words run branch-free; a trailing partial word (m/4 not a multiple of 32) has
             // nt < 8 tiles.
             auto sketch_word = [&](int wb, int nt, auto full) {
                 constexpr bool FULL = decltype(full)::value;
-                uint32_t bits[NG];
+                const int tau0 = wb >> 2;
+                uint32_t by[NG][4];
 #pragma unroll
-                for (int gi = 0; gi < NG; ++gi) bits[gi] = 0u;
+                for (int hf = 0; hf < 2; ++hf) {                // tiles 4 hf .. 4 hf + 3: bytes 2 hf, 2 hf + 1
+                    floatx4 acc[NG][4];
 #pragma unroll
-                for (int tt = 7; tt >= 0; --tt) {
-                    if (FULL || tt < nt) {
-                        const int tau = (wb >> 2) + tt;
-                        floatx4 acc[NG];
+                    for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
-                        for (int gi = 0; gi < NG; ++gi) acc[gi] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+                        for (int tl = 0; tl < 4; ++tl) acc[gi][tl] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-                        for (int k = 0; k < KS; ++k) {
-                            const half8 A = *reinterpret_cast<const half8*>(
-                                S_LDS ? Sg + (tau * KS + k) * 512 : Sg + 4 * tau * D + 8 * k);
+                    for (int k = 0; k < KS; ++k) {
 #pragma unroll
-                            for (int gi = 0; gi < NG; ++gi) {
-                                acc[gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bh[gi][k], acc[gi], 0, 0, 0);
-                                acc[gi] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bl[gi][k], acc[gi], 0, 0, 0);
+                        for (int tl = 0; tl < 4; ++tl) {
+                            const int tt = 4 * hf + tl;
+                            if (FULL || tt < nt) {
+                                const int tau = tau0 + tt;
+                                const half8 A = *reinterpret_cast<const half8*>(
+                                    S_LDS ? Sg + (tau * KS + k) * 512 : Sg + 4 * tau * D + 8 * k);
+#pragma unroll
+                                for (int gi = 0; gi < NG; ++gi) {
+                                    acc[gi][tl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bh[gi][k], acc[gi][tl], 0, 0, 0);
+                                    acc[gi][tl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bl[gi][k], acc[gi][tl], 0, 0, 0);
+                                }
                             }
                         }
+                    }
 #pragma unroll
-                        for (int gi = 0; gi < NG; ++gi)
+                    for (int gi = 0; gi < NG; ++gi)
 #pragma unroll
-                            for (int i = 3; i >= 0; --i) bits[gi] = __builtin_amdgcn_alignbit(bits[gi], f2u(acc[gi][i]), 31);
+                        for (int j = 2 * hf; j < 2 * hf + 2; ++j) {
+                            by[gi][j] = 0u;
+#pragma unroll
+                            for (int tt = 2 * j + 1; tt >= 2 * j; --tt)
+                                if (FULL || tt < nt)
+#pragma unroll
+                                    for (int i = 3; i >= 0; --i)
+                                        by[gi][j] = __builtin_amdgcn_alignbit(by[gi][j], f2u(acc[gi][tt - 4 * hf][i]), 31);
+                        }
+                }
+                if constexpr (FULL && NG == 1) {
+                    // issue order: the first kPD S reads, then per step its two MFMAs and the read
+                    // kPD steps ahead, so each read has kPD steps of matrix work to land
+                    constexpr int kPD = 4;
+                    __builtin_amdgcn_sched_group_barrier(0x100, kPD, 0);
+#pragma unroll
+                    for (int p = 0; p < 8 * KS; ++p) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                        if (p + kPD < 8 * KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                     }
                 }
                 const int nb = FULL ? 4 : (nt >> 1);          // bytes in this word
 #pragma unroll
                 for (int gi = 0; gi < NG; ++gi) {
+                    const uint32_t bw = ~((((by[gi][3] << 8) | by[gi][2]) << 16) | ((by[gi][1] << 8) | by[gi][0]));
                     if (validv[gi]) {
-                        const uint32_t bw = ~bits[gi];
                         uint8_t* dst = a.packed + a.off_sketch + vecv[gi] * (int64_t)(m / 8) + g * (m / 32) + (wb >> 3);
                         if (FULL && (m & 127) == 0) *reinterpret_cast<uint32_t*>(dst) = bw;
                         else if (nb == 2 && (m & 63) == 0) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)bw;
