@@ -15,10 +15,13 @@
  *   - WHT = unnormalised Sylvester Hadamard matrix H in natural order; inverse s ⊙ (H ŷ)/sqrt(d).
  *   - Vectors are normalised by their exact norm n before rotation; n is stored as fp16 (RNE).
  *   - idx_j = #{i : t_i <= y_j} over the 2^b - 1 thresholds (ties go up), centroids ascending.
- *   - QJL (m > 0): z = S_h e with S_h an m x d matrix of N(0,1) draws rounded to fp16;
- *     sketch bit i = [z_i >= 0]; the fp16 (RNE) residual norm ||e|| is stored too.
+ *   - QJL (m > 0): z = S_h e with S_h an m x d matrix of N(0,1) draws rounded to fp16, or, with
+ *     sketch = TQ_SKETCH_RHT, the randomized Hadamard sketch S_h = H diag(s2_h) (m = d; the pages'
+ *     sign(WHT(e ⊙ s2))); sketch bit i = [z_i >= 0]; the fp16 (RNE) residual norm ||e|| is stored
+ *     too.  Scores and attention use the same estimator for both kinds.
  *   - Random tables: SplitMix64 (Steele, Lea, Flood 2014) keyed by (seed, tag, head); signs use
- *     tag 1 (s_j = -1 iff bit 63 of word j), S uses tag 2 with Box-Muller (1958) on word pairs.
+ *     tag 1 (s_j = -1 iff bit 63 of word j), S uses tag 2 with Box-Muller (1958) on word pairs, the
+ *     RHT signs s2 use tag 3 like tag 1.
  *     The RNG head of stream st is st % n_heads.
  *
  * Packed tensor (one caller-allocated byte buffer, see tq_get_layout): four planes, each starting
@@ -33,7 +36,7 @@
  * `stream` (a hipStream_t; NULL = the null stream); device faults surface at the caller's next
  * synchronisation.  All device pointers are caller-owned and must be 16-byte aligned; the library
  * never allocates or frees caller-visible memory.  Internally it keeps a mutex-guarded cache of
- * read-only device tables (codebook, signs, S, search grid) per (device, d, b, m, n_heads, seed),
+ * read-only device tables (codebook, signs, S, search grid) per (device, d, b, m, n_heads, seed, sketch),
  * built on the host in fp64 on first use; tq_clear_cache() frees them.  Calls are thread-safe.
  * NaN/Inf inputs propagate unchecked.  A vector norm above 65504 is outside the fp16 norm format
  * and is stored as +Inf.
@@ -49,7 +52,7 @@ extern "C" {
 #endif
 
 #define TQ_OK 0
-#define TQ_EINVAL (-1)       /* bad value: d not in {64,128,256}, b not in 1..8, m % 32, null ptr, n <= 0 */
+#define TQ_EINVAL (-1)       /* bad value: d not in {64,128,256}, b not in 1..8, m % 32, sketch, null ptr, n <= 0 */
 #define TQ_EUNSUPPORTED (-2) /* valid but not built, e.g. an attention (b_K, b_V) pair not compiled */
 #define TQ_EALIGN (-3)       /* a device pointer is not 16-byte aligned */
 #define TQ_EWORKSPACE (-4)   /* workspace smaller than the matching *_workspace_bytes() */
@@ -57,12 +60,18 @@ extern "C" {
 
 typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
 
+/* Kind of the QJL sketch matrix S_h (tq_params.sketch). */
+#define TQ_SKETCH_GAUSSIAN 0 /* m rows of i.i.d. N(0,1) draws rounded to fp16 (tag 2) */
+#define TQ_SKETCH_RHT 1      /* randomized Hadamard: S_h = H diag(s2_h), s2_h the signs of tag 3, m = d
+                                ("Ablation...", §2 TurboQuant: b = sign(WHT(e ⊙ s2))) */
+
 typedef struct {
     int32_t d;        /* head_dim: 64, 128 or 256 */
     int32_t b;        /* codebook bits per coordinate, 1..8 */
-    int32_t m;        /* QJL sketch rows; 0 = no sketch; a multiple of 32, at most d */
+    int32_t m;        /* QJL sketch rows; 0 = no sketch; a multiple of 32, at most d (= d for RHT) */
     int32_t n_heads;  /* heads with distinct random state; stream st uses head st % n_heads */
     uint64_t seed;    /* keys the random signs and S */
+    int32_t sketch;   /* TQ_SKETCH_GAUSSIAN or TQ_SKETCH_RHT; ignored when m = 0 */
 } tq_params;
 
 typedef struct {

@@ -23,15 +23,17 @@ _DT = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}
 @dataclass(frozen=True)
 class Codec:
     """d: head_dim (64/128/256); b: codebook bits; m: QJL sketch rows (0 = none);
-    n_heads: heads with distinct random state (stream st uses head st % n_heads); seed."""
+    n_heads: heads with distinct random state (stream st uses head st % n_heads); seed;
+    sketch: 0 = Gaussian S, 1 = randomized Hadamard S = H diag(s2) (needs m = d)."""
     d: int
     b: int
     m: int = 0
     n_heads: int = 1
     seed: int = 0
+    sketch: int = 0
 
     def params(self) -> _lib.Params:
-        return _lib.Params(self.d, self.b, self.m, self.n_heads, self.seed & ((1 << 64) - 1))
+        return _lib.Params(self.d, self.b, self.m, self.n_heads, self.seed & ((1 << 64) - 1), self.sketch)
 
 
 def _stream(device=None) -> ctypes.c_void_p:

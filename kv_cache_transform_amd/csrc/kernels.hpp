@@ -9,6 +9,7 @@ namespace tq {
 struct DevTables {
     int d = 0, b = 0, m = 0, n_heads = 0;
     uint64_t seed = 0;
+    int sketch = 0;                    // TQ_SKETCH_GAUSSIAN or TQ_SKETCH_RHT
     int G = 0;                         // search grid cells
     const uint32_t* grid = nullptr;    // (G+2) x {thr fp32 bits, base}
     const float* cent = nullptr;       // 2^b centroids (fp32)
@@ -18,7 +19,7 @@ struct DevTables {
     const _Float16* lut_hl = nullptr;  // per entry: P fp16 hi parts, then P fp16 lo parts of 2^12 x centroid
     const float* signs_slot = nullptr; // [head][4][d/4] ±1 of coordinate in_coord(d, s, g)
     const float* signs = nullptr;      // [head][d] ±1
-    const _Float16* S = nullptr;       // [head][m][d] fp16 Gaussian
+    const _Float16* S = nullptr;       // [head][m][d] fp16: Gaussian draws, or ±1 of H diag(s2) (m = d)
     void* blob = nullptr;              // single allocation owning all of the above
 };
 

@@ -32,6 +32,21 @@ void head_signs(uint64_t seed, uint32_t head, int d, std::vector<float>& out) {
     }
 }
 
+void rht_matrix_f16(uint64_t seed, uint32_t head, int d, std::vector<uint16_t>& out) {
+    out.resize((size_t)d * d);
+    std::vector<int> s2(d);
+    uint64_t st = stream_key(seed, 3, head);
+    for (int j = 0; j < d; ++j) {
+        st += kGamma;
+        s2[j] = (mix64(st) >> 63) ? -1 : 1;
+    }
+    for (int i = 0; i < d; ++i)
+        for (int j = 0; j < d; ++j) {
+            const int v = ((__builtin_popcount((unsigned)(i & j)) & 1) ? -1 : 1) * s2[j];
+            out[(size_t)i * d + j] = v > 0 ? 0x3c00u : 0xbc00u;   // fp16 +1 / -1
+        }
+}
+
 uint16_t f64_to_f16_bits(double f) {
     _Float16 h = (_Float16)f;  // fptrunc double -> half: a single round-to-nearest-even
     uint16_t r;

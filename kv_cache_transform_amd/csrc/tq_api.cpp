@@ -26,6 +26,8 @@ int check_params(const tq_params* p) {
     if (p->b < 1 || p->b > 8) return TQ_EINVAL;
     if (p->m < 0 || p->m % 32 != 0 || p->m > p->d) return TQ_EINVAL;
     if (p->n_heads < 1) return TQ_EINVAL;
+    if (p->sketch != TQ_SKETCH_GAUSSIAN && p->sketch != TQ_SKETCH_RHT) return TQ_EINVAL;
+    if (p->sketch == TQ_SKETCH_RHT && p->m != 0 && p->m != p->d) return TQ_EINVAL;
     return TQ_OK;
 }
 
@@ -59,7 +61,7 @@ const Codebook& codebook(int d, int b) {  // caller holds g_mu
 }
 
 // ---- device table cache ----------------------------------------------------------------------
-using TableKey = std::tuple<int, int, int, int, int, uint64_t>;  // device, d, b, m, n_heads, seed
+using TableKey = std::tuple<int, int, int, int, int, uint64_t, int>;  // device, d, b, m, n_heads, seed, sketch
 std::map<TableKey, DevTables> g_tables;
 std::map<int, int> g_num_cus;
 
@@ -112,7 +114,8 @@ int build_tables(const tq_params* p, int device, DevTables* out) {  // caller ho
                 signs_slot[((size_t)h * 4 + g) * C + s] = sh[i];
             }
         if (m > 0) {
-            gaussian_matrix_f16(p->seed, h, m, d, Sh);
+            if (p->sketch == TQ_SKETCH_RHT) rht_matrix_f16(p->seed, h, d, Sh);
+            else gaussian_matrix_f16(p->seed, h, m, d, Sh);
             std::memcpy(&S[(size_t)h * m * d], Sh.data(), (size_t)m * d * 2);
         }
     }
@@ -136,7 +139,7 @@ int build_tables(const tq_params* p, int device, DevTables* out) {  // caller ho
     }
     uint8_t* base = static_cast<uint8_t*>(dev);
     DevTables t;
-    t.d = d; t.b = b; t.m = m; t.n_heads = H; t.seed = p->seed;
+    t.d = d; t.b = b; t.m = m; t.n_heads = H; t.seed = p->seed; t.sketch = p->sketch;
     t.G = grid.G;
     t.grid = reinterpret_cast<const uint32_t*>(base + o_grid);
     t.cent = reinterpret_cast<const float*>(base + o_cent);
@@ -173,7 +176,7 @@ int get_tables(const tq_params* p, DevTables* out, int* num_cus) {
     if (hipGetDevice(&device) != hipSuccess) return TQ_EHIP;
     if (device_cus(num_cus) != TQ_OK) return TQ_EHIP;
     std::lock_guard<std::mutex> lk(g_mu);
-    const TableKey key{device, p->d, p->b, p->m, p->n_heads, p->seed};
+    const TableKey key{device, p->d, p->b, p->m, p->n_heads, p->seed, p->sketch};
     auto it = g_tables.find(key);
     if (it != g_tables.end()) {
         *out = it->second;
@@ -271,7 +274,8 @@ int tq_host_tables(const tq_params* p, int32_t head, double* thresholds, double*
     }
     if (S && p->m > 0) {
         std::vector<uint16_t> h;
-        gaussian_matrix_f16(p->seed, head, p->m, p->d, h);
+        if (p->sketch == TQ_SKETCH_RHT) rht_matrix_f16(p->seed, head, p->d, h);
+        else gaussian_matrix_f16(p->seed, head, p->m, p->d, h);
         for (size_t i = 0; i < h.size(); ++i) S[i] = f16_bits_to_f32(h[i]);
     }
     return TQ_OK;

@@ -24,7 +24,8 @@ Readings where the pages are silent (each listed in the design doc):
   * WHT is the unnormalised Sylvester-ordered Hadamard matrix H (H_2n = [[H, H], [H, -H]]).
   * Codebook index = number of thresholds <= y (ties go to the upper cell), centroids ascending.
   * Vectors are normalised by their exact norm; the norm is stored as fp16 (round to nearest even).
-  * QJL uses a seeded Gaussian S (m x d) on the WHT-domain residual; sign(0) = +1.
+  * QJL uses a seeded Gaussian S (m x d) on the WHT-domain residual, or the randomized Hadamard
+    sketch S = H diag(s2) (m = d); sign(0) = +1.
   * Random signs and S come from SplitMix64 keyed by (seed, tag, head); Gaussians by Box-Muller.
 """
 from __future__ import annotations
@@ -41,6 +42,7 @@ GAMMA = 0x9E3779B97F4A7C15
 _M64 = (1 << 64) - 1
 TAG_SIGNS = 1
 TAG_GAUSS = 2
+TAG_RHT = 3
 
 
 def mix64(z: int) -> int:
@@ -99,6 +101,20 @@ def gaussian_matrix(seed: int, head: int, m: int, d: int) -> np.ndarray:
         u2 = c[k] * sc
         out[k] = math.sqrt(-2.0 * math.log(u1)) * math.cos(two_pi * u2)
     return out.astype(np.float16).reshape(m, d)
+
+
+def rht_signs(seed: int, head: int, d: int) -> np.ndarray:
+    """Second sign vector s2 of the randomized Hadamard sketch ([AB] §2 TurboQuant: "a fixed sign
+    vector s2"), drawn like the rotation signs but from tag 3."""
+    w = words(stream_key(seed, TAG_RHT, head), d)
+    return np.where((w >> np.uint64(63)) == 1, -1.0, 1.0)
+
+
+def rht_matrix(seed: int, head: int, d: int) -> np.ndarray:
+    """The randomized Hadamard sketch as a matrix: S = H diag(s2) (d x d, entries ±1), so that
+    S e = WHT(e ⊙ s2) ([AB] §2 TurboQuant, b = sign(WHT(e ⊙ s2))) and the estimator of the Gaussian
+    case applies with m = d.  fp16 holds ±1 exactly."""
+    return (hadamard(d) * rht_signs(seed, head, d)[None, :]).astype(np.float16)
 
 
 # ----------------------------------------------------------------------------------------------
@@ -205,6 +221,22 @@ def hadamard(d: int) -> np.ndarray:
     return linalg.hadamard(d).astype(np.float64)
 
 
+def fwht(v: np.ndarray) -> np.ndarray:
+    """Unnormalised Walsh-Hadamard transform along the last axis by radix-2 butterflies (natural
+    order: the pair (j, j + h) of each stage becomes (a + b, a - b)); equals v @ H."""
+    v = np.array(v, dtype=np.float64, copy=True)
+    d = v.shape[-1]
+    h = 1
+    while h < d:
+        w = v.reshape(v.shape[:-1] + (d // (2 * h), 2, h))
+        a, b = w[..., 0, :].copy(), w[..., 1, :].copy()
+        w[..., 0, :] = a + b
+        w[..., 1, :] = a - b
+        v = w.reshape(v.shape)
+        h *= 2
+    return v
+
+
 def rotate(u: np.ndarray, s: np.ndarray) -> np.ndarray:
     d = u.shape[-1]
     return (u * s) @ hadamard(d) / math.sqrt(d)          # H is symmetric
@@ -265,9 +297,23 @@ def encode(x: np.ndarray, s: np.ndarray, thresholds: np.ndarray, centroids: np.n
     return out
 
 
-def decode(idx: np.ndarray, n16: np.ndarray, s: np.ndarray, centroids: np.ndarray) -> np.ndarray:
-    """x̂ = n16 · s ⊙ (H c[idx]) / sqrt(d)  (the MSE reconstruction; QJL is not applied)."""
+def qjl_correction(sigma: np.ndarray, r16: np.ndarray, S: np.ndarray) -> np.ndarray:
+    """WHT-domain QJL correction Δŷ = sqrt(pi/2)/m · ||e|| · S^T (2σ - 1) per row ([AB] §2
+    TurboQuant: sqrt(pi/2)/d · ||e|| · s2 ⊙ WHT(b) for S = H diag(s2), m = d; the same form with
+    the Gaussian S), with ||e|| the stored r16."""
+    S = np.asarray(S, dtype=np.float64)
+    m = S.shape[0]
+    pm = 2.0 * np.asarray(sigma, dtype=np.float64) - 1.0
+    return math.sqrt(math.pi / 2.0) / m * np.asarray(r16, dtype=np.float64)[:, None] * (pm @ S)
+
+
+def decode(idx: np.ndarray, n16: np.ndarray, s: np.ndarray, centroids: np.ndarray,
+           corr: np.ndarray | None = None) -> np.ndarray:
+    """x̂ = n16 · s ⊙ (H (c[idx] + Δŷ)) / sqrt(d); Δŷ = corr (qjl_correction) or 0 for the MSE
+    reconstruction."""
     y_hat = centroids[np.asarray(idx)]
+    if corr is not None:
+        y_hat = y_hat + corr
     return np.asarray(n16, dtype=np.float64)[:, None] * unrotate(y_hat, s)
 
 

@@ -30,11 +30,18 @@ def codebook(d, b):
 
 
 class Tables:
-    def __init__(self, d, b, m, n_heads, seed):
-        self.d, self.b, self.m, self.n_heads, self.seed = d, b, m, n_heads, seed
+    def __init__(self, d, b, m, n_heads, seed, sketch=0):
+        """sketch: 0 = Gaussian S (m x d), 1 = randomized Hadamard S = H diag(s2) (m = d)."""
+        self.d, self.b, self.m, self.n_heads, self.seed, self.sketch = d, b, m, n_heads, seed, sketch
         self.t, self.c = codebook(d, b)
         self.s = [O.head_signs(seed, h, d) for h in range(n_heads)]
-        self.S = [O.gaussian_matrix(seed, h, m, d).astype(np.float64) for h in range(n_heads)] if m else None
+        if not m:
+            self.S = None
+        elif sketch == 1:
+            assert m == d
+            self.S = [O.rht_matrix(seed, h, d).astype(np.float64) for h in range(n_heads)]
+        else:
+            self.S = [O.gaussian_matrix(seed, h, m, d).astype(np.float64) for h in range(n_heads)]
 
     def head(self, st):
         return st % self.n_heads

@@ -61,6 +61,14 @@ def test_host_signs_and_S_match_oracle_exactly(seed, head, d, m):
     assert np.array_equal(h["S"], O.gaussian_matrix(seed, head, m, d).astype(np.float32))
 
 
+@pytest.mark.parametrize("seed,head,d", [(4001, 0, 128), (77, 5, 64), (2**63 + 3, 1, 256)])
+def test_host_rht_sketch_matches_oracle_exactly(seed, head, d):
+    _lib_or_skip()
+    h = T.host_tables(T.Codec(d, 3, d, head + 1, seed, sketch=_lib.TQ_SKETCH_RHT), head)
+    assert np.array_equal(h["signs"], O.head_signs(seed, head, d).astype(np.float32))
+    assert np.array_equal(h["S"], O.rht_matrix(seed, head, d).astype(np.float32))
+
+
 def test_status_strings():
     _lib_or_skip()
     for s in (0, -1, -2, -3, -4, -5):
@@ -68,15 +76,16 @@ def test_status_strings():
     assert _lib.status_string(-99) == "unknown status"
 
 
-def _p(d=128, b=4, m=0, H=1, seed=0):
-    return ctypes.byref(_lib.Params(d, b, m, H, seed))
+def _p(d=128, b=4, m=0, H=1, seed=0, sketch=0):
+    return ctypes.byref(_lib.Params(d, b, m, H, seed, sketch))
 
 
 def test_argument_validation_before_any_gpu_call():
     L = _lib_or_skip()
     lay = _lib.Layout()
     bad = [(_p(d=96), "d"), (_p(d=32), "d"), (_p(b=0), "b"), (_p(b=9), "b"), (_p(m=48), "m%32"),
-           (_p(m=256, d=128), "m>d"), (_p(H=0), "n_heads")]
+           (_p(m=256, d=128), "m>d"), (_p(H=0), "n_heads"), (_p(m=128, sketch=2), "sketch kind"),
+           (_p(m=64, sketch=1), "RHT needs m = d"), (_p(sketch=-1), "sketch kind")]
     for p, why in bad:
         assert L.tq_get_layout(p, 1, 1, ctypes.byref(lay)) == _lib.TQ_EINVAL, why
         assert L.tq_encode(p, ctypes.c_void_p(16), 1, 1, 1, ctypes.c_void_p(16), None) == _lib.TQ_EINVAL, why

@@ -135,15 +135,15 @@ def test_cfg3_reduced_scores(b, m, nq):
     print(f"scores b={b} m={m}: worst row rel L2 {worst:.2e}")
 
 
-def _attention_case(batch, hq, hkv, N, d, b, m, out_dtype, seed=4001, scale=0.0):
-    ck, cv = T.Codec(d, b, m, hkv, seed), T.Codec(d, b, 0, hkv, seed + 1)
+def _attention_case(batch, hq, hkv, N, d, b, m, out_dtype, seed=4001, scale=0.0, sketch=0):
+    ck, cv = T.Codec(d, b, m, hkv, seed, sketch), T.Codec(d, b, 0, hkv, seed + 1)
     K = I.rope_gaussian(batch * hkv, N, d, seed, device=DEV)
     V = I.rope_gaussian(batch * hkv, N, d, seed + 1, device=DEV)
     q = I.cfg4_queries(batch, hq, d, N, seed + 2, device=DEV)
     pk, pv = T.encode(ck, K), T.encode(cv, V)
     out = T.decode_attention(ck, cv, q, pk, pv, hkv, N, scale, out_dtype=out_dtype)
     torch.cuda.synchronize()
-    tk, tv = P.Tables(d, b, m, hkv, seed), P.Tables(d, b, 0, hkv, seed + 1)
+    tk, tv = P.Tables(d, b, m, hkv, seed, sketch), P.Tables(d, b, 0, hkv, seed + 1)
     rk = O.unpack_tensor(pk.cpu().numpy(), d, b, m, batch * hkv, N)
     rv = O.unpack_tensor(pv.cpu().numpy(), d, b, 0, batch * hkv, N)
     q64 = _x64(q)
@@ -170,6 +170,33 @@ def test_decode_attention_reduced(batch, hq, hkv, N, d, b, m):
     eb, rowb = _attention_case(batch, hq, hkv, N, d, b, m, torch.bfloat16)
     print(f"attention {batch}x{hq}/{hkv} N={N} d={d} b={b} m={m}: rel L2 f32 {e32:.2e} (row max {row32:.2e}),"
           f" bf16 {eb:.2e} (row max {rowb:.2e})")
+    assert e32 <= 2e-3 and eb <= 2e-3
+
+
+# ---------------------------------------------------------------------------------------------
+# randomized Hadamard sketch (S = H diag(s2), m = d)
+@pytest.mark.parametrize("d,b,dt", [(64, 3, torch.bfloat16), (128, 2, torch.bfloat16), (128, 4, torch.bfloat16),
+                                    (256, 3, torch.bfloat16), (128, 3, torch.float32)])
+def test_rht_encode_decode_scores_parity(d, b, dt):
+    S, N, H, nq, seed = 3, 700, 2, 9, 6100 + d + b
+    codec = T.Codec(d, b, d, H, seed, sketch=1)
+    x = I.gaussian((S, N, d), seed, device=DEV, dtype=dt)
+    buf = _enc(codec, x)
+    tb = P.Tables(d, b, d, H, seed, sketch=1)
+    st = P.check_encode(tb, _x64(x), buf)
+    out = T.decode(codec, torch.as_tensor(buf, device=DEV), S, N, torch.float32).cpu().numpy()
+    P.check_decode_f32(tb, st["recs"], list(range(S)), out)
+    q = I.gaussian((S, nq, d), seed + 5, device=DEV)
+    sc = T.qk_scores(codec, q, torch.as_tensor(buf, device=DEV), N).cpu().numpy()
+    worst = P.check_scores(tb, st["recs"], list(range(S)), _x64(q), sc)
+    print(f"rht d={d} b={b}: flagged={st['flagged']} sketch_flagged={st['sketch_flagged']} scores row max {worst:.2e}")
+
+
+@pytest.mark.parametrize("batch,hq,hkv,N,d,b", [(2, 8, 2, 3000, 128, 4), (1, 4, 2, 900, 256, 3), (1, 8, 1, 500, 64, 4)])
+def test_rht_decode_attention(batch, hq, hkv, N, d, b):
+    e32, _ = _attention_case(batch, hq, hkv, N, d, b, d, torch.float32, sketch=1)
+    eb, _ = _attention_case(batch, hq, hkv, N, d, b, d, torch.bfloat16, sketch=1)
+    print(f"rht attention d={d} b={b}: rel L2 f32 {e32:.2e}, bf16 {eb:.2e}")
     assert e32 <= 2e-3 and eb <= 2e-3
 
 

@@ -92,3 +92,35 @@ def test_softmax_over_wrong_axis_is_caught(monkeypatch):
     real = O.softmax
     monkeypatch.setattr(O, "softmax", lambda x, axis=-1: real(x, axis=0))
     _fails(CC.test_attention_rotated_equals_dense)
+
+
+# ---- randomized Hadamard sketch and the QJL decode correction ----------------------------------
+from tests import test_oracle_rht as RH  # noqa: E402
+
+
+def test_rht_without_second_signs_is_caught(monkeypatch):
+    monkeypatch.setattr(O, "rht_matrix", lambda seed, head, d: O.hadamard(d).astype(np.float16))
+    _fails(RH.test_rht_matrix_is_hadamard_times_second_signs)
+
+
+def test_rht_signs_from_the_rotation_tag_are_caught(monkeypatch):
+    monkeypatch.setattr(O, "rht_signs", lambda seed, head, d: O.head_signs(seed, head, d))
+    _fails(RH.test_rht_signs_balanced_and_distinct_from_rotation_signs)
+
+
+def test_correction_without_sqrt_is_caught(monkeypatch):
+    def corr(sigma, r16, S):
+        S = np.asarray(S, dtype=np.float64)
+        pm = 2.0 * np.asarray(sigma, dtype=np.float64) - 1.0
+        return (math.pi / 2.0) / S.shape[0] * np.asarray(r16, dtype=np.float64)[:, None] * (pm @ S)
+    monkeypatch.setattr(O, "qjl_correction", corr)
+    _fails(RH.test_correction_closed_form_on_a_hadamard_column)
+
+
+def test_correction_through_S_instead_of_S_transpose_is_caught(monkeypatch):
+    def corr(sigma, r16, S):
+        S = np.asarray(S, dtype=np.float64)
+        pm = 2.0 * np.asarray(sigma, dtype=np.float64) - 1.0
+        return math.sqrt(math.pi / 2.0) / S.shape[0] * np.asarray(r16, dtype=np.float64)[:, None] * (pm @ S.T)
+    monkeypatch.setattr(O, "qjl_correction", corr)
+    _fails(RH.test_correction_closed_form_on_a_hadamard_column)
