@@ -175,6 +175,21 @@ def main():
                              "hbm_frac": round(dec_alg / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     del xh
 
+    # the same K encode with the randomized Hadamard sketch (S = H diag(s2), m = d = 128): the
+    # sketch is one more 32-point transform of the residual, not a dense m x d product
+    ck_rht = T.Codec(d, 4, 128, Hkv, 4001, sketch=1)
+    T.encode(ck_rht, K, pk)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(3):
+        T.encode(ck_rht, K, pk)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    rms = e0.elapsed_time(e1) / 3
+    kern["encode_k_rht"] = {"ms": round(rms, 4), "alg_bytes": alg["encode_k"],
+                            "achieved_GBs": round(alg["encode_k"] / (rms * 1e-3) / 1e9, 1),
+                            "hbm_frac": round(alg["encode_k"] / (rms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
     copy = copy_ceiling(torch, dev, stream)
     del K, V
     torch.cuda.empty_cache()
@@ -244,7 +259,8 @@ def other_workloads(torch, T, I, dev, stream) -> dict:
     """Per-kernel lines (not part of `value`) for the other workload shapes: encode / decode of
     outlier-channel K,V (32 heads x 32768 x 128, b = 4), encode with a QJL sketch and q.k scores
     (8 heads x 65536 x 128, b = 3, m = 128, 32 queries per head), and heavy-tailed d = 256 vectors
-    (16 heads x 262144, Student-t nu = 3, b = 3, with and without a sketch of m = 256)."""
+    (16 heads x 262144, Student-t nu = 3, b = 3, with and without a sketch of m = 256); the sketch
+    encodes also with the randomized Hadamard sketch (m = d)."""
     out = {}
     H, N, d = 32, 32768, 128
     x = I.outlier_gaussian(H, N, d, 4, 10.0, 2001, device=dev)
@@ -271,17 +287,20 @@ def other_workloads(torch, T, I, dev, stream) -> dict:
                                                          nv * (256 + 48 + 16 + 4))
     out["gaussian K 8x65536x128 b3 m128: scores, 32 queries"] = _line(
         _time(torch, stream, lambda: T.qk_scores(c, q, pk, N, out=sc, workspace=ws)), nv * (48 + 16 + 4 + 4 * nq))
+    c = T.Codec(d, 3, 128, H, 3001, sketch=1)
+    out["gaussian K 8x65536x128 b3 RHT m128: encode"] = _line(_time(torch, stream, lambda: T.encode(c, x, pk)),
+                                                             nv * (256 + 48 + 16 + 4))
     del x, q, pk, sc, ws
 
     H, N, d = 16, 262144, 256
     x = I.student_t(H, N, d, 3, 5001, device=dev)
     nv = H * N
-    for m in (0, 256):
-        c = T.Codec(d, 3, m, H, 5004)
+    for m, kind in ((0, 0), (256, 0), (256, 1)):
+        c = T.Codec(d, 3, m, H, 5004, sketch=kind)
         pk = T.encode(c, x)
         rec = 96 + m // 8 + 2 + (2 if m else 0)
-        out[f"student-t K 16x262144x256 b3 m{m}: encode"] = _line(_time(torch, stream, lambda: T.encode(c, x, pk)),
-                                                                 nv * (512 + rec))
+        name = f"student-t K 16x262144x256 b3 {'RHT ' if kind else ''}m{m}: encode"
+        out[name] = _line(_time(torch, stream, lambda: T.encode(c, x, pk)), nv * (512 + rec))
         if m == 0:
             xh = torch.empty(H, N, d, dtype=torch.bfloat16, device=dev)
             out["student-t K 16x262144x256 b3: decode to bf16"] = _line(

@@ -56,7 +56,7 @@ __global__ __launch_bounds__(256, ((D > 128 && (QJL || !BF16)) || (QJL && !BF16)
     _Float16* lds_S = reinterpret_cast<_Float16*>(lds + a_off + NAW);
     if constexpr (QJL) {
         for (int i = threadIdx.x; i < L; i += blockDim.x) lds_c[i] = a.t.cent_x1024[i];
-        if constexpr (S_LDS) {
+        if (S_LDS && !(BF16 && a.t.sketch == 1)) {
             // S in the order the MFMA A operand reads it (see the sketch loop): the 16-byte piece
             // of lane l for row tile tau and k-step k sits at piece index (tau KS + k) 64 + l, so
             // every A read is one contiguous 1 KiB wave access.  Lane l = rho + 16 gp reads row
@@ -83,11 +83,17 @@ __global__ __launch_bounds__(256, ((D > 128 && (QJL || !BF16)) || (QJL && !BF16)
     //   H[output (mg, h, mi)][input (l/16, jj)] * sign of input coordinate (l/16) C + 8 kb + jj,
     // with output coordinate bits {n-2,n-1} = mg, bit 2 = h, bits {0,1} = mi.  The random signs of
     // the head are folded in, so the tiles are built per block in LDS (one 16-byte entry per lane).
+    // With the randomized Hadamard sketch (bf16 input), the same tiles with the second signs s2 and
+    // ±1 in fp16 take the place of S: the sketch z = H (e ⊙ s2) is the same transform of the residual.
     if constexpr (BF16) {
-        for (int e = threadIdx.x; e < 2 * NKB * 64; e += blockDim.x) {
-            const int l = e & 63, tile = e >> 6, h = tile / NKB, kb = tile - h * NKB;
+        const bool rht = QJL && a.t.sketch == 1;
+        for (int e = threadIdx.x; e < (rht ? 4 : 2) * NKB * 64; e += blockDim.x) {
+            const int second = e >= 2 * NKB * 64;       // an RHT tile
+            const int ee = second ? e - 2 * NKB * 64 : e;
+            const int l = ee & 63, tile = ee >> 6, h = tile / NKB, kb = tile - h * NKB;
             const int lg = l >> 4, mi = l & 3, mg = (l >> 2) & 3;
-            const float* sh = a.t.signs + (int64_t)head * D + lg * C + 8 * kb;
+            const float* sh = (second ? a.t.signs2 : a.t.signs) + (int64_t)head * D + lg * C + 8 * kb;
+            const uint32_t one = second ? 0x3c00u : 0x3f80u;   // fp16 / bf16 +1
             u32x4 wv;
 #pragma unroll
             for (int t = 0; t < 4; ++t) {
@@ -97,11 +103,12 @@ __global__ __launch_bounds__(256, ((D > 128 && (QJL || !BF16)) || (QJL && !BF16)
                     const int jj = 2 * t + q;
                     const uint32_t par = (uint32_t)((__builtin_popcount(mi & jj & 3) + h * (jj >> 2) +
                                                      __builtin_popcount(mg & lg)) & 1) ^ (f2u(sh[jj]) >> 31);
-                    w2 |= (0x3f80u | (par << 15)) << (16 * q);
+                    w2 |= (one | (par << 15)) << (16 * q);
                 }
                 wv[t] = w2;
             }
-            lds_A[e] = wv;
+            if (second) reinterpret_cast<u32x4*>(lds_S)[ee] = wv;
+            else lds_A[e] = wv;
         }
     }
     __syncthreads();
@@ -258,6 +265,53 @@ __global__ __launch_bounds__(256, ((D > 128 && (QJL || !BF16)) || (QJL && !BF16)
             }
         }
 
+        if constexpr (QJL && BF16) {
+          if (a.t.sketch == 1) {
+            // randomized Hadamard sketch z = H (e ⊙ s2) (m = d): the rotation's 32-point block on
+            // fp16 MFMA with the s2 tiles as A and the residual's exact hi then lo parts as B, then
+            // the middle-bit butterflies; slot p of part g is sketch row g C + p, so the part's C
+            // bits are its z slots in order (one byte per 8 slots via alignbit, inverted: z >= 0)
+            const u32x4* lds_A2 = reinterpret_cast<const u32x4*>(lds_S);
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+                float z[C];
+#pragma unroll
+                for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                    for (int h = 0; h < 2; ++h) {
+                        const half8 A = __builtin_bit_cast(half8, lds_A2[(h * NKB + kb) * 64 + lane]);
+                        floatx4 r = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bh[gi][kb], floatx4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                        r = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bl[gi][kb], r, 0, 0, 0);
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) z[8 * kb + 4 * h + i] = r[i];
+                    }
+                fwht_slots<C, 8>(z);
+                uint8_t* dst = a.packed + a.off_sketch + vecv[gi] * (int64_t)(D / 8) + g * (C / 8);
+#pragma unroll
+                for (int w = 0; w < (C + 31) / 32; ++w) {
+                    constexpr int NBY = C < 32 ? C / 8 : 4;      // bytes per word
+                    uint32_t by[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                    for (int j = 0; j < NBY; ++j)
+#pragma unroll
+                        for (int p = 8 * j + 7; p >= 8 * j; --p) by[j] = __builtin_amdgcn_alignbit(by[j], f2u(z[32 * w + p]), 31);
+                    const uint32_t bw = ~((((by[3] << 8) | by[2]) << 16) | ((by[1] << 8) | by[0]));
+                    if (validv[gi]) {
+                        if constexpr (NBY == 4) *reinterpret_cast<uint32_t*>(dst + 4 * w) = bw;
+                        else *reinterpret_cast<uint16_t*>(dst + 4 * w) = (uint16_t)bw;
+                    }
+                }
+            }
+#pragma unroll
+            for (int gi = 0; gi < NG; ++gi) {
+                const float e2 = sum4(e2v[gi]);
+                if (validv[gi] && g == 0)
+                    *reinterpret_cast<_Float16*>(a.packed + a.off_rnorm + vecv[gi] * 2) =
+                        (_Float16)(sqrtf(e2) * (1.0f / 16384.0f));
+            }
+            continue;
+          }
+        }
         if constexpr (QJL) {
             const _Float16* Sg = S_LDS ? (lds_S + 8 * lane) : (a.t.S + ((int64_t)head * m + row_base) * D + g * C);
             // sketch bits of lane part g: rows [g m/4, (g+1) m/4), 32 per word; tile tt of a word
@@ -368,7 +422,10 @@ static hipError_t launch_one(const EncodeArgs& a, int num_cus, hipStream_t s) {
     constexpr size_t kLdsMax = 163840;
     const size_t grid_bytes = (size_t)(a.t.G + 3) * 8;
     const size_t fixed = (size_t)(L + 4) * 4 + (BF16 ? (size_t)2 * (D / 32) * 64 * 16 : 0);
-    const size_t s_bytes = (size_t)a.t.m * D * 2;
+    // the randomized Hadamard sketch of bf16 input keeps its ±1 tiles (the size of the A tiles) in
+    // place of S
+    const bool rht_tiles = QJL && BF16 && a.t.sketch == 1;
+    const size_t s_bytes = rht_tiles ? (size_t)2 * (D / 32) * 64 * 16 : (size_t)a.t.m * D * 2;
     const bool s_lds = QJL && (D <= 128 || fixed + grid_bytes + s_bytes <= kLdsMax);   // always for d <= 128
     int rl = QJL ? 3 : 4;
     while (rl > 0 && ((grid_bytes << rl) > (QJL ? 8192u : 16384u) ||

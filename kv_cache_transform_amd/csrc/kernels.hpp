@@ -19,6 +19,7 @@ struct DevTables {
     const _Float16* lut_hl = nullptr;  // per entry: P fp16 hi parts, then P fp16 lo parts of 2^12 x centroid
     const float* signs_slot = nullptr; // [head][4][d/4] ±1 of coordinate in_coord(d, s, g)
     const float* signs = nullptr;      // [head][d] ±1
+    const float* signs2 = nullptr;     // [head][d] ±1 second signs of the RHT sketch (sketch = RHT only)
     const _Float16* S = nullptr;       // [head][m][d] fp16: Gaussian draws, or ±1 of H diag(s2) (m = d)
     void* blob = nullptr;              // single allocation owning all of the above
 };

@@ -32,17 +32,22 @@ void head_signs(uint64_t seed, uint32_t head, int d, std::vector<float>& out) {
     }
 }
 
-void rht_matrix_f16(uint64_t seed, uint32_t head, int d, std::vector<uint16_t>& out) {
-    out.resize((size_t)d * d);
-    std::vector<int> s2(d);
+void rht_signs(uint64_t seed, uint32_t head, int d, std::vector<float>& out) {
+    out.resize(d);
     uint64_t st = stream_key(seed, 3, head);
     for (int j = 0; j < d; ++j) {
         st += kGamma;
-        s2[j] = (mix64(st) >> 63) ? -1 : 1;
+        out[j] = (mix64(st) >> 63) ? -1.0f : 1.0f;
     }
+}
+
+void rht_matrix_f16(uint64_t seed, uint32_t head, int d, std::vector<uint16_t>& out) {
+    out.resize((size_t)d * d);
+    std::vector<float> s2;
+    rht_signs(seed, head, d, s2);
     for (int i = 0; i < d; ++i)
         for (int j = 0; j < d; ++j) {
-            const int v = ((__builtin_popcount((unsigned)(i & j)) & 1) ? -1 : 1) * s2[j];
+            const float v = ((__builtin_popcount((unsigned)(i & j)) & 1) ? -1.0f : 1.0f) * s2[j];
             out[(size_t)i * d + j] = v > 0 ? 0x3c00u : 0xbc00u;   // fp16 +1 / -1
         }
 }

@@ -14,8 +14,10 @@ uint64_t stream_key(uint64_t seed, uint32_t tag, uint32_t head);
 void head_signs(uint64_t seed, uint32_t head, int d, std::vector<float>& out);
 // S[row][col] = fp16_rne(sqrt(-2 ln u1) cos(2 pi u2)) from words (2e, 2e+1), e = row*d + col (tag 2)
 void gaussian_matrix_f16(uint64_t seed, uint32_t head, int m, int d, std::vector<uint16_t>& out);
-// randomized Hadamard sketch S = H diag(s2): S[i][j] = (-1)^popcount(i & j) · s2_j, with s2 the
-// signs of tag 3 (s2_j = -1 iff bit 63 of word j); d x d entries of ±1 as fp16
+// second signs s2 of the randomized Hadamard sketch: s2_j = -1 iff bit 63 of word j (tag 3)
+void rht_signs(uint64_t seed, uint32_t head, int d, std::vector<float>& out);
+// randomized Hadamard sketch S = H diag(s2): S[i][j] = (-1)^popcount(i & j) · s2_j; d x d entries
+// of ±1 as fp16
 void rht_matrix_f16(uint64_t seed, uint32_t head, int d, std::vector<uint16_t>& out);
 
 // ---- Lloyd-Max codebook for f(x) ∝ (1-x^2)^((d-3)/2) on [-1,1] ---------------------------------

@@ -103,7 +103,8 @@ int build_tables(const tq_params* p, int device, DevTables* out) {  // caller ho
             luthl[(size_t)f * 2 * P + P + k] = f32_to_f16_bits(cs - f16_bits_to_f32(hi));
         }
 
-    std::vector<float> signs((size_t)H * d), signs_slot((size_t)H * d), sh;
+    const bool rht = m > 0 && p->sketch == TQ_SKETCH_RHT;
+    std::vector<float> signs((size_t)H * d), signs_slot((size_t)H * d), signs2(rht ? (size_t)H * d : 0), sh;
     std::vector<uint16_t> S((size_t)H * m * d), Sh;
     for (int h = 0; h < H; ++h) {
         head_signs(p->seed, h, d, sh);
@@ -114,8 +115,13 @@ int build_tables(const tq_params* p, int device, DevTables* out) {  // caller ho
                 signs_slot[((size_t)h * 4 + g) * C + s] = sh[i];
             }
         if (m > 0) {
-            if (p->sketch == TQ_SKETCH_RHT) rht_matrix_f16(p->seed, h, d, Sh);
-            else gaussian_matrix_f16(p->seed, h, m, d, Sh);
+            if (rht) {
+                rht_matrix_f16(p->seed, h, d, Sh);
+                rht_signs(p->seed, h, d, sh);
+                std::memcpy(&signs2[(size_t)h * d], sh.data(), d * 4);
+            } else {
+                gaussian_matrix_f16(p->seed, h, m, d, Sh);
+            }
             std::memcpy(&S[(size_t)h * m * d], Sh.data(), (size_t)m * d * 2);
         }
     }
@@ -130,6 +136,7 @@ int build_tables(const tq_params* p, int device, DevTables* out) {  // caller ho
     const int64_t o_ss = blob.add(signs_slot.data(), signs_slot.size() * 4);
     const int64_t o_sg = blob.add(signs.data(), signs.size() * 4);
     const int64_t o_S = m > 0 ? blob.add(S.data(), S.size() * 2) : 0;
+    const int64_t o_s2 = rht ? blob.add(signs2.data(), signs2.size() * 4) : 0;
 
     void* dev = nullptr;
     if (hipMalloc(&dev, blob.host.size()) != hipSuccess) return TQ_EHIP;
@@ -139,7 +146,7 @@ int build_tables(const tq_params* p, int device, DevTables* out) {  // caller ho
     }
     uint8_t* base = static_cast<uint8_t*>(dev);
     DevTables t;
-    t.d = d; t.b = b; t.m = m; t.n_heads = H; t.seed = p->seed; t.sketch = p->sketch;
+    t.d = d; t.b = b; t.m = m; t.n_heads = H; t.seed = p->seed; t.sketch = rht ? TQ_SKETCH_RHT : TQ_SKETCH_GAUSSIAN;
     t.G = grid.G;
     t.grid = reinterpret_cast<const uint32_t*>(base + o_grid);
     t.cent = reinterpret_cast<const float*>(base + o_cent);
@@ -150,6 +157,7 @@ int build_tables(const tq_params* p, int device, DevTables* out) {  // caller ho
     t.signs_slot = reinterpret_cast<const float*>(base + o_ss);
     t.signs = reinterpret_cast<const float*>(base + o_sg);
     t.S = m > 0 ? reinterpret_cast<const _Float16*>(base + o_S) : nullptr;
+    t.signs2 = rht ? reinterpret_cast<const float*>(base + o_s2) : nullptr;
     t.blob = dev;
     (void)device;
     *out = t;
