@@ -189,9 +189,25 @@ def main():
     kern["encode_k_rht"] = {"ms": round(rms, 4), "alg_bytes": alg["encode_k"],
                             "achieved_GBs": round(alg["encode_k"] / (rms * 1e-3) / 1e9, 1),
                             "hbm_frac": round(alg["encode_k"] / (rms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    # and its decode to bf16 with the sketch correction added (84 B in, 256 B out per key)
+    del K
+    xh = torch.empty(streams, N, d, dtype=torch.bfloat16, device=dev)
+    T.decode(ck_rht, pk, streams, N, torch.bfloat16, out=xh, qjl=True)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(3):
+        T.decode(ck_rht, pk, streams, N, torch.bfloat16, out=xh, qjl=True)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    qms = e0.elapsed_time(e1) / 3
+    qalg = nvec * (k_rec + 2 * d)
+    kern["decode_k_rht_qjl_bf16"] = {"ms": round(qms, 4), "alg_bytes": qalg,
+                                     "achieved_GBs": round(qalg / (qms * 1e-3) / 1e9, 1),
+                                     "hbm_frac": round(qalg / (qms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+    del xh
 
     copy = copy_ceiling(torch, dev, stream)
-    del K, V
+    del V
     torch.cuda.empty_cache()
     extra = None if args.no_extra else other_workloads(torch, T, I, dev, stream)
 

@@ -95,6 +95,16 @@ int tq_encode(const tq_params* p, const void* x, tq_dtype x_dtype, int64_t n_str
 int tq_decode(const tq_params* p, const void* packed, int64_t n_streams, int64_t n_tokens,
               void* x_hat, tq_dtype out_dtype, void* stream);
 
+/* Decode with the QJL correction added in the rotated domain ("Ablation...", §2 TurboQuant: the
+ * sketch correction sqrt(pi/2)/d ||e|| s2 ⊙ WHT(b) is added at decode):
+ *   x̂ = n16 · s ⊙ H (c[idx] + Δŷ) / sqrt(d),   Δŷ = sqrt(pi/2)/m · r16 · S^T (2σ - 1),
+ * for either sketch kind (for the RHT sketch S^T (2σ - 1) = s2 ⊙ H (2σ - 1), m = d).  Same arguments,
+ * layout and ownership as tq_decode; p->m must be > 0 (TQ_EINVAL otherwise).  S^T is held in LDS:
+ * TQ_EUNSUPPORTED when d·m·2 bytes plus the kernel's LUT and staging exceed 160 KiB (d = 256 with
+ * m = 256). */
+int tq_decode_qjl(const tq_params* p, const void* packed, int64_t n_streams, int64_t n_tokens,
+                  void* x_hat, tq_dtype out_dtype, void* stream);
+
 /* Workspace for tq_qk_scores (rotated queries and their S-projections). */
 size_t tq_scores_workspace_bytes(const tq_params* pk, int64_t n_streams, int64_t n_q);
 

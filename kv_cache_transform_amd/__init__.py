@@ -67,11 +67,14 @@ def encode(codec: Codec, x: torch.Tensor, out: torch.Tensor | None = None) -> to
 
 
 def decode(codec: Codec, packed: torch.Tensor, n_streams: int, n_tokens: int,
-           dtype: torch.dtype = torch.float32, out: torch.Tensor | None = None) -> torch.Tensor:
+           dtype: torch.dtype = torch.float32, out: torch.Tensor | None = None, qjl: bool = False) -> torch.Tensor:
+    """MSE reconstruction (tq_decode), or with qjl=True the reconstruction with the sketch
+    correction added in the rotated domain (tq_decode_qjl; needs codec.m > 0)."""
     if out is None:
         out = torch.empty(n_streams, n_tokens, codec.d, dtype=dtype, device=packed.device)
-    _lib.check(_lib.lib().tq_decode(ctypes.byref(codec.params()), _ptr(packed), n_streams, n_tokens, _ptr(out),
-                                    _DT[out.dtype], _stream(packed.device)), "tq_decode")
+    fn = _lib.lib().tq_decode_qjl if qjl else _lib.lib().tq_decode
+    _lib.check(fn(ctypes.byref(codec.params()), _ptr(packed), n_streams, n_tokens, _ptr(out),
+                  _DT[out.dtype], _stream(packed.device)), "tq_decode_qjl" if qjl else "tq_decode")
     return out
 
 

@@ -15,7 +15,7 @@ TQ_F32, TQ_BF16, TQ_F16 = 0, 1, 2
 TQ_SKETCH_GAUSSIAN, TQ_SKETCH_RHT = 0, 1
 
 # every symbol include/tq.h declares
-EXPORTS = ("tq_get_layout", "tq_encode", "tq_decode", "tq_scores_workspace_bytes", "tq_qk_scores",
+EXPORTS = ("tq_get_layout", "tq_encode", "tq_decode", "tq_decode_qjl", "tq_scores_workspace_bytes", "tq_qk_scores",
            "tq_attention_workspace_bytes", "tq_decode_attention", "tq_host_tables", "tq_status_string",
            "tq_clear_cache")
 
@@ -52,6 +52,7 @@ def lib() -> ctypes.CDLL:
         "tq_get_layout": (ctypes.c_int, [P, I64, I64, ctypes.POINTER(Layout)]),
         "tq_encode": (ctypes.c_int, [P, VP, ctypes.c_int, I64, I64, VP, VP]),
         "tq_decode": (ctypes.c_int, [P, VP, I64, I64, VP, ctypes.c_int, VP]),
+        "tq_decode_qjl": (ctypes.c_int, [P, VP, I64, I64, VP, ctypes.c_int, VP]),
         "tq_scores_workspace_bytes": (SZ, [P, I64, I64]),
         "tq_qk_scores": (ctypes.c_int, [P, VP, ctypes.c_int, I64, VP, I64, I64, VP, VP, SZ, VP]),
         "tq_attention_workspace_bytes": (SZ, [P, I32, I32, I32, I64]),

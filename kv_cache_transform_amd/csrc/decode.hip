@@ -20,8 +20,15 @@ __device__ __forceinline__ uint32_t bf16_pair_rne(float lo, float hi) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-template <int D, int B, bool OUT_BF16>
-__global__ __launch_bounds__(256, (D == 256 && B == 6 && !OUT_BF16) ? 1 : 2) void decode_kernel(DecodeArgs a) {
+// QJL = true: the corrected reconstruction x̂ = n16 · s ⊙ H (c[idx] + Δŷ) / sqrt(d) with
+// Δŷ = sqrt(pi/2)/m · r16 · S^T (2σ - 1) ("Ablation...", §2 TurboQuant: the sketch correction added
+// at decode, here for either sketch matrix).  S^T (2σ - 1) runs on v_mfma_f32_16x16x32_f16 with
+// A = S^T (fp16, staged in LDS in operand order; row r of tile t is coordinate (r/4) C + 4 t + r%4,
+// so lane part g receives its own coordinates g C + 4 t + i) and B = the ±1 sketch signs (exact),
+// giving exact fp32 sums; c + Δŷ is then split into fp16 hi + lo parts of 2^12 (c + Δŷ) as the B
+// operands of the inverse transform.
+template <int D, int B, bool OUT_BF16, bool QJL = false>
+__global__ __launch_bounds__(256, (D == 256 && B == 6 && !OUT_BF16) || QJL ? 1 : 2) void decode_kernel(DecodeArgs a) {
     constexpr int C = D / 4, NKB = D / 32;
     constexpr int P = lut_group_c(B), NE = 1 << (P * B);
     constexpr int NW = (C * B + 31) / 32;
@@ -37,17 +44,44 @@ __global__ __launch_bounds__(256, (D == 256 && B == 6 && !OUT_BF16) ? 1 : 2) voi
     constexpr int STG = 16 * ROWP;                       // LDS staging bytes per wave
     __shared__ __align__(16) uint8_t stage[4 * STG];
     for (int i = threadIdx.x; i < NE * P * 2; i += blockDim.x) lut[i] = a.t.lut_hl[i];
-    __syncthreads();
-
-    const int lane = threadIdx.x & 63;
-    const int v = lane & 15, g = lane >> 4;
-    const int wave = threadIdx.x >> 6;
     // block = one stream's tile range; waves take every 4th tile
     const int64_t st = blockIdx.x / a.blocks_per_stream;
     const int64_t sub = blockIdx.x - st * a.blocks_per_stream;
     const int64_t tb0 = sub * a.tiles_per_block;
     const int64_t tb1 = tb0 + a.tiles_per_block < a.tiles_per_stream ? tb0 + a.tiles_per_block : a.tiles_per_stream;
     const int head = (int)(st % a.t.n_heads);
+    const int m = a.t.m;
+    const int KSM = m >> 5;                             // k-steps of 32 sketch rows
+    extern __shared__ u32x4 qlds[];                    // QJL: S^T pieces, then the byte -> ±1 table
+    if constexpr (QJL) {
+        // piece (t KSM + ks) 64 + l of lane l = r + 16 kc: S[32 ks + 8 kc + jj][(r/4) C + 4 t + r%4],
+        // jj = 0..7, as 8 fp16
+        const uint16_t* Sh = reinterpret_cast<const uint16_t*>(a.t.S) + (int64_t)head * m * D;
+        const int np = (C / 4) * KSM * 64;
+        for (int i = threadIdx.x; i < np; i += blockDim.x) {
+            const int l = i & 63, tk = i >> 6, t = tk / KSM, ks = tk - t * KSM;
+            const int r = l & 15, kc = l >> 4;
+            const int coord = (r >> 2) * C + 4 * t + (r & 3);
+            const uint16_t* col = Sh + (int64_t)(32 * ks + 8 * kc) * D + coord;
+            u32x4 pc;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) pc[q] = (uint32_t)col[(2 * q) * D] | ((uint32_t)col[(2 * q + 1) * D] << 16);
+            qlds[i] = pc;
+        }
+        // byte e -> 8 fp16 of 2 bit_jj(e) - 1
+        for (int e = threadIdx.x; e < 256; e += blockDim.x) {
+            u32x4 pc;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+                pc[q] = (((e >> (2 * q)) & 1) ? 0x3c00u : 0xbc00u) | ((((e >> (2 * q + 1)) & 1) ? 0x3c00u : 0xbc00u) << 16);
+            qlds[np + e] = pc;
+        }
+    }
+    __syncthreads();
+
+    const int lane = threadIdx.x & 63;
+    const int v = lane & 15, g = lane >> 4;
+    const int wave = threadIdx.x >> 6;
     // ±1 A tiles of the 32-point block (row 4 mg + mi = lane % 16, columns 8 g + jj): output bits
     // {n-2,n-1} = mg, bit 2 = h, bits {0,1} = mi; input bits {n-2,n-1} = g, bits {0,1,2} = jj
     half8 A0[2];
@@ -79,23 +113,58 @@ __global__ __launch_bounds__(256, (D == 256 && B == 6 && !OUT_BF16) ? 1 : 2) voi
     }
     const uint8_t* pidx = a.packed + a.off_idx + st * a.n_tokens * (int64_t)(D * B / 8) + g * CB;
     const uint16_t* pnrm = reinterpret_cast<const uint16_t*>(a.packed + a.off_norm) + st * a.n_tokens;
-    // packed words and norm of one tile for this lane (a vector past the end reads token 0 of the
-    // stream: in bounds, never stored)
-    auto load_tile = [&](uint32_t (&w)[NW], uint32_t& nb, int64_t tl) {
+    const uint8_t* psk = a.packed + a.off_sketch + st * a.n_tokens * (int64_t)(m / 8);
+    const uint16_t* prn = reinterpret_cast<const uint16_t*>(a.packed + a.off_rnorm) + st * a.n_tokens;
+    constexpr int NSW = QJL ? D / 32 : 1;               // sketch dwords per vector at most (m <= d)
+    // packed words, norm (and with QJL the sketch dwords and residual norm) of one tile for this
+    // lane (a vector past the end reads token 0 of the stream: in bounds, never stored)
+    auto load_tile = [&](uint32_t (&w)[NW], uint32_t& nb, uint32_t (&sk)[NSW], uint32_t& rb, int64_t tl) {
         const int64_t tok = tl * 16 + v;
         const int64_t tk = tok < a.n_tokens ? tok : 0;
         load_bytes<CB, CA>(pidx + tk * (D * B / 8), w);
         nb = pnrm[tk];
+        if constexpr (QJL) {
+            const uint32_t* sp = reinterpret_cast<const uint32_t*>(psk + tk * (int64_t)(m / 8));
+#pragma unroll
+            for (int k = 0; k < NSW; ++k) sk[k] = k < KSM ? sp[k] : 0u;
+            rb = prn[tk];
+        }
     };
-    uint32_t wn[NW], nbn;
-    if (tb0 + wave < tb1) load_tile(wn, nbn, tb0 + wave);
+    uint32_t wn[NW], nbn, skn[NSW], rbn = 0u;
+    if (tb0 + wave < tb1) load_tile(wn, nbn, skn, rbn, tb0 + wave);
 #pragma unroll 1
     for (int64_t tile = tb0 + wave; tile < tb1; tile += 4) {
-        uint32_t w[NW];
+        uint32_t w[NW], sk[NSW];
 #pragma unroll
         for (int k = 0; k < NW; ++k) w[k] = wn[k];
+#pragma unroll
+        for (int k = 0; k < NSW; ++k) sk[k] = skn[k];
         const float nrm = (float)__builtin_bit_cast(_Float16, (uint16_t)nbn);
-        if (tile + 4 < tb1) load_tile(wn, nbn, tile + 4);   // next tile's loads overlap this tile's math
+        const float rn = (float)__builtin_bit_cast(_Float16, (uint16_t)rbn);
+        if (tile + 4 < tb1) load_tile(wn, nbn, skn, rbn, tile + 4);   // next tile's loads overlap this tile's math
+        // QJL: dl[s] = (S^T (2σ - 1)) at coordinate g C + s, scaled by 2^12 sqrt(pi/2)/m r16
+        float dl[QJL ? C : 1];
+        if constexpr (QJL) {
+            const int np = (C / 4) * KSM * 64;
+            floatx4 acc[C / 4];
+#pragma unroll
+            for (int t = 0; t < C / 4; ++t) acc[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int ks = 0; ks < NSW; ++ks) {
+                if (ks < KSM) {
+                    const half8 Bs = __builtin_bit_cast(half8, qlds[np + __builtin_amdgcn_ubfe(sk[ks], 8 * g, 8)]);
+#pragma unroll
+                    for (int t = 0; t < C / 4; ++t)
+                        acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(half8, qlds[(t * KSM + ks) * 64 + lane]),
+                                                                        Bs, acc[t], 0, 0, 0);
+                }
+            }
+            const float kq = rn * (1.2533141373155003f * 4096.0f) / (float)m;   // 2^12 sqrt(pi/2)/m r16
+#pragma unroll
+            for (int t = 0; t < C / 4; ++t)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dl[4 * t + i] = acc[t][i] * kq;
+        }
         float x[C];
 #pragma unroll
         for (int kb = 0; kb < NKB; ++kb) {
@@ -110,6 +179,20 @@ __global__ __launch_bounds__(256, (D == 256 && B == 6 && !OUT_BF16) ? 1 : 2) voi
                     bh[q * P + k] = e[k];
                     bl[q * P + k] = e[P + k];
                 }
+            }
+            if constexpr (QJL) {
+                // 2^12 (c + Δŷ), re-split exactly into fp16 hi + lo
+                u32x4 hv, lv;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const float t0 = ((float)bh[2 * q] + (float)bl[2 * q]) + dl[8 * kb + 2 * q];
+                    const float t1 = ((float)bh[2 * q + 1] + (float)bl[2 * q + 1]) + dl[8 * kb + 2 * q + 1];
+                    const half2v hh = {(_Float16)t0, (_Float16)t1};
+                    hv[q] = __builtin_bit_cast(uint32_t, hh);
+                    lv[q] = sub_f16pair_from_f32(hv[q], t0, t1);
+                }
+                bh = __builtin_bit_cast(half8, hv);
+                bl = __builtin_bit_cast(half8, lv);
             }
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
@@ -177,6 +260,60 @@ static hipError_t launch_one(const DecodeArgs& a, int num_cus, hipStream_t s) {
     b.tiles_per_block = (a.tiles_per_stream + bps - 1) / bps;
     hipLaunchKernelGGL((decode_kernel<D, B, BF>), dim3((unsigned)(a.n_streams * bps)), dim3(256), 0, s, b);
     return hipGetLastError();
+}
+
+// QJL-corrected decode: S^T in LDS (d m 2 bytes) plus the 4 KiB sign table as dynamic LDS beside the
+// kernel's static LUT and staging buffer; unsupported when that exceeds one CU's 160 KiB
+template <int D, int B, bool BF>
+static hipError_t launch_one_qjl(const DecodeArgs& a, int num_cus, hipStream_t s, bool* supported) {
+    constexpr int P = lut_group_c(B), NE = 1 << (P * B);
+    constexpr size_t kLdsMax = 163840;
+    const size_t stat = (size_t)NE * P * 4 + (size_t)4 * 16 * ((BF ? 2 : 4) * D + 16);
+    const size_t dyn = (size_t)D * a.t.m * 2 + 256 * 16;
+    *supported = stat + dyn <= kLdsMax;
+    if (!*supported) return hipSuccess;
+    const void* kern = reinterpret_cast<const void*>(&decode_kernel<D, B, BF, true>);
+    if (dyn > 65536) {
+        static std::mutex mu;
+        static bool raised = false;
+        std::lock_guard<std::mutex> lock(mu);
+        if (!raised) {
+            const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kLdsMax - stat));
+            if (e != hipSuccess) return e;
+            raised = true;
+        }
+    }
+    int nb = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, 256, dyn) != hipSuccess || nb < 1) nb = 1;
+    DecodeArgs b = a;
+    int64_t bps = ((int64_t)num_cus * nb + a.n_streams - 1) / a.n_streams;
+    if (bps > a.tiles_per_stream) bps = a.tiles_per_stream;
+    if (bps < 1) bps = 1;
+    b.blocks_per_stream = bps;
+    b.tiles_per_block = (a.tiles_per_stream + bps - 1) / bps;
+    hipLaunchKernelGGL((decode_kernel<D, B, BF, true>), dim3((unsigned)(a.n_streams * bps)), dim3(256), dyn, s, b);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_d_qjl(const DecodeArgs& a, bool bf, int num_cus, hipStream_t s, bool* supported) {
+#define TQ_DEC_CASE(BB) \
+    case BB: return bf ? launch_one_qjl<D, BB, true>(a, num_cus, s, supported) : launch_one_qjl<D, BB, false>(a, num_cus, s, supported);
+    switch (a.t.b) {
+        TQ_DEC_CASE(1) TQ_DEC_CASE(2) TQ_DEC_CASE(3) TQ_DEC_CASE(4)
+        TQ_DEC_CASE(5) TQ_DEC_CASE(6) TQ_DEC_CASE(7) TQ_DEC_CASE(8)
+    }
+#undef TQ_DEC_CASE
+    return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode_qjl(const DecodeArgs& a, bool out_bf16, int num_cus, hipStream_t s, bool* supported) {
+    switch (a.t.d) {
+        case 64: return launch_d_qjl<64>(a, out_bf16, num_cus, s, supported);
+        case 128: return launch_d_qjl<128>(a, out_bf16, num_cus, s, supported);
+        case 256: return launch_d_qjl<256>(a, out_bf16, num_cus, s, supported);
+    }
+    return hipErrorInvalidValue;
 }
 
 template <int D>

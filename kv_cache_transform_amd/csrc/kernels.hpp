@@ -43,6 +43,7 @@ struct DecodeArgs {
     void* out;
     int64_t n_streams, n_tokens;
     int64_t off_idx, off_norm;
+    int64_t off_sketch, off_rnorm;  // read only by the QJL-corrected decode
     int64_t tiles_per_stream, n_tiles, tiles_per_wave;
     int64_t blocks_per_stream, tiles_per_block;
     DevTables t;
@@ -94,6 +95,7 @@ struct AttnArgs {
 // launchers: return hipSuccess or the launch error
 hipError_t launch_encode(const EncodeArgs& a, bool x_bf16, int num_cus, hipStream_t s);
 hipError_t launch_decode(const DecodeArgs& a, bool out_bf16, int num_cus, hipStream_t s);
+hipError_t launch_decode_qjl(const DecodeArgs& a, bool out_bf16, int num_cus, hipStream_t s, bool* supported);
 hipError_t launch_qprep(const QPrepArgs& a, hipStream_t s);
 hipError_t launch_scores(const ScoresArgs& a, int num_cus, hipStream_t s);
 bool attention_supported(int d, int bk, int bv);

@@ -345,6 +345,39 @@ int tq_decode(const tq_params* p, const void* packed, int64_t n_streams, int64_t
     return hip_status(launch_decode(a, out_dtype == TQ_BF16, cus, static_cast<hipStream_t>(stream)));
 }
 
+int tq_decode_qjl(const tq_params* p, const void* packed, int64_t n_streams, int64_t n_tokens, void* x_hat,
+                  tq_dtype out_dtype, void* stream) {
+    int rc = check_params(p);
+    if (rc != TQ_OK) return rc;
+    if (p->m == 0) return TQ_EINVAL;
+    if (n_streams < 0 || n_tokens < 0) return TQ_EINVAL;
+    if (out_dtype != TQ_F32 && out_dtype != TQ_BF16) return TQ_EINVAL;
+    if (n_streams == 0 || n_tokens == 0) return TQ_OK;
+    if (!x_hat || !packed) return TQ_EINVAL;
+    if (!aligned16(x_hat) || !aligned16(packed)) return TQ_EALIGN;
+    DevTables t;
+    int cus = 0;
+    if ((rc = get_tables(p, &t, &cus)) != TQ_OK) return rc;
+    tq_layout lay;
+    layout_of(p, n_streams, n_tokens, &lay);
+    DecodeArgs a{};
+    a.packed = static_cast<const uint8_t*>(packed);
+    a.out = x_hat;
+    a.n_streams = n_streams;
+    a.n_tokens = n_tokens;
+    a.off_idx = lay.off_idx;
+    a.off_norm = lay.off_norm;
+    a.off_sketch = lay.off_sketch;
+    a.off_rnorm = lay.off_rnorm;
+    a.tiles_per_stream = (n_tokens + 15) / 16;
+    a.n_tiles = n_streams * a.tiles_per_stream;
+    a.t = t;
+    bool supported = true;
+    const hipError_t e = launch_decode_qjl(a, out_dtype == TQ_BF16, cus, static_cast<hipStream_t>(stream), &supported);
+    if (!supported) return TQ_EUNSUPPORTED;
+    return hip_status(e);
+}
+
 size_t tq_scores_workspace_bytes(const tq_params* pk, int64_t n_streams, int64_t n_q) {
     if (check_params(pk) != TQ_OK || n_streams < 0 || n_q < 0) return 0;
     const int64_t rows = n_streams * n_q + 16;

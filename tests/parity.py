@@ -109,8 +109,18 @@ def rel_l2(a, b):
     return float(np.linalg.norm(a - b) / nb) if nb > 0 else float(np.linalg.norm(a - b))
 
 
-def check_decode_f32(tb, recs, streams, xh_gpu: np.ndarray, tol=1e-5) -> float:
-    ref = oracle_decode(tb, recs, streams)
+def oracle_decode_qjl(tb, recs, streams):
+    """Reconstruction with the QJL correction, from the GPU's indices, norms and sketch bits."""
+    out = []
+    for r, st in zip(recs, streams):
+        h = tb.head(st)
+        corr = O.qjl_correction(r["sigma"], r["r16"], tb.S[h])
+        out.append(O.decode(r["idx"], r["n16"], tb.s[h], tb.c, corr))
+    return out
+
+
+def check_decode_f32(tb, recs, streams, xh_gpu: np.ndarray, tol=1e-5, qjl=False) -> float:
+    ref = oracle_decode_qjl(tb, recs, streams) if qjl else oracle_decode(tb, recs, streams)
     worst = 0.0
     for k, r in enumerate(ref):
         e = rel_l2(xh_gpu[k], r)
@@ -119,9 +129,9 @@ def check_decode_f32(tb, recs, streams, xh_gpu: np.ndarray, tol=1e-5) -> float:
     return worst
 
 
-def check_decode_bf16(tb, recs, streams, xh_bf16_as_f64: np.ndarray) -> int:
+def check_decode_bf16(tb, recs, streams, xh_bf16_as_f64: np.ndarray, qjl=False) -> int:
     """Each bf16 output equals the oracle value rounded to bf16, or its neighbour (fp32 path)."""
-    ref = oracle_decode(tb, recs, streams)
+    ref = oracle_decode_qjl(tb, recs, streams) if qjl else oracle_decode(tb, recs, streams)
     far = 0
     for k, r in enumerate(ref):
         ulp = np.maximum(np.abs(r), 1e-30) * 2.0 ** -8

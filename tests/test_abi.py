@@ -97,6 +97,9 @@ def test_argument_validation_before_any_gpu_call():
     assert L.tq_encode(p, ctypes.c_void_p(16), 7, 2, 2, ctypes.c_void_p(16), None) == _lib.TQ_EINVAL
     assert L.tq_encode(p, ctypes.c_void_p(18), 1, 2, 2, ctypes.c_void_p(16), None) == _lib.TQ_EALIGN
     assert L.tq_decode(p, ctypes.c_void_p(16), 2, 2, ctypes.c_void_p(20), 0, None) == _lib.TQ_EALIGN
+    # the corrected decode needs a sketch
+    assert L.tq_decode_qjl(p, ctypes.c_void_p(16), 2, 2, ctypes.c_void_p(16), 0, None) == _lib.TQ_EINVAL
+    assert L.tq_decode_qjl(_p(m=128), ctypes.c_void_p(16), 2, 2, ctypes.c_void_p(20), 0, None) == _lib.TQ_EALIGN
     # empty inputs are a valid no-op
     assert L.tq_encode(p, None, 1, 0, 5, None, None) == _lib.TQ_OK
     assert L.tq_decode(p, None, 3, 0, None, 0, None) == _lib.TQ_OK

@@ -192,6 +192,45 @@ def test_rht_encode_decode_scores_parity(d, b, dt):
     print(f"rht d={d} b={b}: flagged={st['flagged']} sketch_flagged={st['sketch_flagged']} scores row max {worst:.2e}")
 
 
+@pytest.mark.parametrize("d,b,m,kind", [(128, 4, 128, 0), (64, 3, 64, 0), (256, 3, 128, 0), (128, 2, 32, 0),
+                                         (128, 4, 128, 1), (64, 2, 64, 1), (128, 6, 96, 0)])
+def test_decode_with_qjl_correction(d, b, m, kind):
+    """tq_decode_qjl: n16 · s ⊙ H (c[idx] + sqrt(pi/2)/m · r16 · S^T (2σ - 1)) / sqrt(d), from the GPU's
+    packed fields; fp32 within 1e-5 relative L2, bf16 within one rounding."""
+    S, N, H, seed = 3, 530, 2, 7300 + d + b + m + kind
+    codec = T.Codec(d, b, m, H, seed, kind)
+    x = I.gaussian((S, N, d), seed, device=DEV)
+    buf = _enc(codec, x)
+    tb = P.Tables(d, b, m, H, seed, kind)
+    recs = O.unpack_tensor(buf, d, b, m, S, N)
+    gbuf = torch.as_tensor(buf, device=DEV)
+    out = T.decode(codec, gbuf, S, N, torch.float32, qjl=True).cpu().numpy()
+    err = P.check_decode_f32(tb, recs, list(range(S)), out, qjl=True)
+    xb = T.decode(codec, gbuf, S, N, torch.bfloat16, qjl=True)
+    P.check_decode_bf16(tb, recs, list(range(S)), O.bf16_bits_to_f64(I.bf16_bits(xb)), qjl=True)
+    # the correction brings the reconstruction closer to the input
+    plain = T.decode(codec, gbuf, S, N, torch.float32).cpu().numpy()
+    x64 = _x64(x)
+    e_plain, e_corr = np.sum((plain - x64) ** 2), np.sum((out - x64) ** 2)
+    print(f"qjl decode d={d} b={b} m={m} kind={kind}: rel L2 vs oracle {err:.2e}; error vs input "
+          f"{e_corr / e_plain:.3f} of the MSE decode's")
+    if kind == 1:
+        assert e_corr < 0.75 * e_plain
+
+
+def test_decode_with_qjl_correction_limits():
+    x = I.gaussian((1, 40, 128), 3, device=DEV)
+    buf = T.encode(T.Codec(128, 4, 0, 1, 3), x)
+    with pytest.raises(T._lib.TQError):                       # no sketch to correct with
+        T.decode(T.Codec(128, 4, 0, 1, 3), buf, 1, 40, qjl=True)
+    c = T.Codec(256, 3, 256, 1, 3)
+    x = I.gaussian((1, 40, 256), 3, device=DEV)
+    buf = T.encode(c, x)
+    with pytest.raises(T._lib.TQError) as ei:                 # S^T does not fit beside the staging
+        T.decode(c, buf, 1, 40, qjl=True)
+    assert ei.value.status == T._lib.TQ_EUNSUPPORTED
+
+
 @pytest.mark.parametrize("batch,hq,hkv,N,d,b", [(2, 8, 2, 3000, 128, 4), (1, 4, 2, 900, 256, 3), (1, 8, 1, 500, 64, 4)])
 def test_rht_decode_attention(batch, hq, hkv, N, d, b):
     e32, _ = _attention_case(batch, hq, hkv, N, d, b, d, torch.float32, sketch=1)
