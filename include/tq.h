@@ -84,6 +84,13 @@ typedef struct {
 /* Packed-buffer geometry for n_streams x n_tokens vectors (host only, no GPU call). */
 int tq_get_layout(const tq_params* p, int64_t n_streams, int64_t n_tokens, tq_layout* out);
 
+/* Encode x [n_streams][n_new][d] (F32 or BF16) as tokens [t0, t0 + n_new) of every stream of a packed
+ * tensor laid out for n_streams x capacity tokens (tq_get_layout with n_tokens = capacity); the other
+ * tokens' records are left untouched, so a cache can grow one decode step (or one chunk) at a time.
+ * TQ_EINVAL unless 0 <= t0 and t0 + n_new <= capacity.  Otherwise as tq_encode. */
+int tq_encode_append(const tq_params* p, const void* x, tq_dtype x_dtype, int64_t n_streams,
+                     int64_t n_new, void* packed, int64_t capacity, int64_t t0, void* stream);
+
 /* Encode x [n_streams][n_tokens][d] (F32 or BF16) into `packed` (layout from tq_get_layout).
  * Steps per vector: norm, sign flip, WHT, scale, Lloyd-Max search, bit-pack, and with m > 0 the
  * residual, S·e and its sign bits ("Ablation...", §2 TurboQuant). */
@@ -131,6 +138,18 @@ int tq_decode_attention(const tq_params* pk, const tq_params* pv, const void* q,
                         const void* packed_k, const void* packed_v, int64_t n_tokens,
                         float softmax_scale, void* out, tq_dtype out_dtype,
                         void* workspace, size_t workspace_bytes, void* stream);
+
+/* tq_decode_attention over caches of different lengths: batch element b attends to its first
+ * lengths[b] tokens only (a decode step over sequences of different lengths).
+ * lengths: device pointer to `batch` int32 values, 4-byte aligned, read by the kernels on `stream`;
+ * values are clamped to [0, n_tokens] (the capacity the packed tensors are laid out for, which also
+ * sizes the workspace); a length of 0 gives zero outputs for that batch element.  NULL = every
+ * element has n_tokens tokens, as tq_decode_attention.  Everything else as tq_decode_attention. */
+int tq_decode_attention_varlen(const tq_params* pk, const tq_params* pv, const void* q, tq_dtype q_dtype,
+                               int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, const void* packed_k,
+                               const void* packed_v, int64_t n_tokens, const int32_t* lengths,
+                               float softmax_scale, void* out, tq_dtype out_dtype, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 /* Host-side copies of the tables the kernels use, for inspection and tests (no GPU call):
  * thresholds[2^b-1] and centroids[2^b] in fp64, signs[d] (±1) and S[m·d] (fp16 values as float)

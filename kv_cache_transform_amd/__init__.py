@@ -66,6 +66,19 @@ def encode(codec: Codec, x: torch.Tensor, out: torch.Tensor | None = None) -> to
     return out
 
 
+def encode_append(codec: Codec, x: torch.Tensor, packed: torch.Tensor, capacity: int, t0: int) -> torch.Tensor:
+    """x: [n_streams, n_new, d] -> tokens [t0, t0 + n_new) of `packed`, a buffer laid out for
+    n_streams x capacity tokens (get_layout(codec, n_streams, capacity))."""
+    if x.dim() != 3 or x.shape[-1] != codec.d or not x.is_contiguous():
+        raise ValueError("x must be a contiguous [n_streams, n_new, d] tensor")
+    S, N, _ = x.shape
+    if packed.dtype != torch.uint8 or packed.numel() < get_layout(codec, S, capacity)["total_bytes"]:
+        raise ValueError("packed buffer too small for the capacity")
+    _lib.check(_lib.lib().tq_encode_append(ctypes.byref(codec.params()), _ptr(x), _DT[x.dtype], S, N, _ptr(packed),
+                                           capacity, t0, _stream(x.device)), "tq_encode_append")
+    return packed
+
+
 def decode(codec: Codec, packed: torch.Tensor, n_streams: int, n_tokens: int,
            dtype: torch.dtype = torch.float32, out: torch.Tensor | None = None, qjl: bool = False) -> torch.Tensor:
     """MSE reconstruction (tq_decode), or with qjl=True the reconstruction with the sketch
@@ -101,18 +114,22 @@ def attention_workspace_bytes(ck: Codec, batch: int, n_q_heads: int, n_kv_heads:
 def decode_attention(ck: Codec, cv: Codec, q: torch.Tensor, packed_k: torch.Tensor, packed_v: torch.Tensor,
                      n_kv_heads: int, n_tokens: int, softmax_scale: float = 0.0,
                      out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
-                     workspace: torch.Tensor | None = None) -> torch.Tensor:
-    """q: [batch, n_q_heads, d] -> attention output [batch, n_q_heads, d] over the packed cache."""
+                     workspace: torch.Tensor | None = None, lengths: torch.Tensor | None = None) -> torch.Tensor:
+    """q: [batch, n_q_heads, d] -> attention output [batch, n_q_heads, d] over the packed cache of
+    n_tokens per stream; lengths (int32 [batch] on the GPU): valid tokens per batch element."""
     B, Hq, d = q.shape
     if workspace is None:
         workspace = torch.empty(max(attention_workspace_bytes(ck, B, Hq, n_kv_heads, n_tokens), 16),
                                 dtype=torch.uint8, device=q.device)
     if out is None:
         out = torch.empty(B, Hq, d, dtype=out_dtype, device=q.device)
-    _lib.check(_lib.lib().tq_decode_attention(
+    if lengths is not None and (lengths.dtype != torch.int32 or lengths.numel() < B or not lengths.is_contiguous()):
+        raise ValueError("lengths must be a contiguous int32 tensor with one entry per batch element")
+    _lib.check(_lib.lib().tq_decode_attention_varlen(
         ctypes.byref(ck.params()), ctypes.byref(cv.params()), _ptr(q), _DT[q.dtype], B, Hq, n_kv_heads,
-        _ptr(packed_k), _ptr(packed_v), n_tokens, ctypes.c_float(softmax_scale), _ptr(out), _DT[out.dtype],
-        _ptr(workspace), workspace.numel(), _stream(q.device)), "tq_decode_attention")
+        _ptr(packed_k), _ptr(packed_v), n_tokens, _ptr(lengths) if lengths is not None else None,
+        ctypes.c_float(softmax_scale), _ptr(out), _DT[out.dtype],
+        _ptr(workspace), workspace.numel(), _stream(q.device)), "tq_decode_attention_varlen")
     return out
 
 

@@ -15,8 +15,9 @@ TQ_F32, TQ_BF16, TQ_F16 = 0, 1, 2
 TQ_SKETCH_GAUSSIAN, TQ_SKETCH_RHT = 0, 1
 
 # every symbol include/tq.h declares
-EXPORTS = ("tq_get_layout", "tq_encode", "tq_decode", "tq_decode_qjl", "tq_scores_workspace_bytes", "tq_qk_scores",
-           "tq_attention_workspace_bytes", "tq_decode_attention", "tq_host_tables", "tq_status_string",
+EXPORTS = ("tq_get_layout", "tq_encode", "tq_encode_append", "tq_decode", "tq_decode_qjl", "tq_scores_workspace_bytes", "tq_qk_scores",
+           "tq_attention_workspace_bytes", "tq_decode_attention", "tq_decode_attention_varlen", "tq_host_tables",
+           "tq_status_string",
            "tq_clear_cache")
 
 
@@ -51,6 +52,7 @@ def lib() -> ctypes.CDLL:
     sig = {
         "tq_get_layout": (ctypes.c_int, [P, I64, I64, ctypes.POINTER(Layout)]),
         "tq_encode": (ctypes.c_int, [P, VP, ctypes.c_int, I64, I64, VP, VP]),
+        "tq_encode_append": (ctypes.c_int, [P, VP, ctypes.c_int, I64, I64, VP, I64, I64, VP]),
         "tq_decode": (ctypes.c_int, [P, VP, I64, I64, VP, ctypes.c_int, VP]),
         "tq_decode_qjl": (ctypes.c_int, [P, VP, I64, I64, VP, ctypes.c_int, VP]),
         "tq_scores_workspace_bytes": (SZ, [P, I64, I64]),
@@ -58,6 +60,8 @@ def lib() -> ctypes.CDLL:
         "tq_attention_workspace_bytes": (SZ, [P, I32, I32, I32, I64]),
         "tq_decode_attention": (ctypes.c_int, [P, P, VP, ctypes.c_int, I32, I32, I32, VP, VP, I64,
                                                ctypes.c_float, VP, ctypes.c_int, VP, SZ, VP]),
+        "tq_decode_attention_varlen": (ctypes.c_int, [P, P, VP, ctypes.c_int, I32, I32, I32, VP, VP, I64, VP,
+                                                      ctypes.c_float, VP, ctypes.c_int, VP, SZ, VP]),
         "tq_host_tables": (ctypes.c_int, [P, I32, VP, VP, VP, VP]),
         "tq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "tq_clear_cache": (None, []),

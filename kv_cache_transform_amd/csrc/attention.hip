@@ -354,13 +354,20 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attn_kernel(AttnArgs 
     if (item >= n_streams * a.n_split) return;
     const int64_t st = item / a.n_split;
     const int split = (int)(item - st * a.n_split);
+    const int bidx = (int)(st / a.n_kv_heads), kvh = (int)(st - (int64_t)bidx * a.n_kv_heads);
+    // this batch element's cache holds `len` valid tokens; a split past them stays empty (its
+    // partials are max -inf, sum 0, zero sums, and the combine gives it weight 0)
+    int64_t len = a.n_tokens;
+    if (a.lens) {
+        const int64_t l = a.lens[bidx];
+        len = l < 0 ? 0 : (l < a.n_tokens ? l : a.n_tokens);
+    }
     const int64_t t_begin = (int64_t)split * a.tokens_per_split;
-    const int64_t t_end = t_begin + a.tokens_per_split < a.n_tokens ? t_begin + a.tokens_per_split : a.n_tokens;
+    const int64_t t_end = t_begin + a.tokens_per_split < len ? t_begin + a.tokens_per_split : len;
     const int m = a.tk.m;
     const int mks = m >> 5;
 
     // query operands (B of the score products): lane column q = l16, k-block g
-    const int bidx = (int)(st / a.n_kv_heads), kvh = (int)(st - (int64_t)bidx * a.n_kv_heads);
     const bool qvalid = l16 < a.group;
     const int64_t qrow = (int64_t)bidx * a.n_q_heads + (int64_t)kvh * a.group + (qvalid ? l16 : 0);
     half8 qb[KS], pb[QJL ? KS : 1];
@@ -394,7 +401,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attn_kernel(AttnArgs 
     // last refill re-reads the final chunk) so the load counters stay static and a wait covers only
     // the buffer about to be used.
     AttnChunk<Gm::NWK, Gm::NWV, Gm::NKS> A, B;
-    const int64_t n_full = (t_end - t_begin) >> 5;
+    const int64_t n_full = t_end > t_begin ? (t_end - t_begin) >> 5 : 0;
     int64_t c = 0;
     if (n_full > 0) {
         attn_load<D, BK, BV, QJL, true>(A, P, t_begin, t_end, l16, g, m);
@@ -459,6 +466,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
     if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
     __syncthreads();
     const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    if (M == -INFINITY) {                                // an empty cache (length 0): output zeros
+        for (int j = threadIdx.x; j < d; j += blockDim.x) {
+            if (a.out_bf16) reinterpret_cast<__bf16*>(a.out)[row * d + j] = (__bf16)0.0f;
+            else reinterpret_cast<float*>(a.out)[row * d + j] = 0.0f;
+        }
+        return;
+    }
     float ls = 0.0f;
     for (int s = threadIdx.x; s < ns; s += blockDim.x) {
         const float w = exp2f(ml[s * 32] - M);

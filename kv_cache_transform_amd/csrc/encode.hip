@@ -173,7 +173,8 @@ __global__ __launch_bounds__(256, ((D > 128 && (QJL || !BF16)) || (QJL && !BF16)
         for (int gi = 0; gi < NG; ++gi) {
             const int64_t tok = (t + gi) * 16 + v;
             const bool valid = (t + gi) < tb1 && tok < a.n_tokens;
-            const int64_t vec = st * a.n_tokens + (valid ? tok : 0);
+            // packed record of this vector: token t0 + tok of a cache of `cap` tokens per stream
+            const int64_t vec = st * a.cap + a.t0 + (valid ? tok : 0);
             validv[gi] = valid;
             vecv[gi] = vec;
 

@@ -28,6 +28,7 @@ struct EncodeArgs {
     const void* x;           // [n_streams][n_tokens][d]
     uint8_t* packed;
     int64_t n_streams, n_tokens;
+    int64_t cap, t0;         // the packed planes hold `cap` tokens per stream; x goes to [t0, t0 + n_tokens)
     int64_t off_idx, off_sketch, off_norm, off_rnorm;
     int64_t tiles_per_stream;  // ceil(n_tokens / 16)
     int64_t n_tiles;           // n_streams * tiles_per_stream
@@ -83,6 +84,8 @@ struct AttnArgs {
     void* out;               // [batch][n_q_heads][d]
     int out_bf16;
     int64_t n_tokens;
+    const int32_t* lens;     // [batch] valid tokens of each batch element's cache (clamped to
+                             // [0, n_tokens]); null: all n_tokens
     int batch, n_q_heads, n_kv_heads, group;  // group = n_q_heads / n_kv_heads
     int n_split;
     int64_t tokens_per_split;

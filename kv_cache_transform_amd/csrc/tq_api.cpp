@@ -289,33 +289,42 @@ int tq_host_tables(const tq_params* p, int32_t head, double* thresholds, double*
     return TQ_OK;
 }
 
-int tq_encode(const tq_params* p, const void* x, tq_dtype x_dtype, int64_t n_streams, int64_t n_tokens,
-              void* packed, void* stream) {
+int tq_encode_append(const tq_params* p, const void* x, tq_dtype x_dtype, int64_t n_streams, int64_t n_new,
+                     void* packed, int64_t capacity, int64_t t0, void* stream) {
     int rc = check_params(p);
     if (rc != TQ_OK) return rc;
-    if (n_streams < 0 || n_tokens < 0) return TQ_EINVAL;
+    if (n_streams < 0 || n_new < 0 || capacity < 0 || t0 < 0 || t0 > capacity || n_new > capacity - t0)
+        return TQ_EINVAL;
     if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return TQ_EINVAL;
-    if (n_streams == 0 || n_tokens == 0) return TQ_OK;
+    if (n_streams == 0 || n_new == 0) return TQ_OK;
     if (!x || !packed) return TQ_EINVAL;
     if (!aligned16(x) || !aligned16(packed)) return TQ_EALIGN;
     DevTables t;
     int cus = 0;
     if ((rc = get_tables(p, &t, &cus)) != TQ_OK) return rc;
     tq_layout lay;
-    layout_of(p, n_streams, n_tokens, &lay);
+    layout_of(p, n_streams, capacity, &lay);
     EncodeArgs a{};
     a.x = x;
     a.packed = static_cast<uint8_t*>(packed);
     a.n_streams = n_streams;
-    a.n_tokens = n_tokens;
+    a.n_tokens = n_new;
+    a.cap = capacity;
+    a.t0 = t0;
     a.off_idx = lay.off_idx;
     a.off_sketch = lay.off_sketch;
     a.off_norm = lay.off_norm;
     a.off_rnorm = lay.off_rnorm;
-    a.tiles_per_stream = (n_tokens + 15) / 16;
+    a.tiles_per_stream = (n_new + 15) / 16;
     a.n_tiles = n_streams * a.tiles_per_stream;
     a.t = t;
     return hip_status(launch_encode(a, x_dtype == TQ_BF16, cus, static_cast<hipStream_t>(stream)));
+}
+
+int tq_encode(const tq_params* p, const void* x, tq_dtype x_dtype, int64_t n_streams, int64_t n_tokens,
+              void* packed, void* stream) {
+    if (n_tokens < 0) return TQ_EINVAL;
+    return tq_encode_append(p, x, x_dtype, n_streams, n_tokens, packed, n_tokens, 0, stream);
 }
 
 int tq_decode(const tq_params* p, const void* packed, int64_t n_streams, int64_t n_tokens, void* x_hat,
@@ -443,6 +452,15 @@ int tq_decode_attention(const tq_params* pk, const tq_params* pv, const void* q,
                         int32_t n_q_heads, int32_t n_kv_heads, const void* packed_k, const void* packed_v,
                         int64_t n_tokens, float softmax_scale, void* out, tq_dtype out_dtype, void* workspace,
                         size_t workspace_bytes, void* stream) {
+    return tq_decode_attention_varlen(pk, pv, q, q_dtype, batch, n_q_heads, n_kv_heads, packed_k, packed_v, n_tokens,
+                                      nullptr, softmax_scale, out, out_dtype, workspace, workspace_bytes, stream);
+}
+
+int tq_decode_attention_varlen(const tq_params* pk, const tq_params* pv, const void* q, tq_dtype q_dtype,
+                               int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, const void* packed_k,
+                               const void* packed_v, int64_t n_tokens, const int32_t* lengths, float softmax_scale,
+                               void* out, tq_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                               void* stream) {
     int rc = check_params(pk);
     if (rc != TQ_OK) return rc;
     if ((rc = check_params(pv)) != TQ_OK) return rc;
@@ -458,6 +476,7 @@ int tq_decode_attention(const tq_params* pk, const tq_params* pv, const void* q,
     if (!q || !packed_k || !packed_v || !out || !workspace) return TQ_EINVAL;
     if (!aligned16(q) || !aligned16(packed_k) || !aligned16(packed_v) || !aligned16(out) || !aligned16(workspace))
         return TQ_EALIGN;
+    if (lengths && (reinterpret_cast<uintptr_t>(lengths) & 3u)) return TQ_EALIGN;
     const AttnWs w = attn_ws(pk, batch, n_q_heads, n_kv_heads, n_tokens);
     if (workspace_bytes < (size_t)w.total) return TQ_EWORKSPACE;
     if (!attention_supported(pk->d, pk->b, pv->b)) return TQ_EUNSUPPORTED;
@@ -496,6 +515,7 @@ int tq_decode_attention(const tq_params* pk, const tq_params* pv, const void* q,
     a.out = out;
     a.out_bf16 = out_dtype == TQ_BF16;
     a.n_tokens = n_tokens;
+    a.lens = lengths;
     a.batch = batch;
     a.n_q_heads = n_q_heads;
     a.n_kv_heads = n_kv_heads;

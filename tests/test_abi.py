@@ -97,6 +97,12 @@ def test_argument_validation_before_any_gpu_call():
     assert L.tq_encode(p, ctypes.c_void_p(16), 7, 2, 2, ctypes.c_void_p(16), None) == _lib.TQ_EINVAL
     assert L.tq_encode(p, ctypes.c_void_p(18), 1, 2, 2, ctypes.c_void_p(16), None) == _lib.TQ_EALIGN
     assert L.tq_decode(p, ctypes.c_void_p(16), 2, 2, ctypes.c_void_p(20), 0, None) == _lib.TQ_EALIGN
+    # appends must land inside the capacity
+    x16, b16 = ctypes.c_void_p(16), ctypes.c_void_p(16)
+    assert L.tq_encode_append(p, x16, 1, 2, 5, b16, 10, 6, None) == _lib.TQ_EINVAL      # 6 + 5 > 10
+    assert L.tq_encode_append(p, x16, 1, 2, 5, b16, 10, -1, None) == _lib.TQ_EINVAL
+    assert L.tq_encode_append(p, x16, 1, 2, -1, b16, 10, 0, None) == _lib.TQ_EINVAL
+    assert L.tq_encode_append(p, x16, 1, 2, 0, b16, 10, 10, None) == _lib.TQ_OK          # empty append
     # the corrected decode needs a sketch
     assert L.tq_decode_qjl(p, ctypes.c_void_p(16), 2, 2, ctypes.c_void_p(16), 0, None) == _lib.TQ_EINVAL
     assert L.tq_decode_qjl(_p(m=128), ctypes.c_void_p(16), 2, 2, ctypes.c_void_p(20), 0, None) == _lib.TQ_EALIGN

@@ -239,6 +239,67 @@ def test_rht_decode_attention(batch, hq, hkv, N, d, b):
     assert e32 <= 2e-3 and eb <= 2e-3
 
 
+# ---------------------------------------------------------------------------------------------
+# growing caches: appends at an offset, and attention over per-batch lengths
+@pytest.mark.parametrize("d,b,m,kind,dt", [(128, 4, 128, 0, torch.bfloat16), (128, 3, 0, 0, torch.bfloat16),
+                                           (64, 4, 64, 1, torch.bfloat16), (128, 4, 128, 0, torch.float32)])
+def test_encode_append_equals_one_encode(d, b, m, kind, dt):
+    S, cap, H, seed = 3, 1000, 3, 8800 + d + b + m + kind
+    codec = T.Codec(d, b, m, H, seed, kind)
+    x = I.gaussian((S, cap, d), seed, device=DEV, dtype=dt)
+    whole = _enc(codec, x)
+    lay = T.get_layout(codec, S, cap)
+    buf = torch.full((lay["total_bytes"],), 0xA5, dtype=torch.uint8, device=DEV)
+    cuts = [0, 300, 301, 717, 718, 1000]                      # tile-aligned and ragged offsets, 1-token steps
+    for t0, t1 in zip(cuts[:-1], cuts[1:]):
+        T.encode_append(codec, x[:, t0:t1].contiguous(), buf, cap, t0)
+    torch.cuda.synchronize()
+    got = O.unpack_tensor(buf.cpu().numpy(), d, b, m, S, cap)
+    ref = O.unpack_tensor(whole, d, b, m, S, cap)
+    for r, g in zip(ref, got):
+        for k in r:
+            assert np.array_equal(r[k], g[k]), k
+    # an append writes only its own records: a fresh buffer keeps the fill outside [t0, t1)
+    part = torch.full((lay["total_bytes"],), 0xA5, dtype=torch.uint8, device=DEV)
+    T.encode_append(codec, x[:, 301:717].contiguous(), part, cap, 301)
+    pb = part.cpu().numpy()
+    ib = d * b // 8
+    for st in range(S):
+        lo, hi = lay["off_idx"] + (st * cap + 301) * ib, lay["off_idx"] + (st * cap + 717) * ib
+        row0, row1 = lay["off_idx"] + st * cap * ib, lay["off_idx"] + (st + 1) * cap * ib
+        assert np.all(pb[row0:lo] == 0xA5) and np.all(pb[hi:row1] == 0xA5)
+        assert np.array_equal(pb[lo:hi], whole[lo:hi])
+    tb = P.Tables(d, b, m, H, seed, kind)
+    P.check_encode(tb, _x64(x[:1]), buf.cpu().numpy(), streams=[0], n_streams=S, n_tokens=cap)
+
+
+@pytest.mark.parametrize("lens", [(3000, 37, 1999), (0, 513, 3000)])
+def test_decode_attention_per_batch_lengths(lens):
+    batch, hq, hkv, N, d, b, m, seed = 3, 8, 2, 3000, 128, 4, 128, 4101
+    ck, cv = T.Codec(d, b, m, hkv, seed), T.Codec(d, b, 0, hkv, seed + 1)
+    K = I.rope_gaussian(batch * hkv, N, d, seed, device=DEV)
+    V = I.rope_gaussian(batch * hkv, N, d, seed + 1, device=DEV)
+    q = I.cfg4_queries(batch, hq, d, N, seed + 2, device=DEV)
+    pk, pv = T.encode(ck, K), T.encode(cv, V)
+    ln = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    out = T.decode_attention(ck, cv, q, pk, pv, hkv, N, out_dtype=torch.float32, lengths=ln).cpu().numpy()
+    tk, tv = P.Tables(d, b, m, hkv, seed), P.Tables(d, b, 0, hkv, seed + 1)
+    rk = O.unpack_tensor(pk.cpu().numpy(), d, b, m, batch * hkv, N)
+    rv = O.unpack_tensor(pv.cpu().numpy(), d, b, 0, batch * hkv, N)
+    q64 = _x64(q)
+    g = hq // hkv
+    for bi in range(batch):
+        L = lens[bi]
+        for h in range(hq):
+            if L == 0:
+                assert np.all(out[bi, h] == 0.0)
+                continue
+            st = bi * hkv + h // g
+            cut = lambda r: {k: v[:L] for k, v in r.items()}
+            ref = P.oracle_attention_row(tk, tv, cut(rk[st]), cut(rv[st]), st, q64[bi, h], 1 / math.sqrt(d))
+            assert P.rel_l2(out[bi, h], ref) <= 2e-3, (bi, h, L)
+
+
 def test_decode_attention_explicit_scale():
     e, _ = _attention_case(1, 4, 2, 900, 128, 4, 128, torch.float32, scale=0.05)
     assert e <= 2e-3
