@@ -175,6 +175,31 @@ def main():
                              "hbm_frac": round(dec_alg / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     del xh
 
+    # a decode step on a growing cache: append one token to every stream of K (launch-bound), and
+    # attention over per-batch lengths spread evenly from N/2 to N
+    x1 = K[:, -1:].contiguous()
+    T.encode_append(ck, x1, pk, N, N - 1)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(20):
+        T.encode_append(ck, x1, pk, N, N - 1)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    kern["append_k_1_token"] = {"us": round(e0.elapsed_time(e1) / 20 * 1e3, 2), "vectors": streams}
+    lens = torch.linspace(N // 2, N, B).to(torch.int32).to(dev)
+    T.decode_attention(ck, cv, q, pk, pv, Hkv, N, out=out, workspace=ws, lengths=lens)
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for _ in range(5):
+        T.decode_attention(ck, cv, q, pk, pv, Hkv, N, out=out, workspace=ws, lengths=lens)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    vms = e0.elapsed_time(e1) / 5
+    valg = int(lens.sum().item()) * Hkv * (k_rec + v_rec) + 2 * B * Hq * d * 2
+    kern["decode_attention_varlen"] = {"ms": round(vms, 4), "alg_bytes": valg,
+                                       "achieved_GBs": round(valg / (vms * 1e-3) / 1e9, 1),
+                                       "hbm_frac": round(valg / (vms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+
     # the same K encode with the randomized Hadamard sketch (S = H diag(s2), m = d = 128): the
     # sketch is one more 32-point transform of the residual, not a dense m x d product
     ck_rht = T.Codec(d, 4, 128, Hkv, 4001, sketch=1)

@@ -355,15 +355,17 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attn_kernel(AttnArgs 
     const int64_t st = item / a.n_split;
     const int split = (int)(item - st * a.n_split);
     const int bidx = (int)(st / a.n_kv_heads), kvh = (int)(st - (int64_t)bidx * a.n_kv_heads);
-    // this batch element's cache holds `len` valid tokens; a split past them stays empty (its
-    // partials are max -inf, sum 0, zero sums, and the combine gives it weight 0)
-    int64_t len = a.n_tokens;
+    // this batch element's cache holds `len` valid tokens, shared out over the stream's splits in
+    // runs of a multiple of 32 (a split past them stays empty: partials max -inf, sum 0, zero sums,
+    // which the combine weighs 0)
+    int64_t len = a.n_tokens, tps = a.tokens_per_split;
     if (a.lens) {
         const int64_t l = a.lens[bidx];
         len = l < 0 ? 0 : (l < a.n_tokens ? l : a.n_tokens);
+        tps = ((len + a.n_split - 1) / a.n_split + 31) / 32 * 32;
     }
-    const int64_t t_begin = (int64_t)split * a.tokens_per_split;
-    const int64_t t_end = t_begin + a.tokens_per_split < len ? t_begin + a.tokens_per_split : len;
+    const int64_t t_begin = (int64_t)split * tps;
+    const int64_t t_end = t_begin + tps < len ? t_begin + tps : len;
     const int m = a.tk.m;
     const int mks = m >> 5;
 
