@@ -34,17 +34,17 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published (the sketch p
 # the kernel's sources are the ones it was measured on (sha256 of the .hip file + shared headers).
 FETCH_UNIT_B, WRITE_UNIT_B = 2048, 1024
 TRAFFIC = {
-    "encode_k": {"fetch": 2098025.375, "write": 1391707.84375, "src": "encode.hip",
-        "sha": "96bbda8c00975444861aa8b7e569fce557d7b872f6c2719db99a63d417063e34"},
-    "encode_v": {"fetch": 2097223.25, "write": 1092332.84375, "src": "encode.hip",
-        "sha": "96bbda8c00975444861aa8b7e569fce557d7b872f6c2719db99a63d417063e34"},
-    "decode_attention": {"fetch": 1229638.5625, "write": 4160.0, "src": "attention.hip",
-        "sha": "928a924af0421b170117dd4d03b4a24eb397a6d49842374465a8112789982bec"},
-    "decode_v_bf16": {"fetch": 551138.8125, "write": 4194304.0, "src": "decode.hip",
-        "sha": "5a3129d3790b8270d5ecf5a4d85b72e2f8f55ccf96c6adabbec4f1d0b6e5fda1"},
+    "encode_k": {"fetch": 2098029.375, "write": 1392972.4375, "src": "encode.hip",
+        "sha": "b0fc47b1a37a968e2c667fab99fbd7aab761170b8bbb05594186e63e8bfcc6f0"},
+    "encode_v": {"fetch": 2097225.5, "write": 1092388.96875, "src": "encode.hip",
+        "sha": "b0fc47b1a37a968e2c667fab99fbd7aab761170b8bbb05594186e63e8bfcc6f0"},
+    "decode_attention": {"fetch": 1229662.75, "write": 4160.0, "src": "attention.hip",
+        "sha": "f4aba8cac61d105d85e7e11543cae7b1c581c4d4821f2a3667ec5e5e4233c2cd"},
+    "decode_v_bf16": {"fetch": 551112.0625, "write": 4194304.0, "src": "decode.hip",
+        "sha": "1305b66b060b192e2cba4cafc8529e576e0dc6284221101dbdf82d295d994d66"},
 }
 TRAFFIC_HEADERS_SHA = ("9241f7e7fc6398e3b61bd782d033f3beac2c8fe34392745cceb9f2f364e6409c"   # common.hpp
-                       "377a1b066127f7208daee3eefdc2a15cc9ce6d34cd3fada46c623eb8e04674af")  # kernels.hpp
+                       "6e57abc34782d6aeec8cd0c4e32a9c38d93958dc7a1ff9c2e10d2f5c99ce77f4")  # kernels.hpp
 
 
 def _sha(path: str) -> str:
@@ -175,61 +175,62 @@ def main():
                              "hbm_frac": round(dec_alg / (dms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     del xh
 
-    # a decode step on a growing cache: append one token to every stream of K (launch-bound), and
-    # attention over per-batch lengths spread evenly from N/2 to N
-    x1 = K[:, -1:].contiguous()
-    T.encode_append(ck, x1, pk, N, N - 1)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(20):
+    if not args.no_extra:
+        # a decode step on a growing cache: append one token to every stream of K (launch-bound), and
+        # attention over per-batch lengths spread evenly from N/2 to N
+        x1 = K[:, -1:].contiguous()
         T.encode_append(ck, x1, pk, N, N - 1)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    kern["append_k_1_token"] = {"us": round(e0.elapsed_time(e1) / 20 * 1e3, 2), "vectors": streams}
-    lens = torch.linspace(N // 2, N, B).to(torch.int32).to(dev)
-    T.decode_attention(ck, cv, q, pk, pv, Hkv, N, out=out, workspace=ws, lengths=lens)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(5):
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(20):
+            T.encode_append(ck, x1, pk, N, N - 1)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        kern["append_k_1_token"] = {"us": round(e0.elapsed_time(e1) / 20 * 1e3, 2), "vectors": streams}
+        lens = torch.linspace(N // 2, N, B).to(torch.int32).to(dev)
         T.decode_attention(ck, cv, q, pk, pv, Hkv, N, out=out, workspace=ws, lengths=lens)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    vms = e0.elapsed_time(e1) / 5
-    valg = int(lens.sum().item()) * Hkv * (k_rec + v_rec) + 2 * B * Hq * d * 2
-    kern["decode_attention_varlen"] = {"ms": round(vms, 4), "alg_bytes": valg,
-                                       "achieved_GBs": round(valg / (vms * 1e-3) / 1e9, 1),
-                                       "hbm_frac": round(valg / (vms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(5):
+            T.decode_attention(ck, cv, q, pk, pv, Hkv, N, out=out, workspace=ws, lengths=lens)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        vms = e0.elapsed_time(e1) / 5
+        valg = int(lens.sum().item()) * Hkv * (k_rec + v_rec) + 2 * B * Hq * d * 2
+        kern["decode_attention_varlen"] = {"ms": round(vms, 4), "alg_bytes": valg,
+                                           "achieved_GBs": round(valg / (vms * 1e-3) / 1e9, 1),
+                                           "hbm_frac": round(valg / (vms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
-    # the same K encode with the randomized Hadamard sketch (S = H diag(s2), m = d = 128): the
-    # sketch is one more 32-point transform of the residual, not a dense m x d product
-    ck_rht = T.Codec(d, 4, 128, Hkv, 4001, sketch=1)
-    T.encode(ck_rht, K, pk)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(3):
+        # the same K encode with the randomized Hadamard sketch (S = H diag(s2), m = d = 128): the
+        # sketch is one more 32-point transform of the residual, not a dense m x d product
+        ck_rht = T.Codec(d, 4, 128, Hkv, 4001, sketch=1)
         T.encode(ck_rht, K, pk)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    rms = e0.elapsed_time(e1) / 3
-    kern["encode_k_rht"] = {"ms": round(rms, 4), "alg_bytes": alg["encode_k"],
-                            "achieved_GBs": round(alg["encode_k"] / (rms * 1e-3) / 1e9, 1),
-                            "hbm_frac": round(alg["encode_k"] / (rms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-    # and its decode to bf16 with the sketch correction added (84 B in, 256 B out per key)
-    del K
-    xh = torch.empty(streams, N, d, dtype=torch.bfloat16, device=dev)
-    T.decode(ck_rht, pk, streams, N, torch.bfloat16, out=xh, qjl=True)
-    torch.cuda.synchronize()
-    e0.record(stream)
-    for _ in range(3):
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(3):
+            T.encode(ck_rht, K, pk)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rms = e0.elapsed_time(e1) / 3
+        kern["encode_k_rht"] = {"ms": round(rms, 4), "alg_bytes": alg["encode_k"],
+                                "achieved_GBs": round(alg["encode_k"] / (rms * 1e-3) / 1e9, 1),
+                                "hbm_frac": round(alg["encode_k"] / (rms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        # and its decode to bf16 with the sketch correction added (84 B in, 256 B out per key)
+        xh = torch.empty(streams, N, d, dtype=torch.bfloat16, device=dev)
         T.decode(ck_rht, pk, streams, N, torch.bfloat16, out=xh, qjl=True)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    qms = e0.elapsed_time(e1) / 3
-    qalg = nvec * (k_rec + 2 * d)
-    kern["decode_k_rht_qjl_bf16"] = {"ms": round(qms, 4), "alg_bytes": qalg,
-                                     "achieved_GBs": round(qalg / (qms * 1e-3) / 1e9, 1),
-                                     "hbm_frac": round(qalg / (qms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-    del xh
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(3):
+            T.decode(ck_rht, pk, streams, N, torch.bfloat16, out=xh, qjl=True)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        qms = e0.elapsed_time(e1) / 3
+        qalg = nvec * (k_rec + 2 * d)
+        kern["decode_k_rht_qjl_bf16"] = {"ms": round(qms, 4), "alg_bytes": qalg,
+                                         "achieved_GBs": round(qalg / (qms * 1e-3) / 1e9, 1),
+                                         "hbm_frac": round(qalg / (qms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del xh
+    del K
 
     copy = copy_ceiling(torch, dev, stream)
     del V
