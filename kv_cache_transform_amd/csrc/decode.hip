@@ -53,11 +53,14 @@ __global__ __launch_bounds__(256, (D == 256 && B == 6 && !OUT_BF16) || QJL ? 1 :
     const int m = a.t.m;
     const int KSM = m >> 5;                             // k-steps of 32 sketch rows
     extern __shared__ u32x4 qlds[];                    // QJL: S^T pieces, then the byte -> ±1 table
+    // randomized Hadamard sketch: S^T (2σ - 1) = s2 ⊙ H (2σ - 1), the decode's own 32-point block and
+    // butterflies on the ±1 signs, so S^T is not staged
+    const bool rht = QJL && a.t.sketch == 1;
+    const int np = rht ? 0 : (C / 4) * KSM * 64;     // S^T pieces in LDS before the sign table
     if constexpr (QJL) {
         // piece (t KSM + ks) 64 + l of lane l = r + 16 kc: S[32 ks + 8 kc + jj][(r/4) C + 4 t + r%4],
         // jj = 0..7, as 8 fp16
         const uint16_t* Sh = reinterpret_cast<const uint16_t*>(a.t.S) + (int64_t)head * m * D;
-        const int np = (C / 4) * KSM * 64;
         for (int i = threadIdx.x; i < np; i += blockDim.x) {
             const int l = i & 63, tk = i >> 6, t = tk / KSM, ks = tk - t * KSM;
             const int r = l & 15, kc = l >> 4;
@@ -111,6 +114,14 @@ __global__ __launch_bounds__(256, (D == 256 && B == 6 && !OUT_BF16) || QJL ? 1 :
 #pragma unroll
         for (int s = 0; s < C; ++s) smask[s] = f2u(ss[s]) & 0x80000000u;
     }
+    uint32_t s2mask[QJL ? C : 1];   // RHT: sign bit of s2 at coordinate g C + s
+    if constexpr (QJL) {
+        if (rht) {
+            const float* ss = a.t.signs2 + (int64_t)head * D + g * C;
+#pragma unroll
+            for (int s = 0; s < C; ++s) s2mask[s] = f2u(ss[s]) & 0x80000000u;
+        }
+    }
     const uint8_t* pidx = a.packed + a.off_idx + st * a.n_tokens * (int64_t)(D * B / 8) + g * CB;
     const uint16_t* pnrm = reinterpret_cast<const uint16_t*>(a.packed + a.off_norm) + st * a.n_tokens;
     const uint8_t* psk = a.packed + a.off_sketch + st * a.n_tokens * (int64_t)(m / 8);
@@ -124,9 +135,14 @@ __global__ __launch_bounds__(256, (D == 256 && B == 6 && !OUT_BF16) || QJL ? 1 :
         load_bytes<CB, CA>(pidx + tk * (D * B / 8), w);
         nb = pnrm[tk];
         if constexpr (QJL) {
-            const uint32_t* sp = reinterpret_cast<const uint32_t*>(psk + tk * (int64_t)(m / 8));
+            const uint8_t* sb = psk + tk * (int64_t)(m / 8);
+            if (rht) {      // the lane's own NKB bytes: sketch rows g C .. g C + C - 1
+                load_bytes<NKB, NKB>(sb + g * NKB, sk);
+            } else {
+                const uint32_t* sp = reinterpret_cast<const uint32_t*>(sb);
 #pragma unroll
-            for (int k = 0; k < NSW; ++k) sk[k] = k < KSM ? sp[k] : 0u;
+                for (int k = 0; k < NSW; ++k) sk[k] = k < KSM ? sp[k] : 0u;
+            }
             rb = prn[tk];
         }
     };
@@ -145,7 +161,24 @@ __global__ __launch_bounds__(256, (D == 256 && B == 6 && !OUT_BF16) || QJL ? 1 :
         // QJL: dl[s] = (S^T (2σ - 1)) at coordinate g C + s, scaled by 2^12 sqrt(pi/2)/m r16
         float dl[QJL ? C : 1];
         if constexpr (QJL) {
-            const int np = (C / 4) * KSM * 64;
+          const float kq = rn * (1.2533141373155003f * 4096.0f) / (float)m;   // 2^12 sqrt(pi/2)/m r16
+          if (rht) {
+            // H b on the ±1 signs of coordinates g C + 8 kb + jj (byte g C/8 + kb of the sketch),
+            // exact in fp16 and fp32; then s2 and the scale
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb) {
+                const half8 Bs = __builtin_bit_cast(half8, qlds[__builtin_amdgcn_ubfe(sk[kb >> 2], 8 * (kb & 3), 8)]);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const floatx4 r = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0[h], Bs, floatx4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) dl[8 * kb + 4 * h + i] = r[i];
+                }
+            }
+            fwht_slots<C, 8>(dl);
+#pragma unroll
+            for (int s2 = 0; s2 < C; ++s2) dl[s2] = u2f(f2u(dl[s2]) ^ s2mask[s2]) * kq;
+          } else {
             floatx4 acc[C / 4];
 #pragma unroll
             for (int t = 0; t < C / 4; ++t) acc[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
@@ -159,11 +192,11 @@ __global__ __launch_bounds__(256, (D == 256 && B == 6 && !OUT_BF16) || QJL ? 1 :
                                                                         Bs, acc[t], 0, 0, 0);
                 }
             }
-            const float kq = rn * (1.2533141373155003f * 4096.0f) / (float)m;   // 2^12 sqrt(pi/2)/m r16
 #pragma unroll
             for (int t = 0; t < C / 4; ++t)
 #pragma unroll
                 for (int i = 0; i < 4; ++i) dl[4 * t + i] = acc[t][i] * kq;
+          }
         }
         float x[C];
 #pragma unroll
@@ -269,7 +302,7 @@ static hipError_t launch_one_qjl(const DecodeArgs& a, int num_cus, hipStream_t s
     constexpr int P = lut_group_c(B), NE = 1 << (P * B);
     constexpr size_t kLdsMax = 163840;
     const size_t stat = (size_t)NE * P * 4 + (size_t)4 * 16 * ((BF ? 2 : 4) * D + 16);
-    const size_t dyn = (size_t)D * a.t.m * 2 + 256 * 16;
+    const size_t dyn = (a.t.sketch == 1 ? 0 : (size_t)D * a.t.m * 2) + 256 * 16;
     *supported = stat + dyn <= kLdsMax;
     if (!*supported) return hipSuccess;
     const void* kern = reinterpret_cast<const void*>(&decode_kernel<D, B, BF, true>);
