@@ -60,6 +60,11 @@ extern "C" {
 
 typedef enum { TQ_F32 = 0, TQ_BF16 = 1, TQ_F16 = 2 } tq_dtype;
 
+/* Rotation before quantisation (tq_params.rotation). */
+#define TQ_ROTATION_WHT 0    /* y = WHT(x ⊙ s)/(sqrt(d) ||x||): TurboQuant ("Ablation...", §2 TurboQuant) */
+#define TQ_ROTATION_NONE 1   /* y = x/||x||, the Beta codebook applied without rotation: the pages' Plain-KV
+                                ("Ablation...", §4, surviving schemes) */
+
 /* Kind of the QJL sketch matrix S_h (tq_params.sketch). */
 #define TQ_SKETCH_GAUSSIAN 0 /* m rows of i.i.d. N(0,1) draws rounded to fp16 (tag 2) */
 #define TQ_SKETCH_RHT 1      /* randomized Hadamard: S_h = H diag(s2_h), s2_h the signs of tag 3, m = d
@@ -72,6 +77,8 @@ typedef struct {
     int32_t n_heads;  /* heads with distinct random state; stream st uses head st % n_heads */
     uint64_t seed;    /* keys the random signs and S */
     int32_t sketch;   /* TQ_SKETCH_GAUSSIAN or TQ_SKETCH_RHT; ignored when m = 0 */
+    int32_t rotation; /* TQ_ROTATION_WHT (0) or TQ_ROTATION_NONE; scores, attention and decode use the
+                         same domain as the encode */
 } tq_params;
 
 typedef struct {

@@ -24,16 +24,19 @@ _DT = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}
 class Codec:
     """d: head_dim (64/128/256); b: codebook bits; m: QJL sketch rows (0 = none);
     n_heads: heads with distinct random state (stream st uses head st % n_heads); seed;
-    sketch: 0 = Gaussian S, 1 = randomized Hadamard S = H diag(s2) (needs m = d)."""
+    sketch: 0 = Gaussian S, 1 = randomized Hadamard S = H diag(s2) (needs m = d);
+    rotation: 0 = WHT with random signs (TurboQuant), 1 = none (Plain-KV)."""
     d: int
     b: int
     m: int = 0
     n_heads: int = 1
     seed: int = 0
     sketch: int = 0
+    rotation: int = 0
 
     def params(self) -> _lib.Params:
-        return _lib.Params(self.d, self.b, self.m, self.n_heads, self.seed & ((1 << 64) - 1), self.sketch)
+        return _lib.Params(self.d, self.b, self.m, self.n_heads, self.seed & ((1 << 64) - 1), self.sketch,
+                           self.rotation)
 
 
 def _stream(device=None) -> ctypes.c_void_p:

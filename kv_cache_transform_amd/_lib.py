@@ -13,6 +13,7 @@ LIB_PATH = os.path.join(_HERE, "libtq.so")
 TQ_OK, TQ_EINVAL, TQ_EUNSUPPORTED, TQ_EALIGN, TQ_EWORKSPACE, TQ_EHIP = 0, -1, -2, -3, -4, -5
 TQ_F32, TQ_BF16, TQ_F16 = 0, 1, 2
 TQ_SKETCH_GAUSSIAN, TQ_SKETCH_RHT = 0, 1
+TQ_ROTATION_WHT, TQ_ROTATION_NONE = 0, 1
 
 # every symbol include/tq.h declares
 EXPORTS = ("tq_get_layout", "tq_encode", "tq_encode_append", "tq_decode", "tq_decode_qjl", "tq_scores_workspace_bytes", "tq_qk_scores",
@@ -23,7 +24,8 @@ EXPORTS = ("tq_get_layout", "tq_encode", "tq_encode_append", "tq_decode", "tq_de
 
 class Params(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("b", ctypes.c_int32), ("m", ctypes.c_int32),
-                ("n_heads", ctypes.c_int32), ("seed", ctypes.c_uint64), ("sketch", ctypes.c_int32)]
+                ("n_heads", ctypes.c_int32), ("seed", ctypes.c_uint64), ("sketch", ctypes.c_int32),
+                ("rotation", ctypes.c_int32)]
 
 
 class Layout(ctypes.Structure):

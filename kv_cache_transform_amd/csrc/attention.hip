@@ -500,7 +500,8 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
         buf[j] = ((acc0 + acc1) + (acc2 + acc3)) * Linv;
     }
     __syncthreads();
-    for (int hh = 1; hh < d; hh <<= 1) {
+    const bool rot = a.tv.rotation != 1;               // Plain-KV values: no inverse rotation
+    for (int hh = 1; hh < (rot ? d : 1); hh <<= 1) {
         for (int i = threadIdx.x; i < d / 2; i += blockDim.x) {
             const int lo = (i / hh) * 2 * hh + (i % hh);
             const float x0 = buf[lo], x1 = buf[lo + hh];
@@ -509,10 +510,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
         }
         __syncthreads();
     }
-    const float inv = 1.0f / sqrtf((float)d);
+    const float inv = rot ? 1.0f / sqrtf((float)d) : 1.0f;
     const float* sg = a.tv.signs + (int64_t)kvh * d;
     for (int j = threadIdx.x; j < d; j += blockDim.x) {
-        const float o = buf[j] * inv * sg[j];
+        const float o = rot ? buf[j] * inv * sg[j] : buf[j];
         if (a.out_bf16) reinterpret_cast<__bf16*>(a.out)[row * d + j] = (__bf16)o;
         else reinterpret_cast<float*>(a.out)[row * d + j] = o;
     }

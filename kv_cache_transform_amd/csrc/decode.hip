@@ -108,11 +108,12 @@ __global__ __launch_bounds__(256, (D == 256 && B == 6 && !OUT_BF16) || QJL ? 1 :
             A0[h] = __builtin_bit_cast(half8, wv);
         }
     }
+    const bool plain = a.t.rotation == 1;              // Plain-KV: no inverse rotation, no signs
     uint32_t smask[C];       // sign bit of output coordinate g C + s
     {
         const float* ss = a.t.signs + (int64_t)head * D + g * C;
 #pragma unroll
-        for (int s = 0; s < C; ++s) smask[s] = f2u(ss[s]) & 0x80000000u;
+        for (int s = 0; s < C; ++s) smask[s] = plain ? 0u : f2u(ss[s]) & 0x80000000u;
     }
     uint32_t s2mask[QJL ? C : 1];   // RHT: sign bit of s2 at coordinate g C + s
     if constexpr (QJL) {
@@ -227,16 +228,21 @@ __global__ __launch_bounds__(256, (D == 256 && B == 6 && !OUT_BF16) || QJL ? 1 :
                 bh = __builtin_bit_cast(half8, hv);
                 bl = __builtin_bit_cast(half8, lv);
             }
+            if (plain) {                                   // no rotation: the coordinates themselves
 #pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                floatx4 r = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0[h], bh, floatx4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
-                r = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0[h], bl, r, 0, 0, 0);
+                for (int jj = 0; jj < 8; ++jj) x[8 * kb + jj] = (float)bh[jj] + (float)bl[jj];
+            } else {
 #pragma unroll
-                for (int i = 0; i < 4; ++i) x[8 * kb + 4 * h + i] = r[i];
+                for (int h = 0; h < 2; ++h) {
+                    floatx4 r = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0[h], bh, floatx4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                    r = __builtin_amdgcn_mfma_f32_16x16x32_f16(A0[h], bl, r, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) x[8 * kb + 4 * h + i] = r[i];
+                }
             }
         }
-        fwht_slots<C, 8>(x);
-        const float sc = nrm * (kInvSqrtD / 4096.0f);     // the LUT holds 2^12 c
+        if (!plain) fwht_slots<C, 8>(x);
+        const float sc = nrm * ((plain ? 1.0f : kInvSqrtD) / 4096.0f);     // the LUT holds 2^12 c
         // the wave's 16 vectors are 16 consecutive rows of the output, one contiguous 16 ES d-byte
         // block: stage the rows in LDS (row stride padded by 16 bytes against bank conflicts) and
         // write the block back linearly, 1 KiB per store instruction

@@ -116,6 +116,7 @@ __global__ __launch_bounds__(256, ((D > 128 && (QJL || !BF16)) || (QJL && !BF16)
     const int lane = threadIdx.x & 63;
     const int v = lane & 15, g = lane >> 4;
     const int wave = threadIdx.x >> 6;
+    const bool plain = a.t.rotation == 1;          // Plain-KV: no sign flip, no WHT
     const float gA = 0.5f * (float)G;
     const float gB = 0.5f * (float)G + 1.0f;       // entry 0 is a guard cell
 
@@ -146,6 +147,14 @@ __global__ __launch_bounds__(256, ((D > 128 && (QJL || !BF16)) || (QJL && !BF16)
         } else {
             constexpr int RB = 4 * R;                     // bytes per run
             constexpr int RA = cmin(pow2_align(RB), 16);
+            if (plain) {                                  // no rotation: coordinates g C .. g C + C - 1
+                if (valid) load_bytes<4 * C, 16>(reinterpret_cast<const uint8_t*>(a.x) + vec * (int64_t)(4 * D) + 4 * g * C, w);
+                else {
+#pragma unroll
+                    for (int k = 0; k < NIW; ++k) w[k] = 0u;
+                }
+                return;
+            }
             const uint8_t* base = reinterpret_cast<const uint8_t*>(a.x) + vec * (int64_t)(4 * D) + 4 * g * R;
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
@@ -188,16 +197,25 @@ __global__ __launch_bounds__(256, ((D > 128 && (QJL || !BF16)) || (QJL && !BF16)
                     const bf16x2 wv = __builtin_bit_cast(bf16x2, w[k]);
                     n2 = __builtin_amdgcn_fdot2_f32_bf16(wv, wv, n2, false);
                 }
+                if (plain) {
+                    // no rotation: slot s is coordinate g C + s itself
 #pragma unroll
-                for (int kb = 0; kb < NKB; ++kb) {
-                    const bf16x8 Bv = __builtin_bit_cast(bf16x8, u32x4{w[4 * kb], w[4 * kb + 1], w[4 * kb + 2], w[4 * kb + 3]});
+                    for (int k = 0; k < C / 2; ++k) {
+                        x[2 * k] = u2f(w[k] << 16);
+                        x[2 * k + 1] = u2f(w[k] & 0xffff0000u);
+                    }
+                } else {
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const floatx4 r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                            __builtin_bit_cast(bf16x8, lds_A[(h * NKB + kb) * 64 + lane]), Bv,
-                            floatx4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                    for (int kb = 0; kb < NKB; ++kb) {
+                        const bf16x8 Bv = __builtin_bit_cast(bf16x8, u32x4{w[4 * kb], w[4 * kb + 1], w[4 * kb + 2], w[4 * kb + 3]});
 #pragma unroll
-                        for (int i = 0; i < 4; ++i) x[8 * kb + 4 * h + i] = r[i];
+                        for (int h = 0; h < 2; ++h) {
+                            const floatx4 r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                __builtin_bit_cast(bf16x8, lds_A[(h * NKB + kb) * 64 + lane]), Bv,
+                                floatx4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+                            for (int i = 0; i < 4; ++i) x[8 * kb + 4 * h + i] = r[i];
+                        }
                     }
                 }
                 // last reads of the raw words: the next pass's loads may reuse their registers
@@ -205,21 +223,23 @@ __global__ __launch_bounds__(256, ((D > 128 && (QJL || !BF16)) || (QJL && !BF16)
                 for (int k = 0; k < NIW; ++k) asm volatile("" ::"v"(w[k]) : "memory");
                 asm volatile("" ::"v"(n2) : "memory");
                 if (t + 4 * NG < tb1) load_group(nxt[gi], t + 4 * NG + gi);
-                fwht_slots<C, 8>(x);
+                if (!plain) fwht_slots<C, 8>(x);
             } else {
 #pragma unroll
                 for (int s = 0; s < C; ++s) {
                     const float xv = u2f(w[s]);
                     n2 = fmaf(xv, xv, n2);
-                    x[s] = xv * sg[s];
+                    x[s] = plain ? xv : xv * sg[s];
                 }
                 if (t + 4 * NG < tb1) load_group(nxt[gi], t + 4 * NG + gi);
-                fwht_slots<C, 1>(x);
-                fwht_cross<C>(x);
+                if (!plain) {
+                    fwht_slots<C, 1>(x);
+                    fwht_cross<C>(x);
+                }
             }
             n2 = sum4(n2);
             const float n = sqrtf(n2);
-            const float sc = n > 0.0f ? kInvSqrtD / n : 0.0f;
+            const float sc = n > 0.0f ? (plain ? 1.0f : kInvSqrtD) / n : 0.0f;
             const float sA = sc * gA;
             const float sE = sc * 16384.0f;
 

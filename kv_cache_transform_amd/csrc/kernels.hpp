@@ -10,6 +10,7 @@ struct DevTables {
     int d = 0, b = 0, m = 0, n_heads = 0;
     uint64_t seed = 0;
     int sketch = 0;                    // TQ_SKETCH_GAUSSIAN or TQ_SKETCH_RHT
+    int rotation = 0;                  // TQ_ROTATION_WHT or TQ_ROTATION_NONE (no sign flip, no WHT)
     int G = 0;                         // search grid cells
     const uint32_t* grid = nullptr;    // (G+2) x {thr fp32 bits, base}
     const float* cent = nullptr;       // 2^b centroids (fp32)

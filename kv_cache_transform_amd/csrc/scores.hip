@@ -32,10 +32,10 @@ __global__ __launch_bounds__(256) void qprep_kernel(QPrepArgs a) {
         } else {
             x = reinterpret_cast<const float*>(a.q)[row * d + j];
         }
-        buf[j] = x * sg[j];
+        buf[j] = a.t.rotation == 1 ? x : x * sg[j];
     }
     __syncthreads();
-    for (int h = 1; h < d; h <<= 1) {
+    for (int h = 1; h < (a.t.rotation == 1 ? 1 : d); h <<= 1) {   // no rotation: q_rot = q
         for (int i = threadIdx.x; i < d / 2; i += blockDim.x) {
             const int lo = (i / h) * 2 * h + (i % h);
             const float x0 = buf[lo], x1 = buf[lo + h];
@@ -44,7 +44,7 @@ __global__ __launch_bounds__(256) void qprep_kernel(QPrepArgs a) {
         }
         __syncthreads();
     }
-    const float inv = 1.0f / sqrtf((float)d);
+    const float inv = a.t.rotation == 1 ? 1.0f : 1.0f / sqrtf((float)d);
     for (int j = threadIdx.x; j < d; j += blockDim.x) {
         const float r = buf[j] * inv;
         buf[j] = r;

@@ -28,6 +28,7 @@ int check_params(const tq_params* p) {
     if (p->n_heads < 1) return TQ_EINVAL;
     if (p->sketch != TQ_SKETCH_GAUSSIAN && p->sketch != TQ_SKETCH_RHT) return TQ_EINVAL;
     if (p->sketch == TQ_SKETCH_RHT && p->m != 0 && p->m != p->d) return TQ_EINVAL;
+    if (p->rotation != TQ_ROTATION_WHT && p->rotation != TQ_ROTATION_NONE) return TQ_EINVAL;
     return TQ_OK;
 }
 
@@ -61,7 +62,7 @@ const Codebook& codebook(int d, int b) {  // caller holds g_mu
 }
 
 // ---- device table cache ----------------------------------------------------------------------
-using TableKey = std::tuple<int, int, int, int, int, uint64_t, int>;  // device, d, b, m, n_heads, seed, sketch
+using TableKey = std::tuple<int, int, int, int, int, uint64_t, int, int>;  // device, d, b, m, n_heads, seed, sketch, rotation
 std::map<TableKey, DevTables> g_tables;
 std::map<int, int> g_num_cus;
 
@@ -146,7 +147,7 @@ int build_tables(const tq_params* p, int device, DevTables* out) {  // caller ho
     }
     uint8_t* base = static_cast<uint8_t*>(dev);
     DevTables t;
-    t.d = d; t.b = b; t.m = m; t.n_heads = H; t.seed = p->seed; t.sketch = rht ? TQ_SKETCH_RHT : TQ_SKETCH_GAUSSIAN;
+    t.d = d; t.b = b; t.m = m; t.n_heads = H; t.seed = p->seed; t.sketch = rht ? TQ_SKETCH_RHT : TQ_SKETCH_GAUSSIAN; t.rotation = p->rotation;
     t.G = grid.G;
     t.grid = reinterpret_cast<const uint32_t*>(base + o_grid);
     t.cent = reinterpret_cast<const float*>(base + o_cent);
@@ -184,7 +185,7 @@ int get_tables(const tq_params* p, DevTables* out, int* num_cus) {
     if (hipGetDevice(&device) != hipSuccess) return TQ_EHIP;
     if (device_cus(num_cus) != TQ_OK) return TQ_EHIP;
     std::lock_guard<std::mutex> lk(g_mu);
-    const TableKey key{device, p->d, p->b, p->m, p->n_heads, p->seed, p->sketch};
+    const TableKey key{device, p->d, p->b, p->m, p->n_heads, p->seed, p->sketch, p->rotation};
     auto it = g_tables.find(key);
     if (it != g_tables.end()) {
         *out = it->second;

@@ -237,12 +237,18 @@ def fwht(v: np.ndarray) -> np.ndarray:
     return v
 
 
-def rotate(u: np.ndarray, s: np.ndarray) -> np.ndarray:
+def rotate(u: np.ndarray, s: np.ndarray | None) -> np.ndarray:
+    """y = H (u ⊙ s) / sqrt(d); s = None is Plain-KV ([AB] §4: the Beta codebook without the WHT),
+    y = u."""
+    if s is None:
+        return np.array(u, dtype=np.float64, copy=True)
     d = u.shape[-1]
     return (u * s) @ hadamard(d) / math.sqrt(d)          # H is symmetric
 
 
-def unrotate(y: np.ndarray, s: np.ndarray) -> np.ndarray:
+def unrotate(y: np.ndarray, s: np.ndarray | None) -> np.ndarray:
+    if s is None:
+        return np.array(y, dtype=np.float64, copy=True)
     d = y.shape[-1]
     return s * (y @ hadamard(d)) / math.sqrt(d)
 

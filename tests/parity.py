@@ -30,11 +30,12 @@ def codebook(d, b):
 
 
 class Tables:
-    def __init__(self, d, b, m, n_heads, seed, sketch=0):
-        """sketch: 0 = Gaussian S (m x d), 1 = randomized Hadamard S = H diag(s2) (m = d)."""
+    def __init__(self, d, b, m, n_heads, seed, sketch=0, rotation=0):
+        """sketch: 0 = Gaussian S (m x d), 1 = randomized Hadamard S = H diag(s2) (m = d);
+        rotation: 0 = WHT with signs, 1 = none (the oracle's s = None)."""
         self.d, self.b, self.m, self.n_heads, self.seed, self.sketch = d, b, m, n_heads, seed, sketch
         self.t, self.c = codebook(d, b)
-        self.s = [O.head_signs(seed, h, d) for h in range(n_heads)]
+        self.s = [None if rotation == 1 else O.head_signs(seed, h, d) for h in range(n_heads)]
         if not m:
             self.S = None
         elif sketch == 1:

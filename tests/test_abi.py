@@ -76,8 +76,8 @@ def test_status_strings():
     assert _lib.status_string(-99) == "unknown status"
 
 
-def _p(d=128, b=4, m=0, H=1, seed=0, sketch=0):
-    return ctypes.byref(_lib.Params(d, b, m, H, seed, sketch))
+def _p(d=128, b=4, m=0, H=1, seed=0, sketch=0, rotation=0):
+    return ctypes.byref(_lib.Params(d, b, m, H, seed, sketch, rotation))
 
 
 def test_argument_validation_before_any_gpu_call():
@@ -85,7 +85,7 @@ def test_argument_validation_before_any_gpu_call():
     lay = _lib.Layout()
     bad = [(_p(d=96), "d"), (_p(d=32), "d"), (_p(b=0), "b"), (_p(b=9), "b"), (_p(m=48), "m%32"),
            (_p(m=256, d=128), "m>d"), (_p(H=0), "n_heads"), (_p(m=128, sketch=2), "sketch kind"),
-           (_p(m=64, sketch=1), "RHT needs m = d"), (_p(sketch=-1), "sketch kind")]
+           (_p(m=64, sketch=1), "RHT needs m = d"), (_p(sketch=-1), "sketch kind"), (_p(rotation=2), "rotation")]
     for p, why in bad:
         assert L.tq_get_layout(p, 1, 1, ctypes.byref(lay)) == _lib.TQ_EINVAL, why
         assert L.tq_encode(p, ctypes.c_void_p(16), 1, 1, 1, ctypes.c_void_p(16), None) == _lib.TQ_EINVAL, why

@@ -300,6 +300,50 @@ def test_decode_attention_per_batch_lengths(lens):
             assert P.rel_l2(out[bi, h], ref) <= 2e-3, (bi, h, L)
 
 
+# ---------------------------------------------------------------------------------------------
+# Plain-KV: the Beta codebook on the unrotated unit vector (rotation = none)
+@pytest.mark.parametrize("d,b,m,kind,dt", [(128, 4, 0, 0, torch.bfloat16), (128, 3, 128, 0, torch.bfloat16),
+                                           (64, 2, 64, 1, torch.bfloat16), (256, 5, 0, 0, torch.bfloat16),
+                                           (128, 4, 32, 0, torch.float32)])
+def test_plain_encode_decode_scores_parity(d, b, m, kind, dt):
+    S, N, H, nq, seed = 2, 600, 2, 5, 9100 + d + b + m
+    codec = T.Codec(d, b, m, H, seed, kind, rotation=1)
+    x = I.gaussian((S, N, d), seed, device=DEV, dtype=dt)
+    buf = _enc(codec, x)
+    tb = P.Tables(d, b, m, H, seed, kind, rotation=1)
+    st = P.check_encode(tb, _x64(x), buf)
+    gbuf = torch.as_tensor(buf, device=DEV)
+    out = T.decode(codec, gbuf, S, N, torch.float32).cpu().numpy()
+    P.check_decode_f32(tb, st["recs"], list(range(S)), out)
+    if m:
+        outq = T.decode(codec, gbuf, S, N, torch.float32, qjl=True).cpu().numpy()
+        P.check_decode_f32(tb, st["recs"], list(range(S)), outq, qjl=True)
+    q = I.gaussian((S, nq, d), seed + 3, device=DEV)
+    sc = T.qk_scores(codec, q, gbuf, N).cpu().numpy()
+    P.check_scores(tb, st["recs"], list(range(S)), _x64(q), sc)
+
+
+@pytest.mark.parametrize("rk,rv", [(1, 1), (1, 0), (0, 1)])
+def test_plain_decode_attention(rk, rv):
+    batch, hq, hkv, N, d, b, m, seed = 2, 8, 2, 1500, 128, 4, 128, 9300
+    ck, cv = T.Codec(d, b, m, hkv, seed, rotation=rk), T.Codec(d, b, 0, hkv, seed + 1, rotation=rv)
+    K = I.rope_gaussian(batch * hkv, N, d, seed, device=DEV)
+    V = I.rope_gaussian(batch * hkv, N, d, seed + 1, device=DEV)
+    q = I.cfg4_queries(batch, hq, d, N, seed + 2, device=DEV)
+    pk, pv = T.encode(ck, K), T.encode(cv, V)
+    out = T.decode_attention(ck, cv, q, pk, pv, hkv, N, out_dtype=torch.float32).cpu().numpy()
+    tk, tv = P.Tables(d, b, m, hkv, seed, rotation=rk), P.Tables(d, b, 0, hkv, seed + 1, rotation=rv)
+    rkk = O.unpack_tensor(pk.cpu().numpy(), d, b, m, batch * hkv, N)
+    rvv = O.unpack_tensor(pv.cpu().numpy(), d, b, 0, batch * hkv, N)
+    q64 = _x64(q)
+    g = hq // hkv
+    for bi in range(batch):
+        for h in range(hq):
+            st = bi * hkv + h // g
+            ref = P.oracle_attention_row(tk, tv, rkk[st], rvv[st], st, q64[bi, h], 1 / math.sqrt(d))
+            assert P.rel_l2(out[bi, h], ref) <= 2e-3, (bi, h)
+
+
 def test_decode_attention_explicit_scale():
     e, _ = _attention_case(1, 4, 2, 900, 128, 4, 128, torch.float32, scale=0.05)
     assert e <= 2e-3
