@@ -230,6 +230,19 @@ def main():
                                          "achieved_GBs": round(qalg / (qms * 1e-3) / 1e9, 1),
                                          "hbm_frac": round(qalg / (qms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         del xh
+        # the V encode without rotation (Plain-KV): the same quantiser on the unrotated unit vector
+        cv_plain = T.Codec(d, 4, 0, Hkv, 4002, rotation=1)
+        T.encode(cv_plain, V, pv)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(3):
+            T.encode(cv_plain, V, pv)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        pms = e0.elapsed_time(e1) / 3
+        kern["encode_v_plain"] = {"ms": round(pms, 4), "alg_bytes": alg["encode_v"],
+                                  "achieved_GBs": round(alg["encode_v"] / (pms * 1e-3) / 1e9, 1),
+                                  "hbm_frac": round(alg["encode_v"] / (pms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
     sample_k, sample_v = K[:1, :2048].clone(), V[:1, :2048].clone()   # the CPU baseline's sample
     del K
 
