@@ -34,17 +34,17 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published (the sketch p
 # the kernel's sources are the ones it was measured on (sha256 of the .hip file + shared headers).
 FETCH_UNIT_B, WRITE_UNIT_B = 2048, 1024
 TRAFFIC = {
-    "encode_k": {"fetch": 2098029.375, "write": 1392972.4375, "src": "encode.hip",
-        "sha": "b0fc47b1a37a968e2c667fab99fbd7aab761170b8bbb05594186e63e8bfcc6f0"},
-    "encode_v": {"fetch": 2097225.5, "write": 1092388.96875, "src": "encode.hip",
-        "sha": "b0fc47b1a37a968e2c667fab99fbd7aab761170b8bbb05594186e63e8bfcc6f0"},
-    "decode_attention": {"fetch": 1229662.75, "write": 4160.0, "src": "attention.hip",
-        "sha": "f4aba8cac61d105d85e7e11543cae7b1c581c4d4821f2a3667ec5e5e4233c2cd"},
-    "decode_v_bf16": {"fetch": 551112.0625, "write": 4194304.0, "src": "decode.hip",
-        "sha": "1305b66b060b192e2cba4cafc8529e576e0dc6284221101dbdf82d295d994d66"},
+    "encode_k": {"fetch": 2098035.625, "write": 1393991.71875, "src": "encode.hip",
+        "sha": "0adeae70cbcd033f6e2f467023ae3e13733375d59baa196f3d078c45409c9a01"},
+    "encode_v": {"fetch": 2099468.6875, "write": 1091291.1875, "src": "encode.hip",
+        "sha": "0adeae70cbcd033f6e2f467023ae3e13733375d59baa196f3d078c45409c9a01"},
+    "decode_attention": {"fetch": 1229886.5625, "write": 4160.0, "src": "attention.hip",
+        "sha": "5eaa6f22be6d97fd700da9ac46a3e41690d14c0314e54edf6993c26acab1c6d7"},
+    "decode_v_bf16": {"fetch": 550498.0, "write": 4194304.0, "src": "decode.hip",
+        "sha": "2add9ea1fa8cf5d1d37b9846a4505b28cdfa3553557c2e41c88d2f2cc96455e9"},
 }
 TRAFFIC_HEADERS_SHA = ("9241f7e7fc6398e3b61bd782d033f3beac2c8fe34392745cceb9f2f364e6409c"   # common.hpp
-                       "6e57abc34782d6aeec8cd0c4e32a9c38d93958dc7a1ff9c2e10d2f5c99ce77f4")  # kernels.hpp
+                       "4b7bff386ff4b44e581f4d585bec686d2e3a7033871a21ebe797ef96ebd8decf")  # kernels.hpp
 
 
 def _sha(path: str) -> str:
