@@ -124,3 +124,98 @@ def test_correction_through_S_instead_of_S_transpose_is_caught(monkeypatch):
         return math.sqrt(math.pi / 2.0) / S.shape[0] * np.asarray(r16, dtype=np.float64)[:, None] * (pm @ S.T)
     monkeypatch.setattr(O, "qjl_correction", corr)
     _fails(RH.test_correction_closed_form_on_a_hadamard_column)
+
+
+# ---- SpectralQuant oracle ---------------------------------------------------------------------
+from oracle import sq_oracle as SQ
+from tests import test_oracle_sq as SP
+
+
+def test_sq_projection_through_the_transpose_is_caught(monkeypatch):
+    monkeypatch.setattr(SQ, "project", lambda x, model: np.asarray(x, dtype=np.float64) @ model["U"].T)
+    _fails(SP.test_codec_distortion_is_the_gaussian_rate_distortion_of_its_allocation, False)
+
+
+def test_sq_scale_by_variance_instead_of_deviation_is_caught(monkeypatch):
+    real = SQ.calibrate
+    def calibrate(*a, **k):
+        m = real(*a, **k)
+        m["sigma"] = m["sigma"] ** 2
+        return m
+    monkeypatch.setattr(SQ, "calibrate", calibrate)
+    _fails(SP.test_codec_distortion_is_the_gaussian_rate_distortion_of_its_allocation, True)
+
+
+def test_sq_waterfill_to_the_smallest_distortion_is_caught(monkeypatch):
+    def waterfill(lam_sem, total, b_tail, b_max=8):
+        bits = np.full(len(lam_sem), b_tail, dtype=np.int64)
+        for _ in range(total - int(bits.sum())):
+            k = int(np.argmin(np.where(bits < b_max, lam_sem * 4.0 ** -bits, np.inf)))
+            bits[k] += 1
+        return bits
+    monkeypatch.setattr(SQ, "waterfill", waterfill)
+    _fails(SP.test_waterfill_is_uniform_at_ratio_at_most_4_and_optimal_otherwise)
+
+
+def test_sq_tail_at_the_semantic_width_is_caught(monkeypatch):
+    real = SQ.calibrate
+    def calibrate(x, b, b_tail, **k):
+        return real(x, b, b, **k)
+    monkeypatch.setattr(SQ, "calibrate", calibrate)
+    _fails(SP.test_storage_bits_match_the_pages)
+
+
+def test_sq_inverted_gap_ratio_is_caught(monkeypatch):
+    def effective_dim(lam, gamma=10.0, d_eff_max=0):
+        d_eff = min(max(SQ.participation_ratio(lam), 1), len(lam))
+        if gamma > 0:
+            for k in range(1, d_eff):
+                if lam[k] / lam[k - 1] > gamma:
+                    d_eff = k
+                    break
+        return min(d_eff, d_eff_max) if d_eff_max > 0 else d_eff
+    monkeypatch.setattr(SQ, "effective_dim", effective_dim)
+    _fails(SP.test_gap_criterion_trims_a_spurious_dimension_and_the_cap_applies)
+
+
+def test_sq_centred_covariance_is_caught(monkeypatch):
+    def covariance(x_cal):
+        x = np.asarray(x_cal, dtype=np.float64)
+        x = x - x.mean(axis=0)
+        return x.T @ x / x.shape[0]
+    monkeypatch.setattr(SQ, "covariance", covariance)
+    _fails(SP.test_covariance_is_not_centred)
+
+
+def test_sq_msb_first_fields_are_caught(monkeypatch):
+    def pack(idx, bits, rec_bytes):
+        n, d = idx.shape
+        out = np.zeros((n, rec_bytes * 8), dtype=np.uint8)
+        pos = 0
+        for k in range(d):
+            w = int(bits[k])
+            for i in range(w):
+                out[:, pos + i] = (idx[:, k] >> (w - 1 - i)) & 1
+            pos += w
+        return np.packbits(out, axis=1, bitorder="little")
+    monkeypatch.setattr(SQ, "pack", pack)
+    _fails(SP.test_index_is_the_nearest_centroid_and_records_round_trip)
+
+
+def test_sq_unconverged_codebook_is_caught(monkeypatch):
+    real = SQ.gauss_lloyd_max.__wrapped__
+    monkeypatch.setattr(SQ, "gauss_lloyd_max", lambda b, **k: real(b, max_iter=2))
+    _fails(SP.test_gauss_codebook_matches_max_1960_table)
+
+
+def test_sq_ties_to_the_lower_cell_are_caught(monkeypatch):
+    real = SQ.encode
+    def encode(x, model):
+        r = real(x, model)
+        for w in np.unique(model["bits"]):
+            cols = model["bits"] == w
+            t, _ = SQ.gauss_lloyd_max(int(w))
+            r["idx"][:, cols] = np.sum(r["u"][:, cols, None] > t[None, None, :], axis=2)
+        return r
+    monkeypatch.setattr(SQ, "encode", encode)
+    _fails(SP.test_index_counts_thresholds_with_ties_to_the_upper_cell)
