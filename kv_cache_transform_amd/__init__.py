@@ -15,7 +15,7 @@ from . import _lib
 from ._lib import TQError, TQ_BF16, TQ_F32
 
 __all__ = ["Codec", "TQError", "get_layout", "encode", "decode", "qk_scores", "decode_attention",
-           "attention_workspace_bytes", "host_tables", "clear_cache"]
+           "attention_workspace_bytes", "host_tables", "clear_cache", "SQCodec", "sq_host_codebook"]
 
 _DT = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}
 
@@ -152,3 +152,109 @@ def host_tables(codec: Codec, head: int = 0) -> dict:
 
 def clear_cache() -> None:
     _lib.lib().tq_clear_cache()
+
+
+class SQCodec:
+    """SpectralQuant codec (include/tq_sq.h): one calibrated eigenbasis per head, the semantic
+    dimensions at b bits (or water-filled), the tail at b_tail bits, per-dimension Gaussian
+    Lloyd-Max codebooks ("Ablation, Statistical Inference, and Validation for KV-Cache
+    Compression", §2 "SpectralQuant", §6, §7).  Build with ``SQCodec.calibrate``; the device tables
+    live on the device that was current then and are freed with the object."""
+
+    def __init__(self, d: int, n_heads: int, basis, lam, bits, d_eff=None, device=None):
+        import numpy as np
+        self.d, self.n_heads = int(d), int(n_heads)
+        self.basis = np.ascontiguousarray(basis, dtype=np.float64).reshape(n_heads, d, d)
+        self.lam = np.ascontiguousarray(lam, dtype=np.float64).reshape(n_heads, d)
+        self.bits = np.ascontiguousarray(bits, dtype=np.int32).reshape(n_heads, d)
+        self.d_eff = None if d_eff is None else np.asarray(d_eff, dtype=np.int32)
+        self._h = None
+        p = _lib.SqParams(self.d, self.n_heads, 1, 1, 0, 0, 0.0)
+        h = ctypes.c_void_p()
+        with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
+            self.device = torch.cuda.current_device()
+            _lib.check(_lib.lib().tq_sq_create(ctypes.byref(p), self.basis.ctypes.data, self.lam.ctypes.data,
+                                               self.bits.ctypes.data, ctypes.byref(h)), "tq_sq_create")
+        self._h = h
+        rb = ctypes.c_int64()
+        _lib.check(_lib.lib().tq_sq_record_bytes(self._h, ctypes.byref(rb)), "tq_sq_record_bytes")
+        self.record_bytes = int(rb.value)
+
+    @staticmethod
+    def calibrate_host(x_cal, b: int, b_tail: int, waterfill: bool = False, gamma: float = 10.0,
+                       d_eff_max: int = 0) -> dict:
+        """x_cal: [n_heads, n_cal, d] float32 (host or device) -> the model arrays (host numpy)."""
+        import numpy as np
+        x = x_cal.detach().float().cpu().numpy() if isinstance(x_cal, torch.Tensor) else np.asarray(x_cal)
+        x = np.ascontiguousarray(x, dtype=np.float32)
+        H, n_cal, d = x.shape
+        p = _lib.SqParams(d, H, b, b_tail, int(bool(waterfill)), d_eff_max, float(gamma))
+        basis = np.zeros((H, d, d), dtype=np.float64)
+        lam = np.zeros((H, d), dtype=np.float64)
+        bits = np.zeros((H, d), dtype=np.int32)
+        d_eff = np.zeros(H, dtype=np.int32)
+        _lib.check(_lib.lib().tq_sq_calibrate(ctypes.byref(p), x.ctypes.data, n_cal, basis.ctypes.data,
+                                              lam.ctypes.data, bits.ctypes.data, d_eff.ctypes.data),
+                   "tq_sq_calibrate")
+        return {"basis": basis, "lam": lam, "bits": bits, "d_eff": d_eff}
+
+    @classmethod
+    def calibrate(cls, x_cal, b: int, b_tail: int, waterfill: bool = False, gamma: float = 10.0,
+                  d_eff_max: int = 0, device=None) -> "SQCodec":
+        m = cls.calibrate_host(x_cal, b, b_tail, waterfill, gamma, d_eff_max)
+        H, d = m["lam"].shape
+        return cls(d, H, m["basis"], m["lam"], m["bits"], m["d_eff"], device)
+
+    def __del__(self):
+        if getattr(self, "_h", None) is not None:
+            try:
+                torch.cuda.synchronize(self.device)
+            except Exception:
+                pass
+            _lib.lib().tq_sq_destroy(self._h)
+            self._h = None
+
+    def encode(self, x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+        """x: [n_streams, n_tokens, d] bfloat16 -> packed records (uint8, n_streams·n_tokens·record_bytes)."""
+        if x.dim() != 3 or x.shape[-1] != self.d or not x.is_contiguous():
+            raise ValueError("x must be a contiguous [n_streams, n_tokens, d] tensor")
+        S, N, _ = x.shape
+        need = S * N * self.record_bytes
+        if out is None:
+            out = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+        elif out.numel() < need or out.dtype != torch.uint8:
+            raise ValueError("packed buffer too small")
+        _lib.check(_lib.lib().tq_sq_encode(self._h, _ptr(x), _DT.get(x.dtype, -1), S, N, _ptr(out),
+                                           _stream(x.device)), "tq_sq_encode")
+        return out
+
+    def decode(self, packed: torch.Tensor, n_streams: int, n_tokens: int, dtype: torch.dtype = torch.float32,
+               out: torch.Tensor | None = None) -> torch.Tensor:
+        if out is None:
+            out = torch.empty(n_streams, n_tokens, self.d, dtype=dtype, device=packed.device)
+        _lib.check(_lib.lib().tq_sq_decode(self._h, _ptr(packed), n_streams, n_tokens, _ptr(out),
+                                           _DT[out.dtype], _stream(packed.device)), "tq_sq_decode")
+        return out
+
+    def qk_scores(self, q: torch.Tensor, packed_k: torch.Tensor, n_tokens: int, out: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None) -> torch.Tensor:
+        """q: [n_streams, n_q, d] -> <Uᵀq, ẑ> as float32 [n_streams, n_q, n_tokens]."""
+        S, nq, _ = q.shape
+        ws = int(_lib.lib().tq_sq_scores_workspace_bytes(self._h, S, nq))
+        if workspace is None:
+            workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=q.device)
+        if out is None:
+            out = torch.empty(S, nq, n_tokens, dtype=torch.float32, device=q.device)
+        _lib.check(_lib.lib().tq_sq_qk_scores(self._h, _ptr(q), _DT[q.dtype], nq, _ptr(packed_k), S, n_tokens,
+                                              _ptr(out), _ptr(workspace), workspace.numel(), _stream(q.device)),
+                   "tq_sq_qk_scores")
+        return out
+
+
+def sq_host_codebook(b: int) -> dict:
+    """The library's b-bit Gaussian Lloyd-Max codebook (host fp64)."""
+    import numpy as np
+    thr = np.zeros((1 << b) - 1, dtype=np.float64)
+    cen = np.zeros(1 << b, dtype=np.float64)
+    _lib.check(_lib.lib().tq_sq_host_codebook(b, thr.ctypes.data, cen.ctypes.data), "tq_sq_host_codebook")
+    return {"thresholds": thr, "centroids": cen}

@@ -1,4 +1,4 @@
-"""ctypes loader for libtq.so (the C ABI declared in include/tq.h).
+"""ctypes loader for libtq.so (the C ABI declared in include/tq.h and include/tq_sq.h).
 
 The library is required: there is no fallback implementation.  If libtq.so has not been built
 (``python -m kv_cache_transform_amd.build``) every call raises."""
@@ -20,12 +20,21 @@ EXPORTS = ("tq_get_layout", "tq_encode", "tq_encode_append", "tq_decode", "tq_de
            "tq_attention_workspace_bytes", "tq_decode_attention", "tq_decode_attention_varlen", "tq_host_tables",
            "tq_status_string",
            "tq_clear_cache")
+# every symbol include/tq_sq.h declares
+SQ_EXPORTS = ("tq_sq_calibrate", "tq_sq_create", "tq_sq_destroy", "tq_sq_record_bytes", "tq_sq_encode",
+              "tq_sq_decode", "tq_sq_scores_workspace_bytes", "tq_sq_qk_scores", "tq_sq_host_codebook")
 
 
 class Params(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("b", ctypes.c_int32), ("m", ctypes.c_int32),
                 ("n_heads", ctypes.c_int32), ("seed", ctypes.c_uint64), ("sketch", ctypes.c_int32),
                 ("rotation", ctypes.c_int32)]
+
+
+class SqParams(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("b", ctypes.c_int32),
+                ("b_tail", ctypes.c_int32), ("waterfill", ctypes.c_int32), ("d_eff_max", ctypes.c_int32),
+                ("gamma", ctypes.c_double)]
 
 
 class Layout(ctypes.Structure):
@@ -51,6 +60,7 @@ def lib() -> ctypes.CDLL:
         raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -m kv_cache_transform_amd.build`")
     L = ctypes.CDLL(LIB_PATH)
     P, I64, VP, I32, SZ = ctypes.POINTER(Params), ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
+    Q = ctypes.POINTER(SqParams)
     sig = {
         "tq_get_layout": (ctypes.c_int, [P, I64, I64, ctypes.POINTER(Layout)]),
         "tq_encode": (ctypes.c_int, [P, VP, ctypes.c_int, I64, I64, VP, VP]),
@@ -67,6 +77,15 @@ def lib() -> ctypes.CDLL:
         "tq_host_tables": (ctypes.c_int, [P, I32, VP, VP, VP, VP]),
         "tq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "tq_clear_cache": (None, []),
+        "tq_sq_calibrate": (ctypes.c_int, [Q, VP, I64, VP, VP, VP, VP]),
+        "tq_sq_create": (ctypes.c_int, [Q, VP, VP, VP, ctypes.POINTER(VP)]),
+        "tq_sq_destroy": (None, [VP]),
+        "tq_sq_record_bytes": (ctypes.c_int, [VP, ctypes.POINTER(I64)]),
+        "tq_sq_encode": (ctypes.c_int, [VP, VP, ctypes.c_int, I64, I64, VP, VP]),
+        "tq_sq_decode": (ctypes.c_int, [VP, VP, I64, I64, VP, ctypes.c_int, VP]),
+        "tq_sq_scores_workspace_bytes": (SZ, [VP, I64, I64]),
+        "tq_sq_qk_scores": (ctypes.c_int, [VP, VP, ctypes.c_int, I64, VP, I64, I64, VP, VP, SZ, VP]),
+        "tq_sq_host_codebook": (ctypes.c_int, [I32, VP, VP]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)

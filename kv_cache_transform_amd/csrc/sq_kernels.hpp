@@ -1,0 +1,67 @@
+// Device tables and launchers of the SpectralQuant codec (calibrated eigenbasis, per-dimension
+// Gaussian Lloyd-Max codebooks; "Ablation, Statistical Inference, and Validation for KV-Cache
+// Compression", §2 "SpectralQuant").
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace tq {
+
+// Search-grid domain of a Gaussian codebook: u = z/σ in [-kSqRange, kSqRange] maps to
+// u_grid = u·G/(2 kSqRange) + G/2 + 1 in [1, G+1]; outside it the cells clamp to 0 and G+2.
+constexpr double kSqRange = 8.0;
+
+struct SqDev {
+    int d = 0, n_heads = 0, rec_words = 0;
+    // encode: Uᵀ·2^8 as fp16 hi, lo in MFMA B-operand order [head][part][tile D/16][kstep D/32][lane][8]
+    const _Float16* enc_b = nullptr;
+    // encode: per (head, dimension k) {mul, add, meta, cmax}: u_grid = z·2^(8+sc)·mul... (see sq.hip)
+    const float4* enc_desc = nullptr;
+    const uint32_t* grids = nullptr;   // the grids of every width in use, 2 words per cell
+    // decode: (U diag(σ))·2^e_h as fp16 hi, lo in MFMA A-operand order [head][part][tile][kstep][lane][8]
+    const _Float16* dec_a = nullptr;
+    const float* dec_scale = nullptr;  // [head] 2^-(e_h + 12)
+    // field extraction per (head, kstep, lane part g): {first dword, rel offsets 0..3, rel 4..7, widths}
+    const uint4* fields = nullptr;
+    const _Float16* cb_hl = nullptr;   // codebook of width w at 2^w - 2: (hi, lo) of c·2^12, 2 halves each
+    const _Float16* cb_h = nullptr;    // same indexing, fp16 c
+    const float* U32 = nullptr;        // [head][j][k] fp32
+    const float* sigma = nullptr;      // [head][k]
+    int lds_grid_words = 0;            // total words of `grids`
+    void* blob = nullptr;
+};
+
+struct SqEncodeArgs {
+    SqDev t;
+    const uint16_t* x;      // bf16 [streams][tokens][d]
+    uint32_t* out;          // records [streams][tokens][rec_words]
+    int64_t n_streams, n_tokens, tiles_per_stream;
+    int64_t blocks_per_stream, tiles_per_block;
+};
+
+struct SqDecodeArgs {
+    SqDev t;
+    const uint32_t* in;
+    void* out;              // fp32 or bf16 [streams][tokens][d]
+    int64_t n_streams, n_tokens, tiles_per_stream;
+    int64_t blocks_per_stream, tiles_per_block;
+};
+
+struct SqScoresArgs {
+    SqDev t;
+    const void* q;          // [streams][n_q][d] fp32 or bf16
+    int q_bf16;
+    const uint32_t* in;
+    float* scores;          // [streams][n_q][tokens]
+    _Float16* qp;           // workspace: [streams][nq_pad][d] fp16 of (Uᵀq ⊙ σ)·2^e_row
+    float* qscale;          // workspace: [streams][nq_pad] 2^-e_row
+    int64_t n_streams, n_tokens, n_q, nq_pad, tiles_per_stream;
+    int64_t blocks_per_stream, tiles_per_block;
+};
+
+hipError_t launch_sq_encode(const SqEncodeArgs& a, int num_cus, hipStream_t s);
+hipError_t launch_sq_decode(const SqDecodeArgs& a, bool out_bf16, int num_cus, hipStream_t s);
+hipError_t launch_sq_scores(const SqScoresArgs& a, int num_cus, hipStream_t s);
+
+}  // namespace tq

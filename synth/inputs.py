@@ -94,6 +94,39 @@ def student_t(n_streams: int, n_tokens: int, d: int, nu: int, seed: int, device=
     return out
 
 
+def low_rank(n_streams: int, n_tokens: int, d: int, spectrum, noise: float, seed: int, subspace_seed: int,
+             n_heads: int | None = None, device="cpu", dtype=torch.bfloat16, exclude_seed: int | None = None
+             ) -> torch.Tensor:
+    """Tokens in a random rank-r subspace plus isotropic noise: x = B_h (g ⊙ sqrt(spectrum)) + noise·n,
+    g, n ~ N(0, I), B_h a d x r orthonormal basis drawn per head h = stream % n_heads from
+    `subspace_seed` (QR of a Gaussian matrix).  With `exclude_seed`, B_h is drawn inside the
+    orthogonal complement of the basis that seed gives (K and V in orthogonal subspaces).  These are
+    the structured regimes "lowrank", "lowrank_aligned", "lowrank_steep" and "lowrank_misalign" of
+    "Ablation, Statistical Inference, and Validation for KV-Cache Compression", §8 (Table 4)."""
+    spec = np.asarray(spectrum, dtype=np.float64)
+    r = len(spec)
+    n_heads = n_heads or n_streams
+    bases = []
+    for h in range(n_heads):
+        rng = np.random.default_rng(subspace_seed * 7919 + h)
+        if exclude_seed is None:
+            B, _ = np.linalg.qr(rng.standard_normal((d, r)))
+        else:
+            E, _ = np.linalg.qr(np.random.default_rng(exclude_seed * 7919 + h).standard_normal((d, r)))
+            M = rng.standard_normal((d, r))
+            B, _ = np.linalg.qr(M - E @ (E.T @ M))
+        bases.append(torch.from_numpy(B * np.sqrt(spec)[None, :]).float())
+    out = torch.empty(n_streams, n_tokens, d, dtype=dtype, device=device)
+    for s in range(n_streams):
+        g = _gen(seed * 1000003 + s, device)
+        z = torch.randn(n_tokens, r, generator=g, device=device, dtype=torch.float32)
+        x = z @ bases[s % n_heads].to(device).T
+        if noise > 0:
+            x += noise * torch.randn(n_tokens, d, generator=g, device=device, dtype=torch.float32)
+        out[s] = x.to(dtype)
+    return out
+
+
 def bf16_bits(t: torch.Tensor) -> np.ndarray:
     """Exact host copy of a bf16 tensor as uint16 bit patterns."""
     return t.detach().cpu().contiguous().view(torch.int16).numpy().view(np.uint16)
