@@ -243,6 +243,35 @@ def main():
         kern["encode_v_plain"] = {"ms": round(pms, 4), "alg_bytes": alg["encode_v"],
                                   "achieved_GBs": round(alg["encode_v"] / (pms * 1e-3) / 1e9, 1),
                                   "hbm_frac": round(alg["encode_v"] / (pms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        # SpectralQuant on the same K cache: one eigenbasis per kv head calibrated on that head's first
+        # 512 tokens of batch element 0, semantic dimensions at 4 bits, the tail at 2 bits
+        sq = T.SQCodec.calibrate(K[:Hkv, :512].float(), 4, 2, device=0)
+        sq_alg = nvec * (2 * d + sq.record_bytes)
+        sq.encode(K, pk)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(3):
+            sq.encode(K, pk)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        sms = e0.elapsed_time(e1) / 3
+        kern["sq_encode_k"] = {"ms": round(sms, 4), "alg_bytes": sq_alg, "record_bytes": sq.record_bytes,
+                               "d_eff": [int(v) for v in sq.d_eff],
+                               "achieved_GBs": round(sq_alg / (sms * 1e-3) / 1e9, 1),
+                               "hbm_frac": round(sq_alg / (sms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        xh = torch.empty(streams, N, d, dtype=torch.bfloat16, device=dev)
+        sq.decode(pk, streams, N, torch.bfloat16, out=xh)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(3):
+            sq.decode(pk, streams, N, torch.bfloat16, out=xh)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        sdm = e0.elapsed_time(e1) / 3
+        kern["sq_decode_k_bf16"] = {"ms": round(sdm, 4), "alg_bytes": sq_alg,
+                                    "achieved_GBs": round(sq_alg / (sdm * 1e-3) / 1e9, 1),
+                                    "hbm_frac": round(sq_alg / (sdm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del xh, sq
     sample_k, sample_v = K[:1, :2048].clone(), V[:1, :2048].clone()   # the CPU baseline's sample
     del K
 

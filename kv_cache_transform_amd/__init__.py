@@ -206,13 +206,14 @@ class SQCodec:
         return cls(d, H, m["basis"], m["lam"], m["bits"], m["d_eff"], device)
 
     def __del__(self):
-        if getattr(self, "_h", None) is not None:
-            try:
-                torch.cuda.synchronize(self.device)
-            except Exception:
-                pass
-            _lib.lib().tq_sq_destroy(self._h)
-            self._h = None
+        h, self._h = getattr(self, "_h", None), None
+        if h is None:
+            return
+        try:        # at interpreter exit the modules may already be gone: then the process frees it
+            torch.cuda.synchronize(self.device)
+            _lib.lib().tq_sq_destroy(h)
+        except Exception:
+            pass
 
     def encode(self, x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
         """x: [n_streams, n_tokens, d] bfloat16 -> packed records (uint8, n_streams·n_tokens·record_bytes)."""

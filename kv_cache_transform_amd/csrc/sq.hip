@@ -10,8 +10,10 @@
 //           two per vector into fp16, exactly), B = U·2^8 as an fp16 hi + lo pair from LDS, two
 //           products per step.  Lane (n = l%16, g) ends with coordinate k = 16t + n of vectors
 //           4g + r, so its per-dimension constants (scale, grid, bit offset, width) stay in
-//           registers.  Each index is OR-ed into a per-wave LDS record (ds_or), and the wave's 16
-//           records are then written out linearly.
+//           registers.  The 4 lanes of a quad hold dimensions 4q..4q+3, whose fields are adjacent:
+//           their shifted indices are OR-ed together over DPP, the quad's first lane ORs the group
+//           into the vector's record in LDS (ds_or), and the wave's 16 records are then written
+//           out linearly.
 //   decode  D[j][vector] = Σ_k (U diag σ)[j][k] · c[vector][k]: A = U diag(σ)·2^e as hi + lo from LDS,
 //           B = the codebook values as hi + lo of c·2^12 (three products per step, about 2^-21
 //           relative).  Lane (v, g) extracts its 8 contiguous fields k = 32s + 8g + i of vector v
@@ -34,6 +36,15 @@ constexpr size_t kLdsMax = 163840;
 
 __device__ __forceinline__ half8 as_half8(const u32x4& w) { return __builtin_bit_cast(half8, w); }
 
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+// OR of v over the 4 lanes of its quad (DPP quad permutations [1,0,3,2] then [2,3,0,1])
+__device__ __forceinline__ uint32_t quad_or(uint32_t v) {
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xb1, 0xf, 0xf, true);
+    v |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4e, 0xf, 0xf, true);
+    return v;
+}
+
 // bf16 pair (one word) times 2^sc into an fp16 pair (exact for every value within 2^-24 of the
 // vector's largest; smaller ones are truncated to the fp16 subnormal grid)
 __device__ __forceinline__ uint32_t bf16x2_to_f16x2_scaled(uint32_t w, int sc) {
@@ -42,13 +53,35 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2_scaled(uint32_t w, int sc) {
     return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(f0, f1));
 }
 
-// field i of a lane's 8-field window: words d0..d3 from the record, rel < 96, width 1..8
-__device__ __forceinline__ uint32_t window_field(uint32_t d0, uint32_t d1, uint32_t d2, uint32_t d3,
-                                                 uint32_t rel, uint32_t wid) {
-    const uint32_t di = rel >> 5;
-    const uint32_t lo = di == 0 ? d0 : (di == 1 ? d1 : d2);
-    const uint32_t hi = di == 0 ? d1 : (di == 1 ? d2 : d3);
-    return __builtin_amdgcn_ubfe(__builtin_amdgcn_alignbit(hi, lo, rel & 31u), 0, wid);
+__device__ __forceinline__ uint32_t bf16_pair(float lo, float hi) {
+    const bf16x2 v = {(__bf16)lo, (__bf16)hi};   // round to nearest even
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// records of `count` words starting at `src` (valid words < n_valid) into registers, one word per
+// lane per step; NP steps cover up to 64·NP words
+template <int NP>
+__device__ __forceinline__ void fetch_words(const uint32_t* src, int count, int n_valid, int lane, uint32_t (&w)[NP]) {
+#pragma unroll
+    for (int j = 0; j < NP; ++j) {
+        const int i = lane + 64 * j;
+        w[j] = (i < count && i < n_valid) ? src[i] : 0u;
+    }
+}
+
+// the lane's 8 fields of one k-step: the 64 bits from bit r0 of record word w0 hold them all; each
+// comes out as its row index width·256 + value of the [width][256] codebook tables
+__device__ __forceinline__ void fields8(const uint32_t* rec, const uint4& fd, uint32_t (&ix)[8]) {
+    const uint32_t* w = rec + (fd.x & 0xffu);
+    const uint32_t r0 = fd.x >> 8;
+    const uint32_t d0 = w[0], d1 = w[1], d2 = w[2];
+    const uint64_t win = ((uint64_t)__builtin_amdgcn_alignbit(d2, d1, r0) << 32) | __builtin_amdgcn_alignbit(d1, d0, r0);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const uint32_t pos = i == 0 ? 0u : __builtin_amdgcn_ubfe(i <= 4 ? fd.y : fd.z, 8 * ((i - 1) & 3), 8);
+        const uint32_t wid = __builtin_amdgcn_ubfe(fd.w, 4 * i, 4);
+        ix[i] = (wid << 8) | __builtin_amdgcn_ubfe((uint32_t)(win >> pos), 0, wid);
+    }
 }
 
 int blocks_per_cu(const void* k, int threads, size_t lds) {
@@ -101,25 +134,27 @@ __global__ __launch_bounds__(kEncThreads, 1) void sq_encode_kernel(SqEncodeArgs 
     const int RW = a.t.rec_words;
     u32x4* Bt = reinterpret_cast<u32x4*>(smem);                                 // [part][t][s][lane]
     uint2* grid = reinterpret_cast<uint2*>(smem + (size_t)2 * T * S * 1024);
+    // per wave: 16 records and one pad word (the second word of a group at the end of the last record)
+    const int WS = 16 * RW + 1;
     uint32_t* stage = reinterpret_cast<uint32_t*>(smem + (size_t)2 * T * S * 1024 +
                                                   (size_t)((a.t.lds_grid_words + 3) / 4) * 16) +
-                      wave * 16 * RW;
+                      wave * WS;
     {
         const u32x4* src = reinterpret_cast<const u32x4*>(a.t.enc_b) + (size_t)head * 2 * T * S * 64;
         for (int i = threadIdx.x; i < 2 * T * S * 64; i += kEncThreads) Bt[i] = src[i];
         uint32_t* gw = reinterpret_cast<uint32_t*>(grid);
         for (int i = threadIdx.x; i < a.t.lds_grid_words; i += kEncThreads) gw[i] = a.t.grids[i];
-        for (int i = lane; i < 16 * RW; i += 64) stage[i] = 0u;
+        for (int i = lane; i < WS; i += 64) stage[i] = 0u;
     }
-    float mul[T], add[T], cmax[T];
-    uint32_t meta[T];
+    float mul[T], add[T];
+    uint32_t meta[T], meta2[T];
 #pragma unroll
     for (int t = 0; t < T; ++t) {
         const float4 dsc = a.t.enc_desc[(size_t)head * D + 16 * t + n];
         mul[t] = dsc.x;
         add[t] = dsc.y;
         meta[t] = f2u(dsc.z);
-        cmax[t] = dsc.w;
+        meta2[t] = f2u(dsc.w);
     }
     __syncthreads();
 
@@ -150,14 +185,14 @@ __global__ __launch_bounds__(kEncThreads, 1) void sq_encode_kernel(SqEncodeArgs 
         int sc[NG];
 #pragma unroll
         for (int q = 0; q < NG; ++q) {
-            uint32_t e2 = 0u;
+            // magnitudes as unsigned 16-bit pairs (monotone in |x|), maximum per half, then per lane
+            u16x2 m2 = {0, 0};
 #pragma unroll
             for (int s = 0; s < S; ++s)
 #pragma unroll
-                for (int w = 0; w < 4; ++w) {
-                    const uint32_t v = raw[q][s][w] & 0x7f807f80u;
-                    e2 = max(e2, max(v & 0xffffu, v >> 16));
-                }
+                for (int w = 0; w < 4; ++w)
+                    m2 = __builtin_elementwise_max(m2, __builtin_bit_cast(u16x2, raw[q][s][w] & 0x7fff7fffu));
+            uint32_t e2 = (uint32_t)max(m2[0], m2[1]) & 0x7f80u;
             uint32_t ea = e2, eb = e2;
             xswap16u(ea, eb);
             e2 = max(ea, eb);
@@ -180,11 +215,13 @@ __global__ __launch_bounds__(kEncThreads, 1) void sq_encode_kernel(SqEncodeArgs 
 
         floatx4 acc[NG][T];
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
+        for (int q = 0; q < NG; ++q)
 #pragma unroll
-            for (int q = 0; q < NG; ++q) acc[q][t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+            for (int t = 0; t < T; ++t) acc[q][t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-            for (int s = 0; s < S; ++s) {
+        for (int s = 0; s < S; ++s)
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
                 const half8 bh = as_half8(Bt[(t * S + s) * 64 + lane]);
                 const half8 bl = as_half8(Bt[((T + t) * S + s) * 64 + lane]);
 #pragma unroll
@@ -193,7 +230,6 @@ __global__ __launch_bounds__(kEncThreads, 1) void sq_encode_kernel(SqEncodeArgs 
                     acc[q][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[q][s], bl, acc[q][t], 0, 0, 0);
                 }
             }
-        }
 
 #pragma unroll
         for (int q = 0; q < NG; ++q) {
@@ -204,19 +240,30 @@ __global__ __launch_bounds__(kEncThreads, 1) void sq_encode_kernel(SqEncodeArgs 
             for (int r = 0; r < 4; ++r) scr[r] = __shfl(sc[q], 4 * g + r);
 #pragma unroll
             for (int t = 0; t < T; ++t) {
-                const uint32_t off = (meta[t] >> 16) & 0x3ffu, wid = meta[t] >> 26, goff = meta[t] & 0xffffu;
-                const uint32_t wi = off >> 5, sh = off & 31u;
+                const uint32_t goff = meta[t] & 0xffffu, qrel = meta2[t] & 0xffu;
+                uint32_t val[4];
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const float z = __builtin_amdgcn_ldexpf(acc[q][t][r], -scr[r]);
                     const float ug = fmaf(z, mul[t], add[t]);
-                    const int cell = (int)fminf(fmaxf(ug, 0.0f), cmax[t]);
+                    const int cell = (int)__builtin_amdgcn_fmed3f(ug, 0.0f, 2.0f * add[t]);
                     const uint2 e = grid[goff + cell];
-                    const uint32_t idx = e.y + (ug >= u2f(e.x) ? 1u : 0u);
-                    uint32_t* rec = stage + (4 * g + r) * RW;
-                    atomicOr(rec + wi, idx << sh);
-                    if (sh + wid > 32u) atomicOr(rec + wi + 1, idx >> (32u - sh));
+                    // the 4 neighbouring dimensions 4q..4q+3 (the lanes of one quad) OR-ed together
+                    val[r] = quad_or((e.y + (ug >= u2f(e.x) ? 1u : 0u)) << qrel);
                 }
+                // the quad's first lane ORs the group's bits into its record (two words; the second
+                // is zero unless the group straddles them)
+                if ((lane & 3) == 0) {
+                    const uint32_t off = (meta[t] >> 16) & 0x3ffu, wi = off >> 5, sh = off & 31u;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const uint64_t v64 = (uint64_t)val[r] << sh;
+                        uint32_t* rec = stage + (4 * g + r) * RW + wi;
+                        atomicOr(rec, (uint32_t)v64);
+                        atomicOr(rec + 1, (uint32_t)(v64 >> 32));
+                    }
+                }
+
             }
             // the wave's 16 records, written out linearly and the staging cleared
             const int64_t valid = min((int64_t)16, a.n_tokens - tq_ * 16);
@@ -235,7 +282,7 @@ static hipError_t launch_enc(const SqEncodeArgs& a, int num_cus, hipStream_t s) 
     constexpr int NG = 2;
     SqEncodeArgs b = a;
     const size_t lds = (size_t)2 * (D / 16) * (D / 32) * 1024 + (size_t)((a.t.lds_grid_words + 3) / 4) * 16 +
-                       (size_t)(kEncThreads / 64) * 16 * a.t.rec_words * 4;
+                       (size_t)(kEncThreads / 64) * (16 * a.t.rec_words + 1) * 4;
     if (lds > kLdsMax) return hipErrorInvalidValue;
     const void* kern = reinterpret_cast<const void*>(&sq_encode_kernel<D, NG>);
     if (lds > 65536) {
@@ -256,6 +303,7 @@ hipError_t launch_sq_encode(const SqEncodeArgs& a, int num_cus, hipStream_t s) {
 // decode
 // ---------------------------------------------------------------------------------------------
 constexpr int kDecThreads = 512;
+constexpr int kCbRows = 9;   // codebook rows of widths 0..8
 
 template <int D, bool BF, int NG>
 __global__ __launch_bounds__(kDecThreads, 1) void sq_decode_kernel(SqDecodeArgs a) {
@@ -266,14 +314,15 @@ __global__ __launch_bounds__(kDecThreads, 1) void sq_decode_kernel(SqDecodeArgs 
     const int64_t st = blockIdx.x / a.blocks_per_stream, blk = blockIdx.x % a.blocks_per_stream;
     const int head = (int)(st % a.t.n_heads);
     const int RW = a.t.rec_words, RWS = 16 * RW + 4;    // +4: a window may run past the last record
-    u32x4* At = reinterpret_cast<u32x4*>(smem);                                  // [part][t][s][lane]
-    uint32_t* cb = reinterpret_cast<uint32_t*>(smem + (size_t)2 * T * S * 1024);  // 510 (hi, lo) pairs
-    uint32_t* stage = cb + 512 + wave * NG * RWS;
+    uint32_t* cb = reinterpret_cast<uint32_t*>(smem);                            // [width][256] (hi, lo)
+    u32x4* At = reinterpret_cast<u32x4*>(smem + kCbRows * 256 * 4);              // [part][t][s][lane]
+    uint32_t* stage = reinterpret_cast<uint32_t*>(smem + kCbRows * 256 * 4 + (size_t)2 * T * S * 1024) +
+                      wave * NG * RWS;
     {
         const u32x4* src = reinterpret_cast<const u32x4*>(a.t.dec_a) + (size_t)head * 2 * T * S * 64;
         for (int i = threadIdx.x; i < 2 * T * S * 64; i += kDecThreads) At[i] = src[i];
         const uint32_t* c = reinterpret_cast<const uint32_t*>(a.t.cb_hl);
-        for (int i = threadIdx.x; i < 510; i += kDecThreads) cb[i] = c[i];
+        for (int i = threadIdx.x; i < kCbRows * 256; i += kDecThreads) cb[i] = c[i];
         for (int i = lane; i < NG * RWS; i += 64) stage[i] = 0u;
     }
     uint4 fd[S];
@@ -286,70 +335,75 @@ __global__ __launch_bounds__(kDecThreads, 1) void sq_decode_kernel(SqDecodeArgs 
     const int64_t t_end = min(t_begin + a.tiles_per_block, a.tiles_per_stream);
     const uint32_t* is = a.in + (size_t)st * a.n_tokens * RW;
 
-    for (int64_t tile = t_begin + (int64_t)wave * NG; tile < t_end; tile += (int64_t)nwaves * NG) {
-        // the NG tiles' records into LDS
+    // records of the next NG tiles are fetched into registers one iteration ahead
+    constexpr int NP = (16 * (D / 4) + 63) / 64;        // words per tile: 16 records of at most D/4 words
+    uint32_t pre[NG][NP];
+    auto fetch = [&](int64_t tile0) {
 #pragma unroll
         for (int q = 0; q < NG; ++q) {
-            const int64_t tq_ = tile + q;
-            const int64_t valid = tq_ < t_end ? min((int64_t)16, a.n_tokens - tq_ * 16) : 0;
-            const uint32_t* src = is + (size_t)tq_ * 16 * RW;
-            for (int i = lane; i < 16 * RW; i += 64) stage[q * RWS + i] = i < valid * RW ? src[i] : 0u;
+            const int64_t tq_ = tile0 + q;
+            const int valid = tq_ < t_end ? (int)min((int64_t)16, a.n_tokens - tq_ * 16) : 0;
+            fetch_words<NP>(is + (size_t)tq_ * 16 * RW, 16 * RW, valid * RW, lane, pre[q]);
         }
-        half8 Bh[NG][S], Bl[NG][S];
+    };
+    fetch(t_begin + (int64_t)wave * NG);
+    for (int64_t tile = t_begin + (int64_t)wave * NG; tile < t_end; tile += (int64_t)nwaves * NG) {
 #pragma unroll
         for (int q = 0; q < NG; ++q)
 #pragma unroll
-            for (int s = 0; s < S; ++s) {
-                const uint32_t* w = stage + q * RWS + v * RW + fd[s].x;
-                const uint32_t d0 = w[0], d1 = w[1], d2 = w[2], d3 = w[3];
+            for (int j = 0; j < NP; ++j)
+                if (lane + 64 * j < 16 * RW) stage[q * RWS + lane + 64 * j] = pre[q][j];
+        fetch(tile + (int64_t)nwaves * NG);
+        // k-step outer: the step's fields become the B operands of both tiles, and every A tile read
+        // from LDS feeds NG x 3 independent products
+        floatx4 acc[NG][T];
+#pragma unroll
+        for (int q = 0; q < NG; ++q)
+#pragma unroll
+            for (int t = 0; t < T; ++t) acc[q][t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int s = 0; s < S; ++s) {
+            half8 Bh[NG], Bl[NG];
+#pragma unroll
+            for (int q = 0; q < NG; ++q) {
+                uint32_t ix[8];
+                fields8(stage + q * RWS + v * RW, fd[s], ix);
                 u32x4 hv, lv;
 #pragma unroll
                 for (int i = 0; i < 8; i += 2) {
-                    uint32_t pr[2];
-#pragma unroll
-                    for (int k = 0; k < 2; ++k) {
-                        const int ii = i + k;
-                        const uint32_t rel = ((ii < 4 ? fd[s].y : fd[s].z) >> (8 * (ii & 3))) & 0xffu;
-                        const uint32_t wid = (fd[s].w >> (4 * ii)) & 0xfu;
-                        const uint32_t f = window_field(d0, d1, d2, d3, rel, wid);
-                        pr[k] = cb[(1u << wid) - 2u + f];
-                    }
-                    hv[i / 2] = (pr[0] & 0xffffu) | (pr[1] << 16);
-                    lv[i / 2] = (pr[0] >> 16) | (pr[1] & 0xffff0000u);
+                    const uint32_t p0 = cb[ix[i]], p1 = cb[ix[i + 1]];
+                    hv[i / 2] = (p0 & 0xffffu) | (p1 << 16);
+                    lv[i / 2] = (p0 >> 16) | (p1 & 0xffff0000u);
                 }
-                Bh[q][s] = as_half8(hv);
-                Bl[q][s] = as_half8(lv);
+                Bh[q] = as_half8(hv);
+                Bl[q] = as_half8(lv);
             }
 #pragma unroll
-        for (int t = 0; t < T; ++t) {
-            floatx4 acc[NG];
-#pragma unroll
-            for (int q = 0; q < NG; ++q) acc[q] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-            for (int s = 0; s < S; ++s) {
+            for (int t = 0; t < T; ++t) {
                 const half8 ah = as_half8(At[(t * S + s) * 64 + lane]);
                 const half8 al = as_half8(At[((T + t) * S + s) * 64 + lane]);
 #pragma unroll
                 for (int q = 0; q < NG; ++q) {
-                    acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, Bh[q][s], acc[q], 0, 0, 0);
-                    acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, Bl[q][s], acc[q], 0, 0, 0);
-                    acc[q] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, Bh[q][s], acc[q], 0, 0, 0);
+                    acc[q][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, Bh[q], acc[q][t], 0, 0, 0);
+                    acc[q][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, Bl[q], acc[q][t], 0, 0, 0);
+                    acc[q][t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, Bh[q], acc[q][t], 0, 0, 0);
                 }
             }
+        }
 #pragma unroll
-            for (int q = 0; q < NG; ++q) {
-                const int64_t tok = (tile + q) * 16 + v;
-                if (tile + q >= t_end || tok >= a.n_tokens) continue;
-                const size_t o = ((size_t)st * a.n_tokens + tok) * D + 16 * t + 4 * g;
+        for (int q = 0; q < NG; ++q) {
+            const int64_t tok = (tile + q) * 16 + v;
+            if (tile + q >= t_end || tok >= a.n_tokens) continue;
+            const size_t o = ((size_t)st * a.n_tokens + tok) * D + 4 * g;
+#pragma unroll
+            for (int t = 0; t < T; ++t) {
                 if constexpr (BF) {
-                    uint32_t w0 = (f2u(acc[q][0] * scale) + 0x7fffu + ((f2u(acc[q][0] * scale) >> 16) & 1u)) >> 16;
-                    uint32_t w1 = (f2u(acc[q][1] * scale) + 0x7fffu + ((f2u(acc[q][1] * scale) >> 16) & 1u)) >> 16;
-                    uint32_t w2 = (f2u(acc[q][2] * scale) + 0x7fffu + ((f2u(acc[q][2] * scale) >> 16) & 1u)) >> 16;
-                    uint32_t w3 = (f2u(acc[q][3] * scale) + 0x7fffu + ((f2u(acc[q][3] * scale) >> 16) & 1u)) >> 16;
-                    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + o) = u32x2{w0 | (w1 << 16), w2 | (w3 << 16)};
+                    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + o + 16 * t) =
+                        u32x2{bf16_pair(acc[q][t][0] * scale, acc[q][t][1] * scale),
+                              bf16_pair(acc[q][t][2] * scale, acc[q][t][3] * scale)};
                 } else {
-                    *reinterpret_cast<floatx4*>(static_cast<float*>(a.out) + o) =
-                        floatx4{acc[q][0] * scale, acc[q][1] * scale, acc[q][2] * scale, acc[q][3] * scale};
+                    *reinterpret_cast<floatx4*>(static_cast<float*>(a.out) + o + 16 * t) =
+                        floatx4{acc[q][t][0] * scale, acc[q][t][1] * scale, acc[q][t][2] * scale, acc[q][t][3] * scale};
                 }
             }
         }
@@ -360,7 +414,7 @@ template <int D, bool BF>
 static hipError_t launch_dec(const SqDecodeArgs& a, int num_cus, hipStream_t s) {
     constexpr int NG = 2;
     SqDecodeArgs b = a;
-    const size_t lds = (size_t)2 * (D / 16) * (D / 32) * 1024 + 512 * 4 +
+    const size_t lds = (size_t)kCbRows * 256 * 4 + (size_t)2 * (D / 16) * (D / 32) * 1024 +
                        (size_t)(kDecThreads / 64) * NG * (16 * a.t.rec_words + 4) * 4;
     if (lds > kLdsMax) return hipErrorInvalidValue;
     const void* kern = reinterpret_cast<const void*>(&sq_decode_kernel<D, BF, NG>);
@@ -425,16 +479,16 @@ __global__ __launch_bounds__(kScThreads) void sq_scores_kernel(SqScoresArgs a) {
     const int head = (int)(st % a.t.n_heads);
     const int RW = a.t.rec_words, RWS = 16 * RW + 4;
     const int nqt = (int)(a.nq_pad / 16);
-    _Float16* qp = reinterpret_cast<_Float16*>(smem);
-    float* qsc = reinterpret_cast<float*>(smem + (size_t)a.nq_pad * QROW * 2);
-    uint16_t* cb = reinterpret_cast<uint16_t*>(qsc + a.nq_pad);
-    uint32_t* stage = reinterpret_cast<uint32_t*>(cb + 512) + wave * RWS;
+    uint16_t* cb = reinterpret_cast<uint16_t*>(smem);                            // [width][256] fp16
+    _Float16* qp = reinterpret_cast<_Float16*>(smem + kCbRows * 256 * 2);
+    float* qsc = reinterpret_cast<float*>(smem + kCbRows * 256 * 2 + (size_t)a.nq_pad * QROW * 2);
+    uint32_t* stage = reinterpret_cast<uint32_t*>(qsc + a.nq_pad) + wave * RWS;
     {
         const _Float16* src = a.qp + (size_t)st * a.nq_pad * D;
         for (int i = threadIdx.x; i < a.nq_pad * D; i += kScThreads) qp[(i / D) * QROW + i % D] = src[i];
         for (int i = threadIdx.x; i < a.nq_pad; i += kScThreads) qsc[i] = a.qscale[(size_t)st * a.nq_pad + i];
         const uint16_t* c = reinterpret_cast<const uint16_t*>(a.t.cb_h);
-        for (int i = threadIdx.x; i < 510; i += kScThreads) cb[i] = c[i];
+        for (int i = threadIdx.x; i < kCbRows * 256; i += kScThreads) cb[i] = c[i];
         for (int i = lane; i < RWS; i += 64) stage[i] = 0u;
     }
     uint4 fd[S];
@@ -446,28 +500,26 @@ __global__ __launch_bounds__(kScThreads) void sq_scores_kernel(SqScoresArgs a) {
     const int64_t t_end = min(t_begin + a.tiles_per_block, a.tiles_per_stream);
     const uint32_t* is = a.in + (size_t)st * a.n_tokens * RW;
     float* out = a.scores + (size_t)st * a.n_q * a.n_tokens;
+    constexpr int NP = (16 * (D / 4) + 63) / 64;
+    uint32_t pre[NP];
+    auto fetch = [&](int64_t tile) {
+        const int valid = tile < t_end ? (int)min((int64_t)16, a.n_tokens - tile * 16) : 0;
+        fetch_words<NP>(is + (size_t)tile * 16 * RW, 16 * RW, valid * RW, lane, pre);
+    };
+    fetch(t_begin + wave);
     for (int64_t tile = t_begin + wave; tile < t_end; tile += nwaves) {
-        const int64_t valid = min((int64_t)16, a.n_tokens - tile * 16);
-        const uint32_t* src = is + (size_t)tile * 16 * RW;
-        for (int i = lane; i < 16 * RW; i += 64) stage[i] = i < valid * RW ? src[i] : 0u;
+#pragma unroll
+        for (int j = 0; j < NP; ++j)
+            if (lane + 64 * j < 16 * RW) stage[lane + 64 * j] = pre[j];
+        fetch(tile + nwaves);
         half8 B[S];
 #pragma unroll
         for (int s = 0; s < S; ++s) {
-            const uint32_t* w = stage + v * RW + fd[s].x;
-            const uint32_t d0 = w[0], d1 = w[1], d2 = w[2], d3 = w[3];
+            uint32_t ix[8];
+            fields8(stage + v * RW, fd[s], ix);
             u32x4 hv;
 #pragma unroll
-            for (int i = 0; i < 8; i += 2) {
-                uint32_t pr[2];
-#pragma unroll
-                for (int k = 0; k < 2; ++k) {
-                    const int ii = i + k;
-                    const uint32_t rel = ((ii < 4 ? fd[s].y : fd[s].z) >> (8 * (ii & 3))) & 0xffu;
-                    const uint32_t wid = (fd[s].w >> (4 * ii)) & 0xfu;
-                    pr[k] = cb[(1u << wid) - 2u + window_field(d0, d1, d2, d3, rel, wid)];
-                }
-                hv[i / 2] = pr[0] | (pr[1] << 16);
-            }
+            for (int i = 0; i < 8; i += 2) hv[i / 2] = (uint32_t)cb[ix[i]] | ((uint32_t)cb[ix[i + 1]] << 16);
             B[s] = as_half8(hv);
         }
         const int64_t tok = tile * 16 + v;
@@ -496,7 +548,7 @@ hipError_t launch_sq_scores(const SqScoresArgs& a, int num_cus, hipStream_t s) {
     else hipLaunchKernelGGL((sq_qprep_kernel<128>), dim3(rows), dim3(128), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const size_t lds = (size_t)a.nq_pad * (a.t.d + 8) * 2 + (size_t)a.nq_pad * 4 + 512 * 2 +
+    const size_t lds = (size_t)kCbRows * 256 * 2 + (size_t)a.nq_pad * (a.t.d + 8) * 2 + (size_t)a.nq_pad * 4 +
                        (size_t)(kScThreads / 64) * (16 * a.t.rec_words + 4) * 4;
     if (lds > kLdsMax) return hipErrorInvalidValue;
     const void* kern = a.t.d == 64 ? reinterpret_cast<const void*>(&sq_scores_kernel<64>)

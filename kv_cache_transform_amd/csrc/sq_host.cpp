@@ -318,12 +318,12 @@ int tq_sq_create(const tq_sq_params* p, const double* basis, const double* lambd
         gG[w] = g.G;
         grids.insert(grids.end(), g.entries.begin(), g.entries.end());
     }
-    // codebooks of every width, concatenated at 2^w - 2
-    std::vector<uint16_t> cb_hl(2 * 510), cb_h(510);
+    // codebooks of every width w at rows w·256 (row 0 unused): (hi, lo) of c·2^12 and fp16 c
+    std::vector<uint16_t> cb_hl(2 * 256 * (kBMax + 1), 0), cb_h(256 * (kBMax + 1), 0);
     for (int w = 1; w <= kBMax; ++w) {
         const GaussBook& gb = gauss_book(w);
         for (int i = 0; i < (1 << w); ++i) {
-            const int e = (1 << w) - 2 + i;
+            const int e = w * 256 + i;
             split_f16(gb.cent[i] * 4096.0, &cb_hl[2 * e], &cb_hl[2 * e + 1]);
             cb_h[e] = f64_to_f16_bits(gb.cent[i]);
         }
@@ -364,15 +364,18 @@ int tq_sq_create(const tq_sq_params* p, const double* basis, const double* lambd
                         enc_b[base] = hi;
                         enc_b[base + (size_t)T * S * 512] = lo;
                     }
-        // encode per-dimension descriptor: u_grid = (acc · 2^-sc) · mul + add, acc = 2^(8+sc) z
+        // encode per-dimension descriptor: u_grid = (acc · 2^-sc) · mul + add with acc = 2^(8+sc) z
+        // and add = G/2 + 1 (cells clamp to [0, 2·add]); meta = grid offset | bit offset << 16 |
+        // width << 26; meta2 = the field's bit position within its group of 4 dimensions 4q..4q+3
         for (int k = 0; k < d; ++k) {
-            const int w = bh[k], G = gG[w];
+            const int w = bh[k], G = gG[w], kq = k & ~3;
             float* o = &desc[((size_t)h * d + k) * 4];
             o[0] = (float)(std::ldexp(1.0, -8) * (G / (2.0 * kSqRange)) / sg[k]);
             o[1] = (float)(0.5 * G + 1.0);
             const uint32_t meta = (uint32_t)goff[w] | ((uint32_t)off[k] << 16) | ((uint32_t)w << 26);
+            const uint32_t meta2 = (uint32_t)(off[k] - off[kq]);
             std::memcpy(&o[2], &meta, 4);
-            o[3] = (float)(G + 2);
+            std::memcpy(&o[3], &meta2, 4);
         }
         // decode A operand: A[m = lane % 16][kk = 8 g + i] of (tile t, kstep s) = U[16 t + m][32 s + 8 g + i] σ · 2^e
         double mx = 0.0;
@@ -391,20 +394,23 @@ int tq_sq_create(const tq_sq_params* p, const double* basis, const double* lambd
                         dec_a[base] = hi;
                         dec_a[base + (size_t)T * S * 512] = lo;
                     }
-        // field extraction of the 8 fields k = 32 s + 8 g + i
+        // field extraction of the 8 fields k = 32 s + 8 g + i: they lie in the 64 bits from bit
+        // off[k0] = 32 w0 + r0 of the record; {w0 | r0 << 8, positions of fields 1..4 and 5..7
+        // within those 64 bits (8 bits each), widths (4 bits each)}
         for (int s = 0; s < S; ++s)
             for (int g = 0; g < 4; ++g) {
-                const int k0 = 32 * s + 8 * g, w0 = off[k0] >> 5;
-                uint32_t r03 = 0, r47 = 0, wid = 0;
+                const int k0 = 32 * s + 8 * g, w0 = off[k0] >> 5, r0 = off[k0] & 31;
+                uint32_t p14 = 0, p57 = 0, wid = 0;
                 for (int i = 0; i < 8; ++i) {
-                    const uint32_t rel = (uint32_t)(off[k0 + i] - 32 * w0);
-                    if (i < 4) r03 |= rel << (8 * i); else r47 |= rel << (8 * (i - 4));
+                    const uint32_t pos = (uint32_t)(off[k0 + i] - off[k0]);
+                    if (i >= 1 && i <= 4) p14 |= pos << (8 * (i - 1));
+                    if (i >= 5) p57 |= pos << (8 * (i - 5));
                     wid |= (uint32_t)bh[k0 + i] << (4 * i);
                 }
                 uint32_t* f = &fields[(((size_t)h * S + s) * 4 + g) * 4];
-                f[0] = (uint32_t)w0;
-                f[1] = r03;
-                f[2] = r47;
+                f[0] = (uint32_t)w0 | ((uint32_t)r0 << 8);
+                f[1] = p14;
+                f[2] = p57;
                 f[3] = wid;
             }
     }

@@ -22,10 +22,11 @@ struct SqDev {
     // decode: (U diag(σ))·2^e_h as fp16 hi, lo in MFMA A-operand order [head][part][tile][kstep][lane][8]
     const _Float16* dec_a = nullptr;
     const float* dec_scale = nullptr;  // [head] 2^-(e_h + 12)
-    // field extraction per (head, kstep, lane part g): {first dword, rel offsets 0..3, rel 4..7, widths}
+    // field extraction per (head, kstep, lane part g): {first word | bit << 8, positions 1..4,
+    // positions 5..7, widths}
     const uint4* fields = nullptr;
-    const _Float16* cb_hl = nullptr;   // codebook of width w at 2^w - 2: (hi, lo) of c·2^12, 2 halves each
-    const _Float16* cb_h = nullptr;    // same indexing, fp16 c
+    const _Float16* cb_hl = nullptr;   // [width 0..8][256] (hi, lo) of c·2^12, 2 halves each
+    const _Float16* cb_h = nullptr;    // [width 0..8][256] fp16 c
     const float* U32 = nullptr;        // [head][j][k] fp32
     const float* sigma = nullptr;      // [head][k]
     int lds_grid_words = 0;            // total words of `grids`
