@@ -95,6 +95,27 @@ int tq_sq_qk_scores(const tq_sq_codec* codec, const void* q, tq_dtype q_dtype, i
                     const void* packed_k, int64_t n_streams, int64_t n_tokens, float* scores,
                     void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace for tq_sq_decode_attention (projected queries and split-K partials); a function of
+ * the arguments only. */
+size_t tq_sq_attention_workspace_bytes(const tq_sq_codec* ck, int32_t batch, int32_t n_q_heads,
+                                       int32_t n_kv_heads, int64_t n_tokens);
+
+/* One decode step of GQA attention over SpectralQuant caches ("Ablation...", §2 eq. (1) with the
+ * SpectralQuant score <U_Kᵀq, ẑ_K> and values x̂_V = U_V ẑ_V):
+ *   out[b][h] = Σ_t softmax_t(<U_Kᵀq[b][h], ẑ_K,t> · scale) · x̂_V,t,   scale = softmax_scale or 1/sqrt(d)
+ * kv head = h / (n_q_heads/n_kv_heads); stream = b·n_kv_heads + kv head for both packed tensors (laid
+ * out for n_tokens per stream); the weights are applied to ẑ_V in the V basis and U_V is applied once
+ * per output row.  lengths: NULL, or a device pointer to `batch` int32 values (4-byte aligned)
+ * clamped to [0, n_tokens]: element b attends to its first lengths[b] tokens, and a length of 0 gives
+ * zero outputs.  q: [batch][n_q_heads][d] F32 or BF16; out: same shape, F32 or BF16.  ck and cv must
+ * have n_heads == n_kv_heads and equal d; n_q_heads / n_kv_heads <= 16.  Products on fp16 MFMA with
+ * fp32 accumulation (relative error ~1e-3). */
+int tq_sq_decode_attention(const tq_sq_codec* ck, const tq_sq_codec* cv, const void* q, tq_dtype q_dtype,
+                           int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, const void* packed_k,
+                           const void* packed_v, int64_t n_tokens, const int32_t* lengths,
+                           float softmax_scale, void* out, tq_dtype out_dtype, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
 /* Host copies of the b-bit Lloyd-Max codebook of a unit Gaussian the kernels use (no GPU call):
  * thresholds[2^b - 1] and centroids[2^b] ascending, fp64; either may be NULL.  TQ_EINVAL unless
  * 1 <= b <= 8. */

@@ -22,7 +22,8 @@ EXPORTS = ("tq_get_layout", "tq_encode", "tq_encode_append", "tq_decode", "tq_de
            "tq_clear_cache")
 # every symbol include/tq_sq.h declares
 SQ_EXPORTS = ("tq_sq_calibrate", "tq_sq_create", "tq_sq_destroy", "tq_sq_record_bytes", "tq_sq_encode",
-              "tq_sq_decode", "tq_sq_scores_workspace_bytes", "tq_sq_qk_scores", "tq_sq_host_codebook")
+              "tq_sq_decode", "tq_sq_scores_workspace_bytes", "tq_sq_qk_scores", "tq_sq_attention_workspace_bytes",
+              "tq_sq_decode_attention", "tq_sq_host_codebook")
 
 
 class Params(ctypes.Structure):
@@ -86,6 +87,9 @@ def lib() -> ctypes.CDLL:
         "tq_sq_scores_workspace_bytes": (SZ, [VP, I64, I64]),
         "tq_sq_qk_scores": (ctypes.c_int, [VP, VP, ctypes.c_int, I64, VP, I64, I64, VP, VP, SZ, VP]),
         "tq_sq_host_codebook": (ctypes.c_int, [I32, VP, VP]),
+        "tq_sq_attention_workspace_bytes": (SZ, [VP, I32, I32, I32, I64]),
+        "tq_sq_decode_attention": (ctypes.c_int, [VP, VP, VP, ctypes.c_int, I32, I32, I32, VP, VP, I64, VP,
+                                                  ctypes.c_float, VP, ctypes.c_int, VP, SZ, VP]),
     }
     for name, (res, args) in sig.items():
         f = getattr(L, name)

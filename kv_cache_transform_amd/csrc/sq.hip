@@ -455,7 +455,7 @@ __global__ __launch_bounds__(D) void sq_qprep_kernel(SqScoresArgs a) {
     const float* U = a.t.U32 + (size_t)head * D * D;
     float acc = 0.0f;
     for (int j = 0; j < D; ++j) acc = fmaf(U[(size_t)j * D + k], qs[j], acc);
-    acc *= a.t.sigma[(size_t)head * D + k];
+    acc *= a.t.sigma[(size_t)head * D + k] * a.qmul;
     float m = fabsf(acc);
     for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
     if ((k & 63) == 0) red[k >> 6] = m;
@@ -541,12 +541,16 @@ __global__ __launch_bounds__(kScThreads) void sq_scores_kernel(SqScoresArgs a) {
     }
 }
 
-hipError_t launch_sq_scores(const SqScoresArgs& a, int num_cus, hipStream_t s) {
-    SqScoresArgs b = a;
+hipError_t launch_sq_qprep(const SqScoresArgs& a, hipStream_t s) {
     const unsigned rows = (unsigned)(a.n_streams * a.nq_pad);
     if (a.t.d == 64) hipLaunchKernelGGL((sq_qprep_kernel<64>), dim3(rows), dim3(64), 0, s, a);
     else hipLaunchKernelGGL((sq_qprep_kernel<128>), dim3(rows), dim3(128), 0, s, a);
-    hipError_t e = hipGetLastError();
+    return hipGetLastError();
+}
+
+hipError_t launch_sq_scores(const SqScoresArgs& a, int num_cus, hipStream_t s) {
+    SqScoresArgs b = a;
+    hipError_t e = launch_sq_qprep(a, s);
     if (e != hipSuccess) return e;
     const size_t lds = (size_t)kCbRows * 256 * 2 + (size_t)a.nq_pad * (a.t.d + 8) * 2 + (size_t)a.nq_pad * 4 +
                        (size_t)(kScThreads / 64) * (16 * a.t.rec_words + 4) * 4;
@@ -562,6 +566,214 @@ hipError_t launch_sq_scores(const SqScoresArgs& a, int num_cus, hipStream_t s) {
     if (a.t.d == 64) hipLaunchKernelGGL((sq_scores_kernel<64>), grid, dim3(kScThreads), lds, s, b);
     else hipLaunchKernelGGL((sq_scores_kernel<128>), grid, dim3(kScThreads), lds, s, b);
     return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------------------------
+// decode-attention
+// ---------------------------------------------------------------------------------------------
+// One wave per (stream, split) over 32-token chunks:
+//   scores  D[token][query] = Σ_k c_K[token][k] · q'[query][k]  (A = the keys' codebook values from
+//           their records, B = the projected queries, held in registers), already in base-2 units;
+//   softmax online per query (running max and sum, the partial output rescaled when the max rises);
+//   values  D[k][query] += Σ_t c_V[t][k] · p[t][query]: B = the weights exactly as the score product
+//           left them (lane (query, g) holds tokens 4g + r of both 16-token halves, which is the
+//           token order τ(g, i) used along the contraction), A = for dimension 16t + l%16 the value
+//           fields of those 8 tokens, each read at the dimension's fixed bit offset.
+// The partial outputs stay in the V basis without σ_V; the combine kernel merges the splits, then
+// applies σ_V and U_V once per output row.
+constexpr int kAttnThreads = 256;
+
+template <int D, int RWM>
+__global__ __launch_bounds__(kAttnThreads, 2) void sq_attn_kernel(SqAttnArgs a) {
+    constexpr int T = D / 16, S = D / 32;
+    constexpr int NP = (32 * RWM + 63) / 64;           // record words of a 32-token chunk per lane
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    uint16_t* cb = reinterpret_cast<uint16_t*>(smem);                              // [width][256] fp16
+    const int RWk = a.tk.rec_words, RWv = a.tv.rec_words;
+    const int WS = 32 * (RWk + RWv) + 4;
+    uint32_t* sk = reinterpret_cast<uint32_t*>(smem + kCbRows * 256 * 2) + wave * WS;
+    uint32_t* sv = sk + 32 * RWk + 2;
+    {
+        const uint16_t* c = reinterpret_cast<const uint16_t*>(a.tk.cb_h);
+        for (int i = threadIdx.x; i < kCbRows * 256; i += kAttnThreads) cb[i] = c[i];
+        for (int i = lane; i < WS; i += 64) sk[i] = 0u;
+    }
+    __syncthreads();
+    const int64_t item = (int64_t)blockIdx.x * (kAttnThreads / 64) + wave;
+    if (item >= a.n_streams * a.n_split) return;
+    const int64_t st = item / a.n_split, sp = item % a.n_split;
+    const int hk = (int)(st % a.hkv);
+    int64_t len = a.n_tokens;
+    if (a.lens) len = min(max((int64_t)a.lens[st / a.hkv], (int64_t)0), a.n_tokens);
+    const int64_t t0 = sp * a.tps, t1 = min(t0 + a.tps, len);
+
+    half8 Bq[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s)
+        Bq[s] = *reinterpret_cast<const half8*>(a.qp + ((size_t)st * 16 + n) * D + 32 * s + 8 * g);
+    const float qs = a.qscale[st * 16 + n];
+    uint4 fk[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) fk[s] = a.tk.fields[((size_t)hk * S + s) * 4 + g];
+    uint32_t vm[T];   // value dimension 16t + n: bit offset << 16 | width << 26 (from its descriptor)
+#pragma unroll
+    for (int t = 0; t < T; ++t) vm[t] = f2u(a.tv.enc_desc[(size_t)hk * D + 16 * t + n].z);
+
+    const uint32_t* ks = a.kin + (size_t)st * a.n_tokens * RWk;
+    const uint32_t* vs = a.vin + (size_t)st * a.n_tokens * RWv;
+    uint32_t pk[NP], pv[NP];
+    auto fetch = [&](int64_t c0) {
+        const int valid = c0 < t1 ? (int)min((int64_t)32, a.n_tokens - c0) : 0;
+        fetch_words<NP>(ks + (size_t)c0 * RWk, 32 * RWk, valid * RWk, lane, pk);
+        fetch_words<NP>(vs + (size_t)c0 * RWv, 32 * RWv, valid * RWv, lane, pv);
+    };
+    float m = -INFINITY, l = 0.0f;
+    floatx4 acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    fetch(t0);
+    for (int64_t c0 = t0; c0 < t1; c0 += 32) {
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+            if (lane + 64 * j < 32 * RWk) sk[lane + 64 * j] = pk[j];
+            if (lane + 64 * j < 32 * RWv) sv[lane + 64 * j] = pv[j];
+        }
+        fetch(c0 + 32);
+        // scores of the two 16-token halves (the field descriptors pass through an empty asm each
+        // chunk so that their decoded positions and widths are not kept live across the loop)
+#pragma unroll
+        for (int s = 0; s < S; ++s) asm volatile("" : "+v"(fk[s].x), "+v"(fk[s].y), "+v"(fk[s].z), "+v"(fk[s].w));
+        float sc[2][4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            floatx4 d4 = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                uint32_t ix[8];
+                fields8(sk + (16 * h + n) * RWk, fk[s], ix);
+                u32x4 hv;
+#pragma unroll
+                for (int i = 0; i < 8; i += 2) hv[i / 2] = (uint32_t)cb[ix[i]] | ((uint32_t)cb[ix[i + 1]] << 16);
+                d4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(hv), Bq[s], d4, 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                sc[h][r] = (c0 + 16 * h + 4 * g + r < t1) ? d4[r] * qs : -INFINITY;
+        }
+        // online softmax for query n (its 32 scores live on lanes n, n+16, n+32, n+48)
+        float cm = sc[0][0];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) cm = fmaxf(cm, sc[h][r]);
+        float x0 = cm, x1 = cm;
+        xswap16(x0, x1);
+        cm = fmaxf(x0, x1);
+        x0 = cm;
+        x1 = cm;
+        xswap32(x0, x1);
+        cm = fmaxf(x0, x1);
+        const float mn = fmaxf(m, cm);
+        const float alpha = mn == -INFINITY ? 1.0f : exp2f(m - mn);
+        float p[2][4], ps = 0.0f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                p[h][r] = mn == -INFINITY ? 0.0f : exp2f(sc[h][r] - mn);
+                ps += p[h][r];
+            }
+        l = l * alpha + sum4(ps);
+        m = mn;
+#pragma unroll
+        for (int t = 0; t < T; ++t) acc[t] *= alpha;
+        const half8 P = half8{(_Float16)p[0][0], (_Float16)p[0][1], (_Float16)p[0][2], (_Float16)p[0][3],
+                              (_Float16)p[1][0], (_Float16)p[1][1], (_Float16)p[1][2], (_Float16)p[1][3]};
+        // values: dimension 16t + n of the tokens τ(g, i) = 4g + i (i < 4), 16 + 4g + i - 4 (i >= 4).
+        // The word index goes through an empty asm each chunk so that its 8·T per-token forms are
+        // not kept live across the loop.
+        int zo = 0;
+        asm volatile("" : "+v"(zo));
+#pragma unroll
+        for (int t = 0; t < T; ++t) asm volatile("" : "+v"(vm[t]));
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const uint32_t off = (vm[t] >> 16) & 0x3ffu, wid = vm[t] >> 26;
+            const uint32_t wi = off >> 5, sh = off & 31u, hi = wid << 8;
+            u32x4 av;
+#pragma unroll
+            for (int i = 0; i < 8; i += 2) {
+                uint32_t c2[2];
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const int ii = i + k, tok = ii < 4 ? 4 * g + ii : 16 + 4 * g + ii - 4;
+                    const uint32_t* w = sv + (zo + tok * RWv + (int)wi);
+                    c2[k] = cb[hi | __builtin_amdgcn_ubfe(__builtin_amdgcn_alignbit(w[1], w[0], sh), 0, wid)];
+                }
+                av[i / 2] = c2[0] | (c2[1] << 16);
+            }
+            acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(av), P, acc[t], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);   // keep each dimension tile's reads next to its product
+        }
+    }
+    float* pp = a.part + ((size_t)item * 16 + n) * D;
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+        *reinterpret_cast<floatx4*>(pp + 16 * t + 4 * g) = acc[t];
+    if (g == 0) *reinterpret_cast<float2*>(a.ml + ((size_t)item * 16 + n) * 2) = float2{m, l};
+}
+
+// one block of D threads per output row (b, h): merge the splits, scale by σ_V, rotate by U_V
+template <int D>
+__global__ __launch_bounds__(D) void sq_attn_combine_kernel(SqAttnArgs a) {
+    __shared__ float y[D];
+    const int k = threadIdx.x;
+    const int64_t row = blockIdx.x, b = row / a.hq, h = row % a.hq;
+    const int64_t hk = h / a.g, qi = h % a.g, st = b * a.hkv + hk;
+    float M = -INFINITY;
+    for (int64_t sp = 0; sp < a.n_split; ++sp) M = fmaxf(M, a.ml[((st * a.n_split + sp) * 16 + qi) * 2]);
+    float L = 0.0f, acc = 0.0f;
+    if (M != -INFINITY) {
+        for (int64_t sp = 0; sp < a.n_split; ++sp) {
+            const size_t r = (size_t)(st * a.n_split + sp) * 16 + qi;
+            const float w = exp2f(a.ml[r * 2] - M);
+            L += a.ml[r * 2 + 1] * w;
+            acc += a.part[r * D + k] * w;
+        }
+        acc = acc / L * a.tv.sigma[(size_t)hk * D + k];
+    }
+    y[k] = acc;
+    __syncthreads();
+    const float* U = a.tv.U32 + ((size_t)hk * D + k) * D;
+    float o = 0.0f;
+    for (int j = 0; j < D; ++j) o = fmaf(U[j], y[j], o);
+    const size_t oi = (size_t)row * D + k;
+    if (a.out_bf16) static_cast<__bf16*>(a.out)[oi] = (__bf16)o;
+    else static_cast<float*>(a.out)[oi] = o;
+}
+
+template <int D, int RWM>
+static hipError_t launch_attn(const SqAttnArgs& a, hipStream_t s) {
+    const size_t lds = (size_t)kCbRows * 256 * 2 +
+                       (size_t)(kAttnThreads / 64) * (32 * (a.tk.rec_words + a.tv.rec_words) + 4) * 4;
+    const unsigned blocks = (unsigned)((a.n_streams * a.n_split + kAttnThreads / 64 - 1) / (kAttnThreads / 64));
+    hipLaunchKernelGGL((sq_attn_kernel<D, RWM>), dim3(blocks), dim3(kAttnThreads), lds, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const unsigned rows = (unsigned)(a.n_streams / a.hkv * a.hq);
+    hipLaunchKernelGGL((sq_attn_combine_kernel<D>), dim3(rows), dim3(D), 0, s, a);
+    return hipGetLastError();
+}
+
+// records of up to 16 words (at most 4 bits per dimension on average at d = 128) take the smaller
+// register prefetch
+hipError_t launch_sq_attention(const SqAttnArgs& a, hipStream_t s) {
+    const int rw = max(a.tk.rec_words, a.tv.rec_words);
+    if (a.tk.d == 64) return rw <= 8 ? launch_attn<64, 8>(a, s) : launch_attn<64, 16>(a, s);
+    return rw <= 16 ? launch_attn<128, 16>(a, s) : launch_attn<128, 32>(a, s);
 }
 
 }  // namespace tq

@@ -230,6 +230,26 @@ struct Blob {
     }
 };
 
+// attention split geometry, a function of the arguments only: about as many (stream, split) waves
+// as 256 CUs hold at eight per CU, splits of at least 256 tokens in multiples of 32, at most 1024
+struct SqAttnWs {
+    int64_t tps, n_split, o_qs, o_part, o_ml, total;
+};
+SqAttnWs sq_attn_ws(int d, int64_t streams, int64_t n_tokens) {
+    SqAttnWs w{};
+    int64_t ns = (256 * 8 + streams - 1) / (streams > 0 ? streams : 1);
+    ns = std::min(ns, (n_tokens + 255) / 256);
+    ns = std::max<int64_t>(std::min<int64_t>(ns, 1024), 1);
+    w.tps = std::max<int64_t>(((n_tokens + ns - 1) / ns + 31) / 32 * 32, 32);
+    w.n_split = std::max<int64_t>((n_tokens + w.tps - 1) / w.tps, 1);
+    auto al = [](int64_t x) { return (x + 255) / 256 * 256; };
+    w.o_qs = al(streams * 16 * d * 2);
+    w.o_part = w.o_qs + al(streams * 16 * 4);
+    w.o_ml = w.o_part + al(streams * w.n_split * 16 * d * 4);
+    w.total = w.o_ml + al(streams * w.n_split * 16 * 2 * 4);
+    return w;
+}
+
 void split_f16(double v, uint16_t* hi, uint16_t* lo) {
     *hi = f64_to_f16_bits(v);
     *lo = f64_to_f16_bits(v - (double)f16_bits_to_f32(*hi));
@@ -543,8 +563,74 @@ int tq_sq_qk_scores(const tq_sq_codec* codec, const void* q, tq_dtype q_dtype, i
     const int64_t qp = (n_streams * a.nq_pad * codec->dev.d * 2 + 255) / 256 * 256;
     a.qp = static_cast<_Float16*>(workspace);
     a.qscale = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + qp);
+    a.qmul = 1.0f;
     a.tiles_per_stream = (n_tokens + 15) / 16;
     return launch_sq_scores(a, codec->num_cus, static_cast<hipStream_t>(stream)) == hipSuccess ? TQ_OK : TQ_EHIP;
+}
+
+size_t tq_sq_attention_workspace_bytes(const tq_sq_codec* ck, int32_t batch, int32_t n_q_heads,
+                                       int32_t n_kv_heads, int64_t n_tokens) {
+    if (!ck || batch < 0 || n_q_heads < 1 || n_kv_heads < 1 || n_tokens < 0) return 0;
+    return (size_t)sq_attn_ws(ck->dev.d, (int64_t)batch * n_kv_heads, n_tokens).total;
+}
+
+int tq_sq_decode_attention(const tq_sq_codec* ck, const tq_sq_codec* cv, const void* q, tq_dtype q_dtype,
+                           int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, const void* packed_k,
+                           const void* packed_v, int64_t n_tokens, const int32_t* lengths,
+                           float softmax_scale, void* out, tq_dtype out_dtype, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    if (!ck || !cv || batch < 0 || n_q_heads < 1 || n_kv_heads < 1 || n_tokens < 0) return TQ_EINVAL;
+    if (n_q_heads % n_kv_heads != 0 || n_q_heads / n_kv_heads > 16) return TQ_EINVAL;
+    if (ck->dev.d != cv->dev.d || ck->dev.n_heads != n_kv_heads || cv->dev.n_heads != n_kv_heads) return TQ_EINVAL;
+    if ((q_dtype != TQ_F32 && q_dtype != TQ_BF16) || (out_dtype != TQ_F32 && out_dtype != TQ_BF16)) {
+        const bool known = q_dtype == TQ_F16 || out_dtype == TQ_F16;
+        return known ? TQ_EUNSUPPORTED : TQ_EINVAL;
+    }
+    if (!std::isfinite(softmax_scale) || softmax_scale < 0.0f) return TQ_EINVAL;
+    if (batch == 0) return TQ_OK;
+    if (!q || !out || !workspace || (n_tokens > 0 && (!packed_k || !packed_v))) return TQ_EINVAL;
+    if (!aligned16(q) || !aligned16(out) || !aligned16(workspace) ||
+        (n_tokens > 0 && (!aligned16(packed_k) || !aligned16(packed_v))))
+        return TQ_EALIGN;
+    if (lengths && (reinterpret_cast<uintptr_t>(lengths) & 3u)) return TQ_EALIGN;
+    const int64_t streams = (int64_t)batch * n_kv_heads;
+    const SqAttnWs w = sq_attn_ws(ck->dev.d, streams, n_tokens);
+    if (workspace_bytes < (size_t)w.total) return TQ_EWORKSPACE;
+    if (!on_codec_device(ck) || !on_codec_device(cv)) return TQ_EINVAL;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)ck->dev.d);
+    SqScoresArgs qa{};
+    qa.t = ck->dev;
+    qa.q = q;
+    qa.q_bf16 = q_dtype == TQ_BF16;
+    qa.qp = reinterpret_cast<_Float16*>(ws);
+    qa.qscale = reinterpret_cast<float*>(ws + w.o_qs);
+    qa.qmul = scale * 1.4426950408889634f;   // scores in base-2 units for exp2
+    qa.n_streams = streams;
+    qa.n_q = n_q_heads / n_kv_heads;
+    qa.nq_pad = 16;
+    if (launch_sq_qprep(qa, s) != hipSuccess) return TQ_EHIP;
+    SqAttnArgs a{};
+    a.tk = ck->dev;
+    a.tv = cv->dev;
+    a.qp = qa.qp;
+    a.qscale = qa.qscale;
+    a.kin = static_cast<const uint32_t*>(packed_k);
+    a.vin = static_cast<const uint32_t*>(packed_v);
+    a.lens = lengths;
+    a.part = reinterpret_cast<float*>(ws + w.o_part);
+    a.ml = reinterpret_cast<float*>(ws + w.o_ml);
+    a.out = out;
+    a.out_bf16 = out_dtype == TQ_BF16;
+    a.n_streams = streams;
+    a.n_tokens = n_tokens;
+    a.tps = w.tps;
+    a.n_split = w.n_split;
+    a.hkv = n_kv_heads;
+    a.hq = n_q_heads;
+    a.g = n_q_heads / n_kv_heads;
+    return launch_sq_attention(a, s) == hipSuccess ? TQ_OK : TQ_EHIP;
 }
 
 int tq_sq_host_codebook(int32_t b, double* thresholds, double* centroids) {

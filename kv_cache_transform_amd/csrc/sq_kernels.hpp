@@ -57,12 +57,29 @@ struct SqScoresArgs {
     float* scores;          // [streams][n_q][tokens]
     _Float16* qp;           // workspace: [streams][nq_pad][d] fp16 of (Uᵀq ⊙ σ)·2^e_row
     float* qscale;          // workspace: [streams][nq_pad] 2^-e_row
+    float qmul;             // factor on every projected query (1 for scores; scale·log2 e for attention)
     int64_t n_streams, n_tokens, n_q, nq_pad, tiles_per_stream;
     int64_t blocks_per_stream, tiles_per_block;
+};
+
+struct SqAttnArgs {
+    SqDev tk, tv;
+    const _Float16* qp;     // [streams][16][d] fp16 projected queries (scaled by 2^e_row)
+    const float* qscale;    // [streams][16] 2^-e_row
+    const uint32_t* kin;
+    const uint32_t* vin;
+    const int32_t* lens;    // [batch] or null
+    float* part;            // [streams][n_split][16][d] unnormalised partial outputs in the V basis
+    float* ml;              // [streams][n_split][16][2] running max (base 2) and sum
+    void* out;              // [batch][hq][d]
+    int out_bf16;
+    int64_t n_streams, n_tokens, tps, n_split, hkv, hq, g;
 };
 
 hipError_t launch_sq_encode(const SqEncodeArgs& a, int num_cus, hipStream_t s);
 hipError_t launch_sq_decode(const SqDecodeArgs& a, bool out_bf16, int num_cus, hipStream_t s);
 hipError_t launch_sq_scores(const SqScoresArgs& a, int num_cus, hipStream_t s);
+hipError_t launch_sq_qprep(const SqScoresArgs& a, hipStream_t s);
+hipError_t launch_sq_attention(const SqAttnArgs& a, hipStream_t s);
 
 }  // namespace tq

@@ -179,3 +179,64 @@ def test_sq_rejects_unsupported_inputs():
     assert e.value.status == T._lib.TQ_EUNSUPPORTED
     with pytest.raises(T.TQError):
         codec.qk_scores(torch.randn(1, 257, 64, device=DEV), codec.encode(x), 16)
+
+
+def _sq_models(regime, d, b, b_tail, hkv, seed):
+    xc = _tokens(regime, hkv, 512, d, seed + 1000, hkv)
+    codec = T.SQCodec.calibrate(xc.float(), b, b_tail, device=0)
+    xc64 = _f64(xc)
+    return codec, [Q.calibrate(xc64[h], b, b_tail) for h in range(hkv)]
+
+
+@pytest.mark.parametrize("batch,hq,hkv,N,d,regime,bk,bv,lens,out_dtype", [
+    (2, 8, 2, 1000, 128, "lowrank_aligned", (4, 2), (4, 2), None, torch.float32),
+    (1, 4, 4, 777, 64, "isotropic", (3, 2), (2, 1), None, torch.bfloat16),
+    (2, 16, 1, 300, 128, "lowrank_steep", (5, 2), (3, 2), None, torch.float32),
+    (3, 8, 2, 600, 128, "lowrank_aligned", (4, 2), (4, 2), [600, 1, 0], torch.float32),
+    (2, 4, 2, 2500, 128, "isotropic", (6, 6), (6, 6), [2500, 1234], torch.float32),
+    (1, 2, 1, 64, 64, "isotropic", (8, 8), (8, 8), None, torch.float32),
+])
+def test_sq_decode_attention(batch, hq, hkv, N, d, regime, bk, bv, lens, out_dtype):
+    S, G = batch * hkv, hq // hkv
+    ck, mk = _sq_models(regime, d, bk[0], bk[1], hkv, 21)
+    cv, mv = _sq_models(regime, d, bv[0], bv[1], hkv, 22)
+    K = _tokens(regime, S, N, d, 31, hkv)
+    V = _tokens(regime, S, N, d, 32, hkv)
+    pk, pv = ck.encode(K), cv.encode(V)
+    q = torch.randn(batch, hq, d, generator=torch.Generator(device=DEV).manual_seed(3), device=DEV)
+    lt = None if lens is None else torch.tensor(lens, dtype=torch.int32, device=DEV)
+    out = T.sq_decode_attention(ck, cv, q, pk, pv, hkv, N, out_dtype=out_dtype, lengths=lt)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    q64 = q.cpu().numpy().astype(np.float64)
+    rk = pk.cpu().numpy()[: S * N * ck.record_bytes].reshape(S, N, ck.record_bytes)
+    rv = pv.cpu().numpy()[: S * N * cv.record_bytes].reshape(S, N, cv.record_bytes)
+    scale = 1.0 / np.sqrt(d)
+    worst = 0.0
+    for b in range(batch):
+        n_b = N if lens is None else lens[b]
+        for h in range(hq):
+            hk = h // G
+            st = b * hkv + hk
+            if n_b == 0:
+                assert np.all(got[b, h] == 0.0)
+                continue
+            ik = Q.unpack(rk[st, :n_b], mk[hk]["bits"])
+            iv = Q.unpack(rv[st, :n_b], mv[hk]["bits"])
+            sc = Q.scores(q64[b, h][None, :], ik, mk[hk])
+            want = Q.attention(sc, iv, mv[hk], scale)[0]
+            rel = np.linalg.norm(got[b, h] - want) / np.linalg.norm(want)
+            worst = max(worst, rel)
+    print(f"sq attention worst row rel {worst:.2e}")
+    assert worst < (2e-3 if out_dtype == torch.float32 else 5e-3)
+
+
+def test_sq_attention_validates_arguments():
+    ck, _ = _sq_models("isotropic", 64, 4, 2, 2, 21)
+    c1, _ = _sq_models("isotropic", 64, 4, 2, 1, 21)
+    q = torch.randn(1, 4, 64, device=DEV)
+    pk = ck.encode(_tokens("isotropic", 2, 32, 64, 1, 2))
+    with pytest.raises(T.TQError):          # codec heads must equal n_kv_heads
+        T.sq_decode_attention(ck, c1, q, pk, pk, 2, 32)
+    with pytest.raises(T.TQError):          # more than 16 query heads per kv head
+        T.sq_decode_attention(ck, ck, torch.randn(1, 34, 64, device=DEV), pk, pk, 2, 32)
