@@ -219,3 +219,43 @@ def test_sq_ties_to_the_lower_cell_are_caught(monkeypatch):
         return r
     monkeypatch.setattr(SQ, "encode", encode)
     _fails(SP.test_index_counts_thresholds_with_ties_to_the_upper_cell)
+
+
+# ---- Fmag oracle ------------------------------------------------------------------------------
+from oracle import fmag_oracle as FM
+from tests import test_oracle_fmag as FP
+
+
+def test_fmag_conjugated_spectrum_is_caught(monkeypatch):
+    real = FM.rfft
+    monkeypatch.setattr(FM, "rfft", lambda x: np.conj(real(x)))
+    _fails(FP.test_transform_is_the_written_out_dft_and_its_real_inverse, 16)
+
+
+def test_fmag_min_max_over_2_to_the_b_levels_is_caught(monkeypatch):
+    real = FM.encode
+    def encode(x, b, p):
+        r = real(x, b, p)
+        span = (r["hi"] - r["lo"])[:, None]
+        r["q"] = np.minimum(np.floor((r["mag"] - r["lo"][:, None]) / span * (1 << b) + 0.5).astype(np.int64),
+                            (1 << b) - 1)
+        return r
+    monkeypatch.setattr(FM, "encode", encode)
+    _fails(FP.test_min_max_quantiser_exact_points_and_bound)
+
+
+def test_fmag_phase_truncated_instead_of_rounded_is_caught(monkeypatch):
+    real = FM.encode
+    def encode(x, b, p):
+        r = real(x, b, p)
+        if r["pidx"] is not None:
+            P = 1 << p
+            r["pidx"] = np.floor((r["phase"] + math.pi) / (2 * math.pi) * P).astype(np.int64) % P
+        return r
+    monkeypatch.setattr(FM, "encode", encode)
+    _fails(FP.test_phase_levels_and_bound, 6)
+
+
+def test_fmag_inverse_without_the_half_spectrum_weights_is_caught(monkeypatch):
+    monkeypatch.setattr(FM, "irfft", lambda X, d: np.fft.ifft(np.concatenate([X, np.zeros((X.shape[0], d - X.shape[1]))], axis=1), n=d).real)
+    _fails(FP.test_transform_is_the_written_out_dft_and_its_real_inverse, 16)
