@@ -15,7 +15,7 @@ from . import _lib
 from ._lib import TQError, TQ_BF16, TQ_F32
 
 __all__ = ["Codec", "TQError", "get_layout", "encode", "decode", "qk_scores", "decode_attention",
-           "attention_workspace_bytes", "host_tables", "clear_cache", "SQCodec", "sq_host_codebook", "sq_decode_attention"]
+           "attention_workspace_bytes", "host_tables", "clear_cache", "SQCodec", "sq_host_codebook", "sq_decode_attention", "FmagCodec"]
 
 _DT = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}
 
@@ -279,3 +279,55 @@ def sq_host_codebook(b: int) -> dict:
     cen = np.zeros(1 << b, dtype=np.float64)
     _lib.check(_lib.lib().tq_sq_host_codebook(b, thr.ctypes.data, cen.ctypes.data), "tq_sq_host_codebook")
     return {"thresholds": thr, "centroids": cen}
+
+
+@dataclass(frozen=True)
+class FmagCodec:
+    """Fourier-magnitude codec (include/tq_fmag.h; "Fourier Magnitude KV Cache Quantization",
+    "Method"): d = 64 or 128, b magnitude bits (1..8), p phase bits (1..8, or 16 for a bf16 phase)."""
+    d: int
+    b: int = 4
+    p: int = 8
+
+    def params(self) -> _lib.FmagParams:
+        return _lib.FmagParams(self.d, self.b, self.p)
+
+    @property
+    def record_bytes(self) -> int:
+        n = ctypes.c_int64()
+        _lib.check(_lib.lib().tq_fmag_record_bytes(ctypes.byref(self.params()), ctypes.byref(n)), "tq_fmag_record_bytes")
+        return int(n.value)
+
+    def encode(self, x: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+        if x.dim() != 3 or x.shape[-1] != self.d or not x.is_contiguous():
+            raise ValueError("x must be a contiguous [n_streams, n_tokens, d] tensor")
+        S, N, _ = x.shape
+        need = S * N * self.record_bytes
+        if out is None:
+            out = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+        elif out.numel() < need or out.dtype != torch.uint8:
+            raise ValueError("packed buffer too small")
+        _lib.check(_lib.lib().tq_fmag_encode(ctypes.byref(self.params()), _ptr(x), _DT.get(x.dtype, -1), S, N,
+                                             _ptr(out), _stream(x.device)), "tq_fmag_encode")
+        return out
+
+    def decode(self, packed: torch.Tensor, n_streams: int, n_tokens: int, dtype: torch.dtype = torch.float32,
+               out: torch.Tensor | None = None) -> torch.Tensor:
+        if out is None:
+            out = torch.empty(n_streams, n_tokens, self.d, dtype=dtype, device=packed.device)
+        _lib.check(_lib.lib().tq_fmag_decode(ctypes.byref(self.params()), _ptr(packed), n_streams, n_tokens, _ptr(out),
+                                             _DT[out.dtype], _stream(packed.device)), "tq_fmag_decode")
+        return out
+
+    def qk_scores(self, q: torch.Tensor, packed: torch.Tensor, n_tokens: int, out: torch.Tensor | None = None,
+                  workspace: torch.Tensor | None = None) -> torch.Tensor:
+        S, nq, _ = q.shape
+        ws = int(_lib.lib().tq_fmag_scores_workspace_bytes(ctypes.byref(self.params()), S, nq))
+        if workspace is None:
+            workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=q.device)
+        if out is None:
+            out = torch.empty(S, nq, n_tokens, dtype=torch.float32, device=q.device)
+        _lib.check(_lib.lib().tq_fmag_qk_scores(ctypes.byref(self.params()), _ptr(q), _DT[q.dtype], nq, _ptr(packed),
+                                                S, n_tokens, _ptr(out), _ptr(workspace), workspace.numel(),
+                                                _stream(q.device)), "tq_fmag_qk_scores")
+        return out

@@ -1,4 +1,4 @@
-"""ctypes loader for libtq.so (the C ABI declared in include/tq.h and include/tq_sq.h).
+"""ctypes loader for libtq.so (the C ABI declared in include/tq.h, tq_sq.h and tq_fmag.h).
 
 The library is required: there is no fallback implementation.  If libtq.so has not been built
 (``python -m kv_cache_transform_amd.build``) every call raises."""
@@ -24,6 +24,9 @@ EXPORTS = ("tq_get_layout", "tq_encode", "tq_encode_append", "tq_decode", "tq_de
 SQ_EXPORTS = ("tq_sq_calibrate", "tq_sq_create", "tq_sq_destroy", "tq_sq_record_bytes", "tq_sq_encode",
               "tq_sq_decode", "tq_sq_scores_workspace_bytes", "tq_sq_qk_scores", "tq_sq_attention_workspace_bytes",
               "tq_sq_decode_attention", "tq_sq_host_codebook")
+# every symbol include/tq_fmag.h declares
+FMAG_EXPORTS = ("tq_fmag_record_bytes", "tq_fmag_encode", "tq_fmag_decode", "tq_fmag_scores_workspace_bytes",
+                "tq_fmag_qk_scores")
 
 
 class Params(ctypes.Structure):
@@ -36,6 +39,10 @@ class SqParams(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("b", ctypes.c_int32),
                 ("b_tail", ctypes.c_int32), ("waterfill", ctypes.c_int32), ("d_eff_max", ctypes.c_int32),
                 ("gamma", ctypes.c_double)]
+
+
+class FmagParams(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int32), ("b", ctypes.c_int32), ("p", ctypes.c_int32)]
 
 
 class Layout(ctypes.Structure):
@@ -62,6 +69,7 @@ def lib() -> ctypes.CDLL:
     L = ctypes.CDLL(LIB_PATH)
     P, I64, VP, I32, SZ = ctypes.POINTER(Params), ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_size_t
     Q = ctypes.POINTER(SqParams)
+    FP = ctypes.POINTER(FmagParams)
     sig = {
         "tq_get_layout": (ctypes.c_int, [P, I64, I64, ctypes.POINTER(Layout)]),
         "tq_encode": (ctypes.c_int, [P, VP, ctypes.c_int, I64, I64, VP, VP]),
@@ -88,6 +96,11 @@ def lib() -> ctypes.CDLL:
         "tq_sq_qk_scores": (ctypes.c_int, [VP, VP, ctypes.c_int, I64, VP, I64, I64, VP, VP, SZ, VP]),
         "tq_sq_host_codebook": (ctypes.c_int, [I32, VP, VP]),
         "tq_sq_attention_workspace_bytes": (SZ, [VP, I32, I32, I32, I64]),
+        "tq_fmag_record_bytes": (ctypes.c_int, [FP, ctypes.POINTER(I64)]),
+        "tq_fmag_encode": (ctypes.c_int, [FP, VP, ctypes.c_int, I64, I64, VP, VP]),
+        "tq_fmag_decode": (ctypes.c_int, [FP, VP, I64, I64, VP, ctypes.c_int, VP]),
+        "tq_fmag_scores_workspace_bytes": (SZ, [FP, I64, I64]),
+        "tq_fmag_qk_scores": (ctypes.c_int, [FP, VP, ctypes.c_int, I64, VP, I64, I64, VP, VP, SZ, VP]),
         "tq_sq_decode_attention": (ctypes.c_int, [VP, VP, VP, ctypes.c_int, I32, I32, I32, VP, VP, I64, VP,
                                                   ctypes.c_float, VP, ctypes.c_int, VP, SZ, VP]),
     }

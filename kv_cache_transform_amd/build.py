@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 OBJ = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libtq.so")
 SOURCES = ["tables.cpp", "tq_api.cpp", "encode.hip", "decode.hip", "scores.hip", "attention.hip",
-           "sq_host.cpp", "sq.hip"]
+           "sq_host.cpp", "sq.hip", "fmag_host.cpp", "fmag.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=gfx950", "-fno-strict-aliasing",

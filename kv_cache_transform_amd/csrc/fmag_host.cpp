@@ -1,0 +1,251 @@
+// Fourier-magnitude codec, host side: the DFT and inverse-DFT operand tiles, the phase-level
+// table, the query-side tables of the scores, and the C ABI of include/tq_fmag.h ("Fourier Magnitude
+// KV Cache Quantization", forum thread, "Method").
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <tuple>
+#include <vector>
+
+#include "../../include/tq_fmag.h"
+#include "fmag_kernels.hpp"
+#include "tables.hpp"
+
+namespace tq {
+namespace {
+
+int check(const tq_fmag_params* p) {
+    if (!p) return TQ_EINVAL;
+    if (p->d != 64 && p->d != 128) return TQ_EINVAL;
+    if (p->b < 1 || p->b > 8) return TQ_EINVAL;
+    if (!((p->p >= 1 && p->p <= 8) || p->p == TQ_FMAG_PHASE_BF16)) return TQ_EINVAL;
+    return TQ_OK;
+}
+
+int record_words(const tq_fmag_params* p) {
+    const int nb = p->d / 2 + 1;
+    return (nb * (p->b + p->p) + 31) / 32 + 2;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+// DFT coefficient of input j for spectrum coordinate c (X_c = Σ_j F(j, c) x_j) and the inverse
+// coefficient (x_j = Σ_c G(j, c) X_c) in the coordinate order of fmag_kernels.hpp
+double dft_coef(int d, int j, int c) {
+    if (c < d / 2) return std::cos(2.0 * M_PI * j * c / d);
+    if (c == d / 2) return (j & 1) ? -1.0 : 1.0;
+    return -std::sin(2.0 * M_PI * j * (c - d / 2) / d);
+}
+double idft_coef(int d, int j, int c) {
+    if (c == 0) return 1.0 / d;
+    if (c < d / 2) return 2.0 / d * std::cos(2.0 * M_PI * j * c / d);
+    if (c == d / 2) return ((j & 1) ? -1.0 : 1.0) / d;
+    return -2.0 / d * std::sin(2.0 * M_PI * j * (c - d / 2) / d);
+}
+
+void split16(double v, uint16_t* hi, uint16_t* lo) {
+    *hi = f64_to_f16_bits(v);
+    *lo = f64_to_f16_bits(v - (double)f16_bits_to_f32(*hi));
+}
+
+using Key = std::tuple<int, int, int, int>;   // device, d, b, p
+std::mutex g_mu;
+std::map<Key, FmDev> g_tables;
+std::map<int, int> g_cus;
+
+int build(const tq_fmag_params* p, FmDev* out) {
+    const int d = p->d, T = d / 16, S = d / 32;
+    std::vector<uint16_t> enc((size_t)2 * T * S * 512), dec((size_t)2 * T * S * 512);
+    const double gmax = 2.0 / d;
+    const int e = 13 - (int)std::floor(std::log2(gmax));
+    for (int t = 0; t < T; ++t)
+        for (int s = 0; s < S; ++s)
+            for (int l = 0; l < 64; ++l)
+                for (int i = 0; i < 8; ++i) {
+                    const size_t o = (((size_t)t * S + s) * 64 + l) * 8 + i, lo_off = (size_t)T * S * 512;
+                    // encode B[kk = 8g + i][n = l % 16]: input j = 32 s + 8 g + i, coordinate c = 16 t + n
+                    split16(dft_coef(d, 32 * s + 8 * (l / 16) + i, 16 * t + (l % 16)) * 256.0, &enc[o], &enc[o + lo_off]);
+                    // decode A[m = l % 16][kk = 8 g + i]: output j = 16 t + m, coordinate c = 32 s + 8 g + i
+                    split16(std::ldexp(idft_coef(d, 16 * t + (l % 16), 32 * s + 8 * (l / 16) + i), e), &dec[o],
+                            &dec[o + lo_off]);
+                }
+    std::vector<float> cs(512, 0.0f);
+    if (p->p <= 8)
+        for (int i = 0; i < (1 << p->p); ++i) {
+            const double a = -M_PI + 2.0 * M_PI * i / (1 << p->p);
+            cs[2 * i] = (float)std::cos(a);
+            cs[2 * i + 1] = (float)std::sin(a);
+        }
+    std::vector<float> U((size_t)d * d), w(d);
+    for (int j = 0; j < d; ++j)
+        for (int c = 0; c < d; ++c) U[(size_t)j * d + c] = (float)dft_coef(d, j, c);
+    for (int c = 0; c < d; ++c) w[c] = (float)((c == 0 || c == d / 2 ? 1.0 : 2.0) / d);
+
+    size_t off = 0;
+    auto place = [&](size_t bytes) { const size_t o = off; off = (off + bytes + 255) / 256 * 256; return o; };
+    const size_t o_e = place(enc.size() * 2), o_d = place(dec.size() * 2), o_c = place(cs.size() * 4),
+                 o_u = place(U.size() * 4), o_w = place(w.size() * 4);
+    std::vector<uint8_t> blob(off);
+    std::memcpy(blob.data() + o_e, enc.data(), enc.size() * 2);
+    std::memcpy(blob.data() + o_d, dec.data(), dec.size() * 2);
+    std::memcpy(blob.data() + o_c, cs.data(), cs.size() * 4);
+    std::memcpy(blob.data() + o_u, U.data(), U.size() * 4);
+    std::memcpy(blob.data() + o_w, w.data(), w.size() * 4);
+    void* mem = nullptr;
+    if (hipMalloc(&mem, blob.size()) != hipSuccess) return TQ_EHIP;
+    if (hipMemcpy(mem, blob.data(), blob.size(), hipMemcpyHostToDevice) != hipSuccess) {
+        (void)hipFree(mem);
+        return TQ_EHIP;
+    }
+    uint8_t* base = static_cast<uint8_t*>(mem);
+    FmDev t;
+    t.d = d;
+    t.b = p->b;
+    t.p = p->p;
+    t.rec_words = record_words(p);
+    t.enc_b = reinterpret_cast<const _Float16*>(base + o_e);
+    t.dec_a = reinterpret_cast<const _Float16*>(base + o_d);
+    t.dec_scale = (float)std::ldexp(1.0, -e);
+    t.cs = reinterpret_cast<const float*>(base + o_c);
+    t.qprep.d = d;
+    t.qprep.n_heads = 1;
+    t.qprep.U32 = reinterpret_cast<const float*>(base + o_u);
+    t.qprep.sigma = reinterpret_cast<const float*>(base + o_w);
+    t.blob = mem;
+    *out = t;
+    return TQ_OK;
+}
+
+int tables(const tq_fmag_params* p, FmDev* out, int* cus) {
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) return TQ_EHIP;
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto c = g_cus.find(device);
+    if (c == g_cus.end()) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, device) != hipSuccess) return TQ_EHIP;
+        c = g_cus.emplace(device, n).first;
+    }
+    *cus = c->second;
+    const Key key{device, p->d, p->b, p->p};
+    auto it = g_tables.find(key);
+    if (it == g_tables.end()) {
+        FmDev t;
+        const int rc = build(p, &t);
+        if (rc != TQ_OK) return rc;
+        it = g_tables.emplace(key, t).first;
+    }
+    *out = it->second;
+    return TQ_OK;
+}
+
+}  // namespace
+
+// frees the Fmag tables (called by tq_clear_cache)
+void fmag_clear_tables() {
+    std::lock_guard<std::mutex> lk(g_mu);
+    for (auto& kv : g_tables) (void)hipFree(kv.second.blob);
+    g_tables.clear();
+}
+
+}  // namespace tq
+
+using namespace tq;
+
+extern "C" {
+
+int tq_fmag_record_bytes(const tq_fmag_params* p, int64_t* bytes) {
+    if (check(p) != TQ_OK || !bytes) return TQ_EINVAL;
+    *bytes = (int64_t)record_words(p) * 4;
+    return TQ_OK;
+}
+
+int tq_fmag_encode(const tq_fmag_params* p, const void* x, tq_dtype x_dtype, int64_t n_streams,
+                   int64_t n_tokens, void* packed, void* stream) {
+    if (check(p) != TQ_OK || n_streams < 0 || n_tokens < 0) return TQ_EINVAL;
+    if (x_dtype != TQ_BF16) return x_dtype == TQ_F32 || x_dtype == TQ_F16 ? TQ_EUNSUPPORTED : TQ_EINVAL;
+    if (n_streams == 0 || n_tokens == 0) return TQ_OK;
+    if (!x || !packed) return TQ_EINVAL;
+    if (!aligned16(x) || !aligned16(packed)) return TQ_EALIGN;
+    FmEncodeArgs a{};
+    int cus = 0;
+    const int rc = tables(p, &a.t, &cus);
+    if (rc != TQ_OK) return rc;
+    a.x = static_cast<const uint16_t*>(x);
+    a.out = static_cast<uint32_t*>(packed);
+    a.n_streams = n_streams;
+    a.n_tokens = n_tokens;
+    a.tiles_per_stream = (n_tokens + 15) / 16;
+    return launch_fmag_encode(a, cus, static_cast<hipStream_t>(stream)) == hipSuccess ? TQ_OK : TQ_EHIP;
+}
+
+int tq_fmag_decode(const tq_fmag_params* p, const void* packed, int64_t n_streams, int64_t n_tokens,
+                   void* x_hat, tq_dtype out_dtype, void* stream) {
+    if (check(p) != TQ_OK || n_streams < 0 || n_tokens < 0) return TQ_EINVAL;
+    if (out_dtype != TQ_F32 && out_dtype != TQ_BF16) return out_dtype == TQ_F16 ? TQ_EUNSUPPORTED : TQ_EINVAL;
+    if (n_streams == 0 || n_tokens == 0) return TQ_OK;
+    if (!packed || !x_hat) return TQ_EINVAL;
+    if (!aligned16(packed) || !aligned16(x_hat)) return TQ_EALIGN;
+    FmDecodeArgs a{};
+    int cus = 0;
+    const int rc = tables(p, &a.t, &cus);
+    if (rc != TQ_OK) return rc;
+    a.in = static_cast<const uint32_t*>(packed);
+    a.out = x_hat;
+    a.n_streams = n_streams;
+    a.n_tokens = n_tokens;
+    a.tiles_per_stream = (n_tokens + 15) / 16;
+    return launch_fmag_decode(a, out_dtype == TQ_BF16, cus, static_cast<hipStream_t>(stream)) == hipSuccess ? TQ_OK
+                                                                                                            : TQ_EHIP;
+}
+
+size_t tq_fmag_scores_workspace_bytes(const tq_fmag_params* p, int64_t n_streams, int64_t n_q) {
+    if (check(p) != TQ_OK || n_streams < 0 || n_q < 0) return 0;
+    const int64_t nq_pad = (n_q + 15) / 16 * 16;
+    const int64_t qp = (n_streams * nq_pad * p->d * 2 + 255) / 256 * 256;
+    return (size_t)(qp + (n_streams * nq_pad * 4 + 255) / 256 * 256);
+}
+
+int tq_fmag_qk_scores(const tq_fmag_params* p, const void* q, tq_dtype q_dtype, int64_t n_q,
+                      const void* packed, int64_t n_streams, int64_t n_tokens, float* scores,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+    if (check(p) != TQ_OK || n_streams < 0 || n_tokens < 0 || n_q < 0 || n_q > 256) return TQ_EINVAL;
+    if (q_dtype != TQ_F32 && q_dtype != TQ_BF16) return q_dtype == TQ_F16 ? TQ_EUNSUPPORTED : TQ_EINVAL;
+    if (n_streams == 0 || n_tokens == 0 || n_q == 0) return TQ_OK;
+    if (!q || !packed || !scores || !workspace) return TQ_EINVAL;
+    if (!aligned16(q) || !aligned16(packed) || !aligned16(scores) || !aligned16(workspace)) return TQ_EALIGN;
+    if (workspace_bytes < tq_fmag_scores_workspace_bytes(p, n_streams, n_q)) return TQ_EWORKSPACE;
+    FmScoresArgs a{};
+    int cus = 0;
+    const int rc = tables(p, &a.t, &cus);
+    if (rc != TQ_OK) return rc;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    const int64_t nq_pad = (n_q + 15) / 16 * 16;
+    const int64_t qpb = (n_streams * nq_pad * p->d * 2 + 255) / 256 * 256;
+    SqScoresArgs qa{};
+    qa.t = a.t.qprep;
+    qa.q = q;
+    qa.q_bf16 = q_dtype == TQ_BF16;
+    qa.qp = static_cast<_Float16*>(workspace);
+    qa.qscale = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + qpb);
+    qa.qmul = 1.0f;
+    qa.n_streams = n_streams;
+    qa.n_q = n_q;
+    qa.nq_pad = nq_pad;
+    if (launch_sq_qprep(qa, s) != hipSuccess) return TQ_EHIP;
+    a.qp = qa.qp;
+    a.qscale = qa.qscale;
+    a.in = static_cast<const uint32_t*>(packed);
+    a.scores = scores;
+    a.n_streams = n_streams;
+    a.n_tokens = n_tokens;
+    a.n_q = n_q;
+    a.nq_pad = nq_pad;
+    a.tiles_per_stream = (n_tokens + 15) / 16;
+    return launch_fmag_scores(a, cus, s) == hipSuccess ? TQ_OK : TQ_EHIP;
+}
+
+}  // extern "C"

@@ -11,6 +11,7 @@
 #include <vector>
 
 #include "../../include/tq.h"
+#include "fmag_kernels.hpp"
 #include "kernels.hpp"
 #include "tables.hpp"
 
@@ -539,9 +540,12 @@ int tq_decode_attention_varlen(const tq_params* pk, const tq_params* pv, const v
 }
 
 void tq_clear_cache(void) {
-    std::lock_guard<std::mutex> lk(g_mu);
-    for (auto& kv : g_tables) (void)hipFree(kv.second.blob);
-    g_tables.clear();
+    {
+        std::lock_guard<std::mutex> lk(g_mu);
+        for (auto& kv : g_tables) (void)hipFree(kv.second.blob);
+        g_tables.clear();
+    }
+    fmag_clear_tables();
 }
 
 }  // extern "C"

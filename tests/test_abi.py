@@ -27,7 +27,7 @@ def test_exports_every_declared_symbol():
     for h in sorted(os.listdir(os.path.join(ROOT, "include"))):
         if h.endswith(".h"):
             declared |= set(re.findall(r"\b(tq_[a-z_]+)\s*\(", open(os.path.join(ROOT, "include", h)).read()))
-    assert declared == set(_lib.EXPORTS) | set(_lib.SQ_EXPORTS)
+    assert declared == set(_lib.EXPORTS) | set(_lib.SQ_EXPORTS) | set(_lib.FMAG_EXPORTS)
     for name in declared:
         assert hasattr(L, name), name
 
@@ -141,3 +141,19 @@ def test_product_package_does_not_import_the_oracle():
             if f.endswith((".py", ".cpp", ".hip", ".hpp", ".h")):
                 txt = open(os.path.join(dirpath, f)).read()
                 assert "oracle" not in txt.replace("no oracle", ""), f
+
+
+def test_fmag_record_size_and_validation():
+    L = _lib_or_skip()
+    from oracle import fmag_oracle as FO
+    for d, b, p in ((128, 4, 8), (128, 4, 16), (64, 3, 6), (64, 8, 8), (128, 1, 1)):
+        assert T.FmagCodec(d, b, p).record_bytes == 4 * FO.record_words(d, b, p)
+    n = ctypes.c_int64()
+    for d, b, p in ((256, 4, 8), (128, 0, 8), (128, 9, 8), (128, 4, 0), (128, 4, 9), (128, 4, 12)):
+        prm = _lib.FmagParams(d, b, p)
+        assert L.tq_fmag_record_bytes(ctypes.byref(prm), ctypes.byref(n)) == _lib.TQ_EINVAL
+        assert L.tq_fmag_encode(ctypes.byref(prm), None, _lib.TQ_BF16, 1, 1, None, None) == _lib.TQ_EINVAL
+    prm = _lib.FmagParams(128, 4, 8)
+    assert L.tq_fmag_encode(ctypes.byref(prm), None, _lib.TQ_F32, 1, 1, None, None) == _lib.TQ_EUNSUPPORTED
+    assert L.tq_fmag_encode(ctypes.byref(prm), None, _lib.TQ_BF16, 1, 0, None, None) == _lib.TQ_OK
+    assert L.tq_fmag_decode(ctypes.byref(prm), None, 1, 1, None, _lib.TQ_F32, None) == _lib.TQ_EINVAL

@@ -1,0 +1,137 @@
+"""GPU parity of the Fourier-magnitude codec (through the C ABI) against the Fmag oracle.
+
+Tolerances.  The kernel's spectrum comes from fp16 products of the exact (power-of-two scaled) input
+with the DFT matrix as an fp16 hi + lo pair, accumulated in fp32: its error is below
+e_X = 2^-18 Σ_j |x_j| per coefficient.  So
+  * lo and hi within e_X of the oracle's;
+  * magnitude indices equal except where the oracle's (|X| - lo)/(hi - lo)·(2^b - 1) lies within
+    (2^b - 1)·3 e_X/(hi - lo) + 1e-5 of a rounding point;
+  * phase fields equal except where the oracle's phase lies within e_X/|X_k| + 1e-6 rad (about the
+    error of an fp32 atan2 of coefficients that far off) of a rounding point, or at ±π;
+  * records word-identical to the oracle's packing of the GPU's own fields;
+  * fp32 decode within 1e-5 relative L2 per stream of the oracle's decode of the GPU's records;
+  * scores within 2e-3 relative L2 per (stream, query) row.
+Page: "Fourier Magnitude KV Cache Quantization" (forum thread), "Method"."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_transform_amd as T
+from oracle import fmag_oracle as F
+from oracle import tq_oracle as O
+from synth import inputs as I
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    T._lib.lib()
+    yield
+
+
+def _f64(x):
+    return O.bf16_bits_to_f64(I.bf16_bits(x))
+
+
+def _data(kind, S, N, d, seed):
+    if kind == "gauss":
+        return I.gaussian((S, N, d), seed, device=DEV)
+    if kind == "rope":
+        return I.rope_gaussian(S, N, d, seed, device=DEV)
+    return I.student_t(S, N, d, 3, seed, device=DEV)
+
+
+def _check(codec, x, packed):
+    S, N, d = x.shape
+    b, p = codec.b, codec.p
+    W = F.record_words(d, b, p)
+    words = packed.cpu().numpy()[: S * N * W * 4].view(np.uint32).reshape(S, N, W)
+    x64 = _f64(x)
+    recs, flagged, mism = [], 0, 0
+    for st in range(S):
+        g = F.unpack(words[st], b, p, d)
+        assert np.array_equal(words[st], F.pack({**g, "pbf": g["pbf"]}, b, p, d)), "record layout or padding"
+        o = F.encode(x64[st], b, p)
+        ex = 2.0 ** -18 * np.abs(x64[st]).sum(axis=1)
+        assert np.all(np.abs(g["lo"] - o["lo"]) <= ex) and np.all(np.abs(g["hi"] - o["hi"]) <= ex)
+        L = (1 << b) - 1
+        span = np.maximum(o["hi"] - o["lo"], 1e-300)
+        mflag = F.magnitude_flags(o, 1e-5) | (np.abs(o["t"] - np.floor(o["t"]) - 0.5) < (L * 3 * ex / span)[:, None])
+        pband = ex[:, None] / np.maximum(o["mag"], 1e-300) + 1e-6
+        if p == F.PHASE_BF16:
+            f = np.abs(o["phase"])
+            ulp = 2.0 ** (np.floor(np.log2(np.maximum(f, 1e-300))) - 7)
+            dist = np.abs(f / ulp - np.floor(f / ulp) - 0.5) * ulp
+            pflag = (dist < pband) | (np.abs(f - math.pi) < pband) | (o["mag"] <= 10 * ex[:, None])
+            pdiff = g["pbf"] != o["pbf"]
+        else:
+            u = (o["phase"] + math.pi) / (2 * math.pi) * (1 << p)
+            pflag = (np.abs(u - np.floor(u) - 0.5) < pband * (1 << p) / (2 * math.pi)) | (o["mag"] <= 10 * ex[:, None])
+            pdiff = g["pidx"] != o["pidx"]
+        qdiff = g["q"] != o["q"]
+        assert not (qdiff & ~mflag).any(), (st, np.argwhere(qdiff & ~mflag)[:5])
+        assert not (pdiff & ~pflag).any(), (st, np.argwhere(pdiff & ~pflag)[:5], o["phase"][pdiff & ~pflag][:5])
+        flagged += int(mflag.sum() + pflag.sum())
+        mism += int(qdiff.sum() + pdiff.sum())
+        recs.append(g)
+    return recs, flagged, mism
+
+
+@pytest.mark.parametrize("d,b,p,kind", [
+    (128, 4, 8, "rope"), (128, 4, 16, "gauss"), (128, 3, 6, "gauss"), (64, 4, 8, "gauss"),
+    (64, 2, 16, "tdist"), (128, 8, 8, "tdist"), (64, 1, 1, "gauss"), (128, 5, 3, "rope"),
+])
+def test_fmag_encode_decode_scores_parity(d, b, p, kind):
+    S, N = 3, 1000
+    codec = T.FmagCodec(d, b, p)
+    x = _data(kind, S, N, d, 41)
+    packed = codec.encode(x)
+    torch.cuda.synchronize()
+    recs, flagged, mism = _check(codec, x, packed)
+    print(f"fmag d={d} b={b} p={p} {kind}: flagged {flagged}, mismatched {mism}")
+    xh = codec.decode(packed, S, N, torch.float32).cpu().numpy()
+    xb = _f64(codec.decode(packed, S, N, torch.bfloat16))
+    for st in range(S):
+        want = F.decode(recs[st], b, p, d)
+        rel = np.linalg.norm(xh[st] - want) / np.linalg.norm(want)
+        assert rel < 1e-5, (st, rel)
+        assert np.all(np.abs(xb[st] - want) <= np.abs(want) * 2.0 ** -8 + 1e-5 * np.abs(want).max())
+    q = torch.randn(S, 19, d, generator=torch.Generator(device=DEV).manual_seed(9), device=DEV)
+    sc = codec.qk_scores(q, packed, N).cpu().numpy()
+    q64 = q.cpu().numpy().astype(np.float64)
+    for st in range(S):
+        want = F.scores(q64[st], recs[st], b, p, d)
+        rel = np.linalg.norm(sc[st] - want, axis=1) / np.linalg.norm(want, axis=1)
+        assert rel.max() < 2e-3, (st, rel.max())
+
+
+@pytest.mark.parametrize("N", [1, 15, 17])
+def test_fmag_short_streams_and_zero_vectors(N):
+    codec = T.FmagCodec(128, 4, 8)
+    x = _data("gauss", 2, N, 128, 7)
+    x[1, 0] = 0            # a zero vector: lo = hi = 0, every field 0 or the phase of +0
+    packed = codec.encode(x)
+    torch.cuda.synchronize()
+    recs, _, _ = _check(codec, x, packed)
+    xh = codec.decode(packed, 2, N).cpu().numpy()
+    assert np.all(xh[1, 0] == 0.0)
+    for st in range(2):
+        want = F.decode(recs[st], 4, 8, 128)
+        assert np.linalg.norm(xh[st] - want) <= 1e-5 * np.linalg.norm(want)
+
+
+def test_fmag_leaves_other_bytes_and_rejects_fp32():
+    codec = T.FmagCodec(64, 4, 8)
+    x = _data("gauss", 2, 40, 64, 3)
+    rb = codec.record_bytes
+    buf = torch.full((2 * 40 * rb + 256,), 0xA5, dtype=torch.uint8, device=DEV)
+    codec.encode(x, buf)
+    torch.cuda.synchronize()
+    assert torch.all(buf[2 * 40 * rb:] == 0xA5)
+    with pytest.raises(T.TQError):
+        codec.encode(x.float())
