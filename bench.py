@@ -291,6 +291,35 @@ def main():
                                        "achieved_GBs": round(sqa_alg / (sam * 1e-3) / 1e9, 1),
                                        "hbm_frac": round(sqa_alg / (sam * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         del sq, sqv, sws
+        # the Fourier-magnitude codec on the same K cache: 4-bit magnitudes and 8-bit phases
+        # ("Fmag4+phase8b"), 108-byte records
+        fm = T.FmagCodec(d, 4, 8)
+        fm_alg = nvec * (2 * d + fm.record_bytes)
+        fpk = torch.empty(nvec * fm.record_bytes, dtype=torch.uint8, device=dev)
+        fm.encode(K, fpk)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(3):
+            fm.encode(K, fpk)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        fms = e0.elapsed_time(e1) / 3
+        kern["fmag_encode_k"] = {"ms": round(fms, 4), "alg_bytes": fm_alg, "record_bytes": fm.record_bytes,
+                                 "achieved_GBs": round(fm_alg / (fms * 1e-3) / 1e9, 1),
+                                 "hbm_frac": round(fm_alg / (fms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        xh = torch.empty(streams, N, d, dtype=torch.bfloat16, device=dev)
+        fm.decode(fpk, streams, N, torch.bfloat16, out=xh)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(3):
+            fm.decode(fpk, streams, N, torch.bfloat16, out=xh)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        fdm = e0.elapsed_time(e1) / 3
+        kern["fmag_decode_k_bf16"] = {"ms": round(fdm, 4), "alg_bytes": fm_alg,
+                                      "achieved_GBs": round(fm_alg / (fdm * 1e-3) / 1e9, 1),
+                                      "hbm_frac": round(fm_alg / (fdm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del xh, fpk
     sample_k, sample_v = K[:1, :2048].clone(), V[:1, :2048].clone()   # the CPU baseline's sample
     del K
 

@@ -130,8 +130,8 @@ void grid_split(Args& b, const void* kern, int threads, size_t lds, int num_cus)
 // ---------------------------------------------------------------------------------------------
 constexpr int kFmThreads = 512;
 
-template <int D>
-__global__ __launch_bounds__(kFmThreads, 1) void fmag_encode_kernel(FmEncodeArgs a) {
+template <int D, bool PQ>   // PQ: p-bit phase indices (else bf16 phases); 4 waves per SIMD (two blocks per CU)
+__global__ __launch_bounds__(kFmThreads, 4) void fmag_encode_kernel(FmEncodeArgs a) {
     constexpr int T = D / 16, S = D / 32, TH = T / 2, NB = D / 2 + 1;
     extern __shared__ __align__(16) uint8_t smem[];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nwaves = kFmThreads / 64;
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(kFmThreads, 1) void fmag_encode_kernel(FmEncodeArgs
                     nyq = im;
                     im = 0.0f;
                 }
-                mag[t] = sqrtf(re * re + im * im);
+                mag[t] = __builtin_amdgcn_sqrtf(fmaf(re, re, im * im));
                 ph[t] = atan2f(im, re);
                 lo = fminf(lo, mag[t]);
                 hi = fmaxf(hi, mag[t]);
@@ -232,15 +232,14 @@ __global__ __launch_bounds__(kFmThreads, 1) void fmag_encode_kernel(FmEncodeArgs
             for (int t = 0; t < TH; ++t) {
                 const uint32_t kb = (uint32_t)(16 * t + n);
                 const uint32_t qv = (uint32_t)fminf(floorf((mag[t] - lo) * inv + 0.5f), Lm1);
-                uint32_t pv;
-                if (p == 16u) pv = (f2u(ph[t]) + 0x7fffu + ((f2u(ph[t]) >> 16) & 1u)) >> 16;   // bf16, nearest even
-                else pv = (uint32_t)(int)floorf((ph[t] + kPi) * pscale + 0.5f) & ((1u << p) - 1u);
                 const uint32_t qg = quad_or4(qv << ((n & 3) * b));
                 if ((n & 3) == 0) or_bits(rec, kb * b, qg);
-                if (p <= 8u) {
+                if constexpr (PQ) {
+                    const uint32_t pv = (uint32_t)(int)floorf((ph[t] + kPi) * pscale + 0.5f) & ((1u << p) - 1u);
                     const uint32_t pg = quad_or4(pv << ((n & 3) * p));
                     if ((n & 3) == 0) or_bits(rec, NB * b + kb * p, pg);
                 } else {
+                    const uint32_t pv = (f2u(ph[t]) + 0x7fffu + ((f2u(ph[t]) >> 16) & 1u)) >> 16;   // bf16, nearest even
                     const uint32_t pg = pair_or(pv << ((n & 1) * 16));
                     if ((n & 1) == 0) or_bits(rec, NB * b + kb * 16, pg);
                 }
@@ -250,8 +249,8 @@ __global__ __launch_bounds__(kFmThreads, 1) void fmag_encode_kernel(FmEncodeArgs
                 const uint32_t qv = (uint32_t)fminf(floorf((m - lo) * inv + 0.5f), Lm1);
                 const float phn = atan2f(0.0f, nyq);
                 uint32_t pv;
-                if (p == 16u) pv = (f2u(phn) + 0x7fffu + ((f2u(phn) >> 16) & 1u)) >> 16;
-                else pv = (uint32_t)(int)floorf((phn + kPi) * pscale + 0.5f) & ((1u << p) - 1u);
+                if constexpr (PQ) pv = (uint32_t)(int)floorf((phn + kPi) * pscale + 0.5f) & ((1u << p) - 1u);
+                else pv = (f2u(phn) + 0x7fffu + ((f2u(phn) >> 16) & 1u)) >> 16;
                 or_bits(rec, (uint32_t)(D / 2) * b, qv);
                 or_bits(rec, NB * b + (uint32_t)(D / 2) * p, pv);
                 rec[RW - 2] = f2u(lo);
@@ -268,23 +267,25 @@ __global__ __launch_bounds__(kFmThreads, 1) void fmag_encode_kernel(FmEncodeArgs
     }
 }
 
-template <int D>
+template <int D, bool PQ>
 static hipError_t launch_fenc(const FmEncodeArgs& a, int num_cus, hipStream_t s) {
     FmEncodeArgs b = a;
     const size_t lds = (size_t)2 * (D / 16) * (D / 32) * 1024 + (size_t)(kFmThreads / 64) * (16 * a.t.rec_words + 1) * 4;
-    const void* kern = reinterpret_cast<const void*>(&fmag_encode_kernel<D>);
+    const void* kern = reinterpret_cast<const void*>(&fmag_encode_kernel<D, PQ>);
     if (lds > 65536) {
         const hipError_t e = allow_lds(kern);
         if (e != hipSuccess) return e;
     }
     grid_split(b, kern, kFmThreads, lds, num_cus);
-    hipLaunchKernelGGL((fmag_encode_kernel<D>), dim3((unsigned)(b.n_streams * b.blocks_per_stream)), dim3(kFmThreads),
+    hipLaunchKernelGGL((fmag_encode_kernel<D, PQ>), dim3((unsigned)(b.n_streams * b.blocks_per_stream)), dim3(kFmThreads),
                        lds, s, b);
     return hipGetLastError();
 }
 
 hipError_t launch_fmag_encode(const FmEncodeArgs& a, int num_cus, hipStream_t s) {
-    return a.t.d == 64 ? launch_fenc<64>(a, num_cus, s) : launch_fenc<128>(a, num_cus, s);
+    const bool pq = a.t.p <= 8;
+    if (a.t.d == 64) return pq ? launch_fenc<64, true>(a, num_cus, s) : launch_fenc<64, false>(a, num_cus, s);
+    return pq ? launch_fenc<128, true>(a, num_cus, s) : launch_fenc<128, false>(a, num_cus, s);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -294,7 +295,7 @@ hipError_t launch_fmag_encode(const FmEncodeArgs& a, int num_cus, hipStream_t s)
 // the real parts of bins κ = c, else the imaginary parts of bins κ = c - d/2, whose first slot
 // (g = 0, i = 0) is the real Nyquist bin.  Values are X̂ = (lo + q Δ)·(cos or sin of the phase),
 // times 2^es (es from the token's hi, so |X̂|·2^es < 2^15).
-template <int D>
+template <int D, bool PQ>
 __device__ __forceinline__ void spectrum8(const uint32_t* rec, int RW, uint32_t b, uint32_t p, int s, int g,
                                           const float* cs, float (&out)[8], int& es) {
     constexpr int S = D / 32, NB = D / 2 + 1;
@@ -310,11 +311,11 @@ __device__ __forceinline__ void spectrum8(const uint32_t* rec, int RW, uint32_t 
         const float mag = fmaf((float)get_field(rec, kb * b, b), delta, lo);
         const uint32_t pf = get_field(rec, NB * b + kb * p, p);
         float trig;
-        if (p == 16u) {
+        if constexpr (PQ) {
+            trig = cs[2 * pf + ((im && !nyq) ? 1 : 0)];
+        } else {
             const float ph = u2f(pf << 16);
             trig = (im && !nyq) ? __sinf(ph) : __cosf(ph);
-        } else {
-            trig = cs[2 * pf + ((im && !nyq) ? 1 : 0)];
         }
         out[i] = __builtin_amdgcn_ldexpf(mag * trig, es);
     }
@@ -323,7 +324,7 @@ __device__ __forceinline__ void spectrum8(const uint32_t* rec, int RW, uint32_t 
 // ---------------------------------------------------------------------------------------------
 // decode
 // ---------------------------------------------------------------------------------------------
-template <int D, bool BF>
+template <int D, bool BF, bool PQ>
 __global__ __launch_bounds__(kFmThreads, 1) void fmag_decode_kernel(FmDecodeArgs a) {
     constexpr int T = D / 16, S = D / 32, NP = (16 * (D / 2) + 63) / 64;
     extern __shared__ __align__(16) uint8_t smem[];
@@ -364,7 +365,7 @@ __global__ __launch_bounds__(kFmThreads, 1) void fmag_decode_kernel(FmDecodeArgs
 #pragma unroll
         for (int s = 0; s < S; ++s) {
             float x8[8];
-            spectrum8<D>(stage + v * RW, RW, b, p, s, g, cs, x8, es);
+            spectrum8<D, PQ>(stage + v * RW, RW, b, p, s, g, cs, x8, es);
             u32x4 hv, lv;
 #pragma unroll
             for (int i = 0; i < 8; i += 2) {
@@ -399,24 +400,29 @@ __global__ __launch_bounds__(kFmThreads, 1) void fmag_decode_kernel(FmDecodeArgs
     }
 }
 
-template <int D, bool BF>
+template <int D, bool BF, bool PQ>
 static hipError_t launch_fdec(const FmDecodeArgs& a, int num_cus, hipStream_t s) {
     FmDecodeArgs b = a;
     const size_t lds = 2048 + (size_t)2 * (D / 16) * (D / 32) * 1024 + (size_t)(kFmThreads / 64) * (16 * a.t.rec_words + 2) * 4;
-    const void* kern = reinterpret_cast<const void*>(&fmag_decode_kernel<D, BF>);
+    const void* kern = reinterpret_cast<const void*>(&fmag_decode_kernel<D, BF, PQ>);
     if (lds > 65536) {
         const hipError_t e = allow_lds(kern);
         if (e != hipSuccess) return e;
     }
     grid_split(b, kern, kFmThreads, lds, num_cus);
-    hipLaunchKernelGGL((fmag_decode_kernel<D, BF>), dim3((unsigned)(b.n_streams * b.blocks_per_stream)), dim3(kFmThreads),
+    hipLaunchKernelGGL((fmag_decode_kernel<D, BF, PQ>), dim3((unsigned)(b.n_streams * b.blocks_per_stream)), dim3(kFmThreads),
                        lds, s, b);
     return hipGetLastError();
 }
 
+template <int D>
+static hipError_t launch_fdec_d(const FmDecodeArgs& a, bool out_bf16, int num_cus, hipStream_t s) {
+    if (a.t.p <= 8) return out_bf16 ? launch_fdec<D, true, true>(a, num_cus, s) : launch_fdec<D, false, true>(a, num_cus, s);
+    return out_bf16 ? launch_fdec<D, true, false>(a, num_cus, s) : launch_fdec<D, false, false>(a, num_cus, s);
+}
+
 hipError_t launch_fmag_decode(const FmDecodeArgs& a, bool out_bf16, int num_cus, hipStream_t s) {
-    if (a.t.d == 64) return out_bf16 ? launch_fdec<64, true>(a, num_cus, s) : launch_fdec<64, false>(a, num_cus, s);
-    return out_bf16 ? launch_fdec<128, true>(a, num_cus, s) : launch_fdec<128, false>(a, num_cus, s);
+    return a.t.d == 64 ? launch_fdec_d<64>(a, out_bf16, num_cus, s) : launch_fdec_d<128>(a, out_bf16, num_cus, s);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -425,7 +431,7 @@ hipError_t launch_fmag_decode(const FmDecodeArgs& a, bool out_bf16, int num_cus,
 // ---------------------------------------------------------------------------------------------
 constexpr int kFsThreads = 256;
 
-template <int D>
+template <int D, bool PQ>
 __global__ __launch_bounds__(kFsThreads) void fmag_scores_kernel(FmScoresArgs a) {
     constexpr int S = D / 32, QROW = D + 8, NP = (16 * (D / 2) + 63) / 64;
     extern __shared__ __align__(16) uint8_t smem[];
@@ -468,7 +474,7 @@ __global__ __launch_bounds__(kFsThreads) void fmag_scores_kernel(FmScoresArgs a)
 #pragma unroll
         for (int s = 0; s < S; ++s) {
             float x8[8];
-            spectrum8<D>(stage + v * RW, RW, b, p, s, g, cs, x8, es);
+            spectrum8<D, PQ>(stage + v * RW, RW, b, p, s, g, cs, x8, es);
             u32x4 hv;
 #pragma unroll
             for (int i = 0; i < 8; i += 2)
@@ -496,21 +502,26 @@ __global__ __launch_bounds__(kFsThreads) void fmag_scores_kernel(FmScoresArgs a)
     }
 }
 
-hipError_t launch_fmag_scores(const FmScoresArgs& a, int num_cus, hipStream_t s) {
+template <int D, bool PQ>
+static hipError_t launch_fsc(const FmScoresArgs& a, int num_cus, hipStream_t s) {
     FmScoresArgs b = a;
-    const size_t lds = 2048 + (size_t)a.nq_pad * (a.t.d + 8) * 2 + (size_t)a.nq_pad * 4 +
+    const size_t lds = 2048 + (size_t)a.nq_pad * (D + 8) * 2 + (size_t)a.nq_pad * 4 +
                        (size_t)(kFsThreads / 64) * (16 * a.t.rec_words + 2) * 4;
-    const void* kern = a.t.d == 64 ? reinterpret_cast<const void*>(&fmag_scores_kernel<64>)
-                                   : reinterpret_cast<const void*>(&fmag_scores_kernel<128>);
+    const void* kern = reinterpret_cast<const void*>(&fmag_scores_kernel<D, PQ>);
     if (lds > 65536) {
         const hipError_t e = allow_lds(kern);
         if (e != hipSuccess) return e;
     }
     grid_split(b, kern, kFsThreads, lds, num_cus);
-    const dim3 grid((unsigned)(b.n_streams * b.blocks_per_stream));
-    if (a.t.d == 64) hipLaunchKernelGGL((fmag_scores_kernel<64>), grid, dim3(kFsThreads), lds, s, b);
-    else hipLaunchKernelGGL((fmag_scores_kernel<128>), grid, dim3(kFsThreads), lds, s, b);
+    hipLaunchKernelGGL((fmag_scores_kernel<D, PQ>), dim3((unsigned)(b.n_streams * b.blocks_per_stream)),
+                       dim3(kFsThreads), lds, s, b);
     return hipGetLastError();
+}
+
+hipError_t launch_fmag_scores(const FmScoresArgs& a, int num_cus, hipStream_t s) {
+    const bool pq = a.t.p <= 8;
+    if (a.t.d == 64) return pq ? launch_fsc<64, true>(a, num_cus, s) : launch_fsc<64, false>(a, num_cus, s);
+    return pq ? launch_fsc<128, true>(a, num_cus, s) : launch_fsc<128, false>(a, num_cus, s);
 }
 
 }  // namespace tq
