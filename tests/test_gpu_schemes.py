@@ -1,0 +1,109 @@
+"""The [AB] scheme comparison on the structured regimes, run on the HIP path: TQ-KV, Plain-KV,
+SQU-KV (uniform) and SQW-KV (water-filling) at budgets b = 2 and 4, scored by d2 of eq. (2) on the
+attention output ("Ablation, Statistical Inference, and Validation for KV-Cache Compression", §2
+"Error metric"; §8 and its figures for the findings checked here):
+  * heavy tails (Student-t ν = 3): TQ-KV beats SQU-KV (the calibrated basis is misaligned);
+  * on a structured regime at b = 2 SQU-KV beats TQ-KV: here the steep rank-4 spectrum.  On the
+    flat rank-8 subspace with 5 % noise (this build's reading of lowrank_aligned; the pages' regime
+    table is missing) SQU-KV does not win at b = 2, unlike the pages' ranking; the table printed
+    by the fixture records both;
+  * water-filling equals uniform allocation when the semantic variances are within a factor 4
+    (§6), and changes it on the steep rank-4 spectrum;
+  * Plain-KV is comparable to TQ-KV on isotropic data.
+These are measurements with the pages' qualitative claims as bounds, not parity."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import kv_cache_transform_amd as T
+from oracle import tq_oracle as O
+from synth import inputs as I
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+H, N, D, NQ = 4, 2048, 128, 16
+
+
+def _f64(x):
+    return O.bf16_bits_to_f64(I.bf16_bits(x))
+
+
+def _tokens(regime, n, seed, sub):
+    if regime == "isotropic":
+        return I.gaussian((H, n, D), seed, device=DEV)
+    if regime == "fattail":
+        return I.student_t(H, n, D, 3, seed, device=DEV)
+    spec = {"lowrank_aligned": [1.0] * 8, "lowrank_steep": [1.0, 0.5, 0.25, 0.125]}[regime]
+    return I.low_rank(H, n, D, spec, 0.05, seed, sub, n_heads=H, device=DEV)
+
+
+def _d2(That, Tref):
+    r = float(np.sum((That - Tref) ** 2) / np.sum(Tref ** 2))
+    cos = float(np.sum(That * Tref) / (np.linalg.norm(That) * np.linalg.norm(Tref)))
+    return math.hypot(1 - cos, r / (1 + r))
+
+
+def _schemes(regime, b):
+    K, V = _tokens(regime, N, 700, 81), _tokens(regime, N, 701, 82)
+    Kc, Vc = _tokens(regime, 512, 702, 81), _tokens(regime, 512, 703, 82)   # calibration draws
+    q = I.gaussian((1, H * NQ, D), 709, device=DEV)
+    k64, v64, q64 = _f64(K), _f64(V), _f64(q)[0].reshape(H, NQ, D)
+    sc = 1.0 / math.sqrt(D)
+    Tref = np.stack([(lambda s: (np.exp(s - s.max(1, keepdims=True)) / np.exp(s - s.max(1, keepdims=True)).sum(1, keepdims=True)))(q64[h] @ k64[h].T * sc) @ v64[h] for h in range(H)])
+    out = {}
+    for name, rot in (("TQ-KV", 0), ("Plain-KV", 1)):
+        ck, cv = T.Codec(D, b, 0, H, 11, rotation=rot), T.Codec(D, b, 0, H, 12, rotation=rot)
+        o = T.decode_attention(ck, cv, q, T.encode(ck, K), T.encode(cv, V), H, N, out_dtype=torch.float32)
+        out[name] = _d2(o.cpu().numpy()[0].reshape(H, NQ, D), Tref)
+    for name, water in (("SQU-KV", False), ("SQW-KV", True)):
+        ck = T.SQCodec.calibrate(Kc.float(), b, min(2, b), waterfill=water, device=0)
+        cv = T.SQCodec.calibrate(Vc.float(), b, min(2, b), waterfill=water, device=0)
+        o = T.sq_decode_attention(ck, cv, q, ck.encode(K), cv.encode(V), H, N, out_dtype=torch.float32)
+        out[name] = _d2(o.cpu().numpy()[0].reshape(H, NQ, D), Tref)
+        out[name + " bits"] = (ck.bits.copy(), cv.bits.copy(), int(ck.d_eff[0]))
+    return out
+
+
+@pytest.fixture(scope="module")
+def table():
+    assert torch.cuda.is_available(), "GPU tests need an MI355X"
+    res = {(r, b): _schemes(r, b) for r in ("lowrank_aligned", "lowrank_steep", "isotropic", "fattail") for b in (2, 4)}
+    print("\nd2 (eq. 2) of the attention output, 4 heads x 2048 tokens, d = 128, 16 queries per head")
+    print(f"{'regime':16s} {'b':>2s} {'TQ-KV':>8s} {'Plain-KV':>9s} {'SQU-KV':>8s} {'SQW-KV':>8s}  d_eff")
+    for (r, b), v in res.items():
+        print(f"{r:16s} {b:2d} {v['TQ-KV']:8.4f} {v['Plain-KV']:9.4f} {v['SQU-KV']:8.4f} {v['SQW-KV']:8.4f}  "
+              f"{v['SQU-KV bits'][2]}")
+    return res
+
+
+def test_tq_beats_sq_on_heavy_tails(table):
+    for b in (2, 4):
+        assert table[("fattail", b)]["TQ-KV"] < table[("fattail", b)]["SQU-KV"]
+
+
+def test_sq_beats_tq_on_the_steep_low_rank_regime_at_two_bits(table):
+    assert table[("lowrank_steep", 2)]["SQU-KV"] < table[("lowrank_steep", 2)]["TQ-KV"]
+
+
+def test_waterfilling_is_uniform_on_flat_spectra_and_acts_on_the_steep_one(table):
+    for b in (2, 4):
+        v = table[("lowrank_aligned", b)]
+        assert np.array_equal(v["SQU-KV bits"][0], v["SQW-KV bits"][0])
+        assert v["SQU-KV"] == v["SQW-KV"]
+    st = table[("lowrank_steep", 4)]
+    assert not np.array_equal(st["SQU-KV bits"][0], st["SQW-KV bits"][0])
+
+
+def test_water_filling_changes_d2_only_slightly(table):
+    # §6: on the steep spectrum the difference stays within |Δd2| <= 0.030
+    for b in (2, 4):
+        v = table[("lowrank_steep", b)]
+        assert abs(v["SQW-KV"] - v["SQU-KV"]) <= 0.030
+
+
+def test_plain_is_comparable_to_tq_on_isotropic_data(table):
+    for b in (2, 4):
+        v = table[("isotropic", b)]
+        assert 0.7 < v["Plain-KV"] / v["TQ-KV"] < 1.4
