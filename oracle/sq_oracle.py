@@ -34,6 +34,12 @@ Readings where the pages are silent (each listed in the design doc):
     The uniform variant gives every semantic dimension b bits.
   * Records are the fields idx_0 .. idx_{d-1} in basis order, LSB first, at bit offsets
     Σ_{j<k} b_j; a record takes 4·ceil(max over heads of Σ_k b_k / 32) bytes.  No norm is stored.
+  * The selective QJL sketch (SQU-QKV; §2 "SpectralQuant"): S ∈ {±1}^{m x d_eff} per head, entry
+    (i, k) = -1 iff bit 63 of SplitMix64 word i·d + k of tag 4 (the first d_eff columns of an m x d
+    table); e_z = z - ẑ over the semantic dimensions; sketch bit i = [(S e_z)_i >= 0]; ||e_z|| is stored
+    as fp16.  The score adds sqrt(pi/2)/m · ||e_z|| · <S q_Z, 2σ - 1> with q_Z the semantic part of Uᵀq.
+    A record with a sketch holds the index fields, then the m sketch bits, then the fp16 norm,
+    padded to 4·ceil((max Σ_k b_k + m + 16)/32) bytes.
 """
 from __future__ import annotations
 
@@ -43,8 +49,11 @@ import math
 import numpy as np
 from scipy import special
 
+from oracle import tq_oracle as _T
+
 B_MAX = 8
 LAMBDA_FLOOR = 1e-12
+TAG_SQ_SKETCH = 4
 
 
 # ----------------------------------------------------------------------------------------------
@@ -194,6 +203,21 @@ def calibrate(x_cal: np.ndarray, b: int, b_tail: int, water: bool = False, gamma
     return {"U": U, "lam": lam, "sigma": np.sqrt(lam_c), "bits": bits, "d_eff": d_eff}
 
 
+def sketch_matrix(seed: int, head: int, m: int, d: int) -> np.ndarray:
+    """The m x d table of ±1 whose first d_eff columns are the selective QJL sketch of one head."""
+    w = _T.words(_T.stream_key(seed, TAG_SQ_SKETCH, head), m * d)
+    return np.where((w >> np.uint64(63)) == 1, -1.0, 1.0).reshape(m, d)
+
+
+def with_sketch(model: dict, m: int, seed: int, head: int) -> dict:
+    """The model with the selective QJL sketch of m rows on its semantic dimensions."""
+    out = dict(model)
+    d = model["U"].shape[0]
+    out["m"] = m
+    out["S"] = sketch_matrix(seed, head, m, d)[:, : model["d_eff"]]
+    return out
+
+
 def storage_bits(d: int, d_eff: int, b_sem: int, b_tail: int) -> int:
     """Bits per token of the uniform scheme ([AB] §3.2)."""
     return b_sem * d_eff + b_tail * (d - d_eff)
@@ -209,7 +233,8 @@ def project(x: np.ndarray, model: dict) -> np.ndarray:
 
 
 def encode(x: np.ndarray, model: dict) -> dict:
-    """Per token: z = Uᵀx, u_k = z_k/σ_k, idx_k = #{thresholds of the b_k-bit codebook <= u_k}."""
+    """Per token: z = Uᵀx, u_k = z_k/σ_k, idx_k = #{thresholds of the b_k-bit codebook <= u_k}; with
+    a sketch also e_z, its sketch values S e_z, the bits σ and the fp16 norm r16."""
     z = project(x, model)
     u = z / model["sigma"]
     idx = np.zeros(u.shape, dtype=np.int64)
@@ -217,7 +242,19 @@ def encode(x: np.ndarray, model: dict) -> dict:
         cols = model["bits"] == w
         t, _ = gauss_lloyd_max(int(w))
         idx[:, cols] = np.sum(u[:, cols, None] >= t[None, None, :], axis=2)
-    return {"z": z, "u": u, "idx": idx}
+    out = {"z": z, "u": u, "idx": idx}
+    if model.get("m"):
+        out.update(sketch_of(z, idx, model))
+    return out
+
+
+def sketch_of(z: np.ndarray, idx: np.ndarray, model: dict) -> dict:
+    """The selective QJL sketch of tokens with projections z and indices idx."""
+    de = model["d_eff"]
+    e = z[:, :de] - dequantise(idx, model)[:, :de]
+    zs = e @ model["S"].T
+    return {"e": e, "zs": zs, "sigma_bits": (zs >= 0).astype(np.int64),
+            "r16": _T.fp16_rne(np.linalg.norm(e, axis=1))}
 
 
 def dequantise(idx: np.ndarray, model: dict) -> np.ndarray:
@@ -245,10 +282,16 @@ def boundary_distance(u: np.ndarray, model: dict) -> np.ndarray:
     return out
 
 
-def scores(q: np.ndarray, idx: np.ndarray, model: dict) -> np.ndarray:
-    """ŝ[i, t] = <Uᵀq_i, ẑ_t> ([AB] §2 "SpectralQuant" with the tail included)."""
+def scores(q: np.ndarray, idx: np.ndarray, model: dict, sigma_bits=None, r16=None) -> np.ndarray:
+    """ŝ[i, t] = <Uᵀq_i, ẑ_t> ([AB] §2 "SpectralQuant" with the tail included), plus with a sketch
+    sqrt(pi/2)/m · r16_t · <S q_Z, 2σ_t - 1>."""
     qz = np.asarray(q, dtype=np.float64) @ model["U"]
-    return qz @ dequantise(idx, model).T
+    out = qz @ dequantise(idx, model).T
+    if model.get("m"):
+        p = qz[:, : model["d_eff"]] @ model["S"].T
+        pm = 2.0 * np.asarray(sigma_bits, dtype=np.float64) - 1.0
+        out = out + math.sqrt(math.pi / 2) / model["m"] * (p @ pm.T) * np.asarray(r16, dtype=np.float64)[None, :]
+    return out
 
 
 def attention(score_est: np.ndarray, idx_v: np.ndarray, model_v: dict, scale: float) -> np.ndarray:
@@ -264,13 +307,15 @@ def attention(score_est: np.ndarray, idx_v: np.ndarray, model_v: dict, scale: fl
 # Packed records
 # ----------------------------------------------------------------------------------------------
 
-def record_bytes(bits_per_head: list) -> int:
-    """4·ceil(max_h Σ_k b_k / 32)."""
-    return 4 * ((max(int(np.sum(bh)) for bh in bits_per_head) + 31) // 32)
+def record_bytes(bits_per_head: list, m: int = 0) -> int:
+    """4·ceil(max_h Σ_k b_k / 32), or 4·ceil((max_h Σ_k b_k + m + 16)/32) with an m-bit sketch."""
+    extra = m + 16 if m else 0
+    return 4 * ((max(int(np.sum(bh)) for bh in bits_per_head) + extra + 31) // 32)
 
 
-def pack(idx: np.ndarray, bits: np.ndarray, rec_bytes: int) -> np.ndarray:
-    """Rows of indices -> uint8 records, field k LSB first at bit Σ_{j<k} b_j."""
+def pack(idx: np.ndarray, bits: np.ndarray, rec_bytes: int, sigma_bits=None, r16=None) -> np.ndarray:
+    """Rows of indices -> uint8 records, field k LSB first at bit Σ_{j<k} b_j; then the sketch bits
+    and the fp16 norm when given."""
     n, d = idx.shape
     out = np.zeros((n, rec_bytes * 8), dtype=np.uint8)
     pos = 0
@@ -278,11 +323,17 @@ def pack(idx: np.ndarray, bits: np.ndarray, rec_bytes: int) -> np.ndarray:
         for i in range(int(bits[k])):
             out[:, pos + i] = (idx[:, k] >> i) & 1
         pos += int(bits[k])
+    if sigma_bits is not None:
+        m = sigma_bits.shape[1]
+        out[:, pos:pos + m] = sigma_bits
+        h = np.asarray(r16, dtype=np.float16).view(np.uint16).astype(np.int64)
+        for i in range(16):
+            out[:, pos + m + i] = (h >> i) & 1
     return np.packbits(out, axis=1, bitorder="little")
 
 
-def unpack(rec: np.ndarray, bits: np.ndarray) -> np.ndarray:
-    """uint8 records -> indices (inverse of ``pack``)."""
+def unpack(rec: np.ndarray, bits: np.ndarray, m: int = 0):
+    """uint8 records -> indices (inverse of ``pack``); with m > 0 also (sketch bits, r16)."""
     allbits = np.unpackbits(np.asarray(rec, dtype=np.uint8), axis=1, bitorder="little").astype(np.int64)
     d = len(bits)
     idx = np.zeros((rec.shape[0], d), dtype=np.int64)
@@ -291,4 +342,10 @@ def unpack(rec: np.ndarray, bits: np.ndarray) -> np.ndarray:
         for i in range(int(bits[k])):
             idx[:, k] |= allbits[:, pos + i] << i
         pos += int(bits[k])
-    return idx
+    if not m:
+        return idx
+    sig = allbits[:, pos:pos + m].copy()
+    h = np.zeros(rec.shape[0], dtype=np.int64)
+    for i in range(16):
+        h |= allbits[:, pos + m + i] << i
+    return idx, sig, h.astype(np.uint16).view(np.float16).astype(np.float64)

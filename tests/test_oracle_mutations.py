@@ -259,3 +259,25 @@ def test_fmag_phase_truncated_instead_of_rounded_is_caught(monkeypatch):
 def test_fmag_inverse_without_the_half_spectrum_weights_is_caught(monkeypatch):
     monkeypatch.setattr(FM, "irfft", lambda X, d: np.fft.ifft(np.concatenate([X, np.zeros((X.shape[0], d - X.shape[1]))], axis=1), n=d).real)
     _fails(FP.test_transform_is_the_written_out_dft_and_its_real_inverse, 16)
+
+
+def test_sq_sketch_with_the_residual_sign_flipped_is_caught(monkeypatch):
+    real = SQ.sketch_of
+    def sketch_of(z, idx, model):
+        r = real(z, idx, model)
+        r["sigma_bits"] = 1 - r["sigma_bits"]
+        return r
+    monkeypatch.setattr(SQ, "sketch_of", sketch_of)
+    _fails(SP.test_sketch_bits_and_norm_written_out)
+
+
+def test_sq_correction_without_the_sqrt_is_caught(monkeypatch):
+    real = SQ.scores
+    def scores(q, idx, model, sigma_bits=None, r16=None):
+        out = real(q, idx, model, sigma_bits, r16)
+        if model.get("m"):
+            base = real(q, idx, {k: v for k, v in model.items() if k != "m"})
+            out = base + (out - base) * math.sqrt(2 / math.pi) * (math.pi / 2)
+        return out
+    monkeypatch.setattr(SQ, "scores", scores)
+    _fails(SP.test_selective_qjl_estimate_is_close_to_unbiased)

@@ -235,3 +235,70 @@ def test_index_counts_thresholds_with_ties_to_the_upper_cell():
             assert np.array_equal(idx, expect)
             pos = np.searchsorted(t, sel)
             assert np.array_equal(idx, pos + 1 if want is None else pos)
+
+
+# ---- the selective QJL sketch (SQU-QKV) --------------------------------------------------------
+
+def _sq_model_with_sketch(d=64, d_eff=16, m=32, seed=5, head=1, rng_seed=3):
+    rng = np.random.default_rng(rng_seed)
+    lam = np.concatenate((np.linspace(3.2, 2.8, d_eff), np.full(d - d_eff, 0.05)))
+    x = _gaussian_data(rng, lam, 3000)
+    model = Q.calibrate(x[:2000], 3, 2, gamma=0.0, d_eff_max=d_eff)
+    assert model["d_eff"] == d_eff
+    return Q.with_sketch(model, m, seed, head), x[2000:]
+
+
+def test_sketch_matrix_definition():
+    from oracle import tq_oracle as O
+    S = Q.sketch_matrix(77, 3, 16, 64)
+    assert S.shape == (16, 64) and set(np.unique(S)) == {-1.0, 1.0}
+    w = O.words(O.stream_key(77, 4, 3), 16 * 64)
+    assert S[2, 5] == (-1.0 if int(w[2 * 64 + 5]) >> 63 else 1.0)
+    assert abs(S.mean()) < 0.1
+    assert not np.array_equal(S[0], O.head_signs(77, 3, 64))       # a different tag
+    model, _ = _sq_model_with_sketch()
+    assert np.array_equal(model["S"], Q.sketch_matrix(5, 1, 32, 64)[:, :16])
+
+
+def test_sketch_bits_and_norm_written_out():
+    model, x = _sq_model_with_sketch()
+    r = Q.encode(x[:5], model)
+    zh = Q.dequantise(r["idx"], model)
+    for t in range(5):
+        e = [r["z"][t, k] - zh[t, k] for k in range(16)]
+        for i in range(32):
+            zi = sum(model["S"][i, k] * e[k] for k in range(16))
+            assert r["sigma_bits"][t, i] == (1 if zi >= 0 else 0)
+        assert r["r16"][t] == np.float16(math.sqrt(sum(v * v for v in e)))
+
+
+def test_selective_qjl_estimate_is_close_to_unbiased():
+    # over random ±1 sketches the correction estimates <q_Z, e_z> on the semantic dimensions (exactly
+    # so for Gaussian sketches; a ±1 sketch on 32 dimensions is within a few per cent)
+    model, x = _sq_model_with_sketch(d_eff=32, m=64)
+    q = np.random.default_rng(8).standard_normal((1, 64))
+    r0 = Q.encode(x[:1], model)
+    target = float((q @ model["U"])[0, :32] @ r0["e"][0])
+    nosk = {k: v for k, v in model.items() if k not in ("m", "S")}
+    base = Q.scores(q, r0["idx"], nosk)[0, 0]
+    est = []
+    for seed in range(20000):
+        ms = Q.with_sketch(model, 64, 1000 + seed, 0)
+        sk = Q.sketch_of(r0["z"], r0["idx"], ms)
+        est.append(Q.scores(q, r0["idx"], ms, sk["sigma_bits"], sk["r16"])[0, 0] - base)
+    est = np.array(est)
+    se = est.std() / math.sqrt(len(est))
+    assert abs(est.mean() - target) < 3 * se + 0.03 * abs(target), (est.mean(), target, se)
+
+
+def test_sketch_records_round_trip_and_m0_is_unchanged():
+    model, x = _sq_model_with_sketch()
+    r = Q.encode(x[:40], model)
+    rb = Q.record_bytes([model["bits"]], 32)
+    assert rb == 4 * ((int(model["bits"].sum()) + 32 + 16 + 31) // 32)
+    rec = Q.pack(r["idx"], model["bits"], rb, r["sigma_bits"], r["r16"])
+    idx, sig, r16 = Q.unpack(rec, model["bits"], 32)
+    assert np.array_equal(idx, r["idx"]) and np.array_equal(sig, r["sigma_bits"]) and np.array_equal(r16, r["r16"])
+    plain = dict(model)
+    plain["m"] = 0
+    assert np.array_equal(Q.scores(x[:3], r["idx"], plain), Q.scores(x[:3], r["idx"], {k: v for k, v in model.items() if k not in ("m", "S")}))
