@@ -19,7 +19,8 @@
  *   - Water-filling is greedy one bit at a time to the largest λ_k 4^(-b_k) below 8 bits, ties to the
  *     fewer bits, then the lower k.  round() is round-half-up.  d_eff >= 1.
  *   - A record is the fields idx_0 .. idx_{d-1} in basis order, LSB first at bit offsets Σ_{j<k} b_j,
- *     padded to 4·ceil(max over heads of Σ_k b_k / 32) bytes.  No norm is stored.
+ *     then (with a sketch) the m sketch bits and the fp16 norm, padded to 4·ceil((max over heads of
+ *     Σ_k b_k + [m + 16]) / 32) bytes.  No vector norm is stored.
  *   - The model of stream st is head st % n_heads.
  *
  * Packed tensor: one caller-allocated device buffer of n_streams·n_tokens records [stream][token],
@@ -45,6 +46,9 @@ typedef struct {
     int32_t waterfill; /* 0: every semantic dimension gets b bits (uniform); 1: greedy water-filling */
     int32_t d_eff_max; /* cap on d_eff (the known rank); 0 = none */
     double gamma;      /* spectral-gap threshold; <= 0 disables the criterion (the pages use 10) */
+    int32_t m;         /* rows of the selective QJL sketch on the semantic dimensions (SQU-QKV): 0 (none),
+                          16, 32, 48 or 64; needs d_eff <= 32 in every head */
+    uint64_t seed;     /* keys the ±1 sketch (SplitMix64 tag 4, as tq.h's generator) */
 } tq_sq_params;
 
 /* Calibrate one model per head on the host (no GPU call).
@@ -61,12 +65,19 @@ typedef struct tq_sq_codec tq_sq_codec;
 
 /* Build a codec's device tables on the current device from a model (normally the output of
  * tq_sq_calibrate; host arrays in the same layout; p->b, b_tail, waterfill, gamma and d_eff_max are
- * not used here).  TQ_EINVAL for d not in {64, 128}, bits outside 1..8, a non-finite basis entry or
- * lambda, or a NULL pointer (eigenvalues below 1e-12·λ_1, rounding-level negatives included, are
+ * not used here).  With p->m > 0 the records also carry the selective QJL sketch ("Ablation,
+ * Statistical Inference, and Validation for KV-Cache Compression", §2 "SpectralQuant", SQU-QKV): for
+ * the residual e_z = z - ẑ on the first d_eff[h] dimensions, the m sign bits σ of S e_z with
+ * S[i][k] = -1 iff bit 63 of word i·d + k of the (p->seed, tag 4, head) SplitMix64 stream, then
+ * ||e_z|| rounded to fp16; the scores and the attention add sqrt(pi/2)/m · ||e_z|| · <S q_Z, 2σ - 1>
+ * (q_Z the query's first d_eff coordinates in the basis).  d_eff ([n_heads]) may be NULL when
+ * p->m = 0.  TQ_EUNSUPPORTED for a sketch with some d_eff[h] > 32.  TQ_EINVAL for d not in {64, 128},
+ * bits outside 1..8, m not in {0, 16, 32, 48, 64}, d_eff[h] outside 1..d, a non-finite basis entry
+ * or lambda, or a NULL pointer (eigenvalues below 1e-12·λ_1, rounding-level negatives included, are
  * floored there); TQ_EHIP if the upload fails.  *out is set only on success.  The encode, decode
  * and scores calls return TQ_EINVAL unless that device is current. */
 int tq_sq_create(const tq_sq_params* p, const double* basis, const double* lambda, const int32_t* bits,
-                 tq_sq_codec** out);
+                 const int32_t* d_eff, tq_sq_codec** out);
 
 /* Free the codec's device tables.  No work using it may be pending.  NULL is a no-op. */
 void tq_sq_destroy(tq_sq_codec* codec);

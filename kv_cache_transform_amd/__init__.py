@@ -159,22 +159,25 @@ class SQCodec:
     dimensions at b bits (or water-filled), the tail at b_tail bits, per-dimension Gaussian
     Lloyd-Max codebooks ("Ablation, Statistical Inference, and Validation for KV-Cache
     Compression", §2 "SpectralQuant", §6, §7).  Build with ``SQCodec.calibrate``; the device tables
-    live on the device that was current then and are freed with the object."""
+    live on the device that was current then and are freed with the object.  m > 0 adds the
+    selective QJL sketch of the semantic residual (SQU-QKV), keyed by ``seed``; it needs d_eff."""
 
-    def __init__(self, d: int, n_heads: int, basis, lam, bits, d_eff=None, device=None):
+    def __init__(self, d: int, n_heads: int, basis, lam, bits, d_eff=None, device=None, m: int = 0,
+                 seed: int = 0):
         import numpy as np
-        self.d, self.n_heads = int(d), int(n_heads)
+        self.d, self.n_heads, self.m, self.seed = int(d), int(n_heads), int(m), int(seed)
         self.basis = np.ascontiguousarray(basis, dtype=np.float64).reshape(n_heads, d, d)
         self.lam = np.ascontiguousarray(lam, dtype=np.float64).reshape(n_heads, d)
         self.bits = np.ascontiguousarray(bits, dtype=np.int32).reshape(n_heads, d)
-        self.d_eff = None if d_eff is None else np.asarray(d_eff, dtype=np.int32)
+        self.d_eff = None if d_eff is None else np.ascontiguousarray(d_eff, dtype=np.int32).reshape(n_heads)
         self._h = None
-        p = _lib.SqParams(self.d, self.n_heads, 1, 1, 0, 0, 0.0)
+        p = _lib.SqParams(self.d, self.n_heads, 1, 1, 0, 0, 0.0, self.m, self.seed)
         h = ctypes.c_void_p()
+        de = self.d_eff.ctypes.data if self.d_eff is not None else None
         with torch.cuda.device(device if device is not None else torch.cuda.current_device()):
             self.device = torch.cuda.current_device()
             _lib.check(_lib.lib().tq_sq_create(ctypes.byref(p), self.basis.ctypes.data, self.lam.ctypes.data,
-                                               self.bits.ctypes.data, ctypes.byref(h)), "tq_sq_create")
+                                               self.bits.ctypes.data, de, ctypes.byref(h)), "tq_sq_create")
         self._h = h
         rb = ctypes.c_int64()
         _lib.check(_lib.lib().tq_sq_record_bytes(self._h, ctypes.byref(rb)), "tq_sq_record_bytes")
@@ -188,7 +191,7 @@ class SQCodec:
         x = x_cal.detach().float().cpu().numpy() if isinstance(x_cal, torch.Tensor) else np.asarray(x_cal)
         x = np.ascontiguousarray(x, dtype=np.float32)
         H, n_cal, d = x.shape
-        p = _lib.SqParams(d, H, b, b_tail, int(bool(waterfill)), d_eff_max, float(gamma))
+        p = _lib.SqParams(d, H, b, b_tail, int(bool(waterfill)), d_eff_max, float(gamma), 0, 0)
         basis = np.zeros((H, d, d), dtype=np.float64)
         lam = np.zeros((H, d), dtype=np.float64)
         bits = np.zeros((H, d), dtype=np.int32)
@@ -200,10 +203,10 @@ class SQCodec:
 
     @classmethod
     def calibrate(cls, x_cal, b: int, b_tail: int, waterfill: bool = False, gamma: float = 10.0,
-                  d_eff_max: int = 0, device=None) -> "SQCodec":
-        m = cls.calibrate_host(x_cal, b, b_tail, waterfill, gamma, d_eff_max)
-        H, d = m["lam"].shape
-        return cls(d, H, m["basis"], m["lam"], m["bits"], m["d_eff"], device)
+                  d_eff_max: int = 0, device=None, m: int = 0, seed: int = 0) -> "SQCodec":
+        md = cls.calibrate_host(x_cal, b, b_tail, waterfill, gamma, d_eff_max)
+        H, d = md["lam"].shape
+        return cls(d, H, md["basis"], md["lam"], md["bits"], md["d_eff"], device, m, seed)
 
     def __del__(self):
         h, self._h = getattr(self, "_h", None), None

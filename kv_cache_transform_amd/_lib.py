@@ -38,7 +38,7 @@ class Params(ctypes.Structure):
 class SqParams(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("n_heads", ctypes.c_int32), ("b", ctypes.c_int32),
                 ("b_tail", ctypes.c_int32), ("waterfill", ctypes.c_int32), ("d_eff_max", ctypes.c_int32),
-                ("gamma", ctypes.c_double)]
+                ("gamma", ctypes.c_double), ("m", ctypes.c_int32), ("seed", ctypes.c_uint64)]
 
 
 class FmagParams(ctypes.Structure):
@@ -87,7 +87,7 @@ def lib() -> ctypes.CDLL:
         "tq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "tq_clear_cache": (None, []),
         "tq_sq_calibrate": (ctypes.c_int, [Q, VP, I64, VP, VP, VP, VP]),
-        "tq_sq_create": (ctypes.c_int, [Q, VP, VP, VP, ctypes.POINTER(VP)]),
+        "tq_sq_create": (ctypes.c_int, [Q, VP, VP, VP, VP, ctypes.POINTER(VP)]),
         "tq_sq_destroy": (None, [VP]),
         "tq_sq_record_bytes": (ctypes.c_int, [VP, ctypes.POINTER(I64)]),
         "tq_sq_encode": (ctypes.c_int, [VP, VP, ctypes.c_int, I64, I64, VP, VP]),

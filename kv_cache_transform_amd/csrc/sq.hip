@@ -69,6 +69,12 @@ __device__ __forceinline__ void fetch_words(const uint32_t* src, int count, int 
     }
 }
 
+// `width` (1..31) bits from bit `pos` of a record in LDS (reads the word after the one holding pos)
+__device__ __forceinline__ uint32_t get_bits_at(const uint32_t* rec, uint32_t pos, uint32_t width) {
+    const uint32_t* w = rec + (pos >> 5);
+    return __builtin_amdgcn_ubfe(__builtin_amdgcn_alignbit(w[1], w[0], pos & 31u), 0, width);
+}
+
 // the lane's 8 fields of one k-step: the 64 bits from bit r0 of record word w0 hold them all; each
 // comes out as its row index width·256 + value of the [width][256] codebook tables
 __device__ __forceinline__ void fields8(const uint32_t* rec, const uint4& fd, uint32_t (&ix)[8]) {
@@ -123,7 +129,8 @@ void split_grid(Args& b, const void* kern, int threads, size_t lds, int num_cus)
 // ---------------------------------------------------------------------------------------------
 constexpr int kEncThreads = 512;
 
-template <int D, int NG>
+// SK: the codec carries the selective sketch (compiled apart so that the plain path keeps its registers)
+template <int D, int NG, bool SK>
 __global__ __launch_bounds__(kEncThreads, 1) void sq_encode_kernel(SqEncodeArgs a) {
     constexpr int T = D / 16, S = D / 32;
     extern __shared__ __align__(16) uint8_t smem[];
@@ -139,12 +146,32 @@ __global__ __launch_bounds__(kEncThreads, 1) void sq_encode_kernel(SqEncodeArgs 
     uint32_t* stage = reinterpret_cast<uint32_t*>(smem + (size_t)2 * T * S * 1024 +
                                                   (size_t)((a.t.lds_grid_words + 3) / 4) * 16) +
                       wave * WS;
+    // with the selective sketch: after all waves' records, a 16 x 32-word transposition buffer per
+    // wave, then the ±1 sketch tiles of this head
+    const int M = SK ? a.t.m : 0;
+    uint32_t* tbuf = reinterpret_cast<uint32_t*>(smem + (size_t)2 * T * S * 1024 +
+                                                 (size_t)((a.t.lds_grid_words + 3) / 4) * 16) +
+                     (kEncThreads / 64) * WS + wave * 512;
+    u32x4* skt = reinterpret_cast<u32x4*>(reinterpret_cast<uint32_t*>(smem + (size_t)2 * T * S * 1024 +
+                                                                      (size_t)((a.t.lds_grid_words + 3) / 4) * 16) +
+                                          (kEncThreads / 64) * (WS + 512));
     {
         const u32x4* src = reinterpret_cast<const u32x4*>(a.t.enc_b) + (size_t)head * 2 * T * S * 64;
         for (int i = threadIdx.x; i < 2 * T * S * 64; i += kEncThreads) Bt[i] = src[i];
         uint32_t* gw = reinterpret_cast<uint32_t*>(grid);
         for (int i = threadIdx.x; i < a.t.lds_grid_words; i += kEncThreads) gw[i] = a.t.grids[i];
         for (int i = lane; i < WS; i += 64) stage[i] = 0u;
+        if (M > 0) {
+            const u32x4* ks = reinterpret_cast<const u32x4*>(a.t.sk_b) + (size_t)head * (M / 16) * 64;
+            for (int i = threadIdx.x; i < (M / 16) * 64; i += kEncThreads) skt[i] = ks[i];
+        }
+    }
+    const int deff = M > 0 ? a.t.deff[head] : 0;
+    const uint32_t skoff = M > 0 ? (uint32_t)a.t.sk_off[head] : 0u;
+    float sgk[2] = {0.0f, 0.0f};
+    if (M > 0) {
+        sgk[0] = a.t.sigma[(size_t)head * D + n];
+        sgk[1] = a.t.sigma[(size_t)head * D + 16 + n];
     }
     float mul[T], add[T];
     uint32_t meta[T], meta2[T];
@@ -238,6 +265,7 @@ __global__ __launch_bounds__(kEncThreads, 1) void sq_encode_kernel(SqEncodeArgs 
             int scr[4];
 #pragma unroll
             for (int r = 0; r < 4; ++r) scr[r] = __shfl(sc[q], 4 * g + r);
+            uint32_t ik[2][4];   // the indices of dimensions n and 16 + n (the sketch's residual)
 #pragma unroll
             for (int t = 0; t < T; ++t) {
                 const uint32_t goff = meta[t] & 0xffffu, qrel = meta2[t] & 0xffu;
@@ -248,8 +276,10 @@ __global__ __launch_bounds__(kEncThreads, 1) void sq_encode_kernel(SqEncodeArgs 
                     const float ug = fmaf(z, mul[t], add[t]);
                     const int cell = (int)__builtin_amdgcn_fmed3f(ug, 0.0f, 2.0f * add[t]);
                     const uint2 e = grid[goff + cell];
+                    const uint32_t ix = e.y + (ug >= u2f(e.x) ? 1u : 0u);
+                    if (t < 2) ik[t][r] = ix;
                     // the 4 neighbouring dimensions 4q..4q+3 (the lanes of one quad) OR-ed together
-                    val[r] = quad_or((e.y + (ug >= u2f(e.x) ? 1u : 0u)) << qrel);
+                    val[r] = quad_or(ix << qrel);
                 }
                 // the quad's first lane ORs the group's bits into its record (two words; the second
                 // is zero unless the group straddles them)
@@ -265,6 +295,81 @@ __global__ __launch_bounds__(kEncThreads, 1) void sq_encode_kernel(SqEncodeArgs 
                 }
 
             }
+            if (M > 0) {
+                // selective QJL sketch: e = z - σ c[idx] on the semantic dimensions (all among the
+                // first 32, which lanes n hold in tiles 0 and 1), its norm over the 16-lane row, then
+                // S e on MFMA after a transposition through LDS into the vectors' operand layout
+                float ev[2][4], r2[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+                    const uint32_t wid = meta[t] >> 26;
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const float z = __builtin_amdgcn_ldexpf(acc[q][t][r], -(8 + scr[r]));
+                        const float c = a.t.cent32[(wid << 8) | ik[t][r]];
+                        const float e = (16 * t + n < deff) ? fmaf(-sgk[t], c, z) : 0.0f;
+                        ev[t][r] = e;
+                        r2[r] = fmaf(e, e, r2[r]);
+                    }
+                }
+                float nrm[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    float v = r2[r];
+                    v += u2f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)f2u(v), 0xb1, 0xf, 0xf, false));
+                    v += u2f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)f2u(v), 0x4e, 0xf, 0xf, false));
+                    v += u2f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)f2u(v), 0x141, 0xf, 0xf, false));
+                    v += u2f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)f2u(v), 0x140, 0xf, 0xf, false));
+                    nrm[r] = sqrtf(v);
+                    const int es = nrm[r] > 0.0f ? 141 - (int)((f2u(nrm[r]) >> 23) & 0xffu) : 0;
+#pragma unroll
+                    for (int t = 0; t < 2; ++t) {
+                        const float x = __builtin_amdgcn_ldexpf(ev[t][r], es);
+                        const _Float16 hi = (_Float16)x, lo = (_Float16)(x - (float)hi);
+                        tbuf[(4 * g + r) * 32 + 16 * t + n] =
+                            (uint32_t)__builtin_bit_cast(uint16_t, hi) | ((uint32_t)__builtin_bit_cast(uint16_t, lo) << 16);
+                    }
+                }
+                // operand layout: lane (n, g) takes dimensions 8g..8g+7 of vector n
+                const u32x4 w0 = reinterpret_cast<const u32x4*>(tbuf)[(n * 32 + 8 * g) / 4];
+                const u32x4 w1 = reinterpret_cast<const u32x4*>(tbuf)[(n * 32 + 8 * g) / 4 + 1];
+                u32x4 hv, lv;
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    hv[i] = __builtin_amdgcn_perm(w0[2 * i + 1], w0[2 * i], 0x05040100u);
+                    lv[i] = __builtin_amdgcn_perm(w0[2 * i + 1], w0[2 * i], 0x07060302u);
+                    hv[2 + i] = __builtin_amdgcn_perm(w1[2 * i + 1], w1[2 * i], 0x05040100u);
+                    lv[2 + i] = __builtin_amdgcn_perm(w1[2 * i + 1], w1[2 * i], 0x07060302u);
+                }
+                for (int ts = 0; ts < M / 16; ++ts) {
+                    const half8 sb = as_half8(skt[ts * 64 + lane]);
+                    floatx4 zs = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(hv), sb, floatx4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                    zs = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(lv), sb, zs, 0, 0, 0);
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const uint64_t mask = __ballot(zs[r] >= 0.0f);   // lane (row n, g) -> bit 16g + n
+                        if (n == 0) {
+                            const uint32_t bits16 = (uint32_t)(mask >> (16 * g)) & 0xffffu;
+                            const uint32_t pos = skoff + 16u * ts;
+                            const uint64_t v64 = (uint64_t)bits16 << (pos & 31u);
+                            uint32_t* rec = stage + (4 * g + r) * RW + (pos >> 5);
+                            atomicOr(rec, (uint32_t)v64);
+                            atomicOr(rec + 1, (uint32_t)(v64 >> 32));
+                        }
+                    }
+                }
+                if (n == 0) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const uint32_t h = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)nrm[r]);
+                        const uint32_t pos = skoff + (uint32_t)M;
+                        const uint64_t v64 = (uint64_t)h << (pos & 31u);
+                        uint32_t* rec = stage + (4 * g + r) * RW + (pos >> 5);
+                        atomicOr(rec, (uint32_t)v64);
+                        atomicOr(rec + 1, (uint32_t)(v64 >> 32));
+                    }
+                }
+            }
             // the wave's 16 records, written out linearly and the staging cleared
             const int64_t valid = min((int64_t)16, a.n_tokens - tq_ * 16);
             uint32_t* dst = os + (size_t)tq_ * 16 * RW;
@@ -277,26 +382,28 @@ __global__ __launch_bounds__(kEncThreads, 1) void sq_encode_kernel(SqEncodeArgs 
     }
 }
 
-template <int D>
+template <int D, bool SK>
 static hipError_t launch_enc(const SqEncodeArgs& a, int num_cus, hipStream_t s) {
     constexpr int NG = 2;
     SqEncodeArgs b = a;
     const size_t lds = (size_t)2 * (D / 16) * (D / 32) * 1024 + (size_t)((a.t.lds_grid_words + 3) / 4) * 16 +
-                       (size_t)(kEncThreads / 64) * (16 * a.t.rec_words + 1) * 4;
+                       (size_t)(kEncThreads / 64) * (16 * a.t.rec_words + 1) * 4 +
+                       (a.t.m > 0 ? (size_t)(kEncThreads / 64) * 512 * 4 + (size_t)(a.t.m / 16) * 1024 : 0);
     if (lds > kLdsMax) return hipErrorInvalidValue;
-    const void* kern = reinterpret_cast<const void*>(&sq_encode_kernel<D, NG>);
+    const void* kern = reinterpret_cast<const void*>(&sq_encode_kernel<D, NG, SK>);
     if (lds > 65536) {
         const hipError_t e = raise_lds(kern);
         if (e != hipSuccess) return e;
     }
     split_grid(b, kern, kEncThreads, lds, num_cus);
-    hipLaunchKernelGGL((sq_encode_kernel<D, NG>), dim3((unsigned)(b.n_streams * b.blocks_per_stream)),
+    hipLaunchKernelGGL((sq_encode_kernel<D, NG, SK>), dim3((unsigned)(b.n_streams * b.blocks_per_stream)),
                        dim3(kEncThreads), lds, s, b);
     return hipGetLastError();
 }
 
 hipError_t launch_sq_encode(const SqEncodeArgs& a, int num_cus, hipStream_t s) {
-    return a.t.d == 64 ? launch_enc<64>(a, num_cus, s) : launch_enc<128>(a, num_cus, s);
+    if (a.t.m > 0) return a.t.d == 64 ? launch_enc<64, true>(a, num_cus, s) : launch_enc<128, true>(a, num_cus, s);
+    return a.t.d == 64 ? launch_enc<64, false>(a, num_cus, s) : launch_enc<128, false>(a, num_cus, s);
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -336,7 +443,7 @@ __global__ __launch_bounds__(kDecThreads, 1) void sq_decode_kernel(SqDecodeArgs 
     const uint32_t* is = a.in + (size_t)st * a.n_tokens * RW;
 
     // records of the next NG tiles are fetched into registers one iteration ahead
-    constexpr int NP = (16 * (D / 4) + 63) / 64;        // words per tile: 16 records of at most D/4 words
+    constexpr int NP = (16 * (D / 4 + 3) + 63) / 64;    // words per tile: 16 records of at most D/4 + 3 words
     uint32_t pre[NG][NP];
     auto fetch = [&](int64_t tile0) {
 #pragma unroll
@@ -453,9 +560,9 @@ __global__ __launch_bounds__(D) void sq_qprep_kernel(SqScoresArgs a) {
     qs[k] = qv;
     __syncthreads();
     const float* U = a.t.U32 + (size_t)head * D * D;
-    float acc = 0.0f;
-    for (int j = 0; j < D; ++j) acc = fmaf(U[(size_t)j * D + k], qs[j], acc);
-    acc *= a.t.sigma[(size_t)head * D + k] * a.qmul;
+    float raw = 0.0f;
+    for (int j = 0; j < D; ++j) raw = fmaf(U[(size_t)j * D + k], qs[j], raw);
+    const float acc = raw * a.t.sigma[(size_t)head * D + k] * a.qmul;
     float m = fabsf(acc);
     for (int o = 32; o > 0; o >>= 1) m = fmaxf(m, __shfl_xor(m, o));
     if ((k & 63) == 0) red[k >> 6] = m;
@@ -465,6 +572,23 @@ __global__ __launch_bounds__(D) void sq_qprep_kernel(SqScoresArgs a) {
     const int e = m > 0.0f ? 13 - ((int)((f2u(m) >> 23) & 0xffu) - 127) : 0;
     a.qp[(size_t)row * D + k] = (_Float16)__builtin_amdgcn_ldexpf(acc, e);
     if (k == 0) a.qscale[row] = __builtin_amdgcn_ldexpf(1.0f, -e);
+    if (a.t.m > 0) {
+        // the selective sketch's side: p = S q_Z over the first 32 dimensions (zero rows and columns
+        // beyond m and d_eff), in the first wave, fp16 with its own row scale
+        __shared__ float qz[32];
+        if (k < 32) qz[k] = raw * a.qmul;
+        __syncthreads();
+        if (k < 64) {
+            const float* Srow = a.t.sk32 + ((size_t)head * 64 + k) * 32;
+            float pv = 0.0f;
+            for (int j = 0; j < 32; ++j) pv = fmaf(Srow[j], qz[j], pv);
+            float mp = fabsf(pv);
+            for (int o = 32; o > 0; o >>= 1) mp = fmaxf(mp, __shfl_xor(mp, o));
+            const int e2 = mp > 0.0f ? 13 - ((int)((f2u(mp) >> 23) & 0xffu) - 127) : 0;
+            a.pp[(size_t)row * 64 + k] = (_Float16)__builtin_amdgcn_ldexpf(pv, e2);
+            if (k == 0) a.pscale[row] = __builtin_amdgcn_ldexpf(1.2533141373155003f / (float)a.t.m, -e2);
+        }
+    }
 }
 
 constexpr int kScThreads = 256;
@@ -479,18 +603,31 @@ __global__ __launch_bounds__(kScThreads) void sq_scores_kernel(SqScoresArgs a) {
     const int head = (int)(st % a.t.n_heads);
     const int RW = a.t.rec_words, RWS = 16 * RW + 4;
     const int nqt = (int)(a.nq_pad / 16);
+    const bool sk = a.t.m > 0;
     uint16_t* cb = reinterpret_cast<uint16_t*>(smem);                            // [width][256] fp16
     _Float16* qp = reinterpret_cast<_Float16*>(smem + kCbRows * 256 * 2);
     float* qsc = reinterpret_cast<float*>(smem + kCbRows * 256 * 2 + (size_t)a.nq_pad * QROW * 2);
-    uint32_t* stage = reinterpret_cast<uint32_t*>(qsc + a.nq_pad) + wave * RWS;
+    // with the sketch: S q_Z rows (64 + 8 halves each), their scales and the byte -> ±1 table
+    _Float16* ppl = reinterpret_cast<_Float16*>(qsc + a.nq_pad);
+    float* psc = reinterpret_cast<float*>(ppl + (sk ? a.nq_pad * 72 : 0));
+    u32x4* pm = reinterpret_cast<u32x4*>(psc + (sk ? a.nq_pad : 0));
+    uint32_t* stage = reinterpret_cast<uint32_t*>(pm + (sk ? 256 : 0)) + wave * RWS;
     {
         const _Float16* src = a.qp + (size_t)st * a.nq_pad * D;
         for (int i = threadIdx.x; i < a.nq_pad * D; i += kScThreads) qp[(i / D) * QROW + i % D] = src[i];
         for (int i = threadIdx.x; i < a.nq_pad; i += kScThreads) qsc[i] = a.qscale[(size_t)st * a.nq_pad + i];
         const uint16_t* c = reinterpret_cast<const uint16_t*>(a.t.cb_h);
         for (int i = threadIdx.x; i < kCbRows * 256; i += kScThreads) cb[i] = c[i];
+        if (sk) {
+            const _Float16* ps = a.pp + (size_t)st * a.nq_pad * 64;
+            for (int i = threadIdx.x; i < a.nq_pad * 64; i += kScThreads) ppl[(i / 64) * 72 + i % 64] = ps[i];
+            for (int i = threadIdx.x; i < a.nq_pad; i += kScThreads) psc[i] = a.pscale[(size_t)st * a.nq_pad + i];
+            const u32x4* t = reinterpret_cast<const u32x4*>(a.t.pm1);
+            for (int i = threadIdx.x; i < 256; i += kScThreads) pm[i] = t[i];
+        }
         for (int i = lane; i < RWS; i += 64) stage[i] = 0u;
     }
+    const uint32_t skoff = sk ? (uint32_t)a.t.sk_off[head] : 0u;
     uint4 fd[S];
 #pragma unroll
     for (int s = 0; s < S; ++s) fd[s] = a.t.fields[((size_t)head * S + s) * 4 + g];
@@ -500,7 +637,7 @@ __global__ __launch_bounds__(kScThreads) void sq_scores_kernel(SqScoresArgs a) {
     const int64_t t_end = min(t_begin + a.tiles_per_block, a.tiles_per_stream);
     const uint32_t* is = a.in + (size_t)st * a.n_tokens * RW;
     float* out = a.scores + (size_t)st * a.n_q * a.n_tokens;
-    constexpr int NP = (16 * (D / 4) + 63) / 64;
+    constexpr int NP = (16 * (D / 4 + 3) + 63) / 64;   // records of at most D/4 + 3 words
     uint32_t pre[NP];
     auto fetch = [&](int64_t tile) {
         const int valid = tile < t_end ? (int)min((int64_t)16, a.n_tokens - tile * 16) : 0;
@@ -522,19 +659,36 @@ __global__ __launch_bounds__(kScThreads) void sq_scores_kernel(SqScoresArgs a) {
             for (int i = 0; i < 8; i += 2) hv[i / 2] = (uint32_t)cb[ix[i]] | ((uint32_t)cb[ix[i + 1]] << 16);
             B[s] = as_half8(hv);
         }
+        // the sketch's ±1 operand (bits 32 s + 8 g + i of token v) and the token's fp16 norm
+        half8 Bs[2];
+        float rt = 0.0f;
+        if (sk) {
+            const uint32_t* rec = stage + v * RW;
+#pragma unroll
+            for (int s = 0; s < 2; ++s) Bs[s] = as_half8(pm[get_bits_at(rec, skoff + 32 * s + 8 * g, 8)]);
+            rt = (float)__builtin_bit_cast(_Float16, (uint16_t)get_bits_at(rec, skoff + a.t.m, 16));
+        }
         const int64_t tok = tile * 16 + v;
         for (int qt = 0; qt < nqt; ++qt) {
-            floatx4 acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+            floatx4 acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f}, acs = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int s = 0; s < S; ++s) {
                 const half8 aq = *reinterpret_cast<const half8*>(qp + (qt * 16 + v) * QROW + 32 * s + 8 * g);
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, B[s], acc, 0, 0, 0);
             }
+            if (sk) {
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const half8 ap = *reinterpret_cast<const half8*>(ppl + (qt * 16 + v) * 72 + 32 * s + 8 * g);
+                    acs = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap, Bs[s], acs, 0, 0, 0);
+                }
+            }
             if (tok < a.n_tokens) {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     const int qi = qt * 16 + 4 * g + r;
-                    if (qi < a.n_q) out[(size_t)qi * a.n_tokens + tok] = acc[r] * qsc[qi];
+                    if (qi < a.n_q)
+                        out[(size_t)qi * a.n_tokens + tok] = acc[r] * qsc[qi] + (sk ? acs[r] * psc[qi] * rt : 0.0f);
                 }
             }
         }
@@ -553,6 +707,7 @@ hipError_t launch_sq_scores(const SqScoresArgs& a, int num_cus, hipStream_t s) {
     hipError_t e = launch_sq_qprep(a, s);
     if (e != hipSuccess) return e;
     const size_t lds = (size_t)kCbRows * 256 * 2 + (size_t)a.nq_pad * (a.t.d + 8) * 2 + (size_t)a.nq_pad * 4 +
+                       (a.t.m > 0 ? (size_t)a.nq_pad * 72 * 2 + (size_t)a.nq_pad * 4 + 4096 : 0) +
                        (size_t)(kScThreads / 64) * (16 * a.t.rec_words + 4) * 4;
     if (lds > kLdsMax) return hipErrorInvalidValue;
     const void* kern = a.t.d == 64 ? reinterpret_cast<const void*>(&sq_scores_kernel<64>)
@@ -583,7 +738,7 @@ hipError_t launch_sq_scores(const SqScoresArgs& a, int num_cus, hipStream_t s) {
 // applies σ_V and U_V once per output row.
 constexpr int kAttnThreads = 256;
 
-template <int D, int RWM>
+template <int D, int RWM, bool SK>
 __global__ __launch_bounds__(kAttnThreads, 2) void sq_attn_kernel(SqAttnArgs a) {
     constexpr int T = D / 16, S = D / 32;
     constexpr int NP = (32 * RWM + 63) / 64;           // record words of a 32-token chunk per lane
@@ -591,13 +746,19 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sq_attn_kernel(SqAttnArgs a) 
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int n = lane & 15, g = lane >> 4;
     uint16_t* cb = reinterpret_cast<uint16_t*>(smem);                              // [width][256] fp16
+    u32x4* pm = reinterpret_cast<u32x4*>(smem + kCbRows * 256 * 2);                // byte -> 8 x ±1 fp16
     const int RWk = a.tk.rec_words, RWv = a.tv.rec_words;
     const int WS = 32 * (RWk + RWv) + 4;
-    uint32_t* sk = reinterpret_cast<uint32_t*>(smem + kCbRows * 256 * 2) + wave * WS;
+    uint32_t* sk = reinterpret_cast<uint32_t*>(smem + kCbRows * 256 * 2 + 4096) + wave * WS;
     uint32_t* sv = sk + 32 * RWk + 2;
+    const int MK = SK ? a.tk.m : 0;   // the keys' sketch length
     {
         const uint16_t* c = reinterpret_cast<const uint16_t*>(a.tk.cb_h);
         for (int i = threadIdx.x; i < kCbRows * 256; i += kAttnThreads) cb[i] = c[i];
+        if (MK > 0) {
+            const u32x4* t = reinterpret_cast<const u32x4*>(a.tk.pm1);
+            for (int i = threadIdx.x; i < 256; i += kAttnThreads) pm[i] = t[i];
+        }
         for (int i = lane; i < WS; i += 64) sk[i] = 0u;
     }
     __syncthreads();
@@ -614,6 +775,17 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sq_attn_kernel(SqAttnArgs a) 
     for (int s = 0; s < S; ++s)
         Bq[s] = *reinterpret_cast<const half8*>(a.qp + ((size_t)st * 16 + n) * D + 32 * s + 8 * g);
     const float qs = a.qscale[st * 16 + n];
+    // the key sketch's query side (S q_Z of query n) and its scale
+    half8 Bp[2];
+    float pks = 0.0f;
+    uint32_t skoff = 0u;
+    if (MK > 0) {
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+            Bp[s] = *reinterpret_cast<const half8*>(a.pp + ((size_t)st * 16 + n) * 64 + 32 * s + 8 * g);
+        pks = a.pscale[st * 16 + n];
+        skoff = (uint32_t)a.tk.sk_off[hk];
+    }
     uint4 fk[S];
 #pragma unroll
     for (int s = 0; s < S; ++s) fk[s] = a.tk.fields[((size_t)hk * S + s) * 4 + g];
@@ -659,9 +831,23 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sq_attn_kernel(SqAttnArgs a) 
                 d4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(hv), Bq[s], d4, 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
+            float add4[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+            if (MK > 0) {   // sqrt(pi/2)/m · ||e_z|| · <S q_Z, 2σ - 1>, tokens 16h + n as A
+                floatx4 dc = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                for (int s = 0; s < 2; ++s) {
+                    const half8 as = as_half8(pm[get_bits_at(sk + (16 * h + n) * RWk, skoff + 32 * s + 8 * g, 8)]);
+                    dc = __builtin_amdgcn_mfma_f32_16x16x32_f16(as, Bp[s], dc, 0, 0, 0);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r) {
+                    const uint32_t rb = get_bits_at(sk + (16 * h + 4 * g + r) * RWk, skoff + (uint32_t)MK, 16);
+                    add4[r] = dc[r] * pks * (float)__builtin_bit_cast(_Float16, (uint16_t)rb);
+                }
+            }
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                sc[h][r] = (c0 + 16 * h + 4 * g + r < t1) ? d4[r] * qs : -INFINITY;
+                sc[h][r] = (c0 + 16 * h + 4 * g + r < t1) ? d4[r] * qs + add4[r] : -INFINITY;
         }
         // online softmax for query n (its 32 scores live on lanes n, n+16, n+32, n+48)
         float cm = sc[0][0];
@@ -755,12 +941,12 @@ __global__ __launch_bounds__(D) void sq_attn_combine_kernel(SqAttnArgs a) {
     else static_cast<float*>(a.out)[oi] = o;
 }
 
-template <int D, int RWM>
+template <int D, int RWM, bool SK>
 static hipError_t launch_attn(const SqAttnArgs& a, hipStream_t s) {
-    const size_t lds = (size_t)kCbRows * 256 * 2 +
+    const size_t lds = (size_t)kCbRows * 256 * 2 + 4096 +
                        (size_t)(kAttnThreads / 64) * (32 * (a.tk.rec_words + a.tv.rec_words) + 4) * 4;
     const unsigned blocks = (unsigned)((a.n_streams * a.n_split + kAttnThreads / 64 - 1) / (kAttnThreads / 64));
-    hipLaunchKernelGGL((sq_attn_kernel<D, RWM>), dim3(blocks), dim3(kAttnThreads), lds, s, a);
+    hipLaunchKernelGGL((sq_attn_kernel<D, RWM, SK>), dim3(blocks), dim3(kAttnThreads), lds, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const unsigned rows = (unsigned)(a.n_streams / a.hkv * a.hq);
@@ -769,11 +955,17 @@ static hipError_t launch_attn(const SqAttnArgs& a, hipStream_t s) {
 }
 
 // records of up to 16 words (at most 4 bits per dimension on average at d = 128) take the smaller
-// register prefetch
+// register prefetch, the larger d/4 words of 8-bit fields; with a key sketch (at most 64 bits and a
+// 16-bit norm more) a middle size covers up to 5 bits per dimension at d = 128 without spilling
 hipError_t launch_sq_attention(const SqAttnArgs& a, hipStream_t s) {
     const int rw = max(a.tk.rec_words, a.tv.rec_words);
-    if (a.tk.d == 64) return rw <= 8 ? launch_attn<64, 8>(a, s) : launch_attn<64, 16>(a, s);
-    return rw <= 16 ? launch_attn<128, 16>(a, s) : launch_attn<128, 32>(a, s);
+    if (a.tk.m > 0) {
+        if (a.tk.d == 64) return rw <= 8 ? launch_attn<64, 8, true>(a, s) : launch_attn<64, 19, true>(a, s);
+        if (rw <= 16) return launch_attn<128, 16, true>(a, s);
+        return rw <= 24 ? launch_attn<128, 24, true>(a, s) : launch_attn<128, 35, true>(a, s);
+    }
+    if (a.tk.d == 64) return rw <= 8 ? launch_attn<64, 8, false>(a, s) : launch_attn<64, 16, false>(a, s);
+    return rw <= 16 ? launch_attn<128, 16, false>(a, s) : launch_attn<128, 32, false>(a, s);
 }
 
 }  // namespace tq

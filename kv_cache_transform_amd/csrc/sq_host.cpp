@@ -233,9 +233,9 @@ struct Blob {
 // attention split geometry, a function of the arguments only: about as many (stream, split) waves
 // as 256 CUs hold at eight per CU, splits of at least 256 tokens in multiples of 32, at most 1024
 struct SqAttnWs {
-    int64_t tps, n_split, o_qs, o_part, o_ml, total;
+    int64_t tps, n_split, o_qs, o_pp, o_ps, o_part, o_ml, total;
 };
-SqAttnWs sq_attn_ws(int d, int64_t streams, int64_t n_tokens) {
+SqAttnWs sq_attn_ws(int d, int m, int64_t streams, int64_t n_tokens) {
     SqAttnWs w{};
     int64_t ns = (256 * 8 + streams - 1) / (streams > 0 ? streams : 1);
     ns = std::min(ns, (n_tokens + 255) / 256);
@@ -244,7 +244,9 @@ SqAttnWs sq_attn_ws(int d, int64_t streams, int64_t n_tokens) {
     w.n_split = std::max<int64_t>((n_tokens + w.tps - 1) / w.tps, 1);
     auto al = [](int64_t x) { return (x + 255) / 256 * 256; };
     w.o_qs = al(streams * 16 * d * 2);
-    w.o_part = w.o_qs + al(streams * 16 * 4);
+    w.o_pp = w.o_qs + al(streams * 16 * 4);          // with a key sketch: S q_Z rows (64 fp16) and scales
+    w.o_ps = w.o_pp + (m > 0 ? al(streams * 16 * 64 * 2) : 0);
+    w.o_part = w.o_ps + (m > 0 ? al(streams * 16 * 4) : 0);
     w.o_ml = w.o_part + al(streams * w.n_split * 16 * d * 4);
     w.total = w.o_ml + al(streams * w.n_split * 16 * 2 * 4);
     return w;
@@ -313,9 +315,17 @@ int tq_sq_calibrate(const tq_sq_params* p, const float* x_cal, int64_t n_cal, do
 }
 
 int tq_sq_create(const tq_sq_params* p, const double* basis, const double* lambda, const int32_t* bits,
-                 tq_sq_codec** out) {
+                 const int32_t* d_eff, tq_sq_codec** out) {
     if (check_sq_params(p, true) != TQ_OK || !basis || !lambda || !bits || !out) return TQ_EINVAL;
-    const int d = p->d, H = p->n_heads, T = d / 16, S = d / 32;
+    const int d = p->d, H = p->n_heads, T = d / 16, S = d / 32, M = p->m;
+    if (M != 0 && M != 16 && M != 32 && M != 48 && M != 64) return TQ_EINVAL;
+    if (M > 0) {
+        if (!d_eff) return TQ_EINVAL;
+        for (int h = 0; h < H; ++h) {
+            if (d_eff[h] < 1 || d_eff[h] > d) return TQ_EINVAL;
+            if (d_eff[h] > 32) return TQ_EUNSUPPORTED;
+        }
+    }
     for (int64_t i = 0; i < (int64_t)H * d * d; ++i)
         if (!std::isfinite(basis[i])) return TQ_EINVAL;
     for (int64_t i = 0; i < (int64_t)H * d; ++i) {
@@ -354,7 +364,7 @@ int tq_sq_create(const tq_sq_params* p, const double* basis, const double* lambd
         for (int k = 0; k < d; ++k) s += bits[(size_t)h * d + k];
         max_bits = std::max(max_bits, s);
     }
-    const int rec_words = (max_bits + 31) / 32;
+    const int rec_words = (max_bits + (M > 0 ? M + 16 : 0) + 31) / 32;
 
     std::vector<uint16_t> enc_b((size_t)H * 2 * T * S * 512), dec_a((size_t)H * 2 * T * S * 512);
     std::vector<float> desc((size_t)H * d * 4), dscale(H), U32((size_t)H * d * d), sig((size_t)H * d);
@@ -435,7 +445,44 @@ int tq_sq_create(const tq_sq_params* p, const double* basis, const double* lambd
             }
     }
 
+    // the selective QJL sketch
+    std::vector<uint16_t> skb(M > 0 ? (size_t)H * (M / 16) * 512 : 1, 0);
+    std::vector<float> sk32(M > 0 ? (size_t)H * 64 * 32 : 1, 0.0f), cent32(256 * (kBMax + 1), 0.0f);
+    std::vector<int32_t> skoff(H, 0), deffv(H, 0);
+    std::vector<uint16_t> pm1(256 * 8);
+    for (int v = 0; v < 256; ++v)
+        for (int i = 0; i < 8; ++i) pm1[v * 8 + i] = ((v >> i) & 1) ? 0x3c00u : 0xbc00u;   // fp16 +1, -1
+    for (int w = 1; w <= kBMax; ++w) {
+        const GaussBook& gb = gauss_book(w);
+        for (int i = 0; i < (1 << w); ++i) cent32[w * 256 + i] = (float)gb.cent[i];
+    }
+    for (int h = 0; h < H; ++h) {
+        int sb = 0;
+        for (int k = 0; k < d; ++k) sb += bits[(size_t)h * d + k];
+        skoff[h] = sb;
+        deffv[h] = d_eff ? d_eff[h] : 0;
+        if (M == 0) continue;
+        const uint64_t key = stream_key(p->seed, 4, (uint32_t)h);
+        auto sgn = [&](int i, int k) {   // S[i][k] = -1 iff bit 63 of word i·d + k
+            return (mix64(key + (uint64_t)(i * d + k + 1) * 0x9E3779B97F4A7C15ull) >> 63) ? -1.0f : 1.0f;
+        };
+        for (int i = 0; i < M; ++i)
+            for (int k = 0; k < d_eff[h]; ++k) sk32[((size_t)h * 64 + i) * 32 + k] = sgn(i, k);
+        for (int ts = 0; ts < M / 16; ++ts)
+            for (int l = 0; l < 64; ++l)
+                for (int i = 0; i < 8; ++i) {   // B[kk = 8 g + i][n = l % 16] = S[16 ts + n][8 g + i]
+                    const float v = sk32[((size_t)h * 64 + 16 * ts + (l % 16)) * 32 + 8 * (l / 16) + i];
+                    skb[(((size_t)h * (M / 16) + ts) * 64 + l) * 8 + i] = f64_to_f16_bits(v);
+                }
+    }
+
     Blob blob;
+    const int64_t o_skb = blob.add(skb.data(), skb.size() * 2);
+    const int64_t o_sk32 = blob.add(sk32.data(), sk32.size() * 4);
+    const int64_t o_c32 = blob.add(cent32.data(), cent32.size() * 4);
+    const int64_t o_skoff = blob.add(skoff.data(), skoff.size() * 4);
+    const int64_t o_deff = blob.add(deffv.data(), deffv.size() * 4);
+    const int64_t o_pm1 = blob.add(pm1.data(), pm1.size() * 2);
     const int64_t o_eb = blob.add(enc_b.data(), enc_b.size() * 2);
     const int64_t o_ed = blob.add(desc.data(), desc.size() * 4);
     const int64_t o_gr = blob.add(grids.data(), grids.size() * 4);
@@ -473,6 +520,13 @@ int tq_sq_create(const tq_sq_params* p, const double* basis, const double* lambd
     t.cb_h = reinterpret_cast<const _Float16*>(base + o_h);
     t.U32 = reinterpret_cast<const float*>(base + o_u);
     t.sigma = reinterpret_cast<const float*>(base + o_sg);
+    t.m = M;
+    t.sk_b = reinterpret_cast<const _Float16*>(base + o_skb);
+    t.sk32 = reinterpret_cast<const float*>(base + o_sk32);
+    t.sk_off = reinterpret_cast<const int32_t*>(base + o_skoff);
+    t.deff = reinterpret_cast<const int32_t*>(base + o_deff);
+    t.cent32 = reinterpret_cast<const float*>(base + o_c32);
+    t.pm1 = reinterpret_cast<const _Float16*>(base + o_pm1);
     t.blob = mem;
     c->device = device;
     c->num_cus = cus;
@@ -533,11 +587,28 @@ int tq_sq_decode(const tq_sq_codec* codec, const void* packed, int64_t n_streams
                ? TQ_OK : TQ_EHIP;
 }
 
+namespace {
+// scores workspace: projected queries (fp16), their scales, and with a sketch S q_Z (64 fp16 per row)
+// and its scales
+struct SqScoresWs {
+    int64_t o_qs, o_pp, o_ps, total;
+};
+SqScoresWs sq_scores_ws(const tq_sq_codec* codec, int64_t n_streams, int64_t n_q) {
+    auto al = [](int64_t x) { return (x + 255) / 256 * 256; };
+    const int64_t rows = n_streams * ((n_q + 15) / 16 * 16);
+    const bool sk = codec->dev.m > 0;
+    SqScoresWs w{};
+    w.o_qs = al(rows * codec->dev.d * 2);
+    w.o_pp = w.o_qs + al(rows * 4);
+    w.o_ps = w.o_pp + (sk ? al(rows * 64 * 2) : 0);
+    w.total = w.o_ps + (sk ? al(rows * 4) : 0);
+    return w;
+}
+}  // namespace
+
 size_t tq_sq_scores_workspace_bytes(const tq_sq_codec* codec, int64_t n_streams, int64_t n_q) {
     if (!codec || n_streams < 0 || n_q < 0) return 0;
-    const int64_t nq_pad = (n_q + 15) / 16 * 16;
-    const int64_t qp = (n_streams * nq_pad * codec->dev.d * 2 + 255) / 256 * 256;
-    return (size_t)(qp + (n_streams * nq_pad * 4 + 255) / 256 * 256);
+    return (size_t)sq_scores_ws(codec, n_streams, n_q).total;
 }
 
 int tq_sq_qk_scores(const tq_sq_codec* codec, const void* q, tq_dtype q_dtype, int64_t n_q,
@@ -560,9 +631,14 @@ int tq_sq_qk_scores(const tq_sq_codec* codec, const void* q, tq_dtype q_dtype, i
     a.n_tokens = n_tokens;
     a.n_q = n_q;
     a.nq_pad = (n_q + 15) / 16 * 16;
-    const int64_t qp = (n_streams * a.nq_pad * codec->dev.d * 2 + 255) / 256 * 256;
-    a.qp = static_cast<_Float16*>(workspace);
-    a.qscale = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + qp);
+    const SqScoresWs w = sq_scores_ws(codec, n_streams, n_q);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    a.qp = reinterpret_cast<_Float16*>(ws);
+    a.qscale = reinterpret_cast<float*>(ws + w.o_qs);
+    if (codec->dev.m > 0) {
+        a.pp = reinterpret_cast<_Float16*>(ws + w.o_pp);
+        a.pscale = reinterpret_cast<float*>(ws + w.o_ps);
+    }
     a.qmul = 1.0f;
     a.tiles_per_stream = (n_tokens + 15) / 16;
     return launch_sq_scores(a, codec->num_cus, static_cast<hipStream_t>(stream)) == hipSuccess ? TQ_OK : TQ_EHIP;
@@ -571,7 +647,7 @@ int tq_sq_qk_scores(const tq_sq_codec* codec, const void* q, tq_dtype q_dtype, i
 size_t tq_sq_attention_workspace_bytes(const tq_sq_codec* ck, int32_t batch, int32_t n_q_heads,
                                        int32_t n_kv_heads, int64_t n_tokens) {
     if (!ck || batch < 0 || n_q_heads < 1 || n_kv_heads < 1 || n_tokens < 0) return 0;
-    return (size_t)sq_attn_ws(ck->dev.d, (int64_t)batch * n_kv_heads, n_tokens).total;
+    return (size_t)sq_attn_ws(ck->dev.d, ck->dev.m, (int64_t)batch * n_kv_heads, n_tokens).total;
 }
 
 int tq_sq_decode_attention(const tq_sq_codec* ck, const tq_sq_codec* cv, const void* q, tq_dtype q_dtype,
@@ -594,7 +670,7 @@ int tq_sq_decode_attention(const tq_sq_codec* ck, const tq_sq_codec* cv, const v
         return TQ_EALIGN;
     if (lengths && (reinterpret_cast<uintptr_t>(lengths) & 3u)) return TQ_EALIGN;
     const int64_t streams = (int64_t)batch * n_kv_heads;
-    const SqAttnWs w = sq_attn_ws(ck->dev.d, streams, n_tokens);
+    const SqAttnWs w = sq_attn_ws(ck->dev.d, ck->dev.m, streams, n_tokens);
     if (workspace_bytes < (size_t)w.total) return TQ_EWORKSPACE;
     if (!on_codec_device(ck) || !on_codec_device(cv)) return TQ_EINVAL;
     const hipStream_t s = static_cast<hipStream_t>(stream);
@@ -606,6 +682,10 @@ int tq_sq_decode_attention(const tq_sq_codec* ck, const tq_sq_codec* cv, const v
     qa.q_bf16 = q_dtype == TQ_BF16;
     qa.qp = reinterpret_cast<_Float16*>(ws);
     qa.qscale = reinterpret_cast<float*>(ws + w.o_qs);
+    if (ck->dev.m > 0) {
+        qa.pp = reinterpret_cast<_Float16*>(ws + w.o_pp);
+        qa.pscale = reinterpret_cast<float*>(ws + w.o_ps);
+    }
     qa.qmul = scale * 1.4426950408889634f;   // scores in base-2 units for exp2
     qa.n_streams = streams;
     qa.n_q = n_q_heads / n_kv_heads;
@@ -616,6 +696,8 @@ int tq_sq_decode_attention(const tq_sq_codec* ck, const tq_sq_codec* cv, const v
     a.tv = cv->dev;
     a.qp = qa.qp;
     a.qscale = qa.qscale;
+    a.pp = qa.pp;
+    a.pscale = qa.pscale;
     a.kin = static_cast<const uint32_t*>(packed_k);
     a.vin = static_cast<const uint32_t*>(packed_v);
     a.lens = lengths;

@@ -30,6 +30,14 @@ struct SqDev {
     const float* U32 = nullptr;        // [head][j][k] fp32
     const float* sigma = nullptr;      // [head][k]
     int lds_grid_words = 0;            // total words of `grids`
+    // selective QJL sketch (m > 0): sketch rows over the first 32 dimensions (zero beyond d_eff)
+    int m = 0;
+    const _Float16* sk_b = nullptr;    // encode B operand [head][tile m/16][lane][8]: S[16ts + n][8g + i]
+    const float* sk32 = nullptr;       // [head][64][32] fp32 S (rows >= m and columns >= d_eff zero)
+    const int32_t* sk_off = nullptr;   // [head] bit offset of the sketch field (Σ_k b_k)
+    const int32_t* deff = nullptr;     // [head] d_eff
+    const float* cent32 = nullptr;     // [width 0..8][256] fp32 centroids
+    const _Float16* pm1 = nullptr;     // [256][8] ±1 of a byte's bits, LSB first
     void* blob = nullptr;
 };
 
@@ -57,6 +65,8 @@ struct SqScoresArgs {
     float* scores;          // [streams][n_q][tokens]
     _Float16* qp;           // workspace: [streams][nq_pad][d] fp16 of (Uᵀq ⊙ σ)·2^e_row
     float* qscale;          // workspace: [streams][nq_pad] 2^-e_row
+    _Float16* pp;           // workspace with a sketch: [streams][nq_pad][64] fp16 of (S q_Z)·2^e'_row
+    float* pscale;          // [streams][nq_pad] 2^-e'_row · sqrt(pi/2)/m (q_Z already carries qmul)
     float qmul;             // factor on every projected query (1 for scores; scale·log2 e for attention)
     int64_t n_streams, n_tokens, n_q, nq_pad, tiles_per_stream;
     int64_t blocks_per_stream, tiles_per_block;
@@ -66,6 +76,8 @@ struct SqAttnArgs {
     SqDev tk, tv;
     const _Float16* qp;     // [streams][16][d] fp16 projected queries (scaled by 2^e_row)
     const float* qscale;    // [streams][16] 2^-e_row
+    const _Float16* pp;     // with a key sketch: [streams][16][64] fp16 S q_Z (scaled)
+    const float* pscale;    // [streams][16]
     const uint32_t* kin;
     const uint32_t* vin;
     const int32_t* lens;    // [batch] or null

@@ -102,14 +102,22 @@ def test_sq_entry_points_validate_before_any_device_call():
     h = ctypes.c_void_p()
     for bits in (np.zeros(64, np.int32), np.full(64, 9, np.int32)):
         assert L.tq_sq_create(ctypes.byref(p), basis.ctypes.data, lam.ctypes.data, bits.ctypes.data,
-                              ctypes.byref(h)) == _lib.TQ_EINVAL
+                              None, ctypes.byref(h)) == _lib.TQ_EINVAL
     bad = lam.copy()
     bad[3] = np.nan
     assert L.tq_sq_create(ctypes.byref(p), basis.ctypes.data, bad.ctypes.data, np.full(64, 4, np.int32).ctypes.data,
-                          ctypes.byref(h)) == _lib.TQ_EINVAL
+                          None, ctypes.byref(h)) == _lib.TQ_EINVAL
     p256 = P(256, 1, 4, 2, 0, 0, 10.0)
     assert L.tq_sq_create(ctypes.byref(p256), np.eye(256).ravel().ctypes.data, np.ones(256).ctypes.data,
-                          np.full(256, 4, np.int32).ctypes.data, ctypes.byref(h)) == _lib.TQ_EINVAL
+                          np.full(256, 4, np.int32).ctypes.data, None, ctypes.byref(h)) == _lib.TQ_EINVAL
+    # the selective sketch: m in {16, 32, 48, 64}, d_eff given and in 1..d; more than 32 is unsupported
+    four = np.full(64, 4, np.int32)
+    for m, de, want in ((20, 8, _lib.TQ_EINVAL), (64, None, _lib.TQ_EINVAL), (32, 0, _lib.TQ_EINVAL),
+                        (16, 65, _lib.TQ_EINVAL), (64, 33, _lib.TQ_EUNSUPPORTED), (80, 8, _lib.TQ_EINVAL)):
+        ps = P(64, 1, 4, 2, 0, 0, 10.0, m, 7)
+        dv = None if de is None else np.array([de], np.int32)
+        assert L.tq_sq_create(ctypes.byref(ps), basis.ctypes.data, lam.ctypes.data, four.ctypes.data,
+                              None if dv is None else dv.ctypes.data, ctypes.byref(h)) == want, (m, de)
     assert h.value is None
     assert L.tq_sq_encode(None, None, _lib.TQ_BF16, 1, 1, None, None) == _lib.TQ_EINVAL
     assert L.tq_sq_decode(None, None, 1, 1, None, _lib.TQ_F32, None) == _lib.TQ_EINVAL
