@@ -27,6 +27,10 @@ Readings where the pages are silent (each listed in the design doc):
   * QJL uses a seeded Gaussian S (m x d) on the WHT-domain residual, or the randomized Hadamard
     sketch S = H diag(s2) (m = d); sign(0) = +1.
   * Random signs and S come from SplitMix64 keyed by (seed, tag, head); Gaussians by Box-Muller.
+  * The sketch projects the residual in half precision: ê = fp16(2^14 e)/2^14 with round to nearest
+    even (|2^14 e| < 2^15, so only the precision is lost, never the range), z = S ê summed exactly;
+    the stored norm r16 is that of the exact e.  The pages fix no precision for the projection;
+    this is the precision the library takes the sign decisions in.
 """
 from __future__ import annotations
 
@@ -281,12 +285,43 @@ def boundary_distance(y: np.ndarray, thresholds: np.ndarray, idx: np.ndarray | N
     return np.minimum(lo, hi)
 
 
+SKETCH_SCALE = 2.0 ** 14
+
+
+def sketch_input(e: np.ndarray) -> np.ndarray:
+    """ê: the residual as the projection takes it, 2^14 e rounded to the nearest fp16 (ties to
+    even), scaled back (exact in fp64)."""
+    return fp16_rne(SKETCH_SCALE * np.asarray(e, dtype=np.float64)).astype(np.float64) / SKETCH_SCALE
+
+
+def sketch(e: np.ndarray, S: np.ndarray, tol: float = FLAG_TOL) -> dict:
+    """Sketch of residual rows e (N, d): z = ê Sᵀ, σ = [z >= 0] (sign(0) = +1).
+
+    sflag marks the decisions another implementation may take differently when its residual is off
+    by at most `tol` per coordinate: |z_i| < tol + Σ_k |S_ik| · step_k over the coordinates k whose
+    2^14 e_k lies within 2^14 tol of an fp16 rounding midpoint (step_k = that fp16 spacing / 2^14,
+    the change of ê_k if it rounds the other way)."""
+    S = np.asarray(S, dtype=np.float64)
+    e = np.asarray(e, dtype=np.float64)
+    v = SKETCH_SCALE * e
+    h = fp16_rne(v)
+    hv = h.astype(np.float64)
+    lo = np.where(hv <= v, hv, np.nextafter(h, np.float16(-np.inf)).astype(np.float64))
+    hi = np.where(hv >= v, hv, np.nextafter(h, np.float16(np.inf)).astype(np.float64))
+    step = hi - lo                                  # 0 when v is exactly representable
+    mid = 0.5 * (lo + hi)
+    near = (step > 0) & (np.abs(v - mid) < SKETCH_SCALE * tol)
+    z = sketch_input(e) @ S.T
+    band = tol + (np.where(near, step, 0.0) / SKETCH_SCALE) @ np.abs(S).T
+    return {"z": z, "sigma": z >= 0.0, "sflag": np.abs(z) < band}
+
+
 def encode(x: np.ndarray, s: np.ndarray, thresholds: np.ndarray, centroids: np.ndarray,
            S: np.ndarray | None = None) -> dict:
     """Encode rows of x (N, d) that share one RNG head.
 
     Returns idx (N,d), n16 (N,) fp16, flag (N,d) bool [|y - t_i| < 1e-6], y (N,d); with S (m x d)
-    also e, r16, z, sigma (N,m) bool [z >= 0], sflag (N,m) bool [|z| < 1e-6]."""
+    also e, r16 (of the exact e), z = S ê, sigma (N,m) bool [z >= 0] and sflag (N,m) (``sketch``)."""
     x = np.asarray(x, dtype=np.float64)
     n = np.sqrt(np.sum(x * x, axis=1))
     safe = np.where(n > 0, n, 1.0)
@@ -297,9 +332,7 @@ def encode(x: np.ndarray, s: np.ndarray, thresholds: np.ndarray, centroids: np.n
            "y": y, "norm": n}
     if S is not None:
         e = y - centroids[idx]
-        z = e @ np.asarray(S, dtype=np.float64).T
-        out.update(e=e, r16=fp16_rne(np.sqrt(np.sum(e * e, axis=1))), z=z,
-                   sigma=z >= 0.0, sflag=np.abs(z) < FLAG_TOL)
+        out.update(e=e, r16=fp16_rne(np.sqrt(np.sum(e * e, axis=1))), **sketch(e, S))
     return out
 
 

@@ -54,7 +54,7 @@ def test_encode_sketch_is_sign_of_wht_of_signed_residual():
     s, S = O.head_signs(5, 0, d), O.rht_matrix(5, 0, d)
     x = np.random.default_rng(1).standard_normal((200, d))
     r = O.encode(x, s, t, c, S)
-    z = O.fwht(r["e"] * O.rht_signs(5, 0, d))
+    z = O.fwht(O.sketch_input(r["e"]) * O.rht_signs(5, 0, d))     # the half-precision residual
     assert np.array_equal(r["sigma"], z >= 0.0)
     assert np.allclose(r["z"], z, rtol=0, atol=1e-12)
 
