@@ -16,6 +16,7 @@ headline step and reported under "kernels"; they are not part of `value`.
 from __future__ import annotations
 
 import argparse
+import ctypes
 import json
 import math
 import os
@@ -319,7 +320,25 @@ def main():
         kern["fmag_decode_k_bf16"] = {"ms": round(fdm, 4), "alg_bytes": fm_alg,
                                       "achieved_GBs": round(fm_alg / (fdm * 1e-3) / 1e9, 1),
                                       "hbm_frac": round(fm_alg / (fdm * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-        del xh, fpk
+        del xh
+        # Fmag decode-attention over Fmag K and V caches of the same shape, 32 query heads per batch
+        fpv = torch.empty(nvec * fm.record_bytes, dtype=torch.uint8, device=dev)
+        fm.encode(V, fpv)
+        fws = torch.empty(max(int(T._lib.lib().tq_fmag_attention_workspace_bytes(
+            ctypes.byref(fm.params()), B, Hq, Hkv, N)), 16), dtype=torch.uint8, device=dev)
+        T.fmag_decode_attention(fm, fm, q, fpk, fpv, Hkv, N, out=out, workspace=fws)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(3):
+            T.fmag_decode_attention(fm, fm, q, fpk, fpv, Hkv, N, out=out, workspace=fws)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        fam = e0.elapsed_time(e1) / 3
+        fa_alg = nvec * 2 * fm.record_bytes + 2 * B * Hq * d * 2
+        kern["fmag_decode_attention"] = {"ms": round(fam, 4), "alg_bytes": fa_alg,
+                                         "achieved_GBs": round(fa_alg / (fam * 1e-3) / 1e9, 1),
+                                         "hbm_frac": round(fa_alg / (fam * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+        del fpk, fpv, fws
     sample_k, sample_v = K[:1, :2048].clone(), V[:1, :2048].clone()   # the CPU baseline's sample
     del K
 

@@ -64,6 +64,24 @@ int tq_fmag_qk_scores(const tq_fmag_params* p, const void* q, tq_dtype q_dtype, 
                       const void* packed, int64_t n_streams, int64_t n_tokens, float* scores,
                       void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace for tq_fmag_decode_attention (projected queries and per-split partials). */
+size_t tq_fmag_attention_workspace_bytes(const tq_fmag_params* pk, int32_t batch, int32_t n_q_heads,
+                                         int32_t n_kv_heads, int64_t n_tokens);
+
+/* Decode-step attention over Fmag K and V caches ("Method": attention runs on the reconstructed
+ * cache): out[b][h] = Σ_t softmax_t(scale·<q[b][h], x̂_K,t>)·x̂_V,t over the first lengths[b] tokens
+ * (all n_tokens when lengths is NULL; a row with no token is 0).  K and V may use different b and p,
+ * with the same d.  q: [batch][n_q_heads][d] F32 or BF16; packed_k / packed_v: [batch·n_kv_heads]
+ * streams of n_tokens records; query head h reads kv head h / (n_q_heads / n_kv_heads), at most 16
+ * query heads per kv head; softmax_scale 0 means 1/sqrt(d); out [batch][n_q_heads][d] F32 or BF16.
+ * The scores use the Parseval form of tq_fmag_qk_scores; the weighted sum is taken over the
+ * reconstructed spectra (the inverse FFT is linear) and one inverse DFT per output row finishes it.
+ * fp16 MFMA products with fp32 accumulation: relative error ~1e-3. */
+int tq_fmag_decode_attention(const tq_fmag_params* pk, const tq_fmag_params* pv, const void* q, tq_dtype q_dtype,
+                             int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, const void* packed_k,
+                             const void* packed_v, int64_t n_tokens, const int32_t* lengths, float softmax_scale,
+                             void* out, tq_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

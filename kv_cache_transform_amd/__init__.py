@@ -15,7 +15,8 @@ from . import _lib
 from ._lib import TQError, TQ_BF16, TQ_F32
 
 __all__ = ["Codec", "TQError", "get_layout", "encode", "decode", "qk_scores", "decode_attention",
-           "attention_workspace_bytes", "host_tables", "clear_cache", "SQCodec", "sq_host_codebook", "sq_decode_attention", "FmagCodec"]
+           "attention_workspace_bytes", "host_tables", "clear_cache", "SQCodec", "sq_host_codebook", "sq_decode_attention", "FmagCodec",
+           "fmag_decode_attention"]
 
 _DT = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}
 
@@ -334,3 +335,24 @@ class FmagCodec:
                                                 S, n_tokens, _ptr(out), _ptr(workspace), workspace.numel(),
                                                 _stream(q.device)), "tq_fmag_qk_scores")
         return out
+
+
+def fmag_decode_attention(ck: FmagCodec, cv: FmagCodec, q: torch.Tensor, packed_k: torch.Tensor,
+                          packed_v: torch.Tensor, n_kv_heads: int, n_tokens: int, softmax_scale: float = 0.0,
+                          out_dtype: torch.dtype = torch.bfloat16, out: torch.Tensor | None = None,
+                          workspace: torch.Tensor | None = None, lengths: torch.Tensor | None = None) -> torch.Tensor:
+    """q: [batch, n_q_heads, d] -> attention output over Fmag K/V caches (tq_fmag_decode_attention)."""
+    B, Hq, d = q.shape
+    pk, pv = ck.params(), cv.params()
+    if workspace is None:
+        ws = int(_lib.lib().tq_fmag_attention_workspace_bytes(ctypes.byref(pk), B, Hq, n_kv_heads, n_tokens))
+        workspace = torch.empty(max(ws, 16), dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty(B, Hq, d, dtype=out_dtype, device=q.device)
+    if lengths is not None and (lengths.dtype != torch.int32 or lengths.numel() < B or not lengths.is_contiguous()):
+        raise ValueError("lengths must be a contiguous int32 tensor with one entry per batch element")
+    _lib.check(_lib.lib().tq_fmag_decode_attention(
+        ctypes.byref(pk), ctypes.byref(pv), _ptr(q), _DT[q.dtype], B, Hq, n_kv_heads, _ptr(packed_k), _ptr(packed_v),
+        n_tokens, _ptr(lengths) if lengths is not None else None, ctypes.c_float(softmax_scale), _ptr(out),
+        _DT[out.dtype], _ptr(workspace), workspace.numel(), _stream(q.device)), "tq_fmag_decode_attention")
+    return out

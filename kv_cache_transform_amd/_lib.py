@@ -26,7 +26,7 @@ SQ_EXPORTS = ("tq_sq_calibrate", "tq_sq_create", "tq_sq_destroy", "tq_sq_record_
               "tq_sq_decode_attention", "tq_sq_host_codebook")
 # every symbol include/tq_fmag.h declares
 FMAG_EXPORTS = ("tq_fmag_record_bytes", "tq_fmag_encode", "tq_fmag_decode", "tq_fmag_scores_workspace_bytes",
-                "tq_fmag_qk_scores")
+                "tq_fmag_qk_scores", "tq_fmag_attention_workspace_bytes", "tq_fmag_decode_attention")
 
 
 class Params(ctypes.Structure):
@@ -101,6 +101,9 @@ def lib() -> ctypes.CDLL:
         "tq_fmag_decode": (ctypes.c_int, [FP, VP, I64, I64, VP, ctypes.c_int, VP]),
         "tq_fmag_scores_workspace_bytes": (SZ, [FP, I64, I64]),
         "tq_fmag_qk_scores": (ctypes.c_int, [FP, VP, ctypes.c_int, I64, VP, I64, I64, VP, VP, SZ, VP]),
+        "tq_fmag_attention_workspace_bytes": (SZ, [FP, I32, I32, I32, I64]),
+        "tq_fmag_decode_attention": (ctypes.c_int, [FP, FP, VP, ctypes.c_int, I32, I32, I32, VP, VP, I64, VP,
+                                                    ctypes.c_float, VP, ctypes.c_int, VP, SZ, VP]),
         "tq_sq_decode_attention": (ctypes.c_int, [VP, VP, VP, ctypes.c_int, I32, I32, I32, VP, VP, I64, VP,
                                                   ctypes.c_float, VP, ctypes.c_int, VP, SZ, VP]),
     }

@@ -524,4 +524,268 @@ hipError_t launch_fmag_scores(const FmScoresArgs& a, int num_cus, hipStream_t s)
     return pq ? launch_fsc<128, true>(a, num_cus, s) : launch_fsc<128, false>(a, num_cus, s);
 }
 
+// ---------------------------------------------------------------------------------------------
+// decode-attention
+// ---------------------------------------------------------------------------------------------
+// One wave per (stream, split) over 32-token chunks, like the SpectralQuant attention, with the
+// reconstructed spectra in place of codebook values (the inverse FFT is linear, so Σ_t p_t x̂_t is
+// the inverse FFT of Σ_t p_t X̂_t):
+//   scores  D[token][query] = Σ_c X̂_K[token][c]·q'[query][c]: A = the keys' spectrum coordinates
+//           (per token times 2^es), B = the projected queries, both as fp16 hi + lo pairs (three
+//           products: the scores carry about 2^-21 relative error, so the softmax of heavy-tailed
+//           keys keeps its precision); each row then scaled by its token's 2^-es, in base-2 units;
+//   softmax online per query;
+//   values  D[c][query] += Σ_t X̂_V[t][c]·p[t][query]: B = the weights as the score product left
+//           them (tokens τ(g, i) = 4g + i, 16 + 4g + i - 4 along the contraction), A = coordinate
+//           16t + l%16 of those 8 tokens, all scaled by one power of two per chunk (from the chunk's
+//           largest magnitude) that the fp32 accumulation undoes; the weights as fp16 hi + lo.
+// The combine merges the splits and applies the weighted inverse real DFT once per output row.
+constexpr int kFaThreads = 256;
+
+template <bool PQ>
+__device__ __forceinline__ float phase_trig(const uint32_t* rec, uint32_t pos, uint32_t p, bool sine, const float* cs) {
+    const uint32_t pf = get_field(rec, pos, p);
+    if constexpr (PQ) return cs[2 * pf + (sine ? 1 : 0)];
+    const float ph = u2f(pf << 16);
+    return sine ? __sinf(ph) : __cosf(ph);
+}
+
+template <int D, int RWM, bool PQK, bool PQV>
+__global__ __launch_bounds__(kFaThreads, 2) void fmag_attn_kernel(FmAttnArgs a) {
+    constexpr int T = D / 16, S = D / 32, NB = D / 2 + 1;
+    constexpr int NP = (32 * RWM + 63) / 64;           // record words of a 32-token chunk per lane
+    extern __shared__ __align__(16) uint8_t smem[];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int n = lane & 15, g = lane >> 4;
+    float* csk = reinterpret_cast<float*>(smem);       // [256][2] cos, sin of the K phase levels
+    float* csv = csk + 512;                            // the V phase levels
+    const int RWk = a.tk.rec_words, RWv = a.tv.rec_words;
+    const int WS = 32 * (RWk + RWv) + 4;
+    _Float16* qlo = reinterpret_cast<_Float16*>(smem + 4096) + wave * (16 * D);   // this wave's q' remainders
+    uint32_t* sk = reinterpret_cast<uint32_t*>(smem + 4096 + (kFaThreads / 64) * 16 * D * 2) + wave * WS;
+    uint32_t* sv = sk + 32 * RWk + 2;
+    const uint32_t bk = (uint32_t)a.tk.b, pk_ = (uint32_t)a.tk.p, bv = (uint32_t)a.tv.b, pv_ = (uint32_t)a.tv.p;
+    {
+        if (PQK)
+            for (int i = threadIdx.x; i < (2 << pk_); i += kFaThreads) csk[i] = a.tk.cs[i];
+        if (PQV)
+            for (int i = threadIdx.x; i < (2 << pv_); i += kFaThreads) csv[i] = a.tv.cs[i];
+        for (int i = lane; i < WS; i += 64) sk[i] = 0u;
+    }
+    __syncthreads();
+    const int64_t item = (int64_t)blockIdx.x * (kFaThreads / 64) + wave;
+    if (item >= a.n_streams * a.n_split) return;
+    const int64_t st = item / a.n_split, sp = item % a.n_split;
+    int64_t len = a.n_tokens;
+    if (a.lens) len = min(max((int64_t)a.lens[st / a.hkv], (int64_t)0), a.n_tokens);
+    const int64_t t0 = sp * a.tps, t1 = min(t0 + a.tps, len);
+
+    half8 Bq[S];
+#pragma unroll
+    for (int s = 0; s < S; ++s) {
+        Bq[s] = *reinterpret_cast<const half8*>(a.qp + ((size_t)st * 16 + n) * D + 32 * s + 8 * g);
+        *reinterpret_cast<half8*>(qlo + n * D + 32 * s + 8 * g) =
+            *reinterpret_cast<const half8*>(a.qplo + ((size_t)st * 16 + n) * D + 32 * s + 8 * g);
+    }
+    const float qs = a.qscale[st * 16 + n];
+    const float vden = 1.0f / (float)((1 << bv) - 1);
+
+    const uint32_t* ks = a.kin + (size_t)st * a.n_tokens * RWk;
+    const uint32_t* vs = a.vin + (size_t)st * a.n_tokens * RWv;
+    uint32_t pk[NP], pv[NP];
+    auto fetch = [&](int64_t c0) {
+        const int valid = c0 < t1 ? (int)min((int64_t)32, a.n_tokens - c0) : 0;
+        fetch_rec<NP>(ks + (size_t)c0 * RWk, 32 * RWk, valid * RWk, lane, pk);
+        fetch_rec<NP>(vs + (size_t)c0 * RWv, 32 * RWv, valid * RWv, lane, pv);
+    };
+    float m = -INFINITY, l = 0.0f;
+    floatx4 acc[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) acc[t] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+    fetch(t0);
+    for (int64_t c0 = t0; c0 < t1; c0 += 32) {
+#pragma unroll
+        for (int j = 0; j < NP; ++j) {
+            if (lane + 64 * j < 32 * RWk) sk[lane + 64 * j] = pk[j];
+            if (lane + 64 * j < 32 * RWv) sv[lane + 64 * j] = pv[j];
+        }
+        fetch(c0 + 32);
+        // the lane indices pass through an empty asm each chunk so that the field positions derived
+        // from them are recomputed here instead of being kept live across the loop
+        int gl = g, nl = n;
+        asm volatile("" : "+v"(gl), "+v"(nl));
+        // scores of the two 16-token halves
+        float sc[2][4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            floatx4 d4 = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int s = 0; s < S; ++s) {
+                float x8[8];
+                int es;
+                spectrum8<D, PQK>(sk + (16 * h + nl) * RWk, RWk, bk, pk_, s, gl, csk, x8, es);
+                u32x4 hv, lv;
+#pragma unroll
+                for (int i = 0; i < 8; i += 2) {
+                    const _Float16 h0 = (_Float16)x8[i], h1 = (_Float16)x8[i + 1];
+                    hv[i / 2] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+                    lv[i / 2] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(x8[i] - (float)h0)) |
+                                ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(x8[i + 1] - (float)h1)) << 16);
+                }
+                const half8 bl = *reinterpret_cast<const half8*>(qlo + nl * D + 32 * s + 8 * gl);
+                d4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(hv), Bq[s], d4, 0, 0, 0);
+                d4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(lv), Bq[s], d4, 0, 0, 0);
+                d4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(hv), bl, d4, 0, 0, 0);
+                __builtin_amdgcn_sched_barrier(0);   // one k-step's spectrum at a time
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int tok = 16 * h + 4 * gl + r;
+                const float hi = u2f(sk[tok * RWk + RWk - 1]);
+                const int es = hi > 0.0f ? 141 - (int)((f2u(hi) >> 23) & 0xffu) : 0;
+                sc[h][r] = (c0 + tok < t1) ? d4[r] * qs * __builtin_amdgcn_ldexpf(1.0f, -es) : -INFINITY;
+            }
+        }
+        // online softmax for query n (its 32 scores live on lanes n, n+16, n+32, n+48)
+        float cm = sc[0][0];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) cm = fmaxf(cm, sc[h][r]);
+        float x0 = cm, x1 = cm;
+        xswap16(x0, x1);
+        cm = fmaxf(x0, x1);
+        x0 = cm;
+        x1 = cm;
+        xswap32(x0, x1);
+        cm = fmaxf(x0, x1);
+        const float mn = fmaxf(m, cm);
+        const float alpha = mn == -INFINITY ? 1.0f : exp2f(m - mn);
+        float p[2][4], psum = 0.0f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                p[h][r] = mn == -INFINITY ? 0.0f : exp2f(sc[h][r] - mn);
+                psum += p[h][r];
+            }
+        l = l * alpha + sum4(psum);
+        m = mn;
+        half8 P, PL;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const float pf = p[i >> 2][i & 3];
+            P[i] = (_Float16)pf;
+            PL[i] = (_Float16)(pf - (float)P[i]);
+        }
+        // values: one power of two for the chunk from its largest magnitude (every |X̂| <= hi)
+        float hm = row_max(u2f(sv[(lane & 31) * RWv + RWv - 1]));   // 16 tokens per row, then both rows
+        x0 = hm;
+        x1 = hm;
+        xswap16(x0, x1);
+        hm = fmaxf(x0, x1);
+        const int ev = hm > 0.0f ? 141 - (int)((f2u(hm) >> 23) & 0xffu) : 0;
+        const float vsc = __builtin_amdgcn_ldexpf(1.0f, -ev);
+        float vlo[8], vdl[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int tok = i < 4 ? 4 * gl + i : 16 + 4 * gl + i - 4;
+            vlo[i] = u2f(sv[tok * RWv + RWv - 2]);
+            vdl[i] = (u2f(sv[tok * RWv + RWv - 1]) - vlo[i]) * vden;
+        }
+#pragma unroll
+        for (int t = 0; t < T; ++t) {
+            const int c = 16 * t + nl;
+            const bool im = c > D / 2;
+            const uint32_t kb = (uint32_t)(c <= D / 2 ? c : c - D / 2);
+            u32x4 av;
+#pragma unroll
+            for (int i = 0; i < 8; i += 2) {
+                uint32_t h2[2];
+#pragma unroll
+                for (int k = 0; k < 2; ++k) {
+                    const int ii = i + k, tok = ii < 4 ? 4 * gl + ii : 16 + 4 * gl + ii - 4;
+                    const uint32_t* rec = sv + tok * RWv;
+                    const float mag = fmaf((float)get_field(rec, kb * bv, bv), vdl[ii], vlo[ii]);
+                    const float trig = phase_trig<PQV>(rec, (uint32_t)NB * bv + kb * pv_, pv_, im, csv);
+                    h2[k] = __builtin_bit_cast(uint16_t, (_Float16)__builtin_amdgcn_ldexpf(mag * trig, ev));
+                }
+                av[i / 2] = h2[0] | (h2[1] << 16);
+            }
+            floatx4 d = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(av), P, floatx4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+            d = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_h8(av), PL, d, 0, 0, 0);
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[t][r] = fmaf(d[r], vsc, acc[t][r] * alpha);
+            __builtin_amdgcn_sched_barrier(0);   // keep each coordinate tile's reads next to its product
+        }
+    }
+    float* pp = a.part + ((size_t)item * 16 + n) * D;
+#pragma unroll
+    for (int t = 0; t < T; ++t)
+        *reinterpret_cast<floatx4*>(pp + 16 * t + 4 * g) = acc[t];
+    if (g == 0) *reinterpret_cast<float2*>(a.ml + ((size_t)item * 16 + n) * 2) = float2{m, l};
+}
+
+// one block of D threads per output row (b, h): merge the splits, apply the inverse real DFT
+template <int D>
+__global__ __launch_bounds__(D) void fmag_attn_combine_kernel(FmAttnArgs a) {
+    __shared__ float y[D];
+    const int k = threadIdx.x;
+    const int64_t row = blockIdx.x, b = row / a.hq, h = row % a.hq;
+    const int64_t hk = h / a.g, qi = h % a.g, st = b * a.hkv + hk;
+    float M = -INFINITY;
+    for (int64_t sp = 0; sp < a.n_split; ++sp) M = fmaxf(M, a.ml[((st * a.n_split + sp) * 16 + qi) * 2]);
+    float L = 0.0f, acc = 0.0f;
+    if (M != -INFINITY) {
+        for (int64_t sp = 0; sp < a.n_split; ++sp) {
+            const size_t r = (size_t)(st * a.n_split + sp) * 16 + qi;
+            const float w = exp2f(a.ml[r * 2] - M);
+            L += a.ml[r * 2 + 1] * w;
+            acc += a.part[r * D + k] * w;
+        }
+        acc = acc / L;
+    }
+    y[k] = acc;
+    __syncthreads();
+    const float* G = a.tv.G32 + (size_t)k * D;
+    float o = 0.0f;
+    for (int c = 0; c < D; ++c) o = fmaf(G[c], y[c], o);
+    const size_t oi = (size_t)row * D + k;
+    if (a.out_bf16) static_cast<__bf16*>(a.out)[oi] = (__bf16)o;
+    else static_cast<float*>(a.out)[oi] = o;
+}
+
+template <int D, int RWM, bool PQK, bool PQV>
+static hipError_t launch_fattn(const FmAttnArgs& a, hipStream_t s) {
+    const size_t lds = 4096 + (size_t)(kFaThreads / 64) * 16 * D * 2 +
+                       (size_t)(kFaThreads / 64) * (32 * (a.tk.rec_words + a.tv.rec_words) + 4) * 4;
+    const void* kern = reinterpret_cast<const void*>(&fmag_attn_kernel<D, RWM, PQK, PQV>);
+    if (lds > 65536) {
+        const hipError_t e = allow_lds(kern);
+        if (e != hipSuccess) return e;
+    }
+    const unsigned blocks = (unsigned)((a.n_streams * a.n_split + kFaThreads / 64 - 1) / (kFaThreads / 64));
+    hipLaunchKernelGGL((fmag_attn_kernel<D, RWM, PQK, PQV>), dim3(blocks), dim3(kFaThreads), lds, s, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const unsigned rows = (unsigned)(a.n_streams / a.hkv * a.hq);
+    hipLaunchKernelGGL((fmag_attn_combine_kernel<D>), dim3(rows), dim3(D), 0, s, a);
+    return hipGetLastError();
+}
+
+template <int D, int RWM>
+static hipError_t launch_fattn_pq(const FmAttnArgs& a, hipStream_t s) {
+    const bool qk = a.tk.p <= 8, qv = a.tv.p <= 8;
+    if (qk) return qv ? launch_fattn<D, RWM, true, true>(a, s) : launch_fattn<D, RWM, true, false>(a, s);
+    return qv ? launch_fattn<D, RWM, false, true>(a, s) : launch_fattn<D, RWM, false, false>(a, s);
+}
+
+// records of up to 28 words (b + p <= 12 at d = 128, every width at d = 64) take the smaller
+// register prefetch; the larger covers 8-bit magnitudes with bf16 phases at d = 128 (51 words)
+hipError_t launch_fmag_attention(const FmAttnArgs& a, hipStream_t s) {
+    const int rw = max(a.tk.rec_words, a.tv.rec_words);
+    if (a.tk.d == 64) return launch_fattn_pq<64, 28>(a, s);
+    return rw <= 28 ? launch_fattn_pq<128, 28>(a, s) : launch_fattn_pq<128, 51>(a, s);
+}
+
 }  // namespace tq

@@ -3,6 +3,7 @@
 // KV Cache Quantization", forum thread, "Method").
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <map>
@@ -79,21 +80,25 @@ int build(const tq_fmag_params* p, FmDev* out) {
             cs[2 * i] = (float)std::cos(a);
             cs[2 * i + 1] = (float)std::sin(a);
         }
-    std::vector<float> U((size_t)d * d), w(d);
+    std::vector<float> U((size_t)d * d), w(d), G((size_t)d * d);
     for (int j = 0; j < d; ++j)
-        for (int c = 0; c < d; ++c) U[(size_t)j * d + c] = (float)dft_coef(d, j, c);
+        for (int c = 0; c < d; ++c) {
+            U[(size_t)j * d + c] = (float)dft_coef(d, j, c);
+            G[(size_t)j * d + c] = (float)idft_coef(d, j, c);
+        }
     for (int c = 0; c < d; ++c) w[c] = (float)((c == 0 || c == d / 2 ? 1.0 : 2.0) / d);
 
     size_t off = 0;
     auto place = [&](size_t bytes) { const size_t o = off; off = (off + bytes + 255) / 256 * 256; return o; };
     const size_t o_e = place(enc.size() * 2), o_d = place(dec.size() * 2), o_c = place(cs.size() * 4),
-                 o_u = place(U.size() * 4), o_w = place(w.size() * 4);
+                 o_u = place(U.size() * 4), o_w = place(w.size() * 4), o_g = place(G.size() * 4);
     std::vector<uint8_t> blob(off);
     std::memcpy(blob.data() + o_e, enc.data(), enc.size() * 2);
     std::memcpy(blob.data() + o_d, dec.data(), dec.size() * 2);
     std::memcpy(blob.data() + o_c, cs.data(), cs.size() * 4);
     std::memcpy(blob.data() + o_u, U.data(), U.size() * 4);
     std::memcpy(blob.data() + o_w, w.data(), w.size() * 4);
+    std::memcpy(blob.data() + o_g, G.data(), G.size() * 4);
     void* mem = nullptr;
     if (hipMalloc(&mem, blob.size()) != hipSuccess) return TQ_EHIP;
     if (hipMemcpy(mem, blob.data(), blob.size(), hipMemcpyHostToDevice) != hipSuccess) {
@@ -114,6 +119,7 @@ int build(const tq_fmag_params* p, FmDev* out) {
     t.qprep.n_heads = 1;
     t.qprep.U32 = reinterpret_cast<const float*>(base + o_u);
     t.qprep.sigma = reinterpret_cast<const float*>(base + o_w);
+    t.G32 = reinterpret_cast<const float*>(base + o_g);
     t.blob = mem;
     *out = t;
     return TQ_OK;
@@ -140,6 +146,27 @@ int tables(const tq_fmag_params* p, FmDev* out, int* cus) {
     }
     *out = it->second;
     return TQ_OK;
+}
+
+// attention split geometry, a function of the arguments only: about as many (stream, split) waves
+// as 256 CUs hold at eight per CU, splits of at least 256 tokens in multiples of 32, at most 1024
+struct AttnWs {
+    int64_t tps, n_split, o_qlo, o_qs, o_part, o_ml, total;
+};
+AttnWs attn_ws(int d, int64_t streams, int64_t n_tokens) {
+    AttnWs w{};
+    int64_t ns = (256 * 8 + streams - 1) / (streams > 0 ? streams : 1);
+    ns = std::min(ns, (n_tokens + 255) / 256);
+    ns = std::max<int64_t>(std::min<int64_t>(ns, 1024), 1);
+    w.tps = std::max<int64_t>(((n_tokens + ns - 1) / ns + 31) / 32 * 32, 32);
+    w.n_split = std::max<int64_t>((n_tokens + w.tps - 1) / w.tps, 1);
+    auto al = [](int64_t x) { return (x + 255) / 256 * 256; };
+    w.o_qlo = al(streams * 16 * d * 2);
+    w.o_qs = w.o_qlo + al(streams * 16 * d * 2);
+    w.o_part = w.o_qs + al(streams * 16 * 4);
+    w.o_ml = w.o_part + al(streams * w.n_split * 16 * d * 4);
+    w.total = w.o_ml + al(streams * w.n_split * 16 * 2 * 4);
+    return w;
 }
 
 }  // namespace
@@ -246,6 +273,74 @@ int tq_fmag_qk_scores(const tq_fmag_params* p, const void* q, tq_dtype q_dtype, 
     a.nq_pad = nq_pad;
     a.tiles_per_stream = (n_tokens + 15) / 16;
     return launch_fmag_scores(a, cus, s) == hipSuccess ? TQ_OK : TQ_EHIP;
+}
+
+size_t tq_fmag_attention_workspace_bytes(const tq_fmag_params* pk, int32_t batch, int32_t n_q_heads,
+                                         int32_t n_kv_heads, int64_t n_tokens) {
+    if (check(pk) != TQ_OK || batch < 0 || n_q_heads < 1 || n_kv_heads < 1 || n_tokens < 0) return 0;
+    return (size_t)attn_ws(pk->d, (int64_t)batch * n_kv_heads, n_tokens).total;
+}
+
+int tq_fmag_decode_attention(const tq_fmag_params* pk, const tq_fmag_params* pv, const void* q, tq_dtype q_dtype,
+                             int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, const void* packed_k,
+                             const void* packed_v, int64_t n_tokens, const int32_t* lengths, float softmax_scale,
+                             void* out, tq_dtype out_dtype, void* workspace, size_t workspace_bytes, void* stream) {
+    if (check(pk) != TQ_OK || check(pv) != TQ_OK || pk->d != pv->d) return TQ_EINVAL;
+    if (batch < 0 || n_q_heads < 1 || n_kv_heads < 1 || n_tokens < 0) return TQ_EINVAL;
+    if (n_q_heads % n_kv_heads != 0 || n_q_heads / n_kv_heads > 16) return TQ_EINVAL;
+    if ((q_dtype != TQ_F32 && q_dtype != TQ_BF16) || (out_dtype != TQ_F32 && out_dtype != TQ_BF16)) {
+        const bool known = q_dtype == TQ_F16 || out_dtype == TQ_F16;
+        return known ? TQ_EUNSUPPORTED : TQ_EINVAL;
+    }
+    if (!std::isfinite(softmax_scale) || softmax_scale < 0.0f) return TQ_EINVAL;
+    if (batch == 0) return TQ_OK;
+    if (!q || !out || !workspace || (n_tokens > 0 && (!packed_k || !packed_v))) return TQ_EINVAL;
+    if (!aligned16(q) || !aligned16(out) || !aligned16(workspace) ||
+        (n_tokens > 0 && (!aligned16(packed_k) || !aligned16(packed_v))))
+        return TQ_EALIGN;
+    if (lengths && (reinterpret_cast<uintptr_t>(lengths) & 3u)) return TQ_EALIGN;
+    const int64_t streams = (int64_t)batch * n_kv_heads;
+    const AttnWs w = attn_ws(pk->d, streams, n_tokens);
+    if (workspace_bytes < (size_t)w.total) return TQ_EWORKSPACE;
+    FmAttnArgs a{};
+    int cus = 0;
+    int rc = tables(pk, &a.tk, &cus);
+    if (rc != TQ_OK) return rc;
+    rc = tables(pv, &a.tv, &cus);
+    if (rc != TQ_OK) return rc;
+    const hipStream_t s = static_cast<hipStream_t>(stream);
+    uint8_t* ws = static_cast<uint8_t*>(workspace);
+    const float scale = softmax_scale > 0.0f ? softmax_scale : 1.0f / std::sqrt((float)pk->d);
+    SqScoresArgs qa{};
+    qa.t = a.tk.qprep;
+    qa.q = q;
+    qa.q_bf16 = q_dtype == TQ_BF16;
+    qa.qp = reinterpret_cast<_Float16*>(ws);
+    qa.qplo = reinterpret_cast<_Float16*>(ws + w.o_qlo);
+    qa.qscale = reinterpret_cast<float*>(ws + w.o_qs);
+    qa.qmul = scale * 1.4426950408889634f;   // scores in base-2 units for exp2
+    qa.n_streams = streams;
+    qa.n_q = n_q_heads / n_kv_heads;
+    qa.nq_pad = 16;
+    if (launch_sq_qprep(qa, s) != hipSuccess) return TQ_EHIP;
+    a.qp = qa.qp;
+    a.qplo = qa.qplo;
+    a.qscale = qa.qscale;
+    a.kin = static_cast<const uint32_t*>(packed_k);
+    a.vin = static_cast<const uint32_t*>(packed_v);
+    a.lens = lengths;
+    a.part = reinterpret_cast<float*>(ws + w.o_part);
+    a.ml = reinterpret_cast<float*>(ws + w.o_ml);
+    a.out = out;
+    a.out_bf16 = out_dtype == TQ_BF16;
+    a.n_streams = streams;
+    a.n_tokens = n_tokens;
+    a.tps = w.tps;
+    a.n_split = w.n_split;
+    a.hkv = n_kv_heads;
+    a.hq = n_q_heads;
+    a.g = n_q_heads / n_kv_heads;
+    return launch_fmag_attention(a, s) == hipSuccess ? TQ_OK : TQ_EHIP;
 }
 
 }  // extern "C"

@@ -22,6 +22,7 @@ struct FmDev {
     float dec_scale = 0.0f;           // 2^-e
     const float* cs = nullptr;        // [2^p][2] cos, sin of the phase levels (p <= 8)
     SqDev qprep;                      // U = the DFT matrix [j][c], σ = w_c/d: the query side of the scores
+    const float* G32 = nullptr;       // [j][c] the weighted inverse real DFT in fp32 (attention combine)
     void* blob = nullptr;
 };
 
@@ -51,9 +52,28 @@ struct FmScoresArgs {
     int64_t blocks_per_stream, tiles_per_block;
 };
 
+// decode-attention over Fmag K and V caches: one wave per (stream, split); the partial outputs stay
+// in the spectrum domain (Σ_t p_t X̂_t), the combine merges the splits and applies the inverse DFT
+struct FmAttnArgs {
+    FmDev tk, tv;
+    const _Float16* qp;     // [streams][16][d] projected queries (q' of the scores, times scale·log2 e)
+    const _Float16* qplo;   // [streams][16][d] their fp16 remainders (hi + lo carry q' to about 2^-22)
+    const float* qscale;    // [streams][16]
+    const uint32_t* kin;
+    const uint32_t* vin;
+    const int32_t* lens;    // [batch] valid tokens, or null
+    float* part;            // [streams·n_split][16][d] unnormalised spectrum-domain outputs
+    float* ml;              // [streams·n_split][16][2] running max (base 2) and sum
+    void* out;
+    bool out_bf16;
+    int64_t n_streams, n_tokens, tps, n_split;
+    int hkv, hq, g;
+};
+
 hipError_t launch_fmag_encode(const FmEncodeArgs& a, int num_cus, hipStream_t s);
 hipError_t launch_fmag_decode(const FmDecodeArgs& a, bool out_bf16, int num_cus, hipStream_t s);
 hipError_t launch_fmag_scores(const FmScoresArgs& a, int num_cus, hipStream_t s);
+hipError_t launch_fmag_attention(const FmAttnArgs& a, hipStream_t s);
 void fmag_clear_tables();
 
 }  // namespace tq

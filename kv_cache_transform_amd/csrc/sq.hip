@@ -570,7 +570,10 @@ __global__ __launch_bounds__(D) void sq_qprep_kernel(SqScoresArgs a) {
     m = red[0];
     for (int w = 1; w < D / 64; ++w) m = fmaxf(m, red[w]);
     const int e = m > 0.0f ? 13 - ((int)((f2u(m) >> 23) & 0xffu) - 127) : 0;
-    a.qp[(size_t)row * D + k] = (_Float16)__builtin_amdgcn_ldexpf(acc, e);
+    const float qv2 = __builtin_amdgcn_ldexpf(acc, e);
+    const _Float16 qh = (_Float16)qv2;
+    a.qp[(size_t)row * D + k] = qh;
+    if (a.qplo) a.qplo[(size_t)row * D + k] = (_Float16)(qv2 - (float)qh);
     if (k == 0) a.qscale[row] = __builtin_amdgcn_ldexpf(1.0f, -e);
     if (a.t.m > 0) {
         // the selective sketch's side: p = S q_Z over the first 32 dimensions (zero rows and columns

@@ -68,6 +68,7 @@ struct SqScoresArgs {
     _Float16* pp;           // workspace with a sketch: [streams][nq_pad][64] fp16 of (S q_Z)·2^e'_row
     float* pscale;          // [streams][nq_pad] 2^-e'_row · sqrt(pi/2)/m (q_Z already carries qmul)
     float qmul;             // factor on every projected query (1 for scores; scale·log2 e for attention)
+    _Float16* qplo = nullptr;  // optional [streams][nq_pad][d]: the fp16 remainder (q'·2^e - qp) of each entry
     int64_t n_streams, n_tokens, n_q, nq_pad, tiles_per_stream;
     int64_t blocks_per_stream, tiles_per_block;
 };

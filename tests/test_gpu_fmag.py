@@ -135,3 +135,54 @@ def test_fmag_leaves_other_bytes_and_rejects_fp32():
     assert torch.all(buf[2 * 40 * rb:] == 0xA5)
     with pytest.raises(T.TQError):
         codec.encode(x.float())
+
+
+@pytest.mark.parametrize("batch,hq,hkv,N,d,kind,bpk,bpv,lens,out_dtype", [
+    (2, 8, 2, 1000, 128, "rope", (4, 8), (4, 8), None, torch.float32),
+    (1, 4, 4, 777, 64, "gauss", (3, 6), (4, 16), None, torch.bfloat16),
+    (2, 16, 1, 300, 128, "tdist", (4, 16), (2, 3), None, torch.float32),
+    (3, 8, 2, 600, 128, "gauss", (8, 16), (8, 16), [600, 1, 0], torch.float32),   # 51-word records
+    (2, 4, 2, 2500, 64, "rope", (1, 1), (5, 8), [2500, 1234], torch.float32),
+])
+def test_fmag_decode_attention(batch, hq, hkv, N, d, kind, bpk, bpv, lens, out_dtype):
+    """Attention rows from the GPU's own records against softmax(scale·ŝ) @ x̂ of the oracle:
+    within 2e-3 relative L2 per row (5e-3 with bf16 output)."""
+    S, G = batch * hkv, hq // hkv
+    ck, cv = T.FmagCodec(d, *bpk), T.FmagCodec(d, *bpv)
+    K = _data(kind, S, N, d, 51)
+    V = _data(kind, S, N, d, 52)
+    pk, pv = ck.encode(K), cv.encode(V)
+    q = torch.randn(batch, hq, d, generator=torch.Generator(device=DEV).manual_seed(3), device=DEV)
+    lt = None if lens is None else torch.tensor(lens, dtype=torch.int32, device=DEV)
+    out = T.fmag_decode_attention(ck, cv, q, pk, pv, hkv, N, out_dtype=out_dtype, lengths=lt)
+    torch.cuda.synchronize()
+    got = out.float().cpu().numpy()
+    q64 = q.cpu().numpy().astype(np.float64)
+    Wk, Wv = F.record_words(d, *bpk), F.record_words(d, *bpv)
+    wk = pk.cpu().numpy()[: S * N * Wk * 4].view(np.uint32).reshape(S, N, Wk)
+    wv = pv.cpu().numpy()[: S * N * Wv * 4].view(np.uint32).reshape(S, N, Wv)
+    worst = 0.0
+    for b in range(batch):
+        n_b = N if lens is None else lens[b]
+        for h in range(hq):
+            st = b * hkv + h // G
+            if n_b == 0:
+                assert np.all(got[b, h] == 0.0)
+                continue
+            rk = F.unpack(wk[st, :n_b], *bpk, d)
+            rv = F.unpack(wv[st, :n_b], *bpv, d)
+            sc = F.scores(q64[b, h][None, :], rk, *bpk, d)
+            want = F.attention(sc, rv, *bpv, d, 1.0 / math.sqrt(d))[0]
+            worst = max(worst, np.linalg.norm(got[b, h] - want) / np.linalg.norm(want))
+    print(f"fmag attention worst row rel {worst:.2e}")
+    assert worst < (2e-3 if out_dtype == torch.float32 else 5e-3)
+
+
+def test_fmag_attention_validates_arguments():
+    ck, c2 = T.FmagCodec(64, 4, 8), T.FmagCodec(128, 4, 8)
+    q = torch.randn(1, 4, 64, device=DEV)
+    pk = ck.encode(_data("gauss", 2, 32, 64, 1))
+    with pytest.raises(T.TQError):          # K and V head sizes differ
+        T.fmag_decode_attention(ck, c2, q, pk, pk, 2, 32)
+    with pytest.raises(T.TQError):          # more than 16 query heads per kv head
+        T.fmag_decode_attention(ck, ck, torch.randn(1, 34, 64, device=DEV), pk, pk, 2, 32)

@@ -140,3 +140,27 @@ def test_record_round_trip_and_layout(b, p):
         assert np.array_equal(u["pidx"], r["pidx"])
     # the first field is the DC magnitude index, LSB first
     assert (w[:, 0] & ((1 << b) - 1)).tolist() == r["q"][:, 0].tolist()
+
+
+@pytest.mark.parametrize("b,p", [(4, 8), (3, 16)])
+def test_attention_pins(b, p):
+    """softmax(scale·ŝ) @ x̂ ("Method": attention runs on the reconstructed cache): a single token
+    returns its reconstruction; equal scores give the mean; one dominant score gives its token; and
+    by linearity of the inverse FFT the result equals irfft of the weighted spectra."""
+    d = 64
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((40, d))
+    r = F.encode(x, b, p)
+    xh = F.decode(r, b, p, d)
+    one = {k: (v[:1] if isinstance(v, np.ndarray) and v.shape[:1] == (40,) else v) for k, v in r.items()}
+    assert np.allclose(F.attention(np.array([[3.7]]), one, b, p, d, 0.125), xh[:1], rtol=0, atol=1e-12)
+    assert np.allclose(F.attention(np.zeros((2, 40)), r, b, p, d, 1.0), np.tile(xh.mean(axis=0), (2, 1)),
+                       rtol=0, atol=1e-12)
+    s = np.zeros((1, 40))
+    s[0, 17] = 1e4
+    assert np.allclose(F.attention(s, r, b, p, d, 1.0)[0], xh[17], rtol=0, atol=1e-12)
+    sc = rng.standard_normal((3, 40)) * 4
+    w = np.exp(0.5 * sc - (0.5 * sc).max(axis=1, keepdims=True))
+    w /= w.sum(axis=1, keepdims=True)
+    freq = np.fft.irfft(w @ F.spectrum(r, b, p), n=d)
+    assert np.allclose(F.attention(sc, r, b, p, d, 0.5), freq, rtol=0, atol=1e-12)
