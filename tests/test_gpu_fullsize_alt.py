@@ -1,7 +1,8 @@
 """GPU parity of the SpectralQuant and Fourier-magnitude paths at the benchmark's full shape (K and V
 [16·8, 131072, 128] bf16, RoPE-rotated Gaussian), in the launch configuration the benchmark times:
 the HIP path runs over the whole tensors, the oracles check token ranges (start, middle, ragged end)
-of a few streams and whole attention rows.  Tolerances as in test_gpu_sq.py and test_gpu_fmag.py."""
+of a few streams and whole attention rows (SpectralQuant and Fmag caches).  Tolerances as in
+test_gpu_sq.py and test_gpu_fmag.py."""
 import numpy as np
 import pytest
 import torch
@@ -83,8 +84,8 @@ def test_sq_full_shape_encode_decode_attention(kv):
 
 
 @pytest.mark.timeout(900)
-def test_fmag_full_shape_encode_decode_scores(kv):
-    K, _ = kv
+def test_fmag_full_shape_encode_decode_scores_attention(kv):
+    K, V = kv
     codec = T.FmagCodec(D, 4, 8)
     packed = codec.encode(K)
     xh = codec.decode(packed, B * HKV, N, torch.float32)
@@ -107,3 +108,17 @@ def test_fmag_full_shape_encode_decode_scores(kv):
     want = F.scores(q.cpu().numpy()[0].astype(np.float64), rec, 4, 8, D)
     rel = np.linalg.norm(sc - want, axis=1) / np.linalg.norm(want, axis=1)
     assert rel.max() < 2e-3
+    # whole attention rows over the full context, K and V both Fmag caches (the benchmark's launch)
+    pv = codec.encode(V)
+    qa = I.cfg4_queries(B, HQ, D, N, 4003, device=DEV)
+    out = T.fmag_decode_attention(codec, codec, qa, packed, pv, HKV, N, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    q64 = _f64(qa)
+    for b, h in ((0, 0), (9, 21), (15, 31)):
+        stq = b * HKV + h // (HQ // HKV)
+        rk = F.unpack(packed[stq * N * W * 4:(stq + 1) * N * W * 4].cpu().numpy().view(np.uint32).reshape(N, W), 4, 8, D)
+        rv = F.unpack(pv[stq * N * W * 4:(stq + 1) * N * W * 4].cpu().numpy().view(np.uint32).reshape(N, W), 4, 8, D)
+        scr = F.scores(q64[b, h][None, :], rk, 4, 8, D)
+        want = F.attention(scr, rv, 4, 8, D, 1.0 / np.sqrt(D))[0]
+        assert np.linalg.norm(got[b, h] - want) <= 2e-3 * np.linalg.norm(want), (b, h)
