@@ -304,12 +304,31 @@ __device__ __forceinline__ void spectrum8(const uint32_t* rec, int RW, uint32_t 
     es = hi > 0.0f ? 141 - (int)((f2u(hi) >> 23) & 0xffu) : 0;
     const bool im = s >= S / 2;
     const uint32_t k0 = (uint32_t)(32 * (im ? s - S / 2 : s) + 8 * g);
+    // the 8 bins' fields are contiguous: one 64-bit window of magnitudes (8 b <= 64 bits) and one or
+    // two of phases (8 p <= 128 bits), each from three record words
+    auto window = [&](uint32_t pos) {
+        const uint32_t* w = rec + (pos >> 5);
+        const uint32_t sh = pos & 31u;
+        return ((uint64_t)__builtin_amdgcn_alignbit(w[2], w[1], sh) << 32) | __builtin_amdgcn_alignbit(w[1], w[0], sh);
+    };
+    const uint64_t mw = window(k0 * b);
+    const uint32_t ppos = (uint32_t)NB * b + k0 * p;
+    const uint64_t pw0 = window(ppos);
+    const uint64_t pw1 = PQ ? 0ull : window(ppos + 64u);
+    const uint32_t mmask = (1u << b) - 1u;
+    const uint64_t pmask = (1ull << p) - 1ull;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-        const bool nyq = s == S / 2 && g == 0 && i == 0;   // coordinate d/2 only
-        const uint32_t kb = nyq ? (uint32_t)(D / 2) : k0 + i;
-        const float mag = fmaf((float)get_field(rec, kb * b, b), delta, lo);
-        const uint32_t pf = get_field(rec, NB * b + kb * p, p);
+        const bool nyq = s == S / 2 && g == 0 && i == 0;   // coordinate d/2 only: the real Nyquist bin
+        uint32_t mf = (uint32_t)(mw >> (i * b)) & mmask;
+        uint32_t pf;
+        if constexpr (PQ) pf = (uint32_t)((pw0 >> (i * p)) & pmask);
+        else pf = (uint32_t)((i < 4 ? pw0 >> (16 * i) : pw1 >> (16 * (i - 4))) & 0xffffu);
+        if (nyq) {
+            mf = get_field(rec, (uint32_t)(D / 2) * b, b);
+            pf = get_field(rec, (uint32_t)NB * b + (uint32_t)(D / 2) * p, p);
+        }
+        const float mag = fmaf((float)mf, delta, lo);
         float trig;
         if constexpr (PQ) {
             trig = cs[2 * pf + ((im && !nyq) ? 1 : 0)];
@@ -551,7 +570,7 @@ __device__ __forceinline__ float phase_trig(const uint32_t* rec, uint32_t pos, u
 }
 
 template <int D, int RWM, bool PQK, bool PQV>
-__global__ __launch_bounds__(kFaThreads, 2) void fmag_attn_kernel(FmAttnArgs a) {
+__global__ __launch_bounds__(kFaThreads, RWM <= 28 ? 3 : 2) void fmag_attn_kernel(FmAttnArgs a) {
     constexpr int T = D / 16, S = D / 32, NB = D / 2 + 1;
     constexpr int NP = (32 * RWM + 63) / 64;           // record words of a 32-token chunk per lane
     extern __shared__ __align__(16) uint8_t smem[];

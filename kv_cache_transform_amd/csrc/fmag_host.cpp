@@ -149,13 +149,14 @@ int tables(const tq_fmag_params* p, FmDev* out, int* cus) {
 }
 
 // attention split geometry, a function of the arguments only: about as many (stream, split) waves
-// as 256 CUs hold at eight per CU, splits of at least 256 tokens in multiples of 32, at most 1024
+// as 256 CUs hold at twelve per CU (three per SIMD), splits of at least 256 tokens in multiples of
+// 32, at most 1024
 struct AttnWs {
     int64_t tps, n_split, o_qlo, o_qs, o_part, o_ml, total;
 };
 AttnWs attn_ws(int d, int64_t streams, int64_t n_tokens) {
     AttnWs w{};
-    int64_t ns = (256 * 8 + streams - 1) / (streams > 0 ? streams : 1);
+    int64_t ns = (256 * 12 + streams - 1) / (streams > 0 ? streams : 1);
     ns = std::min(ns, (n_tokens + 255) / 256);
     ns = std::max<int64_t>(std::min<int64_t>(ns, 1024), 1);
     w.tps = std::max<int64_t>(((n_tokens + ns - 1) / ns + 31) / 32 * 32, 32);
