@@ -186,3 +186,31 @@ def test_fmag_attention_validates_arguments():
         T.fmag_decode_attention(ck, c2, q, pk, pk, 2, 32)
     with pytest.raises(T.TQError):          # more than 16 query heads per kv head
         T.fmag_decode_attention(ck, ck, torch.randn(1, 34, 64, device=DEV), pk, pk, 2, 32)
+
+
+@pytest.mark.parametrize("N", [0, 1, 33])
+def test_fmag_attention_short_caches(N):
+    """An empty cache gives zero rows; one token returns its reconstruction; a ragged chunk."""
+    ck = T.FmagCodec(128, 4, 8)
+    B, Hq, Hkv = 2, 8, 2
+    K = _data("gauss", B * Hkv, max(N, 1), 128, 61)[:, :N].contiguous()
+    V = _data("gauss", B * Hkv, max(N, 1), 128, 62)[:, :N].contiguous()
+    pk = ck.encode(K) if N else torch.zeros(16, dtype=torch.uint8, device=DEV)
+    pv = ck.encode(V) if N else torch.zeros(16, dtype=torch.uint8, device=DEV)
+    q = torch.randn(B, Hq, 128, generator=torch.Generator(device=DEV).manual_seed(4), device=DEV)
+    out = T.fmag_decode_attention(ck, ck, q, pk, pv, Hkv, N, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    if N == 0:
+        assert np.all(got == 0.0)
+        return
+    W = F.record_words(128, 4, 8)
+    wv = pv.cpu().numpy()[: B * Hkv * N * W * 4].view(np.uint32).reshape(B * Hkv, N, W)
+    wk = pk.cpu().numpy()[: B * Hkv * N * W * 4].view(np.uint32).reshape(B * Hkv, N, W)
+    q64 = q.cpu().numpy().astype(np.float64)
+    for b in range(B):
+        for h in range(Hq):
+            st = b * Hkv + h // (Hq // Hkv)
+            rk, rv = F.unpack(wk[st], 4, 8, 128), F.unpack(wv[st], 4, 8, 128)
+            want = F.attention(F.scores(q64[b, h][None, :], rk, 4, 8, 128), rv, 4, 8, 128, 1.0 / math.sqrt(128))[0]
+            assert np.linalg.norm(got[b, h] - want) <= 2e-3 * np.linalg.norm(want), (b, h)
