@@ -149,14 +149,17 @@ int tables(const tq_fmag_params* p, FmDev* out, int* cus) {
 }
 
 // attention split geometry, a function of the arguments only: about as many (stream, split) waves
-// as 256 CUs hold at twelve per CU (three per SIMD), splits of at least 256 tokens in multiples of
-// 32, at most 1024
+// as 256 CUs hold (twelve per CU, three per SIMD; eight when a record exceeds 28 words, whose
+// kernel runs at two per SIMD), splits of at least 256 tokens in multiples of 32, at most 1024
 struct AttnWs {
     int64_t tps, n_split, o_qlo, o_qs, o_part, o_ml, total;
 };
-AttnWs attn_ws(int d, int64_t streams, int64_t n_tokens) {
+int64_t waves_per_cu(const tq_fmag_params* pk, const tq_fmag_params* pv) {
+    return (pk->d == 64 || std::max(record_words(pk), record_words(pv)) <= 28) ? 12 : 8;
+}
+AttnWs attn_ws(int d, int64_t per_cu, int64_t streams, int64_t n_tokens) {
     AttnWs w{};
-    int64_t ns = (256 * 12 + streams - 1) / (streams > 0 ? streams : 1);
+    int64_t ns = (256 * per_cu + streams - 1) / (streams > 0 ? streams : 1);
     ns = std::min(ns, (n_tokens + 255) / 256);
     ns = std::max<int64_t>(std::min<int64_t>(ns, 1024), 1);
     w.tps = std::max<int64_t>(((n_tokens + ns - 1) / ns + 31) / 32 * 32, 32);
@@ -279,7 +282,8 @@ int tq_fmag_qk_scores(const tq_fmag_params* p, const void* q, tq_dtype q_dtype, 
 size_t tq_fmag_attention_workspace_bytes(const tq_fmag_params* pk, int32_t batch, int32_t n_q_heads,
                                          int32_t n_kv_heads, int64_t n_tokens) {
     if (check(pk) != TQ_OK || batch < 0 || n_q_heads < 1 || n_kv_heads < 1 || n_tokens < 0) return 0;
-    return (size_t)attn_ws(pk->d, (int64_t)batch * n_kv_heads, n_tokens).total;
+    // sized for the larger geometry (the value codec may allow it): an upper bound for any V
+    return (size_t)attn_ws(pk->d, 12, (int64_t)batch * n_kv_heads, n_tokens).total;
 }
 
 int tq_fmag_decode_attention(const tq_fmag_params* pk, const tq_fmag_params* pv, const void* q, tq_dtype q_dtype,
@@ -301,7 +305,7 @@ int tq_fmag_decode_attention(const tq_fmag_params* pk, const tq_fmag_params* pv,
         return TQ_EALIGN;
     if (lengths && (reinterpret_cast<uintptr_t>(lengths) & 3u)) return TQ_EALIGN;
     const int64_t streams = (int64_t)batch * n_kv_heads;
-    const AttnWs w = attn_ws(pk->d, streams, n_tokens);
+    const AttnWs w = attn_ws(pk->d, waves_per_cu(pk, pv), streams, n_tokens);
     if (workspace_bytes < (size_t)w.total) return TQ_EWORKSPACE;
     FmAttnArgs a{};
     int cus = 0;
