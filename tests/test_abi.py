@@ -157,3 +157,31 @@ def test_fmag_record_size_and_validation():
     assert L.tq_fmag_encode(ctypes.byref(prm), None, _lib.TQ_F32, 1, 1, None, None) == _lib.TQ_EUNSUPPORTED
     assert L.tq_fmag_encode(ctypes.byref(prm), None, _lib.TQ_BF16, 1, 0, None, None) == _lib.TQ_OK
     assert L.tq_fmag_decode(ctypes.byref(prm), None, 1, 1, None, _lib.TQ_F32, None) == _lib.TQ_EINVAL
+
+
+def test_fmag_attention_validates_before_any_device_call():
+    """tq_fmag_decode_attention checks its arguments on the host: bad params, mismatched head sizes,
+    a query-head count that is not a multiple of the kv heads or more than 16 per kv head, unsupported
+    dtypes, a negative or non-finite scale, missing or misaligned pointers, a short workspace."""
+    L = _lib_or_skip()
+    P = _lib.FmagParams
+    pk, pv, p64, bad = P(128, 4, 8), P(128, 3, 16), P(64, 4, 8), P(128, 9, 8)
+    r = lambda a, b, hq=8, hkv=2, qd=_lib.TQ_F32, od=_lib.TQ_F32, sc=0.0, q=None, o=None, ws=None, wsb=0, N=16, k=None, v=None: \
+        L.tq_fmag_decode_attention(ctypes.byref(a), ctypes.byref(b), q, qd, 1, hq, hkv, k, v, N, None,
+                                   ctypes.c_float(sc), o, od, ws, wsb, None)
+    assert r(bad, pv) == _lib.TQ_EINVAL
+    assert r(pk, p64) == _lib.TQ_EINVAL                       # head sizes differ
+    assert r(pk, pv, hq=6, hkv=4) == _lib.TQ_EINVAL           # not a multiple
+    assert r(pk, pv, hq=34, hkv=2) == _lib.TQ_EINVAL          # 17 query heads per kv head
+    assert r(pk, pv, qd=_lib.TQ_F16) == _lib.TQ_EUNSUPPORTED
+    assert r(pk, pv, sc=-1.0) == _lib.TQ_EINVAL
+    assert r(pk, pv, sc=float("nan")) == _lib.TQ_EINVAL
+    assert r(pk, pv) == _lib.TQ_EINVAL                        # NULL q, out, workspace
+    buf = (ctypes.c_uint8 * 4096)()
+    base = ctypes.addressof(buf)
+    a16 = (base + 15) // 16 * 16
+    assert r(pk, pv, q=a16 + 4, o=a16, ws=a16, wsb=64, k=a16, v=a16) == _lib.TQ_EALIGN
+    need = L.tq_fmag_attention_workspace_bytes(ctypes.byref(pk), 1, 8, 2, 16)
+    assert need > 0
+    assert r(pk, pv, q=a16, o=a16, ws=a16, wsb=need - 1, k=a16, v=a16) == _lib.TQ_EWORKSPACE
+    assert L.tq_fmag_attention_workspace_bytes(ctypes.byref(bad), 1, 8, 2, 16) == 0
