@@ -239,8 +239,16 @@ __global__ __launch_bounds__(256, ((D > 128 && (QJL || !BF16)) || (QJL && !BF16)
                 }
             }
             n2 = sum4(n2);
-            const float n = sqrtf(n2);
-            const float sc = n > 0.0f ? (plain ? 1.0f : kInvSqrtD) / n : 0.0f;
+            // hardware square root and reciprocal square root (about 1 ulp: y moves by ~1e-7, far
+            // inside the 1e-6 decision bands); a denormal n² keeps the exact forms
+            float n, sc;
+            if (n2 >= 0x1p-126f) {
+                n = __builtin_amdgcn_sqrtf(n2);
+                sc = (plain ? 1.0f : kInvSqrtD) * __builtin_amdgcn_rsqf(n2);
+            } else {
+                n = sqrtf(n2);
+                sc = n > 0.0f ? (plain ? 1.0f : kInvSqrtD) / n : 0.0f;
+            }
             const float sA = sc * gA;
             const float sE = sc * 16384.0f;
 

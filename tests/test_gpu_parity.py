@@ -59,6 +59,24 @@ def test_encode_decode_parity(d, b, m, dt):
     P.check_decode_bf16(tb, recs, list(range(S)), O.bf16_bits_to_f64(I.bf16_bits(xb)))
 
 
+@pytest.mark.parametrize("m,rht", [(0, 0), (128, 0), (128, 1)])
+def test_encode_parity_across_vector_scales(m, rht):
+    """Vectors scaled by 2^-60, 2^-20, 2^-8, 1 and 2^8 (squared norms from about 2^-113 to 2^23):
+    the normalisation (hardware square root and reciprocal square root) keeps every decision
+    within the bands and the norms within one fp16 step.  Powers of two keep the bf16 inputs exact;
+    at 2^-20 the fp16 norm is subnormal, at 2^-60 it rounds to 0 on both sides (a zero decode)."""
+    d, b, H, N = 128, 4, 2, 40
+    codec = T.Codec(d, b, m, H, 77, sketch=rht)
+    base = I.gaussian((5, N, d), 78, device=DEV, dtype=torch.float32)
+    scale = torch.tensor([2.0 ** -60, 2.0 ** -20, 2.0 ** -8, 1.0, 2.0 ** 8], device=DEV).view(5, 1, 1)
+    x = (base * scale).to(torch.bfloat16)
+    buf = _enc(codec, x)
+    tb = P.Tables(d, b, m, H, 77, sketch=rht)
+    st = P.check_encode(tb, _x64(x), buf)
+    xh = T.decode(codec, torch.as_tensor(buf, device=DEV), 5, N, torch.float32).cpu().numpy()
+    P.check_decode_f32(tb, st["recs"], list(range(5)), xh)
+
+
 @pytest.mark.parametrize("d,b,m,dt,S,H,N", [(128, 4, 128, torch.bfloat16, 5, 3, 1000),
                                               (128, 3, 0, torch.bfloat16, 7, 16, 333),
                                               (64, 3, 64, torch.float32, 4, 3, 517)])
