@@ -46,7 +46,7 @@ int tq_fmag_record_bytes(const tq_fmag_params* p, int64_t* bytes);
 
 /* Encode x [n_streams][n_tokens][d] (BF16; TQ_EUNSUPPORTED otherwise) into `packed`. The DFT runs on
  * fp16 MFMA (x exact after a per-vector power-of-two scale, the DFT matrix as an fp16 hi + lo pair,
- * fp32 accumulation); magnitudes, atan2 phases and the min-max in fp32. */
+ * fp32 accumulation); magnitudes, phases (an fp32 atan2 within 5e-7 rad) and the min-max in fp32. */
 int tq_fmag_encode(const tq_fmag_params* p, const void* x, tq_dtype x_dtype, int64_t n_streams,
                    int64_t n_tokens, void* packed, void* stream);
 

@@ -32,6 +32,28 @@ constexpr float kPi = 3.14159265358979323846f;
 
 __device__ __forceinline__ half8 as_h8(const u32x4& w) { return __builtin_bit_cast(half8, w); }
 
+// atan2 in fp32: atan(t) on t = min/max in [0, 1] by an odd degree-15 polynomial (a weighted
+// least-squares minimax fit to atan, |error| < 4e-8 on [0, 1]), then the octant reconstruction
+// with the signs taken from the sign bits as atan2 does (±0 and ±π included); |error| < 5e-7 rad
+__device__ __forceinline__ float atan2_poly(float y, float x) {
+    const float ax = fabsf(x), ay = fabsf(y);
+    const float mx = fmaxf(ax, ay), mn = fminf(ax, ay);
+    const float t = mx > 0.0f ? mn * __builtin_amdgcn_rcpf(mx) : 0.0f;
+    const float s = t * t;
+    float p = -0.00405309209600091f;
+    p = fmaf(p, s, 0.021856697276234627f);
+    p = fmaf(p, s, -0.05590154603123665f);
+    p = fmaf(p, s, 0.09641234576702118f);
+    p = fmaf(p, s, -0.13908158242702484f);
+    p = fmaf(p, s, 0.19946442544460297f);
+    p = fmaf(p, s, -0.3332984447479248f);
+    p = fmaf(p, s, 0.9999993443489075f);
+    float r = p * t;
+    if (ay > ax) r = 1.57079632679489662f - r;
+    if (f2u(x) >> 31) r = kPi - r;
+    return copysignf(r, y);
+}
+
 __device__ __forceinline__ uint32_t bf16x2_scaled_f16(uint32_t w, int sc) {
     const float f0 = __builtin_amdgcn_ldexpf(u2f(w << 16), sc);
     const float f1 = __builtin_amdgcn_ldexpf(u2f(w & 0xffff0000u), sc);
@@ -216,7 +238,7 @@ __global__ __launch_bounds__(kFmThreads, 4) void fmag_encode_kernel(FmEncodeArgs
                     im = 0.0f;
                 }
                 mag[t] = __builtin_amdgcn_sqrtf(fmaf(re, re, im * im));
-                ph[t] = atan2f(im, re);
+                ph[t] = atan2_poly(im, re);
                 lo = fminf(lo, mag[t]);
                 hi = fmaxf(hi, mag[t]);
             }
@@ -247,7 +269,7 @@ __global__ __launch_bounds__(kFmThreads, 4) void fmag_encode_kernel(FmEncodeArgs
             if (n == 0) {   // the Nyquist bin (real: phase 0 or π) and the min-max range
                 const float m = fabsf(nyq);
                 const uint32_t qv = (uint32_t)fminf(floorf((m - lo) * inv + 0.5f), Lm1);
-                const float phn = atan2f(0.0f, nyq);
+                const float phn = atan2_poly(0.0f, nyq);
                 uint32_t pv;
                 if constexpr (PQ) pv = (uint32_t)(int)floorf((phn + kPi) * pscale + 0.5f) & ((1u << p) - 1u);
                 else pv = (f2u(phn) + 0x7fffu + ((f2u(phn) >> 16) & 1u)) >> 16;
