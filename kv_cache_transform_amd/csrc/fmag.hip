@@ -701,13 +701,13 @@ __global__ __launch_bounds__(kFaThreads, RWM <= 28 ? 3 : 2) void fmag_attn_kerne
         xswap32(x0, x1);
         cm = fmaxf(x0, x1);
         const float mn = fmaxf(m, cm);
-        const float alpha = mn == -INFINITY ? 1.0f : exp2f(m - mn);
+        const float alpha = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m - mn);   // raw v_exp_f32
         float p[2][4], psum = 0.0f;
 #pragma unroll
         for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                p[h][r] = mn == -INFINITY ? 0.0f : exp2f(sc[h][r] - mn);
+                p[h][r] = mn == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(sc[h][r] - mn);
                 psum += p[h][r];
             }
         l = l * alpha + sum4(psum);
