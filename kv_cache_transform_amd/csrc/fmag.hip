@@ -322,7 +322,7 @@ __device__ __forceinline__ void spectrum8(const uint32_t* rec, int RW, uint32_t 
                                           const float* cs, float (&out)[8], int& es) {
     constexpr int S = D / 32, NB = D / 2 + 1;
     const float lo = u2f(rec[RW - 2]), hi = u2f(rec[RW - 1]);
-    const float delta = (hi - lo) / (float)((1 << b) - 1);
+    const float delta = (hi - lo) * (1.0f / (float)((1 << b) - 1));   // the reciprocal is loop-invariant
     es = hi > 0.0f ? 141 - (int)((f2u(hi) >> 23) & 0xffu) : 0;
     const bool im = s >= S / 2;
     const uint32_t k0 = (uint32_t)(32 * (im ? s - S / 2 : s) + 8 * g);
