@@ -35,13 +35,13 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published (the sketch p
 # the kernel's sources are the ones it was measured on (sha256 of the .hip file + shared headers).
 FETCH_UNIT_B, WRITE_UNIT_B = 2048, 1024
 TRAFFIC = {
-    "encode_k": {"fetch": 2098028.8125, "write": 1395661.84375, "src": "encode.hip",
-        "sha": "33c99c7db09ab06e05b211235c6b89e86d0e6e53c839ee906190ace0725a2c49"},
-    "encode_v": {"fetch": 2102957.5, "write": 1091403.625, "src": "encode.hip",
-        "sha": "33c99c7db09ab06e05b211235c6b89e86d0e6e53c839ee906190ace0725a2c49"},
-    "decode_attention": {"fetch": 1229621.125, "write": 4160.125, "src": "attention.hip",
+    "encode_k": {"fetch": 2098036.3125, "write": 1396372.1875, "src": "encode.hip",
+        "sha": "8a0903eabd6cacabcc36311aa6afbed04c33927a364972d4494d305cbd3cdc24"},
+    "encode_v": {"fetch": 2103114.8125, "write": 1091211.78125, "src": "encode.hip",
+        "sha": "8a0903eabd6cacabcc36311aa6afbed04c33927a364972d4494d305cbd3cdc24"},
+    "decode_attention": {"fetch": 1229622.5625, "write": 4160.0, "src": "attention.hip",
         "sha": "5eaa6f22be6d97fd700da9ac46a3e41690d14c0314e54edf6993c26acab1c6d7"},
-    "decode_v_bf16": {"fetch": 550387.4375, "write": 4194304.0, "src": "decode.hip",
+    "decode_v_bf16": {"fetch": 550394.375, "write": 4194304.0, "src": "decode.hip",
         "sha": "2add9ea1fa8cf5d1d37b9846a4505b28cdfa3553557c2e41c88d2f2cc96455e9"},
 }
 TRAFFIC_HEADERS_SHA = ("9241f7e7fc6398e3b61bd782d033f3beac2c8fe34392745cceb9f2f364e6409c"   # common.hpp
