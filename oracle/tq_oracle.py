@@ -27,10 +27,9 @@ Readings where the pages are silent (each listed in the design doc):
   * QJL uses a seeded Gaussian S (m x d) on the WHT-domain residual, or the randomized Hadamard
     sketch S = H diag(s2) (m = d); sign(0) = +1.
   * Random signs and S come from SplitMix64 keyed by (seed, tag, head); Gaussians by Box-Muller.
-  * The sketch projects the residual in half precision: ê = fp16(2^14 e)/2^14 with round to nearest
-    even (|2^14 e| < 2^15, so only the precision is lost, never the range), z = S ê summed exactly;
-    the stored norm r16 is that of the exact e.  The pages fix no precision for the projection;
-    this is the precision the library takes the sign decisions in.
+  * The Gaussian S holds the fp16 roundings of its Box-Muller draws (the pages say only
+    "Gaussian"; the estimator's unbiasedness is pinned with this table).  The sketch itself is the
+    pages' sign(S e) on the exact fp64 residual e = y - c[idx].
 """
 from __future__ import annotations
 
@@ -285,35 +284,12 @@ def boundary_distance(y: np.ndarray, thresholds: np.ndarray, idx: np.ndarray | N
     return np.minimum(lo, hi)
 
 
-SKETCH_SCALE = 2.0 ** 14
-
-
-def sketch_input(e: np.ndarray) -> np.ndarray:
-    """ê: the residual as the projection takes it, 2^14 e rounded to the nearest fp16 (ties to
-    even), scaled back (exact in fp64)."""
-    return fp16_rne(SKETCH_SCALE * np.asarray(e, dtype=np.float64)).astype(np.float64) / SKETCH_SCALE
-
-
 def sketch(e: np.ndarray, S: np.ndarray, tol: float = FLAG_TOL) -> dict:
-    """Sketch of residual rows e (N, d): z = ê Sᵀ, σ = [z >= 0] (sign(0) = +1).
-
-    sflag marks the decisions another implementation may take differently when its residual is off
-    by at most `tol` per coordinate: |z_i| < tol + Σ_k |S_ik| · step_k over the coordinates k whose
-    2^14 e_k lies within 2^14 tol of an fp16 rounding midpoint (step_k = that fp16 spacing / 2^14,
-    the change of ê_k if it rounds the other way)."""
-    S = np.asarray(S, dtype=np.float64)
-    e = np.asarray(e, dtype=np.float64)
-    v = SKETCH_SCALE * e
-    h = fp16_rne(v)
-    hv = h.astype(np.float64)
-    lo = np.where(hv <= v, hv, np.nextafter(h, np.float16(-np.inf)).astype(np.float64))
-    hi = np.where(hv >= v, hv, np.nextafter(h, np.float16(np.inf)).astype(np.float64))
-    step = hi - lo                                  # 0 when v is exactly representable
-    mid = 0.5 * (lo + hi)
-    near = (step > 0) & (np.abs(v - mid) < SKETCH_SCALE * tol)
-    z = sketch_input(e) @ S.T
-    band = tol + (np.where(near, step, 0.0) / SKETCH_SCALE) @ np.abs(S).T
-    return {"z": z, "sigma": z >= 0.0, "sflag": np.abs(z) < band}
+    """1-bit sketch of residual rows e (N, d) ([AB] §2 TurboQuant: the sign sketch of the WHT-domain
+    residual; SpectralQuant paragraph: sign(S e) in the asymmetric estimator): z = e Sᵀ in fp64,
+    σ = [z >= 0] (sign(0) = +1), sflag = [|z| < tol] (decisions within the tolerance of zero)."""
+    z = np.asarray(e, dtype=np.float64) @ np.asarray(S, dtype=np.float64).T
+    return {"z": z, "sigma": z >= 0.0, "sflag": np.abs(z) < tol}
 
 
 def encode(x: np.ndarray, s: np.ndarray, thresholds: np.ndarray, centroids: np.ndarray,
@@ -321,7 +297,7 @@ def encode(x: np.ndarray, s: np.ndarray, thresholds: np.ndarray, centroids: np.n
     """Encode rows of x (N, d) that share one RNG head.
 
     Returns idx (N,d), n16 (N,) fp16, flag (N,d) bool [|y - t_i| < 1e-6], y (N,d); with S (m x d)
-    also e, r16 (of the exact e), z = S ê, sigma (N,m) bool [z >= 0] and sflag (N,m) (``sketch``)."""
+    also e, r16 = fp16(||e||), z = S e, sigma (N,m) bool [z >= 0] and sflag (N,m) (``sketch``)."""
     x = np.asarray(x, dtype=np.float64)
     n = np.sqrt(np.sum(x * x, axis=1))
     safe = np.where(n > 0, n, 1.0)

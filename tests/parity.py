@@ -6,9 +6,8 @@ legitimately flagged encode decision cannot propagate.
 
 Tolerances (the workload statement's, with the readings listed in the design doc):
   * packed indices bit-exact except coordinates the oracle flags within 1e-6 of a threshold;
-    sketch bits exact except where the oracle's sketch flags them: |z| < 1e-6, widened by the
-    fp16 step of any residual coordinate within 1e-6 of a rounding midpoint (recomputed from the
-    GPU's indices where one differed);
+    sketch bits exact except where the oracle flags them, |S e| < 1e-6 on the exact residual
+    (recomputed from the GPU's indices where one differed);
   * n16 / r16 equal or one fp16 ulp apart (fp32 vs fp64 rounding before the fp16 rounding);
   * fp32 reconstructions within 1e-5 relative L2 per stream;
   * scores within 2e-3 relative L2 per (stream, query) row; attention within 2e-3 relative L2.

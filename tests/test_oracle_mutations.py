@@ -8,7 +8,7 @@ import pytest
 from oracle import tq_oracle as O
 from tests import test_oracle_codebook as CB
 from tests import test_oracle_codec as CC
-from tests import test_oracle_sketch_precision as SKP
+from tests import test_oracle_sketch as SKP
 
 
 def _fails(fn, *args):
@@ -284,25 +284,26 @@ def test_sq_correction_without_the_sqrt_is_caught(monkeypatch):
     _fails(SP.test_selective_qjl_estimate_is_close_to_unbiased)
 
 
-def test_truncated_sketch_residual_is_caught(monkeypatch):
-    def rtz(e):
-        v = O.SKETCH_SCALE * np.asarray(e, dtype=np.float64)
-        h = v.astype(np.float16).astype(np.float64)
-        h = np.where(np.abs(h) > np.abs(v), np.nextafter(v.astype(np.float16), np.float16(0)).astype(np.float64), h)
-        return h / O.SKETCH_SCALE
-    monkeypatch.setattr(O, "sketch_input", rtz)
-    _fails(SKP.test_half_precision_residual_written_out)
-    _fails(SKP.test_sketch_of_a_small_case_written_out)
-
-
-def test_unscaled_sketch_residual_is_caught(monkeypatch):
-    monkeypatch.setattr(O, "sketch_input", lambda e: O.fp16_rne(e).astype(np.float64))
-    _fails(SKP.test_half_precision_residual_written_out)
-
-
-def test_sketch_band_without_the_rounding_term_is_caught(monkeypatch):
-    def narrow(e, S, tol=O.FLAG_TOL):
-        z = O.sketch_input(e) @ np.asarray(S, dtype=np.float64).T
+def test_half_precision_sketch_residual_is_caught(monkeypatch):
+    def half(e, S, tol=O.FLAG_TOL):
+        eh = (np.asarray(e, dtype=np.float64) * 2.0 ** 14).astype(np.float16).astype(np.float64) / 2.0 ** 14
+        z = eh @ np.asarray(S, dtype=np.float64).T
         return {"z": z, "sigma": z >= 0.0, "sflag": np.abs(z) < tol}
-    monkeypatch.setattr(O, "sketch", narrow)
-    _fails(SKP.test_flag_band_covers_every_perturbation_within_the_tolerance)
+    monkeypatch.setattr(O, "sketch", half)
+    _fails(SKP.test_sketch_takes_the_exact_residual)
+
+
+def test_sketch_of_the_negated_residual_is_caught(monkeypatch):
+    real = O.sketch
+    monkeypatch.setattr(O, "sketch", lambda e, S, tol=O.FLAG_TOL: real(-np.asarray(e), S, tol))
+    _fails(SKP.test_encoded_sketch_by_brute_force_at_d8)
+
+
+def test_sketch_sign_of_zero_negative_is_caught(monkeypatch):
+    real = O.sketch
+    def neg0(e, S, tol=O.FLAG_TOL):
+        r = real(e, S, tol)
+        r["sigma"] = r["z"] > 0.0
+        return r
+    monkeypatch.setattr(O, "sketch", neg0)
+    _fails(SKP.test_sketch_of_a_small_case_written_out)
