@@ -15,12 +15,12 @@
  *   - WHT = unnormalised Sylvester Hadamard matrix H in natural order; inverse s ⊙ (H ŷ)/sqrt(d).
  *   - Vectors are normalised by their exact norm n before rotation; n is stored as fp16 (RNE).
  *   - idx_j = #{i : t_i <= y_j} over the 2^b - 1 thresholds (ties go up), centroids ascending.
- *   - QJL (m > 0): z = S_h ê with S_h an m x d matrix of N(0,1) draws rounded to fp16, or, with
+ *   - QJL (m > 0): z = S_h e with S_h an m x d matrix of N(0,1) draws rounded to fp16, or, with
  *     sketch = TQ_SKETCH_RHT, the randomized Hadamard sketch S_h = H diag(s2_h) (m = d; the pages'
- *     sign(WHT(e ⊙ s2))); ê = fp16(2^14 e)/2^14 (round to nearest even: the projection runs in
- *     half precision, the products exact, the sums in fp32); sketch bit i = [z_i >= 0]; the fp16
- *     (RNE) norm ||e|| of the exact residual is stored too.  Scores and attention use the same
- *     estimator for both kinds.
+ *     sign(WHT(e ⊙ s2))); e is the residual itself, taken into the projection as two fp16 parts
+ *     (exact to ~2^-22 relative), so z is fp32-accurate: a bit can differ from the sign of the
+ *     exact projection only where |z_i| < 1e-6.  Sketch bit i = [z_i >= 0] (sign(0) = +1); the fp16
+ *     (RNE) norm ||e|| is stored too.  Scores and attention use the same estimator for both kinds.
  *   - Random tables: SplitMix64 (Steele, Lea, Flood 2014) keyed by (seed, tag, head); signs use
  *     tag 1 (s_j = -1 iff bit 63 of word j), S uses tag 2 with Box-Muller (1958) on word pairs, the
  *     RHT signs s2 use tag 3 like tag 1.

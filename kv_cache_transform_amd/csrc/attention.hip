@@ -5,8 +5,8 @@
 // Split-K (flash-decoding): one wave per (stream = batch·n_kv + kv head, token split).  Per chunk
 // of 32 tokens:
 //   scores  D[token][q] = K̂ Q^T on v_mfma_f32_16x16x32_f16 (A = dequantised keys, lane = token
-//           l%16 with its packed k-block l/16; B = fp16 rotated queries), plus the QJL term
-//           <p, 2σ-1> with A = ±1 sketch bits and B = fp16 S·q_rot;
+//           l%16 with its packed k-block l/16; B = the rotated queries as fp16 hi + lo parts, two
+//           products), plus the QJL term <p, 2σ-1> with A = ±1 sketch bits and B = fp16 S·q_rot;
 //   softmax online in base 2; the score accumulator of lane (q = l%16, g = l/16) holds tokens
 //           {4g+i, 16+4g+i}, exactly the k-block g of the B operand of the next product;
 //   values  O^T[coord][q] += V̂^T W^T (A = dequantised values, lane = coordinate row l%16 over its
@@ -55,12 +55,14 @@ struct AttnGeom {
     // banks of 4 bytes and serves 128 bytes per cycle, i.e. 128/E lanes of an E-byte read at once;
     // holding 128/E copies with entry e of copy c at (e·copies + c)·E gives every lane of such a
     // phase its own banks (lane l reads copy l % copies).  Done when the copies fit in 32 KiB.
-    static constexpr int KE = 2 * PK;                // bytes per K LUT entry
+    // A K entry holds the fp16 hi parts of 2^12 c for its PK coordinates, then their lo parts.
+    static constexpr int KE = 4 * PK;                // bytes per K LUT entry
     static constexpr int KR = (NEK * KE * (128 / KE) <= 32768) ? 128 / KE : 1;
     static constexpr int VR = VPAIR ? 32 : 1;        // copies of the 1 KiB value pair LUT
-    // 4-bit keys and values: both LUTs have 256 entries of 4 bytes, so one table of 256-byte rows
-    // holds entry e of both (32 K copies, then 32 V copies), and a lane's address is the byte
-    // index shifted by 8 or-ed with its copy offset: one v_perm_b32 per lookup.
+    // 4-bit keys and values: the LUTs have 256 entries of 8 (K: hi pair, lo pair) and 4 bytes (V),
+    // so one table of 256-byte rows holds entry e of both (16 K copies, then 32 V copies), and a
+    // lane's address is the byte index shifted by 8 or-ed with its copy offset: one v_perm_b32 per
+    // lookup.
     static constexpr bool KV256 = VPAIR && PK == 2 && NEK == 256;
 };
 
@@ -155,56 +157,61 @@ template <int D, int BK, int BV, bool QJL, bool FULL>
 __device__ __forceinline__ void attn_chunk(const AttnChunk<AttnGeom<D, BK, BV>::NWK, AttnGeom<D, BK, BV>::NWV, AttnGeom<D, BK, BV>::NKS>& cur,
                                            AttnState<AttnGeom<D, BK, BV>::NT>& S, int64_t t0, int64_t t_end,
                                            int g, int mks,
-                                           const half8 (&qb)[AttnGeom<D, BK, BV>::KS], const half8* pb,
+                                           const half8 (&qb)[AttnGeom<D, BK, BV>::KS],
+                                           const half8 (&qbl)[AttnGeom<D, BK, BV>::KS], const half8* pb, float rowf,
                                            const uint8_t* kl, const _Float16* vlut, const uint8_t* vl2,
                                            const u32x2* sgn4, const uint8_t* kvl, uint32_t koff, uint32_t voff,
                                            uint32_t ksh) {
     using Gm = AttnGeom<D, BK, BV>;
     constexpr int KS = Gm::KS, PK = Gm::PK, NT = Gm::NT;
     // ---- scores for the two 16-token tiles ----------------------------------------------------
+    // K̂ Qᵀ as hi·hi + lo·hi + hi·lo of the fp16 parts of 2^12 c and of the queries: only the fp32
+    // accumulation rounds, so the logits stay fp32-accurate however sharp the softmax.
     float lg[8];
 #pragma unroll
     for (int T = 0; T < 2; ++T) {
-        half8 ka[KS];
+        floatx4 s1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int k = 0; k < KS; ++k) {
             constexpr int KST = Gm::KR * Gm::KE;      // bytes between entries of one copy
-            if constexpr (PK == 8) {
-                const uint32_t f = get_bits<8 * BK>(cur.kw[T], (8 * k) * BK);
-                ka[k] = *reinterpret_cast<const half8*>(kl + f * KST);
-            } else if constexpr (PK == 4) {
+            half8 ka, kal;
+            if constexpr (PK == 4) {
 #pragma unroll
                 for (int h = 0; h < 2; ++h) {
                     const uint32_t f = get_bits<4 * BK>(cur.kw[T], (8 * k + 4 * h) * BK);
-                    const half4 e = *reinterpret_cast<const half4*>(kl + f * KST);
-                    ka[k][4 * h + 0] = e[0]; ka[k][4 * h + 1] = e[1];
-                    ka[k][4 * h + 2] = e[2]; ka[k][4 * h + 3] = e[3];
+                    const half8 e = *reinterpret_cast<const half8*>(kl + f * KST);
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        ka[4 * h + u] = e[u];
+                        kal[4 * h + u] = e[4 + u];
+                    }
                 }
             } else if constexpr (Gm::KV256) {
                 // coordinates (8k + 2h, +1) are byte h of packed word k
 #pragma unroll
                 for (int h = 0; h < 4; ++h) {
-                    const half2v e = *reinterpret_cast<const half2v*>(kvl + row256(cur.kw[T][k], koff, h));
-                    ka[k][2 * h] = e[0];
-                    ka[k][2 * h + 1] = e[1];
+                    const half4 e = *reinterpret_cast<const half4*>(kvl + row256(cur.kw[T][k], koff, h));
+                    ka[2 * h] = e[0];
+                    ka[2 * h + 1] = e[1];
+                    kal[2 * h] = e[2];
+                    kal[2 * h + 1] = e[3];
                 }
-            } else if constexpr (PK == 2) {
+            } else {
+                static_assert(PK == 2, "attention keys use 2 or 4 coordinates per LUT entry");
 #pragma unroll
                 for (int h = 0; h < 4; ++h) {
                     const uint32_t f = get_bits<2 * BK>(cur.kw[T], (8 * k + 2 * h) * BK);
-                    const half2v e = *reinterpret_cast<const half2v*>(kl + f * KST);
-                    ka[k][2 * h] = e[0];
-                    ka[k][2 * h + 1] = e[1];
+                    const half4 e = *reinterpret_cast<const half4*>(kl + f * KST);
+                    ka[2 * h] = e[0];
+                    ka[2 * h + 1] = e[1];
+                    kal[2 * h] = e[2];
+                    kal[2 * h + 1] = e[3];
                 }
-            } else {
-#pragma unroll
-                for (int h = 0; h < 8; ++h)
-                    ka[k][h] = *reinterpret_cast<const _Float16*>(kl + get_bits<BK>(cur.kw[T], (8 * k + h) * BK) * KST);
             }
+            s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[k], s1, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kal, qb[k], s1, 0, 0, 0);
+            s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qbl[k], s1, 0, 0, 0);
         }
-        floatx4 s1 = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-        for (int k = 0; k < KS; ++k) s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka[k], qb[k], s1, 0, 0, 0);
         floatx4 s2 = {0.0f, 0.0f, 0.0f, 0.0f};
         if constexpr (QJL) {
 #pragma unroll
@@ -219,13 +226,14 @@ __device__ __forceinline__ void attn_chunk(const AttnChunk<AttnGeom<D, BK, BV>::
             }
         }
         // output lane (q = l16, g) holds tokens t0 + 16T + 4g + i; the queries (and their sketch
-        // projections) already carry the softmax scale in log2 units (and sqrt(pi/2)/m), so the
-        // base-2 logit is n16 (s1 + r16 s2)
+        // projections) already carry the softmax scale in log2 units (and sqrt(pi/2)/m) and the
+        // row's power of two, and the keys 2^12, so the base-2 logit is
+        // n16 · rowf · (2^-12 s1 + r16 s2), with rowf the row factor (times 2^-12 for s1)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float sc = s1[i];
-            if constexpr (QJL) sc = fmaf(half_of(cur.kr[T], i), s2[i], sc);
-            float v = half_of(cur.kn[T], i) * sc;
+            if constexpr (QJL) sc = fmaf(half_of(cur.kr[T], i) * 4096.0f, s2[i], sc);
+            float v = (half_of(cur.kn[T], i) * rowf) * sc;
             if (!FULL && t0 + 16 * T + 4 * g + i >= t_end) v = -INFINITY;
             lg[4 * T + i] = v;
         }
@@ -303,26 +311,26 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attn_kernel(AttnArgs 
     __shared__ uint32_t klut[KV ? 1 : NEK * KE / 4 * KR];          // copy c of entry e at (e KR + c) KE bytes
     __shared__ _Float16 vlut[LV];
     __shared__ uint32_t vlut2[Gm::VPAIR && !KV ? 256 * VR : 1];  // copy c of entry e at word e VR + c
-    __shared__ uint32_t kvlut[KV ? 256 * 64 : 1];                 // row e: 32 K copies, 32 V copies
+    __shared__ uint32_t kvlut[KV ? 256 * 64 : 1];                 // row e: 16 K copies (8 B), 32 V copies (4 B)
     __shared__ u32x2 sgn4[16];                                     // ±1 halves of the 4 bits of a nibble
     if constexpr (KV) {
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(a.tk.lut_f16);
+        const uint32_t* src = reinterpret_cast<const uint32_t*>(a.tk.lut_hl);   // entry e: hi pair, lo pair
         for (int i = threadIdx.x; i < 256 * 64; i += blockDim.x) {
             const int e = i >> 6, c = i & 63;
             if (c < 32) {
-                kvlut[i] = src[e];
+                kvlut[i] = src[2 * e + (c & 1)];
             } else {
                 const half2v hv = {(_Float16)a.tv.cent[e & 15], (_Float16)a.tv.cent[e >> 4]};
                 kvlut[i] = __builtin_bit_cast(uint32_t, hv);
             }
         }
     } else {
-        const uint16_t* src = reinterpret_cast<const uint16_t*>(a.tk.lut_f16);
+        const uint16_t* src = reinterpret_cast<const uint16_t*>(a.tk.lut_hl);
         uint16_t* dst = reinterpret_cast<uint16_t*>(klut);
         for (int i = threadIdx.x; i < NEK * KR; i += blockDim.x) {
             const int e = i / KR, c = i - e * KR;
 #pragma unroll
-            for (int h = 0; h < PK; ++h) dst[(e * KR + c) * PK + h] = src[e * PK + h];
+            for (int h = 0; h < 2 * PK; ++h) dst[(e * KR + c) * 2 * PK + h] = src[e * 2 * PK + h];
         }
     }
     for (int i = threadIdx.x; i < LV; i += blockDim.x) vlut[i] = (_Float16)a.tv.cent[i];
@@ -347,7 +355,7 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attn_kernel(AttnArgs 
     const uint8_t* kl = reinterpret_cast<const uint8_t*>(klut) + (lane % KR) * KE;      // the lane's copies
     const uint8_t* vl2 = reinterpret_cast<const uint8_t*>(vlut2) + (lane % VR) * 4;
     const uint8_t* kvl = reinterpret_cast<const uint8_t*>(kvlut);
-    const uint32_t koff = (uint32_t)(lane & 31) * 4u, voff = 128u + (uint32_t)(lane & 31) * 4u;
+    const uint32_t koff = (uint32_t)(lane & 15) * 8u, voff = 128u + (uint32_t)(lane & 31) * 4u;
     const uint32_t ksh = (uint32_t)((g * (a.tk.m >> 5)) & 3) * 8u;   // bit offset of the lane's sketch bytes
     const int64_t item = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
     const int64_t n_streams = (int64_t)a.batch * a.n_kv_heads;
@@ -372,13 +380,16 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attn_kernel(AttnArgs 
     // query operands (B of the score products): lane column q = l16, k-block g
     const bool qvalid = l16 < a.group;
     const int64_t qrow = (int64_t)bidx * a.n_q_heads + (int64_t)kvh * a.group + (qvalid ? l16 : 0);
-    half8 qb[KS], pb[QJL ? KS : 1];
+    half8 qb[KS], qbl[KS], pb[QJL ? KS : 1];
+    const float rowf = a.o.rowf[qrow] * (1.0f / 4096.0f);
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
-        qb[k] = *reinterpret_cast<const half8*>(a.q_rot + qrow * D + g * C + 8 * k);
+        qb[k] = *reinterpret_cast<const half8*>(a.o.qh + qrow * D + g * C + 8 * k);
+        qbl[k] = *reinterpret_cast<const half8*>(a.o.ql + qrow * D + g * C + 8 * k);
         if (!qvalid) qb[k] = half8{};
+        if (!qvalid) qbl[k] = half8{};
         if constexpr (QJL) {
-            if (k < mks) pb[k] = *reinterpret_cast<const half8*>(a.p + qrow * m + g * (m / 4) + 8 * k);
+            if (k < mks) pb[k] = *reinterpret_cast<const half8*>(a.o.ph + qrow * m + g * (m / 4) + 8 * k);
             else pb[k] = half8{};
             if (!qvalid) pb[k] = half8{};
         }
@@ -413,25 +424,25 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attn_kernel(AttnArgs 
             // math, so the wait before a chunk leaves the other buffer's loads in flight)
             attn_load<D, BK, BV, QJL, true>(B, P, t_begin + (c + 1) * 32, t_end, l16, g, m);
             __builtin_amdgcn_sched_barrier(0);
-            attn_chunk<D, BK, BV, QJL, true>(A, S, t_begin + c * 32, t_end, g, mks, qb, pb, kl,
+            attn_chunk<D, BK, BV, QJL, true>(A, S, t_begin + c * 32, t_end, g, mks, qb, qbl, pb, rowf, kl,
                                              vlut, vl2, sgn4, kvl, koff, voff, ksh);
             __builtin_amdgcn_sched_barrier(0);
             const int64_t cn = c + 2 < n_full ? c + 2 : n_full - 1;
             attn_load<D, BK, BV, QJL, true>(A, P, t_begin + cn * 32, t_end, l16, g, m);
             __builtin_amdgcn_sched_barrier(0);
-            attn_chunk<D, BK, BV, QJL, true>(B, S, t_begin + (c + 1) * 32, t_end, g, mks, qb, pb, kl,
+            attn_chunk<D, BK, BV, QJL, true>(B, S, t_begin + (c + 1) * 32, t_end, g, mks, qb, qbl, pb, rowf, kl,
                                              vlut, vl2, sgn4, kvl, koff, voff, ksh);
             __builtin_amdgcn_sched_barrier(0);
         }
         if (c < n_full) {          // odd count: A holds chunk c
-            attn_chunk<D, BK, BV, QJL, true>(A, S, t_begin + c * 32, t_end, g, mks, qb, pb, kl,
+            attn_chunk<D, BK, BV, QJL, true>(A, S, t_begin + c * 32, t_end, g, mks, qb, qbl, pb, rowf, kl,
                                              vlut, vl2, sgn4, kvl, koff, voff, ksh);
             ++c;
         }
     }
     if (t_begin + c * 32 < t_end) {
         attn_load<D, BK, BV, QJL, false>(A, P, t_begin + c * 32, t_end, l16, g, m);
-        attn_chunk<D, BK, BV, QJL, false>(A, S, t_begin + c * 32, t_end, g, mks, qb, pb, kl,
+        attn_chunk<D, BK, BV, QJL, false>(A, S, t_begin + c * 32, t_end, g, mks, qb, qbl, pb, rowf, kl,
                                           vlut, vl2, sgn4, kvl, koff, voff, ksh);
     }
     // ---- partial results: lane (q = l16, g) holds O[coord NT*(4g+i) + n][q] --------------------

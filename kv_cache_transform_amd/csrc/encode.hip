@@ -7,9 +7,11 @@
 // Search: a uniform grid over y in [-1,1] held in LDS maps y to the one threshold that can lie in
 // its cell plus the count of thresholds below; one compare finishes the search for any b.
 // S·e: v_mfma_f32_16x16x32_f16 with the lane's own residual as the B operand (lane l = vector
-// l%16, k-block l/16 matches the MFMA operand layout): 2^14 e rounded to the nearest fp16
-// (|2^14 e| < 2^15 always, so only precision is lost), the precision the sign decisions are
-// defined in; S stored as fp16 values; exact products, accumulation in fp32.
+// l%16, k-block l/16 matches the MFMA operand layout).  2^14 e (|2^14 e| < 2^15 always) is split
+// into an fp16 part truncated toward zero and the fp16 rounding of the remainder, together exact
+// to about 2^-22 relative; S is stored as fp16 values, so both products are exact and only the
+// fp32 accumulation rounds.  z is then within ~1e-8 of the fp64 projection of the residual, far
+// inside the 1e-6 band of a sign decision.
 #include <map>
 #include <mutex>
 #include <type_traits>
@@ -175,7 +177,7 @@ __global__ __launch_bounds__(256, ((D > 128 && (QJL || !BF16)) || (QJL && !BF16)
     for (int64_t t = tb0 + wave * NG; t < tb1; t += 4 * NG) {
         // keep the LDS operand tables in LDS (re-read per pass) instead of pinned in registers
         asm volatile("" ::: "memory");
-        half8 bh[NG][QJL ? C / 8 : 1];
+        half8 bh[NG][QJL ? C / 8 : 1], bl[NG][QJL ? C / 8 : 1];
         float e2v[NG];
         bool validv[NG];
         int64_t vecv[NG];
@@ -278,14 +280,19 @@ __global__ __launch_bounds__(256, ((D > 128 && (QJL || !BF16)) || (QJL && !BF16)
             }
             if constexpr (QJL) {
                 e2v[gi] = e2;
-                // B operands: lane's residual slots [8k, 8k+8) for k-step k, in fp16 (nearest even)
+                // B operands: lane's residual slots [8k, 8k+8) for k-step k, as hi + lo fp16 parts
 #pragma unroll
                 for (int k = 0; k < C / 8; ++k) {
-                    u32x4 hv;
+                    u32x4 hv, lv;
 #pragma unroll
-                    for (int u = 0; u < 4; ++u)
-                        hv[u] = __builtin_bit_cast(uint32_t, half2v{(_Float16)x[8 * k + 2 * u], (_Float16)x[8 * k + 2 * u + 1]});
+                    for (int u = 0; u < 4; ++u) {
+                        const float e0 = x[8 * k + 2 * u], e1 = x[8 * k + 2 * u + 1];
+                        const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(e0, e1));
+                        hv[u] = h;
+                        lv[u] = sub_f16pair_from_f32(h, e0, e1);
+                    }
                     bh[gi][k] = __builtin_bit_cast(half8, hv);
+                    bl[gi][k] = __builtin_bit_cast(half8, lv);
                 }
             }
         }
@@ -293,7 +300,7 @@ __global__ __launch_bounds__(256, ((D > 128 && (QJL || !BF16)) || (QJL && !BF16)
         if constexpr (QJL && BF16) {
           if (a.t.sketch == 1) {
             // randomized Hadamard sketch z = H (e ⊙ s2) (m = d): the rotation's 32-point block on
-            // fp16 MFMA with the s2 tiles as A and the residual's fp16 values as B, then
+            // fp16 MFMA with the s2 tiles as A and the residual's hi then lo parts as B, then
             // the middle-bit butterflies; slot p of part g is sketch row g C + p, so the part's C
             // bits are its z slots in order (one byte per 8 slots via alignbit, inverted: z >= 0)
             const u32x4* lds_A2 = reinterpret_cast<const u32x4*>(lds_S);
@@ -305,7 +312,8 @@ __global__ __launch_bounds__(256, ((D > 128 && (QJL || !BF16)) || (QJL && !BF16)
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
                         const half8 A = __builtin_bit_cast(half8, lds_A2[(h * NKB + kb) * 64 + lane]);
-                        const floatx4 r = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bh[gi][kb], floatx4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                        floatx4 r = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bh[gi][kb], floatx4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                        r = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bl[gi][kb], r, 0, 0, 0);
 #pragma unroll
                         for (int i = 0; i < 4; ++i) z[8 * kb + 4 * h + i] = r[i];
                     }
@@ -366,8 +374,10 @@ __global__ __launch_bounds__(256, ((D > 128 && (QJL || !BF16)) || (QJL && !BF16)
                                 const half8 A = *reinterpret_cast<const half8*>(
                                     S_LDS ? Sg + (tau * KS + k) * 512 : Sg + 4 * tau * D + 8 * k);
 #pragma unroll
-                                for (int gi = 0; gi < NG; ++gi)
+                                for (int gi = 0; gi < NG; ++gi) {
                                     acc[gi][tl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bh[gi][k], acc[gi][tl], 0, 0, 0);
+                                    acc[gi][tl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bl[gi][k], acc[gi][tl], 0, 0, 0);
+                                }
                             }
                         }
                     }
@@ -385,13 +395,13 @@ __global__ __launch_bounds__(256, ((D > 128 && (QJL || !BF16)) || (QJL && !BF16)
                         }
                 }
                 if constexpr (FULL && NG == 1) {
-                    // issue order: the first kPD S reads, then per step its MFMA and the read kPD
-                    // steps ahead, so each read has kPD steps of matrix work to land
+                    // issue order: the first kPD S reads, then per step its two MFMAs and the read
+                    // kPD steps ahead, so each read has kPD steps of matrix work to land
                     constexpr int kPD = 4;
                     __builtin_amdgcn_sched_group_barrier(0x100, kPD, 0);
 #pragma unroll
                     for (int p = 0; p < 8 * KS; ++p) {
-                        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+                        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
                         if (p + kPD < 8 * KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
                     }
                 }

@@ -484,11 +484,16 @@ __global__ __launch_bounds__(kFsThreads) void fmag_scores_kernel(FmScoresArgs a)
     const int nqt = (int)(a.nq_pad / 16);
     float* cs = reinterpret_cast<float*>(smem);
     _Float16* qp = reinterpret_cast<_Float16*>(smem + 2048);
-    float* qsc = reinterpret_cast<float*>(smem + 2048 + (size_t)a.nq_pad * QROW * 2);
+    _Float16* qpl = qp + (size_t)a.nq_pad * QROW;
+    float* qsc = reinterpret_cast<float*>(smem + 2048 + (size_t)a.nq_pad * QROW * 4);
     uint32_t* stage = reinterpret_cast<uint32_t*>(qsc + a.nq_pad) + wave * RWS;
     {
         const _Float16* src = a.qp + (size_t)st * a.nq_pad * D;
-        for (int i = threadIdx.x; i < a.nq_pad * D; i += kFsThreads) qp[(i / D) * QROW + i % D] = src[i];
+        const _Float16* srl = a.qplo + (size_t)st * a.nq_pad * D;
+        for (int i = threadIdx.x; i < a.nq_pad * D; i += kFsThreads) {
+            qp[(i / D) * QROW + i % D] = src[i];
+            qpl[(i / D) * QROW + i % D] = srl[i];
+        }
         for (int i = threadIdx.x; i < a.nq_pad; i += kFsThreads) qsc[i] = a.qscale[(size_t)st * a.nq_pad + i];
         if (p <= 8u)
             for (int i = threadIdx.x; i < (2 << p); i += kFsThreads) cs[i] = a.t.cs[i];
@@ -510,18 +515,24 @@ __global__ __launch_bounds__(kFsThreads) void fmag_scores_kernel(FmScoresArgs a)
         for (int j = 0; j < NP; ++j)
             if (lane + 64 * j < 16 * RW) stage[lane + 64 * j] = pre[j];
         fetch(tile + nwaves);
-        half8 B[S];
+        // the token's spectrum entries as fp16 hi + lo parts (three products with the query's parts:
+        // fp32-accurate scores)
+        half8 B[S], BL[S];
         int es = 0;
 #pragma unroll
         for (int s = 0; s < S; ++s) {
             float x8[8];
             spectrum8<D, PQ>(stage + v * RW, RW, b, p, s, g, cs, x8, es);
-            u32x4 hv;
+            u32x4 hv, lv;
 #pragma unroll
-            for (int i = 0; i < 8; i += 2)
-                hv[i / 2] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x8[i]) |
-                            ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)x8[i + 1]) << 16);
+            for (int i = 0; i < 8; i += 2) {
+                const _Float16 h0 = (_Float16)x8[i], h1 = (_Float16)x8[i + 1];
+                hv[i / 2] = (uint32_t)__builtin_bit_cast(uint16_t, h0) | ((uint32_t)__builtin_bit_cast(uint16_t, h1) << 16);
+                lv[i / 2] = (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(x8[i] - (float)h0)) |
+                            ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)(x8[i + 1] - (float)h1)) << 16);
+            }
             B[s] = as_h8(hv);
+            BL[s] = as_h8(lv);
         }
         const int64_t tok = tile * 16 + v;
         const float tsc = __builtin_amdgcn_ldexpf(1.0f, -es);
@@ -529,8 +540,12 @@ __global__ __launch_bounds__(kFsThreads) void fmag_scores_kernel(FmScoresArgs a)
             floatx4 acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int s = 0; s < S; ++s) {
-                const half8 aq = *reinterpret_cast<const half8*>(qp + (qt * 16 + v) * QROW + 32 * s + 8 * g);
+                const int o = (qt * 16 + v) * QROW + 32 * s + 8 * g;
+                const half8 aq = *reinterpret_cast<const half8*>(qp + o);
+                const half8 al = *reinterpret_cast<const half8*>(qpl + o);
                 acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, B[s], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, B[s], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, BL[s], acc, 0, 0, 0);
             }
             if (tok < a.n_tokens) {
 #pragma unroll
@@ -546,7 +561,7 @@ __global__ __launch_bounds__(kFsThreads) void fmag_scores_kernel(FmScoresArgs a)
 template <int D, bool PQ>
 static hipError_t launch_fsc(const FmScoresArgs& a, int num_cus, hipStream_t s) {
     FmScoresArgs b = a;
-    const size_t lds = 2048 + (size_t)a.nq_pad * (D + 8) * 2 + (size_t)a.nq_pad * 4 +
+    const size_t lds = 2048 + (size_t)a.nq_pad * (D + 8) * 4 + (size_t)a.nq_pad * 4 +
                        (size_t)(kFsThreads / 64) * (16 * a.t.rec_words + 2) * 4;
     const void* kern = reinterpret_cast<const void*>(&fmag_scores_kernel<D, PQ>);
     if (lds > 65536) {

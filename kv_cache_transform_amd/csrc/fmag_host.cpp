@@ -237,7 +237,7 @@ size_t tq_fmag_scores_workspace_bytes(const tq_fmag_params* p, int64_t n_streams
     if (check(p) != TQ_OK || n_streams < 0 || n_q < 0) return 0;
     const int64_t nq_pad = (n_q + 15) / 16 * 16;
     const int64_t qp = (n_streams * nq_pad * p->d * 2 + 255) / 256 * 256;
-    return (size_t)(qp + (n_streams * nq_pad * 4 + 255) / 256 * 256);
+    return (size_t)(2 * qp + (n_streams * nq_pad * 4 + 255) / 256 * 256);
 }
 
 int tq_fmag_qk_scores(const tq_fmag_params* p, const void* q, tq_dtype q_dtype, int64_t n_q,
@@ -261,13 +261,15 @@ int tq_fmag_qk_scores(const tq_fmag_params* p, const void* q, tq_dtype q_dtype, 
     qa.q = q;
     qa.q_bf16 = q_dtype == TQ_BF16;
     qa.qp = static_cast<_Float16*>(workspace);
-    qa.qscale = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + qpb);
+    qa.qplo = reinterpret_cast<_Float16*>(static_cast<uint8_t*>(workspace) + qpb);
+    qa.qscale = reinterpret_cast<float*>(static_cast<uint8_t*>(workspace) + 2 * qpb);
     qa.qmul = 1.0f;
     qa.n_streams = n_streams;
     qa.n_q = n_q;
     qa.nq_pad = nq_pad;
     if (launch_sq_qprep(qa, s) != hipSuccess) return TQ_EHIP;
     a.qp = qa.qp;
+    a.qplo = qa.qplo;
     a.qscale = qa.qscale;
     a.in = static_cast<const uint32_t*>(packed);
     a.scores = scores;

@@ -45,6 +45,7 @@ struct FmDecodeArgs {
 struct FmScoresArgs {
     FmDev t;
     const _Float16* qp;     // [streams][nq_pad][d]
+    const _Float16* qplo;   // [streams][nq_pad][d] fp16 remainders (qp + qplo = the fp32 value)
     const float* qscale;    // [streams][nq_pad]
     const uint32_t* in;
     float* scores;

@@ -51,21 +51,32 @@ struct DecodeArgs {
     DevTables t;
 };
 
+// Query operands of the score products, written by qprep_kernel into the caller's workspace: per
+// row r (a query of one stream), fp16 hi and lo parts of 2^e_r · q_scale · q_rot and of
+// 2^e_r · p_scale · S q_rot (one power of two per row, chosen so the largest entry of the two lies in
+// [2^13, 2^14): no fp16 overflow, and hi + lo hold every entry to ~2^-22 relative), and the row
+// factor 2^-e_r that undoes the scaling.
+struct QOps {
+    _Float16* qh;           // [rows][d]
+    _Float16* ql;           // [rows][d]
+    _Float16* ph;           // [rows][m] (m > 0)
+    _Float16* pl;           // [rows][m] (m > 0)
+    float* rowf;            // [rows] 2^-e_r
+};
+
 struct QPrepArgs {
     const void* q;          // [n_rows][d], row r belongs to stream r / n_q_per_stream
     int q_bf16;
     int64_t n_rows;
     int n_q_per_stream;     // rows per stream (RNG head = stream % n_heads)
-    _Float16* q_rot;        // [n_rows][d], times q_scale
-    _Float16* p;            // [n_rows][m] (m > 0), times p_scale
+    QOps o;
     float q_scale, p_scale; // 1 for scores; attention folds its softmax scale (and the QJL factor) in
     DevTables t;
 };
 
 struct ScoresArgs {
     const uint8_t* packed;
-    const _Float16* q_rot;  // [n_streams][n_q][d]
-    const _Float16* p;      // [n_streams][n_q][m]
+    QOps o;                 // rows [n_streams][n_q]
     float* scores;          // [n_streams][n_q][n_tokens]
     int64_t n_streams, n_tokens;
     int n_q;
@@ -78,8 +89,8 @@ struct ScoresArgs {
 struct AttnArgs {
     const uint8_t* pk;       // packed K
     const uint8_t* pv;       // packed V
-    const _Float16* q_rot;   // [batch*n_q_heads][d]  rotated with the K signs of its kv head, times scale_log2
-    const _Float16* p;       // [batch*n_q_heads][m]  S q_rot, times scale_log2 sqrt(pi/2)/m
+    QOps o;                  // rows [batch*n_q_heads]: q_rot (rotated with the K signs of its kv head)
+                             // times scale_log2, S q_rot times scale_log2 sqrt(pi/2)/m
     float* part;             // [batch*n_kv][n_split][16 queries][d] rotated-domain partial sums
     float* part_ml;          // [batch*n_kv][n_split][16][2] running max (log2 units) and sum
     void* out;               // [batch][n_q_heads][d]

@@ -4,8 +4,9 @@
 // with a Gaussian S):
 //   q_rot = H (q ⊙ s) / sqrt(d),  p = S q_rot,
 //   ŝ(q, k) = n16 · ( <q_rot, c[idx]> + sqrt(pi/2)/m · r16 · <p, 2σ - 1> ).
-// The two contractions over d and m are v_mfma_f32_16x16x32_f16 tiles: A = 16 queries (fp16
-// q_rot / p), B = 16 keys dequantised straight from the packed bytes.  Lane l holds key l%16 and the
+// The two contractions over d and m are v_mfma_f32_16x16x32_f16 tiles: A = 16 queries (fp16 hi + lo
+// parts of q_rot / p), B = 16 keys dequantised straight from the packed bytes (hi + lo parts of the
+// centroids, or the exact ±1 signs).  Lane l holds key l%16 and the
 // k-block l/16, which is exactly the contiguous packed chunk g = l/16 the encoder wrote.
 #include <map>
 #include <mutex>
@@ -17,12 +18,16 @@
 namespace tq {
 
 // ---------------------------------------------------------------------------------------------
-// q_rot and p per query row; one block of 256 threads per row (tiny amount of work).
+// q_rot and p per query row; one block of 256 threads per row (tiny amount of work).  Both are
+// formed in fp32, scaled by the row's power of two 2^e (the largest |entry| of the two in
+// [2^13, 2^14)) and written as fp16 hi + lo parts: hi the nearest fp16, lo the nearest fp16 of the
+// remainder, so hi + lo is within ~2^-22 of the fp32 value for every entry above the fp16 subnormal
+// range (2^-14 of a unit at most 2^-27 of the row's largest entry).
 __global__ __launch_bounds__(256) void qprep_kernel(QPrepArgs a) {
     const int64_t row = blockIdx.x;
     const int d = a.t.d, m = a.t.m;
     const int head = (int)((row / a.n_q_per_stream) % a.t.n_heads);
-    __shared__ float buf[256];
+    __shared__ float buf[256], pbuf[256], red[4];
     const float* sg = a.t.signs + (int64_t)head * d;
     for (int j = threadIdx.x; j < d; j += blockDim.x) {
         float x;
@@ -45,20 +50,36 @@ __global__ __launch_bounds__(256) void qprep_kernel(QPrepArgs a) {
         __syncthreads();
     }
     const float inv = a.t.rotation == 1 ? 1.0f : 1.0f / sqrtf((float)d);
-    for (int j = threadIdx.x; j < d; j += blockDim.x) {
-        const float r = buf[j] * inv;
-        buf[j] = r;
-        a.q_rot[row * d + j] = (_Float16)(r * a.q_scale);
-    }
+    for (int j = threadIdx.x; j < d; j += blockDim.x) buf[j] *= inv;
     __syncthreads();
+    float mx = 0.0f;
     if (m > 0) {
         const _Float16* S = a.t.S + (int64_t)head * m * d;
         for (int i = threadIdx.x; i < m; i += blockDim.x) {
             float acc = 0.0f;
             for (int j = 0; j < d; ++j) acc = fmaf((float)S[(int64_t)i * d + j], buf[j], acc);
-            a.p[row * m + i] = (_Float16)(acc * a.p_scale);
+            pbuf[i] = acc * a.p_scale;
+            mx = fmaxf(mx, fabsf(pbuf[i]));
         }
     }
+    for (int j = threadIdx.x; j < d; j += blockDim.x) mx = fmaxf(mx, fabsf(buf[j] * a.q_scale));
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+    __syncthreads();
+    mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+    // 2^e with the row's largest entry in [2^13, 2^14); an all-zero (or non-finite) row keeps e = 0
+    const int ex = (int)((f2u(mx) >> 23) & 0xffu);
+    const int e = (mx > 0.0f && ex < 255) ? 13 - (ex == 0 ? -126 : ex - 127) : 0;
+    auto split = [&](float v, _Float16* hp, _Float16* lp, int64_t k) {
+        const float sv = __builtin_amdgcn_ldexpf(v, e);
+        const _Float16 h = (_Float16)sv;
+        hp[k] = h;
+        lp[k] = (_Float16)(sv - (float)h);
+    };
+    for (int j = threadIdx.x; j < d; j += blockDim.x) split(buf[j] * a.q_scale, a.o.qh, a.o.ql, row * d + j);
+    if (m > 0)
+        for (int i = threadIdx.x; i < m; i += blockDim.x) split(pbuf[i], a.o.ph, a.o.pl, row * m + i);
+    if (threadIdx.x == 0) a.o.rowf[row] = __builtin_amdgcn_ldexpf(1.0f, -e);
 }
 
 hipError_t launch_qprep(const QPrepArgs& a, hipStream_t s) {
@@ -68,49 +89,61 @@ hipError_t launch_qprep(const QPrepArgs& a, hipStream_t s) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Dequantise the lane's C packed coordinates into C/8 fp16x8 MFMA operands.
+// Dequantise the lane's C packed coordinates into C/8 pairs of fp16x8 MFMA operands: hi and lo parts
+// of 2^12 c[idx] (the LUT entry of P coordinates holds their P hi parts, then their P lo parts).
 template <int C, int B>
-__device__ __forceinline__ void dequant_f16(const uint32_t (&w)[(C * B + 31) / 32], const _Float16* lut,
-                                            half8 (&out)[C / 8]) {
+__device__ __forceinline__ void dequant_hl(const uint32_t (&w)[(C * B + 31) / 32], const _Float16* lut,
+                                           half8 (&oh)[C / 8], half8 (&ol)[C / 8]) {
     constexpr int P = lut_group_c(B);
 #pragma unroll
     for (int k = 0; k < C / 8; ++k) {
         if constexpr (P == 8) {
             const uint32_t f = get_bits<8 * B>(w, (8 * k) * B);
-            out[k] = *reinterpret_cast<const half8*>(lut + f * 8);
+            oh[k] = *reinterpret_cast<const half8*>(lut + f * 16);
+            ol[k] = *reinterpret_cast<const half8*>(lut + f * 16 + 8);
         } else if constexpr (P == 4) {
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 const uint32_t f = get_bits<4 * B>(w, (8 * k + 4 * h) * B);
-                const half4 e = *reinterpret_cast<const half4*>(lut + f * 4);
-                out[k][4 * h + 0] = e[0]; out[k][4 * h + 1] = e[1];
-                out[k][4 * h + 2] = e[2]; out[k][4 * h + 3] = e[3];
+                const half8 e = *reinterpret_cast<const half8*>(lut + f * 8);
+#pragma unroll
+                for (int u = 0; u < 4; ++u) {
+                    oh[k][4 * h + u] = e[u];
+                    ol[k][4 * h + u] = e[4 + u];
+                }
             }
         } else if constexpr (P == 2) {
 #pragma unroll
             for (int h = 0; h < 4; ++h) {
                 const uint32_t f = get_bits<2 * B>(w, (8 * k + 2 * h) * B);
-                const half2v e = *reinterpret_cast<const half2v*>(lut + f * 2);
-                out[k][2 * h] = e[0];
-                out[k][2 * h + 1] = e[1];
+                const half4 e = *reinterpret_cast<const half4*>(lut + f * 4);
+                oh[k][2 * h] = e[0];
+                oh[k][2 * h + 1] = e[1];
+                ol[k][2 * h] = e[2];
+                ol[k][2 * h + 1] = e[3];
             }
         } else {
 #pragma unroll
             for (int h = 0; h < 8; ++h) {
                 const uint32_t f = get_bits<B>(w, (8 * k + h) * B);
-                out[k][h] = lut[f];
+                const half2v e = *reinterpret_cast<const half2v*>(lut + f * 2);
+                oh[k][h] = e[0];
+                ol[k][h] = e[1];
             }
         }
     }
 }
 
 // Scores of 16 keys (one wave tile) against all queries of the stream.  Lane (t16, g) holds key
-// t16's packed chunk g (its B-operand rows), dequantised to fp16 through an LDS LUT; the queries
-// (q_rot, and p = S q_rot with the sketch) are A operands, staged once per block in LDS (rows padded
-// by 16 bytes so a 16-lane column read spreads over the banks) when they fit, else read from the
-// workspace.  The next tile's packed bytes, norms and sketch words are loaded while the current
-// tile is computed.  Output lane (t16, g) holds queries 4g + i of key t16: each store writes, per
-// query, 16 consecutive keys.
+// t16's packed chunk g (its B-operand rows), dequantised through an LDS LUT into fp16 hi + lo parts
+// of 2^12 c; the queries (hi + lo parts of 2^e q_rot, and of 2^e S q_rot with the sketch) are A
+// operands, staged once per block in LDS (rows padded by 16 bytes so a 16-lane column read spreads
+// over the banks) when they fit, else read from the workspace.  <q_rot, c> takes the three products
+// hi·hi + lo·hi + hi·lo and <p, 2σ - 1> the two products with the exact ±1 signs, so only the fp32
+// accumulation rounds: the scores are fp32-accurate, also for a short row or a cancelling score.
+// The next tile's packed bytes, norms and sketch words are loaded while the current tile is
+// computed.  Output lane (t16, g) holds queries 4g + i of key t16: each store writes, per query, 16
+// consecutive keys.
 template <int D, int B, bool QJL, bool QL>
 __global__ __launch_bounds__(256) void scores_kernel(ScoresArgs a) {
     constexpr int C = D / 4;
@@ -123,17 +156,21 @@ __global__ __launch_bounds__(256) void scores_kernel(ScoresArgs a) {
 
     extern __shared__ uint4 smem4[];
     _Float16* lut = reinterpret_cast<_Float16*>(smem4);
-    constexpr int LUT_B = (NE * P * 2 + 15) & ~15;
+    constexpr int LUT_B = (NE * P * 4 + 15) & ~15;
     u32x2* sgn4 = reinterpret_cast<u32x2*>(reinterpret_cast<uint8_t*>(smem4) + LUT_B);
-    _Float16* qs = reinterpret_cast<_Float16*>(reinterpret_cast<uint8_t*>(smem4) + LUT_B + 128);
+    uint8_t* qbase = reinterpret_cast<uint8_t*>(smem4) + LUT_B + 128;
     const int m = a.t.m;
     const int nqp = (a.n_q + 15) & ~15;          // staged rows (zero past n_q)
-    constexpr int QSD = D + 8;                   // padded row of staged q_rot (halves)
-    const int QSM = m + 8;                       // padded row of staged p
-    _Float16* ps = qs + nqp * QSD;
+    constexpr int QSD = D + 8;                   // padded row of staged queries (halves)
+    const int QSM = m + 8;                       // padded row of staged projections
+    float* rfs = reinterpret_cast<float*>(qbase);                   // [nqp] row factors
+    _Float16* qsh = reinterpret_cast<_Float16*>(qbase + nqp * 4);
+    _Float16* qsl = qsh + nqp * QSD;
+    _Float16* psh = qsl + nqp * QSD;
+    _Float16* psl = psh + nqp * QSM;
 
     const int64_t st = blockIdx.x / a.blocks_per_stream;
-    for (int i = threadIdx.x; i < NE * P; i += blockDim.x) lut[i] = a.t.lut_f16[i];
+    for (int i = threadIdx.x; i < NE * P * 2; i += blockDim.x) lut[i] = a.t.lut_hl[i];
     if (threadIdx.x < 16) {
         uint32_t w[2];
 #pragma unroll
@@ -143,19 +180,28 @@ __global__ __launch_bounds__(256) void scores_kernel(ScoresArgs a) {
         sgn4[threadIdx.x] = u32x2{w[0], w[1]};
     }
     if constexpr (QL) {
-        // stage this stream's queries: 8 halves (16 bytes) per thread step
+        // stage this stream's query operands: 8 halves (16 bytes) per thread step
+        for (int i = threadIdx.x; i < nqp; i += blockDim.x) rfs[i] = i < a.n_q ? a.o.rowf[st * a.n_q + i] : 0.0f;
         for (int i = threadIdx.x; i < nqp * (D / 8); i += blockDim.x) {
             const int r = i / (D / 8), c8 = i - r * (D / 8);
-            u32x4 v = {0u, 0u, 0u, 0u};
-            if (r < a.n_q) v = *reinterpret_cast<const u32x4*>(a.q_rot + (st * a.n_q + r) * D + 8 * c8);
-            *reinterpret_cast<u32x4*>(qs + r * QSD + 8 * c8) = v;
+            u32x4 vh = {0u, 0u, 0u, 0u}, vl = {0u, 0u, 0u, 0u};
+            if (r < a.n_q) {
+                vh = *reinterpret_cast<const u32x4*>(a.o.qh + (st * a.n_q + r) * D + 8 * c8);
+                vl = *reinterpret_cast<const u32x4*>(a.o.ql + (st * a.n_q + r) * D + 8 * c8);
+            }
+            *reinterpret_cast<u32x4*>(qsh + r * QSD + 8 * c8) = vh;
+            *reinterpret_cast<u32x4*>(qsl + r * QSD + 8 * c8) = vl;
         }
         if constexpr (QJL)
             for (int i = threadIdx.x; i < nqp * (m / 8); i += blockDim.x) {
                 const int r = i / (m / 8), c8 = i - r * (m / 8);
-                u32x4 v = {0u, 0u, 0u, 0u};
-                if (r < a.n_q) v = *reinterpret_cast<const u32x4*>(a.p + (st * a.n_q + r) * m + 8 * c8);
-                *reinterpret_cast<u32x4*>(ps + r * QSM + 8 * c8) = v;
+                u32x4 vh = {0u, 0u, 0u, 0u}, vl = {0u, 0u, 0u, 0u};
+                if (r < a.n_q) {
+                    vh = *reinterpret_cast<const u32x4*>(a.o.ph + (st * a.n_q + r) * m + 8 * c8);
+                    vl = *reinterpret_cast<const u32x4*>(a.o.pl + (st * a.n_q + r) * m + 8 * c8);
+                }
+                *reinterpret_cast<u32x4*>(psh + r * QSM + 8 * c8) = vh;
+                *reinterpret_cast<u32x4*>(psl + r * QSM + 8 * c8) = vl;
             }
     }
     __syncthreads();
@@ -199,8 +245,8 @@ __global__ __launch_bounds__(256) void scores_kernel(ScoresArgs a) {
         if (tile + 4 < tb1) load_tile(nx, tile + 4);     // next tile's loads overlap this tile
         const int64_t tok = tile * 16 + t16;
         const bool valid = tok < a.n_tokens;
-        half8 kb[KS];
-        dequant_f16<C, B>(cur.w, lut, kb);
+        half8 kh[KS], kl[KS];
+        dequant_hl<C, B>(cur.w, lut, kh, kl);
         half8 sb[QJL ? KS : 1];
         if constexpr (QJL) {
 #pragma unroll
@@ -212,25 +258,35 @@ __global__ __launch_bounds__(256) void scores_kernel(ScoresArgs a) {
             }
         }
         const float n16 = (float)__builtin_bit_cast(_Float16, cur.n16);
-        const float c1 = n16, c2 = QJL ? n16 * lam * (float)__builtin_bit_cast(_Float16, cur.r16) : 0.0f;
+        const float c1 = n16 * (1.0f / 4096.0f);           // undoes the 2^12 of the centroid parts
+        const float c2 = QJL ? n16 * lam * (float)__builtin_bit_cast(_Float16, cur.r16) : 0.0f;
         float* orow = a.scores + (st * a.n_q) * a.n_tokens + tok;
         for (int qt = 0; qt < nqt; ++qt) {
             const int qr = qt * 16 + t16;                    // A-operand row for this lane
             floatx4 acc1 = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int k = 0; k < KS; ++k) {
-                const half8 A = QL ? *reinterpret_cast<const half8*>(qs + qr * QSD + g * C + 8 * k)
-                                   : *reinterpret_cast<const half8*>(a.q_rot + (st * a.n_q + qr) * D + g * C + 8 * k);
-                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, kb[k], acc1, 0, 0, 0);
+                const int64_t go = (st * a.n_q + qr) * D + g * C + 8 * k;
+                const half8 Ah = QL ? *reinterpret_cast<const half8*>(qsh + qr * QSD + g * C + 8 * k)
+                                    : *reinterpret_cast<const half8*>(a.o.qh + go);
+                const half8 Al = QL ? *reinterpret_cast<const half8*>(qsl + qr * QSD + g * C + 8 * k)
+                                    : *reinterpret_cast<const half8*>(a.o.ql + go);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, kh[k], acc1, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, kh[k], acc1, 0, 0, 0);
+                acc1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, kl[k], acc1, 0, 0, 0);
             }
             floatx4 acc2 = {0.0f, 0.0f, 0.0f, 0.0f};
             if constexpr (QJL) {
 #pragma unroll
                 for (int k = 0; k < KS; ++k) {
                     if (k < mks) {
-                        const half8 A = QL ? *reinterpret_cast<const half8*>(ps + qr * QSM + g * (m / 4) + 8 * k)
-                                           : *reinterpret_cast<const half8*>(a.p + (st * a.n_q + qr) * m + g * (m / 4) + 8 * k);
-                        acc2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, sb[k], acc2, 0, 0, 0);
+                        const int64_t go = (st * a.n_q + qr) * m + g * (m / 4) + 8 * k;
+                        const half8 Ah = QL ? *reinterpret_cast<const half8*>(psh + qr * QSM + g * (m / 4) + 8 * k)
+                                            : *reinterpret_cast<const half8*>(a.o.ph + go);
+                        const half8 Al = QL ? *reinterpret_cast<const half8*>(psl + qr * QSM + g * (m / 4) + 8 * k)
+                                            : *reinterpret_cast<const half8*>(a.o.pl + go);
+                        acc2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(Ah, sb[k], acc2, 0, 0, 0);
+                        acc2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(Al, sb[k], acc2, 0, 0, 0);
                     }
                 }
             }
@@ -238,7 +294,11 @@ __global__ __launch_bounds__(256) void scores_kernel(ScoresArgs a) {
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int q = qt * 16 + 4 * g + i;
-                    if (q < a.n_q) orow[(int64_t)q * a.n_tokens] = QJL ? fmaf(acc2[i], c2, acc1[i] * c1) : acc1[i] * c1;
+                    if (q < a.n_q) {
+                        const float rf = QL ? rfs[q] : a.o.rowf[st * a.n_q + q];
+                        const float v = QJL ? fmaf(acc2[i], c2, acc1[i] * c1) : acc1[i] * c1;
+                        orow[(int64_t)q * a.n_tokens] = v * rf;
+                    }
                 }
             }
         }
@@ -262,9 +322,9 @@ template <int D, int B, bool QJL>
 static hipError_t launch_one(const ScoresArgs& a, int num_cus, hipStream_t s) {
     ScoresArgs b = a;
     constexpr int P = lut_group_c(B), NE = 1 << (P * B);
-    const size_t lut_b = (size_t)((NE * P * 2 + 15) & ~15) + 128;
+    const size_t lut_b = (size_t)((NE * P * 4 + 15) & ~15) + 128;
     const int nqp = (a.n_q + 15) & ~15;
-    const size_t q_b = (size_t)nqp * (D + 8) * 2 + (QJL ? (size_t)nqp * (a.t.m + 8) * 2 : 0);
+    const size_t q_b = (size_t)nqp * 4 + (size_t)nqp * (D + 8) * 4 + (QJL ? (size_t)nqp * (a.t.m + 8) * 4 : 0);
     const bool ql = lut_b + q_b <= 98304;        // stage the queries when they fit in 96 KiB
     const size_t lds = lut_b + (ql ? q_b : 0);
     const void* kern = ql ? reinterpret_cast<const void*>(&scores_kernel<D, B, QJL, true>)

@@ -544,7 +544,8 @@ hipError_t launch_sq_decode(const SqDecodeArgs& a, bool out_bf16, int num_cus, h
 // scores
 // ---------------------------------------------------------------------------------------------
 // one block of D threads per (stream, padded query row): q'_k = σ_k Σ_j U[j][k] q_j in fp32, then
-// scaled by 2^e (largest |q'| in [2^13, 2^14)) into fp16; rows past n_q are zero
+// scaled by 2^e (largest |q'| in [2^13, 2^14)) into an fp16 hi part and the fp16 remainder (together
+// within ~2^-22 of the fp32 value); rows past n_q are zero
 template <int D>
 __global__ __launch_bounds__(D) void sq_qprep_kernel(SqScoresArgs a) {
     __shared__ float qs[D];
@@ -588,7 +589,10 @@ __global__ __launch_bounds__(D) void sq_qprep_kernel(SqScoresArgs a) {
             float mp = fabsf(pv);
             for (int o = 32; o > 0; o >>= 1) mp = fmaxf(mp, __shfl_xor(mp, o));
             const int e2 = mp > 0.0f ? 13 - ((int)((f2u(mp) >> 23) & 0xffu) - 127) : 0;
-            a.pp[(size_t)row * 64 + k] = (_Float16)__builtin_amdgcn_ldexpf(pv, e2);
+            const float pv2 = __builtin_amdgcn_ldexpf(pv, e2);
+            const _Float16 ph = (_Float16)pv2;
+            a.pp[(size_t)row * 64 + k] = ph;
+            if (a.pplo) a.pplo[(size_t)row * 64 + k] = (_Float16)(pv2 - (float)ph);
             if (k == 0) a.pscale[row] = __builtin_amdgcn_ldexpf(1.2533141373155003f / (float)a.t.m, -e2);
         }
     }
@@ -596,6 +600,11 @@ __global__ __launch_bounds__(D) void sq_qprep_kernel(SqScoresArgs a) {
 
 constexpr int kScThreads = 256;
 
+// Scores of 16 tokens (one wave tile) against all queries of the stream: A = the projected queries
+// as fp16 hi + lo parts, B = the tokens' codebook values as hi + lo parts of c·2^12 (three products
+// hi·hi + lo·hi + hi·lo); with the selective sketch, A = S q_Z as hi + lo parts and B = the exact ±1
+// signs (two products).  Only the fp32 accumulation rounds, so the scores are fp32-accurate, also
+// for one token or a cancelling score.
 template <int D>
 __global__ __launch_bounds__(kScThreads) void sq_scores_kernel(SqScoresArgs a) {
     constexpr int S = D / 32, QROW = D + 8;   // padded fp16 rows: 16 B apart in the banks
@@ -607,23 +616,33 @@ __global__ __launch_bounds__(kScThreads) void sq_scores_kernel(SqScoresArgs a) {
     const int RW = a.t.rec_words, RWS = 16 * RW + 4;
     const int nqt = (int)(a.nq_pad / 16);
     const bool sk = a.t.m > 0;
-    uint16_t* cb = reinterpret_cast<uint16_t*>(smem);                            // [width][256] fp16
-    _Float16* qp = reinterpret_cast<_Float16*>(smem + kCbRows * 256 * 2);
-    float* qsc = reinterpret_cast<float*>(smem + kCbRows * 256 * 2 + (size_t)a.nq_pad * QROW * 2);
-    // with the sketch: S q_Z rows (64 + 8 halves each), their scales and the byte -> ±1 table
+    uint32_t* cb = reinterpret_cast<uint32_t*>(smem);                            // [width][256] fp16 (hi, lo)
+    _Float16* qp = reinterpret_cast<_Float16*>(smem + kCbRows * 256 * 4);
+    _Float16* qpl = qp + (size_t)a.nq_pad * QROW;
+    float* qsc = reinterpret_cast<float*>(qpl + (size_t)a.nq_pad * QROW);
+    // with the sketch: S q_Z rows (64 + 8 halves each, hi then lo), their scales and the byte -> ±1 table
     _Float16* ppl = reinterpret_cast<_Float16*>(qsc + a.nq_pad);
-    float* psc = reinterpret_cast<float*>(ppl + (sk ? a.nq_pad * 72 : 0));
+    _Float16* ppll = ppl + (sk ? a.nq_pad * 72 : 0);
+    float* psc = reinterpret_cast<float*>(ppll + (sk ? a.nq_pad * 72 : 0));
     u32x4* pm = reinterpret_cast<u32x4*>(psc + (sk ? a.nq_pad : 0));
     uint32_t* stage = reinterpret_cast<uint32_t*>(pm + (sk ? 256 : 0)) + wave * RWS;
     {
         const _Float16* src = a.qp + (size_t)st * a.nq_pad * D;
-        for (int i = threadIdx.x; i < a.nq_pad * D; i += kScThreads) qp[(i / D) * QROW + i % D] = src[i];
+        const _Float16* srl = a.qplo + (size_t)st * a.nq_pad * D;
+        for (int i = threadIdx.x; i < a.nq_pad * D; i += kScThreads) {
+            qp[(i / D) * QROW + i % D] = src[i];
+            qpl[(i / D) * QROW + i % D] = srl[i];
+        }
         for (int i = threadIdx.x; i < a.nq_pad; i += kScThreads) qsc[i] = a.qscale[(size_t)st * a.nq_pad + i];
-        const uint16_t* c = reinterpret_cast<const uint16_t*>(a.t.cb_h);
+        const uint32_t* c = reinterpret_cast<const uint32_t*>(a.t.cb_hl);
         for (int i = threadIdx.x; i < kCbRows * 256; i += kScThreads) cb[i] = c[i];
         if (sk) {
             const _Float16* ps = a.pp + (size_t)st * a.nq_pad * 64;
-            for (int i = threadIdx.x; i < a.nq_pad * 64; i += kScThreads) ppl[(i / 64) * 72 + i % 64] = ps[i];
+            const _Float16* psl = a.pplo + (size_t)st * a.nq_pad * 64;
+            for (int i = threadIdx.x; i < a.nq_pad * 64; i += kScThreads) {
+                ppl[(i / 64) * 72 + i % 64] = ps[i];
+                ppll[(i / 64) * 72 + i % 64] = psl[i];
+            }
             for (int i = threadIdx.x; i < a.nq_pad; i += kScThreads) psc[i] = a.pscale[(size_t)st * a.nq_pad + i];
             const u32x4* t = reinterpret_cast<const u32x4*>(a.t.pm1);
             for (int i = threadIdx.x; i < 256; i += kScThreads) pm[i] = t[i];
@@ -652,15 +671,20 @@ __global__ __launch_bounds__(kScThreads) void sq_scores_kernel(SqScoresArgs a) {
         for (int j = 0; j < NP; ++j)
             if (lane + 64 * j < 16 * RW) stage[lane + 64 * j] = pre[j];
         fetch(tile + nwaves);
-        half8 B[S];
+        half8 Bh[S], Bl[S];
 #pragma unroll
         for (int s = 0; s < S; ++s) {
             uint32_t ix[8];
             fields8(stage + v * RW, fd[s], ix);
-            u32x4 hv;
+            u32x4 hv, lv;
 #pragma unroll
-            for (int i = 0; i < 8; i += 2) hv[i / 2] = (uint32_t)cb[ix[i]] | ((uint32_t)cb[ix[i + 1]] << 16);
-            B[s] = as_half8(hv);
+            for (int i = 0; i < 8; i += 2) {
+                const uint32_t e0 = cb[ix[i]], e1 = cb[ix[i + 1]];
+                hv[i / 2] = (e0 & 0xffffu) | (e1 << 16);
+                lv[i / 2] = (e0 >> 16) | (e1 & 0xffff0000u);
+            }
+            Bh[s] = as_half8(hv);
+            Bl[s] = as_half8(lv);
         }
         // the sketch's ±1 operand (bits 32 s + 8 g + i of token v) and the token's fp16 norm
         half8 Bs[2];
@@ -676,14 +700,19 @@ __global__ __launch_bounds__(kScThreads) void sq_scores_kernel(SqScoresArgs a) {
             floatx4 acc = floatx4{0.0f, 0.0f, 0.0f, 0.0f}, acs = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
             for (int s = 0; s < S; ++s) {
-                const half8 aq = *reinterpret_cast<const half8*>(qp + (qt * 16 + v) * QROW + 32 * s + 8 * g);
-                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(aq, B[s], acc, 0, 0, 0);
+                const int o = (qt * 16 + v) * QROW + 32 * s + 8 * g;
+                const half8 ah = *reinterpret_cast<const half8*>(qp + o);
+                const half8 al = *reinterpret_cast<const half8*>(qpl + o);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, Bh[s], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, Bh[s], acc, 0, 0, 0);
+                acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, Bl[s], acc, 0, 0, 0);
             }
             if (sk) {
 #pragma unroll
                 for (int s = 0; s < 2; ++s) {
-                    const half8 ap = *reinterpret_cast<const half8*>(ppl + (qt * 16 + v) * 72 + 32 * s + 8 * g);
-                    acs = __builtin_amdgcn_mfma_f32_16x16x32_f16(ap, Bs[s], acs, 0, 0, 0);
+                    const int o = (qt * 16 + v) * 72 + 32 * s + 8 * g;
+                    acs = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const half8*>(ppl + o), Bs[s], acs, 0, 0, 0);
+                    acs = __builtin_amdgcn_mfma_f32_16x16x32_f16(*reinterpret_cast<const half8*>(ppll + o), Bs[s], acs, 0, 0, 0);
                 }
             }
             if (tok < a.n_tokens) {
@@ -691,7 +720,7 @@ __global__ __launch_bounds__(kScThreads) void sq_scores_kernel(SqScoresArgs a) {
                 for (int r = 0; r < 4; ++r) {
                     const int qi = qt * 16 + 4 * g + r;
                     if (qi < a.n_q)
-                        out[(size_t)qi * a.n_tokens + tok] = acc[r] * qsc[qi] + (sk ? acs[r] * psc[qi] * rt : 0.0f);
+                        out[(size_t)qi * a.n_tokens + tok] = acc[r] * (qsc[qi] * (1.0f / 4096.0f)) + (sk ? acs[r] * psc[qi] * rt : 0.0f);
                 }
             }
         }
@@ -709,8 +738,8 @@ hipError_t launch_sq_scores(const SqScoresArgs& a, int num_cus, hipStream_t s) {
     SqScoresArgs b = a;
     hipError_t e = launch_sq_qprep(a, s);
     if (e != hipSuccess) return e;
-    const size_t lds = (size_t)kCbRows * 256 * 2 + (size_t)a.nq_pad * (a.t.d + 8) * 2 + (size_t)a.nq_pad * 4 +
-                       (a.t.m > 0 ? (size_t)a.nq_pad * 72 * 2 + (size_t)a.nq_pad * 4 + 4096 : 0) +
+    const size_t lds = (size_t)kCbRows * 256 * 4 + (size_t)a.nq_pad * (a.t.d + 8) * 4 + (size_t)a.nq_pad * 4 +
+                       (a.t.m > 0 ? (size_t)a.nq_pad * 72 * 4 + (size_t)a.nq_pad * 4 + 4096 : 0) +
                        (size_t)(kScThreads / 64) * (16 * a.t.rec_words + 4) * 4;
     if (lds > kLdsMax) return hipErrorInvalidValue;
     const void* kern = a.t.d == 64 ? reinterpret_cast<const void*>(&sq_scores_kernel<64>)
@@ -773,10 +802,12 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sq_attn_kernel(SqAttnArgs a) 
     if (a.lens) len = min(max((int64_t)a.lens[st / a.hkv], (int64_t)0), a.n_tokens);
     const int64_t t0 = sp * a.tps, t1 = min(t0 + a.tps, len);
 
-    half8 Bq[S];
+    half8 Bq[S], Bql[S];
 #pragma unroll
-    for (int s = 0; s < S; ++s)
+    for (int s = 0; s < S; ++s) {
         Bq[s] = *reinterpret_cast<const half8*>(a.qp + ((size_t)st * 16 + n) * D + 32 * s + 8 * g);
+        Bql[s] = *reinterpret_cast<const half8*>(a.qplo + ((size_t)st * 16 + n) * D + 32 * s + 8 * g);
+    }
     const float qs = a.qscale[st * 16 + n];
     // the key sketch's query side (S q_Z of query n) and its scale
     half8 Bp[2];
@@ -832,6 +863,7 @@ __global__ __launch_bounds__(kAttnThreads, 2) void sq_attn_kernel(SqAttnArgs a) 
 #pragma unroll
                 for (int i = 0; i < 8; i += 2) hv[i / 2] = (uint32_t)cb[ix[i]] | ((uint32_t)cb[ix[i + 1]] << 16);
                 d4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(hv), Bq[s], d4, 0, 0, 0);
+                d4 = __builtin_amdgcn_mfma_f32_16x16x32_f16(as_half8(hv), Bql[s], d4, 0, 0, 0);
                 __builtin_amdgcn_sched_barrier(0);
             }
             float add4[4] = {0.0f, 0.0f, 0.0f, 0.0f};

@@ -233,7 +233,7 @@ struct Blob {
 // attention split geometry, a function of the arguments only: about as many (stream, split) waves
 // as 256 CUs hold at eight per CU, splits of at least 256 tokens in multiples of 32, at most 1024
 struct SqAttnWs {
-    int64_t tps, n_split, o_qs, o_pp, o_ps, o_part, o_ml, total;
+    int64_t tps, n_split, o_qs, o_pp, o_ps, o_ql, o_part, o_ml, total;
 };
 SqAttnWs sq_attn_ws(int d, int m, int64_t streams, int64_t n_tokens) {
     SqAttnWs w{};
@@ -246,7 +246,8 @@ SqAttnWs sq_attn_ws(int d, int m, int64_t streams, int64_t n_tokens) {
     w.o_qs = al(streams * 16 * d * 2);
     w.o_pp = w.o_qs + al(streams * 16 * 4);          // with a key sketch: S q_Z rows (64 fp16) and scales
     w.o_ps = w.o_pp + (m > 0 ? al(streams * 16 * 64 * 2) : 0);
-    w.o_part = w.o_ps + (m > 0 ? al(streams * 16 * 4) : 0);
+    w.o_ql = w.o_ps + (m > 0 ? al(streams * 16 * 4) : 0);   // the fp16 remainders of the projected queries
+    w.o_part = w.o_ql + al(streams * 16 * d * 2);
     w.o_ml = w.o_part + al(streams * w.n_split * 16 * d * 4);
     w.total = w.o_ml + al(streams * w.n_split * 16 * 2 * 4);
     return w;
@@ -591,7 +592,7 @@ namespace {
 // scores workspace: projected queries (fp16), their scales, and with a sketch S q_Z (64 fp16 per row)
 // and its scales
 struct SqScoresWs {
-    int64_t o_qs, o_pp, o_ps, total;
+    int64_t o_qs, o_pp, o_ps, o_ql, o_pl, total;
 };
 SqScoresWs sq_scores_ws(const tq_sq_codec* codec, int64_t n_streams, int64_t n_q) {
     auto al = [](int64_t x) { return (x + 255) / 256 * 256; };
@@ -601,7 +602,9 @@ SqScoresWs sq_scores_ws(const tq_sq_codec* codec, int64_t n_streams, int64_t n_q
     w.o_qs = al(rows * codec->dev.d * 2);
     w.o_pp = w.o_qs + al(rows * 4);
     w.o_ps = w.o_pp + (sk ? al(rows * 64 * 2) : 0);
-    w.total = w.o_ps + (sk ? al(rows * 4) : 0);
+    w.o_ql = w.o_ps + (sk ? al(rows * 4) : 0);
+    w.o_pl = w.o_ql + al(rows * codec->dev.d * 2);
+    w.total = w.o_pl + (sk ? al(rows * 64 * 2) : 0);
     return w;
 }
 }  // namespace
@@ -635,9 +638,11 @@ int tq_sq_qk_scores(const tq_sq_codec* codec, const void* q, tq_dtype q_dtype, i
     uint8_t* ws = static_cast<uint8_t*>(workspace);
     a.qp = reinterpret_cast<_Float16*>(ws);
     a.qscale = reinterpret_cast<float*>(ws + w.o_qs);
+    a.qplo = reinterpret_cast<_Float16*>(ws + w.o_ql);
     if (codec->dev.m > 0) {
         a.pp = reinterpret_cast<_Float16*>(ws + w.o_pp);
         a.pscale = reinterpret_cast<float*>(ws + w.o_ps);
+        a.pplo = reinterpret_cast<_Float16*>(ws + w.o_pl);
     }
     a.qmul = 1.0f;
     a.tiles_per_stream = (n_tokens + 15) / 16;
@@ -682,6 +687,7 @@ int tq_sq_decode_attention(const tq_sq_codec* ck, const tq_sq_codec* cv, const v
     qa.q_bf16 = q_dtype == TQ_BF16;
     qa.qp = reinterpret_cast<_Float16*>(ws);
     qa.qscale = reinterpret_cast<float*>(ws + w.o_qs);
+    qa.qplo = reinterpret_cast<_Float16*>(ws + w.o_ql);
     if (ck->dev.m > 0) {
         qa.pp = reinterpret_cast<_Float16*>(ws + w.o_pp);
         qa.pscale = reinterpret_cast<float*>(ws + w.o_ps);
@@ -696,6 +702,7 @@ int tq_sq_decode_attention(const tq_sq_codec* ck, const tq_sq_codec* cv, const v
     a.tv = cv->dev;
     a.qp = qa.qp;
     a.qscale = qa.qscale;
+    a.qplo = qa.qplo;
     a.pp = qa.pp;
     a.pscale = qa.pscale;
     a.kin = static_cast<const uint32_t*>(packed_k);

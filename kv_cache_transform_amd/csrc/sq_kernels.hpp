@@ -68,7 +68,8 @@ struct SqScoresArgs {
     _Float16* pp;           // workspace with a sketch: [streams][nq_pad][64] fp16 of (S q_Z)·2^e'_row
     float* pscale;          // [streams][nq_pad] 2^-e'_row · sqrt(pi/2)/m (q_Z already carries qmul)
     float qmul;             // factor on every projected query (1 for scores; scale·log2 e for attention)
-    _Float16* qplo = nullptr;  // optional [streams][nq_pad][d]: the fp16 remainder (q'·2^e - qp) of each entry
+    _Float16* qplo = nullptr;  // [streams][nq_pad][d]: the fp16 remainder (q'·2^e - qp) of each entry
+    _Float16* pplo = nullptr;  // with a sketch and not null: [streams][nq_pad][64] the fp16 remainder of pp
     int64_t n_streams, n_tokens, n_q, nq_pad, tiles_per_stream;
     int64_t blocks_per_stream, tiles_per_block;
 };
@@ -76,6 +77,7 @@ struct SqScoresArgs {
 struct SqAttnArgs {
     SqDev tk, tv;
     const _Float16* qp;     // [streams][16][d] fp16 projected queries (scaled by 2^e_row)
+    const _Float16* qplo;   // [streams][16][d] their fp16 remainders (hi + lo = the fp32 value)
     const float* qscale;    // [streams][16] 2^-e_row
     const _Float16* pp;     // with a key sketch: [streams][16][64] fp16 S q_Z (scaled)
     const float* pscale;    // [streams][16]

@@ -220,8 +220,35 @@ int64_t attn_tokens_per_split(int d, int64_t n_streams, int64_t n_tokens) {
     return tps < 32 ? 32 : tps;
 }
 
+// query operands of `rows` rows in a workspace starting at byte `base` (see QOps): hi, lo parts of
+// the rotated queries and of their sketch projections, then the row factors
+struct QOpsLayout {
+    int64_t o_qh, o_ql, o_ph, o_pl, o_rf, end;
+};
+QOpsLayout qops_layout(int64_t base, int64_t rows, int d, int m) {
+    QOpsLayout l{};
+    const int64_t mm = m > 0 ? m : 1;
+    l.o_qh = base;
+    l.o_ql = l.o_qh + align_up(rows * d * 2);
+    l.o_ph = l.o_ql + align_up(rows * d * 2);
+    l.o_pl = l.o_ph + align_up(rows * mm * 2);
+    l.o_rf = l.o_pl + align_up(rows * mm * 2);
+    l.end = l.o_rf + align_up(rows * 4);
+    return l;
+}
+QOps qops_at(uint8_t* ws, const QOpsLayout& l) {
+    QOps o;
+    o.qh = reinterpret_cast<_Float16*>(ws + l.o_qh);
+    o.ql = reinterpret_cast<_Float16*>(ws + l.o_ql);
+    o.ph = reinterpret_cast<_Float16*>(ws + l.o_ph);
+    o.pl = reinterpret_cast<_Float16*>(ws + l.o_pl);
+    o.rowf = reinterpret_cast<float*>(ws + l.o_rf);
+    return o;
+}
+
 struct AttnWs {
-    int64_t o_qrot, o_p, o_part, o_ml, total, n_split;
+    QOpsLayout q;
+    int64_t o_part, o_ml, total, n_split;
 };
 
 AttnWs attn_ws(const tq_params* pk, int32_t batch, int32_t hq, int32_t hkv, int64_t n_tokens) {
@@ -231,9 +258,8 @@ AttnWs attn_ws(const tq_params* pk, int32_t batch, int32_t hq, int32_t hkv, int6
     w.n_split = (n_tokens + tps - 1) / tps;
     if (w.n_split < 1) w.n_split = 1;
     const int64_t streams = (int64_t)batch * hkv;
-    w.o_qrot = 0;
-    w.o_p = align_up(rows * pk->d * 2);
-    w.o_part = w.o_p + align_up(rows * (pk->m > 0 ? pk->m : 1) * 2);
+    w.q = qops_layout(0, rows, pk->d, pk->m);
+    w.o_part = w.q.end;
     w.o_ml = w.o_part + align_up(streams * w.n_split * 16 * pk->d * 4);
     w.total = w.o_ml + align_up(streams * w.n_split * 16 * 2 * 4);
     return w;
@@ -391,8 +417,7 @@ int tq_decode_qjl(const tq_params* p, const void* packed, int64_t n_streams, int
 
 size_t tq_scores_workspace_bytes(const tq_params* pk, int64_t n_streams, int64_t n_q) {
     if (check_params(pk) != TQ_OK || n_streams < 0 || n_q < 0) return 0;
-    const int64_t rows = n_streams * n_q + 16;
-    return (size_t)(align_up(rows * pk->d * 2) + align_up(rows * (pk->m > 0 ? pk->m : 1) * 2));
+    return (size_t)qops_layout(0, n_streams * n_q + 16, pk->d, pk->m).end;
 }
 
 int tq_qk_scores(const tq_params* pk, const void* q, tq_dtype q_dtype, int64_t n_q, const void* packed_k,
@@ -411,9 +436,7 @@ int tq_qk_scores(const tq_params* pk, const void* q, tq_dtype q_dtype, int64_t n
     if ((rc = get_tables(pk, &t, &cus)) != TQ_OK) return rc;
     tq_layout lay;
     layout_of(pk, n_streams, n_tokens, &lay);
-    const int64_t rows = n_streams * n_q + 16;
-    _Float16* qrot = static_cast<_Float16*>(workspace);
-    _Float16* pp = reinterpret_cast<_Float16*>(static_cast<uint8_t*>(workspace) + align_up(rows * pk->d * 2));
+    const QOps qo = qops_at(static_cast<uint8_t*>(workspace), qops_layout(0, n_streams * n_q + 16, pk->d, pk->m));
     hipStream_t s = static_cast<hipStream_t>(stream);
     QPrepArgs qa{};
     qa.q = q;
@@ -422,14 +445,12 @@ int tq_qk_scores(const tq_params* pk, const void* q, tq_dtype q_dtype, int64_t n
     qa.n_q_per_stream = (int)n_q;
     qa.q_scale = 1.0f;
     qa.p_scale = 1.0f;
-    qa.q_rot = qrot;
-    qa.p = pp;
+    qa.o = qo;
     qa.t = t;
     if ((rc = hip_status(launch_qprep(qa, s))) != TQ_OK) return rc;
     ScoresArgs a{};
     a.packed = static_cast<const uint8_t*>(packed_k);
-    a.q_rot = qrot;
-    a.p = pp;
+    a.o = qo;
     a.scores = scores;
     a.n_streams = n_streams;
     a.n_tokens = n_tokens;
@@ -497,8 +518,7 @@ int tq_decode_attention_varlen(const tq_params* pk, const tq_params* pv, const v
     qa.q_bf16 = q_dtype == TQ_BF16;
     qa.n_rows = (int64_t)batch * n_q_heads;
     qa.n_q_per_stream = n_q_heads / n_kv_heads;
-    qa.q_rot = reinterpret_cast<_Float16*>(ws + w.o_qrot);
-    qa.p = reinterpret_cast<_Float16*>(ws + w.o_p);
+    qa.o = qops_at(ws, w.q);
     qa.t = tk;
     // the attention kernel works with base-2 logits: fold scale·log2(e) into the rotated queries
     // and scale·log2(e)·sqrt(pi/2)/m into their sketch projections
@@ -510,8 +530,7 @@ int tq_decode_attention_varlen(const tq_params* pk, const tq_params* pv, const v
     AttnArgs a{};
     a.pk = static_cast<const uint8_t*>(packed_k);
     a.pv = static_cast<const uint8_t*>(packed_v);
-    a.q_rot = qa.q_rot;
-    a.p = qa.p;
+    a.o = qa.o;
     a.part = reinterpret_cast<float*>(ws + w.o_part);
     a.part_ml = reinterpret_cast<float*>(ws + w.o_ml);
     a.out = out;

@@ -10,7 +10,13 @@ Tolerances (the workload statement's, with the readings listed in the design doc):
     (recomputed from the GPU's indices where one differed);
   * n16 / r16 equal or one fp16 ulp apart (fp32 vs fp64 rounding before the fp16 rounding);
   * fp32 reconstructions within 1e-5 relative L2 per stream;
-  * scores within 2e-3 relative L2 per (stream, query) row; attention within 2e-3 relative L2.
+  * scores within 2e-3 relative L2 per (stream, query) row; attention within 2e-3 relative L2 per
+    row.  A bf16 output is held to the distance from the oracle to the set of values that round to
+    it: element i contributes how far the oracle value lies outside the rounding interval of the
+    output element (half-way to its bf16 neighbours), so the row passes iff it is the bf16 rounding
+    of some row within 2e-3 of the oracle.  bf16 rounding alone moves a row by about 1.7e-3 relative
+    L2 (up to 2.1e-3 over 500 Gaussian rows of 128), so the bar against the unrounded value would
+    measure the output format, not the kernel; that distance is reported beside it.
 """
 from __future__ import annotations
 
@@ -163,3 +169,49 @@ def oracle_attention_row(tk: Tables, tv: Tables, rec_k, rec_v, st, q64_row, scal
     hk, hv = tk.head(st), tv.head(st)
     sc = O.scores(q64_row[None, :], rec_k, tk.s[hk], tk.c, tk.S[hk] if tk.m else None)
     return O.attention_rotated(sc, rec_v, tv.s[hv], tv.c, scale)[0]
+
+
+def bf16_rne(x):
+    """fp64 values rounded to the nearest bf16 (8 significant bits, ties to even), exactly: the
+    quotient by the value's ulp is an exact fp64 integer-or-half, rounded half to even."""
+    x = np.asarray(x, dtype=np.float64)
+    ax = np.abs(x)
+    e = np.floor(np.log2(np.where(ax > 0, ax, 1.0)))
+    ulp = np.ldexp(1.0, (e - 7).astype(np.int64))
+    ulp = np.where(ax >= 2.0 ** -126, ulp, 2.0 ** -133)      # bf16 subnormal spacing below 2^-126
+    return np.where(ax > 0, np.round(x / ulp) * ulp, x)
+
+
+def bf16_interval(g):
+    """For bf16 values g (held as fp64), the interval of reals that round to g: half-way to the bf16
+    neighbours below and above (exact in fp64)."""
+    g = np.asarray(g, dtype=np.float64)
+    bits = (g.astype(np.float32).view(np.uint32) >> 16).astype(np.int64)
+    def val(b):
+        return (np.asarray(b, dtype=np.uint32) << 16).view(np.float32).astype(np.float64)
+    # neighbours along the bit pattern (sign-magnitude: step the magnitude)
+    mag = bits & 0x7FFF
+    sgn = bits & 0x8000
+    up = val(sgn | np.minimum(mag + 1, 0x7F7F))                 # away from zero
+    dn = np.where(mag > 0, val(sgn | np.maximum(mag - 1, 0)), -val(sgn | 1))   # toward zero (past 0: -tiny)
+    a, b = 0.5 * (g + dn), 0.5 * (g + up)
+    return np.minimum(a, b), np.maximum(a, b)
+
+
+def check_attention_rows(got, ref, bf16: bool, tol=2e-3) -> dict:
+    """Per-row relative L2 of attention outputs [..., d] against the oracle rows (bf16 outputs by the
+    distance of the oracle to their rounding intervals, see the module docstring).  Returns the worst
+    row against the bar, the worst plain distance to the oracle, and the worst bf16 rounding floor
+    (the oracle rounded to bf16 against itself)."""
+    got = np.asarray(got, dtype=np.float64).reshape(-1, np.shape(ref)[-1])
+    ref = np.asarray(ref, dtype=np.float64).reshape(got.shape)
+    if bf16:
+        lo, hi = bf16_interval(got)
+        dist = np.where(ref < lo, lo - ref, np.where(ref > hi, ref - hi, 0.0))
+    else:
+        dist = got - ref
+    rows = [(float(np.linalg.norm(dist[i]) / max(np.linalg.norm(ref[i]), 1e-300)), rel_l2(got[i], ref[i]),
+             rel_l2(bf16_rne(ref[i]), ref[i]) if bf16 else 0.0) for i in range(got.shape[0])]
+    worst = max(r[0] for r in rows)
+    assert worst <= tol, f"attention row rel L2 {worst:.3e} > {tol}"
+    return dict(worst=worst, worst_unrounded=max(r[1] for r in rows), floor=max(r[2] for r in rows))

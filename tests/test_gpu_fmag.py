@@ -22,6 +22,7 @@ import kv_cache_transform_amd as T
 from oracle import fmag_oracle as F
 from oracle import tq_oracle as O
 from synth import inputs as I
+from tests import parity as P
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -146,7 +147,7 @@ def test_fmag_leaves_other_bytes_and_rejects_fp32():
 ])
 def test_fmag_decode_attention(batch, hq, hkv, N, d, kind, bpk, bpv, lens, out_dtype):
     """Attention rows from the GPU's own records against softmax(scale·ŝ) @ x̂ of the oracle:
-    within 2e-3 relative L2 per row (5e-3 with bf16 output)."""
+    within 2e-3 relative L2 per row (a bf16 output against the oracle rounded to bf16)."""
     S, G = batch * hkv, hq // hkv
     ck, cv = T.FmagCodec(d, *bpk), T.FmagCodec(d, *bpv)
     K = _data(kind, S, N, d, 51)
@@ -161,7 +162,7 @@ def test_fmag_decode_attention(batch, hq, hkv, N, d, kind, bpk, bpv, lens, out_d
     Wk, Wv = F.record_words(d, *bpk), F.record_words(d, *bpv)
     wk = pk.cpu().numpy()[: S * N * Wk * 4].view(np.uint32).reshape(S, N, Wk)
     wv = pv.cpu().numpy()[: S * N * Wv * 4].view(np.uint32).reshape(S, N, Wv)
-    worst = 0.0
+    rows, wants = [], []
     for b in range(batch):
         n_b = N if lens is None else lens[b]
         for h in range(hq):
@@ -172,20 +173,20 @@ def test_fmag_decode_attention(batch, hq, hkv, N, d, kind, bpk, bpv, lens, out_d
             rk = F.unpack(wk[st, :n_b], *bpk, d)
             rv = F.unpack(wv[st, :n_b], *bpv, d)
             sc = F.scores(q64[b, h][None, :], rk, *bpk, d)
-            want = F.attention(sc, rv, *bpv, d, 1.0 / math.sqrt(d))[0]
-            worst = max(worst, np.linalg.norm(got[b, h] - want) / np.linalg.norm(want))
-    print(f"fmag attention worst row rel {worst:.2e}")
-    assert worst < (2e-3 if out_dtype == torch.float32 else 5e-3)
+            wants.append(F.attention(sc, rv, *bpv, d, 1.0 / math.sqrt(d))[0])
+            rows.append(got[b, h])
+    r = P.check_attention_rows(np.array(rows), np.array(wants), out_dtype == torch.bfloat16)
+    print(f"fmag attention worst row rel L2 {r['worst']:.2e} ({r['worst_unrounded']:.2e} against the unrounded oracle)")
 
 
 def test_fmag_attention_validates_arguments():
     ck, c2 = T.FmagCodec(64, 4, 8), T.FmagCodec(128, 4, 8)
-    q = torch.randn(1, 4, 64, device=DEV)
+    q = torch.randn(1, 4, 64, generator=torch.Generator(device=DEV).manual_seed(183), device=DEV)
     pk = ck.encode(_data("gauss", 2, 32, 64, 1))
     with pytest.raises(T.TQError):          # K and V head sizes differ
         T.fmag_decode_attention(ck, c2, q, pk, pk, 2, 32)
     with pytest.raises(T.TQError):          # more than 16 query heads per kv head
-        T.fmag_decode_attention(ck, ck, torch.randn(1, 34, 64, device=DEV), pk, pk, 2, 32)
+        T.fmag_decode_attention(ck, ck, torch.zeros(1, 34, 64, device=DEV), pk, pk, 2, 32)
 
 
 @pytest.mark.parametrize("N", [0, 1, 33])

@@ -173,7 +173,7 @@ def _attention_case(batch, hq, hkv, N, d, b, m, out_dtype, seed=4001, scale=0.0,
             st = bi * hkv + h // g
             ref[bi, h] = P.oracle_attention_row(tk, tv, rk[st], rv[st], st, q64[bi, h], sc)
     got = out.float().cpu().numpy().astype(np.float64)
-    return P.rel_l2(got, ref), max(P.rel_l2(got[bi, h], ref[bi, h]) for bi in range(batch) for h in range(hq))
+    return P.check_attention_rows(got, ref, out_dtype == torch.bfloat16)
 
 
 @pytest.mark.parametrize("batch,hq,hkv,N,d,b,m", [
@@ -184,11 +184,11 @@ def _attention_case(batch, hq, hkv, N, d, b, m, out_dtype, seed=4001, scale=0.0,
     (1, 2, 1, 33, 128, 2, 32),         # tiny cache
 ])
 def test_decode_attention_reduced(batch, hq, hkv, N, d, b, m):
-    e32, row32 = _attention_case(batch, hq, hkv, N, d, b, m, torch.float32)
-    eb, rowb = _attention_case(batch, hq, hkv, N, d, b, m, torch.bfloat16)
-    print(f"attention {batch}x{hq}/{hkv} N={N} d={d} b={b} m={m}: rel L2 f32 {e32:.2e} (row max {row32:.2e}),"
-          f" bf16 {eb:.2e} (row max {rowb:.2e})")
-    assert e32 <= 2e-3 and eb <= 2e-3
+    r32 = _attention_case(batch, hq, hkv, N, d, b, m, torch.float32)
+    rb = _attention_case(batch, hq, hkv, N, d, b, m, torch.bfloat16)
+    print(f"attention {batch}x{hq}/{hkv} N={N} d={d} b={b} m={m}: worst row rel L2 f32 {r32['worst']:.2e},"
+          f" bf16 {rb['worst']:.2e} against the rounded oracle ({rb['worst_unrounded']:.2e} unrounded,"
+          f" rounding floor {rb['floor']:.2e})")
 
 
 # ---------------------------------------------------------------------------------------------
@@ -251,10 +251,9 @@ def test_decode_with_qjl_correction_limits():
 
 @pytest.mark.parametrize("batch,hq,hkv,N,d,b", [(2, 8, 2, 3000, 128, 4), (1, 4, 2, 900, 256, 3), (1, 8, 1, 500, 64, 4)])
 def test_rht_decode_attention(batch, hq, hkv, N, d, b):
-    e32, _ = _attention_case(batch, hq, hkv, N, d, b, d, torch.float32, sketch=1)
-    eb, _ = _attention_case(batch, hq, hkv, N, d, b, d, torch.bfloat16, sketch=1)
-    print(f"rht attention d={d} b={b}: rel L2 f32 {e32:.2e}, bf16 {eb:.2e}")
-    assert e32 <= 2e-3 and eb <= 2e-3
+    r32 = _attention_case(batch, hq, hkv, N, d, b, d, torch.float32, sketch=1)
+    rb = _attention_case(batch, hq, hkv, N, d, b, d, torch.bfloat16, sketch=1)
+    print(f"rht attention d={d} b={b}: worst row rel L2 f32 {r32['worst']:.2e}, bf16 {rb['worst']:.2e}")
 
 
 # ---------------------------------------------------------------------------------------------
@@ -363,8 +362,7 @@ def test_plain_decode_attention(rk, rv):
 
 
 def test_decode_attention_explicit_scale():
-    e, _ = _attention_case(1, 4, 2, 900, 128, 4, 128, torch.float32, scale=0.05)
-    assert e <= 2e-3
+    _attention_case(1, 4, 2, 900, 128, 4, 128, torch.float32, scale=0.05)
 
 
 @pytest.mark.parametrize("b", [2, 3, 5, 6])
@@ -381,6 +379,96 @@ def test_cfg5_reduced_heavy_tail(b, m):
     P.check_decode_f32(tb, st["recs"], list(range(S)), out)
     sc = T.qk_scores(codec, q, torch.as_tensor(buf, device=DEV), N).cpu().numpy()
     P.check_scores(tb, st["recs"], list(range(S)), _x64(q), sc)
+
+
+# ---------------------------------------------------------------------------------------------
+# short rows, cancelling scores, query scales, few-token attention
+def _estimator_vectors(tb, rec, st):
+    """w_t with ŝ(q, k_t) = <q, w_t>: the estimate is linear in q (q_rot = R q), so
+    w_t = n16 · R^T (ŷ + sqrt(pi/2)/m · r16 · S^T(2σ - 1)), the QJL-corrected reconstruction."""
+    h = tb.head(st)
+    corr = O.qjl_correction(rec["sigma"], rec["r16"], tb.S[h]) if tb.m else None
+    return O.decode(rec["idx"], rec["n16"], tb.s[h], tb.c, corr)
+
+
+@pytest.mark.parametrize("N", [1, 2, 15, 17, 33])
+@pytest.mark.parametrize("m", [0, 128])
+def test_scores_short_rows_and_cancelling_scores(N, m):
+    """Rows of a few tokens, where errors cannot average out.  Query 0 of every stream is made
+    orthogonal (in fp64, then rounded to fp32) to the estimator vector of token 0, so its estimate
+    cancels to ~1e-8 of |q| |w|: within a row of N >= 2 the row bar applies; alone (N = 1) the error
+    is held to 2e-3 of |q| |w|, the scale of that inner product."""
+    d, b, S, nq, seed = 128, 3, 3, 5, 7300 + N + m
+    codec = T.Codec(d, b, m, S, seed)
+    k = I.gaussian((S, N, d), seed, device=DEV)
+    buf = _enc(codec, k)
+    tb = P.Tables(d, b, m, S, seed)
+    st = P.check_encode(tb, _x64(k), buf)
+    q64 = np.random.default_rng(seed + 1).standard_normal((S, nq, d))
+    for s_ in range(S):
+        w0 = _estimator_vectors(tb, st["recs"][s_], s_)[0]
+        q64[s_, 0] -= (q64[s_, 0] @ w0) / (w0 @ w0) * w0
+    q = torch.tensor(q64, dtype=torch.float32, device=DEV)
+    q64 = q.cpu().numpy().astype(np.float64)
+    sc = T.qk_scores(codec, q, torch.as_tensor(buf, device=DEV), N).cpu().numpy()
+    worst = 0.0
+    for s_ in range(S):
+        ref = P.oracle_scores(tb, st["recs"][s_], s_, q64[s_])
+        w = _estimator_vectors(tb, st["recs"][s_], s_)
+        assert abs(ref[0, 0]) < 1e-6 * np.linalg.norm(q64[s_, 0]) * np.linalg.norm(w[0])
+        for i in range(nq):
+            if N == 1 and i == 0:
+                err = abs(sc[s_, 0, 0] - ref[0, 0]) / (np.linalg.norm(q64[s_, 0]) * np.linalg.norm(w[0]))
+            else:
+                err = P.rel_l2(sc[s_, i], ref[i])
+            worst = max(worst, err)
+            assert err <= 2e-3, (s_, i, err)
+    print(f"short rows N={N} m={m}: worst {worst:.2e}")
+
+
+@pytest.mark.parametrize("scale", [2.0 ** -30, 2.0 ** -12, 1.0, 2.0 ** 8])
+def test_scores_across_query_scales(scale):
+    """fp32 queries from 2^-30 to 2^8 times N(0,1): the per-row power of two keeps every operand in
+    the fp16 range (no subnormal loss, no overflow)."""
+    d, b, m, S, N, nq, seed = 128, 4, 128, 2, 40, 6, 7400
+    codec = T.Codec(d, b, m, S, seed)
+    k = I.gaussian((S, N, d), seed, device=DEV)
+    buf = _enc(codec, k)
+    tb = P.Tables(d, b, m, S, seed)
+    st = P.check_encode(tb, _x64(k), buf)
+    q = torch.tensor(np.random.default_rng(seed + 2).standard_normal((S, nq, d)) * scale, dtype=torch.float32,
+                     device=DEV)
+    sc = T.qk_scores(codec, q, torch.as_tensor(buf, device=DEV), N).cpu().numpy()
+    worst = P.check_scores(tb, st["recs"], list(range(S)), _x64(q), sc)
+    print(f"query scale {scale:.3g}: worst row rel L2 {worst:.2e}")
+
+
+@pytest.mark.parametrize("N", [1, 2, 3])
+@pytest.mark.parametrize("out_dtype", [torch.float32, torch.bfloat16])
+def test_decode_attention_few_tokens(N, out_dtype):
+    r = _attention_case(2, 8, 2, N, 128, 4, 128, out_dtype, seed=4101 + N)
+    print(f"attention over {N} tokens ({out_dtype}): worst row rel L2 {r['worst']:.2e}")
+
+
+@pytest.mark.parametrize("scale", [2.0 ** -20, 2.0 ** 6])
+def test_decode_attention_across_query_scales(scale):
+    d, b, m, batch, hq, hkv, N, seed = 128, 4, 128, 1, 4, 2, 700, 4201
+    ck, cv = T.Codec(d, b, m, hkv, seed), T.Codec(d, b, 0, hkv, seed + 1)
+    K = I.rope_gaussian(batch * hkv, N, d, seed, device=DEV)
+    V = I.rope_gaussian(batch * hkv, N, d, seed + 1, device=DEV)
+    q = torch.tensor(np.random.default_rng(seed).standard_normal((batch, hq, d)) * scale, dtype=torch.float32,
+                     device=DEV)
+    pk, pv = T.encode(ck, K), T.encode(cv, V)
+    out = T.decode_attention(ck, cv, q, pk, pv, hkv, N, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    tk, tv = P.Tables(d, b, m, hkv, seed), P.Tables(d, b, 0, hkv, seed + 1)
+    rk = O.unpack_tensor(pk.cpu().numpy(), d, b, m, batch * hkv, N)
+    rv = O.unpack_tensor(pv.cpu().numpy(), d, b, 0, batch * hkv, N)
+    q64 = _x64(q)
+    ref = np.array([[P.oracle_attention_row(tk, tv, rk[h // 2], rv[h // 2], h // 2, q64[0, h], 1 / math.sqrt(d))
+                     for h in range(hq)]])
+    r = P.check_attention_rows(out.cpu().numpy(), ref, False)
+    print(f"attention query scale {scale:.3g}: worst row rel L2 {r['worst']:.2e}")
 
 
 # ---------------------------------------------------------------------------------------------

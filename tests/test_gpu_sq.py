@@ -22,6 +22,7 @@ import kv_cache_transform_amd as T
 from oracle import sq_oracle as Q
 from oracle import tq_oracle as O
 from synth import inputs as I
+from tests import parity as P
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -137,7 +138,8 @@ def test_sq_short_and_ragged_streams(N):
     for st in range(5):
         want = Q.decode(idx[st], models[st % 3])
         assert np.linalg.norm(xh[st] - want) <= 1e-5 * np.linalg.norm(want)
-    q = torch.randn(5, 3, 128, device=DEV, dtype=torch.bfloat16)
+    q = torch.randn(5, 3, 128, generator=torch.Generator(device=DEV).manual_seed(140), device=DEV,
+                    dtype=torch.bfloat16)
     sc = codec.qk_scores(q, packed, N).cpu().numpy()
     q64 = _f64(q)
     for st in range(5):
@@ -163,7 +165,7 @@ def test_sq_many_queries_and_fp32_queries():
     packed = codec.encode(x)
     idx, _, _ = _check_encode(codec, models, x, packed)
     for nq in (1, 256):
-        q = torch.randn(2, nq, 64, device=DEV)
+        q = torch.randn(2, nq, 64, generator=torch.Generator(device=DEV).manual_seed(160 + nq), device=DEV)
         sc = codec.qk_scores(q, packed, 300).cpu().numpy()
         q64 = q.cpu().numpy().astype(np.float64)
         for st in range(2):
@@ -178,7 +180,7 @@ def test_sq_rejects_unsupported_inputs():
         codec.encode(x.float())
     assert e.value.status == T._lib.TQ_EUNSUPPORTED
     with pytest.raises(T.TQError):
-        codec.qk_scores(torch.randn(1, 257, 64, device=DEV), codec.encode(x), 16)
+        codec.qk_scores(torch.zeros(1, 257, 64, device=DEV), codec.encode(x), 16)
 
 
 def _sq_models(regime, d, b, b_tail, hkv, seed):
@@ -212,7 +214,7 @@ def test_sq_decode_attention(batch, hq, hkv, N, d, regime, bk, bv, lens, out_dty
     rk = pk.cpu().numpy()[: S * N * ck.record_bytes].reshape(S, N, ck.record_bytes)
     rv = pv.cpu().numpy()[: S * N * cv.record_bytes].reshape(S, N, cv.record_bytes)
     scale = 1.0 / np.sqrt(d)
-    worst = 0.0
+    rows, wants = [], []
     for b in range(batch):
         n_b = N if lens is None else lens[b]
         for h in range(hq):
@@ -224,19 +226,18 @@ def test_sq_decode_attention(batch, hq, hkv, N, d, regime, bk, bv, lens, out_dty
             ik = Q.unpack(rk[st, :n_b], mk[hk]["bits"])
             iv = Q.unpack(rv[st, :n_b], mv[hk]["bits"])
             sc = Q.scores(q64[b, h][None, :], ik, mk[hk])
-            want = Q.attention(sc, iv, mv[hk], scale)[0]
-            rel = np.linalg.norm(got[b, h] - want) / np.linalg.norm(want)
-            worst = max(worst, rel)
-    print(f"sq attention worst row rel {worst:.2e}")
-    assert worst < (2e-3 if out_dtype == torch.float32 else 5e-3)
+            wants.append(Q.attention(sc, iv, mv[hk], scale)[0])
+            rows.append(got[b, h])
+    r = P.check_attention_rows(np.array(rows), np.array(wants), out_dtype == torch.bfloat16)
+    print(f"sq attention worst row rel L2 {r['worst']:.2e} ({r['worst_unrounded']:.2e} against the unrounded oracle)")
 
 
 def test_sq_attention_validates_arguments():
     ck, _ = _sq_models("isotropic", 64, 4, 2, 2, 21)
     c1, _ = _sq_models("isotropic", 64, 4, 2, 1, 21)
-    q = torch.randn(1, 4, 64, device=DEV)
+    q = torch.randn(1, 4, 64, generator=torch.Generator(device=DEV).manual_seed(237), device=DEV)
     pk = ck.encode(_tokens("isotropic", 2, 32, 64, 1, 2))
     with pytest.raises(T.TQError):          # codec heads must equal n_kv_heads
         T.sq_decode_attention(ck, c1, q, pk, pk, 2, 32)
     with pytest.raises(T.TQError):          # more than 16 query heads per kv head
-        T.sq_decode_attention(ck, ck, torch.randn(1, 34, 64, device=DEV), pk, pk, 2, 32)
+        T.sq_decode_attention(ck, ck, torch.zeros(1, 34, 64, device=DEV), pk, pk, 2, 32)
