@@ -160,6 +160,29 @@ int tq_decode_attention_varlen(const tq_params* pk, const tq_params* pv, const v
                                float softmax_scale, void* out, tq_dtype out_dtype, void* workspace,
                                size_t workspace_bytes, void* stream);
 
+/* Allocation-free tq_decode_attention_varlen, for callers that cannot allocate device memory (code
+ * under HIP graph capture, allocation-free serving loops, harnesses that forbid hipMalloc).
+ * Arguments, layouts, results and errors as tq_decode_attention_varlen, without the workspace: the
+ * query operands and split partials live in a device array inside the library, one per GPU, of
+ * tq_attention_noalloc_max_bytes() bytes (32 MiB, held from the first call on a device until the
+ * process ends; the decode step of batch 16 x 32 query heads over 131072 tokens at d = 128 uses
+ * 17.6 MB).  Limits and behaviour:
+ *   - TQ_EWORKSPACE when tq_attention_workspace_bytes() of the arguments exceeds that maximum;
+ *   - TQ_EUNSUPPORTED unless the device tables of pk and pv are already resident on the current
+ *     device: any earlier call with the same parameters there builds them (the tq_encode that
+ *     filled the caches does), and this entry point never builds them, since that allocates;
+ *   - it calls no hipMalloc, hipFree or other allocating routine;
+ *   - every call on one GPU uses that GPU's array, which keeps the last call's contents (every
+ *     byte a call reads it has written first, so nothing needs clearing); calls that overlap on one
+ *     GPU (other host threads, or other streams without ordering) race on it. */
+int tq_decode_attention_noalloc(const tq_params* pk, const tq_params* pv, const void* q, tq_dtype q_dtype,
+                                int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, const void* packed_k,
+                                const void* packed_v, int64_t n_tokens, const int32_t* lengths,
+                                float softmax_scale, void* out, tq_dtype out_dtype, void* stream);
+
+/* Bytes of the device array tq_decode_attention_noalloc works in (the largest workspace it accepts). */
+size_t tq_attention_noalloc_max_bytes(void);
+
 /* Host-side copies of the tables the kernels use, for inspection and tests (no GPU call):
  * thresholds[2^b-1] and centroids[2^b] in fp64, signs[d] (±1) and S[m·d] (fp16 values as float)
  * of RNG head `head`.  Any output pointer may be NULL. */

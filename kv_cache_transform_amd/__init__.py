@@ -15,7 +15,7 @@ from . import _lib
 from ._lib import TQError, TQ_BF16, TQ_F32
 
 __all__ = ["Codec", "TQError", "get_layout", "encode", "decode", "qk_scores", "decode_attention",
-           "attention_workspace_bytes", "host_tables", "clear_cache", "SQCodec", "sq_host_codebook", "sq_decode_attention", "FmagCodec",
+           "attention_workspace_bytes", "decode_attention_noalloc", "host_tables", "clear_cache", "SQCodec", "sq_host_codebook", "sq_decode_attention", "FmagCodec",
            "fmag_decode_attention"]
 
 _DT = {torch.float32: TQ_F32, torch.bfloat16: TQ_BF16}
@@ -134,6 +134,22 @@ def decode_attention(ck: Codec, cv: Codec, q: torch.Tensor, packed_k: torch.Tens
         _ptr(packed_k), _ptr(packed_v), n_tokens, _ptr(lengths) if lengths is not None else None,
         ctypes.c_float(softmax_scale), _ptr(out), _DT[out.dtype],
         _ptr(workspace), workspace.numel(), _stream(q.device)), "tq_decode_attention_varlen")
+    return out
+
+
+def decode_attention_noalloc(ck: Codec, cv: Codec, q: torch.Tensor, packed_k: torch.Tensor,
+                             packed_v: torch.Tensor, n_kv_heads: int, n_tokens: int, out: torch.Tensor,
+                             softmax_scale: float = 0.0, lengths: torch.Tensor | None = None) -> torch.Tensor:
+    """decode_attention into a caller-given `out`, with no device allocation anywhere: the workspace
+    is the library's own per-device array (at most tq_attention_noalloc_max_bytes()), and the codec
+    tables must already be resident (an earlier encode with the same codecs on this device)."""
+    B, Hq, _ = q.shape
+    if lengths is not None and (lengths.dtype != torch.int32 or lengths.numel() < B or not lengths.is_contiguous()):
+        raise ValueError("lengths must be a contiguous int32 tensor with one entry per batch element")
+    _lib.check(_lib.lib().tq_decode_attention_noalloc(
+        ctypes.byref(ck.params()), ctypes.byref(cv.params()), _ptr(q), _DT[q.dtype], B, Hq, n_kv_heads,
+        _ptr(packed_k), _ptr(packed_v), n_tokens, _ptr(lengths) if lengths is not None else None,
+        ctypes.c_float(softmax_scale), _ptr(out), _DT[out.dtype], _stream(q.device)), "tq_decode_attention_noalloc")
     return out
 
 

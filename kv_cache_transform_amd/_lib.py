@@ -17,7 +17,8 @@ TQ_ROTATION_WHT, TQ_ROTATION_NONE = 0, 1
 
 # every symbol include/tq.h declares
 EXPORTS = ("tq_get_layout", "tq_encode", "tq_encode_append", "tq_decode", "tq_decode_qjl", "tq_scores_workspace_bytes", "tq_qk_scores",
-           "tq_attention_workspace_bytes", "tq_decode_attention", "tq_decode_attention_varlen", "tq_host_tables",
+           "tq_attention_workspace_bytes", "tq_decode_attention", "tq_decode_attention_varlen",
+           "tq_decode_attention_noalloc", "tq_attention_noalloc_max_bytes", "tq_host_tables",
            "tq_status_string",
            "tq_clear_cache")
 # every symbol include/tq_sq.h declares
@@ -83,6 +84,9 @@ def lib() -> ctypes.CDLL:
                                                ctypes.c_float, VP, ctypes.c_int, VP, SZ, VP]),
         "tq_decode_attention_varlen": (ctypes.c_int, [P, P, VP, ctypes.c_int, I32, I32, I32, VP, VP, I64, VP,
                                                       ctypes.c_float, VP, ctypes.c_int, VP, SZ, VP]),
+        "tq_decode_attention_noalloc": (ctypes.c_int, [P, P, VP, ctypes.c_int, I32, I32, I32, VP, VP, I64, VP,
+                                                       ctypes.c_float, VP, ctypes.c_int, VP]),
+        "tq_attention_noalloc_max_bytes": (SZ, []),
         "tq_host_tables": (ctypes.c_int, [P, I32, VP, VP, VP, VP]),
         "tq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
         "tq_clear_cache": (None, []),

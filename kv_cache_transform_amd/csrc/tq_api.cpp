@@ -181,6 +181,19 @@ int device_cus(int* cus) {
     return TQ_OK;
 }
 
+// the resident tables of `p` on the current device, without building them (TQ_EUNSUPPORTED if a
+// call with these parameters has not built them yet on this device): no allocation on this path
+int find_tables(const tq_params* p, DevTables* out, int* num_cus) {
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) return TQ_EHIP;
+    if (device_cus(num_cus) != TQ_OK) return TQ_EHIP;
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_tables.find(TableKey{device, p->d, p->b, p->m, p->n_heads, p->seed, p->sketch, p->rotation});
+    if (it == g_tables.end()) return TQ_EUNSUPPORTED;
+    *out = it->second;
+    return TQ_OK;
+}
+
 int get_tables(const tq_params* p, DevTables* out, int* num_cus) {
     int device = 0;
     if (hipGetDevice(&device) != hipSuccess) return TQ_EHIP;
@@ -265,6 +278,30 @@ AttnWs attn_ws(const tq_params* pk, int32_t batch, int32_t hq, int32_t hkv, int6
     return w;
 }
 
+}  // namespace
+
+// ---- device scratch of the allocation-free attention entry point -------------------------------
+// One array per device, for callers that cannot allocate (graph capture, allocation-free serving
+// loops).  Its host-side name is not a device address: the address comes from hipGetSymbolAddress,
+// taken once per device with that device current, and only that pointer reaches kernels.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+namespace {
+std::map<int, void*> g_scratch;   // device -> address of `scratch` (guarded by g_mu)
+
+int scratch_ptr(void** out) {
+    int device = 0;
+    if (hipGetDevice(&device) != hipSuccess) return TQ_EHIP;
+    std::lock_guard<std::mutex> lk(g_mu);
+    auto it = g_scratch.find(device);
+    if (it == g_scratch.end()) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return TQ_EHIP;
+        it = g_scratch.emplace(device, ptr).first;
+    }
+    *out = it->second;
+    return TQ_OK;
+}
 }  // namespace
 }  // namespace tq
 
@@ -479,11 +516,15 @@ int tq_decode_attention(const tq_params* pk, const tq_params* pv, const void* q,
                                       nullptr, softmax_scale, out, out_dtype, workspace, workspace_bytes, stream);
 }
 
-int tq_decode_attention_varlen(const tq_params* pk, const tq_params* pv, const void* q, tq_dtype q_dtype,
-                               int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, const void* packed_k,
-                               const void* packed_v, int64_t n_tokens, const int32_t* lengths, float softmax_scale,
-                               void* out, tq_dtype out_dtype, void* workspace, size_t workspace_bytes,
-                               void* stream) {
+}  // extern "C"
+
+namespace tq {
+namespace {
+// decode-attention on a given workspace; `no_alloc`: find the tables instead of building them
+int attention_impl(const tq_params* pk, const tq_params* pv, const void* q, tq_dtype q_dtype, int32_t batch,
+                   int32_t n_q_heads, int32_t n_kv_heads, const void* packed_k, const void* packed_v,
+                   int64_t n_tokens, const int32_t* lengths, float softmax_scale, void* out, tq_dtype out_dtype,
+                   void* workspace, size_t workspace_bytes, void* stream, bool no_alloc) {
     int rc = check_params(pk);
     if (rc != TQ_OK) return rc;
     if ((rc = check_params(pv)) != TQ_OK) return rc;
@@ -505,8 +546,8 @@ int tq_decode_attention_varlen(const tq_params* pk, const tq_params* pv, const v
     if (!attention_supported(pk->d, pk->b, pv->b)) return TQ_EUNSUPPORTED;
     DevTables tk, tv;
     int cus = 0;
-    if ((rc = get_tables(pk, &tk, &cus)) != TQ_OK) return rc;
-    if ((rc = get_tables(pv, &tv, &cus)) != TQ_OK) return rc;
+    if ((rc = (no_alloc ? find_tables : get_tables)(pk, &tk, &cus)) != TQ_OK) return rc;
+    if ((rc = (no_alloc ? find_tables : get_tables)(pv, &tv, &cus)) != TQ_OK) return rc;
     const int64_t streams = (int64_t)batch * n_kv_heads;
     tq_layout lk, lv;
     layout_of(pk, streams, n_tokens, &lk);
@@ -556,6 +597,36 @@ int tq_decode_attention_varlen(const tq_params* pk, const tq_params* pv, const v
     const hipError_t e = launch_attention(a, cus, s, &supported);
     if (!supported) return TQ_EUNSUPPORTED;
     return hip_status(e);
+}
+}  // namespace
+}  // namespace tq
+
+extern "C" {
+
+int tq_decode_attention_varlen(const tq_params* pk, const tq_params* pv, const void* q, tq_dtype q_dtype,
+                               int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, const void* packed_k,
+                               const void* packed_v, int64_t n_tokens, const int32_t* lengths, float softmax_scale,
+                               void* out, tq_dtype out_dtype, void* workspace, size_t workspace_bytes,
+                               void* stream) {
+    return attention_impl(pk, pv, q, q_dtype, batch, n_q_heads, n_kv_heads, packed_k, packed_v, n_tokens, lengths,
+                          softmax_scale, out, out_dtype, workspace, workspace_bytes, stream, false);
+}
+
+size_t tq_attention_noalloc_max_bytes(void) { return kScratchBytes; }
+
+int tq_decode_attention_noalloc(const tq_params* pk, const tq_params* pv, const void* q, tq_dtype q_dtype,
+                                int32_t batch, int32_t n_q_heads, int32_t n_kv_heads, const void* packed_k,
+                                const void* packed_v, int64_t n_tokens, const int32_t* lengths,
+                                float softmax_scale, void* out, tq_dtype out_dtype, void* stream) {
+    int rc = check_params(pk);
+    if (rc != TQ_OK) return rc;
+    if (batch < 0 || n_q_heads < 1 || n_kv_heads < 1 || n_tokens < 0) return TQ_EINVAL;
+    // the scratch array bounds the workspace: larger problems are rejected before any device call
+    if (tq_attention_workspace_bytes(pk, batch, n_q_heads, n_kv_heads, n_tokens) > kScratchBytes) return TQ_EWORKSPACE;
+    void* ws = nullptr;
+    if ((rc = scratch_ptr(&ws)) != TQ_OK) return rc;
+    return attention_impl(pk, pv, q, q_dtype, batch, n_q_heads, n_kv_heads, packed_k, packed_v, n_tokens, lengths,
+                          softmax_scale, out, out_dtype, ws, kScratchBytes, stream, true);
 }
 
 void tq_clear_cache(void) {
