@@ -72,7 +72,6 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle sample")
     ap.add_argument("--context", type=int, default=131072)
     ap.add_argument("--no-extra", action="store_true", help="skip the per-kernel lines of the other workloads")
     return ap.parse_args()
@@ -151,6 +150,7 @@ def main():
     }
     bf16eq_step = 2 * nvec * d * 2 * 2             # K and V, encode pass + attention pass
     value = bf16eq_step / (ms_step * 1e-3) / 1e9
+    value_single = bf16eq_step / 2 / (ms_step * 1e-3) / 1e9   # the cache's bf16 size once per step
     kern = {}
     for n in names:
         gbs = alg[n] / (kms[n] * 1e-3) / 1e9
@@ -158,6 +158,12 @@ def main():
         kern[n] = {"ms": round(kms[n], 4), "alg_bytes": alg[n], "achieved_GBs": round(gbs, 1),
                    "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bf16_equiv_GBs": round(bf, 1)}
     kern["encode_k"]["sketch_tflops"] = round(nvec * 2 * ck.m * d / (kms["encode_k"] * 1e-3) / 1e12, 2)
+
+    # the CPU baseline's parity sample: the GPU's own records of the step's caches (taken now: the
+    # extra lines below reuse the packed buffers)
+    sample = None
+    if not args.no_cpu_baseline:
+        sample = _parity_sample(K[:1, :2048], V[:1, :2048], pk, pv, ck, cv, streams, N, d)
 
     # standalone decode of the V cache to bf16 (row a8), timed apart from the step
     xh = torch.empty(streams, N, d, dtype=torch.bfloat16, device=dev)
@@ -339,7 +345,6 @@ def main():
                                          "achieved_GBs": round(fa_alg / (fam * 1e-3) / 1e9, 1),
                                          "hbm_frac": round(fa_alg / (fam * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         del fpk, fpv, fws
-    sample_k, sample_v = K[:1, :2048].clone(), V[:1, :2048].clone()   # the CPU baseline's sample
     del K
 
     copy = copy_ceiling(torch, dev, stream)
@@ -372,7 +377,7 @@ def main():
 
     cpu = None
     if not args.no_cpu_baseline:
-        cpu = cpu_baseline(sample_k, sample_v, q, pk, pv, ck, cv, B, Hq, Hkv, N, d, args.cpu_seconds)
+        cpu = cpu_baseline(sample)
 
     line = {
         "metric": "encode & decode-attention bf16-equiv GB/s on 1 MI355X; % of HBM peak",
@@ -384,6 +389,7 @@ def main():
                                f"context {N}, d=128; K b=4 + QJL m=128, V b=4; step = encode K + encode V + "
                                "decode-attention", "batch": B, "n_q_heads": Hq, "n_kv_heads": Hkv,
                    "context": N, "d": d, "b_k": 4, "m_k": 128, "b_v": 4},
+        "value_single_pass": round(value_single, 1),
         "roofline": roof,
         "cpu_baseline": cpu,
         "kernels": kern,
@@ -393,17 +399,28 @@ def main():
     print(json.dumps(line))
 
 
+_FLUSH = []
+
+
 def _time(torch, stream, fn, reps: int = 5) -> float:
-    """average ms of fn() over reps launches on `stream` (after one untimed call)"""
+    """average ms of fn() over reps launches on `stream` (after one untimed call); before every timed
+    launch, outside its events, a 1 GiB buffer is read (a reduction: clean lines only, so no
+    write-back lands in the timed launch) so that neither the L2s nor the 256 MB Infinity Cache
+    still hold the launch's inputs (the smaller workloads would otherwise fit)"""
+    if not _FLUSH:
+        _FLUSH.append(torch.ones(1 << 28, dtype=torch.int32, device=torch.cuda.current_device()))
     fn()
     torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
+    ev = []
     for _ in range(reps):
+        _FLUSH[0].sum()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
         fn()
-    e1.record(stream)
+        e1.record(stream)
+        ev.append((e0, e1))
     torch.cuda.synchronize()
-    return e0.elapsed_time(e1) / reps
+    return sum(a.elapsed_time(b) for a, b in ev) / reps
 
 
 def _line(ms: float, alg_bytes: int) -> dict:
@@ -417,7 +434,8 @@ def other_workloads(torch, T, I, dev, stream) -> dict:
     outlier-channel K,V (32 heads x 32768 x 128, b = 4), encode with a QJL sketch and q.k scores
     (8 heads x 65536 x 128, b = 3, m = 128, 32 queries per head), and heavy-tailed d = 256 vectors
     (16 heads x 262144, Student-t nu = 3, b = 3, with and without a sketch of m = 256); the sketch
-    encodes also with the randomized Hadamard sketch (m = d)."""
+    encodes also with the randomized Hadamard sketch (m = d).  Every timed launch starts from a
+    flushed cache hierarchy (see _time)."""
     out = {}
     H, N, d = 32, 32768, 128
     x = I.outlier_gaussian(H, N, d, 4, 10.0, 2001, device=dev)
@@ -465,6 +483,7 @@ def other_workloads(torch, T, I, dev, stream) -> dict:
             del xh
         del pk
     del x
+    _FLUSH.clear()
     torch.cuda.empty_cache()
     return out
 
@@ -490,47 +509,211 @@ def copy_ceiling(torch, dev, stream, n_bytes: int = 1 << 30, reps: int = 5):
             "frac_of_peak": round(2 * n_bytes / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
 
 
-def cpu_baseline(K, V, q, pk, pv, ck, cv, B, Hq, Hkv, N, d, budget_s):
-    """The oracle (unchanged) timed on the host on a bounded sample of the same workload: encode
-    of the first n_tok tokens of K and V of stream 0, then decode-attention of the 4 query heads of
-    that stream over those tokens (the oracle's scores and rotated-domain attention of its own
-    encoding).
-    Rate scaled to bf16-equivalent GB/s like the GPU value."""
+# ---------------------------------------------------------------------------------------------
+# CPU baseline: the oracle (unchanged) on the host cores, on bounded samples of every workload
+# ---------------------------------------------------------------------------------------------
+def _oracle_samples(name: str, seed: int):
+    """Seeded host inputs of one workload's sample (the same recipes as the GPU inputs, generated on
+    the CPU) and the codec parameters: returns (d, x, q, codecs)."""
     import numpy as np
     import torch
 
     from oracle import tq_oracle as O
     from synth import inputs as I
 
+    def f64(t):
+        return O.bf16_bits_to_f64(I.bf16_bits(t)) if t.dtype == torch.bfloat16 else t.double().numpy()
+
+    if name == "1":
+        return 64, I.per_channel_gaussian(4096, 64, 1).astype(np.float64), None, {"x": (4, 0, 1001)}
+    if name == "2":
+        return 128, f64(I.outlier_gaussian(1, 2048, 128, 4, 10.0, seed)[0]), None, {"x": (4, 0, 2001)}
+    if name == "3":
+        return (128, f64(I.gaussian((1, 2048, 128), seed)[0]), f64(I.gaussian((1, 32, 128), seed + 7)[0]),
+                {"x": (3, 128, 3001)})
+    if name == "4":
+        kv = I.rope_gaussian(2, 2048, 128, seed)
+        return (128, (f64(kv[0]), f64(kv[1])), f64(I.cfg4_queries(1, 4, 128, 131072, seed + 2)[0]),
+                {"k": (4, 128, 4001), "v": (4, 0, 4002)})
+    if name == "5":
+        return (256, f64(I.student_t(1, 1024, 256, 3, seed)[0]), f64(I.gaussian((1, 64, 256), seed + 3)[0]),
+                {"x": (3, 0, 5004), "xs": (3, 256, 5004)})
+    raise ValueError(name)
+
+
+def _oracle_ops(name: str, seed: int, min_s: float) -> dict:
+    """Time the oracle's steps on one workload's sample: {op: [seconds per repetition, bf16-equivalent
+    bytes per repetition]}.  Tables (codebook, signs, S) are built before the clock starts, as the
+    library builds them once per parameter set."""
+    import numpy as np
+
+    from oracle import tq_oracle as O
+
+    d, x, q, cod = _oracle_samples(name, seed)
+    tabs = {}
+    for key, (b, m, sd) in cod.items():
+        t, c = O.lloyd_max(d, b)
+        tabs[key] = (t, c, O.head_signs(sd, 0, d), O.gaussian_matrix(sd, 0, m, d).astype(np.float64) if m else None)
+
+    def clock(fn, nbytes):
+        reps, t0 = 0, time.perf_counter()
+        while True:
+            fn()
+            reps += 1
+            el = time.perf_counter() - t0
+            if el >= min_s:
+                return [el / reps, nbytes]
+
+    out = {}
+    if name == "4":
+        (k, v), (tk, ck, sk, Sk), (tv, cv, sv, _) = x, tabs["k"], tabs["v"]
+        n = k.shape[0]
+        rk, rv = O.encode(k, sk, tk, ck, Sk), O.encode(v, sv, tv, cv)
+        out["encode_k"] = clock(lambda: O.encode(k, sk, tk, ck, Sk), n * d * 2)
+        out["encode_v"] = clock(lambda: O.encode(v, sv, tv, cv), n * d * 2)
+        out["attention"] = clock(lambda: O.attention_rotated(O.scores(q, rk, sk, ck, Sk), rv, sv, cv,
+                                                             1.0 / math.sqrt(d)), 2 * n * d * 2)
+        return out
+    n = x.shape[0]
+    for key, (t, c, s, S) in tabs.items():
+        tag = "" if len(tabs) == 1 else ("_m0" if S is None else f"_m{S.shape[0]}")
+        r = O.encode(x, s, t, c, S)
+        out["encode" + tag] = clock(lambda: O.encode(x, s, t, c, S), n * d * 2)
+        if S is None:
+            out["decode"] = clock(lambda: O.decode(r["idx"], r["n16"], s, c), n * d * 2)
+        if q is not None:
+            out["scores" + tag] = clock(lambda: O.scores(q, r, s, c, S), n * d * 2)
+    return out
+
+
+CPU_CONFIGS = {
+    "1": "4096 x 64 fp32 per-channel Gaussian, b = 4 (the whole workload)",
+    "2": "2048 of the 32 x 32768 x 128 outlier-channel tokens, b = 4",
+    "3": "2048 of the 8 x 65536 x 128 Gaussian keys, b = 3 + QJL m = 128; 32 queries",
+    "4": "2048 K and 2048 V tokens of one (batch, kv head) of the 16 x 8 x 131072 x 128 RoPE caches, "
+         "K b = 4 + QJL m = 128, V b = 4; attention of its 4 query heads",
+    "5": "1024 of the 16 x 262144 x 256 Student-t tokens, b = 3 with m = 0 and m = 256; 64 queries",
+}
+
+
+def _cpu_worker(args):
+    """pool worker: every workload's oracle steps on one thread (BLAS, OpenMP and torch's own pool,
+    whose idle threads would otherwise spin beside the other workers)"""
+    seed, min_s = args
+    import torch
+    from threadpoolctl import threadpool_limits
+    torch.set_num_threads(1)
+    with threadpool_limits(1):
+        return {name: _oracle_ops(name, seed, min_s) for name in CPU_CONFIGS}
+
+
+def _cpu_model() -> str:
+    import subprocess
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+        for line in subprocess.run(["lscpu"], capture_output=True, text=True, timeout=10).stdout.splitlines():
+            if line.startswith("Model name:"):
+                return line.split(":", 1)[1].strip()
     except Exception:
-        threads = os.cpu_count() or 1
-    n_tok = 2048
-    kx = O.bf16_bits_to_f64(I.bf16_bits(K[0, :n_tok]))
-    vx = O.bf16_bits_to_f64(I.bf16_bits(V[0, :n_tok]))
-    q64 = O.bf16_bits_to_f64(I.bf16_bits(q[0, :Hq // Hkv]))
-    t_k, c_k = O.lloyd_max(d, ck.b)
-    t_v, c_v = O.lloyd_max(d, cv.b)
-    s_k, s_v = O.head_signs(ck.seed, 0, d), O.head_signs(cv.seed, 0, d)
-    S_k = O.gaussian_matrix(ck.seed, 0, ck.m, d)
-    reps = 0
-    t0 = time.perf_counter()
-    while True:
-        rk = O.encode(kx, s_k, t_k, c_k, S_k)
-        rv = O.encode(vx, s_v, t_v, c_v)
-        sc = O.scores(q64, rk, s_k, c_k, S_k)
-        O.attention_rotated(sc, rv, s_v, c_v, 1.0 / math.sqrt(d))
-        reps += 1
-        el = time.perf_counter() - t0
-        if el >= budget_s or reps >= 1000:
-            break
-    bytes_bf16 = reps * (2 * n_tok * d * 2) * 2          # encode pass + attention pass, K and V
-    return {"value": round(bytes_bf16 / el / 1e9, 4), "unit": "GB/s (bf16-equivalent)", "cores": threads,
-            "kind": "oracle", "seconds": round(el, 2),
-            "sample": f"stream 0: encode {n_tok} K (QJL) + {n_tok} V tokens, then attention of its "
-                      f"{Hq // Hkv} query heads over them; {reps} repetitions"}
+        pass
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except Exception:
+        pass
+    return "unknown"
+
+
+def _parity_sample(sample_k, sample_v, pk, pv, ck, cv, streams, N, d):
+    """Flag and mismatch counts of the GPU's own packed bytes against the oracle on the CPU
+    baseline's benchmark sample (stream 0, its first tokens): indices differ only at coordinates the
+    oracle flags within 1e-6 of a threshold, sketch bits only where |S e| < 1e-6."""
+    import numpy as np
+
+    import kv_cache_transform_amd as T
+    from oracle import tq_oracle as O
+    from synth import inputs as I
+
+    n = sample_k.shape[1]
+    res = {"tokens": n}
+    for tag, x, buf, c in (("k", sample_k, pk, ck), ("v", sample_v, pv, cv)):
+        lay = T.get_layout(c, streams, N)
+        ib, sb = d * c.b // 8, c.m // 8
+        small = O.layout(d, c.b, c.m, 1, n)
+        host = np.zeros(small["total_bytes"], dtype=np.uint8)
+        host[:n * ib] = buf[lay["off_idx"]:lay["off_idx"] + n * ib].cpu().numpy()
+        host[small["off_norm"]:small["off_norm"] + 2 * n] = buf[lay["off_norm"]:lay["off_norm"] + 2 * n].cpu().numpy()
+        if c.m:
+            host[small["off_sketch"]:small["off_sketch"] + n * sb] = \
+                buf[lay["off_sketch"]:lay["off_sketch"] + n * sb].cpu().numpy()
+            host[small["off_rnorm"]:small["off_rnorm"] + 2 * n] = \
+                buf[lay["off_rnorm"]:lay["off_rnorm"] + 2 * n].cpu().numpy()
+        g = O.unpack_tensor(host, d, c.b, c.m, 1, n)[0]
+        t, cent = O.lloyd_max(d, c.b)
+        S = O.gaussian_matrix(c.seed, 0, c.m, d).astype(np.float64) if c.m else None
+        o = O.encode(O.bf16_bits_to_f64(I.bf16_bits(x[0])), O.head_signs(c.seed, 0, d), t, cent, S)
+        mis = g["idx"] != o["idx"]
+        res[f"{tag}_flagged"] = int(o["flag"].sum())
+        res[f"{tag}_idx_mismatch"] = int(mis.sum())
+        res[f"{tag}_idx_mismatch_unflagged"] = int((mis & ~o["flag"]).sum())
+        if c.m:
+            k = O.sketch(o["y"] - cent[g["idx"]], S)          # from the GPU's indices
+            smis = g["sigma"] != k["sigma"]
+            res[f"{tag}_sketch_flagged"] = int(k["sflag"].sum())
+            res[f"{tag}_sketch_mismatch"] = int(smis.sum())
+            res[f"{tag}_sketch_mismatch_unflagged"] = int((smis & ~k["sflag"]).sum())
+    return res
+
+
+def cpu_baseline(parity_sample: dict, min_s=0.3):
+    """The oracle, unchanged, on the host cores: every workload's steps on a bounded sample (see
+    CPU_CONFIGS), once on one core and once on all cores (a process pool, one BLAS thread per
+    worker, each worker on its own seeded sample), as bf16-equivalent GB/s per step and workload.
+    `value` is the all-core rate of the benchmark step's oracle steps (encode K, encode V, attention,
+    with the bytes counted as the GPU value counts them)."""
+    import multiprocessing as mp
+    import statistics
+
+    from threadpoolctl import threadpool_info, threadpool_limits
+
+    t_all = time.perf_counter()
+    n_cpu = os.cpu_count() or 1
+    workers = max(1, min(n_cpu, 16))
+    import torch
+    torch_threads = torch.get_num_threads()
+    torch.set_num_threads(1)
+    with threadpool_limits(1):
+        one = {name: _oracle_ops(name, 11, min_s) for name in CPU_CONFIGS}
+    torch.set_num_threads(torch_threads)
+    ctx = mp.get_context("spawn")
+    with ctx.Pool(workers) as pool:
+        runs = pool.map(_cpu_worker, [(101 + w, min_s) for w in range(workers)])
+
+    def rate(sec, nbytes, k=1):
+        return round(k * nbytes / sec / 1e9, 5)
+
+    per = {}
+    for name in CPU_CONFIGS:
+        per[name] = {"sample": CPU_CONFIGS[name], "ops": {}}
+        for op, (sec, nbytes) in one[name].items():
+            med = statistics.median(r[name][op][0] for r in runs)
+            per[name]["ops"][op] = {"one_core_GBs": rate(sec, nbytes), "all_cores_GBs": rate(med, nbytes, workers)}
+    step_ops = ("encode_k", "encode_v", "attention")
+    step_bytes = sum(one["4"][op][1] for op in step_ops)
+    step_one = sum(one["4"][op][0] for op in step_ops)
+    step_all = statistics.median(sum(r["4"][op][0] for op in step_ops) for r in runs)
+    blas = sorted({f"{i.get('internal_api')} x{i.get('num_threads')}" for i in threadpool_info()
+                   if i.get("user_api") == "blas"})
+    return {"value": rate(step_all, step_bytes, workers), "unit": "GB/s (bf16-equivalent)", "cores": workers,
+            "kind": "oracle",
+            "sample": "benchmark step (encode K with QJL m = 128, encode V, attention) on " + CPU_CONFIGS["4"] +
+                      f"; {workers} worker processes, each on its own seeded sample, one BLAS thread each",
+            "one_core": {"value": rate(step_one, step_bytes), "cores": 1},
+            "cpu_model": _cpu_model(), "os_cpu_count": n_cpu, "blas": blas,
+            "per_workload": per,
+            "parity_sample": parity_sample,
+            "seconds": round(time.perf_counter() - t_all, 1)}
 
 
 if __name__ == "__main__":
