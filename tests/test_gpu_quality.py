@@ -6,8 +6,13 @@ Metrics, for T = softmax(q Kᵀ/sqrt(d)) V on the exact bf16 cache and T̂ on th
   relMSE_T = ||T - T̂||²_F / ||T||²_F;  d2 = sqrt((1 - cos(T, T̂))² + NF²), NF = relMSE_T/(1 + relMSE_T);
   relMSE_K: only K compressed (scores from tq_qk_scores, exact V); relMSE_V: only V compressed;
   ptcosine_K/V: mean over tokens of cos(k, k̂) with k̂ from tq_decode.
-cos(T, T̂) is taken over the flattened outputs (the pages do not say per row or whole).  These are
-measurements with sanity bounds, not parity; parity lives in test_gpu_parity.py."""
+cos(T, T̂) is taken over the flattened outputs (the pages do not say per row or whole).
+On the key path alone ([AB] §5 "Jensen's inequality", its Figure 2 and Table 2; [SI] abstract):
+  KL = KL(softmax(q·k/sqrt d) || softmax(ŝ/sqrt d)) per query, ŝ the score estimates of tq_qk_scores;
+  top-5 recall = |top5(q·k) ∩ top5(ŝ)| / 5 per query (the pages name the metric without defining it;
+  this is the plain reading: the share of the five highest exact scores among the five highest
+  estimates).
+These are measurements with sanity bounds, not parity; parity lives in test_gpu_parity.py."""
 import math
 
 import numpy as np
@@ -122,3 +127,47 @@ def test_hip_and_oracle_agree_in_distribution_with_different_seeds():
     p_off = stats.ks_2samp(pq(gpu), pq(oracle(b - 1))).pvalue     # the test can tell one bit apart
     print(f"KS HIP vs oracle (different seeds), per-query relMSE_T: p = {p:.3f}; against b-1: p = {p_off:.1e}")
     assert p > 1e-3 and p_off < 1e-6
+
+
+def _regime4(name, seed, sub):
+    """the four regimes of [AB] §8 named in the text (its Table 4 is missing): heavy-tailed, the flat
+    rank-8 and the steep rank-4 (1 : 1/2 : 1/4 : 1/8) subspaces with noise std 0.05, isotropic"""
+    if name == "isotropic":
+        return I.gaussian((H, N, D), seed, device=DEV)
+    if name == "fattail":
+        return I.student_t(H, N, D, 3, seed, device=DEV)
+    spec = {"lowrank_aligned": [1.0] * 8, "lowrank_steep": [1.0, 0.5, 0.25, 0.125]}[name]
+    return I.low_rank(H, N, D, spec, 0.05, seed, sub, n_heads=H, device=DEV)
+
+
+def _kl_top5(K, q, b, m, kind, seed):
+    ck = T.Codec(D, b, m, H, seed, kind)
+    pk = T.encode(ck, K)
+    k64, q64 = _f64(K), _f64(q)[0].reshape(H, NQ, D)
+    s_hat = T.qk_scores(ck, q[0].reshape(H, NQ, D).contiguous(), pk, N).cpu().numpy().astype(np.float64)
+    sc = 1.0 / math.sqrt(D)
+    kl, rec = [], []
+    for h in range(H):
+        ex = q64[h] @ k64[h].T
+        kl.append(O.kl_divergence(_softmax(ex * sc), _softmax(s_hat[h] * sc)))
+        top_ex, top_q = np.argsort(-ex, axis=1)[:, :5], np.argsort(-s_hat[h], axis=1)[:, :5]
+        rec.append([len(set(a.tolist()) & set(c.tolist())) / 5.0 for a, c in zip(top_ex, top_q)])
+    return float(np.mean(kl)), float(np.mean(rec))
+
+
+@pytest.mark.parametrize("regime", ["fattail", "lowrank_aligned", "lowrank_steep", "isotropic"])
+def test_kl_and_top5_recall_across_regimes(regime):
+    K = _regime4(regime, 620, 91)
+    q = I.gaussian((1, H * NQ, D), 629, device=DEV)
+    res = {}
+    for b in (2, 3, 4):
+        for m, kind, label in ((0, 0, "TQ-KV"), (D, 1, "TQ-QKV (RHT)")):
+            kl, rec = _kl_top5(K, q, b, m, kind, 1300 + b)
+            res[(b, label)] = (kl, rec)
+            print(f"{regime:15s} b={b} {label:13s} KL {kl:.5f} top-5 recall {rec:.3f}")
+            assert kl >= 0.0 and 0.0 <= rec <= 1.0
+    for label in ("TQ-KV", "TQ-QKV (RHT)"):
+        kls = [res[(b, label)][0] for b in (2, 3, 4)]
+        recs = [res[(b, label)][1] for b in (2, 3, 4)]
+        assert kls[0] > kls[1] > kls[2], (label, kls)              # more bits, closer attention weights
+        assert recs[2] > recs[0], (label, recs)                     # and more of the top-5 kept

@@ -218,6 +218,35 @@ def test_scores_and_attention_equal_the_dense_products_of_the_decoded_cache():
     assert np.allclose(out, p @ vh, rtol=1e-12, atol=1e-12)
 
 
+def test_scores_use_the_stored_tail():
+    """Reading of the printed estimator <q_Z, z_k>, which sums the semantic dimensions only: the
+    record stores the tail too (§3.2: 8 bits on 4 semantic dimensions plus 2 bits on the other 124
+    make 280 bits per token, tests/golden/sq_storage_bits.txt), and eq. (1) runs on the
+    reconstructed K, so the score takes every stored dimension: exactly <q, K̂>.  Dropping the tail
+    leaves out <q_tail, ẑ_tail>, which is an unbiased part of <q, k> the record does hold: here the
+    semantic-only form errs several times more against the exact q.k."""
+    rng = np.random.default_rng(16)
+    d = 64
+    spec = np.concatenate([np.full(4, 4.0), np.full(d - 4, 0.3)])   # 4 strong dimensions, a real tail
+    k = _gaussian_data(rng, spec, 4500)
+    mk = Q.calibrate(k[:500], 4, 2)
+    de = mk["d_eff"]
+    assert 0 < de < d and np.all(mk["bits"][de:] == 2)
+    rk = Q.encode(k[500:], mk)
+    q = rng.standard_normal((8, d))
+    full = Q.scores(q, rk["idx"], mk)
+    z_hat = Q.dequantise(rk["idx"], mk)
+    qz = q @ mk["U"]
+    semantic = qz[:, :de] @ z_hat[:, :de].T
+    tail = qz[:, de:] @ z_hat[:, de:].T
+    assert np.allclose(full, semantic + tail, rtol=1e-12, atol=1e-12)
+    assert np.allclose(full, q @ Q.decode(rk["idx"], mk).T, rtol=1e-12, atol=1e-12)
+    exact = q @ k[500:].T
+    e_full = np.mean((full - exact) ** 2)
+    e_sem = np.mean((semantic - exact) ** 2)
+    assert e_sem > 5 * e_full, (e_sem, e_full)
+
+
 def test_covariance_is_not_centred():
     x = np.array([[1.0, 2.0], [3.0, 4.0]])
     assert np.allclose(Q.covariance(x), np.array([[5.0, 7.0], [7.0, 10.0]]))
