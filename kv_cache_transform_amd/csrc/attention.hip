@@ -59,12 +59,26 @@ struct AttnGeom {
     static constexpr int KE = 4 * PK;                // bytes per K LUT entry
     static constexpr int KR = (NEK * KE * (128 / KE) <= 32768) ? 128 / KE : 1;
     static constexpr int VR = VPAIR ? 32 : 1;        // copies of the 1 KiB value pair LUT
-    // 4-bit keys and values: the LUTs have 256 entries of 8 (K: hi pair, lo pair) and 4 bytes (V),
-    // so one table of 256-byte rows holds entry e of both (16 K copies, then 32 V copies), and a
+    // 4-bit keys and values: the LUTs have 256 entries of 4 bytes each (V pair; K hi pair; K lo
+    // pair), so two tables of 256-byte rows hold 32 copies of each: row e of the first is
+    // [V pair x 32 | K hi pair x 32], row e of the second (64 KiB on) [K lo pair x 32 | unused].  A
     // lane's address is the byte index shifted by 8 or-ed with its copy offset: one v_perm_b32 per
-    // lookup.
+    // lookup, and the lo pair is the same address plus a constant (the read's immediate offset).
+    // Every read is 4 bytes into the register the MFMA operand needs, and lanes l, l + 16 of a
+    // 32-lane phase use different banks.
     static constexpr bool KV256 = VPAIR && PK == 2 && NEK == 256;
+    static constexpr int KV_LO = 65536 - 128;        // lo pair address - hi pair address
+    // threads per block: the 128 KiB of tables are shared by 8 waves where 2 waves per SIMD fit
+    static constexpr int THREADS = (KV256 && D <= 128) ? 512 : 256;
 };
+
+// a * b + c with a the fp16 number i of the four in v (the compiler folds the widening into the
+// fma: v_fma_mix_f32)
+__device__ __forceinline__ float fma_h(const u32x2& v, int i, float b, float c) {
+    const uint32_t w = v[i >> 1];
+    const _Float16 a = __builtin_bit_cast(_Float16, (uint16_t)((i & 1) ? (w >> 16) : (w & 0xffffu)));
+    return fmaf((float)a, b, c);
+}
 
 // byte offset (idx << 8) | off, idx = byte `which` of w, off < 256: D = {0, 0, w.byte[which], off.byte0}
 __device__ __forceinline__ uint32_t row256(uint32_t w, uint32_t off, int which) {
@@ -188,14 +202,15 @@ __device__ __forceinline__ void attn_chunk(const AttnChunk<AttnGeom<D, BK, BV>::
                 }
             } else if constexpr (Gm::KV256) {
                 // coordinates (8k + 2h, +1) are byte h of packed word k
+                u32x4 kh, kq;
 #pragma unroll
                 for (int h = 0; h < 4; ++h) {
-                    const half4 e = *reinterpret_cast<const half4*>(kvl + row256(cur.kw[T][k], koff, h));
-                    ka[2 * h] = e[0];
-                    ka[2 * h + 1] = e[1];
-                    kal[2 * h] = e[2];
-                    kal[2 * h + 1] = e[3];
+                    const uint8_t* e = kvl + row256(cur.kw[T][k], koff, h);
+                    kh[h] = *reinterpret_cast<const uint32_t*>(e);
+                    kq[h] = *reinterpret_cast<const uint32_t*>(e + Gm::KV_LO);
                 }
+                ka = __builtin_bit_cast(half8, kh);
+                kal = __builtin_bit_cast(half8, kq);
             } else {
                 static_assert(PK == 2, "attention keys use 2 or 4 coordinates per LUT entry");
 #pragma unroll
@@ -227,13 +242,14 @@ __device__ __forceinline__ void attn_chunk(const AttnChunk<AttnGeom<D, BK, BV>::
         }
         // output lane (q = l16, g) holds tokens t0 + 16T + 4g + i; the queries (and their sketch
         // projections) already carry the softmax scale in log2 units (and sqrt(pi/2)/m) and the
-        // row's power of two, and the keys 2^12, so the base-2 logit is
-        // n16 · rowf · (2^-12 s1 + r16 s2), with rowf the row factor (times 2^-12 for s1)
+        // row's power of two, the keys 2^12 and the sign operand ±2^12, so the base-2 logit is
+        // rowf · n16 · (s1 + r16 s2), with rowf the row factor (times 2^-12); lg holds
+        // n16 (s1 + r16 s2) and rowf (> 0, the lane's own) is applied in the softmax
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             float sc = s1[i];
-            if constexpr (QJL) sc = fmaf(half_of(cur.kr[T], i) * 4096.0f, s2[i], sc);
-            float v = (half_of(cur.kn[T], i) * rowf) * sc;
+            if constexpr (QJL) sc = fma_h(cur.kr[T], i, s2[i], sc);
+            float v = fma_h(cur.kn[T], i, sc, 0.0f);
             if (!FULL && t0 + 16 * T + 4 * g + i >= t_end) v = -INFINITY;
             lg[4 * T + i] = v;
         }
@@ -242,7 +258,7 @@ __device__ __forceinline__ void attn_chunk(const AttnChunk<AttnGeom<D, BK, BV>::
     float cmax = lg[0];
 #pragma unroll
     for (int r = 1; r < 8; ++r) cmax = fmaxf(cmax, lg[r]);
-    cmax = max4(cmax);
+    cmax = max4(cmax) * rowf;
     const float m_new = fmaxf(S.m_run, cmax);
     if (__builtin_amdgcn_read_exec() & __ballot(m_new != S.m_run)) {
         const float alpha = __builtin_amdgcn_exp2f(S.m_run - m_new);
@@ -254,11 +270,18 @@ __device__ __forceinline__ void attn_chunk(const AttnChunk<AttnGeom<D, BK, BV>::
     float wsum = 0.0f;
     half8 wb;
 #pragma unroll
-    for (int r = 0; r < 8; ++r) {
-        const _Float16 wh = (_Float16)__builtin_amdgcn_exp2f(lg[r] - m_new);
-        wsum += (float)wh;
-        wb[r] = wh * (_Float16)half_of(cur.vn[r >> 2], r & 3);
-    }
+    for (int T = 0; T < 2; ++T)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            // tokens r, r + 1 of the lane's eight: fp16 norms h of the pair word of tile T
+            const int r = 4 * T + 2 * h;
+            const half2v wh = {(_Float16)__builtin_amdgcn_exp2f(fmaf(rowf, lg[r], -m_new)),
+                               (_Float16)__builtin_amdgcn_exp2f(fmaf(rowf, lg[r + 1], -m_new))};
+            wsum = __builtin_amdgcn_fdot2(wh, half2v{(_Float16)1.0f, (_Float16)1.0f}, wsum, false);
+            const half2v wv = wh * __builtin_bit_cast(half2v, h ? cur.vn[T].y : cur.vn[T].x);
+            wb[r] = wv[0];
+            wb[r + 1] = wv[1];
+        }
     S.l_run += wsum;
     // ---- values: A = V̂^T tile n (row = coordinate NT*l16 + n), 8 tokens of k-block g -------------
     if constexpr (Gm::VPAIR) {
@@ -301,7 +324,7 @@ __device__ __forceinline__ void attn_chunk(const AttnChunk<AttnGeom<D, BK, BV>::
 }
 
 template <int D, int BK, int BV, bool QJL>
-__global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__((AttnGeom<D, BK, BV>::THREADS), (D <= 128 ? 2 : 1)) void attn_kernel(AttnArgs a) {
     using Gm = AttnGeom<D, BK, BV>;
     constexpr int C = Gm::C, KS = Gm::KS, PK = Gm::PK, NEK = Gm::NEK, NT = Gm::NT;
     constexpr int LV = 1 << BV;
@@ -311,18 +334,22 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attn_kernel(AttnArgs 
     __shared__ uint32_t klut[KV ? 1 : NEK * KE / 4 * KR];          // copy c of entry e at (e KR + c) KE bytes
     __shared__ _Float16 vlut[LV];
     __shared__ uint32_t vlut2[Gm::VPAIR && !KV ? 256 * VR : 1];  // copy c of entry e at word e VR + c
-    __shared__ uint32_t kvlut[KV ? 256 * 64 : 1];                 // row e: 16 K copies (8 B), 32 V copies (4 B)
-    __shared__ u32x2 sgn4[16];                                     // ±1 halves of the 4 bits of a nibble
+    __shared__ uint32_t kvlut[KV ? 2 * 256 * 64 : 1];             // the two tables of 256-byte rows
+    __shared__ u32x2 sgn4[16];                                     // ±2^12 halves of the 4 bits of a nibble
     if constexpr (KV) {
         const uint32_t* src = reinterpret_cast<const uint32_t*>(a.tk.lut_hl);   // entry e: hi pair, lo pair
-        for (int i = threadIdx.x; i < 256 * 64; i += blockDim.x) {
-            const int e = i >> 6, c = i & 63;
-            if (c < 32) {
-                kvlut[i] = src[2 * e + (c & 1)];
-            } else {
+        for (int i = threadIdx.x; i < 2 * 256 * 64; i += blockDim.x) {
+            const int tab = i >> 14, e = (i >> 6) & 255, c = i & 63;
+            uint32_t w;
+            if (tab == 0 && c < 32) {
                 const half2v hv = {(_Float16)a.tv.cent[e & 15], (_Float16)a.tv.cent[e >> 4]};
-                kvlut[i] = __builtin_bit_cast(uint32_t, hv);
+                w = __builtin_bit_cast(uint32_t, hv);
+            } else if (tab == 0) {
+                w = src[2 * e];
+            } else {
+                w = c < 32 ? src[2 * e + 1] : 0u;
             }
+            kvlut[i] = w;
         }
     } else {
         const uint16_t* src = reinterpret_cast<const uint16_t*>(a.tk.lut_hl);
@@ -344,8 +371,8 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attn_kernel(AttnArgs 
         uint32_t w[2];
 #pragma unroll
         for (int j = 0; j < 2; ++j)
-            w[j] = (((threadIdx.x >> (2 * j)) & 1) ? 0x3c00u : 0xbc00u) |
-                   ((((threadIdx.x >> (2 * j + 1)) & 1) ? 0x3c00u : 0xbc00u) << 16);
+            w[j] = (((threadIdx.x >> (2 * j)) & 1) ? 0x6c00u : 0xec00u) |
+                   ((((threadIdx.x >> (2 * j + 1)) & 1) ? 0x6c00u : 0xec00u) << 16);
         sgn4[threadIdx.x] = u32x2{w[0], w[1]};
     }
     __syncthreads();
@@ -355,9 +382,9 @@ __global__ __launch_bounds__(256, (D <= 128 ? 2 : 1)) void attn_kernel(AttnArgs 
     const uint8_t* kl = reinterpret_cast<const uint8_t*>(klut) + (lane % KR) * KE;      // the lane's copies
     const uint8_t* vl2 = reinterpret_cast<const uint8_t*>(vlut2) + (lane % VR) * 4;
     const uint8_t* kvl = reinterpret_cast<const uint8_t*>(kvlut);
-    const uint32_t koff = (uint32_t)(lane & 15) * 8u, voff = 128u + (uint32_t)(lane & 31) * 4u;
+    const uint32_t koff = 128u + (uint32_t)(lane & 31) * 4u, voff = (uint32_t)(lane & 31) * 4u;
     const uint32_t ksh = (uint32_t)((g * (a.tk.m >> 5)) & 3) * 8u;   // bit offset of the lane's sketch bytes
-    const int64_t item = (int64_t)blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+    const int64_t item = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave_id();
     const int64_t n_streams = (int64_t)a.batch * a.n_kv_heads;
     if (item >= n_streams * a.n_split) return;
     const int64_t st = item / a.n_split;
@@ -532,9 +559,10 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 
 template <int D, int BK, int BV, bool QJL>
 static hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
+    constexpr int threads = AttnGeom<D, BK, BV>::THREADS, waves = threads / 64;
     const int64_t items = (int64_t)a.batch * a.n_kv_heads * a.n_split;
-    const int64_t blocks = (items + 3) / 4;
-    hipLaunchKernelGGL((attn_kernel<D, BK, BV, QJL>), dim3((unsigned)blocks), dim3(256), 0, s, a);
+    const int64_t blocks = (items + waves - 1) / waves;
+    hipLaunchKernelGGL((attn_kernel<D, BK, BV, QJL>), dim3((unsigned)blocks), dim3(threads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)((int64_t)a.batch * a.n_q_heads)), dim3(256), 0, s, a);

@@ -32,6 +32,10 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t f2u(float f) { return __builtin_bit_cast(uint32_t, f); }
 __device__ __forceinline__ float u2f(uint32_t u) { return __builtin_bit_cast(float, u); }
 
+// the wave's index in its block as a wave-uniform (scalar) value, so that work indices, loop
+// bounds and base addresses derived from it stay in SGPRs
+__device__ __forceinline__ int wave_id() { return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6)); }
+
 // bf16 pair dot products with an inline zero accumulator (three-operand VOP3P form):
 //   dot2_bf16(a, b)        = a.lo*b.lo + a.hi*b.hi
 //   dot2_bf16_nhi(a, b)    = a.lo*b.lo - a.hi*b.hi   (neg_hi on the second operand)
