@@ -118,7 +118,7 @@ __global__ __launch_bounds__(256, ((D > 128 && (QJL || !BF16)) || (QJL && !BF16)
 
     const int lane = threadIdx.x & 63;
     const int v = lane & 15, g = lane >> 4;
-    const int wave = threadIdx.x >> 6;
+    const int wave = wave_id();
     const bool plain = a.t.rotation == 1;          // Plain-KV: no sign flip, no WHT
     const float gA = 0.5f * (float)G;
     const float gB = 0.5f * (float)G + 1.0f;       // entry 0 is a guard cell
