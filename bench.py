@@ -35,16 +35,16 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published (the sketch p
 # the kernel's sources are the ones it was measured on (sha256 of the .hip file + shared headers).
 FETCH_UNIT_B, WRITE_UNIT_B = 2048, 1024
 TRAFFIC = {
-    "encode_k": {"fetch": 2098030.75, "write": 1394614.0625, "src": "encode.hip",
-        "sha": "c589ce80e2a701247301e92e5107468e85a7a0a8088b9237288811d0dd5c6e73"},
-    "encode_v": {"fetch": 2099982.6875, "write": 1091347.4375, "src": "encode.hip",
-        "sha": "c589ce80e2a701247301e92e5107468e85a7a0a8088b9237288811d0dd5c6e73"},
-    "decode_attention": {"fetch": 1230027.0, "write": 4160.0, "src": "attention.hip",
-        "sha": "69a8cd8a939733737d2f09c7b9bbcab78f7f6fcdff7c06fb761153681d8161a9"},
-    "decode_v_bf16": {"fetch": 550382.1875, "write": 4194304.0, "src": "decode.hip",
+    "encode_k": {"fetch": 2098047.4375, "write": 1394455.96875, "src": "encode.hip",
+        "sha": "f5c0fbd7bd1cc3c39b7b4ce796eebf8e47614b993815acc41d6e99a7db5f2283"},
+    "encode_v": {"fetch": 2101601.125, "write": 1091294.4375, "src": "encode.hip",
+        "sha": "f5c0fbd7bd1cc3c39b7b4ce796eebf8e47614b993815acc41d6e99a7db5f2283"},
+    "decode_attention": {"fetch": 1229524.875, "write": 4160.0, "src": "attention.hip",
+        "sha": "4be06b54bfca6982975224479351383ef5ca8ff0715ceec477526c67f395d14a"},
+    "decode_v_bf16": {"fetch": 550860.1875, "write": 4194304.0, "src": "decode.hip",
         "sha": "2add9ea1fa8cf5d1d37b9846a4505b28cdfa3553557c2e41c88d2f2cc96455e9"},
 }
-TRAFFIC_HEADERS_SHA = ("9241f7e7fc6398e3b61bd782d033f3beac2c8fe34392745cceb9f2f364e6409c"   # common.hpp
+TRAFFIC_HEADERS_SHA = ("ab1b24f667c0da7a2104e5378715b7e9fefd5b2b0310679390021387480c9abe"   # common.hpp
                        "68dbed2b9697855851fc18a47835498cefdd60b20f7e0c05282a0b59228d584f")  # kernels.hpp
 
 
