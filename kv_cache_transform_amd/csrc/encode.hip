@@ -22,8 +22,17 @@
 
 namespace tq {
 
+// Waves per block: the sketch of bf16 input at d = 256 with S in LDS runs 8 waves (two per SIMD,
+// 254 VGPRs) on one copy of S, which leaves no room for a second block; everything else runs 4.
+template <int D, bool QJL, bool BF16, bool S_LDS>
+constexpr int enc_waves() { return (QJL && BF16 && S_LDS && D > 128) ? 8 : 4; }
+
 template <int D, int B, bool QJL, bool BF16, bool S_LDS>
-__global__ __launch_bounds__(256, ((D > 128 && (QJL || !BF16)) || (QJL && !BF16) ? 1 : (D > 128 ? 2 : 3))) void encode_kernel(EncodeArgs a) {
+__global__ __launch_bounds__((64 * enc_waves<D, QJL, BF16, S_LDS>()),
+                             ((enc_waves<D, QJL, BF16, S_LDS>()) == 8 ? 2
+                              : ((D > 128 && (QJL || !BF16)) || (QJL && !BF16) ? 1 : (D > 128 ? 2 : 3))))
+void encode_kernel(EncodeArgs a) {
+    constexpr int NWV = enc_waves<D, QJL, BF16, S_LDS>();
     constexpr int C = D / 4, R = D / 16, L = 1 << B;
     constexpr int NW = (C * B + 31) / 32;          // packed words per lane
     constexpr int CB = C * B / 8;                   // packed bytes per lane
@@ -174,7 +183,7 @@ __global__ __launch_bounds__(256, ((D > 128 && (QJL || !BF16)) || (QJL && !BF16)
     for (int gi = 0; gi < NG; ++gi) load_group(nxt[gi], tb0 + wave * NG + gi);
 
 #pragma unroll 1
-    for (int64_t t = tb0 + wave * NG; t < tb1; t += 4 * NG) {
+    for (int64_t t = tb0 + wave * NG; t < tb1; t += NWV * NG) {
         // keep the LDS operand tables in LDS (re-read per pass) instead of pinned in registers
         asm volatile("" ::: "memory");
         half8 bh[NG][QJL ? C / 8 : 1], bl[NG][QJL ? C / 8 : 1];
@@ -225,7 +234,7 @@ __global__ __launch_bounds__(256, ((D > 128 && (QJL || !BF16)) || (QJL && !BF16)
 #pragma unroll
                 for (int k = 0; k < NIW; ++k) asm volatile("" ::"v"(w[k]) : "memory");
                 asm volatile("" ::"v"(n2) : "memory");
-                if (t + 4 * NG < tb1) load_group(nxt[gi], t + 4 * NG + gi);
+                if (t + NWV * NG < tb1) load_group(nxt[gi], t + NWV * NG + gi);
                 if (!plain) fwht_slots<C, 8>(x);
             } else {
 #pragma unroll
@@ -234,7 +243,7 @@ __global__ __launch_bounds__(256, ((D > 128 && (QJL || !BF16)) || (QJL && !BF16)
                     n2 = fmaf(xv, xv, n2);
                     x[s] = plain ? xv : xv * sg[s];
                 }
-                if (t + 4 * NG < tb1) load_group(nxt[gi], t + 4 * NG + gi);
+                if (t + NWV * NG < tb1) load_group(nxt[gi], t + NWV * NG + gi);
                 if (!plain) {
                     fwht_slots<C, 1>(x);
                     fwht_cross<C>(x);
@@ -431,15 +440,16 @@ __global__ __launch_bounds__(256, ((D > 128 && (QJL || !BF16)) || (QJL && !BF16)
     }
 }
 
-// resident blocks per CU of kernel k at `lds` bytes of dynamic LDS (cached per kernel and size)
-static int blocks_per_cu(const void* k, size_t lds) {
+// resident blocks per CU of kernel k at `threads` per block and `lds` bytes of dynamic LDS (cached
+// per kernel and size)
+static int blocks_per_cu(const void* k, size_t lds, int threads) {
     static std::mutex mu;
     static std::map<std::pair<const void*, size_t>, int> cache;
     std::lock_guard<std::mutex> lock(mu);
     auto it = cache.find({k, lds});
     if (it != cache.end()) return it->second;
     int n = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, 256, lds) != hipSuccess || n < 1) n = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, k, threads, lds) != hipSuccess || n < 1) n = 1;
     cache[{k, lds}] = n;
     return n;
 }
@@ -478,8 +488,9 @@ static hipError_t launch_one(const EncodeArgs& a, int num_cus, hipStream_t s) {
             raised = true;
         }
     }
-    // one wave of blocks: as many 256-thread blocks as fit on every CU at once
-    const int64_t target = (int64_t)num_cus * blocks_per_cu(kern, lds);
+    // one wave of blocks: as many blocks as fit on every CU at once
+    const int threads = 64 * (s_lds ? enc_waves<D, QJL, BF16, true>() : enc_waves<D, QJL, BF16, (D <= 128)>());
+    const int64_t target = (int64_t)num_cus * blocks_per_cu(kern, lds, threads);
     int64_t bps = (target + a.n_streams - 1) / a.n_streams;
     if (bps > a.tiles_per_stream) bps = a.tiles_per_stream;
     if (bps < 1) bps = 1;
@@ -487,10 +498,10 @@ static hipError_t launch_one(const EncodeArgs& a, int num_cus, hipStream_t s) {
     b.tiles_per_block = (a.tiles_per_stream + bps - 1) / bps;
     const dim3 grid((unsigned)(a.n_streams * bps));
     if constexpr (D <= 128) {
-        hipLaunchKernelGGL((encode_kernel<D, B, QJL, BF16, true>), grid, dim3(256), lds, s, b);
+        hipLaunchKernelGGL((encode_kernel<D, B, QJL, BF16, true>), grid, dim3(threads), lds, s, b);
     } else {
-        if (s_lds) hipLaunchKernelGGL((encode_kernel<D, B, QJL, BF16, true>), grid, dim3(256), lds, s, b);
-        else hipLaunchKernelGGL((encode_kernel<D, B, QJL, BF16, false>), grid, dim3(256), lds, s, b);
+        if (s_lds) hipLaunchKernelGGL((encode_kernel<D, B, QJL, BF16, true>), grid, dim3(threads), lds, s, b);
+        else hipLaunchKernelGGL((encode_kernel<D, B, QJL, BF16, false>), grid, dim3(threads), lds, s, b);
     }
     return hipGetLastError();
 }
