@@ -167,7 +167,7 @@ struct AttnState {
     float m_run, l_run;
 };
 
-template <int D, int BK, int BV, bool QJL, bool FULL>
+template <int D, int BK, int BV, bool QJL, bool FULL, bool PQ>
 __device__ __forceinline__ void attn_chunk(const AttnChunk<AttnGeom<D, BK, BV>::NWK, AttnGeom<D, BK, BV>::NWV, AttnGeom<D, BK, BV>::NKS>& cur,
                                            AttnState<AttnGeom<D, BK, BV>::NT>& S, int64_t t0, int64_t t_end,
                                            int g, int mks,
@@ -223,21 +223,32 @@ __device__ __forceinline__ void attn_chunk(const AttnChunk<AttnGeom<D, BK, BV>::
                     kal[2 * h + 1] = e[3];
                 }
             }
-            s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[k], s1, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kal, qb[k], s1, 0, 0, 0);
-            s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qbl[k], s1, 0, 0, 0);
+            if constexpr (PQ) {
+                // columns 0-7: query hi parts, 8-15: their lo parts (qb); qbl: hi parts, then zeros
+                s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[k], s1, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kal, qbl[k], s1, 0, 0, 0);
+            } else {
+                s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[k], s1, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kal, qb[k], s1, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qbl[k], s1, 0, 0, 0);
+            }
+        }
+        if constexpr (PQ) {
+            // column q + 8 holds hi·lo of query q: add it in (DPP row_shl:8 within each 16-lane row)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                s1[i] += u2f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)f2u(s1[i]), 0x108, 0xf, 0xf, true));
         }
         floatx4 s2 = {0.0f, 0.0f, 0.0f, 0.0f};
         if constexpr (QJL) {
 #pragma unroll
             for (int k = 0; k < KS; ++k) {
-                if (k < mks) {
-                    const uint32_t wsk = __builtin_amdgcn_alignbit(cur.ks[T][(k >> 2) + 1], cur.ks[T][k >> 2], ksh);
-                    const u32x2 lo = sgn4[(wsk >> (8 * (k & 3))) & 0xfu];
-                    const u32x2 hi = sgn4[(wsk >> (8 * (k & 3) + 4)) & 0xfu];
-                    const half8 sa = __builtin_bit_cast(half8, u32x4{lo[0], lo[1], hi[0], hi[1]});
-                    s2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(sa, pb[k], s2, 0, 0, 0);
-                }
+                // branch-free: steps past the sketch (k >= m/32) multiply a zero query operand
+                const uint32_t wsk = __builtin_amdgcn_alignbit(cur.ks[T][(k >> 2) + 1], cur.ks[T][k >> 2], ksh);
+                const u32x2 lo = sgn4[(wsk >> (8 * (k & 3))) & 0xfu];
+                const u32x2 hi = sgn4[(wsk >> (8 * (k & 3) + 4)) & 0xfu];
+                const half8 sa = __builtin_bit_cast(half8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+                s2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(sa, pb[k], s2, 0, 0, 0);
             }
         }
         // output lane (q = l16, g) holds tokens t0 + 16T + 4g + i; the queries (and their sketch
@@ -323,7 +334,9 @@ __device__ __forceinline__ void attn_chunk(const AttnChunk<AttnGeom<D, BK, BV>::
     }
 }
 
-template <int D, int BK, int BV, bool QJL>
+// PQ: at most 8 query heads per kv head, so the query operand carries hi parts in columns 0-7
+// and lo parts in columns 8-15, and the scores take two products per step instead of three
+template <int D, int BK, int BV, bool QJL, bool PQ>
 __global__ __launch_bounds__((AttnGeom<D, BK, BV>::THREADS), (D <= 128 ? 2 : 1)) void attn_kernel(AttnArgs a) {
     using Gm = AttnGeom<D, BK, BV>;
     constexpr int C = Gm::C, KS = Gm::KS, PK = Gm::PK, NEK = Gm::NEK, NT = Gm::NT;
@@ -404,21 +417,29 @@ __global__ __launch_bounds__((AttnGeom<D, BK, BV>::THREADS), (D <= 128 ? 2 : 1))
     const int m = a.tk.m;
     const int mks = m >> 5;
 
-    // query operands (B of the score products): lane column q = l16, k-block g
+    // query operands (B of the score products): lane column q = l16, k-block g (with PQ, column
+    // q + 8 carries query q's lo parts in qb and zeros in qbl)
     const bool qvalid = l16 < a.group;
-    const int64_t qrow = (int64_t)bidx * a.n_q_heads + (int64_t)kvh * a.group + (qvalid ? l16 : 0);
+    const int qcol = PQ ? (l16 & 7) : l16;
+    const bool qload = qcol < a.group;
+    const int64_t qrow = (int64_t)bidx * a.n_q_heads + (int64_t)kvh * a.group + (qload ? qcol : 0);
     half8 qb[KS], qbl[KS], pb[QJL ? KS : 1];
     const float rowf = a.o.rowf[qrow] * (1.0f / 4096.0f);
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
-        qb[k] = *reinterpret_cast<const half8*>(a.o.qh + qrow * D + g * C + 8 * k);
-        qbl[k] = *reinterpret_cast<const half8*>(a.o.ql + qrow * D + g * C + 8 * k);
-        if (!qvalid) qb[k] = half8{};
-        if (!qvalid) qbl[k] = half8{};
+        const half8 qh = *reinterpret_cast<const half8*>(a.o.qh + qrow * D + g * C + 8 * k);
+        const half8 ql = *reinterpret_cast<const half8*>(a.o.ql + qrow * D + g * C + 8 * k);
+        if constexpr (PQ) {
+            qb[k] = !qload ? half8{} : (l16 < 8 ? qh : ql);
+            qbl[k] = (!qload || l16 >= 8) ? half8{} : qh;
+        } else {
+            qb[k] = qvalid ? qh : half8{};
+            qbl[k] = qvalid ? ql : half8{};
+        }
         if constexpr (QJL) {
             if (k < mks) pb[k] = *reinterpret_cast<const half8*>(a.o.ph + qrow * m + g * (m / 4) + 8 * k);
             else pb[k] = half8{};
-            if (!qvalid) pb[k] = half8{};
+            if (!qload || (PQ && l16 >= 8)) pb[k] = half8{};
         }
     }
 
@@ -451,25 +472,25 @@ __global__ __launch_bounds__((AttnGeom<D, BK, BV>::THREADS), (D <= 128 ? 2 : 1))
             // math, so the wait before a chunk leaves the other buffer's loads in flight)
             attn_load<D, BK, BV, QJL, true>(B, P, t_begin + (c + 1) * 32, t_end, l16, g, m);
             __builtin_amdgcn_sched_barrier(0);
-            attn_chunk<D, BK, BV, QJL, true>(A, S, t_begin + c * 32, t_end, g, mks, qb, qbl, pb, rowf, kl,
+            attn_chunk<D, BK, BV, QJL, true, PQ>(A, S, t_begin + c * 32, t_end, g, mks, qb, qbl, pb, rowf, kl,
                                              vlut, vl2, sgn4, kvl, koff, voff, ksh);
             __builtin_amdgcn_sched_barrier(0);
             const int64_t cn = c + 2 < n_full ? c + 2 : n_full - 1;
             attn_load<D, BK, BV, QJL, true>(A, P, t_begin + cn * 32, t_end, l16, g, m);
             __builtin_amdgcn_sched_barrier(0);
-            attn_chunk<D, BK, BV, QJL, true>(B, S, t_begin + (c + 1) * 32, t_end, g, mks, qb, qbl, pb, rowf, kl,
+            attn_chunk<D, BK, BV, QJL, true, PQ>(B, S, t_begin + (c + 1) * 32, t_end, g, mks, qb, qbl, pb, rowf, kl,
                                              vlut, vl2, sgn4, kvl, koff, voff, ksh);
             __builtin_amdgcn_sched_barrier(0);
         }
         if (c < n_full) {          // odd count: A holds chunk c
-            attn_chunk<D, BK, BV, QJL, true>(A, S, t_begin + c * 32, t_end, g, mks, qb, qbl, pb, rowf, kl,
+            attn_chunk<D, BK, BV, QJL, true, PQ>(A, S, t_begin + c * 32, t_end, g, mks, qb, qbl, pb, rowf, kl,
                                              vlut, vl2, sgn4, kvl, koff, voff, ksh);
             ++c;
         }
     }
     if (t_begin + c * 32 < t_end) {
         attn_load<D, BK, BV, QJL, false>(A, P, t_begin + c * 32, t_end, l16, g, m);
-        attn_chunk<D, BK, BV, QJL, false>(A, S, t_begin + c * 32, t_end, g, mks, qb, qbl, pb, rowf, kl,
+        attn_chunk<D, BK, BV, QJL, false, PQ>(A, S, t_begin + c * 32, t_end, g, mks, qb, qbl, pb, rowf, kl,
                                           vlut, vl2, sgn4, kvl, koff, voff, ksh);
     }
     // ---- partial results: lane (q = l16, g) holds O[coord NT*(4g+i) + n][q] --------------------
@@ -562,7 +583,8 @@ static hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
     constexpr int threads = AttnGeom<D, BK, BV>::THREADS, waves = threads / 64;
     const int64_t items = (int64_t)a.batch * a.n_kv_heads * a.n_split;
     const int64_t blocks = (items + waves - 1) / waves;
-    hipLaunchKernelGGL((attn_kernel<D, BK, BV, QJL>), dim3((unsigned)blocks), dim3(threads), 0, s, a);
+    if (a.group <= 8) hipLaunchKernelGGL((attn_kernel<D, BK, BV, QJL, true>), dim3((unsigned)blocks), dim3(threads), 0, s, a);
+    else hipLaunchKernelGGL((attn_kernel<D, BK, BV, QJL, false>), dim3((unsigned)blocks), dim3(threads), 0, s, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)((int64_t)a.batch * a.n_q_heads)), dim3(256), 0, s, a);
