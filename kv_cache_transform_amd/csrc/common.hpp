@@ -52,9 +52,11 @@ __device__ __forceinline__ float dot2_bf16_nhi(uint32_t a, uint32_t b) {
 
 // (e0 - h.lo, e1 - h.hi) rounded to fp16 and packed, for a packed fp16 pair h and fp32 e0, e1
 // (v_fma_mix{lo,hi}_f16: fp32 fma with an fp16 operand, fp16 result into one half)
+// (the first instruction leaves the high half of its destination as it was, and the second
+// overwrites it, so the destination needs no initial value)
 __device__ __forceinline__ uint32_t sub_f16pair_from_f32(uint32_t h, float e0, float e1) {
-    uint32_t r = 0u;
-    asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "+v"(r) : "v"(h), "v"(e0));
+    uint32_t r;
+    asm("v_fma_mixlo_f16 %0, %1, -1.0, %2 op_sel_hi:[1,0,0]" : "=v"(r) : "v"(h), "v"(e0));
     asm("v_fma_mixhi_f16 %0, %1, -1.0, %2 op_sel:[1,0,0] op_sel_hi:[1,0,0]" : "+v"(r) : "v"(h), "v"(e1));
     return r;
 }

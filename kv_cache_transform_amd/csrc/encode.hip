@@ -12,6 +12,14 @@
 // to about 2^-22 relative; S is stored as fp16 values, so both products are exact and only the
 // fp32 accumulation rounds.  z is then within ~1e-8 of the fp64 projection of the residual, far
 // inside the 1e-6 band of a sign decision.
+//
+// Binade-grid variant (bf16 input, b <= 4, and for the sketch m <= 128): u = 3 + κ y lies in
+// [2, 4), so the search grid is addressed by bits 16..22 of u's fp32 pattern.  One v_perm_b32 puts
+// that byte next to the lane's copy offset (grid rows of 64 copies, one per lane: no bank
+// conflicts), the entry E is added to u's bits, and the top bits of the sum are the index (see
+// build_fq_grid): one v_alignbit packs it and one more v_perm_b32 addresses the lane's copy of
+// its centroid, whose row is the sum's top byte.  The remaining tables (Hadamard tiles, S) sit in
+// the rows of the centroid window that no top byte can reach.
 #include <map>
 #include <mutex>
 #include <type_traits>
@@ -19,20 +27,50 @@
 
 #include "common.hpp"
 #include "kernels.hpp"
+#include "tables.hpp"
 
 namespace tq {
 
-// Waves per block: the sketch of bf16 input at d = 256 with S in LDS runs 8 waves (two per SIMD,
-// 254 VGPRs) on one copy of S, which leaves no room for a second block; everything else runs 4.
-template <int D, bool QJL, bool BF16, bool S_LDS>
-constexpr int enc_waves() { return (QJL && BF16 && S_LDS && D > 128) ? 8 : 4; }
+// LDS map of the binade-grid variant.  [0, 32 KiB): grid row c (c = 0..127) = 64 copies of E[c].
+// From W = 32 KiB: the centroid window, 256 rows of 256 bytes addressed by the top byte of
+// w = bits(u) + E; with R = 2^(8-b) only rows idx·R and idx·R + R - 1 can be addressed, and they
+// hold 64 copies of 2^14 c[idx].  Rows idx·R + 1 .. idx·R + R - 2 hold 1 KiB pieces (four rows
+// each, PPG per gap): the signed Hadamard tiles first, then S (or the randomized Hadamard tiles)
+// in the order the MFMA A operand reads them.
+template <int B>
+struct FqLayout {
+    static constexpr int W = 32768;
+    static constexpr int R = 1 << (8 - B);
+    static constexpr int PPG = (R - 2) / 4;
+    static constexpr int cap = (1 << B) * PPG;
+    static constexpr __host__ __device__ int piece(int p) { return W + ((p / PPG) * R + 1) * 256 + (p % PPG) * 1024; }
+};
+// LDS bytes of the binade-grid kernel: the whole centroid window with the sketch, else 64 KiB.  A
+// grid or centroid address is at most 255·256 + 252 from its table's base whatever u is (a NaN
+// input included), so every read stays inside the array.
+template <int D, int B, bool QJL>
+constexpr int fq_lds_bytes() { return QJL ? FqLayout<B>::W + 65536 : 65536; }
 
-template <int D, int B, bool QJL, bool BF16, bool S_LDS>
-__global__ __launch_bounds__((64 * enc_waves<D, QJL, BF16, S_LDS>()),
-                             ((enc_waves<D, QJL, BF16, S_LDS>()) == 8 ? 2
-                              : ((D > 128 && (QJL || !BF16)) || (QJL && !BF16) ? 1 : (D > 128 ? 2 : 3))))
+// Waves per block: the sketch of bf16 input at d = 256 with S in LDS runs 8 waves (two per SIMD,
+// 254 VGPRs) on one copy of S, which leaves no room for a second block; the binade-grid kernel
+// (64 or 96 KiB of LDS) runs one block per CU of three waves per SIMD; everything else runs 4.
+template <int D, bool QJL, bool BF16, bool S_LDS, bool FQ>
+constexpr int enc_waves() {
+    if (FQ) return 12;
+    return (QJL && BF16 && S_LDS && D > 128) ? 8 : 4;
+}
+template <int D, bool QJL, bool BF16, bool S_LDS, bool FQ>
+constexpr int enc_min_blocks() {
+    if (FQ) return 1;
+    return enc_waves<D, QJL, BF16, S_LDS, FQ>() == 8 ? 2
+           : ((D > 128 && (QJL || !BF16)) || (QJL && !BF16) ? 1 : (D > 128 ? 2 : 3));
+}
+
+template <int D, int B, bool QJL, bool BF16, bool S_LDS, bool FQ>
+__global__ __launch_bounds__((64 * enc_waves<D, QJL, BF16, S_LDS, FQ>()), (enc_min_blocks<D, QJL, BF16, S_LDS, FQ>()))
 void encode_kernel(EncodeArgs a) {
-    constexpr int NWV = enc_waves<D, QJL, BF16, S_LDS>();
+    constexpr int NWV = enc_waves<D, QJL, BF16, S_LDS, FQ>();
+    static_assert(!FQ || (BF16 && B <= 4), "the binade grid serves bf16 input and b <= 4");
     constexpr int C = D / 4, R = D / 16, L = 1 << B;
     constexpr int NW = (C * B + 31) / 32;          // packed words per lane
     constexpr int CB = C * B / 8;                   // packed bytes per lane
@@ -50,15 +88,36 @@ void encode_kernel(EncodeArgs a) {
     const int m = a.t.m;
 
     extern __shared__ uint32_t lds[];
+    using FL = FqLayout<(B <= 4 ? B : 4)>;
+    // the binade-grid tables live in a static array, so every address formed from a table byte
+    // needs no base added (the array is the kernel's only LDS)
+    uint8_t* ldsb;
+    if constexpr (FQ) {
+        __shared__ __attribute__((aligned(16))) uint32_t fq_lds[fq_lds_bytes<D, B, QJL>() / 4];
+        ldsb = reinterpret_cast<uint8_t*>(fq_lds);
+    } else {
+        ldsb = reinterpret_cast<uint8_t*>(lds);
+    }
+    uint32_t* const ldsw = reinterpret_cast<uint32_t*>(ldsb);
     const int G = a.t.G;
     // search grid, replicated 2^rl times with the copies interleaved per cell, so lanes that use
     // different copies read different banks: cell c of copy r = words 2 (c 2^rl + r) + {0, 1}
     const int rl = a.grid_rep_log2;
-    const int ngw = (2 * (G + 3)) << rl;
-    for (int i = threadIdx.x; i < ((G + 3) << rl); i += blockDim.x) {
-        const int c = i >> rl;
-        lds[2 * i] = a.t.grid[2 * c];
-        lds[2 * i + 1] = a.t.grid[2 * c + 1];
+    const int ngw = FQ ? 0 : (2 * (G + 3)) << rl;
+    if constexpr (FQ) {
+        for (int i = threadIdx.x; i < 128 * 64; i += blockDim.x) ldsw[i] = a.t.fq_grid[i >> 6];
+        if constexpr (QJL) {
+            for (int i = threadIdx.x; i < 2 * (1 << B) * 64; i += blockDim.x) {
+                const int r2 = i >> 6, idx = r2 >> 1, row = idx * FL::R + ((r2 & 1) ? FL::R - 1 : 0);
+                ldsw[(FL::W + row * 256) / 4 + (i & 63)] = f2u(a.t.cent_x1024[idx]);
+            }
+        }
+    } else {
+        for (int i = threadIdx.x; i < ((G + 3) << rl); i += blockDim.x) {
+            const int c = i >> rl;
+            lds[2 * i] = a.t.grid[2 * c];
+            lds[2 * i + 1] = a.t.grid[2 * c + 1];
+        }
     }
     float* lds_c = reinterpret_cast<float*>(lds + ngw);
     constexpr int NKB = D / 32;                     // K blocks of the 32-point transform
@@ -67,7 +126,8 @@ void encode_kernel(EncodeArgs a) {
     u32x4* lds_A = reinterpret_cast<u32x4*>(lds + a_off);
     _Float16* lds_S = reinterpret_cast<_Float16*>(lds + a_off + NAW);
     if constexpr (QJL) {
-        for (int i = threadIdx.x; i < L; i += blockDim.x) lds_c[i] = a.t.cent_x1024[i];
+        if constexpr (!FQ)
+            for (int i = threadIdx.x; i < L; i += blockDim.x) lds_c[i] = a.t.cent_x1024[i];
         if (S_LDS && !(BF16 && a.t.sketch == 1)) {
             // S in the order the MFMA A operand reads it (see the sketch loop): the 16-byte piece
             // of lane l for row tile tau and k-step k sits at piece index (tau KS + k) 64 + l, so
@@ -82,7 +142,10 @@ void encode_kernel(EncodeArgs a) {
                 const int q = row / mq, rem = row - q * mq;
                 const int tau = rem >> 2, rh = 4 * q + (rem & 3);
                 const int gp = col / KS, k = col - gp * KS;
-                dst[(tau * KS + k) * 64 + rh + 16 * gp] = src[i];
+                if constexpr (FQ)
+                    *reinterpret_cast<u32x4*>(ldsb + FL::piece(2 * NKB + tau * KS + k) + 16 * (rh + 16 * gp)) = src[i];
+                else
+                    dst[(tau * KS + k) * 64 + rh + 16 * gp] = src[i];
             }
         }
     }
@@ -119,7 +182,8 @@ void encode_kernel(EncodeArgs a) {
                 }
                 wv[t] = w2;
             }
-            if (second) reinterpret_cast<u32x4*>(lds_S)[ee] = wv;
+            if constexpr (FQ) *reinterpret_cast<u32x4*>(ldsb + FL::piece(e >> 6) + 16 * l) = wv;
+            else if (second) reinterpret_cast<u32x4*>(lds_S)[ee] = wv;
             else lds_A[e] = wv;
         }
     }
@@ -143,6 +207,7 @@ void encode_kernel(EncodeArgs a) {
     const int rho = lane & 15;
     const int row_base = (rho >> 2) * (m >> 2) + (rho & 3);
     const uint32_t goff = (uint32_t)(lane & ((1 << rl) - 1)) << 3;   // byte offset of the lane's grid copy
+    const uint32_t lane4 = 4u * (uint32_t)lane;                        // the lane's copy in a binade-grid row
 
     // raw input words of one 16-vector group: bf16 = the lane's C contiguous coordinates; fp32 =
     // runs of R coordinates in the i(s, g) order of the butterfly network (see common.hpp)
@@ -222,8 +287,10 @@ void encode_kernel(EncodeArgs a) {
                         const bf16x8 Bv = __builtin_bit_cast(bf16x8, u32x4{w[4 * kb], w[4 * kb + 1], w[4 * kb + 2], w[4 * kb + 3]});
 #pragma unroll
                         for (int h = 0; h < 2; ++h) {
+                            const u32x4 At = FQ ? *reinterpret_cast<const u32x4*>(ldsb + FL::piece(h * NKB + kb) + 16 * lane)
+                                                : lds_A[(h * NKB + kb) * 64 + lane];
                             const floatx4 r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                __builtin_bit_cast(bf16x8, lds_A[(h * NKB + kb) * 64 + lane]), Bv,
+                                __builtin_bit_cast(bf16x8, At), Bv,
                                 floatx4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
 #pragma unroll
                             for (int i = 0; i < 4; ++i) x[8 * kb + 4 * h + i] = r[i];
@@ -269,8 +336,26 @@ void encode_kernel(EncodeArgs a) {
 #pragma unroll
             for (int k = 0; k < NW; ++k) pk[k] = 0u;
             float e2 = 0.0f;
+            if constexpr (FQ) {
+                // binade grid: u in [2, 4); slots in descending order, so that alignbit leaves the
+                // lowest slot of each word in its low bits
+                const float sU = sc * (float)kFqKappa;
 #pragma unroll
-            for (int s = 0; s < C; ++s) {
+                for (int s = C - 1; s >= 0; --s) {
+                    const float u = fmaf(x[s], sU, 3.0f);
+                    const uint32_t ga = __builtin_amdgcn_perm(f2u(u), lane4, 0x0c0c0600u);
+                    const uint32_t w = f2u(u) + *reinterpret_cast<const uint32_t*>(ldsb + ga);
+                    if constexpr (B == 3) put_bits<B>(pk, s * B, w >> 29);
+                    else pk[(s * B) >> 5] = __builtin_amdgcn_alignbit(pk[(s * B) >> 5], w, 32 - B);
+                    if constexpr (QJL) {
+                        const uint32_t ca = __builtin_amdgcn_perm(w, lane4, 0x0c0c0700u);
+                        x[s] = fmaf(x[s], sE, -*reinterpret_cast<const float*>(ldsb + FL::W + ca));
+                        e2 = fmaf(x[s], x[s], e2);
+                    }
+                }
+            }
+#pragma unroll
+            for (int s = 0; s < (FQ ? 0 : C); ++s) {
                 const float u = fmaf(x[s], sA, gB);
                 const uint32_t cell = (uint32_t)u;
                 const u32x2 ent = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(lds) + ((cell << (3 + rl)) + goff));
@@ -320,7 +405,8 @@ void encode_kernel(EncodeArgs a) {
                 for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
-                        const half8 A = __builtin_bit_cast(half8, lds_A2[(h * NKB + kb) * 64 + lane]);
+                        const half8 A = __builtin_bit_cast(half8, FQ ? *reinterpret_cast<const u32x4*>(ldsb + FL::piece(2 * NKB + h * NKB + kb) + 16 * lane)
+                                                                     : lds_A2[(h * NKB + kb) * 64 + lane]);
                         floatx4 r = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bh[gi][kb], floatx4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
                         r = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bl[gi][kb], r, 0, 0, 0);
 #pragma unroll
@@ -362,7 +448,7 @@ void encode_kernel(EncodeArgs a) {
             // shifts each sign in at bit 0), the bytes joined, and the word inverted (z >= 0).
             // Full words run branch-free; a trailing partial word (m/4 not a multiple of 32) has
             // nt < 8 tiles.
-            auto sketch_word = [&](int wb, int nt, auto full) {
+            auto sketch_word = [&](auto wb, int nt, auto full) {
                 constexpr bool FULL = decltype(full)::value;
                 const int tau0 = wb >> 2;
                 uint32_t by[NG][4];
@@ -380,8 +466,8 @@ void encode_kernel(EncodeArgs a) {
                             const int tt = 4 * hf + tl;
                             if (FULL || tt < nt) {
                                 const int tau = tau0 + tt;
-                                const half8 A = *reinterpret_cast<const half8*>(
-                                    S_LDS ? Sg + (tau * KS + k) * 512 : Sg + 4 * tau * D + 8 * k);
+                                const half8 A = FQ ? *reinterpret_cast<const half8*>(ldsb + FL::piece(2 * NKB + tau * KS + k) + 16 * lane)
+                                                   : *reinterpret_cast<const half8*>(S_LDS ? Sg + (tau * KS + k) * 512 : Sg + 4 * tau * D + 8 * k);
 #pragma unroll
                                 for (int gi = 0; gi < NG; ++gi) {
                                     acc[gi][tl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bh[gi][k], acc[gi][tl], 0, 0, 0);
@@ -427,8 +513,14 @@ void encode_kernel(EncodeArgs a) {
                 }
             };
             const int nbits = m >> 2;
-            for (int wb = 0; wb + 32 <= nbits; wb += 32) sketch_word(wb, 8, std::true_type{});
-            if (nbits & 31) sketch_word(nbits & ~31, (nbits & 31) >> 2, std::false_type{});
+            if constexpr (FQ) {
+                // m <= 128: one word per lane part, so every S piece offset is a constant
+                if (nbits == 32) sketch_word(std::integral_constant<int, 0>{}, 8, std::true_type{});
+                else sketch_word(std::integral_constant<int, 0>{}, nbits >> 2, std::false_type{});
+            } else {
+                for (int wb = 0; wb + 32 <= nbits; wb += 32) sketch_word(wb, 8, std::true_type{});
+                if (nbits & 31) sketch_word(nbits & ~31, (nbits & 31) >> 2, std::false_type{});
+            }
 #pragma unroll
             for (int gi = 0; gi < NG; ++gi) {
                 const float e2 = sum4(e2v[gi]);
@@ -454,8 +546,45 @@ static int blocks_per_cu(const void* k, size_t lds, int threads) {
     return n;
 }
 
+// binade-grid launch: bf16 input, b <= 4, the table built for this codebook, and the Hadamard
+// tiles plus S (or the randomized Hadamard tiles) within the pieces of the centroid window; the
+// Gaussian sketch also needs m <= 128 (one sketch word per lane part)
+template <int D, int B, bool QJL>
+static bool fq_fits(const EncodeArgs& a) {
+    if (a.t.fq_grid == nullptr) return false;
+    if constexpr (QJL && D > 128) return false;   // the sketch at d = 256 spills at two waves per SIMD
+    if constexpr (QJL) {
+        constexpr int nA = 2 * (D / 32);
+        const bool rht = a.t.sketch == 1;
+        if (!rht && (a.t.m > 128 || (a.t.m * D) % 512 != 0)) return false;
+        const int nS = rht ? nA : a.t.m * D / 512;
+        return nA + nS <= FqLayout<B>::cap;
+    }
+    return 2 * (D / 32) <= FqLayout<B>::cap;
+}
+
+template <int D, int B, bool QJL>
+static hipError_t launch_fq(const EncodeArgs& a, int num_cus, hipStream_t s) {
+    EncodeArgs b = a;
+    b.grid_rep_log2 = 0;
+    const void* kern = reinterpret_cast<const void*>(&encode_kernel<D, B, QJL, true, true, true>);
+    const int threads = 64 * enc_waves<D, QJL, true, true, true>();   // static LDS only
+    const int64_t target = (int64_t)num_cus * blocks_per_cu(kern, 0, threads);
+    int64_t bps = (target + a.n_streams - 1) / a.n_streams;
+    if (bps > a.tiles_per_stream) bps = a.tiles_per_stream;
+    if (bps < 1) bps = 1;
+    b.blocks_per_stream = bps;
+    b.tiles_per_block = (a.tiles_per_stream + bps - 1) / bps;
+    const dim3 grid((unsigned)(a.n_streams * bps));
+    hipLaunchKernelGGL((encode_kernel<D, B, QJL, true, true, true>), grid, dim3(threads), 0, s, b);
+    return hipGetLastError();
+}
+
 template <int D, int B, bool QJL, bool BF16>
 static hipError_t launch_one(const EncodeArgs& a, int num_cus, hipStream_t s) {
+    if constexpr (BF16 && B <= 4 && !(QJL && D > 128)) {
+        if (fq_fits<D, B, QJL>(a)) return launch_fq<D, B, QJL>(a, num_cus, s);
+    }
     EncodeArgs b = a;
     const int L = 1 << B;
     // S lives in LDS whenever it fits beside the rest (160 KiB per CU; for d = 256 and m = 256 the
@@ -476,8 +605,8 @@ static hipError_t launch_one(const EncodeArgs& a, int num_cus, hipStream_t s) {
     b.grid_rep_log2 = rl;
     const size_t head_bytes = (grid_bytes << rl) + fixed;
     const size_t lds = head_bytes + (s_lds ? s_bytes : 0);
-    const void* kern = s_lds ? reinterpret_cast<const void*>(&encode_kernel<D, B, QJL, BF16, true>)
-                             : reinterpret_cast<const void*>(&encode_kernel<D, B, QJL, BF16, (D <= 128)>);
+    const void* kern = s_lds ? reinterpret_cast<const void*>(&encode_kernel<D, B, QJL, BF16, true, false>)
+                             : reinterpret_cast<const void*>(&encode_kernel<D, B, QJL, BF16, (D <= 128), false>);
     if (lds > 65536) {           // above the default dynamic LDS limit: raise it once per kernel
         static std::mutex mu;
         static bool raised = false;
@@ -489,7 +618,7 @@ static hipError_t launch_one(const EncodeArgs& a, int num_cus, hipStream_t s) {
         }
     }
     // one wave of blocks: as many blocks as fit on every CU at once
-    const int threads = 64 * (s_lds ? enc_waves<D, QJL, BF16, true>() : enc_waves<D, QJL, BF16, (D <= 128)>());
+    const int threads = 64 * (s_lds ? enc_waves<D, QJL, BF16, true, false>() : enc_waves<D, QJL, BF16, (D <= 128), false>());
     const int64_t target = (int64_t)num_cus * blocks_per_cu(kern, lds, threads);
     int64_t bps = (target + a.n_streams - 1) / a.n_streams;
     if (bps > a.tiles_per_stream) bps = a.tiles_per_stream;
@@ -498,10 +627,10 @@ static hipError_t launch_one(const EncodeArgs& a, int num_cus, hipStream_t s) {
     b.tiles_per_block = (a.tiles_per_stream + bps - 1) / bps;
     const dim3 grid((unsigned)(a.n_streams * bps));
     if constexpr (D <= 128) {
-        hipLaunchKernelGGL((encode_kernel<D, B, QJL, BF16, true>), grid, dim3(threads), lds, s, b);
+        hipLaunchKernelGGL((encode_kernel<D, B, QJL, BF16, true, false>), grid, dim3(threads), lds, s, b);
     } else {
-        if (s_lds) hipLaunchKernelGGL((encode_kernel<D, B, QJL, BF16, true>), grid, dim3(threads), lds, s, b);
-        else hipLaunchKernelGGL((encode_kernel<D, B, QJL, BF16, false>), grid, dim3(threads), lds, s, b);
+        if (s_lds) hipLaunchKernelGGL((encode_kernel<D, B, QJL, BF16, true, false>), grid, dim3(threads), lds, s, b);
+        else hipLaunchKernelGGL((encode_kernel<D, B, QJL, BF16, false, false>), grid, dim3(threads), lds, s, b);
     }
     return hipGetLastError();
 }

@@ -13,6 +13,7 @@ struct DevTables {
     int rotation = 0;                  // TQ_ROTATION_WHT or TQ_ROTATION_NONE (no sign flip, no WHT)
     int G = 0;                         // search grid cells
     const uint32_t* grid = nullptr;    // (G+2) x {thr fp32 bits, base}
+    const uint32_t* fq_grid = nullptr; // binade grid (b <= 4): 128 entries E[c], or null
     const float* cent = nullptr;       // 2^b centroids (fp32)
     const float* cent_x1024 = nullptr; // 2^b centroids x 2^14 (fp32, exact scaling)
     const float* lut_f32 = nullptr;    // dequant LUT: 2^(P b) entries of P fp32 (P = lut_group(b))

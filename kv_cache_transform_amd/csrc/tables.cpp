@@ -249,4 +249,28 @@ bool build_grid(const std::vector<double>& thr_y, Grid& out) {
     return false;
 }
 
+bool build_fq_grid(const std::vector<double>& thr_y, int b, std::vector<uint32_t>& E) {
+    if (b < 1 || b > 4) return false;
+    std::vector<uint32_t> T(thr_y.size());
+    for (size_t k = 0; k < thr_y.size(); ++k) {
+        const float f = (float)(3.0 + kFqKappa * thr_y[k]);
+        std::memcpy(&T[k], &f, 4);
+        if (T[k] < 0x40000000u || T[k] >= 0x40800000u) return false;
+    }
+    E.assign(128, 0u);
+    for (uint32_t c = 0; c < 128; ++c) {
+        const uint32_t lo = 0x40000000u + (c << 16), hi = lo + 0x10000u;
+        uint64_t base = 0;
+        int inside = 0;
+        uint32_t tc = hi;
+        for (uint32_t t : T) {
+            if (t < lo) ++base;
+            else if (t < hi) { ++inside; tc = t; }
+        }
+        if (inside > 1) return false;
+        E[c] = (uint32_t)(((base + 1) << (32 - b)) - (uint64_t)tc);
+    }
+    return true;
+}
+
 }  // namespace tq

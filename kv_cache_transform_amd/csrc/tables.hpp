@@ -37,6 +37,16 @@ struct Grid {
 };
 bool build_grid(const std::vector<double>& thr_y, Grid& out);
 
+// Binade grid for b <= 4: u = 3 + kFqKappa·y lies in [2, 4) for every |y| <= 1, so bits 16..22 of
+// u's fp32 pattern are a cell index c (128 cells of 1/64) and u >= thr compares as the integers.
+// Entry c is E[c] = ((base_c + 1) << (32 - b)) - T_c (mod 2^32), with base_c the thresholds below
+// the cell and T_c the bits of the one threshold inside it (or of the cell's upper end).  Then
+// w = bits(u) + E[c] carries idx = #{k : thr_u[k] <= u} in its top b bits, and bits 16 .. 31 - b
+// are all zero (u >= T_c) or all one (u < T_c), so the top byte of w is idx·2^(8-b) or
+// idx·2^(8-b) + 2^(8-b) - 1.  Returns false if a cell would hold two thresholds.
+constexpr double kFqKappa = 1.0 - 1.0 / 256.0;
+bool build_fq_grid(const std::vector<double>& thr_y, int b, std::vector<uint32_t>& E);
+
 // coordinates per dequantisation lookup for b bits
 inline int lut_group(int b) { return (b == 1 || b == 2 || b == 4) ? 8 / b : ((b == 3 || b == 5 || b == 6) ? 2 : 1); }
 

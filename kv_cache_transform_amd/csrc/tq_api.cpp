@@ -88,6 +88,8 @@ int build_tables(const tq_params* p, int device, DevTables* out) {  // caller ho
     Grid grid;
     if (!build_grid(cb.thr, grid)) return TQ_EUNSUPPORTED;
     const std::vector<uint32_t>& gw = grid.entries;
+    std::vector<uint32_t> fq;
+    const bool fq_ok = build_fq_grid(cb.thr, b, fq);
 
     const int P = lut_group(b), NE = 1 << (P * b);
     std::vector<float> lut32((size_t)NE * P);
@@ -130,6 +132,7 @@ int build_tables(const tq_params* p, int device, DevTables* out) {  // caller ho
 
     Blob blob;
     const int64_t o_grid = blob.add(gw.data(), gw.size() * 4);
+    const int64_t o_fq = fq_ok ? blob.add(fq.data(), fq.size() * 4) : 0;
     const int64_t o_cent = blob.add(cent_f.data(), L * 4);
     const int64_t o_centk = blob.add(cent_k.data(), L * 4);
     const int64_t o_l32 = blob.add(lut32.data(), lut32.size() * 4);
@@ -151,6 +154,7 @@ int build_tables(const tq_params* p, int device, DevTables* out) {  // caller ho
     t.d = d; t.b = b; t.m = m; t.n_heads = H; t.seed = p->seed; t.sketch = rht ? TQ_SKETCH_RHT : TQ_SKETCH_GAUSSIAN; t.rotation = p->rotation;
     t.G = grid.G;
     t.grid = reinterpret_cast<const uint32_t*>(base + o_grid);
+    t.fq_grid = fq_ok ? reinterpret_cast<const uint32_t*>(base + o_fq) : nullptr;
     t.cent = reinterpret_cast<const float*>(base + o_cent);
     t.cent_x1024 = reinterpret_cast<const float*>(base + o_centk);
     t.lut_f32 = reinterpret_cast<const float*>(base + o_l32);
