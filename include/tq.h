@@ -141,7 +141,9 @@ size_t tq_attention_workspace_bytes(const tq_params* pk, int32_t batch, int32_t 
  * with ŝ the score estimate above and x̂^V the decoded values; kv head = h / (n_q_heads/n_kv_heads);
  * stream = b·n_kv_heads + kv head for both packed tensors.  q: [batch][n_q_heads][d] BF16 or F32;
  * out: same shape, BF16 or F32.  pv->m must be 0; pk->d == pv->d; n_heads of both == n_kv_heads;
- * n_q_heads / n_kv_heads <= 16.  Values are accumulated in the rotated domain and rotated back once. */
+ * n_q_heads / n_kv_heads <= 16.  Values are accumulated in the rotated domain and rotated back once.
+ * One stream's packed K index plane (n_tokens·d·b_K/8 bytes) and V index plane must stay below
+ * 2^32 - 2^16 bytes (32-bit buffer offsets within a stream): TQ_EUNSUPPORTED beyond. */
 int tq_decode_attention(const tq_params* pk, const tq_params* pv, const void* q, tq_dtype q_dtype,
                         int32_t batch, int32_t n_q_heads, int32_t n_kv_heads,
                         const void* packed_k, const void* packed_v, int64_t n_tokens,

@@ -17,14 +17,22 @@
 
 namespace tq {
 
+// plain v_max_f32: the operands come out of lane swaps, which the compiler cannot prove quiet, so
+// fmaxf would first canonicalise both (the logits are never signalling NaNs)
+__device__ __forceinline__ float vmax(float a, float b) {
+    float r;
+    asm("v_max_f32 %0, %1, %2" : "=v"(r) : "v"(a), "v"(b));
+    return r;
+}
+
 __device__ __forceinline__ float max4(float t) {
     float a = t, b = t;
     xswap16(a, b);
-    t = fmaxf(a, b);
+    t = vmax(a, b);
     a = t;
     b = t;
     xswap32(a, b);
-    return fmaxf(a, b);
+    return vmax(a, b);
 }
 
 // Everything one 32-token chunk needs, loaded with wide per-lane loads.  Lane (l16, g):
@@ -68,7 +76,8 @@ struct AttnGeom {
     // 32-lane phase use different banks.
     static constexpr bool KV256 = VPAIR && PK == 2 && NEK == 256;
     static constexpr int KV_LO = 65536 - 128;        // lo pair address - hi pair address
-    // threads per block: the 128 KiB of tables are shared by 8 waves where 2 waves per SIMD fit
+    // threads per block: the 128 KiB of tables are shared by the waves of one block per CU (see
+    // attn_threads)
     static constexpr int THREADS = (KV256 && D <= 128) ? 512 : 256;
 };
 
@@ -85,6 +94,46 @@ __device__ __forceinline__ uint32_t row256(uint32_t w, uint32_t off, int which) 
     return __builtin_amdgcn_perm(w, off, 0x0c0c0000u | ((uint32_t)(4 + which) << 8));
 }
 
+// NB bytes at byte offset voff (per lane) + soff (wave-uniform) of buffer r, alignment A (a
+// power of two <= 16): raw buffer loads, so the address is the resource base plus two 32-bit
+// offsets and needs no per-lane 64-bit arithmetic
+template <int NB, int A>
+__device__ __forceinline__ void bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t* w) {
+    if constexpr (A >= 16 && NB >= 16) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+        w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+        if constexpr (NB > 16) bload<NB - 16, 16>(r, voff + 16, soff, w + 4);
+    } else if constexpr (A >= 8 && NB >= 8) {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+        w[0] = v[0]; w[1] = v[1];
+        if constexpr (NB > 8) bload<NB - 8, (A > 8 ? 8 : A)>(r, voff + 8, soff, w + 2);
+    } else if constexpr (A >= 4 && NB >= 4) {
+        w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+        if constexpr (NB > 4) bload<NB - 4, 4>(r, voff + 4, soff, w + 1);
+    } else if constexpr (NB >= 2) {
+        uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+        if constexpr (NB >= 4) lo |= uint32_t(__builtin_amdgcn_raw_buffer_load_b16(r, voff + 2, soff, 0)) << 16;
+        else if constexpr (NB == 3) lo |= uint32_t(__builtin_amdgcn_raw_buffer_load_b8(r, voff + 2, soff, 0)) << 16;
+        w[0] = lo;
+        if constexpr (NB > 4) bload<NB - 4, 2>(r, voff + 4, soff, w + 1);
+    } else if constexpr (NB == 1) {
+        w[0] = __builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
+    }
+}
+
+// a raw buffer over one plane of one stream (no range limit: every full-chunk load is in bounds by
+// construction, and the sketch over-read stays inside the packed buffer as for the global loads)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t plane_rsrc(const uint8_t* base) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, -1, 0x00020000);
+}
+
+// Buffer resources of one stream's planes and the lane's loop-invariant byte offsets within a
+// chunk (full chunks; the chunk's first token enters as the wave-uniform scalar offset)
+struct AttnRes {
+    __amdgpu_buffer_rsrc_t kidx, ksk, kn, kr, vidx, vn;
+    uint32_t o_kw, o_ks, o_n, o_vw;
+};
+
 // Per-wave base pointers of one stream (chunk offsets are added as wave-uniform values).
 struct AttnPtrs {
     const uint8_t* kidx;
@@ -94,6 +143,32 @@ struct AttnPtrs {
     const uint8_t* vidx;
     const uint8_t* vn;
 };
+
+template <int D, int BK, int BV, bool QJL>
+__device__ __forceinline__ void attn_load_full(AttnChunk<AttnGeom<D, BK, BV>::NWK, AttnGeom<D, BK, BV>::NWV, AttnGeom<D, BK, BV>::NKS>& c,
+                                               const AttnRes& R, int64_t t0, int m) {
+    using Gm = AttnGeom<D, BK, BV>;
+    const uint32_t tk = (uint32_t)t0;
+#pragma unroll
+    for (int T = 0; T < 2; ++T) {
+        bload<Gm::CBK, Gm::CAK>(R.kidx, R.o_kw, (tk + 16 * T) * Gm::KROW, c.kw[T]);
+        if constexpr (QJL) {
+            // the covering aligned dwords of the lane's m/32 sketch bytes (see attn_load)
+            const uint32_t so = (tk + 16 * T) * (uint32_t)(m / 8);
+#pragma unroll
+            for (int k = 0; k <= Gm::NKS; ++k) c.ks[T][k] = __builtin_amdgcn_raw_buffer_load_b32(R.ksk, R.o_ks + 4 * k, so, 0);
+        }
+        const uint32_t sn = 2 * tk + 32 * T;
+        c.kn[T] = __builtin_amdgcn_raw_buffer_load_b64(R.kn, R.o_n, sn, 0);
+        if constexpr (QJL) c.kr[T] = __builtin_amdgcn_raw_buffer_load_b64(R.kr, R.o_n, sn, 0);
+        c.vn[T] = __builtin_amdgcn_raw_buffer_load_b64(R.vn, R.o_n, sn, 0);
+    }
+#pragma unroll
+    for (int r = 0; r < 8; ++r) {
+        const int tr = r < 4 ? r : 16 + (r - 4);          // τ(g, r) - 4g
+        bload<Gm::VB, Gm::VA>(R.vidx, R.o_vw, (tk + tr) * Gm::VROW, c.vw[r]);
+    }
+}
 
 template <int D, int BK, int BV, bool QJL, bool FULL>
 __device__ __forceinline__ void attn_load(AttnChunk<AttnGeom<D, BK, BV>::NWK, AttnGeom<D, BK, BV>::NWV, AttnGeom<D, BK, BV>::NKS>& c,
@@ -224,9 +299,10 @@ __device__ __forceinline__ void attn_chunk(const AttnChunk<AttnGeom<D, BK, BV>::
                 }
             }
             if constexpr (PQ) {
-                // columns 0-7: query hi parts, 8-15: their lo parts (qb); qbl: hi parts, then zeros
+                // columns 0-7: query hi parts, 8-15: their lo parts; both key parts multiply both,
+                // so columns 8-15 also carry lo·lo (2^-22 relative: below the fp32 accumulation)
                 s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[k], s1, 0, 0, 0);
-                s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kal, qbl[k], s1, 0, 0, 0);
+                s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kal, qb[k], s1, 0, 0, 0);
             } else {
                 s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(ka, qb[k], s1, 0, 0, 0);
                 s1 = __builtin_amdgcn_mfma_f32_16x16x32_f16(kal, qb[k], s1, 0, 0, 0);
@@ -334,10 +410,16 @@ __device__ __forceinline__ void attn_chunk(const AttnChunk<AttnGeom<D, BK, BV>::
     }
 }
 
+// threads per block: with the shared 4-bit tables at d <= 128, three waves per SIMD when the
+// query operand packs hi and lo parts (group <= 8: 163 VGPRs), else two
+template <int D, int BK, int BV, bool PQ>
+constexpr int attn_threads() { return AttnGeom<D, BK, BV>::THREADS == 512 && PQ ? 768 : AttnGeom<D, BK, BV>::THREADS; }
+
 // PQ: at most 8 query heads per kv head, so the query operand carries hi parts in columns 0-7
 // and lo parts in columns 8-15, and the scores take two products per step instead of three
 template <int D, int BK, int BV, bool QJL, bool PQ>
-__global__ __launch_bounds__((AttnGeom<D, BK, BV>::THREADS), (D <= 128 ? 2 : 1)) void attn_kernel(AttnArgs a) {
+__global__ __launch_bounds__((attn_threads<D, BK, BV, PQ>()), (attn_threads<D, BK, BV, PQ>() == 768 ? 3 : (D <= 128 ? 2 : 1)))
+void attn_kernel(AttnArgs a) {
     using Gm = AttnGeom<D, BK, BV>;
     constexpr int C = Gm::C, KS = Gm::KS, PK = Gm::PK, NEK = Gm::NEK, NT = Gm::NT;
     constexpr int LV = 1 << BV;
@@ -418,7 +500,7 @@ __global__ __launch_bounds__((AttnGeom<D, BK, BV>::THREADS), (D <= 128 ? 2 : 1))
     const int mks = m >> 5;
 
     // query operands (B of the score products): lane column q = l16, k-block g (with PQ, column
-    // q + 8 carries query q's lo parts in qb and zeros in qbl)
+    // q + 8 carries query q's lo parts in qb, and qbl is not used)
     const bool qvalid = l16 < a.group;
     const int qcol = PQ ? (l16 & 7) : l16;
     const bool qload = qcol < a.group;
@@ -431,7 +513,6 @@ __global__ __launch_bounds__((AttnGeom<D, BK, BV>::THREADS), (D <= 128 ? 2 : 1))
         const half8 ql = *reinterpret_cast<const half8*>(a.o.ql + qrow * D + g * C + 8 * k);
         if constexpr (PQ) {
             qb[k] = !qload ? half8{} : (l16 < 8 ? qh : ql);
-            qbl[k] = (!qload || l16 >= 8) ? half8{} : qh;
         } else {
             qb[k] = qvalid ? qh : half8{};
             qbl[k] = qvalid ? ql : half8{};
@@ -456,6 +537,17 @@ __global__ __launch_bounds__((AttnGeom<D, BK, BV>::THREADS), (D <= 128 ? 2 : 1))
     P.kr = a.pk + a.k_off_rnorm + st * a.n_tokens * 2;
     P.vidx = a.pv + a.v_off_idx + st * a.n_tokens * (int64_t)Gm::VROW;
     P.vn = a.pv + a.v_off_norm + st * a.n_tokens * 2;
+    AttnRes R;
+    R.kidx = plane_rsrc(P.kidx);
+    R.ksk = plane_rsrc(P.ksk);
+    R.kn = plane_rsrc(P.kn);
+    R.kr = plane_rsrc(P.kr);
+    R.vidx = plane_rsrc(P.vidx);
+    R.vn = plane_rsrc(P.vn);
+    R.o_kw = (uint32_t)l16 * Gm::KROW + (uint32_t)g * Gm::CBK;
+    R.o_ks = (uint32_t)l16 * (uint32_t)(m / 8) + (uint32_t)((g * (m / 32)) & ~3);
+    R.o_n = 8u * (uint32_t)g;
+    R.o_vw = (uint32_t)(4 * g) * Gm::VROW + (uint32_t)l16 * Gm::VB;
 
     // full 32-token chunks through two ping-pong buffers (next chunk's loads overlap this one's
     // math), then at most one guarded partial chunk.  Every load in the loop is unconditional (the
@@ -465,18 +557,18 @@ __global__ __launch_bounds__((AttnGeom<D, BK, BV>::THREADS), (D <= 128 ? 2 : 1))
     const int64_t n_full = t_end > t_begin ? (t_end - t_begin) >> 5 : 0;
     int64_t c = 0;
     if (n_full > 0) {
-        attn_load<D, BK, BV, QJL, true>(A, P, t_begin, t_end, l16, g, m);
+        attn_load_full<D, BK, BV, QJL>(A, R, t_begin, m);
 #pragma unroll 1
         for (; c + 2 <= n_full; c += 2) {
             // (scheduling barriers keep each buffer's loads together, ahead of the other buffer's
             // math, so the wait before a chunk leaves the other buffer's loads in flight)
-            attn_load<D, BK, BV, QJL, true>(B, P, t_begin + (c + 1) * 32, t_end, l16, g, m);
+            attn_load_full<D, BK, BV, QJL>(B, R, t_begin + (c + 1) * 32, m);
             __builtin_amdgcn_sched_barrier(0);
             attn_chunk<D, BK, BV, QJL, true, PQ>(A, S, t_begin + c * 32, t_end, g, mks, qb, qbl, pb, rowf, kl,
                                              vlut, vl2, sgn4, kvl, koff, voff, ksh);
             __builtin_amdgcn_sched_barrier(0);
             const int64_t cn = c + 2 < n_full ? c + 2 : n_full - 1;
-            attn_load<D, BK, BV, QJL, true>(A, P, t_begin + cn * 32, t_end, l16, g, m);
+            attn_load_full<D, BK, BV, QJL>(A, R, t_begin + cn * 32, m);
             __builtin_amdgcn_sched_barrier(0);
             attn_chunk<D, BK, BV, QJL, true, PQ>(B, S, t_begin + (c + 1) * 32, t_end, g, mks, qb, qbl, pb, rowf, kl,
                                              vlut, vl2, sgn4, kvl, koff, voff, ksh);
@@ -580,11 +672,16 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 
 template <int D, int BK, int BV, bool QJL>
 static hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
-    constexpr int threads = AttnGeom<D, BK, BV>::THREADS, waves = threads / 64;
     const int64_t items = (int64_t)a.batch * a.n_kv_heads * a.n_split;
-    const int64_t blocks = (items + waves - 1) / waves;
-    if (a.group <= 8) hipLaunchKernelGGL((attn_kernel<D, BK, BV, QJL, true>), dim3((unsigned)blocks), dim3(threads), 0, s, a);
-    else hipLaunchKernelGGL((attn_kernel<D, BK, BV, QJL, false>), dim3((unsigned)blocks), dim3(threads), 0, s, a);
+    if (a.group <= 8) {
+        constexpr int threads = attn_threads<D, BK, BV, true>(), waves = threads / 64;
+        const int64_t blocks = (items + waves - 1) / waves;
+        hipLaunchKernelGGL((attn_kernel<D, BK, BV, QJL, true>), dim3((unsigned)blocks), dim3(threads), 0, s, a);
+    } else {
+        constexpr int threads = attn_threads<D, BK, BV, false>(), waves = threads / 64;
+        const int64_t blocks = (items + waves - 1) / waves;
+        hipLaunchKernelGGL((attn_kernel<D, BK, BV, QJL, false>), dim3((unsigned)blocks), dim3(threads), 0, s, a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)((int64_t)a.batch * a.n_q_heads)), dim3(256), 0, s, a);

@@ -225,8 +225,10 @@ int hip_status(hipError_t e) { return e == hipSuccess ? TQ_OK : TQ_EHIP; }
 // so every wave streams one long token range; at least 256 tokens per split, token ranges a
 // multiple of 32, at most 1024 splits
 constexpr int kAttnCUs = 256;
-int64_t attn_tokens_per_split(int d, int64_t n_streams, int64_t n_tokens) {
-    const int64_t target = (int64_t)kAttnCUs * (d <= 128 ? 8 : 4);
+// waves per CU of the attention kernel: 12 for 4-bit keys and values at d <= 128 with at most 8
+// query heads per kv head (three per SIMD), 8 otherwise at d <= 128, 4 at d = 256
+int64_t attn_tokens_per_split(int d, int b, int group, int64_t n_streams, int64_t n_tokens) {
+    const int64_t target = (int64_t)kAttnCUs * (d <= 128 ? (b == 4 && group <= 8 ? 12 : 8) : 4);
     int64_t ns = (target + n_streams - 1) / (n_streams > 0 ? n_streams : 1);
     const int64_t max_ns = (n_tokens + 255) / 256;
     if (ns > max_ns) ns = max_ns;
@@ -271,7 +273,7 @@ struct AttnWs {
 AttnWs attn_ws(const tq_params* pk, int32_t batch, int32_t hq, int32_t hkv, int64_t n_tokens) {
     AttnWs w{};
     const int64_t rows = (int64_t)batch * hq + 16;
-    const int64_t tps = attn_tokens_per_split(pk->d, (int64_t)batch * hkv, n_tokens);
+    const int64_t tps = attn_tokens_per_split(pk->d, pk->b, hkv > 0 ? hq / hkv : 1, (int64_t)batch * hkv, n_tokens);
     w.n_split = (n_tokens + tps - 1) / tps;
     if (w.n_split < 1) w.n_split = 1;
     const int64_t streams = (int64_t)batch * hkv;
@@ -548,6 +550,9 @@ int attention_impl(const tq_params* pk, const tq_params* pv, const void* q, tq_d
     const AttnWs w = attn_ws(pk, batch, n_q_heads, n_kv_heads, n_tokens);
     if (workspace_bytes < (size_t)w.total) return TQ_EWORKSPACE;
     if (!attention_supported(pk->d, pk->b, pv->b)) return TQ_EUNSUPPORTED;
+    // the kernel addresses a stream's planes with 32-bit offsets (the index planes are the largest)
+    const int64_t max_row = std::max<int64_t>(pk->d * pk->b / 8, pv->d * pv->b / 8);
+    if (n_tokens > (int64_t)((1ull << 32) - (1ull << 16)) / max_row) return TQ_EUNSUPPORTED;
     DevTables tk, tv;
     int cus = 0;
     if ((rc = (no_alloc ? find_tables : get_tables)(pk, &tk, &cus)) != TQ_OK) return rc;
@@ -587,7 +592,7 @@ int attention_impl(const tq_params* pk, const tq_params* pv, const void* q, tq_d
     a.n_kv_heads = n_kv_heads;
     a.group = n_q_heads / n_kv_heads;
     a.n_split = (int)w.n_split;
-    a.tokens_per_split = attn_tokens_per_split(pk->d, streams, n_tokens);
+    a.tokens_per_split = attn_tokens_per_split(pk->d, pk->b, a.group, streams, n_tokens);
     a.scale_log2 = scale_log2;
     a.k_off_idx = lk.off_idx;
     a.k_off_sketch = lk.off_sketch;
