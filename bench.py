@@ -35,17 +35,17 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published (the sketch p
 # the kernel's sources are the ones it was measured on (sha256 of the .hip file + shared headers).
 FETCH_UNIT_B, WRITE_UNIT_B = 2048, 1024
 TRAFFIC = {
-    "encode_k": {"fetch": 2098047.4375, "write": 1394455.96875, "src": "encode.hip",
-        "sha": "f5c0fbd7bd1cc3c39b7b4ce796eebf8e47614b993815acc41d6e99a7db5f2283"},
-    "encode_v": {"fetch": 2101601.125, "write": 1091294.4375, "src": "encode.hip",
-        "sha": "f5c0fbd7bd1cc3c39b7b4ce796eebf8e47614b993815acc41d6e99a7db5f2283"},
-    "decode_attention": {"fetch": 1229524.875, "write": 4160.0, "src": "attention.hip",
-        "sha": "4be06b54bfca6982975224479351383ef5ca8ff0715ceec477526c67f395d14a"},
-    "decode_v_bf16": {"fetch": 550860.1875, "write": 4194304.0, "src": "decode.hip",
+    "encode_k": {"fetch": 2097508.4375, "write": 1395709.53125, "src": "encode.hip",
+        "sha": "c8bce0856321870e653ece12d0487ff04b18cdb834acf5a58d0f48dd1515356e"},
+    "encode_v": {"fetch": 2106716.1875, "write": 1090965.15625, "src": "encode.hip",
+        "sha": "c8bce0856321870e653ece12d0487ff04b18cdb834acf5a58d0f48dd1515356e"},
+    "decode_attention": {"fetch": 1232497.125, "write": 6240.0, "src": "attention.hip",
+        "sha": "fa2491b956b2574f05a6a3b654250fd33a463818bb1d026e34335c161bd49920"},
+    "decode_v_bf16": {"fetch": 550325.8125, "write": 4194304.0, "src": "decode.hip",
         "sha": "2add9ea1fa8cf5d1d37b9846a4505b28cdfa3553557c2e41c88d2f2cc96455e9"},
 }
-TRAFFIC_HEADERS_SHA = ("ab1b24f667c0da7a2104e5378715b7e9fefd5b2b0310679390021387480c9abe"   # common.hpp
-                       "68dbed2b9697855851fc18a47835498cefdd60b20f7e0c05282a0b59228d584f")  # kernels.hpp
+TRAFFIC_HEADERS_SHA = ("171296081e898f9aa4b751e3e213ec369098f8cce83d03dc938fb9e239591c0c"   # common.hpp
+                       "c79a58581fb18e7686561d680e8fdc2107a0b0d7c4661d9115f2dda2656965da")  # kernels.hpp
 
 
 def _sha(path: str) -> str:
@@ -687,8 +687,13 @@ def cpu_baseline(parity_sample: dict, min_s=0.3):
         one = {name: _oracle_ops(name, 11, min_s) for name in CPU_CONFIGS}
     torch.set_num_threads(torch_threads)
     ctx = mp.get_context("spawn")
-    with ctx.Pool(workers) as pool:
+    pool = ctx.Pool(workers)
+    try:
         runs = pool.map(_cpu_worker, [(101 + w, min_s) for w in range(workers)])
+    finally:
+        # close and wait, so that no worker outlives the benchmark
+        pool.close()
+        pool.join()
 
     def rate(sec, nbytes, k=1):
         return round(k * nbytes / sec / 1e9, 5)
