@@ -249,7 +249,7 @@ __device__ __forceinline__ void attn_chunk(const AttnChunk<AttnGeom<D, BK, BV>::
                                            const half8 (&qb)[AttnGeom<D, BK, BV>::KS],
                                            const half8 (&qbl)[AttnGeom<D, BK, BV>::KS], const half8* pb, float rowf,
                                            const uint8_t* kl, const _Float16* vlut, const uint8_t* vl2,
-                                           const u32x2* sgn4, const uint8_t* kvl, uint32_t koff, uint32_t voff,
+                                           const uint8_t* sg8, const uint8_t* kvl, uint32_t koff, uint32_t voff,
                                            uint32_t ksh) {
     using Gm = AttnGeom<D, BK, BV>;
     constexpr int KS = Gm::KS, PK = Gm::PK, NT = Gm::NT;
@@ -321,9 +321,9 @@ __device__ __forceinline__ void attn_chunk(const AttnChunk<AttnGeom<D, BK, BV>::
             for (int k = 0; k < KS; ++k) {
                 // branch-free: steps past the sketch (k >= m/32) multiply a zero query operand
                 const uint32_t wsk = __builtin_amdgcn_alignbit(cur.ks[T][(k >> 2) + 1], cur.ks[T][k >> 2], ksh);
-                const u32x2 lo = sgn4[(wsk >> (8 * (k & 3))) & 0xfu];
-                const u32x2 hi = sgn4[(wsk >> (8 * (k & 3) + 4)) & 0xfu];
-                const half8 sa = __builtin_bit_cast(half8, u32x4{lo[0], lo[1], hi[0], hi[1]});
+                // the ±2^12 operand of the step's 8 sketch bits: one 16-byte entry per byte value
+                const uint32_t sb = __builtin_amdgcn_ubfe(wsk, 8 * (k & 3), 8);
+                const half8 sa = *reinterpret_cast<const half8*>(sg8 + sb * 64u);
                 s2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(sa, pb[k], s2, 0, 0, 0);
             }
         }
@@ -380,8 +380,9 @@ __device__ __forceinline__ void attn_chunk(const AttnChunk<AttnGeom<D, BK, BV>::
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
                 const uint32_t w0 = cur.vw[2 * p][j], w1 = cur.vw[2 * p + 1][j];
-                ze[p] = (w0 & 0x0f0f0f0fu) | ((w1 << 4) & 0xf0f0f0f0u);
-                zo[p] = ((w0 >> 4) & 0x0f0f0f0fu) | (w1 & 0xf0f0f0f0u);
+                // one shift and one bit-field insert each (v_bfi_b32)
+                ze[p] = ((w0 & 0x0f0f0f0fu) | ((w1 << 4) & ~0x0f0f0f0fu));
+                zo[p] = ((w0 >> 4) & 0x0f0f0f0fu) | (w1 & ~0x0f0f0f0fu);
             }
 #pragma unroll
             for (int q = 0; q < 8 && 8 * j + q < NT; ++q) {
@@ -430,7 +431,7 @@ void attn_kernel(AttnArgs a) {
     __shared__ _Float16 vlut[LV];
     __shared__ uint32_t vlut2[Gm::VPAIR && !KV ? 256 * VR : 1];  // copy c of entry e at word e VR + c
     __shared__ uint32_t kvlut[KV ? 2 * 256 * 64 : 1];             // the two tables of 256-byte rows
-    __shared__ u32x2 sgn4[16];                                     // ±2^12 halves of the 4 bits of a nibble
+    __shared__ u32x4 sgn8[QJL ? 256 * 4 : 1];                      // copy c of byte e's ±2^12 halves at e·4 + c
     if constexpr (KV) {
         const uint32_t* src = reinterpret_cast<const uint32_t*>(a.tk.lut_hl);   // entry e: hi pair, lo pair
         for (int i = threadIdx.x; i < 2 * 256 * 64; i += blockDim.x) {
@@ -462,14 +463,18 @@ void attn_kernel(AttnArgs a) {
             const half2v hv = {(_Float16)a.tv.cent[e & 15], (_Float16)a.tv.cent[e >> 4]};
             vlut2[i] = __builtin_bit_cast(uint32_t, hv);
         }
-    if (threadIdx.x < 16) {
-        uint32_t w[2];
+    // the sketch operand: entry e holds +2^12 (fp16 0x6c00) for each set bit i of e and -2^12 for
+    // each clear one, in bit order; 4 copies (lane l reads copy l % 4) spread the random lookups of
+    // a wave over the banks
+    if constexpr (QJL)
+        for (int i = threadIdx.x; i < 256 * 4; i += blockDim.x) {
+            const uint32_t e = (uint32_t)i >> 2;
+            u32x4 w;
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
-            w[j] = (((threadIdx.x >> (2 * j)) & 1) ? 0x6c00u : 0xec00u) |
-                   ((((threadIdx.x >> (2 * j + 1)) & 1) ? 0x6c00u : 0xec00u) << 16);
-        sgn4[threadIdx.x] = u32x2{w[0], w[1]};
-    }
+            for (int j = 0; j < 4; ++j)
+                w[j] = (((e >> (2 * j)) & 1u) ? 0x6c00u : 0xec00u) | ((((e >> (2 * j + 1)) & 1u) ? 0x6c00u : 0xec00u) << 16);
+            sgn8[i] = w;
+        }
     __syncthreads();
 
     const int lane = threadIdx.x & 63;
@@ -477,6 +482,7 @@ void attn_kernel(AttnArgs a) {
     const uint8_t* kl = reinterpret_cast<const uint8_t*>(klut) + (lane % KR) * KE;      // the lane's copies
     const uint8_t* vl2 = reinterpret_cast<const uint8_t*>(vlut2) + (lane % VR) * 4;
     const uint8_t* kvl = reinterpret_cast<const uint8_t*>(kvlut);
+    const uint8_t* sg8 = reinterpret_cast<const uint8_t*>(sgn8) + (lane & 3) * 16;   // the lane's copies
     const uint32_t koff = 128u + (uint32_t)(lane & 31) * 4u, voff = (uint32_t)(lane & 31) * 4u;
     const uint32_t ksh = (uint32_t)((g * (a.tk.m >> 5)) & 3) * 8u;   // bit offset of the lane's sketch bytes
     const int64_t item = (int64_t)blockIdx.x * (blockDim.x >> 6) + wave_id();
@@ -565,25 +571,25 @@ void attn_kernel(AttnArgs a) {
             attn_load_full<D, BK, BV, QJL>(B, R, t_begin + (c + 1) * 32, m);
             __builtin_amdgcn_sched_barrier(0);
             attn_chunk<D, BK, BV, QJL, true, PQ>(A, S, t_begin + c * 32, t_end, g, mks, qb, qbl, pb, rowf, kl,
-                                             vlut, vl2, sgn4, kvl, koff, voff, ksh);
+                                             vlut, vl2, sg8, kvl, koff, voff, ksh);
             __builtin_amdgcn_sched_barrier(0);
             const int64_t cn = c + 2 < n_full ? c + 2 : n_full - 1;
             attn_load_full<D, BK, BV, QJL>(A, R, t_begin + cn * 32, m);
             __builtin_amdgcn_sched_barrier(0);
             attn_chunk<D, BK, BV, QJL, true, PQ>(B, S, t_begin + (c + 1) * 32, t_end, g, mks, qb, qbl, pb, rowf, kl,
-                                             vlut, vl2, sgn4, kvl, koff, voff, ksh);
+                                             vlut, vl2, sg8, kvl, koff, voff, ksh);
             __builtin_amdgcn_sched_barrier(0);
         }
         if (c < n_full) {          // odd count: A holds chunk c
             attn_chunk<D, BK, BV, QJL, true, PQ>(A, S, t_begin + c * 32, t_end, g, mks, qb, qbl, pb, rowf, kl,
-                                             vlut, vl2, sgn4, kvl, koff, voff, ksh);
+                                             vlut, vl2, sg8, kvl, koff, voff, ksh);
             ++c;
         }
     }
     if (t_begin + c * 32 < t_end) {
         attn_load<D, BK, BV, QJL, false>(A, P, t_begin + c * 32, t_end, l16, g, m);
         attn_chunk<D, BK, BV, QJL, false, PQ>(A, S, t_begin + c * 32, t_end, g, mks, qb, qbl, pb, rowf, kl,
-                                          vlut, vl2, sgn4, kvl, koff, voff, ksh);
+                                          vlut, vl2, sg8, kvl, koff, voff, ksh);
     }
     // ---- partial results: lane (q = l16, g) holds O[coord NT*(4g+i) + n][q] --------------------
     const float l_tot = sum4(S.l_run);
