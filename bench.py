@@ -35,13 +35,13 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published (the sketch p
 # the kernel's sources are the ones it was measured on (sha256 of the .hip file + shared headers).
 FETCH_UNIT_B, WRITE_UNIT_B = 2048, 1024
 TRAFFIC = {
-    "encode_k": {"fetch": 2097508.4375, "write": 1395709.53125, "src": "encode.hip",
-        "sha": "c8bce0856321870e653ece12d0487ff04b18cdb834acf5a58d0f48dd1515356e"},
-    "encode_v": {"fetch": 2106716.1875, "write": 1090965.15625, "src": "encode.hip",
-        "sha": "c8bce0856321870e653ece12d0487ff04b18cdb834acf5a58d0f48dd1515356e"},
-    "decode_attention": {"fetch": 1232497.125, "write": 6240.0, "src": "attention.hip",
-        "sha": "fa2491b956b2574f05a6a3b654250fd33a463818bb1d026e34335c161bd49920"},
-    "decode_v_bf16": {"fetch": 550325.8125, "write": 4194304.0, "src": "decode.hip",
+    "encode_k": {"fetch": 2097500.625, "write": 1394851.5625, "src": "encode.hip",
+        "sha": "333c5c29daa934b587d685de2722eb2d4e1ea18dcf570b97354214954361c873"},
+    "encode_v": {"fetch": 2105256.9375, "write": 1090695.4375, "src": "encode.hip",
+        "sha": "333c5c29daa934b587d685de2722eb2d4e1ea18dcf570b97354214954361c873"},
+    "decode_attention": {"fetch": 1231930.25, "write": 6240.0, "src": "attention.hip",
+        "sha": "3ef759675fd902b137993d34c823d75eb2036ed2688f7d2beb7aab1c5f47fc55"},
+    "decode_v_bf16": {"fetch": 550256.75, "write": 4194304.0, "src": "decode.hip",
         "sha": "2add9ea1fa8cf5d1d37b9846a4505b28cdfa3553557c2e41c88d2f2cc96455e9"},
 }
 TRAFFIC_HEADERS_SHA = ("171296081e898f9aa4b751e3e213ec369098f8cce83d03dc938fb9e239591c0c"   # common.hpp
