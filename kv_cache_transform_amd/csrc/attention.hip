@@ -94,39 +94,6 @@ __device__ __forceinline__ uint32_t row256(uint32_t w, uint32_t off, int which) 
     return __builtin_amdgcn_perm(w, off, 0x0c0c0000u | ((uint32_t)(4 + which) << 8));
 }
 
-// NB bytes at byte offset voff (per lane) + soff (wave-uniform) of buffer r, alignment A (a
-// power of two <= 16): raw buffer loads, so the address is the resource base plus two 32-bit
-// offsets and needs no per-lane 64-bit arithmetic
-template <int NB, int A>
-__device__ __forceinline__ void bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t* w) {
-    if constexpr (A >= 16 && NB >= 16) {
-        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
-        w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
-        if constexpr (NB > 16) bload<NB - 16, 16>(r, voff + 16, soff, w + 4);
-    } else if constexpr (A >= 8 && NB >= 8) {
-        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
-        w[0] = v[0]; w[1] = v[1];
-        if constexpr (NB > 8) bload<NB - 8, (A > 8 ? 8 : A)>(r, voff + 8, soff, w + 2);
-    } else if constexpr (A >= 4 && NB >= 4) {
-        w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
-        if constexpr (NB > 4) bload<NB - 4, 4>(r, voff + 4, soff, w + 1);
-    } else if constexpr (NB >= 2) {
-        uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
-        if constexpr (NB >= 4) lo |= uint32_t(__builtin_amdgcn_raw_buffer_load_b16(r, voff + 2, soff, 0)) << 16;
-        else if constexpr (NB == 3) lo |= uint32_t(__builtin_amdgcn_raw_buffer_load_b8(r, voff + 2, soff, 0)) << 16;
-        w[0] = lo;
-        if constexpr (NB > 4) bload<NB - 4, 2>(r, voff + 4, soff, w + 1);
-    } else if constexpr (NB == 1) {
-        w[0] = __builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
-    }
-}
-
-// a raw buffer over one plane of one stream (no range limit: every full-chunk load is in bounds by
-// construction, and the sketch over-read stays inside the packed buffer as for the global loads)
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t plane_rsrc(const uint8_t* base) {
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base), (short)0, -1, 0x00020000);
-}
-
 // Buffer resources of one stream's planes and the lane's loop-invariant byte offsets within a
 // chunk (full chunks; the chunk's first token enters as the wave-uniform scalar offset)
 struct AttnRes {
@@ -544,12 +511,12 @@ void attn_kernel(AttnArgs a) {
     P.vidx = a.pv + a.v_off_idx + st * a.n_tokens * (int64_t)Gm::VROW;
     P.vn = a.pv + a.v_off_norm + st * a.n_tokens * 2;
     AttnRes R;
-    R.kidx = plane_rsrc(P.kidx);
-    R.ksk = plane_rsrc(P.ksk);
-    R.kn = plane_rsrc(P.kn);
-    R.kr = plane_rsrc(P.kr);
-    R.vidx = plane_rsrc(P.vidx);
-    R.vn = plane_rsrc(P.vn);
+    R.kidx = buffer_rsrc(P.kidx);
+    R.ksk = buffer_rsrc(P.ksk);
+    R.kn = buffer_rsrc(P.kn);
+    R.kr = buffer_rsrc(P.kr);
+    R.vidx = buffer_rsrc(P.vidx);
+    R.vn = buffer_rsrc(P.vn);
     R.o_kw = (uint32_t)l16 * Gm::KROW + (uint32_t)g * Gm::CBK;
     R.o_ks = (uint32_t)l16 * (uint32_t)(m / 8) + (uint32_t)((g * (m / 32)) & ~3);
     R.o_n = 8u * (uint32_t)g;

@@ -215,6 +215,63 @@ __device__ __forceinline__ void load_bytes(const uint8_t* p, uint32_t* w) {
     }
 }
 
+// ---- raw buffer access: a resource over one byte range, 32-bit per-lane and wave-uniform offsets --
+// A raw buffer (stride 0) over [base, base + bytes): the address is the base plus the offsets, with no
+// per-lane 64-bit arithmetic, and an access whose per-lane offset reaches `bytes` reads 0 or is not
+// written.  bytes = 0xffffffff (as int, -1) leaves the range unchecked.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, int bytes = -1) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, bytes, 0x00020000);
+}
+
+// NB bytes at byte offset voff (per lane) + soff (wave-uniform) of buffer r, alignment A (a
+// power of two <= 16): raw buffer loads, so the address is the resource base plus two 32-bit
+// offsets and needs no per-lane 64-bit arithmetic
+template <int NB, int A>
+__device__ __forceinline__ void bload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, uint32_t* w) {
+    if constexpr (A >= 16 && NB >= 16) {
+        const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff, soff, 0);
+        w[0] = v[0]; w[1] = v[1]; w[2] = v[2]; w[3] = v[3];
+        if constexpr (NB > 16) bload<NB - 16, 16>(r, voff + 16, soff, w + 4);
+    } else if constexpr (A >= 8 && NB >= 8) {
+        const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+        w[0] = v[0]; w[1] = v[1];
+        if constexpr (NB > 8) bload<NB - 8, (A > 8 ? 8 : A)>(r, voff + 8, soff, w + 2);
+    } else if constexpr (A >= 4 && NB >= 4) {
+        w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+        if constexpr (NB > 4) bload<NB - 4, 4>(r, voff + 4, soff, w + 1);
+    } else if constexpr (NB >= 2) {
+        uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(r, voff, soff, 0);
+        if constexpr (NB >= 4) lo |= uint32_t(__builtin_amdgcn_raw_buffer_load_b16(r, voff + 2, soff, 0)) << 16;
+        else if constexpr (NB == 3) lo |= uint32_t(__builtin_amdgcn_raw_buffer_load_b8(r, voff + 2, soff, 0)) << 16;
+        w[0] = lo;
+        if constexpr (NB > 4) bload<NB - 4, 2>(r, voff + 4, soff, w + 1);
+    } else if constexpr (NB == 1) {
+        w[0] = __builtin_amdgcn_raw_buffer_load_b8(r, voff, soff, 0);
+    }
+}
+
+// NB bytes from w to byte offset voff (per lane) + soff (wave-uniform) of buffer r, alignment A
+template <int NB, int A>
+__device__ __forceinline__ void bstore(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, const uint32_t* w) {
+    if constexpr (A >= 16 && NB >= 16) {
+        __builtin_amdgcn_raw_buffer_store_b128(u32x4{w[0], w[1], w[2], w[3]}, r, voff, soff, 0);
+        if constexpr (NB > 16) bstore<NB - 16, 16>(r, voff + 16, soff, w + 4);
+    } else if constexpr (A >= 8 && NB >= 8) {
+        __builtin_amdgcn_raw_buffer_store_b64(u32x2{w[0], w[1]}, r, voff, soff, 0);
+        if constexpr (NB > 8) bstore<NB - 8, (A > 8 ? 8 : A)>(r, voff + 8, soff, w + 2);
+    } else if constexpr (A >= 4 && NB >= 4) {
+        __builtin_amdgcn_raw_buffer_store_b32(w[0], r, voff, soff, 0);
+        if constexpr (NB > 4) bstore<NB - 4, 4>(r, voff + 4, soff, w + 1);
+    } else if constexpr (NB >= 2) {
+        __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(w[0] & 0xffffu), r, voff, soff, 0);
+        if constexpr (NB >= 4) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)(w[0] >> 16), r, voff + 2, soff, 0);
+        else if constexpr (NB == 3) __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(w[0] >> 16), r, voff + 2, soff, 0);
+        if constexpr (NB > 4) bstore<NB - 4, 2>(r, voff + 4, soff, w + 1);
+    } else if constexpr (NB == 1) {
+        __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(w[0] & 0xffu), r, voff, soff, 0);
+    }
+}
+
 constexpr int pow2_align(int x) { return (x % 16 == 0) ? 16 : (x % 8 == 0) ? 8 : (x % 4 == 0) ? 4 : (x % 2 == 0) ? 2 : 1; }
 constexpr int cmin(int a, int b) { return a < b ? a : b; }
 constexpr int ilog2(int x) { return x <= 1 ? 0 : 1 + ilog2(x / 2); }

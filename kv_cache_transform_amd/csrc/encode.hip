@@ -208,11 +208,29 @@ void encode_kernel(EncodeArgs a) {
     const int row_base = (rho >> 2) * (m >> 2) + (rho & 3);
     const uint32_t goff = (uint32_t)(lane & ((1 << rl) - 1)) << 3;   // byte offset of the lane's grid copy
     const uint32_t lane4 = 4u * (uint32_t)lane;                        // the lane's copy in a binade-grid row
+    // binade-grid path: raw buffers over this stream's input and its tokens' record planes, each
+    // exactly as long as the stream's part (the launcher keeps them below 2^31 bytes), so a lane
+    // past the last token reads zeros and its stores are dropped as well as skipped
+    __amdgpu_buffer_rsrc_t rx = buffer_rsrc(a.x, 0), rid = rx, rnm = rx, rsk = rx, rrn = rx;
+    if constexpr (FQ) {
+        const int64_t rec0 = st * a.cap + a.t0;
+        rx = buffer_rsrc(reinterpret_cast<const uint8_t*>(a.x) + st * a.n_tokens * (int64_t)(2 * D), (int)(a.n_tokens * 2 * D));
+        rid = buffer_rsrc(a.packed + a.off_idx + rec0 * (int64_t)(D * B / 8), (int)(a.n_tokens * (D * B / 8)));
+        rnm = buffer_rsrc(a.packed + a.off_norm + rec0 * 2, (int)(a.n_tokens * 2));
+        if constexpr (QJL) {
+            rsk = buffer_rsrc(a.packed + a.off_sketch + rec0 * (int64_t)(m / 8), (int)(a.n_tokens * (m / 8)));
+            rrn = buffer_rsrc(a.packed + a.off_rnorm + rec0 * 2, (int)(a.n_tokens * 2));
+        }
+    }
 
     // raw input words of one 16-vector group: bf16 = the lane's C contiguous coordinates; fp32 =
     // runs of R coordinates in the i(s, g) order of the butterfly network (see common.hpp)
     constexpr int NIW = BF16 ? C / 2 : C;
     auto load_group = [&](uint32_t (&w)[NIW], int64_t tile) {
+        if constexpr (FQ) {
+            bload<2 * C, 16>(rx, (uint32_t)(tile * 16 + v) * (2 * D) + 2 * g * C, 0u, w);
+            return;
+        }
         const int64_t tok = tile * 16 + v;
         const bool valid = tile < tb1 && tok < a.n_tokens;
         const int64_t vec = st * a.n_tokens + (valid ? tok : 0);
@@ -255,6 +273,7 @@ void encode_kernel(EncodeArgs a) {
         float e2v[NG];
         bool validv[NG];
         int64_t vecv[NG];
+        uint32_t tokv[NG];
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi) {
             const int64_t tok = (t + gi) * 16 + v;
@@ -263,6 +282,7 @@ void encode_kernel(EncodeArgs a) {
             const int64_t vec = st * a.cap + a.t0 + (valid ? tok : 0);
             validv[gi] = valid;
             vecv[gi] = vec;
+            tokv[gi] = (uint32_t)tok;
 
             // ---- sign, first butterfly stage, norm ----------------------------------------------
             float x[C];
@@ -369,8 +389,14 @@ void encode_kernel(EncodeArgs a) {
                 }
             }
             if (valid) {
-                store_bytes<CB, CA>(a.packed + a.off_idx + vec * (int64_t)(D * B / 8) + g * CB, pk);
-                if (g == 0) *reinterpret_cast<_Float16*>(a.packed + a.off_norm + vec * 2) = (_Float16)n;
+                if constexpr (FQ) {
+                    const uint32_t tk = (uint32_t)tok;
+                    bstore<CB, CA>(rid, tk * (D * B / 8) + g * CB, 0u, pk);
+                    if (g == 0) __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)n), rnm, tk * 2u, 0u, 0);
+                } else {
+                    store_bytes<CB, CA>(a.packed + a.off_idx + vec * (int64_t)(D * B / 8) + g * CB, pk);
+                    if (g == 0) *reinterpret_cast<_Float16*>(a.packed + a.off_norm + vec * 2) = (_Float16)n;
+                }
             }
             if constexpr (QJL) {
                 e2v[gi] = e2;
@@ -424,17 +450,25 @@ void encode_kernel(EncodeArgs a) {
                         for (int p = 8 * j + 7; p >= 8 * j; --p) by[j] = __builtin_amdgcn_alignbit(by[j], f2u(z[32 * w + p]), 31);
                     const uint32_t bw = ~((((by[3] << 8) | by[2]) << 16) | ((by[1] << 8) | by[0]));
                     if (validv[gi]) {
-                        if constexpr (NBY == 4) *reinterpret_cast<uint32_t*>(dst + 4 * w) = bw;
-                        else *reinterpret_cast<uint16_t*>(dst + 4 * w) = (uint16_t)bw;
+                        if constexpr (FQ) {
+                            const uint32_t o = tokv[gi] * (D / 8) + g * (C / 8) + 4 * w;
+                            if constexpr (NBY == 4) __builtin_amdgcn_raw_buffer_store_b32(bw, rsk, o, 0u, 0);
+                            else __builtin_amdgcn_raw_buffer_store_b16((uint16_t)bw, rsk, o, 0u, 0);
+                        } else {
+                            if constexpr (NBY == 4) *reinterpret_cast<uint32_t*>(dst + 4 * w) = bw;
+                            else *reinterpret_cast<uint16_t*>(dst + 4 * w) = (uint16_t)bw;
+                        }
                     }
                 }
             }
 #pragma unroll
             for (int gi = 0; gi < NG; ++gi) {
                 const float e2 = sum4(e2v[gi]);
-                if (validv[gi] && g == 0)
-                    *reinterpret_cast<_Float16*>(a.packed + a.off_rnorm + vecv[gi] * 2) =
-                        (_Float16)(sqrtf(e2) * (1.0f / 16384.0f));
+                if (validv[gi] && g == 0) {
+                    const _Float16 r16 = (_Float16)(sqrtf(e2) * (1.0f / 16384.0f));
+                    if constexpr (FQ) __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, r16), rrn, tokv[gi] * 2u, 0u, 0);
+                    else *reinterpret_cast<_Float16*>(a.packed + a.off_rnorm + vecv[gi] * 2) = r16;
+                }
             }
             continue;
           }
@@ -505,10 +539,17 @@ void encode_kernel(EncodeArgs a) {
                 for (int gi = 0; gi < NG; ++gi) {
                     const uint32_t bw = ~((((by[gi][3] << 8) | by[gi][2]) << 16) | ((by[gi][1] << 8) | by[gi][0]));
                     if (validv[gi]) {
-                        uint8_t* dst = a.packed + a.off_sketch + vecv[gi] * (int64_t)(m / 8) + g * (m / 32) + (wb >> 3);
-                        if (FULL && (m & 127) == 0) *reinterpret_cast<uint32_t*>(dst) = bw;
-                        else if (nb == 2 && (m & 63) == 0) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)bw;
-                        else for (int q = 0; q < nb; ++q) dst[q] = (uint8_t)(bw >> (8 * q));
+                        if constexpr (FQ) {
+                            const uint32_t o = tokv[gi] * (uint32_t)(m / 8) + (uint32_t)(g * (m / 32)) + (uint32_t)(wb >> 3);
+                            if (FULL && (m & 127) == 0) __builtin_amdgcn_raw_buffer_store_b32(bw, rsk, o, 0u, 0);
+                            else if (nb == 2 && (m & 63) == 0) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)bw, rsk, o, 0u, 0);
+                            else for (int q = 0; q < nb; ++q) __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(bw >> (8 * q)), rsk, o + q, 0u, 0);
+                        } else {
+                            uint8_t* dst = a.packed + a.off_sketch + vecv[gi] * (int64_t)(m / 8) + g * (m / 32) + (wb >> 3);
+                            if (FULL && (m & 127) == 0) *reinterpret_cast<uint32_t*>(dst) = bw;
+                            else if (nb == 2 && (m & 63) == 0) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)bw;
+                            else for (int q = 0; q < nb; ++q) dst[q] = (uint8_t)(bw >> (8 * q));
+                        }
                     }
                 }
             };
@@ -524,9 +565,11 @@ void encode_kernel(EncodeArgs a) {
 #pragma unroll
             for (int gi = 0; gi < NG; ++gi) {
                 const float e2 = sum4(e2v[gi]);
-                if (validv[gi] && g == 0)
-                    *reinterpret_cast<_Float16*>(a.packed + a.off_rnorm + vecv[gi] * 2) =
-                        (_Float16)(sqrtf(e2) * (1.0f / 16384.0f));
+                if (validv[gi] && g == 0) {
+                    const _Float16 r16 = (_Float16)(sqrtf(e2) * (1.0f / 16384.0f));
+                    if constexpr (FQ) __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, r16), rrn, tokv[gi] * 2u, 0u, 0);
+                    else *reinterpret_cast<_Float16*>(a.packed + a.off_rnorm + vecv[gi] * 2) = r16;
+                }
             }
         }
     }
@@ -552,6 +595,9 @@ static int blocks_per_cu(const void* k, size_t lds, int threads) {
 template <int D, int B, bool QJL>
 static bool fq_fits(const EncodeArgs& a) {
     if (a.t.fq_grid == nullptr) return false;
+    // the binade-grid kernel addresses one stream's input and record planes with 32-bit offsets
+    const int64_t lim = (int64_t)1 << 31;
+    if (a.n_tokens * 2 * D >= lim || a.n_tokens * (D * B / 8) >= lim) return false;
     if constexpr (QJL) {
         constexpr int nA = 2 * (D / 32);
         const bool rht = a.t.sketch == 1;

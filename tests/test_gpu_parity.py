@@ -484,6 +484,38 @@ def test_zero_vectors_and_single_token():
     assert np.all(out == 0)
 
 
+@pytest.mark.parametrize("d,b,m", [(64, 1, 0), (128, 2, 0), (128, 3, 128), (128, 4, 128), (64, 4, 64)])
+def test_encode_rotation_aligned_vectors(d, b, m):
+    """Vectors whose rotation is exactly +-e_j (x = c * sign * s ⊙ H[:, j], so y_j = +-1 and the
+    other coordinates are 0): the two ends of the quantiser's domain, and coordinates lying on the
+    middle threshold (t = 0 of the symmetric codebook, flagged by the oracle).  Scales c are powers of
+    two, so the bf16 inputs are exact."""
+    seed = 77 + d + b + m
+    codec = T.Codec(d, b, m, 1, seed)
+    s = O.head_signs(seed, 0, d)
+    Hm = O.hadamard(d)
+    cols = np.arange(d)
+    rows = []
+    for c in (0.5, 4.0, 2.0 ** -10):
+        for sign in (1.0, -1.0):
+            rows.append(sign * c * (s[None, :] * Hm[:, cols].T))
+    x64 = np.concatenate(rows, axis=0)[None]                  # [1, 6 d, d]
+    x = torch.as_tensor(x64, dtype=torch.float32).to(torch.bfloat16).to(DEV)
+    assert np.array_equal(_x64(x), x64)
+    buf = _enc(codec, x)
+    tb = P.Tables(d, b, m, 1, seed)
+    st = P.check_encode(tb, x64, buf)
+    idx = st["recs"][0]["idx"]
+    L = 1 << b
+    y = np.stack([O.rotate(v / np.linalg.norm(v), s) for v in x64[0]])
+    ends = np.abs(y) > 0.5
+    assert ends.sum() == x64.shape[1]
+    assert np.all(idx[ends & (y > 0)] == L - 1) and np.all(idx[ends & (y < 0)] == 0)
+    xh = T.decode(codec, torch.as_tensor(buf, device=DEV), 1, x64.shape[1], torch.float32).cpu().numpy()
+    P.check_decode_f32(tb, st["recs"], [0], xh)
+    print(f"rotation-aligned d={d} b={b} m={m}: flagged {st['flagged']}, index mismatches {st['idx_mismatch']}")
+
+
 def test_norm_above_fp16_range_is_inf():
     d = 64
     codec = T.Codec(d, 3, 0, 1, 5)
