@@ -35,16 +35,16 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published (the sketch p
 # the kernel's sources are the ones it was measured on (sha256 of the .hip file + shared headers).
 FETCH_UNIT_B, WRITE_UNIT_B = 2048, 1024
 TRAFFIC = {
-    "encode_k": {"fetch": 2097500.625, "write": 1394851.5625, "src": "encode.hip",
-        "sha": "333c5c29daa934b587d685de2722eb2d4e1ea18dcf570b97354214954361c873"},
-    "encode_v": {"fetch": 2105256.9375, "write": 1090695.4375, "src": "encode.hip",
-        "sha": "333c5c29daa934b587d685de2722eb2d4e1ea18dcf570b97354214954361c873"},
-    "decode_attention": {"fetch": 1231930.25, "write": 6240.0, "src": "attention.hip",
-        "sha": "3ef759675fd902b137993d34c823d75eb2036ed2688f7d2beb7aab1c5f47fc55"},
-    "decode_v_bf16": {"fetch": 550256.75, "write": 4194304.0, "src": "decode.hip",
+    "encode_k": {"fetch": 2097508.5625, "write": 1395892.03125, "src": "encode.hip",
+        "sha": "8f5183252e566100540547dadba46aca3ad0cf8ad58db3cb4b8702c75a4bc2e9"},
+    "encode_v": {"fetch": 2105563.4375, "write": 1090905.40625, "src": "encode.hip",
+        "sha": "8f5183252e566100540547dadba46aca3ad0cf8ad58db3cb4b8702c75a4bc2e9"},
+    "decode_attention": {"fetch": 1232616.125, "write": 6240.0, "src": "attention.hip",
+        "sha": "3dbc44b6e10d3865cf6738768088b9cbfa4718ea308aff584a85b00b28e9d84f"},
+    "decode_v_bf16": {"fetch": 550379.1875, "write": 4194304.0, "src": "decode.hip",
         "sha": "2add9ea1fa8cf5d1d37b9846a4505b28cdfa3553557c2e41c88d2f2cc96455e9"},
 }
-TRAFFIC_HEADERS_SHA = ("171296081e898f9aa4b751e3e213ec369098f8cce83d03dc938fb9e239591c0c"   # common.hpp
+TRAFFIC_HEADERS_SHA = ("6643b4ed6d32e0cc4205551fb1ef8fab74077690c7d82ac29a903d73ebc0d666"   # common.hpp
                        "c79a58581fb18e7686561d680e8fdc2107a0b0d7c4661d9115f2dda2656965da")  # kernels.hpp
 
 
