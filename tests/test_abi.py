@@ -132,6 +132,13 @@ def test_argument_validation_before_any_gpu_call():
     assert call(pk8, pv, 32, 8, 0) == _lib.TQ_EINVAL                  # empty cache
     assert call(pk8, pv, 32, 8, 1000, scale=-1.0) == _lib.TQ_EINVAL
     assert call(pk8, pv, 32, 8, 1000, wsb=wsa - 1) == _lib.TQ_EWORKSPACE
+    # a stream's planes are addressed with 32-bit offsets: at d = 128, b = 4 (64-byte index rows)
+    # the index plane must stay below 2^32 - 2^16 bytes, i.e. at most 67107840 tokens
+    big = (2**32 - 2**16) // 64 + 1
+    wsb = L.tq_attention_workspace_bytes(pk8, 2, 32, 8, big)
+    assert wsb > wsa
+    assert call(pk8, pv, 32, 8, big, wsb=wsb) == _lib.TQ_EUNSUPPORTED
+    assert call(pk8, pv, 32, 8, big, wsb=wsb - 1) == _lib.TQ_EWORKSPACE   # the workspace is checked first
 
 
 def test_product_package_does_not_import_the_oracle():
