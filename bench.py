@@ -69,8 +69,8 @@ def traffic_bytes(kernel: str):
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
-    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--context", type=int, default=131072)
     ap.add_argument("--no-extra", action="store_true", help="skip the per-kernel lines of the other workloads")
@@ -137,7 +137,8 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
-    kms = {n: sum(a.elapsed_time(b) for a, b in ev[n]) / len(ev[n]) for n in names}
+    samples = {n: [a.elapsed_time(b) for a, b in ev[n]] for n in names}
+    kms = {n: sum(samples[n]) / len(samples[n]) for n in names}
 
     # algorithmic bytes per launch (what each kernel must move at minimum)
     nvec = streams * N
@@ -155,7 +156,7 @@ def main():
     for n in names:
         gbs = alg[n] / (kms[n] * 1e-3) / 1e9
         bf = (2 * nvec * d * 2 if n == "decode_attention" else nvec * d * 2) / (kms[n] * 1e-3) / 1e9
-        kern[n] = {"ms": round(kms[n], 4), "alg_bytes": alg[n], "achieved_GBs": round(gbs, 1),
+        kern[n] = {"ms": round(kms[n], 4), **_spread(samples[n]), "alg_bytes": alg[n], "achieved_GBs": round(gbs, 1),
                    "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bf16_equiv_GBs": round(bf, 1)}
     kern["encode_k"]["sketch_tflops"] = round(nvec * 2 * ck.m * d / (kms["encode_k"] * 1e-3) / 1e12, 2)
 
@@ -402,8 +403,15 @@ def main():
 _FLUSH = []
 
 
-def _time(torch, stream, fn, reps: int = 5) -> float:
-    """average ms of fn() over reps launches on `stream` (after one untimed call); before every timed
+def _spread(ms: list) -> dict:
+    """median and 10th / 90th percentiles of per-launch times (nearest rank)"""
+    v = sorted(ms)
+    at = lambda f: v[min(len(v) - 1, max(0, int(round(f * (len(v) - 1)))))]
+    return {"median_ms": round(at(0.5), 4), "p10_ms": round(at(0.1), 4), "p90_ms": round(at(0.9), 4)}
+
+
+def _time(torch, stream, fn, reps: int = 20) -> list:
+    """per-launch ms of fn() over reps launches on `stream` (after one untimed call); before every timed
     launch, outside its events, a 1 GiB buffer is read (a reduction: clean lines only, so no
     write-back lands in the timed launch) so that neither the L2s nor the 256 MB Infinity Cache
     still hold the launch's inputs (the smaller workloads would otherwise fit)"""
@@ -420,12 +428,14 @@ def _time(torch, stream, fn, reps: int = 5) -> float:
         e1.record(stream)
         ev.append((e0, e1))
     torch.cuda.synchronize()
-    return sum(a.elapsed_time(b) for a, b in ev) / reps
+    return [a.elapsed_time(b) for a, b in ev]
 
 
-def _line(ms: float, alg_bytes: int) -> dict:
+def _line(samples: list, alg_bytes: int) -> dict:
+    """mean ms (the rate's basis), its spread, and the algorithmic rate"""
+    ms = sum(samples) / len(samples)
     gbs = alg_bytes / (ms * 1e-3) / 1e9
-    return {"ms": round(ms, 4), "alg_bytes": alg_bytes, "achieved_GBs": round(gbs, 1),
+    return {"ms": round(ms, 4), **_spread(samples), "alg_bytes": alg_bytes, "achieved_GBs": round(gbs, 1),
             "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)}
 
 
