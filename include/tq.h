@@ -115,9 +115,8 @@ int tq_decode(const tq_params* p, const void* packed, int64_t n_streams, int64_t
  * sketch correction sqrt(pi/2)/d ||e|| s2 ⊙ WHT(b) is added at decode):
  *   x̂ = n16 · s ⊙ H (c[idx] + Δŷ) / sqrt(d),   Δŷ = sqrt(pi/2)/m · r16 · S^T (2σ - 1),
  * for either sketch kind (for the RHT sketch S^T (2σ - 1) = s2 ⊙ H (2σ - 1), m = d).  Same arguments,
- * layout and ownership as tq_decode; p->m must be > 0 (TQ_EINVAL otherwise).  S^T is held in LDS:
- * TQ_EUNSUPPORTED when d·m·2 bytes plus the kernel's LUT and staging exceed 160 KiB (d = 256 with
- * m = 256). */
+ * layout and ownership as tq_decode; p->m must be > 0 (TQ_EINVAL otherwise).  S^T is held in LDS
+ * (d·m·2 bytes, 128 KiB at d = m = 256); every supported (d, b, m) fits. */
 int tq_decode_qjl(const tq_params* p, const void* packed, int64_t n_streams, int64_t n_tokens,
                   void* x_hat, tq_dtype out_dtype, void* stream);
 

@@ -27,10 +27,16 @@ __device__ __forceinline__ uint32_t bf16_pair_rne(float lo, float hi) {
 // so lane part g receives its own coordinates g C + 4 t + i) and B = the ±1 sketch signs (exact),
 // giving exact fp32 sums; c + Δŷ is then split into fp16 hi + lo parts of 2^12 (c + Δŷ) as the B
 // operands of the inverse transform.
-template <int D, int B, bool OUT_BF16, bool QJL = false>
+// LEAN (the corrected decode where S^T fills most of LDS: d = 256, m = 256): a lookup of one
+// coordinate per entry (2^b entries) and direct stores of each lane's contiguous output coordinates
+// instead of the staged row block, so S^T and the tables fit in 133 KiB whatever b is.
+template <int D, int B, bool OUT_BF16, bool QJL = false, bool LEAN = false>
 __global__ __launch_bounds__(256, (D == 256 && B == 6 && !OUT_BF16) || QJL ? 1 : 2) void decode_kernel(DecodeArgs a) {
+    static_assert(!LEAN || QJL, "the lean form serves the corrected decode");
+    constexpr int NWAVES = 4;
     constexpr int C = D / 4, NKB = D / 32;
-    constexpr int P = lut_group_c(B), NE = 1 << (P * B);
+    constexpr int PG = lut_group_c(B);                   // coordinates per entry of the device table
+    constexpr int P = LEAN ? 1 : PG, NE = 1 << (P * B);
     constexpr int NW = (C * B + 31) / 32;
     constexpr int CB = C * B / 8;
     constexpr int CA = cmin(pow2_align(CB), 16);
@@ -42,9 +48,17 @@ __global__ __launch_bounds__(256, (D == 256 && B == 6 && !OUT_BF16) || QJL ? 1 :
     constexpr int ROW = ES * D;                          // output bytes per vector
     constexpr int ROWP = ROW + 16;                       // padded LDS row
     constexpr int STG = 16 * ROWP;                       // LDS staging bytes per wave
-    __shared__ __align__(16) uint8_t stage[4 * STG];
-    for (int i = threadIdx.x; i < NE * P * 2; i += blockDim.x) lut[i] = a.t.lut_hl[i];
-    // block = one stream's tile range; waves take every 4th tile
+    __shared__ __align__(16) uint8_t stage[LEAN ? 16 : NWAVES * STG];
+    if constexpr (LEAN) {
+        // entry i: 2^12 c[i] as hi, lo: the device table's entry whose other coordinates are index 0
+        for (int i = threadIdx.x; i < NE; i += blockDim.x) {
+            lut[2 * i] = a.t.lut_hl[i * 2 * PG];
+            lut[2 * i + 1] = a.t.lut_hl[i * 2 * PG + PG];
+        }
+    } else {
+        for (int i = threadIdx.x; i < NE * P * 2; i += blockDim.x) lut[i] = a.t.lut_hl[i];
+    }
+    // block = one stream's tile range; waves take every NWAVES-th tile
     const int64_t st = blockIdx.x / a.blocks_per_stream;
     const int64_t sub = blockIdx.x - st * a.blocks_per_stream;
     const int64_t tb0 = sub * a.tiles_per_block;
@@ -150,7 +164,7 @@ __global__ __launch_bounds__(256, (D == 256 && B == 6 && !OUT_BF16) || QJL ? 1 :
     uint32_t wn[NW], nbn, skn[NSW], rbn = 0u;
     if (tb0 + wave < tb1) load_tile(wn, nbn, skn, rbn, tb0 + wave);
 #pragma unroll 1
-    for (int64_t tile = tb0 + wave; tile < tb1; tile += 4) {
+    for (int64_t tile = tb0 + wave; tile < tb1; tile += NWAVES) {
         uint32_t w[NW], sk[NSW];
 #pragma unroll
         for (int k = 0; k < NW; ++k) w[k] = wn[k];
@@ -158,7 +172,7 @@ __global__ __launch_bounds__(256, (D == 256 && B == 6 && !OUT_BF16) || QJL ? 1 :
         for (int k = 0; k < NSW; ++k) sk[k] = skn[k];
         const float nrm = (float)__builtin_bit_cast(_Float16, (uint16_t)nbn);
         const float rn = (float)__builtin_bit_cast(_Float16, (uint16_t)rbn);
-        if (tile + 4 < tb1) load_tile(wn, nbn, skn, rbn, tile + 4);   // next tile's loads overlap this tile's math
+        if (tile + NWAVES < tb1) load_tile(wn, nbn, skn, rbn, tile + NWAVES);   // next tile's loads overlap this tile's math
         // QJL: dl[s] = (S^T (2σ - 1)) at coordinate g C + s, scaled by 2^12 sqrt(pi/2)/m r16
         float dl[QJL ? C : 1];
         if constexpr (QJL) {
@@ -256,22 +270,33 @@ __global__ __launch_bounds__(256, (D == 256 && B == 6 && !OUT_BF16) || QJL ? 1 :
 #pragma unroll
             for (int k = 0; k < C; ++k) o[k] = f2u(x[k] * sc) ^ smask[k];
         }
-        uint8_t* wst = stage + wave * STG;
+        if constexpr (LEAN) {
+            // the lane's coordinates g C .. g C + C - 1 of vector `tok` are ES·C contiguous bytes
+            const int64_t tok = tile * 16 + v;
+            if (tok < a.n_tokens) {
+                uint8_t* dst = reinterpret_cast<uint8_t*>(a.out) + (st * a.n_tokens + tok) * (int64_t)ROW + g * (4 * NOW);
 #pragma unroll
-        for (int k = 0; k < NOW / 4; ++k)
-            *reinterpret_cast<u32x4*>(wst + v * ROWP + g * (4 * NOW) + 16 * k) =
-                u32x4{o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]};
-        __builtin_amdgcn_wave_barrier();
-        const int64_t nvalid = a.n_tokens - tile * 16;   // rows of this tile inside the stream
-        uint8_t* gdst = reinterpret_cast<uint8_t*>(a.out) + (st * a.n_tokens + tile * 16) * (int64_t)ROW;
+                for (int k = 0; k < NOW / 4; ++k)
+                    *reinterpret_cast<u32x4*>(dst + 16 * k) = u32x4{o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]};
+            }
+        } else {
+            uint8_t* wst = stage + wave * STG;
 #pragma unroll
-        for (int r = 0; r < ROW / 64; ++r) {
-            const int off = r * 1024 + 16 * lane;      // linear byte offset within the block
-            const int row = off / ROW, col = off - row * ROW;
-            const u32x4 val = *reinterpret_cast<const u32x4*>(wst + row * ROWP + col);
-            if (row < nvalid) *reinterpret_cast<u32x4*>(gdst + off) = val;
+            for (int k = 0; k < NOW / 4; ++k)
+                *reinterpret_cast<u32x4*>(wst + v * ROWP + g * (4 * NOW) + 16 * k) =
+                    u32x4{o[4 * k], o[4 * k + 1], o[4 * k + 2], o[4 * k + 3]};
+            __builtin_amdgcn_wave_barrier();
+            const int64_t nvalid = a.n_tokens - tile * 16;   // rows of this tile inside the stream
+            uint8_t* gdst = reinterpret_cast<uint8_t*>(a.out) + (st * a.n_tokens + tile * 16) * (int64_t)ROW;
+#pragma unroll
+            for (int r = 0; r < ROW / 64; ++r) {
+                const int off = r * 1024 + 16 * lane;      // linear byte offset within the block
+                const int row = off / ROW, col = off - row * ROW;
+                const u32x4 val = *reinterpret_cast<const u32x4*>(wst + row * ROWP + col);
+                if (row < nvalid) *reinterpret_cast<u32x4*>(gdst + off) = val;
+            }
+            __builtin_amdgcn_wave_barrier();
         }
-        __builtin_amdgcn_wave_barrier();
     }
 }
 
@@ -301,37 +326,56 @@ static hipError_t launch_one(const DecodeArgs& a, int num_cus, hipStream_t s) {
     return hipGetLastError();
 }
 
+// raise kernel k's dynamic LDS limit to `bytes` once
+static hipError_t raise_dyn_lds(const void* k, int bytes) {
+    static std::mutex mu;
+    static std::map<const void*, int> done;
+    std::lock_guard<std::mutex> lock(mu);
+    auto it = done.find(k);
+    if (it != done.end() && it->second >= bytes) return hipSuccess;
+    const hipError_t e = hipFuncSetAttribute(k, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess) done[k] = bytes;
+    return e;
+}
+
 // QJL-corrected decode: S^T in LDS (d m 2 bytes) plus the 4 KiB sign table as dynamic LDS beside the
-// kernel's static LUT and staging buffer; unsupported when that exceeds one CU's 160 KiB
-template <int D, int B, bool BF>
-static hipError_t launch_one_qjl(const DecodeArgs& a, int num_cus, hipStream_t s, bool* supported) {
-    constexpr int P = lut_group_c(B), NE = 1 << (P * B);
+// kernel's static LUT and staging buffer.  At d = 256 where that exceeds one CU's 160 KiB (m = 256),
+// the lean form (no staging buffer, a 2^b-entry lookup) runs instead.
+template <int D, int B, bool BF, bool LEAN>
+static hipError_t launch_qjl_form(const DecodeArgs& a, int num_cus, hipStream_t s, size_t stat, size_t dyn) {
     constexpr size_t kLdsMax = 163840;
-    const size_t stat = (size_t)NE * P * 4 + (size_t)4 * 16 * ((BF ? 2 : 4) * D + 16);
-    const size_t dyn = (a.t.sketch == 1 ? 0 : (size_t)D * a.t.m * 2) + 256 * 16;
-    *supported = stat + dyn <= kLdsMax;
-    if (!*supported) return hipSuccess;
-    const void* kern = reinterpret_cast<const void*>(&decode_kernel<D, B, BF, true>);
+    constexpr int threads = 256;
+    const void* kern = reinterpret_cast<const void*>(&decode_kernel<D, B, BF, true, LEAN>);
     if (dyn > 65536) {
-        static std::mutex mu;
-        static bool raised = false;
-        std::lock_guard<std::mutex> lock(mu);
-        if (!raised) {
-            const hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kLdsMax - stat));
-            if (e != hipSuccess) return e;
-            raised = true;
-        }
+        const hipError_t e = raise_dyn_lds(kern, (int)(kLdsMax - stat));
+        if (e != hipSuccess) return e;
     }
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, 256, dyn) != hipSuccess || nb < 1) nb = 1;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, kern, threads, dyn) != hipSuccess || nb < 1) nb = 1;
     DecodeArgs b = a;
     int64_t bps = ((int64_t)num_cus * nb + a.n_streams - 1) / a.n_streams;
     if (bps > a.tiles_per_stream) bps = a.tiles_per_stream;
     if (bps < 1) bps = 1;
     b.blocks_per_stream = bps;
     b.tiles_per_block = (a.tiles_per_stream + bps - 1) / bps;
-    hipLaunchKernelGGL((decode_kernel<D, B, BF, true>), dim3((unsigned)(a.n_streams * bps)), dim3(256), dyn, s, b);
+    hipLaunchKernelGGL((decode_kernel<D, B, BF, true, LEAN>), dim3((unsigned)(a.n_streams * bps)), dim3(threads), dyn, s, b);
     return hipGetLastError();
+}
+
+template <int D, int B, bool BF>
+static hipError_t launch_one_qjl(const DecodeArgs& a, int num_cus, hipStream_t s, bool* supported) {
+    constexpr int P = lut_group_c(B), NE = 1 << (P * B);
+    constexpr size_t kLdsMax = 163840;
+    const size_t stat = (size_t)NE * P * 4 + (size_t)4 * 16 * ((BF ? 2 : 4) * D + 16);
+    const size_t dyn = (a.t.sketch == 1 ? 0 : (size_t)D * a.t.m * 2) + 256 * 16;
+    *supported = true;
+    if (stat + dyn <= kLdsMax) return launch_qjl_form<D, B, BF, false>(a, num_cus, s, stat, dyn);
+    if constexpr (D == 256) {
+        const size_t lean = (size_t)(1 << B) * 4 + 16;
+        if (lean + dyn <= kLdsMax) return launch_qjl_form<D, B, BF, true>(a, num_cus, s, lean, dyn);
+    }
+    *supported = false;
+    return hipSuccess;
 }
 
 template <int D>

@@ -211,7 +211,8 @@ def test_rht_encode_decode_scores_parity(d, b, dt):
 
 
 @pytest.mark.parametrize("d,b,m,kind", [(128, 4, 128, 0), (64, 3, 64, 0), (256, 3, 128, 0), (128, 2, 32, 0),
-                                         (128, 4, 128, 1), (64, 2, 64, 1), (128, 6, 96, 0)])
+                                         (128, 4, 128, 1), (64, 2, 64, 1), (128, 6, 96, 0),
+                                         (256, 3, 256, 0), (256, 6, 256, 0)])
 def test_decode_with_qjl_correction(d, b, m, kind):
     """tq_decode_qjl: n16 · s ⊙ H (c[idx] + sqrt(pi/2)/m · r16 · S^T (2σ - 1)) / sqrt(d), from the GPU's
     packed fields; fp32 within 1e-5 relative L2, bf16 within one rounding."""
@@ -241,12 +242,6 @@ def test_decode_with_qjl_correction_limits():
     buf = T.encode(T.Codec(128, 4, 0, 1, 3), x)
     with pytest.raises(T._lib.TQError):                       # no sketch to correct with
         T.decode(T.Codec(128, 4, 0, 1, 3), buf, 1, 40, qjl=True)
-    c = T.Codec(256, 3, 256, 1, 3)
-    x = I.gaussian((1, 40, 256), 3, device=DEV)
-    buf = T.encode(c, x)
-    with pytest.raises(T._lib.TQError) as ei:                 # S^T does not fit beside the staging
-        T.decode(c, buf, 1, 40, qjl=True)
-    assert ei.value.status == T._lib.TQ_EUNSUPPORTED
 
 
 @pytest.mark.parametrize("batch,hq,hkv,N,d,b", [(2, 8, 2, 3000, 128, 4), (1, 4, 2, 900, 256, 3), (1, 8, 1, 500, 64, 4)])
