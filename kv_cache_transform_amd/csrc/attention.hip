@@ -574,72 +574,112 @@ void attn_kernel(AttnArgs a) {
     }
 }
 
-// merge the splits of one (batch, q head), rotate back, store
+// merge the splits of one (batch, q head), rotate back, store.  Latency-bound, so every load is
+// issued up front: thread t sums coordinate t % D over the splits s = t / D (mod 256 / D), whose
+// partials it fetches before the max is known (16 splits a round); the split maxima and sums go
+// through LDS; the first wave applies the inverse rotation s_V ⊙ H(·)/sqrt(d) in registers (lane l
+// holds coordinates (D/64) l + c, the low index bits in the lane, the rest as lane-xor butterflies).
+template <int D>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
+    constexpr int NPJ = 256 / D, CH = 16, PL = D / 64;
     const int64_t row = blockIdx.x;                      // batch * n_q_heads + h
     const int bidx = (int)(row / a.n_q_heads), h = (int)(row - (int64_t)bidx * a.n_q_heads);
     const int kvh = h / a.group, r = h - kvh * a.group;
     const int64_t st = (int64_t)bidx * a.n_kv_heads + kvh;
-    const int d = a.tv.d, ns = a.n_split;
-    __shared__ float buf[256];
-    __shared__ float wsp[1024];                          // per-split weights (n_split <= 1024)
-    __shared__ float red[8];
-    const float* ml = a.part_ml + (st * ns * 16 + r) * 2;   // split s at ml[s * 32]
-    // max over splits
+    const int ns = a.n_split, tid = threadIdx.x, lane = tid & 63;
+    const int j = tid % D, pj = tid / D;
+    __shared__ float buf[D], sums[256], wsp[1024], red[8];   // n_split <= 1024
+    const float* ml = a.part_ml + (st * ns * 16 + r) * 2;     // split s at ml[s * 32]
+    const float* part = a.part + (st * ns * 16 + r) * (int64_t)D + j;   // split s at part[s * 16 D]
+    float pv[CH];
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+        const int sp = pj + NPJ * k;
+        pv[k] = sp < ns ? part[(int64_t)sp * 16 * D] : 0.0f;
+    }
     float mx = -INFINITY;
-    for (int s = threadIdx.x; s < ns; s += blockDim.x) mx = fmaxf(mx, ml[s * 32]);
+    for (int sp = tid; sp < ns; sp += 256) mx = fmaxf(mx, ml[sp * 32]);
     for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+    if (lane == 0) red[tid >> 6] = mx;
     __syncthreads();
     const float M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     if (M == -INFINITY) {                                // an empty cache (length 0): output zeros
-        for (int j = threadIdx.x; j < d; j += blockDim.x) {
-            if (a.out_bf16) reinterpret_cast<__bf16*>(a.out)[row * d + j] = (__bf16)0.0f;
-            else reinterpret_cast<float*>(a.out)[row * d + j] = 0.0f;
+        if (tid < D) {
+            if (a.out_bf16) reinterpret_cast<__bf16*>(a.out)[row * D + tid] = (__bf16)0.0f;
+            else reinterpret_cast<float*>(a.out)[row * D + tid] = 0.0f;
         }
         return;
     }
     float ls = 0.0f;
-    for (int s = threadIdx.x; s < ns; s += blockDim.x) {
-        const float w = exp2f(ml[s * 32] - M);
-        wsp[s] = w;
-        ls += w * ml[s * 32 + 1];
+    for (int sp = tid; sp < ns; sp += 256) {
+        const float w = exp2f(ml[sp * 32] - M);
+        wsp[sp] = w;
+        ls += w * ml[sp * 32 + 1];
     }
     for (int o = 32; o > 0; o >>= 1) ls += __shfl_xor(ls, o);
-    __syncthreads();
-    if ((threadIdx.x & 63) == 0) red[4 + (threadIdx.x >> 6)] = ls;
+    if (lane == 0) red[4 + (tid >> 6)] = ls;
     __syncthreads();
     const float Linv = 1.0f / (red[4] + red[5] + red[6] + red[7]);
-    const float* part = a.part + (st * ns * 16 + r) * (int64_t)d;  // split s at part[s * 16 d]
-    for (int j = threadIdx.x; j < d; j += blockDim.x) {
-        float acc0 = 0.0f, acc1 = 0.0f, acc2 = 0.0f, acc3 = 0.0f;
-        int s = 0;
-        for (; s + 4 <= ns; s += 4) {
-            acc0 = fmaf(wsp[s], part[(int64_t)s * 16 * d + j], acc0);
-            acc1 = fmaf(wsp[s + 1], part[(int64_t)(s + 1) * 16 * d + j], acc1);
-            acc2 = fmaf(wsp[s + 2], part[(int64_t)(s + 2) * 16 * d + j], acc2);
-            acc3 = fmaf(wsp[s + 3], part[(int64_t)(s + 3) * 16 * d + j], acc3);
-        }
-        for (; s < ns; ++s) acc0 = fmaf(wsp[s], part[(int64_t)s * 16 * d + j], acc0);
-        buf[j] = ((acc0 + acc1) + (acc2 + acc3)) * Linv;
+    float acc = 0.0f;
+#pragma unroll
+    for (int k = 0; k < CH; ++k) {
+        const int sp = pj + NPJ * k;
+        if (sp < ns) acc = fmaf(wsp[sp], pv[k], acc);
     }
+    for (int s0 = NPJ * CH; s0 < ns; s0 += NPJ * CH) {   // more than 16 splits a thread
+#pragma unroll
+        for (int k = 0; k < CH; ++k) {
+            const int sp = s0 + pj + NPJ * k;
+            pv[k] = sp < ns ? part[(int64_t)sp * 16 * D] : 0.0f;
+        }
+#pragma unroll
+        for (int k = 0; k < CH; ++k) {
+            const int sp = s0 + pj + NPJ * k;
+            if (sp < ns) acc = fmaf(wsp[sp], pv[k], acc);
+        }
+    }
+    sums[tid] = acc;
     __syncthreads();
-    const bool rot = a.tv.rotation != 1;               // Plain-KV values: no inverse rotation
-    for (int hh = 1; hh < (rot ? d : 1); hh <<= 1) {
-        for (int i = threadIdx.x; i < d / 2; i += blockDim.x) {
-            const int lo = (i / hh) * 2 * hh + (i % hh);
-            const float x0 = buf[lo], x1 = buf[lo + hh];
-            buf[lo] = x0 + x1;
-            buf[lo + hh] = x0 - x1;
+    if (tid < 64) {
+        const bool rot = a.tv.rotation != 1;           // Plain-KV values: no inverse rotation
+        float v[PL];
+#pragma unroll
+        for (int c = 0; c < PL; ++c) {
+            float t = 0.0f;
+#pragma unroll
+            for (int q = 0; q < NPJ; ++q) t += sums[q * D + PL * lane + c];
+            v[c] = t * Linv;
         }
-        __syncthreads();
-    }
-    const float inv = rot ? 1.0f / sqrtf((float)d) : 1.0f;
-    const float* sg = a.tv.signs + (int64_t)kvh * d;
-    for (int j = threadIdx.x; j < d; j += blockDim.x) {
-        const float o = rot ? buf[j] * inv * sg[j] : buf[j];
-        if (a.out_bf16) reinterpret_cast<__bf16*>(a.out)[row * d + j] = (__bf16)o;
-        else reinterpret_cast<float*>(a.out)[row * d + j] = o;
+        if (rot) {
+#pragma unroll
+            for (int hh = 1; hh < PL; hh <<= 1)
+#pragma unroll
+                for (int c = 0; c < PL; ++c)
+                    if (!(c & hh)) {
+                        const float x0 = v[c], x1 = v[c + hh];
+                        v[c] = x0 + x1;
+                        v[c + hh] = x0 - x1;
+                    }
+#pragma unroll
+            for (int hl = 1; hl < 64; hl <<= 1) {
+                const bool hi = (lane & hl) != 0;
+#pragma unroll
+                for (int c = 0; c < PL; ++c) {
+                    const float o = __shfl_xor(v[c], hl);
+                    v[c] = hi ? o - v[c] : v[c] + o;
+                }
+            }
+            const float inv = 1.0f / sqrtf((float)D);
+            const float* sg = a.tv.signs + (int64_t)kvh * D + PL * lane;
+#pragma unroll
+            for (int c = 0; c < PL; ++c) v[c] = v[c] * inv * sg[c];
+        }
+#pragma unroll
+        for (int c = 0; c < PL; ++c) {
+            const int64_t k = row * D + PL * lane + c;
+            if (a.out_bf16) reinterpret_cast<__bf16*>(a.out)[k] = (__bf16)v[c];
+            else reinterpret_cast<float*>(a.out)[k] = v[c];
+        }
     }
 }
 
@@ -657,7 +697,7 @@ static hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(attn_combine_kernel, dim3((unsigned)((int64_t)a.batch * a.n_q_heads)), dim3(256), 0, s, a);
+    hipLaunchKernelGGL(attn_combine_kernel<D>, dim3((unsigned)((int64_t)a.batch * a.n_q_heads)), dim3(256), 0, s, a);
     return hipGetLastError();
 }
 

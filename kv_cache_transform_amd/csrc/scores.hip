@@ -18,53 +18,81 @@
 namespace tq {
 
 // ---------------------------------------------------------------------------------------------
-// q_rot and p per query row; one block of 256 threads per row (tiny amount of work).  Both are
-// formed in fp32, scaled by the row's power of two 2^e (the largest |entry| of the two in
-// [2^13, 2^14)) and written as fp16 hi + lo parts: hi the nearest fp16, lo the nearest fp16 of the
-// remainder, so hi + lo is within ~2^-22 of the fp32 value for every entry above the fp16 subnormal
-// range (2^-14 of a unit at most 2^-27 of the row's largest entry).
+// q_rot and p per query row; one block of 256 threads per row (tiny amount of work, so the kernel is
+// latency-bound: every load is issued up front).  Thread i < m fetches row i of S as D/8 16-byte
+// pieces before anything else; the first wave loads the query, flips its signs and rotates it in
+// registers (lane l holds coordinates (D/64) l + c: the low index bits in the lane, the rest as
+// lane-xor butterflies, stage by stage from the lowest bit); then p_i = sum_j S_ij q_rot_j in
+// index order.  Both are formed in fp32, scaled by the row's power of two 2^e (the largest |entry|
+// of the two in [2^13, 2^14)) and written as fp16 hi + lo parts: hi the nearest fp16, lo the nearest
+// fp16 of the remainder, so hi + lo is within ~2^-22 of the fp32 value for every entry above the
+// fp16 subnormal range (2^-14 of a unit at most 2^-27 of the row's largest entry).
+template <int D>
 __global__ __launch_bounds__(256) void qprep_kernel(QPrepArgs a) {
+    constexpr int PL = D / 64, NS = D / 8;
     const int64_t row = blockIdx.x;
-    const int d = a.t.d, m = a.t.m;
+    const int m = a.t.m, tid = threadIdx.x, lane = tid & 63;
     const int head = (int)((row / a.n_q_per_stream) % a.t.n_heads);
-    __shared__ float buf[256], pbuf[256], red[4];
-    const float* sg = a.t.signs + (int64_t)head * d;
-    for (int j = threadIdx.x; j < d; j += blockDim.x) {
-        float x;
-        if (a.q_bf16) {
-            const uint16_t u = reinterpret_cast<const uint16_t*>(a.q)[row * d + j];
-            x = u2f(uint32_t(u) << 16);
-        } else {
-            x = reinterpret_cast<const float*>(a.q)[row * d + j];
+    __shared__ float buf[D], red[4];
+    u32x4 srow[NS];
+    if (tid < m) {
+        const u32x4* sp = reinterpret_cast<const u32x4*>(a.t.S + ((int64_t)head * m + tid) * D);
+#pragma unroll
+        for (int k = 0; k < NS; ++k) srow[k] = sp[k];
+    }
+    const bool rot = a.t.rotation != 1;               // no rotation: q_rot = q
+    if (tid < 64) {
+        float v[PL];
+        const float* sg = a.t.signs + (int64_t)head * D + PL * lane;
+#pragma unroll
+        for (int c = 0; c < PL; ++c) {
+            const int64_t j = row * D + PL * lane + c;
+            const float x = a.q_bf16 ? u2f(uint32_t(reinterpret_cast<const uint16_t*>(a.q)[j]) << 16)
+                                     : reinterpret_cast<const float*>(a.q)[j];
+            v[c] = rot ? x * sg[c] : x;
         }
-        buf[j] = a.t.rotation == 1 ? x : x * sg[j];
+        if (rot) {
+#pragma unroll
+            for (int h = 1; h < PL; h <<= 1)
+#pragma unroll
+                for (int c = 0; c < PL; ++c)
+                    if (!(c & h)) {
+                        const float x0 = v[c], x1 = v[c + h];
+                        v[c] = x0 + x1;
+                        v[c + h] = x0 - x1;
+                    }
+#pragma unroll
+            for (int hl = 1; hl < 64; hl <<= 1) {
+                const bool hi = (lane & hl) != 0;
+#pragma unroll
+                for (int c = 0; c < PL; ++c) {
+                    const float o = __shfl_xor(v[c], hl);
+                    v[c] = hi ? o - v[c] : v[c] + o;
+                }
+            }
+            const float inv = 1.0f / sqrtf((float)D);
+#pragma unroll
+            for (int c = 0; c < PL; ++c) v[c] *= inv;
+        }
+#pragma unroll
+        for (int c = 0; c < PL; ++c) buf[PL * lane + c] = v[c];
     }
     __syncthreads();
-    for (int h = 1; h < (a.t.rotation == 1 ? 1 : d); h <<= 1) {   // no rotation: q_rot = q
-        for (int i = threadIdx.x; i < d / 2; i += blockDim.x) {
-            const int lo = (i / h) * 2 * h + (i % h);
-            const float x0 = buf[lo], x1 = buf[lo + h];
-            buf[lo] = x0 + x1;
-            buf[lo + h] = x0 - x1;
+    float mx = 0.0f, p = 0.0f;
+    if (tid < m) {
+        float acc = 0.0f;
+#pragma unroll
+        for (int k = 0; k < NS; ++k) {
+            const half8 hs = __builtin_bit_cast(half8, srow[k]);
+#pragma unroll
+            for (int u = 0; u < 8; ++u) acc = fmaf((float)hs[u], buf[8 * k + u], acc);
         }
-        __syncthreads();
+        p = acc * a.p_scale;
+        mx = fabsf(p);
     }
-    const float inv = a.t.rotation == 1 ? 1.0f : 1.0f / sqrtf((float)d);
-    for (int j = threadIdx.x; j < d; j += blockDim.x) buf[j] *= inv;
-    __syncthreads();
-    float mx = 0.0f;
-    if (m > 0) {
-        const _Float16* S = a.t.S + (int64_t)head * m * d;
-        for (int i = threadIdx.x; i < m; i += blockDim.x) {
-            float acc = 0.0f;
-            for (int j = 0; j < d; ++j) acc = fmaf((float)S[(int64_t)i * d + j], buf[j], acc);
-            pbuf[i] = acc * a.p_scale;
-            mx = fmaxf(mx, fabsf(pbuf[i]));
-        }
-    }
-    for (int j = threadIdx.x; j < d; j += blockDim.x) mx = fmaxf(mx, fabsf(buf[j] * a.q_scale));
+    if (tid < D) mx = fmaxf(mx, fabsf(buf[tid] * a.q_scale));
     for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = mx;
+    if (lane == 0) red[tid >> 6] = mx;
     __syncthreads();
     mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
     // 2^e with the row's largest entry in [2^13, 2^14); an all-zero (or non-finite) row keeps e = 0
@@ -76,15 +104,20 @@ __global__ __launch_bounds__(256) void qprep_kernel(QPrepArgs a) {
         hp[k] = h;
         lp[k] = (_Float16)(sv - (float)h);
     };
-    for (int j = threadIdx.x; j < d; j += blockDim.x) split(buf[j] * a.q_scale, a.o.qh, a.o.ql, row * d + j);
-    if (m > 0)
-        for (int i = threadIdx.x; i < m; i += blockDim.x) split(pbuf[i], a.o.ph, a.o.pl, row * m + i);
-    if (threadIdx.x == 0) a.o.rowf[row] = __builtin_amdgcn_ldexpf(1.0f, -e);
+    if (tid < D) split(buf[tid] * a.q_scale, a.o.qh, a.o.ql, row * D + tid);
+    if (tid < m) split(p, a.o.ph, a.o.pl, row * m + tid);
+    if (tid == 0) a.o.rowf[row] = __builtin_amdgcn_ldexpf(1.0f, -e);
 }
 
 hipError_t launch_qprep(const QPrepArgs& a, hipStream_t s) {
     if (a.n_rows == 0) return hipSuccess;
-    hipLaunchKernelGGL(qprep_kernel, dim3((unsigned)a.n_rows), dim3(256), 0, s, a);
+    const dim3 grid((unsigned)a.n_rows);
+    switch (a.t.d) {
+        case 64: hipLaunchKernelGGL(qprep_kernel<64>, grid, dim3(256), 0, s, a); break;
+        case 128: hipLaunchKernelGGL(qprep_kernel<128>, grid, dim3(256), 0, s, a); break;
+        case 256: hipLaunchKernelGGL(qprep_kernel<256>, grid, dim3(256), 0, s, a); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
