@@ -35,14 +35,14 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published (the sketch p
 # the kernel's sources are the ones it was measured on (sha256 of the .hip file + shared headers).
 FETCH_UNIT_B, WRITE_UNIT_B = 2048, 1024
 TRAFFIC = {
-    "encode_k": {"fetch": 2097508.5625, "write": 1395892.03125, "src": "encode.hip",
+    "encode_k": {"fetch": 2097508.5, "write": 1395650.5625, "src": "encode.hip",
         "sha": "8f5183252e566100540547dadba46aca3ad0cf8ad58db3cb4b8702c75a4bc2e9"},
-    "encode_v": {"fetch": 2105563.4375, "write": 1090905.40625, "src": "encode.hip",
+    "encode_v": {"fetch": 2105695.9375, "write": 1090859.8125, "src": "encode.hip",
         "sha": "8f5183252e566100540547dadba46aca3ad0cf8ad58db3cb4b8702c75a4bc2e9"},
-    "decode_attention": {"fetch": 1232616.125, "write": 6240.0, "src": "attention.hip",
-        "sha": "3dbc44b6e10d3865cf6738768088b9cbfa4718ea308aff584a85b00b28e9d84f"},
-    "decode_v_bf16": {"fetch": 550379.1875, "write": 4194304.0, "src": "decode.hip",
-        "sha": "2add9ea1fa8cf5d1d37b9846a4505b28cdfa3553557c2e41c88d2f2cc96455e9"},
+    "decode_attention": {"fetch": 1232571.9375, "write": 6240.0625, "src": "attention.hip",
+        "sha": "a0d7922a1484082cb5aa8b4e9bd67acbe3fca051da00a00d62cc92680a26448f"},
+    "decode_v_bf16": {"fetch": 550101.5, "write": 4194304.0, "src": "decode.hip",
+        "sha": "5f0e44244900f247d31af0931f1462ce889761a8182fed30d4330630095b966f"},
 }
 TRAFFIC_HEADERS_SHA = ("6643b4ed6d32e0cc4205551fb1ef8fab74077690c7d82ac29a903d73ebc0d666"   # common.hpp
                        "c79a58581fb18e7686561d680e8fdc2107a0b0d7c4661d9115f2dda2656965da")  # kernels.hpp
