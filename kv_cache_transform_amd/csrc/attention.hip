@@ -400,19 +400,25 @@ void attn_kernel(AttnArgs a) {
     __shared__ uint32_t kvlut[KV ? 2 * 256 * 64 : 1];             // the two tables of 256-byte rows
     __shared__ u32x4 sgn8[QJL ? 256 * 4 : 1];                      // copy c of byte e's ±2^12 halves at e·4 + c
     if constexpr (KV) {
-        const uint32_t* src = reinterpret_cast<const uint32_t*>(a.tk.lut_hl);   // entry e: hi pair, lo pair
-        for (int i = threadIdx.x; i < 2 * 256 * 64; i += blockDim.x) {
-            const int tab = i >> 14, e = (i >> 6) & 255, c = i & 63;
-            uint32_t w;
-            if (tab == 0 && c < 32) {
-                const half2v hv = {(_Float16)a.tv.cent[e & 15], (_Float16)a.tv.cent[e >> 4]};
-                w = __builtin_bit_cast(uint32_t, hv);
-            } else if (tab == 0) {
-                w = src[2 * e];
-            } else {
-                w = c < 32 ? src[2 * e + 1] : 0u;
+        // a straight copy of the prebuilt images in 16-byte pieces: a piece of table 0 in words
+        // 0-31 of its row (piece index % 16 < 8) holds value pairs, all else comes from the K codec
+        const u32x4* kimg = reinterpret_cast<const u32x4*>(a.tk.attn_img);
+        const u32x4* vimg = reinterpret_cast<const u32x4*>(a.tv.attn_img);
+        u32x4* dst = reinterpret_cast<u32x4*>(kvlut);
+        // four pieces per round trip (8192 pieces)
+        const int nt = (int)blockDim.x;
+        for (int i = threadIdx.x; i < 2 * 256 * 64 / 4; i += 4 * nt) {
+            u32x4 w[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int k = i + u * nt;
+                if (k < 2 * 256 * 64 / 4) w[u] = ((k >> 12) == 0 && (k & 15) < 8 ? vimg : kimg)[k];
             }
-            kvlut[i] = w;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int k = i + u * nt;
+                if (k < 2 * 256 * 64 / 4) dst[k] = w[u];
+            }
         }
     } else {
         const uint16_t* src = reinterpret_cast<const uint16_t*>(a.tk.lut_hl);

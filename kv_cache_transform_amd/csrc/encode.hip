@@ -105,11 +105,68 @@ void encode_kernel(EncodeArgs a) {
     const int rl = a.grid_rep_log2;
     const int ngw = FQ ? 0 : (2 * (G + 3)) << rl;
     if constexpr (FQ) {
-        for (int i = threadIdx.x; i < 128 * 64; i += blockDim.x) ldsw[i] = a.t.fq_grid[i >> 6];
+        // every global load of the staging (grid entries, centroids, S with the Gaussian sketch,
+        // m <= 128 here) is issued before any LDS store, with compile-time trip counts, so the
+        // prologue waits on memory once rather than once per loop iteration
+        constexpr int NTH = 64 * NWV;
+        constexpr int NGI = (128 * 64 + NTH - 1) / NTH;
+        constexpr int NCE = 2 * (1 << B) * 64;                 // centroid-row words
+        constexpr int NCI = QJL ? (NCE + NTH - 1) / NTH : 1;
+        constexpr int NSI = QJL ? (128 * D / 8 + NTH - 1) / NTH : 1;
+        const int tid = (int)threadIdx.x;
+        uint32_t gv[NGI], cv[NCI];
+        u32x4 sv[NSI];
+#pragma unroll
+        for (int j = 0; j < NGI; ++j) {
+            const int i = tid + j * NTH;
+            gv[j] = a.t.fq_grid[(i < 128 * 64 ? i : 0) >> 6];
+        }
+        const bool gauss = QJL && a.t.sketch != 1;
+        const int n16 = QJL ? m * D / 8 : 0;                  // 16-byte pieces of S
         if constexpr (QJL) {
-            for (int i = threadIdx.x; i < 2 * (1 << B) * 64; i += blockDim.x) {
-                const int r2 = i >> 6, idx = r2 >> 1, row = idx * FL::R + ((r2 & 1) ? FL::R - 1 : 0);
-                ldsw[(FL::W + row * 256) / 4 + (i & 63)] = f2u(a.t.cent_x1024[idx]);
+#pragma unroll
+            for (int j = 0; j < NCI; ++j) {
+                const int i = tid + j * NTH;
+                cv[j] = f2u(a.t.cent_x1024[i < NCE ? (i >> 7) : 0]);
+            }
+            if (gauss) {
+                const u32x4* src = reinterpret_cast<const u32x4*>(a.t.S + (int64_t)head * m * D);
+#pragma unroll
+                for (int j = 0; j < NSI; ++j) {
+                    const int i = tid + j * NTH;
+                    if (i < n16) sv[j] = src[i];
+                }
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NGI; ++j) {
+            const int i = tid + j * NTH;
+            if (i < 128 * 64) ldsw[i] = gv[j];
+        }
+        if constexpr (QJL) {
+#pragma unroll
+            for (int j = 0; j < NCI; ++j) {
+                const int i = tid + j * NTH;
+                if (i < NCE) {
+                    const int r2 = i >> 6, idx = r2 >> 1, row = idx * FL::R + ((r2 & 1) ? FL::R - 1 : 0);
+                    ldsw[(FL::W + row * 256) / 4 + (i & 63)] = cv[j];
+                }
+            }
+            if (gauss) {
+                // S in the order the MFMA A operand reads it (see the sketch loop): lane l = rho +
+                // 16 gp reads row (rho/4)(m/4) + 4 tau + rho%4, columns gp C + 8k .. +8
+                const int mq = m >> 2;
+#pragma unroll
+                for (int j = 0; j < NSI; ++j) {
+                    const int i = tid + j * NTH;
+                    if (i < n16) {
+                        const int row = i / (D / 8), col = i - row * (D / 8);
+                        const int q = row / mq, rem = row - q * mq;
+                        const int tau = rem >> 2, rh = 4 * q + (rem & 3);
+                        const int gp = col / KS, k = col - gp * KS;
+                        *reinterpret_cast<u32x4*>(ldsb + FL::piece(2 * (D / 32) + tau * KS + k) + 16 * (rh + 16 * gp)) = sv[j];
+                    }
+                }
             }
         }
     } else {
@@ -128,7 +185,7 @@ void encode_kernel(EncodeArgs a) {
     if constexpr (QJL) {
         if constexpr (!FQ)
             for (int i = threadIdx.x; i < L; i += blockDim.x) lds_c[i] = a.t.cent_x1024[i];
-        if (S_LDS && !(BF16 && a.t.sketch == 1)) {
+        if (!FQ && S_LDS && !(BF16 && a.t.sketch == 1)) {
             // S in the order the MFMA A operand reads it (see the sketch loop): the 16-byte piece
             // of lane l for row tile tau and k-step k sits at piece index (tau KS + k) 64 + l, so
             // every A read is one contiguous 1 KiB wave access.  Lane l = rho + 16 gp reads row
@@ -142,10 +199,7 @@ void encode_kernel(EncodeArgs a) {
                 const int q = row / mq, rem = row - q * mq;
                 const int tau = rem >> 2, rh = 4 * q + (rem & 3);
                 const int gp = col / KS, k = col - gp * KS;
-                if constexpr (FQ)
-                    *reinterpret_cast<u32x4*>(ldsb + FL::piece(2 * NKB + tau * KS + k) + 16 * (rh + 16 * gp)) = src[i];
-                else
-                    dst[(tau * KS + k) * 64 + rh + 16 * gp] = src[i];
+                dst[(tau * KS + k) * 64 + rh + 16 * gp] = src[i];
             }
         }
     }

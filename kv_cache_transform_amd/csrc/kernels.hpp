@@ -19,6 +19,11 @@ struct DevTables {
     const float* lut_f32 = nullptr;    // dequant LUT: 2^(P b) entries of P fp32 (P = lut_group(b))
     const _Float16* lut_f16 = nullptr; // same in fp16
     const _Float16* lut_hl = nullptr;  // per entry: P fp16 hi parts, then P fp16 lo parts of 2^12 x centroid
+    // b = 4: the decode-attention's two LDS tables of 256-byte rows (2 x 256 x 64 words) as this
+    // codec fills them: row e of table 0 = [fp16 value pair (c[e & 15], c[e >> 4]) x 32 | key hi
+    // pair of byte e x 32], row e of table 1 = [key lo pair x 32 | zeros]; the kernel takes the
+    // value words from the V codec's image and the rest from the K codec's; else null
+    const uint32_t* attn_img = nullptr;
     const float* signs_slot = nullptr; // [head][4][d/4] ±1 of coordinate in_coord(d, s, g)
     const float* signs = nullptr;      // [head][d] ±1
     const float* signs2 = nullptr;     // [head][d] ±1 second signs of the RHT sketch (sketch = RHT only)

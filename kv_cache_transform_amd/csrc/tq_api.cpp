@@ -142,6 +142,23 @@ int build_tables(const tq_params* p, int device, DevTables* out) {  // caller ho
     const int64_t o_sg = blob.add(signs.data(), signs.size() * 4);
     const int64_t o_S = m > 0 ? blob.add(S.data(), S.size() * 2) : 0;
     const int64_t o_s2 = rht ? blob.add(signs2.data(), signs2.size() * 4) : 0;
+    // the decode-attention's 4-bit table image (see DevTables::attn_img): byte e packs the
+    // coordinates (e & 15, e >> 4), P = 2 per LUT entry, so the key pairs are lut_hl's words 2e, 2e + 1
+    std::vector<uint32_t> img(b == 4 ? (size_t)2 * 256 * 64 : 0);
+    if (b == 4) {
+        for (int e = 0; e < 256; ++e) {
+            const uint32_t vp = (uint32_t)lut16[(size_t)e * 2] | ((uint32_t)lut16[(size_t)e * 2 + 1] << 16);
+            const uint32_t kh = (uint32_t)luthl[(size_t)e * 4] | ((uint32_t)luthl[(size_t)e * 4 + 1] << 16);
+            const uint32_t kl = (uint32_t)luthl[(size_t)e * 4 + 2] | ((uint32_t)luthl[(size_t)e * 4 + 3] << 16);
+            for (int c = 0; c < 32; ++c) {
+                img[(size_t)e * 64 + c] = vp;
+                img[(size_t)e * 64 + 32 + c] = kh;
+                img[(size_t)(256 + e) * 64 + c] = kl;
+                img[(size_t)(256 + e) * 64 + 32 + c] = 0u;
+            }
+        }
+    }
+    const int64_t o_img = b == 4 ? blob.add(img.data(), img.size() * 4) : 0;
 
     void* dev = nullptr;
     if (hipMalloc(&dev, blob.host.size()) != hipSuccess) return TQ_EHIP;
@@ -164,6 +181,7 @@ int build_tables(const tq_params* p, int device, DevTables* out) {  // caller ho
     t.signs = reinterpret_cast<const float*>(base + o_sg);
     t.S = m > 0 ? reinterpret_cast<const _Float16*>(base + o_S) : nullptr;
     t.signs2 = rht ? reinterpret_cast<const float*>(base + o_s2) : nullptr;
+    t.attn_img = b == 4 ? reinterpret_cast<const uint32_t*>(base + o_img) : nullptr;
     t.blob = dev;
     (void)device;
     *out = t;
