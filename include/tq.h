@@ -106,6 +106,20 @@ int tq_encode_append(const tq_params* p, const void* x, tq_dtype x_dtype, int64_
 int tq_encode(const tq_params* p, const void* x, tq_dtype x_dtype, int64_t n_streams,
               int64_t n_tokens, void* packed, void* stream);
 
+/* Encode the keys k and the values v of the same tokens, both [n_streams][n_tokens][d] of x_dtype,
+ * into packed_k (layout of pk) and packed_v (layout of pv): the same records, byte for byte, as
+ * tq_encode(pk, k, ...) followed by tq_encode(pv, v, ...) ("Ablation...", §2 TurboQuant: every key
+ * and value vector of the cache is encoded).  For bf16 input with the same d <= 128 and b <= 4 on
+ * both sides, the Walsh-Hadamard rotation, no value sketch and a key sketch that fits the kernel's
+ * tables (Gaussian with m <= 128, or randomized Hadamard), one launch encodes both: each wave takes
+ * a group of keys and then the values of the same tokens, so the value stream's HBM traffic runs
+ * while the key sketch holds the vector units.  Otherwise the two encodes run one after the other
+ * on `stream`.  The caller owns every buffer.  Errors: those of tq_encode for either side, checked
+ * before any launch. */
+int tq_encode_kv(const tq_params* pk, const tq_params* pv, const void* k, const void* v,
+                 tq_dtype x_dtype, int64_t n_streams, int64_t n_tokens, void* packed_k,
+                 void* packed_v, void* stream);
+
 /* Decode the MSE reconstruction x̂ = n16 · s ⊙ (H c[idx]) / sqrt(d) into x_hat
  * [n_streams][n_tokens][d] (F32 or BF16).  The QJL sketch is not applied. */
 int tq_decode(const tq_params* p, const void* packed, int64_t n_streams, int64_t n_tokens,

@@ -70,6 +70,30 @@ def encode(codec: Codec, x: torch.Tensor, out: torch.Tensor | None = None) -> to
     return out
 
 
+def encode_kv(ck: Codec, cv: Codec, k: torch.Tensor, v: torch.Tensor, out_k: torch.Tensor | None = None,
+              out_v: torch.Tensor | None = None):
+    """Keys and values of the same tokens (tq_encode_kv): k, v [n_streams, n_tokens, d] of one dtype
+    on the GPU -> (packed K, packed V), the same bytes as encode(ck, k) and encode(cv, v)."""
+    for x, c in ((k, ck), (v, cv)):
+        if x.dim() != 3 or x.shape[-1] != c.d or not x.is_contiguous():
+            raise ValueError("k and v must be contiguous [n_streams, n_tokens, d] tensors")
+    if k.shape[:2] != v.shape[:2] or k.dtype != v.dtype:
+        raise ValueError("k and v must have the same streams, tokens and dtype")
+    S, N, _ = k.shape
+    outs = []
+    for c, o in ((ck, out_k), (cv, out_v)):
+        need = get_layout(c, S, N)["total_bytes"]
+        if o is None:
+            o = torch.empty(need, dtype=torch.uint8, device=k.device)
+        elif o.numel() < need or o.dtype != torch.uint8:
+            raise ValueError("packed buffer too small")
+        outs.append(o)
+    _lib.check(_lib.lib().tq_encode_kv(ctypes.byref(ck.params()), ctypes.byref(cv.params()), _ptr(k), _ptr(v),
+                                       _DT[k.dtype], S, N, _ptr(outs[0]), _ptr(outs[1]), _stream(k.device)),
+               "tq_encode_kv")
+    return outs[0], outs[1]
+
+
 def encode_append(codec: Codec, x: torch.Tensor, packed: torch.Tensor, capacity: int, t0: int) -> torch.Tensor:
     """x: [n_streams, n_new, d] -> tokens [t0, t0 + n_new) of `packed`, a buffer laid out for
     n_streams x capacity tokens (get_layout(codec, n_streams, capacity))."""

@@ -56,7 +56,11 @@ __global__ __launch_bounds__(256, (D == 256 && B == 6 && !OUT_BF16) || QJL ? 1 :
             lut[2 * i + 1] = a.t.lut_hl[i * 2 * PG + PG];
         }
     } else {
-        for (int i = threadIdx.x; i < NE * P * 2; i += blockDim.x) lut[i] = a.t.lut_hl[i];
+        // 16-byte pieces (the table is a multiple of 8 halves for every b; the device table is 256-byte
+        // aligned), so the copy waits on memory once per 4 KiB rather than per 512 bytes
+        static_assert((NE * P * 2) % 8 == 0, "whole 16-byte pieces");
+        const u32x4* src = reinterpret_cast<const u32x4*>(a.t.lut_hl);
+        for (int i = threadIdx.x; i < NE * P * 2 / 8; i += blockDim.x) reinterpret_cast<u32x4*>(lut)[i] = src[i];
     }
     // block = one stream's tile range; waves take every NWAVES-th tile
     const int64_t st = blockIdx.x / a.blocks_per_stream;

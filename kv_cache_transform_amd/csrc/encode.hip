@@ -643,6 +643,406 @@ static int blocks_per_cu(const void* k, size_t lds, int threads) {
     return n;
 }
 
+// ---------------------------------------------------------------------------------------------
+// Keys and values of the same tokens in one launch (bf16 input, the same d <= 128 and b <= 4 for
+// both, so one codebook and one binade grid; values without a sketch).  The QJL key encode is bound
+// by VALU issue (the quantiser's chain per coordinate plus the sketch products) while the value
+// encode is bound by HBM, so each wave encodes the key group and then the value group of the same
+// 16 tokens: the values' loads and stores stream while the keys' arithmetic holds the SIMD.  The
+// arithmetic per vector is the single-tensor binade-grid kernel's, step for step, so the records
+// are identical to two separate encodes.  LDS: the shared grid, the keys' centroid rows, then in
+// the window pieces the keys' signed Hadamard tiles, their S (or randomized Hadamard tiles) and
+// the values' signed Hadamard tiles.
+
+// one tensor's buffers over the block's stream (as in the binade-grid kernel: each exactly as long
+// as the stream's part, so a lane past the last token reads zeros and its stores are dropped)
+struct FqBufs {
+    __amdgpu_buffer_rsrc_t rx, rid, rnm, rsk, rrn;
+};
+
+// One 16-vector group of one tensor: w holds the lane's raw bf16 words of tile t and receives the
+// loads of tile t_next (issued as soon as w is consumed; skipped when t_next >= tb1).  pA is the
+// first window piece of the tensor's signed Hadamard tiles, pS that of its S / randomized tiles.
+template <int D, int B, bool QJL>
+__device__ __forceinline__ void fq_encode_group(const uint8_t* ldsb, int pA, int pS, bool rht, int m, const FqBufs& R,
+                                                uint32_t (&w)[D / 8], int64_t t, int64_t t_next, int64_t tb1,
+                                                int64_t n_tokens, int lane) {
+    using FL = FqLayout<B>;
+    constexpr int C = D / 4, NKB = D / 32, KS = D / 32;
+    constexpr int NW = (C * B + 31) / 32, CB = C * B / 8, CA = cmin(pow2_align(CB), 16);
+    constexpr float kInvSqrtD = D == 64 ? 0.125f : 0.08838834764831845f;
+    const int v = lane & 15, g = lane >> 4;
+    const uint32_t lane4 = 4u * (uint32_t)lane;
+    const int64_t tok = t * 16 + v;
+    const bool valid = t < tb1 && tok < n_tokens;
+    const uint32_t tk = (uint32_t)tok;
+
+    // sign flip + 32-point block on bf16 MFMA, then the middle bits in registers; the norm
+    float x[C];
+    float n2 = 0.0f;
+#pragma unroll
+    for (int k = 0; k < C / 2; ++k) {
+        const bf16x2 wv = __builtin_bit_cast(bf16x2, w[k]);
+        n2 = __builtin_amdgcn_fdot2_f32_bf16(wv, wv, n2, false);
+    }
+#pragma unroll
+    for (int kb = 0; kb < NKB; ++kb) {
+        const bf16x8 Bv = __builtin_bit_cast(bf16x8, u32x4{w[4 * kb], w[4 * kb + 1], w[4 * kb + 2], w[4 * kb + 3]});
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const u32x4 At = *reinterpret_cast<const u32x4*>(ldsb + FL::piece(pA + h * NKB + kb) + 16 * lane);
+            const floatx4 r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, At), Bv,
+                                                                     floatx4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x[8 * kb + 4 * h + i] = r[i];
+        }
+    }
+#pragma unroll
+    for (int k = 0; k < D / 8; ++k) asm volatile("" ::"v"(w[k]) : "memory");
+    asm volatile("" ::"v"(n2) : "memory");
+    if (t_next < tb1) bload<2 * C, 16>(R.rx, (uint32_t)(t_next * 16 + v) * (2 * D) + 2 * g * C, 0u, w);
+    fwht_slots<C, 8>(x);
+    n2 = sum4(n2);
+    float n, sc;
+    if (n2 >= 0x1p-126f) {
+        n = __builtin_amdgcn_sqrtf(n2);
+        sc = kInvSqrtD * __builtin_amdgcn_rsqf(n2);
+    } else {
+        n = sqrtf(n2);
+        sc = n > 0.0f ? kInvSqrtD / n : 0.0f;
+    }
+    const float sE = sc * 16384.0f;
+
+    // quantise + pack (slots in descending order, so alignbit leaves the lowest slot in the low bits)
+    uint32_t pk[NW];
+#pragma unroll
+    for (int k = 0; k < NW; ++k) pk[k] = 0u;
+    float e2 = 0.0f;
+    const float sU = sc * (float)kFqKappa;
+#pragma unroll
+    for (int s = C - 1; s >= 0; --s) {
+        const float u = fmaf(x[s], sU, 3.0f);
+        const uint32_t ga = __builtin_amdgcn_perm(f2u(u), lane4, 0x0c0c0600u);
+        const uint32_t wq = f2u(u) + *reinterpret_cast<const uint32_t*>(ldsb + ga);
+        if constexpr (B == 3) put_bits<B>(pk, s * B, wq >> 29);
+        else pk[(s * B) >> 5] = __builtin_amdgcn_alignbit(pk[(s * B) >> 5], wq, 32 - B);
+        if constexpr (QJL) {
+            const uint32_t ca = __builtin_amdgcn_perm(wq, lane4, 0x0c0c0700u);
+            x[s] = fmaf(x[s], sE, -*reinterpret_cast<const float*>(ldsb + FL::W + ca));
+            e2 = fmaf(x[s], x[s], e2);
+        }
+    }
+    if (valid) {
+        bstore<CB, CA>(R.rid, tk * (D * B / 8) + g * CB, 0u, pk);
+        if (g == 0) __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)n), R.rnm, tk * 2u, 0u, 0);
+    }
+    if constexpr (QJL) {
+        // the residual 2^14 e as fp16 hi (truncated) + lo parts: the B operands of S·e
+        half8 bh[C / 8], bl[C / 8];
+#pragma unroll
+        for (int k = 0; k < C / 8; ++k) {
+            u32x4 hv, lv;
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float e0 = x[8 * k + 2 * u], e1 = x[8 * k + 2 * u + 1];
+                const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(e0, e1));
+                hv[u] = h;
+                lv[u] = sub_f16pair_from_f32(h, e0, e1);
+            }
+            bh[k] = __builtin_bit_cast(half8, hv);
+            bl[k] = __builtin_bit_cast(half8, lv);
+        }
+        if (rht) {
+            // z = H (e ⊙ s2): the 32-point block with the s2 tiles on fp16 MFMA, hi then lo parts, and
+            // the middle bits; slot p of part g is sketch row g C + p (one byte per 8 slots, inverted)
+            float z[C];
+#pragma unroll
+            for (int kb = 0; kb < NKB; ++kb)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) {
+                    const half8 A = __builtin_bit_cast(half8, *reinterpret_cast<const u32x4*>(ldsb + FL::piece(pS + h * NKB + kb) + 16 * lane));
+                    floatx4 r = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bh[kb], floatx4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
+                    r = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bl[kb], r, 0, 0, 0);
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) z[8 * kb + 4 * h + i] = r[i];
+                }
+            fwht_slots<C, 8>(z);
+#pragma unroll
+            for (int wd = 0; wd < (C + 31) / 32; ++wd) {
+                constexpr int NBY = C < 32 ? C / 8 : 4;
+                uint32_t by[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+                for (int j = 0; j < NBY; ++j)
+#pragma unroll
+                    for (int p = 8 * j + 7; p >= 8 * j; --p) by[j] = __builtin_amdgcn_alignbit(by[j], f2u(z[32 * wd + p]), 31);
+                const uint32_t bw = ~((((by[3] << 8) | by[2]) << 16) | ((by[1] << 8) | by[0]));
+                if (valid) {
+                    const uint32_t o = tk * (D / 8) + g * (C / 8) + 4 * wd;
+                    if constexpr (NBY == 4) __builtin_amdgcn_raw_buffer_store_b32(bw, R.rsk, o, 0u, 0);
+                    else __builtin_amdgcn_raw_buffer_store_b16((uint16_t)bw, R.rsk, o, 0u, 0);
+                }
+            }
+        } else {
+            // Gaussian S (m <= 128: one sketch word per lane part, rows [g m/4, (g+1) m/4)); the products
+            // run k-step outer and row tile inner, and the S reads are issued ahead of their MFMAs
+            auto word = [&](int nt, auto full) {
+                constexpr bool FULL = decltype(full)::value;
+                uint32_t by[4];
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    floatx4 acc[4];
+#pragma unroll
+                    for (int tl = 0; tl < 4; ++tl) acc[tl] = floatx4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+                    for (int k = 0; k < KS; ++k)
+#pragma unroll
+                        for (int tl = 0; tl < 4; ++tl) {
+                            const int tt = 4 * hf + tl;
+                            if (FULL || tt < nt) {
+                                const half8 A = *reinterpret_cast<const half8*>(ldsb + FL::piece(pS + tt * KS + k) + 16 * lane);
+                                acc[tl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bh[k], acc[tl], 0, 0, 0);
+                                acc[tl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bl[k], acc[tl], 0, 0, 0);
+                            }
+                        }
+#pragma unroll
+                    for (int j = 2 * hf; j < 2 * hf + 2; ++j) {
+                        by[j] = 0u;
+#pragma unroll
+                        for (int tt = 2 * j + 1; tt >= 2 * j; --tt)
+                            if (FULL || tt < nt)
+#pragma unroll
+                                for (int i = 3; i >= 0; --i)
+                                    by[j] = __builtin_amdgcn_alignbit(by[j], f2u(acc[tt - 4 * hf][i]), 31);
+                    }
+                }
+                if constexpr (FULL) {
+                    constexpr int kPD = 4;
+                    __builtin_amdgcn_sched_group_barrier(0x100, kPD, 0);
+#pragma unroll
+                    for (int p = 0; p < 8 * KS; ++p) {
+                        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+                        if (p + kPD < 8 * KS) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+                    }
+                }
+                const int nb = FULL ? 4 : (nt >> 1);
+                const uint32_t bw = ~((((by[3] << 8) | by[2]) << 16) | ((by[1] << 8) | by[0]));
+                if (valid) {
+                    const uint32_t o = tk * (uint32_t)(m / 8) + (uint32_t)(g * (m / 32));
+                    if (FULL && (m & 127) == 0) __builtin_amdgcn_raw_buffer_store_b32(bw, R.rsk, o, 0u, 0);
+                    else if (nb == 2 && (m & 63) == 0) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)bw, R.rsk, o, 0u, 0);
+                    else for (int q = 0; q < nb; ++q) __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(bw >> (8 * q)), R.rsk, o + q, 0u, 0);
+                }
+            };
+            const int nbits = m >> 2;
+            if (nbits == 32) word(8, std::true_type{});
+            else word(nbits >> 2, std::false_type{});
+        }
+        const float e2s = sum4(e2);
+        if (valid && g == 0) {
+            const _Float16 r16 = (_Float16)(sqrtf(e2s) * (1.0f / 16384.0f));
+            __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, r16), R.rrn, tk * 2u, 0u, 0);
+        }
+    }
+}
+
+// LDS pieces of the signed Hadamard tiles of one head's signs (bf16 ±1, the 32-point block's A
+// operand, as the binade-grid kernel builds them) at pieces pA .. pA + 2 D/32 - 1; `second` builds
+// the randomized-Hadamard tiles instead (s2, fp16 ±1)
+template <int D, int B>
+__device__ __forceinline__ void fq_stage_hadamard(uint8_t* ldsb, int pA, const float* signs, bool second, int tid, int nth) {
+    using FL = FqLayout<B>;
+    constexpr int C = D / 4, NKB = D / 32;
+    for (int e = tid; e < 2 * NKB * 64; e += nth) {
+        const int l = e & 63, tile = e >> 6, h = tile / NKB, kb = tile - h * NKB;
+        const int lg = l >> 4, mi = l & 3, mg = (l >> 2) & 3;
+        const float* sh = signs + lg * C + 8 * kb;
+        const uint32_t one = second ? 0x3c00u : 0x3f80u;   // fp16 / bf16 +1
+        u32x4 wv;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            uint32_t w2 = 0u;
+#pragma unroll
+            for (int q = 0; q < 2; ++q) {
+                const int jj = 2 * t + q;
+                const uint32_t par = (uint32_t)((__builtin_popcount(mi & jj & 3) + h * (jj >> 2) +
+                                                 __builtin_popcount(mg & lg)) & 1) ^ (f2u(sh[jj]) >> 31);
+                w2 |= (one | (par << 15)) << (16 * q);
+            }
+            wv[t] = w2;
+        }
+        *reinterpret_cast<u32x4*>(ldsb + FL::piece(pA + tile) + 16 * l) = wv;
+    }
+}
+
+template <int D, int B, bool QJL>
+__global__ __launch_bounds__(768, 1) void encode_kv_kernel(EncodeArgs ak, EncodeArgs av) {
+    using FL = FqLayout<B>;
+    constexpr int NWV = 12, NTH = 64 * NWV;
+    constexpr int C = D / 4, NKB = D / 32;
+    static_assert(B <= 4 && D <= 128, "the binade grid serves b <= 4; the fused launch d <= 128");
+    __shared__ __attribute__((aligned(16))) uint32_t fq_lds[fq_lds_bytes<D, B, QJL>() / 4];
+    uint8_t* const ldsb = reinterpret_cast<uint8_t*>(fq_lds);
+    uint32_t* const ldsw = fq_lds;
+
+    const int64_t st = blockIdx.x / ak.blocks_per_stream;
+    const int64_t sub = blockIdx.x - st * ak.blocks_per_stream;
+    const int64_t tb0 = sub * ak.tiles_per_block;
+    const int64_t tb1 = tb0 + ak.tiles_per_block < ak.tiles_per_stream ? tb0 + ak.tiles_per_block : ak.tiles_per_stream;
+    const int hk = (int)(st % ak.t.n_heads), hv = (int)(st % av.t.n_heads);
+    const int m = QJL ? ak.t.m : 0;
+    const bool rht = QJL && ak.t.sketch == 1;
+    const int nS = !QJL ? 0 : (rht ? 2 * NKB : m * D / 512);     // window pieces of S / the RHT tiles
+    const int pSk = 2 * NKB, pAv = 2 * NKB + nS;
+    const int tid = (int)threadIdx.x;
+
+    // staging (as the binade-grid kernel): every global load of the grid, centroid and S copies is
+    // issued before any LDS store
+    {
+        constexpr int NGI = (128 * 64 + NTH - 1) / NTH;
+        constexpr int NCE = 2 * (1 << B) * 64;
+        constexpr int NCI = QJL ? (NCE + NTH - 1) / NTH : 1;
+        constexpr int NSI = QJL ? (128 * D / 8 + NTH - 1) / NTH : 1;
+        uint32_t gv[NGI], cv[NCI];
+        u32x4 sv[NSI];
+#pragma unroll
+        for (int j = 0; j < NGI; ++j) {
+            const int i = tid + j * NTH;
+            gv[j] = ak.t.fq_grid[(i < 128 * 64 ? i : 0) >> 6];
+        }
+        const int n16 = QJL && !rht ? m * D / 8 : 0;
+        if constexpr (QJL) {
+#pragma unroll
+            for (int j = 0; j < NCI; ++j) {
+                const int i = tid + j * NTH;
+                cv[j] = f2u(ak.t.cent_x1024[i < NCE ? (i >> 7) : 0]);
+            }
+            const u32x4* src = reinterpret_cast<const u32x4*>(ak.t.S + (int64_t)hk * m * D);
+#pragma unroll
+            for (int j = 0; j < NSI; ++j) {
+                const int i = tid + j * NTH;
+                if (i < n16) sv[j] = src[i];
+            }
+        }
+#pragma unroll
+        for (int j = 0; j < NGI; ++j) {
+            const int i = tid + j * NTH;
+            if (i < 128 * 64) ldsw[i] = gv[j];
+        }
+        if constexpr (QJL) {
+#pragma unroll
+            for (int j = 0; j < NCI; ++j) {
+                const int i = tid + j * NTH;
+                if (i < NCE) {
+                    const int r2 = i >> 6, idx = r2 >> 1, row = idx * FL::R + ((r2 & 1) ? FL::R - 1 : 0);
+                    ldsw[(FL::W + row * 256) / 4 + (i & 63)] = cv[j];
+                }
+            }
+            const int mq = m >> 2, KS = D / 32;
+#pragma unroll
+            for (int j = 0; j < NSI; ++j) {
+                const int i = tid + j * NTH;
+                if (i < n16) {
+                    const int row = i / (D / 8), col = i - row * (D / 8);
+                    const int q = row / mq, rem = row - q * mq;
+                    const int tau = rem >> 2, rh = 4 * q + (rem & 3);
+                    const int gp = col / KS, k = col - gp * KS;
+                    *reinterpret_cast<u32x4*>(ldsb + FL::piece(pSk + tau * KS + k) + 16 * (rh + 16 * gp)) = sv[j];
+                }
+            }
+        }
+    }
+    fq_stage_hadamard<D, B>(ldsb, 0, ak.t.signs + (int64_t)hk * D, false, tid, NTH);
+    if (rht) fq_stage_hadamard<D, B>(ldsb, pSk, ak.t.signs2 + (int64_t)hk * D, true, tid, NTH);
+    fq_stage_hadamard<D, B>(ldsb, pAv, av.t.signs + (int64_t)hv * D, false, tid, NTH);
+    __syncthreads();
+
+    const int lane = tid & 63;
+    const int v = lane & 15, g = lane >> 4;
+    const int wave = wave_id();
+    auto bufs = [&](const EncodeArgs& a, bool qjl) {
+        FqBufs R;
+        const int64_t rec0 = st * a.cap + a.t0;
+        R.rx = buffer_rsrc(reinterpret_cast<const uint8_t*>(a.x) + st * a.n_tokens * (int64_t)(2 * D), (int)(a.n_tokens * 2 * D));
+        R.rid = buffer_rsrc(a.packed + a.off_idx + rec0 * (int64_t)(D * B / 8), (int)(a.n_tokens * (D * B / 8)));
+        R.rnm = buffer_rsrc(a.packed + a.off_norm + rec0 * 2, (int)(a.n_tokens * 2));
+        R.rsk = R.rrn = R.rnm;
+        if (qjl) {
+            R.rsk = buffer_rsrc(a.packed + a.off_sketch + rec0 * (int64_t)(a.t.m / 8), (int)(a.n_tokens * (a.t.m / 8)));
+            R.rrn = buffer_rsrc(a.packed + a.off_rnorm + rec0 * 2, (int)(a.n_tokens * 2));
+        }
+        return R;
+    };
+    const FqBufs RK = bufs(ak, QJL), RV = bufs(av, false);
+    uint32_t wk[D / 8], wv[D / 8];
+    const int64_t t_first = tb0 + wave;
+    bload<2 * C, 16>(RK.rx, (uint32_t)(t_first * 16 + v) * (2 * D) + 2 * g * C, 0u, wk);
+    bload<2 * C, 16>(RV.rx, (uint32_t)(t_first * 16 + v) * (2 * D) + 2 * g * C, 0u, wv);
+#pragma unroll 1
+    for (int64_t t = t_first; t < tb1; t += NWV) {
+        asm volatile("" ::: "memory");
+        fq_encode_group<D, B, QJL>(ldsb, 0, pSk, rht, m, RK, wk, t, t + NWV, tb1, ak.n_tokens, lane);
+        fq_encode_group<D, B, false>(ldsb, pAv, 0, false, 0, RV, wv, t, t + NWV, tb1, av.n_tokens, lane);
+    }
+}
+
+// whether the fused key + value launch serves this pair (the binade grid for both, the same d,
+// b and rotation with the WHT, one codebook, values without a sketch, the keys' tables within the
+// window pieces)
+template <int D, int B>
+static bool fq_kv_fits(const EncodeArgs& ak, const EncodeArgs& av) {
+    if (ak.t.fq_grid == nullptr || av.t.fq_grid == nullptr || ak.t.rotation != 0 || av.t.rotation != 0) return false;
+    if (av.t.m != 0) return false;
+    const int64_t lim = (int64_t)1 << 31;
+    if (ak.n_tokens * 2 * D >= lim || ak.n_tokens * (D * B / 8) >= lim) return false;
+    constexpr int nA = 2 * (D / 32);
+    int nS = 0;
+    if (ak.t.m > 0) {
+        const bool rht = ak.t.sketch == 1;
+        if (!rht && (ak.t.m > 128 || (ak.t.m * D) % 512 != 0)) return false;
+        nS = rht ? nA : ak.t.m * D / 512;
+    }
+    return 2 * nA + nS <= FqLayout<B>::cap;
+}
+
+template <int D, int B>
+static hipError_t launch_kv_db(const EncodeArgs& ak, const EncodeArgs& av, int num_cus, hipStream_t s, bool* fused) {
+    *fused = false;
+    if (!fq_kv_fits<D, B>(ak, av)) return hipSuccess;
+    *fused = true;
+    EncodeArgs k = ak, v = av;
+    const bool qjl = ak.t.m > 0;
+    const void* kern = qjl ? reinterpret_cast<const void*>(&encode_kv_kernel<D, B, true>)
+                           : reinterpret_cast<const void*>(&encode_kv_kernel<D, B, false>);
+    const int64_t target = (int64_t)num_cus * blocks_per_cu(kern, 0, 768);
+    int64_t bps = (target + ak.n_streams - 1) / ak.n_streams;
+    if (bps > ak.tiles_per_stream) bps = ak.tiles_per_stream;
+    if (bps < 1) bps = 1;
+    k.blocks_per_stream = v.blocks_per_stream = bps;
+    k.tiles_per_block = v.tiles_per_block = (ak.tiles_per_stream + bps - 1) / bps;
+    const dim3 grid((unsigned)(ak.n_streams * bps));
+    if (qjl) hipLaunchKernelGGL((encode_kv_kernel<D, B, true>), grid, dim3(768), 0, s, k, v);
+    else hipLaunchKernelGGL((encode_kv_kernel<D, B, false>), grid, dim3(768), 0, s, k, v);
+    return hipGetLastError();
+}
+
+// keys and values of the same tokens in one launch where fq_kv_fits holds (*fused = true); else
+// nothing is launched and *fused = false (the caller encodes the two tensors apart)
+hipError_t launch_encode_kv(const EncodeArgs& ak, const EncodeArgs& av, int num_cus, hipStream_t s, bool* fused) {
+    *fused = false;
+    if (ak.t.d != av.t.d || ak.t.b != av.t.b || ak.n_streams != av.n_streams || ak.n_tokens != av.n_tokens) return hipSuccess;
+    switch (ak.t.d * 16 + ak.t.b) {
+        case 64 * 16 + 1: return launch_kv_db<64, 1>(ak, av, num_cus, s, fused);
+        case 64 * 16 + 2: return launch_kv_db<64, 2>(ak, av, num_cus, s, fused);
+        case 64 * 16 + 3: return launch_kv_db<64, 3>(ak, av, num_cus, s, fused);
+        case 64 * 16 + 4: return launch_kv_db<64, 4>(ak, av, num_cus, s, fused);
+        case 128 * 16 + 1: return launch_kv_db<128, 1>(ak, av, num_cus, s, fused);
+        case 128 * 16 + 2: return launch_kv_db<128, 2>(ak, av, num_cus, s, fused);
+        case 128 * 16 + 3: return launch_kv_db<128, 3>(ak, av, num_cus, s, fused);
+        case 128 * 16 + 4: return launch_kv_db<128, 4>(ak, av, num_cus, s, fused);
+    }
+    return hipSuccess;
+}
+
 // binade-grid launch: bf16 input, b <= 4, the table built for this codebook, and the Hadamard
 // tiles plus S (or the randomized Hadamard tiles) within the pieces of the centroid window; the
 // Gaussian sketch also needs m <= 128 (one sketch word per lane part)

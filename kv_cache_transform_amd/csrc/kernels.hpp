@@ -115,6 +115,8 @@ struct AttnArgs {
 
 // launchers: return hipSuccess or the launch error
 hipError_t launch_encode(const EncodeArgs& a, bool x_bf16, int num_cus, hipStream_t s);
+// keys and values of the same tokens in one launch (bf16 input); *fused = false: nothing launched
+hipError_t launch_encode_kv(const EncodeArgs& ak, const EncodeArgs& av, int num_cus, hipStream_t s, bool* fused);
 hipError_t launch_decode(const DecodeArgs& a, bool out_bf16, int num_cus, hipStream_t s);
 hipError_t launch_decode_qjl(const DecodeArgs& a, bool out_bf16, int num_cus, hipStream_t s, bool* supported);
 hipError_t launch_qprep(const QPrepArgs& a, hipStream_t s);

@@ -110,6 +110,17 @@ def test_argument_validation_before_any_gpu_call():
     assert L.tq_decode_qjl(_p(m=128), ctypes.c_void_p(16), 2, 2, ctypes.c_void_p(20), 0, None) == _lib.TQ_EALIGN
     # empty inputs are a valid no-op
     assert L.tq_encode(p, None, 1, 0, 5, None, None) == _lib.TQ_OK
+    # the one-launch key + value encode: both parameter sets, pointers, dtype and alignment on the host
+    pkv = _p(m=128)
+    assert L.tq_encode_kv(pkv, _p(b=0), x16, x16, 1, 2, 2, b16, b16, None) == _lib.TQ_EINVAL
+    assert L.tq_encode_kv(None, p, x16, x16, 1, 2, 2, b16, b16, None) == _lib.TQ_EINVAL
+    assert L.tq_encode_kv(pkv, p, x16, None, 1, 2, 2, b16, b16, None) == _lib.TQ_EINVAL
+    assert L.tq_encode_kv(pkv, p, x16, x16, 1, 2, 2, b16, None, None) == _lib.TQ_EINVAL
+    assert L.tq_encode_kv(pkv, p, x16, x16, 7, 2, 2, b16, b16, None) == _lib.TQ_EINVAL
+    assert L.tq_encode_kv(pkv, p, x16, x16, 1, -1, 2, b16, b16, None) == _lib.TQ_EINVAL
+    assert L.tq_encode_kv(pkv, p, x16, ctypes.c_void_p(24), 1, 2, 2, b16, b16, None) == _lib.TQ_EALIGN
+    assert L.tq_encode_kv(pkv, p, None, None, 1, 0, 5, None, None, None) == _lib.TQ_OK
+    assert L.tq_encode_kv(pkv, p, None, None, 1, 3, 0, None, None, None) == _lib.TQ_OK
     assert L.tq_decode(p, None, 3, 0, None, 0, None) == _lib.TQ_OK
     # scores: workspace too small, too many queries
     pk = _p(m=128)
