@@ -35,17 +35,20 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published (the sketch p
 # the kernel's sources are the ones it was measured on (sha256 of the .hip file + shared headers).
 FETCH_UNIT_B, WRITE_UNIT_B = 2048, 1024
 TRAFFIC = {
-    "encode_k": {"fetch": 2097508.5, "write": 1395650.5625, "src": "encode.hip",
-        "sha": "8f5183252e566100540547dadba46aca3ad0cf8ad58db3cb4b8702c75a4bc2e9"},
-    "encode_v": {"fetch": 2105695.9375, "write": 1090859.8125, "src": "encode.hip",
-        "sha": "8f5183252e566100540547dadba46aca3ad0cf8ad58db3cb4b8702c75a4bc2e9"},
-    "decode_attention": {"fetch": 1232571.9375, "write": 6240.0625, "src": "attention.hip",
-        "sha": "a0d7922a1484082cb5aa8b4e9bd67acbe3fca051da00a00d62cc92680a26448f"},
-    "decode_v_bf16": {"fetch": 550101.5, "write": 4194304.0, "src": "decode.hip",
-        "sha": "5f0e44244900f247d31af0931f1462ce889761a8182fed30d4330630095b966f"},
+    "encode_kv": {"fetch": 4194695.125, "write": 2493528.875, "src": "encode.hip",
+        "sha": "f0b42740b4f9412634f6b99bf3c02ce72f038ab034c58b00b85d1235c587faab"},
+    "encode_k": {"fetch": 2097510.5, "write": 1394835.8125, "src": "encode.hip",
+        "sha": "f0b42740b4f9412634f6b99bf3c02ce72f038ab034c58b00b85d1235c587faab"},
+    "encode_v": {"fetch": 2109701.75, "write": 1090989.5, "src": "encode.hip",
+        "sha": "f0b42740b4f9412634f6b99bf3c02ce72f038ab034c58b00b85d1235c587faab"},
+    "decode_attention": {"fetch": 1233018.3125, "write": 6240.0, "src": "attention.hip",
+        "sha": "4a5ef5d6cf48758bd8ce022548ab11229a28468c121500b993a01171da50a630"},
+    "decode_v_bf16": {"fetch": 550434.875, "write": 4194304.0, "src": "decode.hip",
+        "sha": "b1ba67ba042266686af375dd30fa7fbae0fbf2bf933c7820de5b5978f1c26054"},
 }
+TRAFFIC["decode_attention_back_to_back"] = TRAFFIC["decode_attention"]
 TRAFFIC_HEADERS_SHA = ("6643b4ed6d32e0cc4205551fb1ef8fab74077690c7d82ac29a903d73ebc0d666"   # common.hpp
-                       "c79a58581fb18e7686561d680e8fdc2107a0b0d7c4661d9115f2dda2656965da")  # kernels.hpp
+                       "ac32d81f3164d8a735c83e985560964be8ac1e48c58555fb8691aeb330ecffce")  # kernels.hpp
 
 
 def _sha(path: str) -> str:
@@ -168,10 +171,23 @@ def main():
         kms[n] = sum(samples[n]) / len(samples[n])
     T.encode_kv(ck, cv, K, V, pk, pv)     # the step's records again, for the parity sample below
     torch.cuda.synchronize()
+    # decode-attention launched back to back (no encode between calls): the kernel in the power state
+    # of its own load; the step's figure above is the one that counts
+    pairs = []
+    for _ in range(args.steps):
+        a_, b_ = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a_.record(stream)
+        T.decode_attention(ck, cv, q, pk, pv, Hkv, N, out=out, workspace=ws)
+        b_.record(stream)
+        pairs.append((a_, b_))
+    torch.cuda.synchronize()
+    samples["decode_attention_back_to_back"] = [a_.elapsed_time(b_) for a_, b_ in pairs]
+    kms["decode_attention_back_to_back"] = sum(samples["decode_attention_back_to_back"]) / args.steps
+    alg["decode_attention_back_to_back"] = alg["decode_attention"]
     kern = {}
-    for n in ("encode_kv", "encode_k", "encode_v", "decode_attention"):
+    for n in ("encode_kv", "encode_k", "encode_v", "decode_attention", "decode_attention_back_to_back"):
         gbs = alg[n] / (kms[n] * 1e-3) / 1e9
-        nb = {"decode_attention": 2, "encode_kv": 2}.get(n, 1) * nvec * d * 2
+        nb = (1 if n in ("encode_k", "encode_v") else 2) * nvec * d * 2
         bf = nb / (kms[n] * 1e-3) / 1e9
         kern[n] = {"ms": round(kms[n], 4), **_spread(samples[n]), "alg_bytes": alg[n], "achieved_GBs": round(gbs, 1),
                    "hbm_frac": round(gbs / HBM_PEAK_GBS, 4), "bf16_equiv_GBs": round(bf, 1)}
