@@ -490,7 +490,13 @@ def other_workloads(torch, T, I, dev, stream) -> dict:
     out["outlier K 32x32768x128 b4: encode"] = _line(_time(torch, stream, lambda: T.encode(c, x, pk)), nv * (256 + 66))
     out["outlier K 32x32768x128 b4: decode to bf16"] = _line(
         _time(torch, stream, lambda: T.decode(c, pk, H, N, torch.bfloat16, out=xh)), nv * (66 + 256))
-    del x, pk, xh
+    # its K and V (V: other outlier channels, own seed) encoded in one launch (tq_encode_kv)
+    xv = I.outlier_gaussian(H, N, d, 4, 10.0, 2002, device=dev)
+    cv = T.Codec(d, 4, 0, H, 2002)
+    pv = T.encode(cv, xv)
+    out["outlier K,V 32x32768x128 b4: encode K and V (one launch)"] = _line(
+        _time(torch, stream, lambda: T.encode_kv(c, cv, x, xv, pk, pv)), 2 * nv * (256 + 66))
+    del x, xv, pk, pv, xh
 
     H, N, d, nq = 8, 65536, 128, 32
     x = I.gaussian((H, N, d), 3001, device=dev)
