@@ -51,26 +51,25 @@ struct FqLayout {
 template <int D, int B, bool QJL>
 constexpr int fq_lds_bytes() { return QJL ? FqLayout<B>::W + 65536 : 65536; }
 
-// Waves per block: the sketch of bf16 input at d = 256 with S in LDS runs 8 waves (two per SIMD,
-// 254 VGPRs) on one copy of S, which leaves no room for a second block; the binade-grid kernel
-// (64 or 96 KiB of LDS) runs one block per CU of three waves per SIMD; everything else runs 4.
-template <int D, bool QJL, bool BF16, bool S_LDS, bool FQ>
+// Waves per block of the search-grid kernel: the sketch of bf16 input at d = 256 with S in LDS runs
+// 8 waves (two per SIMD, 254 VGPRs) on one copy of S, which leaves no room for a second block;
+// everything else runs 4.  (The binade-grid kernels below run one 12-wave block per CU.)
+template <int D, bool QJL, bool BF16, bool S_LDS>
 constexpr int enc_waves() {
-    if (FQ) return 12;
     return (QJL && BF16 && S_LDS && D > 128) ? 8 : 4;
 }
-template <int D, bool QJL, bool BF16, bool S_LDS, bool FQ>
+template <int D, bool QJL, bool BF16, bool S_LDS>
 constexpr int enc_min_blocks() {
-    if (FQ) return 1;
-    return enc_waves<D, QJL, BF16, S_LDS, FQ>() == 8 ? 2
+    return enc_waves<D, QJL, BF16, S_LDS>() == 8 ? 2
            : ((D > 128 && (QJL || !BF16)) || (QJL && !BF16) ? 1 : (D > 128 ? 2 : 3));
 }
 
-template <int D, int B, bool QJL, bool BF16, bool S_LDS, bool FQ>
-__global__ __launch_bounds__((64 * enc_waves<D, QJL, BF16, S_LDS, FQ>()), (enc_min_blocks<D, QJL, BF16, S_LDS, FQ>()))
+// The search-grid encode: any d, b and input type (the binade-grid kernels below serve bf16 input
+// at b <= 4 and d <= 128).
+template <int D, int B, bool QJL, bool BF16, bool S_LDS>
+__global__ __launch_bounds__((64 * enc_waves<D, QJL, BF16, S_LDS>()), (enc_min_blocks<D, QJL, BF16, S_LDS>()))
 void encode_kernel(EncodeArgs a) {
-    constexpr int NWV = enc_waves<D, QJL, BF16, S_LDS, FQ>();
-    static_assert(!FQ || (BF16 && B <= 4), "the binade grid serves bf16 input and b <= 4");
+    constexpr int NWV = enc_waves<D, QJL, BF16, S_LDS>();
     constexpr int C = D / 4, R = D / 16, L = 1 << B;
     constexpr int NW = (C * B + 31) / 32;          // packed words per lane
     constexpr int CB = C * B / 8;                   // packed bytes per lane
@@ -88,88 +87,12 @@ void encode_kernel(EncodeArgs a) {
     const int m = a.t.m;
 
     extern __shared__ uint32_t lds[];
-    using FL = FqLayout<(B <= 4 ? B : 4)>;
-    // the binade-grid tables live in a static array, so every address formed from a table byte
-    // needs no base added (the array is the kernel's only LDS)
-    uint8_t* ldsb;
-    if constexpr (FQ) {
-        __shared__ __attribute__((aligned(16))) uint32_t fq_lds[fq_lds_bytes<D, B, QJL>() / 4];
-        ldsb = reinterpret_cast<uint8_t*>(fq_lds);
-    } else {
-        ldsb = reinterpret_cast<uint8_t*>(lds);
-    }
-    uint32_t* const ldsw = reinterpret_cast<uint32_t*>(ldsb);
     const int G = a.t.G;
     // search grid, replicated 2^rl times with the copies interleaved per cell, so lanes that use
     // different copies read different banks: cell c of copy r = words 2 (c 2^rl + r) + {0, 1}
     const int rl = a.grid_rep_log2;
-    const int ngw = FQ ? 0 : (2 * (G + 3)) << rl;
-    if constexpr (FQ) {
-        // every global load of the staging (grid entries, centroids, S with the Gaussian sketch,
-        // m <= 128 here) is issued before any LDS store, with compile-time trip counts, so the
-        // prologue waits on memory once rather than once per loop iteration
-        constexpr int NTH = 64 * NWV;
-        constexpr int NGI = (128 * 64 + NTH - 1) / NTH;
-        constexpr int NCE = 2 * (1 << B) * 64;                 // centroid-row words
-        constexpr int NCI = QJL ? (NCE + NTH - 1) / NTH : 1;
-        constexpr int NSI = QJL ? (128 * D / 8 + NTH - 1) / NTH : 1;
-        const int tid = (int)threadIdx.x;
-        uint32_t gv[NGI], cv[NCI];
-        u32x4 sv[NSI];
-#pragma unroll
-        for (int j = 0; j < NGI; ++j) {
-            const int i = tid + j * NTH;
-            gv[j] = a.t.fq_grid[(i < 128 * 64 ? i : 0) >> 6];
-        }
-        const bool gauss = QJL && a.t.sketch != 1;
-        const int n16 = QJL ? m * D / 8 : 0;                  // 16-byte pieces of S
-        if constexpr (QJL) {
-#pragma unroll
-            for (int j = 0; j < NCI; ++j) {
-                const int i = tid + j * NTH;
-                cv[j] = f2u(a.t.cent_x1024[i < NCE ? (i >> 7) : 0]);
-            }
-            if (gauss) {
-                const u32x4* src = reinterpret_cast<const u32x4*>(a.t.S + (int64_t)head * m * D);
-#pragma unroll
-                for (int j = 0; j < NSI; ++j) {
-                    const int i = tid + j * NTH;
-                    if (i < n16) sv[j] = src[i];
-                }
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < NGI; ++j) {
-            const int i = tid + j * NTH;
-            if (i < 128 * 64) ldsw[i] = gv[j];
-        }
-        if constexpr (QJL) {
-#pragma unroll
-            for (int j = 0; j < NCI; ++j) {
-                const int i = tid + j * NTH;
-                if (i < NCE) {
-                    const int r2 = i >> 6, idx = r2 >> 1, row = idx * FL::R + ((r2 & 1) ? FL::R - 1 : 0);
-                    ldsw[(FL::W + row * 256) / 4 + (i & 63)] = cv[j];
-                }
-            }
-            if (gauss) {
-                // S in the order the MFMA A operand reads it (see the sketch loop): lane l = rho +
-                // 16 gp reads row (rho/4)(m/4) + 4 tau + rho%4, columns gp C + 8k .. +8
-                const int mq = m >> 2;
-#pragma unroll
-                for (int j = 0; j < NSI; ++j) {
-                    const int i = tid + j * NTH;
-                    if (i < n16) {
-                        const int row = i / (D / 8), col = i - row * (D / 8);
-                        const int q = row / mq, rem = row - q * mq;
-                        const int tau = rem >> 2, rh = 4 * q + (rem & 3);
-                        const int gp = col / KS, k = col - gp * KS;
-                        *reinterpret_cast<u32x4*>(ldsb + FL::piece(2 * (D / 32) + tau * KS + k) + 16 * (rh + 16 * gp)) = sv[j];
-                    }
-                }
-            }
-        }
-    } else {
+    const int ngw = (2 * (G + 3)) << rl;
+    {
         for (int i = threadIdx.x; i < ((G + 3) << rl); i += blockDim.x) {
             const int c = i >> rl;
             lds[2 * i] = a.t.grid[2 * c];
@@ -183,9 +106,8 @@ void encode_kernel(EncodeArgs a) {
     u32x4* lds_A = reinterpret_cast<u32x4*>(lds + a_off);
     _Float16* lds_S = reinterpret_cast<_Float16*>(lds + a_off + NAW);
     if constexpr (QJL) {
-        if constexpr (!FQ)
-            for (int i = threadIdx.x; i < L; i += blockDim.x) lds_c[i] = a.t.cent_x1024[i];
-        if (!FQ && S_LDS && !(BF16 && a.t.sketch == 1)) {
+        for (int i = threadIdx.x; i < L; i += blockDim.x) lds_c[i] = a.t.cent_x1024[i];
+        if (S_LDS && !(BF16 && a.t.sketch == 1)) {
             // S in the order the MFMA A operand reads it (see the sketch loop): the 16-byte piece
             // of lane l for row tile tau and k-step k sits at piece index (tau KS + k) 64 + l, so
             // every A read is one contiguous 1 KiB wave access.  Lane l = rho + 16 gp reads row
@@ -236,8 +158,7 @@ void encode_kernel(EncodeArgs a) {
                 }
                 wv[t] = w2;
             }
-            if constexpr (FQ) *reinterpret_cast<u32x4*>(ldsb + FL::piece(e >> 6) + 16 * l) = wv;
-            else if (second) reinterpret_cast<u32x4*>(lds_S)[ee] = wv;
+            if (second) reinterpret_cast<u32x4*>(lds_S)[ee] = wv;
             else lds_A[e] = wv;
         }
     }
@@ -261,30 +182,11 @@ void encode_kernel(EncodeArgs a) {
     const int rho = lane & 15;
     const int row_base = (rho >> 2) * (m >> 2) + (rho & 3);
     const uint32_t goff = (uint32_t)(lane & ((1 << rl) - 1)) << 3;   // byte offset of the lane's grid copy
-    const uint32_t lane4 = 4u * (uint32_t)lane;                        // the lane's copy in a binade-grid row
-    // binade-grid path: raw buffers over this stream's input and its tokens' record planes, each
-    // exactly as long as the stream's part (the launcher keeps them below 2^31 bytes), so a lane
-    // past the last token reads zeros and its stores are dropped as well as skipped
-    __amdgpu_buffer_rsrc_t rx = buffer_rsrc(a.x, 0), rid = rx, rnm = rx, rsk = rx, rrn = rx;
-    if constexpr (FQ) {
-        const int64_t rec0 = st * a.cap + a.t0;
-        rx = buffer_rsrc(reinterpret_cast<const uint8_t*>(a.x) + st * a.n_tokens * (int64_t)(2 * D), (int)(a.n_tokens * 2 * D));
-        rid = buffer_rsrc(a.packed + a.off_idx + rec0 * (int64_t)(D * B / 8), (int)(a.n_tokens * (D * B / 8)));
-        rnm = buffer_rsrc(a.packed + a.off_norm + rec0 * 2, (int)(a.n_tokens * 2));
-        if constexpr (QJL) {
-            rsk = buffer_rsrc(a.packed + a.off_sketch + rec0 * (int64_t)(m / 8), (int)(a.n_tokens * (m / 8)));
-            rrn = buffer_rsrc(a.packed + a.off_rnorm + rec0 * 2, (int)(a.n_tokens * 2));
-        }
-    }
 
     // raw input words of one 16-vector group: bf16 = the lane's C contiguous coordinates; fp32 =
     // runs of R coordinates in the i(s, g) order of the butterfly network (see common.hpp)
     constexpr int NIW = BF16 ? C / 2 : C;
     auto load_group = [&](uint32_t (&w)[NIW], int64_t tile) {
-        if constexpr (FQ) {
-            bload<2 * C, 16>(rx, (uint32_t)(tile * 16 + v) * (2 * D) + 2 * g * C, 0u, w);
-            return;
-        }
         const int64_t tok = tile * 16 + v;
         const bool valid = tile < tb1 && tok < a.n_tokens;
         const int64_t vec = st * a.n_tokens + (valid ? tok : 0);
@@ -327,7 +229,6 @@ void encode_kernel(EncodeArgs a) {
         float e2v[NG];
         bool validv[NG];
         int64_t vecv[NG];
-        uint32_t tokv[NG];
 #pragma unroll
         for (int gi = 0; gi < NG; ++gi) {
             const int64_t tok = (t + gi) * 16 + v;
@@ -336,7 +237,6 @@ void encode_kernel(EncodeArgs a) {
             const int64_t vec = st * a.cap + a.t0 + (valid ? tok : 0);
             validv[gi] = valid;
             vecv[gi] = vec;
-            tokv[gi] = (uint32_t)tok;
 
             // ---- sign, first butterfly stage, norm ----------------------------------------------
             float x[C];
@@ -361,8 +261,7 @@ void encode_kernel(EncodeArgs a) {
                         const bf16x8 Bv = __builtin_bit_cast(bf16x8, u32x4{w[4 * kb], w[4 * kb + 1], w[4 * kb + 2], w[4 * kb + 3]});
 #pragma unroll
                         for (int h = 0; h < 2; ++h) {
-                            const u32x4 At = FQ ? *reinterpret_cast<const u32x4*>(ldsb + FL::piece(h * NKB + kb) + 16 * lane)
-                                                : lds_A[(h * NKB + kb) * 64 + lane];
+                            const u32x4 At = lds_A[(h * NKB + kb) * 64 + lane];
                             const floatx4 r = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
                                 __builtin_bit_cast(bf16x8, At), Bv,
                                 floatx4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
@@ -410,26 +309,8 @@ void encode_kernel(EncodeArgs a) {
 #pragma unroll
             for (int k = 0; k < NW; ++k) pk[k] = 0u;
             float e2 = 0.0f;
-            if constexpr (FQ) {
-                // binade grid: u in [2, 4); slots in descending order, so that alignbit leaves the
-                // lowest slot of each word in its low bits
-                const float sU = sc * (float)kFqKappa;
 #pragma unroll
-                for (int s = C - 1; s >= 0; --s) {
-                    const float u = fmaf(x[s], sU, 3.0f);
-                    const uint32_t ga = __builtin_amdgcn_perm(f2u(u), lane4, 0x0c0c0600u);
-                    const uint32_t w = f2u(u) + *reinterpret_cast<const uint32_t*>(ldsb + ga);
-                    if constexpr (B == 3) put_bits<B>(pk, s * B, w >> 29);
-                    else pk[(s * B) >> 5] = __builtin_amdgcn_alignbit(pk[(s * B) >> 5], w, 32 - B);
-                    if constexpr (QJL) {
-                        const uint32_t ca = __builtin_amdgcn_perm(w, lane4, 0x0c0c0700u);
-                        x[s] = fmaf(x[s], sE, -*reinterpret_cast<const float*>(ldsb + FL::W + ca));
-                        e2 = fmaf(x[s], x[s], e2);
-                    }
-                }
-            }
-#pragma unroll
-            for (int s = 0; s < (FQ ? 0 : C); ++s) {
+            for (int s = 0; s < C; ++s) {
                 const float u = fmaf(x[s], sA, gB);
                 const uint32_t cell = (uint32_t)u;
                 const u32x2 ent = *reinterpret_cast<const u32x2*>(reinterpret_cast<const uint8_t*>(lds) + ((cell << (3 + rl)) + goff));
@@ -443,14 +324,8 @@ void encode_kernel(EncodeArgs a) {
                 }
             }
             if (valid) {
-                if constexpr (FQ) {
-                    const uint32_t tk = (uint32_t)tok;
-                    bstore<CB, CA>(rid, tk * (D * B / 8) + g * CB, 0u, pk);
-                    if (g == 0) __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, (_Float16)n), rnm, tk * 2u, 0u, 0);
-                } else {
-                    store_bytes<CB, CA>(a.packed + a.off_idx + vec * (int64_t)(D * B / 8) + g * CB, pk);
-                    if (g == 0) *reinterpret_cast<_Float16*>(a.packed + a.off_norm + vec * 2) = (_Float16)n;
-                }
+                store_bytes<CB, CA>(a.packed + a.off_idx + vec * (int64_t)(D * B / 8) + g * CB, pk);
+                if (g == 0) *reinterpret_cast<_Float16*>(a.packed + a.off_norm + vec * 2) = (_Float16)n;
             }
             if constexpr (QJL) {
                 e2v[gi] = e2;
@@ -485,8 +360,7 @@ void encode_kernel(EncodeArgs a) {
                 for (int kb = 0; kb < NKB; ++kb)
 #pragma unroll
                     for (int h = 0; h < 2; ++h) {
-                        const half8 A = __builtin_bit_cast(half8, FQ ? *reinterpret_cast<const u32x4*>(ldsb + FL::piece(2 * NKB + h * NKB + kb) + 16 * lane)
-                                                                     : lds_A2[(h * NKB + kb) * 64 + lane]);
+                        const half8 A = __builtin_bit_cast(half8, lds_A2[(h * NKB + kb) * 64 + lane]);
                         floatx4 r = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bh[gi][kb], floatx4{0.0f, 0.0f, 0.0f, 0.0f}, 0, 0, 0);
                         r = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bl[gi][kb], r, 0, 0, 0);
 #pragma unroll
@@ -504,14 +378,8 @@ void encode_kernel(EncodeArgs a) {
                         for (int p = 8 * j + 7; p >= 8 * j; --p) by[j] = __builtin_amdgcn_alignbit(by[j], f2u(z[32 * w + p]), 31);
                     const uint32_t bw = ~((((by[3] << 8) | by[2]) << 16) | ((by[1] << 8) | by[0]));
                     if (validv[gi]) {
-                        if constexpr (FQ) {
-                            const uint32_t o = tokv[gi] * (D / 8) + g * (C / 8) + 4 * w;
-                            if constexpr (NBY == 4) __builtin_amdgcn_raw_buffer_store_b32(bw, rsk, o, 0u, 0);
-                            else __builtin_amdgcn_raw_buffer_store_b16((uint16_t)bw, rsk, o, 0u, 0);
-                        } else {
-                            if constexpr (NBY == 4) *reinterpret_cast<uint32_t*>(dst + 4 * w) = bw;
-                            else *reinterpret_cast<uint16_t*>(dst + 4 * w) = (uint16_t)bw;
-                        }
+                        if constexpr (NBY == 4) *reinterpret_cast<uint32_t*>(dst + 4 * w) = bw;
+                        else *reinterpret_cast<uint16_t*>(dst + 4 * w) = (uint16_t)bw;
                     }
                 }
             }
@@ -520,8 +388,7 @@ void encode_kernel(EncodeArgs a) {
                 const float e2 = sum4(e2v[gi]);
                 if (validv[gi] && g == 0) {
                     const _Float16 r16 = (_Float16)(sqrtf(e2) * (1.0f / 16384.0f));
-                    if constexpr (FQ) __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, r16), rrn, tokv[gi] * 2u, 0u, 0);
-                    else *reinterpret_cast<_Float16*>(a.packed + a.off_rnorm + vecv[gi] * 2) = r16;
+                    *reinterpret_cast<_Float16*>(a.packed + a.off_rnorm + vecv[gi] * 2) = r16;
                 }
             }
             continue;
@@ -554,8 +421,7 @@ void encode_kernel(EncodeArgs a) {
                             const int tt = 4 * hf + tl;
                             if (FULL || tt < nt) {
                                 const int tau = tau0 + tt;
-                                const half8 A = FQ ? *reinterpret_cast<const half8*>(ldsb + FL::piece(2 * NKB + tau * KS + k) + 16 * lane)
-                                                   : *reinterpret_cast<const half8*>(S_LDS ? Sg + (tau * KS + k) * 512 : Sg + 4 * tau * D + 8 * k);
+                                const half8 A = *reinterpret_cast<const half8*>(S_LDS ? Sg + (tau * KS + k) * 512 : Sg + 4 * tau * D + 8 * k);
 #pragma unroll
                                 for (int gi = 0; gi < NG; ++gi) {
                                     acc[gi][tl] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, bh[gi][k], acc[gi][tl], 0, 0, 0);
@@ -593,36 +459,22 @@ void encode_kernel(EncodeArgs a) {
                 for (int gi = 0; gi < NG; ++gi) {
                     const uint32_t bw = ~((((by[gi][3] << 8) | by[gi][2]) << 16) | ((by[gi][1] << 8) | by[gi][0]));
                     if (validv[gi]) {
-                        if constexpr (FQ) {
-                            const uint32_t o = tokv[gi] * (uint32_t)(m / 8) + (uint32_t)(g * (m / 32)) + (uint32_t)(wb >> 3);
-                            if (FULL && (m & 127) == 0) __builtin_amdgcn_raw_buffer_store_b32(bw, rsk, o, 0u, 0);
-                            else if (nb == 2 && (m & 63) == 0) __builtin_amdgcn_raw_buffer_store_b16((uint16_t)bw, rsk, o, 0u, 0);
-                            else for (int q = 0; q < nb; ++q) __builtin_amdgcn_raw_buffer_store_b8((uint8_t)(bw >> (8 * q)), rsk, o + q, 0u, 0);
-                        } else {
-                            uint8_t* dst = a.packed + a.off_sketch + vecv[gi] * (int64_t)(m / 8) + g * (m / 32) + (wb >> 3);
-                            if (FULL && (m & 127) == 0) *reinterpret_cast<uint32_t*>(dst) = bw;
-                            else if (nb == 2 && (m & 63) == 0) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)bw;
-                            else for (int q = 0; q < nb; ++q) dst[q] = (uint8_t)(bw >> (8 * q));
-                        }
+                        uint8_t* dst = a.packed + a.off_sketch + vecv[gi] * (int64_t)(m / 8) + g * (m / 32) + (wb >> 3);
+                        if (FULL && (m & 127) == 0) *reinterpret_cast<uint32_t*>(dst) = bw;
+                        else if (nb == 2 && (m & 63) == 0) *reinterpret_cast<uint16_t*>(dst) = (uint16_t)bw;
+                        else for (int q = 0; q < nb; ++q) dst[q] = (uint8_t)(bw >> (8 * q));
                     }
                 }
             };
             const int nbits = m >> 2;
-            if constexpr (FQ) {
-                // m <= 128: one word per lane part, so every S piece offset is a constant
-                if (nbits == 32) sketch_word(std::integral_constant<int, 0>{}, 8, std::true_type{});
-                else sketch_word(std::integral_constant<int, 0>{}, nbits >> 2, std::false_type{});
-            } else {
-                for (int wb = 0; wb + 32 <= nbits; wb += 32) sketch_word(wb, 8, std::true_type{});
-                if (nbits & 31) sketch_word(nbits & ~31, (nbits & 31) >> 2, std::false_type{});
-            }
+            for (int wb = 0; wb + 32 <= nbits; wb += 32) sketch_word(wb, 8, std::true_type{});
+            if (nbits & 31) sketch_word(nbits & ~31, (nbits & 31) >> 2, std::false_type{});
 #pragma unroll
             for (int gi = 0; gi < NG; ++gi) {
                 const float e2 = sum4(e2v[gi]);
                 if (validv[gi] && g == 0) {
                     const _Float16 r16 = (_Float16)(sqrtf(e2) * (1.0f / 16384.0f));
-                    if constexpr (FQ) __builtin_amdgcn_raw_buffer_store_b16(__builtin_bit_cast(uint16_t, r16), rrn, tokv[gi] * 2u, 0u, 0);
-                    else *reinterpret_cast<_Float16*>(a.packed + a.off_rnorm + vecv[gi] * 2) = r16;
+                    *reinterpret_cast<_Float16*>(a.packed + a.off_rnorm + vecv[gi] * 2) = r16;
                 }
             }
         }
@@ -664,9 +516,9 @@ struct FqBufs {
 // loads of tile t_next (issued as soon as w is consumed; skipped when t_next >= tb1).  pA is the
 // first window piece of the tensor's signed Hadamard tiles, pS that of its S / randomized tiles.
 template <int D, int B, bool QJL>
-__device__ __forceinline__ void fq_encode_group(const uint8_t* ldsb, int pA, int pS, bool rht, int m, const FqBufs& R,
-                                                uint32_t (&w)[D / 8], int64_t t, int64_t t_next, int64_t tb1,
-                                                int64_t n_tokens, int lane) {
+__device__ __forceinline__ void fq_encode_group(const uint8_t* ldsb, int pA, int pS, bool rht, bool plain, int m,
+                                                const FqBufs& R, uint32_t (&w)[D / 8], int64_t t, int64_t t_next,
+                                                int64_t tb1, int64_t n_tokens, int lane) {
     using FL = FqLayout<B>;
     constexpr int C = D / 4, NKB = D / 32, KS = D / 32;
     constexpr int NW = (C * B + 31) / 32, CB = C * B / 8, CA = cmin(pow2_align(CB), 16);
@@ -677,7 +529,8 @@ __device__ __forceinline__ void fq_encode_group(const uint8_t* ldsb, int pA, int
     const bool valid = t < tb1 && tok < n_tokens;
     const uint32_t tk = (uint32_t)tok;
 
-    // sign flip + 32-point block on bf16 MFMA, then the middle bits in registers; the norm
+    // sign flip + 32-point block on bf16 MFMA, then the middle bits in registers (Plain-KV: slot s
+    // is coordinate g C + s itself); the norm
     float x[C];
     float n2 = 0.0f;
 #pragma unroll
@@ -685,6 +538,13 @@ __device__ __forceinline__ void fq_encode_group(const uint8_t* ldsb, int pA, int
         const bf16x2 wv = __builtin_bit_cast(bf16x2, w[k]);
         n2 = __builtin_amdgcn_fdot2_f32_bf16(wv, wv, n2, false);
     }
+    if (plain) {
+#pragma unroll
+        for (int k = 0; k < C / 2; ++k) {
+            x[2 * k] = u2f(w[k] << 16);
+            x[2 * k + 1] = u2f(w[k] & 0xffff0000u);
+        }
+    } else {
 #pragma unroll
     for (int kb = 0; kb < NKB; ++kb) {
         const bf16x8 Bv = __builtin_bit_cast(bf16x8, u32x4{w[4 * kb], w[4 * kb + 1], w[4 * kb + 2], w[4 * kb + 3]});
@@ -697,19 +557,23 @@ __device__ __forceinline__ void fq_encode_group(const uint8_t* ldsb, int pA, int
             for (int i = 0; i < 4; ++i) x[8 * kb + 4 * h + i] = r[i];
         }
     }
+    }
 #pragma unroll
     for (int k = 0; k < D / 8; ++k) asm volatile("" ::"v"(w[k]) : "memory");
     asm volatile("" ::"v"(n2) : "memory");
     if (t_next < tb1) bload<2 * C, 16>(R.rx, (uint32_t)(t_next * 16 + v) * (2 * D) + 2 * g * C, 0u, w);
-    fwht_slots<C, 8>(x);
+    if (!plain) fwht_slots<C, 8>(x);
     n2 = sum4(n2);
+    // hardware square root and reciprocal square root (about 1 ulp: y moves by ~1e-7, far inside
+    // the 1e-6 decision bands); a denormal n² keeps the exact forms
+    const float inv_sqrt_d = plain ? 1.0f : kInvSqrtD;
     float n, sc;
     if (n2 >= 0x1p-126f) {
         n = __builtin_amdgcn_sqrtf(n2);
-        sc = kInvSqrtD * __builtin_amdgcn_rsqf(n2);
+        sc = inv_sqrt_d * __builtin_amdgcn_rsqf(n2);
     } else {
         n = sqrtf(n2);
-        sc = n > 0.0f ? kInvSqrtD / n : 0.0f;
+        sc = n > 0.0f ? inv_sqrt_d / n : 0.0f;
     }
     const float sE = sc * 16384.0f;
 
@@ -874,15 +738,140 @@ __device__ __forceinline__ void fq_stage_hadamard(uint8_t* ldsb, int pA, const f
     }
 }
 
+// The binade-grid tables of one key or value codec (as both binade-grid kernels stage them): grid
+// row c = 64 copies of E[c]; with the sketch the centroid rows (64 copies of 2^14 c[idx] in rows
+// idx·R and idx·R + R - 1) and, for the Gaussian sketch (m <= 128 here), S in the MFMA A-operand
+// order at window pieces pS onwards: lane l = rho + 16 gp of row tile tau, k-step k reads row
+// (rho/4)(m/4) + 4 tau + rho%4, columns gp C + 8k .. +8.  Every global load is issued before any
+// LDS store (compile-time trip counts), so the prologue waits on memory once.
+constexpr int kFqWaves = 12;                      // waves per block of the binade-grid kernels
 template <int D, int B, bool QJL>
-__global__ __launch_bounds__(768, 1) void encode_kv_kernel(EncodeArgs ak, EncodeArgs av) {
+__device__ __forceinline__ void fq_stage_tables(uint8_t* ldsb, const DevTables& t, int head, int m, bool rht, int pS,
+                                                int tid) {
     using FL = FqLayout<B>;
-    constexpr int NWV = 12, NTH = 64 * NWV;
+    constexpr int NTH = 64 * kFqWaves, KS = D / 32;
+    constexpr int NGI = (128 * 64 + NTH - 1) / NTH;
+    constexpr int NCE = 2 * (1 << B) * 64;         // centroid-row words
+    constexpr int NCI = QJL ? (NCE + NTH - 1) / NTH : 1;
+    constexpr int NSI = QJL ? (128 * D / 8 + NTH - 1) / NTH : 1;
+    uint32_t* const ldsw = reinterpret_cast<uint32_t*>(ldsb);
+    uint32_t gv[NGI], cv[NCI];
+    u32x4 sv[NSI];
+#pragma unroll
+    for (int j = 0; j < NGI; ++j) {
+        const int i = tid + j * NTH;
+        gv[j] = t.fq_grid[(i < 128 * 64 ? i : 0) >> 6];
+    }
+    const int n16 = QJL && !rht ? m * D / 8 : 0;   // 16-byte pieces of S
+    if constexpr (QJL) {
+#pragma unroll
+        for (int j = 0; j < NCI; ++j) {
+            const int i = tid + j * NTH;
+            cv[j] = f2u(t.cent_x1024[i < NCE ? (i >> 7) : 0]);
+        }
+        if (n16 > 0) {
+            const u32x4* src = reinterpret_cast<const u32x4*>(t.S + (int64_t)head * m * D);
+#pragma unroll
+            for (int j = 0; j < NSI; ++j) {
+                const int i = tid + j * NTH;
+                if (i < n16) sv[j] = src[i];
+            }
+        }
+    }
+#pragma unroll
+    for (int j = 0; j < NGI; ++j) {
+        const int i = tid + j * NTH;
+        if (i < 128 * 64) ldsw[i] = gv[j];
+    }
+    if constexpr (QJL) {
+#pragma unroll
+        for (int j = 0; j < NCI; ++j) {
+            const int i = tid + j * NTH;
+            if (i < NCE) {
+                const int r2 = i >> 6, idx = r2 >> 1, row = idx * FL::R + ((r2 & 1) ? FL::R - 1 : 0);
+                ldsw[(FL::W + row * 256) / 4 + (i & 63)] = cv[j];
+            }
+        }
+        if (n16 > 0) {
+            const int mq = m >> 2;
+#pragma unroll
+            for (int j = 0; j < NSI; ++j) {
+                const int i = tid + j * NTH;
+                if (i < n16) {
+                    const int row = i / (D / 8), col = i - row * (D / 8);
+                    const int q = row / mq, rem = row - q * mq;
+                    const int tau = rem >> 2, rh = 4 * q + (rem & 3);
+                    const int gp = col / KS, k = col - gp * KS;
+                    *reinterpret_cast<u32x4*>(ldsb + FL::piece(pS + tau * KS + k) + 16 * (rh + 16 * gp)) = sv[j];
+                }
+            }
+        }
+    }
+}
+
+// raw buffers over stream st's input and its tokens' record planes, each exactly as long as the
+// stream's part (the launchers keep them below 2^31 bytes)
+template <int D, int B>
+__device__ __forceinline__ FqBufs fq_bufs(const EncodeArgs& a, int64_t st, bool qjl) {
+    FqBufs R;
+    const int64_t rec0 = st * a.cap + a.t0;
+    R.rx = buffer_rsrc(reinterpret_cast<const uint8_t*>(a.x) + st * a.n_tokens * (int64_t)(2 * D), (int)(a.n_tokens * 2 * D));
+    R.rid = buffer_rsrc(a.packed + a.off_idx + rec0 * (int64_t)(D * B / 8), (int)(a.n_tokens * (D * B / 8)));
+    R.rnm = buffer_rsrc(a.packed + a.off_norm + rec0 * 2, (int)(a.n_tokens * 2));
+    R.rsk = R.rrn = R.rnm;
+    if (qjl) {
+        R.rsk = buffer_rsrc(a.packed + a.off_sketch + rec0 * (int64_t)(a.t.m / 8), (int)(a.n_tokens * (a.t.m / 8)));
+        R.rrn = buffer_rsrc(a.packed + a.off_rnorm + rec0 * 2, (int)(a.n_tokens * 2));
+    }
+    return R;
+}
+
+// The binade-grid encode of one tensor (bf16 input, b <= 4, d <= 128; with the Gaussian sketch
+// m <= 128): one 12-wave block per CU (three waves per SIMD), waves walking the block's tiles with
+// the next tile's loads in flight.  Plain-KV skips the signs and the transform.
+template <int D, int B, bool QJL>
+__global__ __launch_bounds__(64 * kFqWaves, 1) void encode_fq_kernel(EncodeArgs a) {
+    constexpr int NWV = kFqWaves, NTH = 64 * NWV;
+    constexpr int C = D / 4, NKB = D / 32;
+    static_assert(B <= 4 && D <= 128, "the binade grid serves b <= 4 at d <= 128");
+    __shared__ __attribute__((aligned(16))) uint32_t fq_lds[fq_lds_bytes<D, B, QJL>() / 4];
+    uint8_t* const ldsb = reinterpret_cast<uint8_t*>(fq_lds);
+    const int64_t st = blockIdx.x / a.blocks_per_stream;
+    const int64_t sub = blockIdx.x - st * a.blocks_per_stream;
+    const int64_t tb0 = sub * a.tiles_per_block;
+    const int64_t tb1 = tb0 + a.tiles_per_block < a.tiles_per_stream ? tb0 + a.tiles_per_block : a.tiles_per_stream;
+    const int head = (int)(st % a.t.n_heads);
+    const int m = QJL ? a.t.m : 0;
+    const bool rht = QJL && a.t.sketch == 1;
+    const bool plain = a.t.rotation == 1;         // Plain-KV: no sign flip, no WHT
+    const int tid = (int)threadIdx.x;
+    fq_stage_tables<D, B, QJL>(ldsb, a.t, head, m, rht, 2 * NKB, tid);
+    fq_stage_hadamard<D, B>(ldsb, 0, a.t.signs + (int64_t)head * D, false, tid, NTH);
+    if (rht) fq_stage_hadamard<D, B>(ldsb, 2 * NKB, a.t.signs2 + (int64_t)head * D, true, tid, NTH);
+    __syncthreads();
+
+    const int lane = tid & 63;
+    const int v = lane & 15, g = lane >> 4;
+    const int wave = wave_id();
+    const FqBufs R = fq_bufs<D, B>(a, st, QJL);
+    uint32_t w[D / 8];
+    const int64_t t_first = tb0 + wave;
+    bload<2 * C, 16>(R.rx, (uint32_t)(t_first * 16 + v) * (2 * D) + 2 * g * C, 0u, w);
+#pragma unroll 1
+    for (int64_t t = t_first; t < tb1; t += NWV) {
+        // keep the LDS operand tables in LDS (re-read per pass) instead of pinned in registers
+        asm volatile("" ::: "memory");
+        fq_encode_group<D, B, QJL>(ldsb, 0, 2 * NKB, rht, plain, m, R, w, t, t + NWV, tb1, a.n_tokens, lane);
+    }
+}
+
+template <int D, int B, bool QJL>
+__global__ __launch_bounds__(64 * kFqWaves, 1) void encode_kv_kernel(EncodeArgs ak, EncodeArgs av) {
+    constexpr int NWV = kFqWaves, NTH = 64 * NWV;
     constexpr int C = D / 4, NKB = D / 32;
     static_assert(B <= 4 && D <= 128, "the binade grid serves b <= 4; the fused launch d <= 128");
     __shared__ __attribute__((aligned(16))) uint32_t fq_lds[fq_lds_bytes<D, B, QJL>() / 4];
     uint8_t* const ldsb = reinterpret_cast<uint8_t*>(fq_lds);
-    uint32_t* const ldsw = fq_lds;
 
     const int64_t st = blockIdx.x / ak.blocks_per_stream;
     const int64_t sub = blockIdx.x - st * ak.blocks_per_stream;
@@ -895,62 +884,7 @@ __global__ __launch_bounds__(768, 1) void encode_kv_kernel(EncodeArgs ak, Encode
     const int pSk = 2 * NKB, pAv = 2 * NKB + nS;
     const int tid = (int)threadIdx.x;
 
-    // staging (as the binade-grid kernel): every global load of the grid, centroid and S copies is
-    // issued before any LDS store
-    {
-        constexpr int NGI = (128 * 64 + NTH - 1) / NTH;
-        constexpr int NCE = 2 * (1 << B) * 64;
-        constexpr int NCI = QJL ? (NCE + NTH - 1) / NTH : 1;
-        constexpr int NSI = QJL ? (128 * D / 8 + NTH - 1) / NTH : 1;
-        uint32_t gv[NGI], cv[NCI];
-        u32x4 sv[NSI];
-#pragma unroll
-        for (int j = 0; j < NGI; ++j) {
-            const int i = tid + j * NTH;
-            gv[j] = ak.t.fq_grid[(i < 128 * 64 ? i : 0) >> 6];
-        }
-        const int n16 = QJL && !rht ? m * D / 8 : 0;
-        if constexpr (QJL) {
-#pragma unroll
-            for (int j = 0; j < NCI; ++j) {
-                const int i = tid + j * NTH;
-                cv[j] = f2u(ak.t.cent_x1024[i < NCE ? (i >> 7) : 0]);
-            }
-            const u32x4* src = reinterpret_cast<const u32x4*>(ak.t.S + (int64_t)hk * m * D);
-#pragma unroll
-            for (int j = 0; j < NSI; ++j) {
-                const int i = tid + j * NTH;
-                if (i < n16) sv[j] = src[i];
-            }
-        }
-#pragma unroll
-        for (int j = 0; j < NGI; ++j) {
-            const int i = tid + j * NTH;
-            if (i < 128 * 64) ldsw[i] = gv[j];
-        }
-        if constexpr (QJL) {
-#pragma unroll
-            for (int j = 0; j < NCI; ++j) {
-                const int i = tid + j * NTH;
-                if (i < NCE) {
-                    const int r2 = i >> 6, idx = r2 >> 1, row = idx * FL::R + ((r2 & 1) ? FL::R - 1 : 0);
-                    ldsw[(FL::W + row * 256) / 4 + (i & 63)] = cv[j];
-                }
-            }
-            const int mq = m >> 2, KS = D / 32;
-#pragma unroll
-            for (int j = 0; j < NSI; ++j) {
-                const int i = tid + j * NTH;
-                if (i < n16) {
-                    const int row = i / (D / 8), col = i - row * (D / 8);
-                    const int q = row / mq, rem = row - q * mq;
-                    const int tau = rem >> 2, rh = 4 * q + (rem & 3);
-                    const int gp = col / KS, k = col - gp * KS;
-                    *reinterpret_cast<u32x4*>(ldsb + FL::piece(pSk + tau * KS + k) + 16 * (rh + 16 * gp)) = sv[j];
-                }
-            }
-        }
-    }
+    fq_stage_tables<D, B, QJL>(ldsb, ak.t, hk, m, rht, pSk, tid);
     fq_stage_hadamard<D, B>(ldsb, 0, ak.t.signs + (int64_t)hk * D, false, tid, NTH);
     if (rht) fq_stage_hadamard<D, B>(ldsb, pSk, ak.t.signs2 + (int64_t)hk * D, true, tid, NTH);
     fq_stage_hadamard<D, B>(ldsb, pAv, av.t.signs + (int64_t)hv * D, false, tid, NTH);
@@ -959,20 +893,7 @@ __global__ __launch_bounds__(768, 1) void encode_kv_kernel(EncodeArgs ak, Encode
     const int lane = tid & 63;
     const int v = lane & 15, g = lane >> 4;
     const int wave = wave_id();
-    auto bufs = [&](const EncodeArgs& a, bool qjl) {
-        FqBufs R;
-        const int64_t rec0 = st * a.cap + a.t0;
-        R.rx = buffer_rsrc(reinterpret_cast<const uint8_t*>(a.x) + st * a.n_tokens * (int64_t)(2 * D), (int)(a.n_tokens * 2 * D));
-        R.rid = buffer_rsrc(a.packed + a.off_idx + rec0 * (int64_t)(D * B / 8), (int)(a.n_tokens * (D * B / 8)));
-        R.rnm = buffer_rsrc(a.packed + a.off_norm + rec0 * 2, (int)(a.n_tokens * 2));
-        R.rsk = R.rrn = R.rnm;
-        if (qjl) {
-            R.rsk = buffer_rsrc(a.packed + a.off_sketch + rec0 * (int64_t)(a.t.m / 8), (int)(a.n_tokens * (a.t.m / 8)));
-            R.rrn = buffer_rsrc(a.packed + a.off_rnorm + rec0 * 2, (int)(a.n_tokens * 2));
-        }
-        return R;
-    };
-    const FqBufs RK = bufs(ak, QJL), RV = bufs(av, false);
+    const FqBufs RK = fq_bufs<D, B>(ak, st, QJL), RV = fq_bufs<D, B>(av, st, false);
     uint32_t wk[D / 8], wv[D / 8];
     const int64_t t_first = tb0 + wave;
     bload<2 * C, 16>(RK.rx, (uint32_t)(t_first * 16 + v) * (2 * D) + 2 * g * C, 0u, wk);
@@ -980,8 +901,8 @@ __global__ __launch_bounds__(768, 1) void encode_kv_kernel(EncodeArgs ak, Encode
 #pragma unroll 1
     for (int64_t t = t_first; t < tb1; t += NWV) {
         asm volatile("" ::: "memory");
-        fq_encode_group<D, B, QJL>(ldsb, 0, pSk, rht, m, RK, wk, t, t + NWV, tb1, ak.n_tokens, lane);
-        fq_encode_group<D, B, false>(ldsb, pAv, 0, false, 0, RV, wv, t, t + NWV, tb1, av.n_tokens, lane);
+        fq_encode_group<D, B, QJL>(ldsb, 0, pSk, rht, false, m, RK, wk, t, t + NWV, tb1, ak.n_tokens, lane);
+        fq_encode_group<D, B, false>(ldsb, pAv, 0, false, false, 0, RV, wv, t, t + NWV, tb1, av.n_tokens, lane);
     }
 }
 
@@ -1013,15 +934,15 @@ static hipError_t launch_kv_db(const EncodeArgs& ak, const EncodeArgs& av, int n
     const bool qjl = ak.t.m > 0;
     const void* kern = qjl ? reinterpret_cast<const void*>(&encode_kv_kernel<D, B, true>)
                            : reinterpret_cast<const void*>(&encode_kv_kernel<D, B, false>);
-    const int64_t target = (int64_t)num_cus * blocks_per_cu(kern, 0, 768);
+    const int64_t target = (int64_t)num_cus * blocks_per_cu(kern, 0, 64 * kFqWaves);
     int64_t bps = (target + ak.n_streams - 1) / ak.n_streams;
     if (bps > ak.tiles_per_stream) bps = ak.tiles_per_stream;
     if (bps < 1) bps = 1;
     k.blocks_per_stream = v.blocks_per_stream = bps;
     k.tiles_per_block = v.tiles_per_block = (ak.tiles_per_stream + bps - 1) / bps;
     const dim3 grid((unsigned)(ak.n_streams * bps));
-    if (qjl) hipLaunchKernelGGL((encode_kv_kernel<D, B, true>), grid, dim3(768), 0, s, k, v);
-    else hipLaunchKernelGGL((encode_kv_kernel<D, B, false>), grid, dim3(768), 0, s, k, v);
+    if (qjl) hipLaunchKernelGGL((encode_kv_kernel<D, B, true>), grid, dim3(64 * kFqWaves), 0, s, k, v);
+    else hipLaunchKernelGGL((encode_kv_kernel<D, B, false>), grid, dim3(64 * kFqWaves), 0, s, k, v);
     return hipGetLastError();
 }
 
@@ -1066,8 +987,8 @@ template <int D, int B, bool QJL>
 static hipError_t launch_fq(const EncodeArgs& a, int num_cus, hipStream_t s) {
     EncodeArgs b = a;
     b.grid_rep_log2 = 0;
-    const void* kern = reinterpret_cast<const void*>(&encode_kernel<D, B, QJL, true, true, true>);
-    const int threads = 64 * enc_waves<D, QJL, true, true, true>();   // static LDS only
+    const void* kern = reinterpret_cast<const void*>(&encode_fq_kernel<D, B, QJL>);
+    const int threads = 64 * kFqWaves;                                 // static LDS only
     const int64_t target = (int64_t)num_cus * blocks_per_cu(kern, 0, threads);
     int64_t bps = (target + a.n_streams - 1) / a.n_streams;
     if (bps > a.tiles_per_stream) bps = a.tiles_per_stream;
@@ -1075,7 +996,7 @@ static hipError_t launch_fq(const EncodeArgs& a, int num_cus, hipStream_t s) {
     b.blocks_per_stream = bps;
     b.tiles_per_block = (a.tiles_per_stream + bps - 1) / bps;
     const dim3 grid((unsigned)(a.n_streams * bps));
-    hipLaunchKernelGGL((encode_kernel<D, B, QJL, true, true, true>), grid, dim3(threads), 0, s, b);
+    hipLaunchKernelGGL((encode_fq_kernel<D, B, QJL>), grid, dim3(threads), 0, s, b);
     return hipGetLastError();
 }
 
@@ -1106,8 +1027,8 @@ static hipError_t launch_one(const EncodeArgs& a, int num_cus, hipStream_t s) {
     b.grid_rep_log2 = rl;
     const size_t head_bytes = (grid_bytes << rl) + fixed;
     const size_t lds = head_bytes + (s_lds ? s_bytes : 0);
-    const void* kern = s_lds ? reinterpret_cast<const void*>(&encode_kernel<D, B, QJL, BF16, true, false>)
-                             : reinterpret_cast<const void*>(&encode_kernel<D, B, QJL, BF16, (D <= 128), false>);
+    const void* kern = s_lds ? reinterpret_cast<const void*>(&encode_kernel<D, B, QJL, BF16, true>)
+                             : reinterpret_cast<const void*>(&encode_kernel<D, B, QJL, BF16, (D <= 128)>);
     if (lds > 65536) {           // above the default dynamic LDS limit: raise it once per kernel
         static std::mutex mu;
         static bool raised = false;
@@ -1119,7 +1040,7 @@ static hipError_t launch_one(const EncodeArgs& a, int num_cus, hipStream_t s) {
         }
     }
     // one wave of blocks: as many blocks as fit on every CU at once
-    const int threads = 64 * (s_lds ? enc_waves<D, QJL, BF16, true, false>() : enc_waves<D, QJL, BF16, (D <= 128), false>());
+    const int threads = 64 * (s_lds ? enc_waves<D, QJL, BF16, true>() : enc_waves<D, QJL, BF16, (D <= 128)>());
     const int64_t target = (int64_t)num_cus * blocks_per_cu(kern, lds, threads);
     int64_t bps = (target + a.n_streams - 1) / a.n_streams;
     if (bps > a.tiles_per_stream) bps = a.tiles_per_stream;
@@ -1128,10 +1049,10 @@ static hipError_t launch_one(const EncodeArgs& a, int num_cus, hipStream_t s) {
     b.tiles_per_block = (a.tiles_per_stream + bps - 1) / bps;
     const dim3 grid((unsigned)(a.n_streams * bps));
     if constexpr (D <= 128) {
-        hipLaunchKernelGGL((encode_kernel<D, B, QJL, BF16, true, false>), grid, dim3(threads), lds, s, b);
+        hipLaunchKernelGGL((encode_kernel<D, B, QJL, BF16, true>), grid, dim3(threads), lds, s, b);
     } else {
-        if (s_lds) hipLaunchKernelGGL((encode_kernel<D, B, QJL, BF16, true, false>), grid, dim3(threads), lds, s, b);
-        else hipLaunchKernelGGL((encode_kernel<D, B, QJL, BF16, false, false>), grid, dim3(threads), lds, s, b);
+        if (s_lds) hipLaunchKernelGGL((encode_kernel<D, B, QJL, BF16, true>), grid, dim3(threads), lds, s, b);
+        else hipLaunchKernelGGL((encode_kernel<D, B, QJL, BF16, false>), grid, dim3(threads), lds, s, b);
     }
     return hipGetLastError();
 }
