@@ -2,6 +2,10 @@
 // §2 TurboQuant): per vector x, n = ||x||, y = H (x ⊙ s) / (sqrt(d) n), idx_j = #{i : t_i <= y_j},
 // b-bit packing; with m > 0 also e = y - c[idx], ||e|| and sign(S e) (1-bit QJL of the residual).
 //
+// Three kernels: the search-grid encode (encode_kernel: any d, b and input type), the binade-grid
+// encode of one tensor (encode_fq_kernel: bf16 input, b <= 4, d <= 128) and the binade-grid encode of
+// the keys and values of the same tokens in one launch (encode_kv_kernel); the last two share the
+// per-group code (fq_encode_group).
 // Work split: one wave64 = 16 vectors x 4 parts (see common.hpp).  Waves walk a contiguous range of
 // 16-vector tiles, so the per-head sign constants are reloaded only when the stream changes.
 // Search: a uniform grid over y in [-1,1] held in LDS maps y to the one threshold that can lie in
