@@ -35,15 +35,15 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published (the sketch p
 # the kernel's sources are the ones it was measured on (sha256 of the .hip file + shared headers).
 FETCH_UNIT_B, WRITE_UNIT_B = 2048, 1024
 TRAFFIC = {
-    "encode_kv": {"fetch": 4194695.125, "write": 2493528.875, "src": "encode.hip",
-        "sha": "f0b42740b4f9412634f6b99bf3c02ce72f038ab034c58b00b85d1235c587faab"},
-    "encode_k": {"fetch": 2097510.5, "write": 1394835.8125, "src": "encode.hip",
-        "sha": "f0b42740b4f9412634f6b99bf3c02ce72f038ab034c58b00b85d1235c587faab"},
-    "encode_v": {"fetch": 2109701.75, "write": 1090989.5, "src": "encode.hip",
-        "sha": "f0b42740b4f9412634f6b99bf3c02ce72f038ab034c58b00b85d1235c587faab"},
-    "decode_attention": {"fetch": 1233018.3125, "write": 6240.0, "src": "attention.hip",
+    "encode_kv": {"fetch": 4194704.0, "write": 2493893.8125, "src": "encode.hip",
+        "sha": "992d71c591d2d8a443bf0051e0ef8e31966255a4ca7629b73e9250ddda24daac"},
+    "encode_k": {"fetch": 2097505.5, "write": 1394466.5625, "src": "encode.hip",
+        "sha": "992d71c591d2d8a443bf0051e0ef8e31966255a4ca7629b73e9250ddda24daac"},
+    "encode_v": {"fetch": 2110658.875, "write": 1090979.96875, "src": "encode.hip",
+        "sha": "992d71c591d2d8a443bf0051e0ef8e31966255a4ca7629b73e9250ddda24daac"},
+    "decode_attention": {"fetch": 1233019.8125, "write": 6241.0, "src": "attention.hip",
         "sha": "4a5ef5d6cf48758bd8ce022548ab11229a28468c121500b993a01171da50a630"},
-    "decode_v_bf16": {"fetch": 550434.875, "write": 4194304.0, "src": "decode.hip",
+    "decode_v_bf16": {"fetch": 550671.375, "write": 4194304.0, "src": "decode.hip",
         "sha": "b1ba67ba042266686af375dd30fa7fbae0fbf2bf933c7820de5b5978f1c26054"},
 }
 TRAFFIC["decode_attention_back_to_back"] = TRAFFIC["decode_attention"]
