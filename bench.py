@@ -229,6 +229,16 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         kern["append_k_1_token"] = {"us": round(e0.elapsed_time(e1) / 20 * 1e3, 2), "vectors": streams}
+        # the decode step's append of one key and one value per stream, in one launch
+        v1 = V[:, -1:].contiguous()
+        T.encode_kv_append(ck, cv, x1, v1, pk, pv, N, N - 1)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(20):
+            T.encode_kv_append(ck, cv, x1, v1, pk, pv, N, N - 1)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        kern["append_kv_1_token"] = {"us": round(e0.elapsed_time(e1) / 20 * 1e3, 2), "vectors": 2 * streams}
         lens = torch.linspace(N // 2, N, B).to(torch.int32).to(dev)
         T.decode_attention(ck, cv, q, pk, pv, Hkv, N, out=out, workspace=ws, lengths=lens)
         torch.cuda.synchronize()

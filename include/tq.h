@@ -120,6 +120,15 @@ int tq_encode_kv(const tq_params* pk, const tq_params* pv, const void* k, const 
                  tq_dtype x_dtype, int64_t n_streams, int64_t n_tokens, void* packed_k,
                  void* packed_v, void* stream);
 
+/* tq_encode_kv into tokens [t0, t0 + n_new) of caches laid out for `capacity` tokens per stream
+ * (layouts of pk and pv at n_streams x capacity): the same records as tq_encode_append on each
+ * side, in one launch under the same conditions (the decode step's append of one key and one value
+ * per stream is one launch).  TQ_EINVAL unless 0 <= t0 and t0 + n_new <= capacity; otherwise as
+ * tq_encode_kv. */
+int tq_encode_kv_append(const tq_params* pk, const tq_params* pv, const void* k, const void* v,
+                        tq_dtype x_dtype, int64_t n_streams, int64_t n_new, void* packed_k,
+                        void* packed_v, int64_t capacity, int64_t t0, void* stream);
+
 /* Decode the MSE reconstruction x̂ = n16 · s ⊙ (H c[idx]) / sqrt(d) into x_hat
  * [n_streams][n_tokens][d] (F32 or BF16).  The QJL sketch is not applied. */
 int tq_decode(const tq_params* p, const void* packed, int64_t n_streams, int64_t n_tokens,

@@ -94,6 +94,25 @@ def encode_kv(ck: Codec, cv: Codec, k: torch.Tensor, v: torch.Tensor, out_k: tor
     return outs[0], outs[1]
 
 
+def encode_kv_append(ck: Codec, cv: Codec, k: torch.Tensor, v: torch.Tensor, packed_k: torch.Tensor,
+                     packed_v: torch.Tensor, capacity: int, t0: int):
+    """Keys and values of the same new tokens (tq_encode_kv_append): k, v [n_streams, n_new, d] into
+    tokens [t0, t0 + n_new) of caches laid out for n_streams x capacity tokens."""
+    for x, c in ((k, ck), (v, cv)):
+        if x.dim() != 3 or x.shape[-1] != c.d or not x.is_contiguous():
+            raise ValueError("k and v must be contiguous [n_streams, n_new, d] tensors")
+    if k.shape[:2] != v.shape[:2] or k.dtype != v.dtype:
+        raise ValueError("k and v must have the same streams, tokens and dtype")
+    S, N, _ = k.shape
+    for c, pb in ((ck, packed_k), (cv, packed_v)):
+        if pb.dtype != torch.uint8 or pb.numel() < get_layout(c, S, capacity)["total_bytes"]:
+            raise ValueError("packed buffer too small for the capacity")
+    _lib.check(_lib.lib().tq_encode_kv_append(ctypes.byref(ck.params()), ctypes.byref(cv.params()), _ptr(k), _ptr(v),
+                                              _DT[k.dtype], S, N, _ptr(packed_k), _ptr(packed_v), capacity, t0,
+                                              _stream(k.device)), "tq_encode_kv_append")
+    return packed_k, packed_v
+
+
 def encode_append(codec: Codec, x: torch.Tensor, packed: torch.Tensor, capacity: int, t0: int) -> torch.Tensor:
     """x: [n_streams, n_new, d] -> tokens [t0, t0 + n_new) of `packed`, a buffer laid out for
     n_streams x capacity tokens (get_layout(codec, n_streams, capacity))."""

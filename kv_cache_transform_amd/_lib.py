@@ -16,7 +16,7 @@ TQ_SKETCH_GAUSSIAN, TQ_SKETCH_RHT = 0, 1
 TQ_ROTATION_WHT, TQ_ROTATION_NONE = 0, 1
 
 # every symbol include/tq.h declares
-EXPORTS = ("tq_get_layout", "tq_encode", "tq_encode_kv", "tq_encode_append", "tq_decode", "tq_decode_qjl", "tq_scores_workspace_bytes", "tq_qk_scores",
+EXPORTS = ("tq_get_layout", "tq_encode", "tq_encode_kv", "tq_encode_kv_append", "tq_encode_append", "tq_decode", "tq_decode_qjl", "tq_scores_workspace_bytes", "tq_qk_scores",
            "tq_attention_workspace_bytes", "tq_decode_attention", "tq_decode_attention_varlen",
            "tq_decode_attention_noalloc", "tq_attention_noalloc_max_bytes", "tq_host_tables",
            "tq_status_string",
@@ -76,6 +76,7 @@ def lib() -> ctypes.CDLL:
         "tq_encode": (ctypes.c_int, [P, VP, ctypes.c_int, I64, I64, VP, VP]),
         "tq_encode_append": (ctypes.c_int, [P, VP, ctypes.c_int, I64, I64, VP, I64, I64, VP]),
         "tq_encode_kv": (ctypes.c_int, [P, P, VP, VP, ctypes.c_int, I64, I64, VP, VP, VP]),
+        "tq_encode_kv_append": (ctypes.c_int, [P, P, VP, VP, ctypes.c_int, I64, I64, VP, VP, I64, I64, VP]),
         "tq_decode": (ctypes.c_int, [P, VP, I64, I64, VP, ctypes.c_int, VP]),
         "tq_decode_qjl": (ctypes.c_int, [P, VP, I64, I64, VP, ctypes.c_int, VP]),
         "tq_scores_workspace_bytes": (SZ, [P, I64, I64]),

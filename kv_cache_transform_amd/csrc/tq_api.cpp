@@ -416,14 +416,16 @@ int tq_encode(const tq_params* p, const void* x, tq_dtype x_dtype, int64_t n_str
     return tq_encode_append(p, x, x_dtype, n_streams, n_tokens, packed, n_tokens, 0, stream);
 }
 
-int tq_encode_kv(const tq_params* pk, const tq_params* pv, const void* k, const void* v, tq_dtype x_dtype,
-                 int64_t n_streams, int64_t n_tokens, void* packed_k, void* packed_v, void* stream) {
+int tq_encode_kv_append(const tq_params* pk, const tq_params* pv, const void* k, const void* v, tq_dtype x_dtype,
+                        int64_t n_streams, int64_t n_new, void* packed_k, void* packed_v, int64_t capacity,
+                        int64_t t0, void* stream) {
     int rc = check_params(pk);
     if (rc != TQ_OK) return rc;
     if ((rc = check_params(pv)) != TQ_OK) return rc;
-    if (n_streams < 0 || n_tokens < 0) return TQ_EINVAL;
+    if (n_streams < 0 || n_new < 0 || capacity < 0 || t0 < 0 || t0 > capacity || n_new > capacity - t0)
+        return TQ_EINVAL;
     if (x_dtype != TQ_F32 && x_dtype != TQ_BF16) return TQ_EINVAL;
-    if (n_streams == 0 || n_tokens == 0) return TQ_OK;
+    if (n_streams == 0 || n_new == 0) return TQ_OK;
     if (!k || !v || !packed_k || !packed_v) return TQ_EINVAL;
     if (!aligned16(k) || !aligned16(v) || !aligned16(packed_k) || !aligned16(packed_v)) return TQ_EALIGN;
     DevTables tk, tv;
@@ -432,19 +434,19 @@ int tq_encode_kv(const tq_params* pk, const tq_params* pv, const void* k, const 
     if ((rc = get_tables(pv, &tv, &cus)) != TQ_OK) return rc;
     auto args = [&](const tq_params* p, const DevTables& t, const void* x, void* packed) {
         tq_layout lay;
-        layout_of(p, n_streams, n_tokens, &lay);
+        layout_of(p, n_streams, capacity, &lay);
         EncodeArgs a{};
         a.x = x;
         a.packed = static_cast<uint8_t*>(packed);
         a.n_streams = n_streams;
-        a.n_tokens = n_tokens;
-        a.cap = n_tokens;
-        a.t0 = 0;
+        a.n_tokens = n_new;
+        a.cap = capacity;
+        a.t0 = t0;
         a.off_idx = lay.off_idx;
         a.off_sketch = lay.off_sketch;
         a.off_norm = lay.off_norm;
         a.off_rnorm = lay.off_rnorm;
-        a.tiles_per_stream = (n_tokens + 15) / 16;
+        a.tiles_per_stream = (n_new + 15) / 16;
         a.n_tiles = n_streams * a.tiles_per_stream;
         a.t = t;
         return a;
@@ -458,6 +460,12 @@ int tq_encode_kv(const tq_params* pk, const tq_params* pv, const void* k, const 
     }
     if ((rc = hip_status(launch_encode(ak, x_dtype == TQ_BF16, cus, s))) != TQ_OK) return rc;
     return hip_status(launch_encode(av, x_dtype == TQ_BF16, cus, s));
+}
+
+int tq_encode_kv(const tq_params* pk, const tq_params* pv, const void* k, const void* v, tq_dtype x_dtype,
+                 int64_t n_streams, int64_t n_tokens, void* packed_k, void* packed_v, void* stream) {
+    if (n_tokens < 0) return TQ_EINVAL;
+    return tq_encode_kv_append(pk, pv, k, v, x_dtype, n_streams, n_tokens, packed_k, packed_v, n_tokens, 0, stream);
 }
 
 int tq_decode(const tq_params* p, const void* packed, int64_t n_streams, int64_t n_tokens, void* x_hat,

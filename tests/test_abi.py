@@ -121,6 +121,9 @@ def test_argument_validation_before_any_gpu_call():
     assert L.tq_encode_kv(pkv, p, x16, ctypes.c_void_p(24), 1, 2, 2, b16, b16, None) == _lib.TQ_EALIGN
     assert L.tq_encode_kv(pkv, p, None, None, 1, 0, 5, None, None, None) == _lib.TQ_OK
     assert L.tq_encode_kv(pkv, p, None, None, 1, 3, 0, None, None, None) == _lib.TQ_OK
+    assert L.tq_encode_kv_append(pkv, p, x16, x16, 1, 2, 5, b16, b16, 10, 6, None) == _lib.TQ_EINVAL   # 6 + 5 > 10
+    assert L.tq_encode_kv_append(pkv, p, x16, x16, 1, 2, 5, b16, b16, 10, -1, None) == _lib.TQ_EINVAL
+    assert L.tq_encode_kv_append(pkv, p, x16, x16, 1, 2, 0, b16, b16, 10, 10, None) == _lib.TQ_OK  # empty append
     assert L.tq_decode(p, None, 3, 0, None, 0, None) == _lib.TQ_OK
     # scores: workspace too small, too many queries
     pk = _p(m=128)

@@ -107,3 +107,20 @@ def test_encode_kv_is_deterministic_and_validates():
         T.encode_kv(ck, cv, k, v[:, :300].contiguous())
     with pytest.raises(ValueError):
         T.encode_kv(ck, cv, k, v.float())
+
+
+@pytest.mark.parametrize("m,sk,n_new,t0,cap", [(128, 0, 1, 999, 1000), (128, 0, 17, 300, 1000), (128, 1, 40, 0, 64),
+                                               (0, 0, 1, 0, 1), (64, 0, 33, 100, 200)])
+def test_encode_kv_append_equals_two_appends(m, sk, n_new, t0, cap):
+    """the decode step's append of new keys and values into caches of a given capacity, in one launch:
+    the same bytes as two tq_encode_append calls (the rest of the caches untouched)"""
+    print(f"encode_kv_append m={m} sketch={sk} n_new={n_new} t0={t0} capacity={cap}", flush=True)
+    S, H = 4, 2
+    ck, cv = T.Codec(128, 4, m, H, 7401, sketch=sk), T.Codec(128, 4, 0, H, 7402)
+    k = I.gaussian((S, n_new, 128), 61 + n_new, device=DEV, dtype=torch.bfloat16)
+    v = I.gaussian((S, n_new, 128), 62 + n_new, device=DEV, dtype=torch.bfloat16)
+    zc = lambda c: torch.zeros(T.get_layout(c, S, cap)["total_bytes"], dtype=torch.uint8, device=DEV)
+    fk, fv = T.encode_kv_append(ck, cv, k, v, zc(ck), zc(cv), cap, t0)
+    rk, rv = T.encode_append(ck, k, zc(ck), cap, t0), T.encode_append(cv, v, zc(cv), cap, t0)
+    torch.cuda.synchronize()
+    assert torch.equal(fk, rk) and torch.equal(fv, rv)
