@@ -292,6 +292,13 @@ __device__ __forceinline__ void attn_chunk(const AttnChunk<AttnGeom<D, BK, BV>::
                 const uint32_t sb = __builtin_amdgcn_ubfe(wsk, 8 * (k & 3), 8);
                 const half8 sa = *reinterpret_cast<const half8*>(sg8 + sb * 64u);
                 s2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(sa, pb[k], s2, 0, 0, 0);
+                if constexpr (!PQ) s2 = __builtin_amdgcn_mfma_f32_16x16x32_f16(sa, pb[KS + k], s2, 0, 0, 0);
+            }
+            if constexpr (PQ) {
+                // column q + 8 holds the signs against the lo part of query q's projection
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    s2[i] += u2f((uint32_t)__builtin_amdgcn_update_dpp(0, (int)f2u(s2[i]), 0x108, 0xf, 0xf, true));
             }
         }
         // output lane (q = l16, g) holds tokens t0 + 16T + 4g + i; the queries (and their sketch
@@ -399,6 +406,78 @@ void attn_kernel(AttnArgs a) {
     __shared__ uint32_t vlut2[Gm::VPAIR && !KV ? 256 * VR : 1];  // copy c of entry e at word e VR + c
     __shared__ uint32_t kvlut[KV ? 2 * 256 * 64 : 1];             // the two tables of 256-byte rows
     __shared__ u32x4 sgn8[QJL ? 256 * 4 : 1];                      // copy c of byte e's ±2^12 halves at e·4 + c
+    // The query prep of the block's stream, when every wave of the block works on that one stream
+    // (a.fused_q, chosen by the host): the query prep kernel's steps for the group's rows, in the same
+    // order and precision, with the rows' operands left in LDS (q_rot and S q_rot in fp32, then per
+    // row the fp16 hi and lo parts of 2^e q_rot q_scale and of 2^e S q_rot p_scale, and the row factor
+    // 2^-e).  Thread i < m fetches row i of S first; wave r < group rotates row r.  The hi and lo
+    // parts of row r's projection overwrite its fp32 values in place (halves r·256 + i and r·256 +
+    // 128 + i), which only wave r reads, and before it writes.
+    constexpr bool FQP = KV && PQ && D <= 128;
+    constexpr int FQM = QJL ? 128 : 0;                             // m <= 128 on this path
+    constexpr int FQS = 2 * D;                                     // halves per row of fq_h
+    __shared__ float fq_rot[FQP ? 8 * D : 1];
+    __shared__ __attribute__((aligned(16))) float fq_p[FQP && QJL ? 8 * 128 : 4];
+    __shared__ __attribute__((aligned(16))) _Float16 fq_h[FQP ? 8 * FQS : 8];
+    _Float16* const fq_ph = reinterpret_cast<_Float16*>(fq_p);
+    __shared__ float fq_rf[FQP ? 8 : 1];
+    u32x4 srow[FQP && QJL ? D / 8 : 1];
+    if constexpr (FQP) {
+        if (a.fused_q) {
+            constexpr int PL = D / 64;
+            const int wv = wave_id(), lane = threadIdx.x & 63;
+            const int64_t st_b = ((int64_t)blockIdx.x * (blockDim.x >> 6)) / a.n_split;
+            const int b_b = (int)(st_b / a.n_kv_heads), h_b = (int)(st_b - (int64_t)b_b * a.n_kv_heads);
+            const int hs = (int)(st_b % a.tk.n_heads);
+            if constexpr (QJL) {
+                if ((int)threadIdx.x < a.tk.m) {
+                    const u32x4* sp = reinterpret_cast<const u32x4*>(a.tk.S + ((int64_t)hs * a.tk.m + threadIdx.x) * D);
+#pragma unroll
+                    for (int k = 0; k < D / 8; ++k) srow[k] = sp[k];
+                }
+            }
+            if (wv < a.group) {
+                // lane l holds coordinates PL l + c: the low index bits in the lane, the rest as
+                // lane-xor butterflies, stage by stage from the lowest bit
+                const int64_t row = (int64_t)b_b * a.n_q_heads + (int64_t)h_b * a.group + wv;
+                const bool rot = a.tk.rotation != 1;
+                float v[PL];
+                const float* sg = a.tk.signs + (int64_t)hs * D + PL * lane;
+#pragma unroll
+                for (int c = 0; c < PL; ++c) {
+                    const int64_t j = row * D + PL * lane + c;
+                    const float x = a.q_bf16 ? u2f(uint32_t(reinterpret_cast<const uint16_t*>(a.q)[j]) << 16)
+                                             : reinterpret_cast<const float*>(a.q)[j];
+                    v[c] = rot ? x * sg[c] : x;
+                }
+                if (rot) {
+#pragma unroll
+                    for (int h = 1; h < PL; h <<= 1)
+#pragma unroll
+                        for (int c = 0; c < PL; ++c)
+                            if (!(c & h)) {
+                                const float x0 = v[c], x1 = v[c + h];
+                                v[c] = x0 + x1;
+                                v[c + h] = x0 - x1;
+                            }
+#pragma unroll
+                    for (int hl = 1; hl < 64; hl <<= 1) {
+                        const bool hi = (lane & hl) != 0;
+#pragma unroll
+                        for (int c = 0; c < PL; ++c) {
+                            const float o = __shfl_xor(v[c], hl);
+                            v[c] = hi ? o - v[c] : v[c] + o;
+                        }
+                    }
+                    const float inv = 1.0f / sqrtf((float)D);
+#pragma unroll
+                    for (int c = 0; c < PL; ++c) v[c] *= inv;
+                }
+#pragma unroll
+                for (int c = 0; c < PL; ++c) fq_rot[wv * D + PL * lane + c] = v[c];
+            }
+        }
+    }
     if constexpr (KV) {
         // a straight copy of the prebuilt images in 16-byte pieces: a piece of table 0 in words
         // 0-31 of its row (piece index % 16 < 8) holds value pairs, all else comes from the K codec
@@ -449,6 +528,69 @@ void attn_kernel(AttnArgs a) {
             sgn8[i] = w;
         }
     __syncthreads();
+    if constexpr (FQP) {
+        if (a.fused_q) {
+            constexpr int PL = D / 64;
+            const int G = a.group, m = QJL ? a.tk.m : 0;
+            if constexpr (QJL) {
+                // p_i = sum_j S_ij q_rot_j in index order, for each row of the group
+                if ((int)threadIdx.x < m)
+                    for (int r = 0; r < G; ++r) {
+                        float acc = 0.0f;
+#pragma unroll
+                        for (int k = 0; k < D / 8; ++k) {
+                            const half8 hs = __builtin_bit_cast(half8, srow[k]);
+#pragma unroll
+                            for (int u = 0; u < 8; ++u) acc = fmaf((float)hs[u], fq_rot[r * D + 8 * k + u], acc);
+                        }
+                        fq_p[r * 128 + threadIdx.x] = acc * a.p_scale;
+                    }
+                __syncthreads();
+            }
+            const int wv = wave_id(), lane = threadIdx.x & 63;
+            if (wv < G) {
+                // 2^e with the row's largest entry in [2^13, 2^14) (an all-zero or non-finite row keeps
+                // e = 0); hi the nearest fp16, lo the nearest fp16 of the remainder
+                float qv[PL], pv[2];
+                float mx = 0.0f;
+#pragma unroll
+                for (int c = 0; c < PL; ++c) {
+                    qv[c] = fq_rot[wv * D + PL * lane + c] * a.q_scale;
+                    mx = fmaxf(mx, fabsf(qv[c]));
+                }
+#pragma unroll
+                for (int c = 0; c < 2; ++c) {
+                    const int i = lane + 64 * c;
+                    pv[c] = (QJL && i < m) ? fq_p[wv * 128 + i] : 0.0f;
+                    mx = fmaxf(mx, fabsf(pv[c]));
+                }
+                for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o));
+                const int ex = (int)((f2u(mx) >> 23) & 0xffu);
+                const int e = (mx > 0.0f && ex < 255) ? 13 - (ex == 0 ? -126 : ex - 127) : 0;
+                _Float16* hrow = fq_h + wv * FQS;
+#pragma unroll
+                for (int c = 0; c < PL; ++c) {
+                    const float sv = __builtin_amdgcn_ldexpf(qv[c], e);
+                    const _Float16 h = (_Float16)sv;
+                    hrow[PL * lane + c] = h;
+                    hrow[D + PL * lane + c] = (_Float16)(sv - (float)h);
+                }
+                if constexpr (QJL)
+#pragma unroll
+                    for (int c = 0; c < 2; ++c) {
+                        const int i = lane + 64 * c;
+                        const float sv = __builtin_amdgcn_ldexpf(pv[c], e);
+                        const _Float16 h = (_Float16)sv;
+                        if (i < m) {
+                            fq_ph[wv * (2 * FQM) + i] = h;
+                            fq_ph[wv * (2 * FQM) + FQM + i] = (_Float16)(sv - (float)h);
+                        }
+                    }
+                if (lane == 0) fq_rf[wv] = __builtin_amdgcn_ldexpf(1.0f, -e);
+            }
+            __syncthreads();
+        }
+    }
 
     const int lane = threadIdx.x & 63;
     const int l16 = lane & 15, g = lane >> 4;
@@ -484,12 +626,16 @@ void attn_kernel(AttnArgs a) {
     const int qcol = PQ ? (l16 & 7) : l16;
     const bool qload = qcol < a.group;
     const int64_t qrow = (int64_t)bidx * a.n_q_heads + (int64_t)kvh * a.group + (qload ? qcol : 0);
-    half8 qb[KS], qbl[KS], pb[QJL ? KS : 1];
-    const float rowf = a.o.rowf[qrow] * (1.0f / 4096.0f);
+    half8 qb[KS], qbl[KS], pb[QJL ? (PQ ? KS : 2 * KS) : 1];   // without PQ, pb[KS + k] the lo parts
+    const bool fq = FQP && a.fused_q;
+    const int qloc = qload ? qcol : 0;                 // the row within the group
+    const float rowf = (fq ? fq_rf[qloc] : a.o.rowf[qrow]) * (1.0f / 4096.0f);
 #pragma unroll
     for (int k = 0; k < KS; ++k) {
-        const half8 qh = *reinterpret_cast<const half8*>(a.o.qh + qrow * D + g * C + 8 * k);
-        const half8 ql = *reinterpret_cast<const half8*>(a.o.ql + qrow * D + g * C + 8 * k);
+        const half8 qh = fq ? *reinterpret_cast<const half8*>(fq_h + qloc * FQS + g * C + 8 * k)
+                            : *reinterpret_cast<const half8*>(a.o.qh + qrow * D + g * C + 8 * k);
+        const half8 ql = fq ? *reinterpret_cast<const half8*>(fq_h + qloc * FQS + D + g * C + 8 * k)
+                            : *reinterpret_cast<const half8*>(a.o.ql + qrow * D + g * C + 8 * k);
         if constexpr (PQ) {
             qb[k] = !qload ? half8{} : (l16 < 8 ? qh : ql);
         } else {
@@ -497,9 +643,20 @@ void attn_kernel(AttnArgs a) {
             qbl[k] = qvalid ? ql : half8{};
         }
         if constexpr (QJL) {
-            if (k < mks) pb[k] = *reinterpret_cast<const half8*>(a.o.ph + qrow * m + g * (m / 4) + 8 * k);
-            else pb[k] = half8{};
-            if (!qload || (PQ && l16 >= 8)) pb[k] = half8{};
+            // PQ: columns 8-15 carry the lo parts of the sketch projection, so the sketch term is
+            // fp32-accurate like the scores (a sharp softmax amplifies an fp16 rounding of it)
+            const bool plo = PQ && l16 >= 8;
+            if (k < mks) {
+                const int o = g * (m / 4) + 8 * k;
+                pb[k] = fq ? *reinterpret_cast<const half8*>(fq_ph + qloc * (2 * FQM) + (plo ? FQM : 0) + o)
+                           : *reinterpret_cast<const half8*>((plo ? a.o.pl : a.o.ph) + qrow * m + o);
+                if constexpr (!PQ) pb[KS + k] = *reinterpret_cast<const half8*>(a.o.pl + qrow * m + o);
+            } else {
+                pb[k] = half8{};
+                if constexpr (!PQ) pb[KS + k] = half8{};
+            }
+            if (!qload) pb[k] = half8{};
+            if constexpr (!PQ) if (!qload) pb[KS + k] = half8{};
         }
     }
 
@@ -710,6 +867,16 @@ static hipError_t launch_one(const AttnArgs& a, hipStream_t s) {
 template <int D, int B>
 static hipError_t launch_db(const AttnArgs& a, hipStream_t s) {
     return a.tk.m > 0 ? launch_one<D, B, B, true>(a, s) : launch_one<D, B, B, false>(a, s);
+}
+
+bool attention_fuses_qprep(const AttnArgs& a) {
+    // the 768-thread geometry (4-bit keys and values, d <= 128, at most 8 query heads per kv head)
+    // with every block's 12 waves on one stream; S rows fit the prep's LDS (m <= 128)
+    const int d = a.tk.d;
+    if (!(a.tk.b == 4 && a.tv.b == 4 && d <= 128 && a.group <= 8 && a.tk.m <= 128)) return false;
+    constexpr int waves = attn_threads<128, 4, 4, true>() / 64;
+    static_assert(attn_threads<64, 4, 4, true>() == attn_threads<128, 4, 4, true>(), "one geometry at d <= 128");
+    return a.n_split % waves == 0;
 }
 
 bool attention_supported(int d, int bk, int bv) {

@@ -111,6 +111,13 @@ struct AttnArgs {
     int64_t k_off_idx, k_off_sketch, k_off_norm, k_off_rnorm;
     int64_t v_off_idx, v_off_norm;
     DevTables tk, tv;
+    // the query prep inside the attention kernel (attention_fuses_qprep): each block computes its
+    // stream's query operands from the raw queries q [batch][n_q_heads][d] (bf16 if q_bf16, else
+    // fp32), scaled by q_scale and p_scale as the query prep kernel does; else o holds them
+    int fused_q;
+    const void* q;
+    int q_bf16;
+    float q_scale, p_scale;
 };
 
 // launchers: return hipSuccess or the launch error
@@ -122,6 +129,10 @@ hipError_t launch_decode_qjl(const DecodeArgs& a, bool out_bf16, int num_cus, hi
 hipError_t launch_qprep(const QPrepArgs& a, hipStream_t s);
 hipError_t launch_scores(const ScoresArgs& a, int num_cus, hipStream_t s);
 bool attention_supported(int d, int bk, int bv);
+// whether launch_attention computes the query operands inside the attention kernel (every block's
+// waves work on one stream, 4-bit keys and values, d <= 128, at most 8 query heads per kv head,
+// m <= 128), so no query prep launch is needed
+bool attention_fuses_qprep(const AttnArgs& a);
 hipError_t launch_attention(const AttnArgs& a, int num_cus, hipStream_t s, bool* supported);
 
 }  // namespace tq

@@ -646,7 +646,6 @@ int attention_impl(const tq_params* pk, const tq_params* pv, const void* q, tq_d
     const float scale_log2 = scale * 1.4426950408889634f;
     qa.q_scale = scale_log2;
     qa.p_scale = pk->m > 0 ? scale_log2 * (float)(std::sqrt(M_PI / 2.0) / pk->m) : 0.0f;
-    if ((rc = hip_status(launch_qprep(qa, s))) != TQ_OK) return rc;
     AttnArgs a{};
     a.pk = static_cast<const uint8_t*>(packed_k);
     a.pv = static_cast<const uint8_t*>(packed_v);
@@ -672,6 +671,14 @@ int attention_impl(const tq_params* pk, const tq_params* pv, const void* q, tq_d
     a.v_off_norm = lv.off_norm;
     a.tk = tk;
     a.tv = tv;
+    a.q = q;
+    a.q_bf16 = qa.q_bf16;
+    a.q_scale = qa.q_scale;
+    a.p_scale = qa.p_scale;
+    // the query prep runs inside the attention kernel where every block covers one stream, else as
+    // its own launch writing the workspace's query operands
+    a.fused_q = attention_fuses_qprep(a) ? 1 : 0;
+    if (!a.fused_q && (rc = hip_status(launch_qprep(qa, s))) != TQ_OK) return rc;
     bool supported = true;
     const hipError_t e = launch_attention(a, cus, s, &supported);
     if (!supported) return TQ_EUNSUPPORTED;

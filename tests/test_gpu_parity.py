@@ -153,15 +153,15 @@ def test_cfg3_reduced_scores(b, m, nq):
     print(f"scores b={b} m={m}: worst row rel L2 {worst:.2e}")
 
 
-def _attention_case(batch, hq, hkv, N, d, b, m, out_dtype, seed=4001, scale=0.0, sketch=0):
-    ck, cv = T.Codec(d, b, m, hkv, seed, sketch), T.Codec(d, b, 0, hkv, seed + 1)
+def _attention_case(batch, hq, hkv, N, d, b, m, out_dtype, seed=4001, scale=0.0, sketch=0, rotation=0):
+    ck, cv = T.Codec(d, b, m, hkv, seed, sketch, rotation), T.Codec(d, b, 0, hkv, seed + 1)
     K = I.rope_gaussian(batch * hkv, N, d, seed, device=DEV)
     V = I.rope_gaussian(batch * hkv, N, d, seed + 1, device=DEV)
     q = I.cfg4_queries(batch, hq, d, N, seed + 2, device=DEV)
     pk, pv = T.encode(ck, K), T.encode(cv, V)
     out = T.decode_attention(ck, cv, q, pk, pv, hkv, N, scale, out_dtype=out_dtype)
     torch.cuda.synchronize()
-    tk, tv = P.Tables(d, b, m, hkv, seed, sketch), P.Tables(d, b, 0, hkv, seed + 1)
+    tk, tv = P.Tables(d, b, m, hkv, seed, sketch, rotation), P.Tables(d, b, 0, hkv, seed + 1)
     rk = O.unpack_tensor(pk.cpu().numpy(), d, b, m, batch * hkv, N)
     rv = O.unpack_tensor(pv.cpu().numpy(), d, b, 0, batch * hkv, N)
     q64 = _x64(q)
@@ -189,6 +189,25 @@ def test_decode_attention_reduced(batch, hq, hkv, N, d, b, m):
     print(f"attention {batch}x{hq}/{hkv} N={N} d={d} b={b} m={m}: worst row rel L2 f32 {r32['worst']:.2e},"
           f" bf16 {rb['worst']:.2e} against the rounded oracle ({rb['worst_unrounded']:.2e} unrounded,"
           f" rounding floor {rb['floor']:.2e})")
+
+
+# shapes whose split count is a multiple of the 12 waves of a block, so every block covers one
+# stream and the attention kernel runs the query prep itself (4-bit keys and values, d <= 128, at
+# most 8 query heads per kv head)
+@pytest.mark.parametrize("batch,hq,hkv,N,d,m,rot", [
+    (2, 8, 2, 3072, 128, 128, 0),      # 12 splits of 256 tokens
+    (2, 8, 2, 3000, 128, 128, 0),      # 12 splits, ragged last split
+    (1, 8, 1, 6144, 128, 128, 0),      # one stream, 24 splits, 8 query heads per kv head
+    (2, 4, 2, 3072, 64, 64, 0),        # d = 64
+    (2, 4, 4, 3072, 128, 0, 0),        # no sketch, one query head per kv head
+    (2, 8, 2, 3072, 128, 32, 0),       # m = 32
+    (2, 8, 2, 3072, 128, 128, 1),      # Plain-KV keys (no rotation of the queries)
+])
+def test_decode_attention_in_kernel_query_prep(batch, hq, hkv, N, d, m, rot):
+    print(f"attention with the in-kernel query prep {batch}x{hq}/{hkv} N={N} d={d} m={m} rotation={rot}", flush=True)
+    r32 = _attention_case(batch, hq, hkv, N, d, 4, m, torch.float32, seed=4301 + N + m, rotation=rot)
+    rb = _attention_case(batch, hq, hkv, N, d, 4, m, torch.bfloat16, seed=4301 + N + m, rotation=rot)
+    print(f"  worst row rel L2 f32 {r32['worst']:.2e}, bf16 {rb['worst']:.2e} against the rounded oracle")
 
 
 # ---------------------------------------------------------------------------------------------
@@ -445,9 +464,10 @@ def test_decode_attention_few_tokens(N, out_dtype):
     print(f"attention over {N} tokens ({out_dtype}): worst row rel L2 {r['worst']:.2e}")
 
 
+@pytest.mark.parametrize("N", [700, 3072])        # 3072: the in-kernel query prep (12 splits per stream)
 @pytest.mark.parametrize("scale", [2.0 ** -20, 2.0 ** 6])
-def test_decode_attention_across_query_scales(scale):
-    d, b, m, batch, hq, hkv, N, seed = 128, 4, 128, 1, 4, 2, 700, 4201
+def test_decode_attention_across_query_scales(scale, N):
+    d, b, m, batch, hq, hkv, seed = 128, 4, 128, 1, 4, 2, 4201
     ck, cv = T.Codec(d, b, m, hkv, seed), T.Codec(d, b, 0, hkv, seed + 1)
     K = I.rope_gaussian(batch * hkv, N, d, seed, device=DEV)
     V = I.rope_gaussian(batch * hkv, N, d, seed + 1, device=DEV)
