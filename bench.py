@@ -35,20 +35,20 @@ MFMA_F16_PEAK_TFLOPS = 2500.0  # MI355X dense fp16 MFMA, published (the sketch p
 # the kernel's sources are the ones it was measured on (sha256 of the .hip file + shared headers).
 FETCH_UNIT_B, WRITE_UNIT_B = 2048, 1024
 TRAFFIC = {
-    "encode_kv": {"fetch": 4194704.0, "write": 2493893.8125, "src": "encode.hip",
+    "encode_kv": {"fetch": 4194704.0, "write": 2495027.78125, "src": "encode.hip",
         "sha": "992d71c591d2d8a443bf0051e0ef8e31966255a4ca7629b73e9250ddda24daac"},
-    "encode_k": {"fetch": 2097505.5, "write": 1394466.5625, "src": "encode.hip",
+    "encode_k": {"fetch": 2097505.5, "write": 1394656.375, "src": "encode.hip",
         "sha": "992d71c591d2d8a443bf0051e0ef8e31966255a4ca7629b73e9250ddda24daac"},
-    "encode_v": {"fetch": 2110658.875, "write": 1090979.96875, "src": "encode.hip",
+    "encode_v": {"fetch": 2111449.75, "write": 1091140.375, "src": "encode.hip",
         "sha": "992d71c591d2d8a443bf0051e0ef8e31966255a4ca7629b73e9250ddda24daac"},
-    "decode_attention": {"fetch": 1233019.8125, "write": 6241.0, "src": "attention.hip",
-        "sha": "4a5ef5d6cf48758bd8ce022548ab11229a28468c121500b993a01171da50a630"},
-    "decode_v_bf16": {"fetch": 550671.375, "write": 4194304.0, "src": "decode.hip",
+    "decode_attention": {"fetch": 1232278.4375, "write": 6240.0, "src": "attention.hip",
+        "sha": "57c6ef526353f7a450afd9a3dc46799f2fd1264f7a21d212250aa6aa4b42032f"},
+    "decode_v_bf16": {"fetch": 550368.25, "write": 4194304.0, "src": "decode.hip",
         "sha": "b1ba67ba042266686af375dd30fa7fbae0fbf2bf933c7820de5b5978f1c26054"},
 }
 TRAFFIC["decode_attention_back_to_back"] = TRAFFIC["decode_attention"]
 TRAFFIC_HEADERS_SHA = ("6643b4ed6d32e0cc4205551fb1ef8fab74077690c7d82ac29a903d73ebc0d666"   # common.hpp
-                       "ac32d81f3164d8a735c83e985560964be8ac1e48c58555fb8691aeb330ecffce")  # kernels.hpp
+                       "183fca10670edac7211b62d0d02df11d2a540416ee2b250c1d8ac7525a821db7")  # kernels.hpp
 
 
 def _sha(path: str) -> str:
