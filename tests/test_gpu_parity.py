@@ -464,10 +464,8 @@ def test_decode_attention_few_tokens(N, out_dtype):
     print(f"attention over {N} tokens ({out_dtype}): worst row rel L2 {r['worst']:.2e}")
 
 
-@pytest.mark.parametrize("N", [700, 3072])        # 3072: the in-kernel query prep (12 splits per stream)
-@pytest.mark.parametrize("scale", [2.0 ** -20, 2.0 ** 6])
-def test_decode_attention_across_query_scales(scale, N):
-    d, b, m, batch, hq, hkv, seed = 128, 4, 128, 1, 4, 2, 4201
+def _query_scale_case(scale, N, hq, b, seed=4201):
+    d, m, batch, hkv = 128, 128, 1, 2
     ck, cv = T.Codec(d, b, m, hkv, seed), T.Codec(d, b, 0, hkv, seed + 1)
     K = I.rope_gaussian(batch * hkv, N, d, seed, device=DEV)
     V = I.rope_gaussian(batch * hkv, N, d, seed + 1, device=DEV)
@@ -480,10 +478,25 @@ def test_decode_attention_across_query_scales(scale, N):
     rk = O.unpack_tensor(pk.cpu().numpy(), d, b, m, batch * hkv, N)
     rv = O.unpack_tensor(pv.cpu().numpy(), d, b, 0, batch * hkv, N)
     q64 = _x64(q)
-    ref = np.array([[P.oracle_attention_row(tk, tv, rk[h // 2], rv[h // 2], h // 2, q64[0, h], 1 / math.sqrt(d))
+    g = hq // hkv
+    ref = np.array([[P.oracle_attention_row(tk, tv, rk[h // g], rv[h // g], h // g, q64[0, h], 1 / math.sqrt(d))
                      for h in range(hq)]])
     r = P.check_attention_rows(out.cpu().numpy(), ref, False)
-    print(f"attention query scale {scale:.3g}: worst row rel L2 {r['worst']:.2e}")
+    print(f"attention query scale {scale:.3g}, {hq} query heads over {hkv} kv heads, b = {b}, {N} tokens: "
+          f"worst row rel L2 {r['worst']:.2e}")
+
+
+@pytest.mark.parametrize("N", [700, 3072])        # 3072: the in-kernel query prep (12 splits per stream)
+@pytest.mark.parametrize("scale", [2.0 ** -20, 2.0 ** 6])
+def test_decode_attention_across_query_scales(scale, N):
+    _query_scale_case(scale, N, 4, 4)
+
+
+# more than 8 query heads per kv head: the sketch term's lo parts take their own MFMAs (no free
+# query columns); b = 3 runs the geometry without the shared 4-bit tables
+@pytest.mark.parametrize("hq,b", [(32, 4), (32, 3), (4, 3)])
+def test_decode_attention_sharp_softmax_other_geometries(hq, b):
+    _query_scale_case(2.0 ** 6, 1000, hq, b, seed=4251 + b)
 
 
 # ---------------------------------------------------------------------------------------------
