@@ -492,6 +492,34 @@ def test_decode_attention_across_query_scales(scale, N):
     _query_scale_case(scale, N, 4, 4)
 
 
+def test_decode_attention_zero_and_tiny_query_rows():
+    """rows of one group with very different scales in the in-kernel query prep (3072 tokens: 12
+    splits per stream): an all-zero row (uniform softmax: the mean of the decoded values), a row
+    scaled by 2^-30 and a row scaled by 2^8 beside an ordinary one; each row takes its own power of
+    two"""
+    d, b, m, batch, hq, hkv, N, seed = 128, 4, 128, 1, 8, 2, 3072, 4281
+    ck, cv = T.Codec(d, b, m, hkv, seed), T.Codec(d, b, 0, hkv, seed + 1)
+    K = I.rope_gaussian(batch * hkv, N, d, seed, device=DEV)
+    V = I.rope_gaussian(batch * hkv, N, d, seed + 1, device=DEV)
+    qn = np.random.default_rng(seed).standard_normal((batch, hq, d))
+    qn[0, 0] = 0.0
+    qn[0, 1] *= 2.0 ** -30
+    qn[0, 2] *= 2.0 ** 8
+    qn[0, 5] = 0.0                              # a zero row in the second group too
+    q = torch.tensor(qn, dtype=torch.float32, device=DEV)
+    pk, pv = T.encode(ck, K), T.encode(cv, V)
+    out = T.decode_attention(ck, cv, q, pk, pv, hkv, N, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    tk, tv = P.Tables(d, b, m, hkv, seed), P.Tables(d, b, 0, hkv, seed + 1)
+    rk = O.unpack_tensor(pk.cpu().numpy(), d, b, m, batch * hkv, N)
+    rv = O.unpack_tensor(pv.cpu().numpy(), d, b, 0, batch * hkv, N)
+    g, q64 = hq // hkv, _x64(q)
+    ref = np.array([[P.oracle_attention_row(tk, tv, rk[h // g], rv[h // g], h // g, q64[0, h], 1 / math.sqrt(d))
+                     for h in range(hq)]])
+    r = P.check_attention_rows(out.cpu().numpy(), ref, False)
+    print(f"zero, 2^-30 and 2^8 query rows: worst row rel L2 {r['worst']:.2e}")
+
+
 # more than 8 query heads per kv head: the sketch term's lo parts take their own MFMAs (no free
 # query columns); b = 3 runs the geometry without the shared 4-bit tables
 @pytest.mark.parametrize("hq,b", [(32, 4), (32, 3), (4, 3)])
