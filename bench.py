@@ -86,7 +86,7 @@ def main():
     if args.gpus != 1 or world != 1:
         if int(os.environ.get("RANK", "0")) == 0:
             print(f"bench.py measures one GPU only (asked for {max(args.gpus, world)}): the codec has no "
-                  f"multi-GPU path in this build; run with --gpus 1", file=sys.stderr)
+                  f"multi-GPU path (one GPU per process is all it runs); run with --gpus 1", file=sys.stderr)
         sys.exit(2)
 
     import torch
@@ -200,7 +200,7 @@ def main():
     if not args.no_cpu_baseline:
         sample = _parity_sample(K[:1, :2048], V[:1, :2048], pk, pv, ck, cv, streams, N, d)
 
-    # standalone decode of the V cache to bf16 (row a8), timed apart from the step
+    # standalone decode of the V cache to bf16, timed apart from the step
     xh = torch.empty(streams, N, d, dtype=torch.bfloat16, device=dev)
     T.decode(cv, pv, streams, N, torch.bfloat16, out=xh)
     torch.cuda.synchronize()

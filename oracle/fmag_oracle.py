@@ -9,7 +9,7 @@ post: take the FFT of each K/V vector along head_dim, quantise the magnitude spe
 with min-max quantisation, keep the phase (at bf16, or at 8 or 6 bits in its "Fmag4+phase8b" and
 "phase6b" variants), and reconstruct with the inverse FFT of mag_q·(cos φ + i sin φ).
 
-Readings where the thread is silent (each listed in the design doc):
+Readings where the thread is silent (the plainest reading the rest supports):
   * The transform is the real FFT of the d real coordinates, X_k = Σ_j x_j e^{-2πi jk/d},
     k = 0..d/2 (the other bins are conjugates), inverted by the real inverse FFT.
   * Min-max is per vector over its d/2 + 1 magnitudes: lo = min, hi = max,

@@ -19,7 +19,7 @@ Sources (cited by page title and section):
   [MAX] J. Max, "Quantizing for minimum distortion", IRE Trans. IT-6 (1960): the Lloyd-Max
         quantiser of a unit Gaussian.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent (the plainest reading the rest supports):
   * The basis is the full eigenbasis of C, eigenvalues descending; the first d_eff columns are the
     semantic dimensions (block power iteration converges to them; ``block_power_iteration`` below
     is the pages' method and is pinned to the library eigensolver), the remaining d - d_eff

@@ -20,7 +20,7 @@ Sources (cited by page title and section):
   [SM]  Steele, Lea, Flood, "Fast splittable pseudorandom number generators" (OOPSLA 2014):
         SplitMix64.  [BM] Box & Muller (1958): normal deviates from two uniforms.
 
-Readings where the pages are silent (each listed in the design doc):
+Readings where the pages are silent (the plainest reading the rest supports):
   * WHT is the unnormalised Sylvester-ordered Hadamard matrix H (H_2n = [[H, H], [H, -H]]).
   * Codebook index = number of thresholds <= y (ties go to the upper cell), centroids ascending.
   * Vectors are normalised by their exact norm; the norm is stored as fp16 (round to nearest even).

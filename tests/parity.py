@@ -4,7 +4,7 @@ All oracle inputs are the exact input bytes handed to the GPU (copied back to th
 score and attention parity are computed by the oracle from the GPU's own packed bytes, so a
 legitimately flagged encode decision cannot propagate.
 
-Tolerances (the workload statement's, with the readings listed in the design doc):
+Tolerances (the bars the codec's parity is held to, and the readings they rest on):
   * packed indices bit-exact except coordinates the oracle flags within 1e-6 of a threshold;
     sketch bits exact except where the oracle flags them, |S e| < 1e-6 on the exact residual
     (recomputed from the GPU's indices where one differed);

@@ -4,7 +4,7 @@ attention output ("Ablation, Statistical Inference, and Validation for KV-Cache 
 "Error metric"; §8 and its figures for the findings checked here):
   * heavy tails (Student-t ν = 3): TQ-KV beats SQU-KV (the calibrated basis is misaligned);
   * on a structured regime at b = 2 SQU-KV beats TQ-KV: here the steep rank-4 spectrum.  On the
-    flat rank-8 subspace with 5 % noise (this build's reading of lowrank_aligned; the pages' regime
+    flat rank-8 subspace with 5 % noise (the reading taken here of lowrank_aligned; the pages' regime
     table is missing) SQU-KV does not win at b = 2, unlike the pages' ranking; the table printed
     by the fixture records both;
   * water-filling equals uniform allocation when the semantic variances are within a factor 4
