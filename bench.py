@@ -6,7 +6,8 @@ cache — batch 16, 32 query heads / 8 KV heads, context 131072, d = 128; K enco
 WHT + Lloyd-Max codebook plus a 1-bit QJL sketch (m = 128), V with a 4-bit codebook; K and V are
 seeded N(0,1) bf16 rotated RoPE-style by position; queries N(0,1) bf16 rotated at t = 131072.
 
-One step = encode K + encode V + decode-attention (query prep, split-K attention, combine).
+One step = encode K and V (one launch) + decode-attention (split-K attention, which does the
+query prep itself on this shape, then the split combine).
 bf16-equivalent bytes of a step = (#K + #V vectors) x d x 2 B, counted once for the encode and
 once for the attention pass over the cache.
 
